@@ -1,0 +1,240 @@
+"""fp64 CPU oracle of the mixture-of-experts layer (ctypes over moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg, never by the product package. It shares no code
+with the HIP library.
+
+Encodings are taken from the numpy dtype of each array:
+float32 -> binary32, uint16 -> bfloat16 bit patterns, uint8 -> OCP E4M3
+bytes, float64 -> binary64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
+ACT_NONE, ACT_RELU = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+             "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.orc_decode.argtypes = [vp, i32, i64]
+        L.orc_decode.restype = dbl
+        L.orc_decode_array.argtypes = [vp, i32, i64, vp]
+        L.orc_round_bf16.argtypes = [dbl]
+        L.orc_round_bf16.restype = dbl
+        L.orc_bf16_bits.argtypes = [dbl]
+        L.orc_bf16_bits.restype = ctypes.c_uint16
+        L.orc_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp]
+        L.orc_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+        L.orc_gather_rows.argtypes = [vp, i64, vp, i32, i32, vp]
+        L.orc_gmm.argtypes = [vp, i32, dbl, vp, i32, dbl, vp, i32, i32, i32, i32, vp, i32, vp, i32]
+        L.orc_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.orc_expert_ffn.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.orc_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                vp, i32]
+        L.orc_layer_tokens.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
+                                       vp, vp, vp, vp, i32]
+        L.orc_layer_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        for name in ("orc_decode_array", "orc_route", "orc_permute", "orc_gather_rows", "orc_gmm",
+                     "orc_combine", "orc_expert_ffn", "orc_layer", "orc_layer_tokens",
+                     "orc_layer_dense"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _code(a: np.ndarray) -> int:
+    m = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): E4M3,
+         np.dtype(np.float64): F64}
+    if a.dtype not in m:
+        raise TypeError(f"oracle: unsupported array dtype {a.dtype}")
+    return m[a.dtype]
+
+
+def _c(a):
+    a = np.ascontiguousarray(a)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def decode(a: np.ndarray) -> np.ndarray:
+    a, pa = _c(a)
+    out = np.empty(a.size, np.float64)
+    _check(lib().orc_decode_array(pa, _code(a), a.size, _p(out)), "decode")
+    return out.reshape(a.shape)
+
+
+def round_bf16(v: float) -> float:
+    return lib().orc_round_bf16(float(v))
+
+
+def bf16_bits(values) -> np.ndarray:
+    v = np.asarray(values, np.float64)
+    f = lib().orc_bf16_bits
+    return np.array([f(float(x)) for x in v.ravel()], np.uint16).reshape(v.shape)
+
+
+def route(x, wr, T, H, E, K, bias=None):
+    """Router scores, top-k and sparse softmax. Returns (idx, gate, logits, gap)."""
+    x, px = _c(x)
+    wr, pw = _c(wr)
+    if _code(x) != _code(wr):
+        raise TypeError("x and wr must share an encoding")
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), np.float64)
+    logits = np.empty((T, E), np.float64)
+    gap = np.empty(T, np.float64)
+    _check(lib().orc_route(px, pw, _code(x), _p(b), T, H, E, K, _p(idx), _p(gate), _p(logits),
+                           _p(gap)), "route")
+    return idx, gate, logits, gap
+
+
+def permute(topk_idx, E):
+    idx, pidx = _c(np.asarray(topk_idx, np.int32))
+    T, K = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    psrc = np.empty(T * K, np.int32)
+    pdst = np.empty(T * K, np.int32)
+    _check(lib().orc_permute(pidx, T, E, K, _p(counts), _p(offsets), _p(psrc), _p(pdst)), "permute")
+    return counts, offsets, psrc, pdst
+
+
+def gather_rows(x, perm_src, K):
+    x, px = _c(x)
+    ps, pps = _c(np.asarray(perm_src, np.int32))
+    A = ps.size
+    out = np.empty((A,) + x.shape[1:], x.dtype)
+    row_bytes = x[0].nbytes if x.shape[0] else 1
+    _check(lib().orc_gather_rows(px, row_bytes, pps, A, K, _p(out)), "gather_rows")
+    return out
+
+
+def gmm(a, w, offsets, act=ACT_NONE, a_scale=1.0, w_scale=1.0, rows=None, nthreads=1):
+    """Grouped GEMM: a (A,Hin), w (e,Hin,N), offsets (e+1). fp64 result."""
+    a, pa = _c(a)
+    w, pw = _c(w)
+    off, poff = _c(np.asarray(offsets, np.int32))
+    e, Hin, N = w.shape
+    if a.shape[1] != Hin:
+        raise ValueError("a and w disagree on Hin")
+    if rows is None:
+        out = np.empty((int(off[e]), N), np.float64)
+        prow, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, np.int32)
+        out = np.empty((rows.size, N), np.float64)
+        prow, nrows = _p(rows), rows.size
+    _check(lib().orc_gmm(pa, _code(a), float(a_scale), pw, _code(w), float(w_scale), poff, e, Hin,
+                         N, act, prow, nrows, _p(out), int(nthreads)), "gmm")
+    return out
+
+
+def combine(yp, perm_dst, gate, T, K):
+    yp, pyp = _c(np.asarray(yp, np.float64))
+    pd, ppd = _c(np.asarray(perm_dst, np.int32))
+    N = yp.shape[1]
+    g = None if gate is None else np.ascontiguousarray(gate, np.float64)
+    out = np.empty((T, N) if g is not None else (T * K, N), np.float64)
+    _check(lib().orc_combine(pyp, ppd, _p(g), T, K, N, _p(out)), "combine")
+    return out
+
+
+def expert_ffn(xrow, w1, w2, ex, act=ACT_RELU):
+    xv, pxv = _c(np.asarray(xrow, np.float64))
+    w1, p1 = _c(w1)
+    w2, p2 = _c(w2)
+    _, H, F = w1.shape
+    out = np.empty(H, np.float64)
+    _check(lib().orc_expert_ffn(pxv, p1, p2, _code(w1), ex, H, F, act, _p(out)), "expert_ffn")
+    return out
+
+
+def layer(x, wr, w1, w2, K, bias=None, act=ACT_RELU, nthreads=1):
+    """Whole layer, sparse form. Returns dict with y, idx, gate, gap, counts."""
+    x, px = _c(x)
+    wr, pwr = _c(wr)
+    w1, p1 = _c(w1)
+    w2, p2 = _c(w2)
+    T, H = x.shape
+    E, _, F = w1.shape
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    y = np.empty((T, H), np.float64)
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), np.float64)
+    gap = np.empty(T, np.float64)
+    counts = np.empty(E, np.int32)
+    _check(lib().orc_layer(px, pwr, _p(b), p1, p2, _code(x), T, H, E, K, F, act, _p(y), _p(idx),
+                           _p(gate), _p(gap), _p(counts), int(nthreads)), "layer")
+    return {"y": y, "idx": idx, "gate": gate, "gap": gap, "counts": counts}
+
+
+def layer_tokens(x, wr, w1, w2, K, tokens, bias=None, act=ACT_RELU, nthreads=1):
+    """Per-token form on a subset of tokens. Returns dict with y, idx, gate, gap."""
+    x, px = _c(x)
+    wr, pwr = _c(wr)
+    w1, p1 = _c(w1)
+    w2, p2 = _c(w2)
+    T, H = x.shape
+    E, _, F = w1.shape
+    tok, ptok = _c(np.asarray(tokens, np.int32))
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    n = tok.size
+    y = np.empty((n, H), np.float64)
+    idx = np.empty((n, K), np.int32)
+    gate = np.empty((n, K), np.float64)
+    gap = np.empty(n, np.float64)
+    _check(lib().orc_layer_tokens(px, pwr, _p(b), p1, p2, _code(x), T, H, E, K, F, act, ptok, n,
+                                  _p(y), _p(idx), _p(gate), _p(gap), int(nthreads)), "layer_tokens")
+    return {"y": y, "idx": idx, "gate": gate, "gap": gap}
+
+
+def layer_dense(x, wr, w1, w2, K, bias=None, act=ACT_RELU):
+    x, px = _c(x)
+    wr, pwr = _c(wr)
+    w1, p1 = _c(w1)
+    w2, p2 = _c(w2)
+    T, H = x.shape
+    E, _, F = w1.shape
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    y = np.empty((T, H), np.float64)
+    _check(lib().orc_layer_dense(px, pwr, _p(b), p1, p2, _code(x), T, H, E, K, F, act, _p(y)),
+           "layer_dense")
+    return y

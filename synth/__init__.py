@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the MoE layer (ctypes over synth.c).
+
+This module draws numbers and encodes them into the byte formats the layer
+reads; it holds none of the layer's own arithmetic. The HIP path and the
+CPU oracle both consume exactly the bytes produced here.
+
+Host arrays use: float32 for binary32, uint16 for bfloat16 bit patterns,
+uint8 for OCP E4M3 bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+
+SEED_BASE = 0x4D6F45000000
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-ffp-contract=off", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        u64, i64, i32, dbl, vp = (ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                                  ctypes.c_void_p)
+        L.synth_u64.argtypes = [u64, u64]
+        L.synth_u64.restype = u64
+        L.synth_normal_f32.argtypes = [u64, i64, dbl, dbl, vp, i32]
+        L.synth_normal_bf16.argtypes = [u64, i64, dbl, dbl, vp, i32]
+        L.synth_int_f32.argtypes = [u64, i64, i32, i32, vp, i32]
+        L.synth_int_bf16.argtypes = [u64, i64, i32, i32, vp, i32]
+        L.synth_f32_to_bf16.argtypes = [vp, i64, vp, i32]
+        L.synth_f32_to_e4m3.argtypes = [vp, i64, ctypes.c_float, vp, i32]
+        L.synth_amax_f32.argtypes = [vp, i64]
+        L.synth_amax_f32.restype = ctypes.c_float
+        L.synth_random_routing.argtypes = [u64, i32, i32, i32, vp]
+        L.synth_random_routing.restype = i32
+        _lib = L
+    return _lib
+
+
+def threads() -> int:
+    """Worker threads for generation: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def seed_for(config: int, tensor_id: int) -> int:
+    return SEED_BASE + 256 * int(config) + int(tensor_id)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def normal(seed: int, shape, std: float = 1.0, mean: float = 0.0, dtype: str = "f32") -> np.ndarray:
+    n = int(np.prod(shape))
+    if dtype == "f32":
+        out = np.empty(n, np.float32)
+        lib().synth_normal_f32(seed, n, mean, std, _ptr(out), threads())
+    elif dtype == "bf16":
+        out = np.empty(n, np.uint16)
+        lib().synth_normal_bf16(seed, n, mean, std, _ptr(out), threads())
+    else:
+        raise ValueError(dtype)
+    return out.reshape(shape)
+
+
+def ints(seed: int, shape, lo: int, hi: int, dtype: str = "f32") -> np.ndarray:
+    n = int(np.prod(shape))
+    if dtype == "f32":
+        out = np.empty(n, np.float32)
+        lib().synth_int_f32(seed, n, lo, hi, _ptr(out), threads())
+    elif dtype == "bf16":
+        out = np.empty(n, np.uint16)
+        lib().synth_int_bf16(seed, n, lo, hi, _ptr(out), threads())
+    else:
+        raise ValueError(dtype)
+    return out.reshape(shape)
+
+
+def to_bf16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().synth_f32_to_bf16(_ptr(a), a.size, _ptr(out), threads())
+    return out
+
+
+def to_e4m3(a: np.ndarray, scale: float) -> np.ndarray:
+    """E4M3(a / scale), round to nearest even, saturating at +-448."""
+    a = np.ascontiguousarray(a, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib().synth_f32_to_e4m3(_ptr(a), a.size, float(scale), _ptr(out), threads())
+    return out
+
+
+def amax(a: np.ndarray) -> float:
+    a = np.ascontiguousarray(a, np.float32)
+    return float(lib().synth_amax_f32(_ptr(a), a.size))
+
+
+def quantize_e4m3(a: np.ndarray):
+    """Per-tensor quantisation input recipe: scale = amax / 448, bytes = E4M3(a / scale)."""
+    s = amax(a) / 448.0
+    if s == 0.0:
+        s = 1.0
+    return to_e4m3(a, s), np.float32(s)
+
+
+def random_routing(seed: int, T: int, E: int, K: int) -> np.ndarray:
+    out = np.empty((T, K), np.int32)
+    if lib().synth_random_routing(seed, T, E, K, _ptr(out)) != 0:
+        raise ValueError("bad routing shape")
+    return out
+
+
+def u64(seed: int, j: int) -> int:
+    return int(lib().synth_u64(seed, j))
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to binary32 (exact)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)

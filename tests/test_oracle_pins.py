@@ -1,0 +1,394 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check below ties one oracle function to a library routine, a closed
+form, an invariant, a special case with a textbook answer, or brute force on
+tiny inputs, so that a dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one of them. CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.sparse
+import scipy.special
+import torch
+
+import oracle
+import synth
+from synth import configs
+
+
+def _dec(a):
+    """Independent decode for pins: numpy/torch views, not the oracle's decoder."""
+    if a.dtype == np.uint16:
+        return synth.bf16_to_f32(a).astype(np.float64)
+    return np.asarray(a, np.float64)
+
+
+# ---------------------------------------------------------------- decoding
+
+def test_bf16_decode_matches_torch():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.decode(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode(codes)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2  # 0x7f and 0xff
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+
+
+def test_round_bf16_matches_torch_on_binary32_values():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 1e3,
+                        rng.standard_normal(2000).astype(np.float32) * 1e-39,  # subnormals
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.0e38, 0.0],
+                                 np.float32)])
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_bits(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_ties_to_even_direct_from_fp64():
+    # 1 + 2^-8 is exactly half-way between bf16 neighbours 1 and 1 + 2^-7: even is 1.
+    assert oracle.round_bf16(1 + 2 ** -8) == 1.0
+    assert oracle.round_bf16(1 + 3 * 2 ** -8) == 1 + 2 * 2 ** -7
+    # just above the half-way point must round up (no double rounding through binary32)
+    assert oracle.round_bf16(1 + 2 ** -8 + 2 ** -40) == 1 + 2 ** -7
+
+
+# ---------------------------------------------------------------- generator encoders
+
+def test_synth_bf16_encoder_matches_torch():
+    x = synth.normal(123, (50000,), 3.0)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.to_bf16(x), ref)
+
+
+def test_synth_e4m3_encoder_matches_torch_in_range():
+    x = synth.normal(7, (50000,), 100.0)
+    x = np.clip(x, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(synth.to_e4m3(x, 1.0), ref)
+
+
+def test_synth_counter_based_prefix_property():
+    a = synth.normal(99, (1000,))
+    b = synth.normal(99, (300,))
+    assert np.array_equal(a[:300], b)
+    assert abs(float(a.mean())) < 0.15 and abs(float(a.std()) - 1) < 0.1
+
+
+def test_random_routing_distinct_and_in_range():
+    idx = synth.random_routing(5, 500, 32, 8)
+    assert idx.min() >= 0 and idx.max() < 32
+    assert all(len(set(r)) == 8 for r in idx.tolist())
+
+
+# ---------------------------------------------------------------- router
+
+def _tiny(integer=False, **kw):
+    return configs.layer_inputs("tiny", integer=integer, **kw)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_route_logits_match_numpy_matmul(integer):
+    d = _tiny(integer)
+    idx, gate, logits, gap = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], d["K"])
+    ref = _dec(d["x"]) @ _dec(d["wr"])
+    np.testing.assert_allclose(logits, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_route_bias_added_before_selection():
+    d = _tiny(bias=True)
+    _, _, logits_b, _ = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], d["K"], bias=d["bias"])
+    _, _, logits, _ = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], d["K"])
+    np.testing.assert_allclose(logits_b - logits, np.broadcast_to(d["bias"].astype(np.float64),
+                                                                  logits.shape), atol=1e-12)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+@pytest.mark.parametrize("K", [1, 2, 3, 8])
+def test_topk_matches_bruteforce_lexsort(integer, K):
+    d = _tiny(integer)
+    idx, gate, logits, gap = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], K)
+    for t in range(d["T"]):
+        order = np.lexsort((np.arange(d["E"]), -logits[t]))  # by -score, then index
+        assert list(idx[t]) == list(order[:K])
+        srt = logits[t][order]
+        want_gap = srt[K - 1] - srt[K] if K < d["E"] else math.inf
+        assert gap[t] == want_gap
+
+
+def test_integer_inputs_exercise_ties_lower_index_wins():
+    d = _tiny(True)
+    idx, _, logits, gap = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], d["K"])
+    ties = 0
+    for t in range(d["T"]):
+        for a in range(d["K"] - 1):
+            if logits[t, idx[t, a]] == logits[t, idx[t, a + 1]]:
+                assert idx[t, a] < idx[t, a + 1]
+                ties += 1
+        ties += int(gap[t] == 0)
+    assert ties > 0  # the integer variant does contain ties
+
+
+def test_explicit_tie_goes_to_lower_index():
+    H, E, K = 4, 6, 3
+    x = np.ones((1, H), np.float32)
+    wr = np.zeros((H, E), np.float32)
+    wr[:, 4] = 1.0
+    wr[:, 1] = 1.0  # experts 1 and 4 tie for first
+    wr[:, 5] = 0.5
+    idx, gate, _, gap = oracle.route(x, wr, 1, H, E, K)
+    assert list(idx[0]) == [1, 4, 5]
+    assert gate[0, 0] == gate[0, 1]
+
+
+def test_gates_sum_to_one_and_k2_closed_form():
+    d = _tiny()
+    idx, gate, logits, _ = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], 2)
+    np.testing.assert_allclose(gate.sum(1), 1.0, atol=1e-15)
+    l0 = logits[np.arange(d["T"]), idx[:, 0]]
+    l1 = logits[np.arange(d["T"]), idx[:, 1]]
+    np.testing.assert_allclose(gate[:, 0], scipy.special.expit(l0 - l1), rtol=1e-14)
+
+
+def test_gates_k_equals_e_is_full_softmax():
+    d = _tiny()
+    E = d["E"]
+    idx, gate, logits, gap = oracle.route(d["x"], d["wr"], d["T"], d["H"], E, E)
+    full = scipy.special.softmax(logits, axis=1)
+    for t in range(d["T"]):
+        np.testing.assert_allclose(gate[t], full[t][idx[t]], rtol=1e-13)
+    assert np.all(np.isinf(gap))
+
+
+def test_gates_k1_is_one():
+    d = _tiny()
+    _, gate, _, _ = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], 1)
+    assert np.all(gate == 1.0)
+
+
+# ---------------------------------------------------------------- dispatch
+
+def _check_perm(idx, E, counts, offsets, psrc, pdst):
+    T, K = idx.shape
+    A = T * K
+    assert counts.sum() == A
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(np.sort(psrc), np.arange(A))
+    assert np.array_equal(psrc[pdst], np.arange(A))
+    assert np.array_equal(pdst[psrc], np.arange(A))
+    for e in range(E):
+        seg = psrc[offsets[e]:offsets[e + 1]]
+        assert np.all(idx.ravel()[seg] == e)
+        assert np.all(np.diff(seg) > 0)  # stable: ascending (token, slot)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_permute_invariants_and_csc_of_mask(integer):
+    d = _tiny(integer)
+    idx, _, _, _ = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], d["K"])
+    counts, offsets, psrc, pdst = oracle.permute(idx, d["E"])
+    _check_perm(idx, d["E"], counts, offsets, psrc, pdst)
+    # the per-expert row blocks are the CSC form of the (T,E) binary activation mask
+    T, K = idx.shape
+    mask = np.zeros((T, d["E"]))
+    mask[np.repeat(np.arange(T), K), idx.ravel()] = 1
+    csc = scipy.sparse.csc_matrix(mask)
+    csc.sort_indices()
+    assert np.array_equal(csc.indptr, offsets)
+    assert np.array_equal(csc.indices, psrc // K)
+
+
+def test_permute_empty_experts_and_skew():
+    idx = synth.random_routing(11, 300, 5, 3)
+    idx[idx == 2] = 0  # expert 2 now empty
+    idx2 = idx.copy()
+    counts, offsets, psrc, pdst = oracle.permute(idx2, 7)  # experts 5 and 6 empty too
+    assert counts[2] == 0 and counts[5] == 0 and counts[6] == 0
+    # duplicates of expert 0 inside a token are still placed stably
+    _check_perm(idx2, 7, counts, offsets, psrc, pdst)
+
+
+def test_permute_rejects_out_of_range_index():
+    idx = np.array([[0, 9]], np.int32)
+    with pytest.raises(ValueError):
+        oracle.permute(idx, 4)
+
+
+def test_gather_rows_is_bitwise_copy():
+    d = _tiny()
+    idx, _, _, _ = oracle.route(d["x"], d["wr"], d["T"], d["H"], d["E"], d["K"])
+    _, _, psrc, pdst = oracle.permute(idx, d["E"])
+    xp = oracle.gather_rows(d["x"], psrc, d["K"])
+    for t in range(d["T"]):
+        for k in range(d["K"]):
+            assert np.array_equal(xp[pdst[t * d["K"] + k]].view(np.uint32),
+                                  d["x"][t].view(np.uint32))
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+def _offsets(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gmm_single_expert_is_plain_matmul(dt):
+    a = synth.normal(1, (37, 50), dtype=dt)
+    w = synth.normal(2, (1, 50, 23), dtype=dt)
+    out = oracle.gmm(a, w, _offsets([37]))
+    np.testing.assert_allclose(out, _dec(a) @ _dec(w)[0], rtol=1e-12, atol=1e-12)
+
+
+def test_gmm_grouped_matches_per_segment_matmul_with_empty_groups():
+    counts = [5, 0, 17, 1, 0, 9]
+    off = _offsets(counts)
+    a = synth.normal(3, (off[-1], 33), dtype="bf16")
+    w = synth.normal(4, (6, 33, 19), dtype="bf16")
+    out = oracle.gmm(a, w, off)
+    A, W = _dec(a), _dec(w)
+    for e in range(6):
+        np.testing.assert_allclose(out[off[e]:off[e + 1]], A[off[e]:off[e + 1]] @ W[e], rtol=1e-12,
+                                   atol=1e-12)
+
+
+def test_gmm_transposed_operand_would_fail():
+    # square weights whose transpose differs: the wrong orientation is caught
+    a = synth.normal(5, (8, 16))
+    w = synth.normal(6, (1, 16, 16))
+    out = oracle.gmm(a, w, _offsets([8]))
+    assert not np.allclose(out, _dec(a) @ _dec(w)[0].T)
+    np.testing.assert_allclose(out, _dec(a) @ _dec(w)[0], rtol=1e-12, atol=1e-12)
+
+
+def test_gmm_relu_and_scales():
+    a = synth.normal(7, (12, 20))
+    w = synth.normal(8, (2, 20, 9))
+    off = _offsets([7, 5])
+    plain = oracle.gmm(a, w, off)
+    both = oracle.gmm(a, w, off, act=oracle.ACT_RELU, a_scale=0.25, w_scale=3.0)
+    np.testing.assert_allclose(both, np.maximum(plain * 0.75, 0), rtol=1e-14, atol=0)
+
+
+def test_gmm_identity_weights_return_input_exactly():
+    a = synth.normal(9, (30, 24), dtype="bf16")
+    w = synth.to_bf16(np.broadcast_to(np.eye(24, dtype=np.float32), (3, 24, 24)).copy())
+    out = oracle.gmm(a, w, _offsets([10, 0, 20]))
+    assert np.array_equal(out, _dec(a))
+
+
+def test_gmm_e4m3_integer_inputs_exact_with_power_of_two_scales():
+    a_f = synth.ints(10, (40, 64), -4, 4)
+    w_f = synth.ints(11, (2, 64, 32), -4, 4)
+    a_q = synth.to_e4m3(a_f, 1.0)
+    w_q = synth.to_e4m3(w_f, 1.0)
+    out = oracle.gmm(a_q, w_q, _offsets([25, 15]), a_scale=0.5, w_scale=4.0)
+    ref = np.concatenate([a_f[:25].astype(np.float64) @ w_f[0], a_f[25:].astype(np.float64) @ w_f[1]])
+    assert np.array_equal(out, ref * 2.0)
+
+
+def test_gmm_row_subset_equals_full():
+    a = synth.normal(12, (50, 16), dtype="bf16")
+    w = synth.normal(13, (3, 16, 8), dtype="bf16")
+    off = _offsets([20, 10, 20])
+    full = oracle.gmm(a, w, off, nthreads=4)
+    rows = np.array([49, 0, 19, 20, 29, 30], np.int32)
+    sub = oracle.gmm(a, w, off, rows=rows)
+    assert np.array_equal(sub, full[rows])
+
+
+# ---------------------------------------------------------------- combine
+
+def test_combine_constant_expert_rows_is_dense_gate_matmul():
+    """SpMM page: with each expert a constant row B_e, y = G @ B (G the gates in (T,E))."""
+    d = _tiny()
+    T, E, K, N = d["T"], d["E"], d["K"], 40
+    idx, gate, _, _ = oracle.route(d["x"], d["wr"], T, d["H"], E, K)
+    counts, offsets, psrc, pdst = oracle.permute(idx, E)
+    B = synth.normal(14, (E, N)).astype(np.float64)
+    expert_of_row = np.repeat(np.arange(E), counts)
+    yp = B[expert_of_row]
+    y = oracle.combine(yp, pdst, gate, T, K)
+    G = np.zeros((T, E))
+    G[np.repeat(np.arange(T), K), idx.ravel()] = gate.ravel()
+    np.testing.assert_allclose(y, G @ B, rtol=1e-14, atol=1e-14)
+
+
+def test_combine_one_hot_gates_is_gather_and_unpermute_is_inverse():
+    d = _tiny()
+    T, E, K = d["T"], d["E"], d["K"]
+    idx, _, _, _ = oracle.route(d["x"], d["wr"], T, d["H"], E, K)
+    _, _, psrc, pdst = oracle.permute(idx, E)
+    yp = synth.normal(15, (T * K, 12)).astype(np.float64)
+    onehot = np.zeros((T, K))
+    onehot[:, 1] = 1.0
+    y = oracle.combine(yp, pdst, onehot, T, K)
+    assert np.array_equal(y, yp[pdst.reshape(T, K)[:, 1]])
+    un = oracle.combine(yp, pdst, None, T, K)
+    assert np.array_equal(un, yp[pdst])
+    # unpermute after the gather of the permuted rows gives back token-major rows
+    assert np.array_equal(un[psrc], yp)
+
+
+# ---------------------------------------------------------------- experts and layer
+
+def test_expert_ffn_matches_numpy():
+    d = _tiny()
+    xv = d["x"][3].astype(np.float64)
+    out = oracle.expert_ffn(xv, d["w1"], d["w2"], 5)
+    ref = np.maximum(xv @ d["w1"][5].astype(np.float64), 0) @ d["w2"][5].astype(np.float64)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_layer_sparse_equals_dense_masked_sum(integer):
+    d = _tiny(integer)
+    res = oracle.layer(d["x"], d["wr"], d["w1"], d["w2"], d["K"], nthreads=2)
+    dense = oracle.layer_dense(d["x"], d["wr"], d["w1"], d["w2"], d["K"])
+    scale = max(1.0, np.abs(dense).max())
+    assert np.abs(res["y"] - dense).max() <= 1e-12 * scale
+    toks = np.arange(d["T"], dtype=np.int32)
+    pt = oracle.layer_tokens(d["x"], d["wr"], d["w1"], d["w2"], d["K"], toks)
+    assert np.abs(pt["y"] - dense).max() <= 1e-12 * scale
+    assert np.array_equal(pt["idx"], res["idx"])
+
+
+def test_layer_identity_experts_return_x():
+    d = _tiny()
+    w1, w2 = configs.identity_ffn(d["H"], d["E"])
+    res = oracle.layer(d["x"], d["wr"], w1, w2, d["K"])
+    np.testing.assert_allclose(res["y"], d["x"].astype(np.float64), rtol=0, atol=4e-16 * 8)
+
+
+def test_layer_integer_variant_hidden_values_are_integers():
+    d = _tiny(True)
+    res = oracle.layer(d["x"], d["wr"], d["w1"], d["w2"], d["K"])
+    counts, offsets, psrc, pdst = oracle.permute(res["idx"], d["E"])
+    xp = oracle.gather_rows(d["x"], psrc, d["K"])
+    hm = oracle.gmm(xp, d["w1"], offsets, act=oracle.ACT_RELU)
+    yp = oracle.gmm(hm, d["w2"], offsets)
+    assert np.all(hm == np.round(hm)) and np.abs(yp).max() < 2 ** 24
+    np.testing.assert_allclose(oracle.combine(yp, pdst, res["gate"], d["T"], d["K"]), res["y"],
+                               rtol=0, atol=0)
+
+
+def test_layer_skew_bias_forced_empty_experts():
+    d = _tiny(bias=True)
+    b = np.zeros(d["E"], np.float32)
+    b[6:] = -1e4
+    res = oracle.layer(d["x"], d["wr"], d["w1"], d["w2"], d["K"], bias=b)
+    assert res["counts"][6] == 0 and res["counts"][7] == 0
+    assert res["counts"].sum() == d["T"] * d["K"]
