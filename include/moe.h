@@ -1,0 +1,188 @@
+/*
+ * moe.h — C ABI of the single-GPU mixture-of-experts layer for MI355X (gfx950).
+ *
+ * The layer computes, per token x,  y = sum_{k<K} g_k(x) * E_{i_k}(x)
+ * (the MoE combination of "稀疏矩阵乘法（SpMM）在大模型中的复兴：利用NVIDIA
+ * Sparse Tensor Core加速MoE推理", section "MoE 模型与专家选择的挑战"), where
+ * i_k are the K highest-scoring experts of a router and g the softmax over
+ * those K scores only ("Advanced GPU Optimization: How to tech an LLM with
+ * CUDA and ROCm? - Part 5", section 1.1 "The Router Kernel (Top-k Gating)").
+ * It is split into the steps of that page's section 1.2 and of the routed-
+ * expert formula of "aclnnQuantGroupedMatMulAlltoAllv" (section 计算公式):
+ * route -> permute (dispatch) -> grouped GEMM -> combine / Unpermute.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" are HIP device pointers; the caller owns every
+ *     buffer. Tensors are dense, row-major, and each device pointer must be
+ *     16-byte aligned (else MOE_ERR_MISALIGNED).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *     work is enqueued on it; no call synchronises the host, allocates or
+ *     frees memory. Outputs are valid once the stream reaches that point.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     a call that returns an error has enqueued nothing and written nothing.
+ *     MOE_ERR_DEVICE reports a failed launch (the state of the outputs is then
+ *     undefined).
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (the op is deterministic by default, as "aclnnQuantGroupedMatMulAlltoAllv"
+ *     states in its constraints). No floating-point atomics are used.
+ *   - Ranges follow the shape constraints of "aclnnQuantGroupedMatMulAlltoAllv":
+ *     H, F, N in (0, 65536); K in [1, 8] (the page gives [2, 8]; K = 1 is
+ *     accepted as the g = 1 special case) and K <= E; E <= 256 (its bound on
+ *     experts times ranks); T*K < 52428800 (its bound on received rows). The
+ *     page's 32-experts-per-card limit is not applied: one GPU here holds
+ *     every expert.
+ *   - Non-finite inputs give unspecified results.
+ *
+ * Element types: MOE_F32 = IEEE binary32, MOE_BF16 = bfloat16, MOE_FP8_E4M3 =
+ * OCP 8-bit E4M3 ("fn": no infinities, max 448). Activations are rounded to
+ * the output type once, round to nearest even.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  MOE_ERR_BAD_SHAPE = 2,           /* a size is out of range or inconsistent */
+  MOE_ERR_BAD_DTYPE = 3,           /* an element-type code is unknown or not allowed here */
+  MOE_ERR_UNSUPPORTED = 4,         /* a valid mode this build does not implement */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes below the *_workspace_size answer */
+  MOE_ERR_MISALIGNED = 6,          /* a device pointer is not 16-byte aligned */
+  MOE_ERR_DEVICE = 7               /* the HIP runtime reported an error */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Quantisation modes, numbered as in "aclnnQuantGroupedMatMulAlltoAllv"
+ * (parameter list): 0 none, 1 per-tensor, 2 per-channel, 3 per-token,
+ * 4 per-group, 5 per-block, 6 mx, 7 dynamic per-token. Modes 2..7 return
+ * MOE_ERR_UNSUPPORTED. */
+typedef enum {
+  MOE_QUANT_NONE = 0,
+  MOE_QUANT_PER_TENSOR = 1,
+  MOE_QUANT_PER_CHANNEL = 2,
+  MOE_QUANT_PER_TOKEN = 3,
+  MOE_QUANT_PER_GROUP = 4,
+  MOE_QUANT_PER_BLOCK = 5,
+  MOE_QUANT_MX = 6,
+  MOE_QUANT_PER_TOKEN_DYNAMIC = 7
+} moe_quant_mode;
+
+typedef enum { MOE_ACT_NONE = 0, MOE_ACT_RELU = 1 } moe_act;
+
+/* Message for a status code (static storage, never NULL). */
+const char* moe_status_string(moe_status s);
+/* MOE_VERSION of the built library. */
+int moe_version(void);
+
+/*
+ * moe_route — router scores, top-k selection, softmax over the k kept scores
+ * ("Part 5", section 1.1; the (N,K) top-K index matrix of the SpMM page,
+ * section "专家选择的计算过程").
+ *   x        device (T,H) in dt            token rows
+ *   w_router device (H,E) in dt            router weights, E contiguous
+ *   dt       MOE_F32 or MOE_BF16
+ *   bias     device (E) fp32 or NULL       added to every score before
+ *                                          selection and softmax
+ *   topk_idx device (T,K) int32 out        experts by descending score; equal
+ *                                          scores -> lower expert index first
+ *   topk_gate device (T,K) fp32 out        g_k = exp(l_k - l_0) / sum_j exp(l_j - l_0)
+ * Scores are accumulated in fp32. T = 0 is a no-op.
+ */
+moe_status moe_route(const void* x, const void* w_router, moe_dtype dt, const float* bias, int T,
+                     int H, int E, int K, int32_t* topk_idx, float* topk_gate, void* stream);
+
+/*
+ * moe_permute — dispatch: per-expert counts, their exclusive scan, and a
+ * stable placement of the T*K (token, slot) pairs into per-expert contiguous
+ * row blocks ("Part 5", section 1.2, token dispatch; the per-expert count
+ * arrays of "aclnnQuantGroupedMatMulAlltoAllv"). With one GPU the dispatch
+ * buffer is the permuted activation buffer. offsets + perm_src are the CSC
+ * form of the (T,E) activation mask of the SpMM page (section "SpMM"/CSC).
+ *   topk_idx device (T,K) int32            values must be in [0,E) (out-of-range
+ *                                          values give unspecified placement but
+ *                                          no out-of-bounds access)
+ *   x        device (T,H) in dt or NULL    NULL: index work only
+ *   counts   device (E) int32 out
+ *   offsets  device (E+1) int32 out        offsets[0] = 0, offsets[E] = T*K
+ *   perm_src device (T*K) int32 out        row -> t*K + k
+ *   perm_dst device (T*K) int32 out        t*K + k -> row
+ *   x_perm   device (T*K,H) in dt out      x_perm[perm_dst[t*K+k]] = x[t]; NULL iff x is
+ *   ws, ws_bytes device scratch of at least moe_permute_workspace_size() bytes
+ * Rows of one expert appear in ascending (t, k) order (stable, deterministic).
+ */
+moe_status moe_permute_workspace_size(int T, int E, int K, size_t* bytes);
+moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int T, int H, int E,
+                       int K, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                       int32_t* perm_dst, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_gmm — grouped GEMM over e experts whose rows are contiguous blocks:
+ *   out[r, n] = act( (sum_h a[r,h] * w[ex,h,n]) * a_scale * w_scale )
+ * for offsets[ex] <= r < offsets[ex+1]  (gmmY = (gmmX @ gmmWeight) * gmmXScale
+ * * gmmWeightScale, "aclnnQuantGroupedMatMulAlltoAllv", section 计算公式; the
+ * expert FFN of "Part 5", section 1.2, local expert execution; the shared-
+ * expert MatMul of the same formula section is the case e = 1).
+ *   a        device (A,Hin) in a_dt        rows grouped by expert
+ *   w        device (e,Hin,N) in w_dt      N contiguous (shape of gmmWeight)
+ *   a_q/w_q  MOE_QUANT_NONE (scale must be NULL) or MOE_QUANT_PER_TENSOR
+ *            (scale = device pointer to one fp32); other modes: UNSUPPORTED
+ *   offsets  device (e+1) int32, non-decreasing, offsets[0] = 0 and
+ *            offsets[e] = A (not checked on the host: the values live on the
+ *            device; offsets outside [0, A] are clamped to it)
+ *   act      MOE_ACT_NONE or MOE_ACT_RELU
+ *   out      device (A,N) in out_dt
+ * Supported types (a_dt, w_dt -> out_dt): F32,F32->F32; BF16,BF16->BF16;
+ * FP8,FP8->BF16 (FP8 requires MOE_QUANT_PER_TENSOR on both sides).
+ * Accumulation is fp32; the scales multiply the fp32 sum; one rounding to
+ * out_dt. Experts with no rows cost nothing and write nothing.
+ */
+moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
+                   const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
+                   const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                   moe_dtype out_dt, void* stream);
+
+/*
+ * moe_combine — back to token order.
+ *   topk_gate != NULL: y[t,n] = sum_{k=0..K-1} gate[t,k] * y_perm[perm_dst[t*K+k], n],
+ *     fp32 sum in ascending k, one rounding (y = sum g_i E_i(x), SpMM page);
+ *     out is (T,N).
+ *   topk_gate == NULL: Unpermute, out[t*K+k, n] = y_perm[perm_dst[t*K+k], n]
+ *     (unpermuteOut = Unpermute(gmmY), "aclnnQuantGroupedMatMulAlltoAllv",
+ *     section 计算公式); out is (T*K,N), a bit copy (in_dt must equal out_dt).
+ *   y_perm   device (T*K,N) in in_dt; perm_dst device (T*K) int32 in [0,T*K)
+ *   topk_gate device (T,K) fp32 or NULL
+ * Types: F32->F32, BF16->BF16.
+ */
+moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_dst,
+                       const float* topk_gate, int T, int K, int N, void* out, moe_dtype out_dt,
+                       void* stream);
+
+/*
+ * moe_layer — the whole layer on one stream: route, permute, GEMM 1 with the
+ * activation (hidden kept in dt), GEMM 2, weighted combine.
+ *   x (T,H), w_router (H,E), bias (E) fp32 or NULL, w1 (E,H,F), w2 (E,F,H),
+ *   y (T,H) out; all device, all in dt (MOE_F32 or MOE_BF16) except bias.
+ *   topk_idx_out (T,K) int32, topk_gate_out (T,K) fp32, counts_out (E) int32:
+ *   optional device outputs (NULL = not wanted).
+ *   ws, ws_bytes: device scratch of at least moe_layer_workspace_size() bytes.
+ */
+moe_status moe_layer_workspace_size(int T, int H, int E, int K, int F, moe_dtype dt, size_t* bytes);
+moe_status moe_layer(const void* x, const void* w_router, const float* bias, const void* w1,
+                     const void* w2, moe_dtype dt, int T, int H, int E, int K, int F, moe_act act,
+                     void* y, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

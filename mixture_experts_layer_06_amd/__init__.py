@@ -1,0 +1,209 @@
+"""Python binding of the gfx950 MoE C-ABI library (libmoe.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind include/moe.h. torch supplies device memory (tensors) and the stream
+(torch.cuda.current_stream()). There is no CPU fallback: if libmoe.so is
+missing the import of any entry point raises.
+
+Tensor element types: torch.float32 -> MOE_F32, torch.bfloat16 -> MOE_BF16,
+torch.uint8 or torch.float8_e4m3fn -> MOE_FP8_E4M3 (OCP E4M3 bytes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime libmoe.so binds to)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+# moe.h enums
+OK, ERR_NULL_POINTER, ERR_BAD_SHAPE, ERR_BAD_DTYPE, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_DEVICE = 5, 6, 7
+F32, BF16, FP8_E4M3 = 0, 1, 2
+QUANT_NONE, QUANT_PER_TENSOR = 0, 1
+ACT_NONE, ACT_RELU = 0, 1
+
+EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_permute_workspace_size",
+           "moe_permute", "moe_gmm", "moe_combine", "moe_layer_workspace_size", "moe_layer")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by build()); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmoe.so not built at {LIB_PATH}; run __graft_entry__.build() "
+                              "or python -m mixture_experts_layer_06_amd._build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.moe_status_string.argtypes = [i32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_version.argtypes = []
+        L.moe_version.restype = i32
+        L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_permute_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.moe_permute.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_gmm.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, vp,
+                              i32, vp]
+        L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
+        L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                vp, vp, sz, vp]
+        for n in EXPORTS[2:]:
+            getattr(L, n).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise MoeError(status, where)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------- entry points
+
+def route(x, w_router, K, bias=None, topk_idx=None, topk_gate=None, stream=None):
+    """moe_route. Returns (topk_idx int32 (T,K), topk_gate fp32 (T,K))."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    if topk_idx is None:
+        topk_idx = _empty((T, K), torch.int32, x)
+    if topk_gate is None:
+        topk_gate = _empty((T, K), torch.float32, x)
+    st = lib().moe_route(_ptr(x), _ptr(w_router), dtype_code(x), _ptr(bias), T, H, E, K,
+                         _ptr(topk_idx), _ptr(topk_gate), _stream(stream))
+    _check(st, "moe_route")
+    return topk_idx, topk_gate
+
+
+def permute_workspace_size(T, E, K) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_permute_workspace_size(T, E, K, ctypes.byref(n)), "moe_permute_workspace_size")
+    return n.value
+
+
+def permute(topk_idx, E, x=None, ws=None, stream=None, out=None):
+    """moe_permute. Returns dict counts, offsets, perm_src, perm_dst, x_perm (or None)."""
+    T, K = topk_idx.shape
+    A = T * K
+    dev = topk_idx
+    o = dict(out or {})
+    counts = o.get("counts", _empty((E,), torch.int32, dev))
+    offsets = o.get("offsets", _empty((E + 1,), torch.int32, dev))
+    psrc = o.get("perm_src", _empty((A,), torch.int32, dev))
+    pdst = o.get("perm_dst", _empty((A,), torch.int32, dev))
+    xp = None
+    H, dt = 1, F32
+    if x is not None:
+        H = x.shape[1]
+        dt = dtype_code(x)
+        xp = o.get("x_perm", _empty((A, H), x.dtype, dev))
+    need = permute_workspace_size(T, E, K)
+    if ws is None and need:
+        ws = _empty((need,), torch.uint8, dev)
+    st = lib().moe_permute(_ptr(topk_idx), _ptr(x), dt, T, H, E, K, _ptr(counts), _ptr(offsets),
+                           _ptr(psrc), _ptr(pdst), _ptr(xp), _ptr(ws) if need else None,
+                           ws.numel() if (ws is not None and need) else 0, _stream(stream))
+    _check(st, "moe_permute")
+    return {"counts": counts, "offsets": offsets, "perm_src": psrc, "perm_dst": pdst, "x_perm": xp}
+
+
+def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, stream=None):
+    """moe_gmm over w (e,Hin,N). Scales (1-element fp32 device tensors) select
+    MOE_QUANT_PER_TENSOR. Output: fp32 for fp32 inputs, else bf16."""
+    A, Hin = a.shape
+    e, Hw, N = w.shape
+    if Hw != Hin:
+        raise ValueError("a and w disagree on Hin")
+    adt, wdt = dtype_code(a), dtype_code(w)
+    odt = F32 if adt == F32 else BF16
+    if out is None:
+        out = _empty((A, N), torch.float32 if odt == F32 else torch.bfloat16, a)
+    aq = QUANT_PER_TENSOR if a_scale is not None else QUANT_NONE
+    wq = QUANT_PER_TENSOR if w_scale is not None else QUANT_NONE
+    st = lib().moe_gmm(_ptr(a), adt, aq, _ptr(a_scale), _ptr(w), wdt, wq, _ptr(w_scale),
+                       _ptr(offsets), e, A, Hin, N, act, _ptr(out), odt, _stream(stream))
+    _check(st, "moe_gmm")
+    return out
+
+
+def combine(y_perm, perm_dst, topk_gate, T, K, out=None, stream=None):
+    """moe_combine: weighted sum (gate given) -> (T,N); Unpermute (gate None) -> (T*K,N)."""
+    N = y_perm.shape[1]
+    dt = dtype_code(y_perm)
+    if out is None:
+        shape = (T, N) if topk_gate is not None else (T * K, N)
+        out = _empty(shape, y_perm.dtype, y_perm)
+    st = lib().moe_combine(_ptr(y_perm), dt, _ptr(perm_dst), _ptr(topk_gate), T, K, N, _ptr(out),
+                           dt, _stream(stream))
+    _check(st, "moe_combine")
+    return out
+
+
+def layer_workspace_size(T, H, E, K, F, dtype_code_) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_layer_workspace_size(T, H, E, K, F, dtype_code_, ctypes.byref(n)),
+           "moe_layer_workspace_size")
+    return n.value
+
+
+def layer(x, w_router, w1, w2, K, bias=None, act=ACT_RELU, y=None, ws=None, topk_idx=None,
+          topk_gate=None, counts=None, stream=None):
+    """moe_layer: route -> permute -> GEMM1(act) -> GEMM2 -> weighted combine. Returns y."""
+    T, H = x.shape
+    E, _, F = w1.shape
+    dt = dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    need = layer_workspace_size(T, H, E, K, F, dt)
+    if ws is None:
+        ws = _empty((max(need, 1),), torch.uint8, x)
+    st = lib().moe_layer(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1), _ptr(w2), dt, T, H, E, K, F,
+                         act, _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
+                         ws.numel(), _stream(stream))
+    _check(st, "moe_layer")
+    return y

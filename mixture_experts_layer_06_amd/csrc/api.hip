@@ -1,0 +1,246 @@
+// api.hip — the extern "C" entry points declared in include/moe.h.
+//
+// Every call validates all of its arguments on the host first and enqueues
+// nothing when one is wrong (the two-stage "check, then execute" contract of
+// "aclnnQuantGroupedMatMulAlltoAllv": the first stage checks parameters and
+// sizes the workspace, the second runs on a stream). The shape limits are
+// that page's constraints, adapted to one GPU that holds every expert.
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxDim = 65536;        // H, F, N in (0, 65536)
+constexpr int kMaxExperts = 256;      // experts x ranks <= 256
+constexpr int kMaxK = 8;              // K in [2, 8] (K = 1 also accepted)
+constexpr int64_t kMaxRows = 52428800;  // received rows in (0, 52428800)
+
+bool dim_ok(int d) { return d > 0 && d < kMaxDim; }
+
+moe_status check_route_shape(int T, int H, int E, int K) {
+  if (T < 0 || !dim_ok(H)) return MOE_ERR_BAD_SHAPE;
+  if (E < 1 || E > kMaxExperts) return MOE_ERR_BAD_SHAPE;
+  if (K < 1 || K > kMaxK || K > E) return MOE_ERR_BAD_SHAPE;
+  if ((int64_t)T * K >= kMaxRows) return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
+
+bool layer_dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool any_dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_FP8_E4M3; }
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    moe_status _st = (expr);          \
+    if (_st != MOE_OK) return _st;    \
+  } while (0)
+
+#define REQUIRE_PTR(p) \
+  if (!(p)) return MOE_ERR_NULL_POINTER
+#define REQUIRE_ALIGNED(p) \
+  if ((p) && !aligned16(p)) return MOE_ERR_MISALIGNED
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct LayerWs {
+  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, xp, hm, total;
+};
+
+LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
+  const int64_t A = (int64_t)T * K;
+  const size_t es = (size_t)dtype_size(dt);
+  LayerWs L;
+  size_t o = 0;
+  L.idx = o; o += round256(A * 4);
+  L.gate = o; o += round256(A * 4);
+  L.counts = o; o += round256((size_t)E * 4);
+  L.offsets = o; o += round256((size_t)(E + 1) * 4);
+  L.psrc = o; o += round256(A * 4);
+  L.pdst = o; o += round256(A * 4);
+  L.perm_ws = o; o += round256(permute_ws_bytes(T, E, K));
+  L.xp = o; o += round256((size_t)A * H * es);  // permuted rows; reused for GEMM 2 output
+  L.hm = o; o += round256((size_t)A * F * es);  // hidden activations
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_BAD_DTYPE: return "element type not allowed for this argument";
+    case MOE_ERR_UNSUPPORTED: return "mode not implemented (quantisation mode or activation)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
+    case MOE_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case MOE_ERR_DEVICE: return "HIP runtime error while enqueuing work";
+  }
+  return "unknown status";
+}
+
+int moe_version(void) { return MOE_VERSION; }
+
+moe_status moe_route(const void* x, const void* w_router, moe_dtype dt, const float* bias, int T,
+                     int H, int E, int K, int32_t* topk_idx, float* topk_gate, void* stream) {
+  if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
+  MOE_TRY(check_route_shape(T, H, E, K));
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_gate);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(w_router);
+  REQUIRE_ALIGNED(bias);
+  REQUIRE_ALIGNED(topk_idx);
+  REQUIRE_ALIGNED(topk_gate);
+  return launch_route(x, w_router, dt, bias, T, H, E, K, topk_idx, topk_gate, (hipStream_t)stream);
+}
+
+moe_status moe_permute_workspace_size(int T, int E, int K, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  MOE_TRY(check_route_shape(T, 1, E, K));
+  *bytes = permute_ws_bytes(T, E, K);
+  return MOE_OK;
+}
+
+moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int T, int H, int E,
+                       int K, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                       int32_t* perm_dst, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (x && !any_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
+  MOE_TRY(check_route_shape(T, x ? H : 1, E, K));
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_NULL_POINTER;
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  if (T > 0) {
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(perm_src);
+    REQUIRE_PTR(perm_dst);
+  }
+  const size_t need = permute_ws_bytes(T, E, K);
+  if (need > 0) {
+    REQUIRE_PTR(ws);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  REQUIRE_ALIGNED(topk_idx);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(counts);
+  REQUIRE_ALIGNED(offsets);
+  REQUIRE_ALIGNED(perm_src);
+  REQUIRE_ALIGNED(perm_dst);
+  REQUIRE_ALIGNED(x_perm);
+  if (need > 0) REQUIRE_ALIGNED(ws);
+  return launch_permute(topk_idx, x, dt, T, H, E, K, counts, offsets, perm_src, perm_dst, x_perm, ws,
+                        (hipStream_t)stream);
+}
+
+moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
+                   const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
+                   const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                   moe_dtype out_dt, void* stream) {
+  if (!any_dtype_ok(a_dt) || !any_dtype_ok(w_dt) || !any_dtype_ok(out_dt)) return MOE_ERR_BAD_DTYPE;
+  const bool pair_ok = (a_dt == MOE_F32 && w_dt == MOE_F32 && out_dt == MOE_F32) ||
+                       (a_dt == MOE_BF16 && w_dt == MOE_BF16 && out_dt == MOE_BF16) ||
+                       (a_dt == MOE_FP8_E4M3 && w_dt == MOE_FP8_E4M3 && out_dt == MOE_BF16);
+  if (!pair_ok) return MOE_ERR_BAD_DTYPE;
+  if ((int)a_q < 0 || (int)a_q > 7 || (int)w_q < 0 || (int)w_q > 7) return MOE_ERR_UNSUPPORTED;
+  if (a_q > MOE_QUANT_PER_TENSOR || w_q > MOE_QUANT_PER_TENSOR) return MOE_ERR_UNSUPPORTED;
+  if (a_dt == MOE_FP8_E4M3 && (a_q != MOE_QUANT_PER_TENSOR || w_q != MOE_QUANT_PER_TENSOR))
+    return MOE_ERR_UNSUPPORTED;
+  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
+  if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
+  if (a_q == MOE_QUANT_PER_TENSOR) REQUIRE_PTR(a_scale);
+  if (w_q == MOE_QUANT_PER_TENSOR) REQUIRE_PTR(w_scale);
+  if (A == 0) return MOE_OK;
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(out);
+  REQUIRE_ALIGNED(a);
+  REQUIRE_ALIGNED(w);
+  REQUIRE_ALIGNED(offsets);
+  REQUIRE_ALIGNED(out);
+  // scales are 4-byte device scalars: natural alignment suffices
+  const float* as = a_q == MOE_QUANT_PER_TENSOR ? a_scale : nullptr;
+  const float* wsc = w_q == MOE_QUANT_PER_TENSOR ? w_scale : nullptr;
+  return launch_gmm(a, a_dt, as, w, wsc, offsets, e, A, Hin, N, act, out, out_dt, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_dst,
+                       const float* topk_gate, int T, int K, int N, void* out, moe_dtype out_dt,
+                       void* stream) {
+  if (!layer_dtype_ok(in_dt) || out_dt != in_dt) return MOE_ERR_BAD_DTYPE;
+  if (T < 0 || K < 1 || K > kMaxK || !dim_ok(N) || (int64_t)T * K >= kMaxRows) return MOE_ERR_BAD_SHAPE;
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(y_perm);
+  REQUIRE_PTR(perm_dst);
+  REQUIRE_PTR(out);
+  REQUIRE_ALIGNED(y_perm);
+  REQUIRE_ALIGNED(perm_dst);
+  REQUIRE_ALIGNED(topk_gate);
+  REQUIRE_ALIGNED(out);
+  return launch_combine(y_perm, in_dt, perm_dst, topk_gate, T, K, N, out, (hipStream_t)stream);
+}
+
+moe_status moe_layer_workspace_size(int T, int H, int E, int K, int F, moe_dtype dt, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
+  MOE_TRY(check_route_shape(T, H, E, K));
+  if (!dim_ok(F)) return MOE_ERR_BAD_SHAPE;
+  *bytes = layer_ws_layout(T, H, E, K, F, dt).total;
+  return MOE_OK;
+}
+
+moe_status moe_layer(const void* x, const void* w_router, const float* bias, const void* w1,
+                     const void* w2, moe_dtype dt, int T, int H, int E, int K, int F, moe_act act,
+                     void* y, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
+  MOE_TRY(check_route_shape(T, H, E, K));
+  if (!dim_ok(F)) return MOE_ERR_BAD_SHAPE;
+  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(ws);
+  const LayerWs L = layer_ws_layout(T, H, E, K, F, dt);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(w_router);
+  REQUIRE_ALIGNED(bias);
+  REQUIRE_ALIGNED(w1);
+  REQUIRE_ALIGNED(w2);
+  REQUIRE_ALIGNED(y);
+  REQUIRE_ALIGNED(topk_idx_out);
+  REQUIRE_ALIGNED(topk_gate_out);
+  REQUIRE_ALIGNED(counts_out);
+  REQUIRE_ALIGNED(ws);
+
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char* base = (unsigned char*)ws;
+  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(base + L.idx);
+  float* gate = topk_gate_out ? topk_gate_out : (float*)(base + L.gate);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* psrc = (int32_t*)(base + L.psrc);
+  int32_t* pdst = (int32_t*)(base + L.pdst);
+  void* xp = base + L.xp;
+  void* hm = base + L.hm;
+  const int A = T * K;
+  MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, s));
+  MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
+  MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, s));
+  MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, s));
+  MOE_TRY(launch_combine(xp, dt, pdst, gate, T, K, H, y, s));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// common.h — internal helpers of the gfx950 MoE library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+typedef uint8_t fp8_t;    // OCP E4M3 byte
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// binary32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// v_perm_b32: result byte i = byte sel[i] of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int dtype_size(moe_dtype dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline moe_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+// Launchers implemented by the kernel files. They assume validated arguments.
+moe_status launch_route(const void* x, const void* wr, moe_dtype dt, const float* bias, int T, int H,
+                        int E, int K, int32_t* idx, float* gate, hipStream_t s);
+size_t permute_ws_bytes(int T, int E, int K);
+moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T, int H, int E, int K,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
+                          void* x_perm, void* ws, hipStream_t s);
+moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
+                      const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
+                      moe_act act, void* out, moe_dtype out_dt, hipStream_t s);
+moe_status launch_combine(const void* y_perm, moe_dtype dt, const int32_t* perm_dst,
+                          const float* gate, int T, int K, int N, void* out, hipStream_t s);
+
+}  // namespace moe

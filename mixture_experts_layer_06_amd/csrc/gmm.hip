@@ -1,0 +1,655 @@
+// gmm.hip — grouped GEMM over experts whose rows are contiguous blocks:
+//   out[r, n] = act( (sum_h a[r,h] * w[ex,h,n]) * a_scale * w_scale ),
+//   offsets[ex] <= r < offsets[ex+1]
+// (gmmY = (gmmX @ gmmWeight) * gmmXScale * gmmWeightScale,
+// "aclnnQuantGroupedMatMulAlltoAllv", section 计算公式; local expert
+// execution, "Advanced GPU Optimization ... Part 5", section 1.2).
+//
+// Weights arrive as (e, Hin, N) with N contiguous, the shape the page gives
+// for gmmWeight. MFMA wants both operands contiguous in the reduction
+// dimension, so every kernel transposes weight data in registers with
+// v_perm_b32 on its way in.
+//
+// Kernels
+//  * gmm_tiled_kernel (bf16 / E4M3, many rows per expert): 256x256 output
+//    tiles, 8 waves (2 x 4, each 128 x 64), 128-byte K slices double-
+//    buffered in LDS (pitch 144 B so MFMA fragment reads are conflict
+//    free). The weight slice is transposed while being written to LDS.
+//    MFMA: v_mfma_f32_16x16x32_bf16 or v_mfma_f32_16x16x128_f8f6f4 with the
+//    weight fragment as the 16-row operand and the activation fragment as
+//    the 16-column operand, so each lane ends up with 4 consecutive output
+//    columns of one row (8-byte stores).
+//    Tiles: per expert ceil(rows/256) x ceil(N/256); the block index is
+//    remapped so each of the 8 XCDs gets a contiguous run of tiles, ordered
+//    in groups of 8 row-tiles so concurrently running tiles share weight and
+//    activation panels in that XCD's L2. The grid is an upper bound sized on
+//    the host; the real tile count is computed on the device from offsets,
+//    and surplus blocks exit at once.
+//  * gmm_stream_kernel (bf16, few rows per expert: decode shapes): one wave
+//    per (expert, 64 output columns), no LDS. Lane l loads rows
+//    k0+8*(l/16)..+7 of columns n0+4*(l%16)..+3 (8-byte loads), transposes
+//    them into 4 fragments and issues 4 MFMAs whose row i means column
+//    n0 + 4i + j; every weight byte is read from HBM exactly once and the
+//    lane's outputs come out as 16 consecutive columns.
+//  * gmm_f32_kernel: fp32 FMA tiles (64 x 64, 4 x 4 per thread), sequential
+//    fp32 accumulation over h.
+#include <type_traits>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Expert offsets (clamped to [0, A]) and the running count of row tiles per
+// expert, in LDS: s_off[0..e], s_pre[0..e] (s_pre[q] = tiles before expert q).
+template <int BM>
+__device__ __forceinline__ void load_tile_prefix(const int32_t* __restrict__ offsets, int e, int A,
+                                                 int* s_off, int* s_pre) {
+  for (int q = threadIdx.x; q <= e; q += blockDim.x) {
+    int v = offsets[q];
+    s_off[q] = v < 0 ? 0 : (v > A ? A : v);
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    // each lane covers 4 consecutive experts (e <= 256)
+    int c[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = lane * 4 + i;
+      int rows = q < e ? s_off[q + 1] - s_off[q] : 0;
+      rows = rows < 0 ? 0 : rows;
+      c[i] = (rows + BM - 1) / BM;
+      local += c[i];
+    }
+    const int incl = wave_incl_scan(local);
+    int run = incl - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = lane * 4 + i;
+      if (q < e) s_pre[q] = run;
+      run += c[i];
+    }
+    if (lane == kWave - 1) s_pre[e] = incl;  // total row tiles
+  }
+  __syncthreads();
+}
+
+struct Tile {
+  int ex, row0, rows, n0;
+};
+
+// Logical tile for this block, or false if the block has no work.
+// XCD-aware: block p runs on XCD p % 8; XCD x takes logical tiles
+// [x*per, (x+1)*per). Inside an expert, tiles go in groups of GM row tiles:
+// group-major, then column tile, then row tile.
+template <int BM, int BN, int GM>
+__device__ __forceinline__ bool pick_tile(const int* s_off, const int* s_pre, int e, int N, Tile& t) {
+  const int ntn = (N + BN - 1) / BN;
+  const int total = s_pre[e] * ntn;
+  if (total == 0) return false;
+  const int p = blockIdx.x;
+  const int per = (total + 7) / 8;
+  const int slot = p >> 3;
+  if (slot >= per) return false;
+  const int L = (p & 7) * per + slot;
+  if (L >= total) return false;
+  const int g = L / ntn;  // global row-tile-major position among s_pre[e] row tiles
+  // find expert ex with s_pre[ex] <= g < s_pre[ex+1] (binary search, s_pre non-decreasing)
+  int lo = 0, hi = e - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= g) lo = mid;
+    else hi = mid - 1;
+  }
+  const int ex = lo;
+  const int mt = s_pre[ex + 1] - s_pre[ex];
+  const int q = L - s_pre[ex] * ntn;  // local index within the expert
+  const int grp = q / (GM * ntn);
+  const int within = q - grp * GM * ntn;
+  const int gsz = min(GM, mt - grp * GM);
+  const int nt = within / gsz;
+  const int m = grp * GM + within % gsz;
+  t.ex = ex;
+  t.row0 = s_off[ex] + m * BM;
+  t.rows = min(BM, s_off[ex + 1] - t.row0);
+  t.n0 = nt * BN;
+  return true;
+}
+
+// 16 bytes at p; bytes at or beyond `avail` read as zero. AL: p is 16-byte
+// aligned and avail is a multiple of 16 (or <= 0).
+template <bool AL, int ELEM>
+__device__ __forceinline__ uint4 ld16(const unsigned char* p, int avail) {
+  if (AL) return avail >= 16 ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0;
+    if (ELEM == 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = d * 4 + h * 2;
+        if (b < avail) v |= (uint32_t)(*reinterpret_cast<const uint16_t*>(p + b)) << (16 * h);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int b = d * 4 + h;
+        if (b < avail) v |= (uint32_t)p[b] << (8 * h);
+      }
+    }
+    w[d] = v;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <bool AL, int ELEM>
+__device__ __forceinline__ uint2 ld8(const unsigned char* p, int avail) {
+  if (AL) return avail >= 8 ? *reinterpret_cast<const uint2*>(p) : make_uint2(0, 0);
+  uint32_t w[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t v = 0;
+    if (ELEM == 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = d * 4 + h * 2;
+        if (b < avail) v |= (uint32_t)(*reinterpret_cast<const uint16_t*>(p + b)) << (16 * h);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int b = d * 4 + h;
+        if (b < avail) v |= (uint32_t)p[b] << (8 * h);
+      }
+    }
+    w[d] = v;
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// bf16: rows r0..r7 of 4 columns (uint2 each) -> 4 columns of 8 rows (uint4 each).
+__device__ __forceinline__ void transpose_8x4_bf16(const uint2 in[8], uint4 out[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = (c >> 1) ? in[2 * p].y : in[2 * p].x;
+      const uint32_t b = (c >> 1) ? in[2 * p + 1].y : in[2 * p + 1].x;
+      d[p] = perm_b32(b, a, sel);
+    }
+    out[c] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// E4M3: rows r0..r7 of 8 columns (uint2 each, one byte per column) ->
+// 8 columns of 8 rows (uint2 each, one byte per row).
+__device__ __forceinline__ void transpose_8x8_u8(const uint2 in[8], uint2 out[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; c += 2) {
+    // byte c and c+1 of each row; rows paired (0,1),(2,3),(4,5),(6,7)
+    const int d = c >> 2;        // which dword of the row
+    const int b = c & 3;         // byte within it (0 or 2)
+    // pair[p] = {r2p[c], r2p+1[c], r2p[c+1], r2p+1[c+1]}
+    const uint32_t sel_pair = (uint32_t)(b) | ((uint32_t)(4 + b) << 8) | ((uint32_t)(b + 1) << 16) |
+                              ((uint32_t)(5 + b) << 24);
+    uint32_t pr[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = d ? in[2 * p].y : in[2 * p].x;
+      const uint32_t hi = d ? in[2 * p + 1].y : in[2 * p + 1].x;
+      pr[p] = perm_b32(hi, lo, sel_pair);
+    }
+    // column c: {r0,r1,r2,r3} = lo16(pr0) | lo16(pr1)<<16 ; {r4..r7} from pr2, pr3
+    out[c].x = perm_b32(pr[1], pr[0], 0x05040100u);
+    out[c].y = perm_b32(pr[3], pr[2], 0x05040100u);
+    out[c + 1].x = perm_b32(pr[1], pr[0], 0x07060302u);
+    out[c + 1].y = perm_b32(pr[3], pr[2], 0x07060302u);
+  }
+}
+
+__device__ __forceinline__ float ld_scale(const float* p) { return p ? *p : 1.0f; }
+
+// ------------------------------------------------------------------ tiled MFMA kernel
+
+constexpr int kKB = 128;    // K-slice bytes per tile step
+constexpr int kPitch = 144; // LDS row pitch (bytes)
+
+template <int ELEM, int BM, int BN, int WM_, int WN_, bool AL, bool OUT_F32>
+struct TiledCfg {
+  static constexpr int kElem = ELEM;
+  static constexpr int kBM = BM, kBN = BN;
+  static constexpr int kWavesM = WM_, kWavesN = WN_;
+  static constexpr int kNT = 64 * WM_ * WN_;
+  static constexpr int kWM = BM / WM_;  // rows per wave
+  static constexpr int kWN = BN / WN_;  // columns per wave
+  static constexpr int kFI = kWM / 16, kFJ = kWN / 16;
+  static constexpr int kKRows = kKB / ELEM;         // K rows of weights per step
+  static constexpr int kKBlk = kKRows / 8;          // 8-row blocks
+  static constexpr int kNQ = (BN * ELEM) / 8;       // 8-byte column groups per weight row
+  static constexpr int kUnits = kKBlk * kNQ;        // weight load units per step
+  static constexpr int kUPT = kUnits / kNT;         // units per thread
+  static constexpr int kAChunks = BM * (kKB / 16);  // 16-byte activation chunks per step
+  static constexpr int kAPT = kAChunks / kNT;
+  static constexpr bool kAligned = AL;
+  static constexpr bool kOutF32 = OUT_F32;
+  static constexpr int kLdsA = BM * kPitch, kLdsB = BN * kPitch;
+  static constexpr int kLds = 2 * (kLdsA + kLdsB);
+  static_assert(kUnits % kNT == 0 && kAChunks % kNT == 0, "load split");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
+    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
+    const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+    const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
+    unsigned char* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_off[257];
+  __shared__ int s_pre[257];
+  load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_pre);
+  Tile tile;
+  if (!pick_tile<C::kBM, C::kBN, 8>(s_off, s_pre, e, N, tile)) return;
+
+  constexpr int E_ = C::kElem;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
+  const int64_t hin_b = (int64_t)Hin * E_;
+  const int64_t n_b = (int64_t)N * E_;
+  const unsigned char* abase = a + (int64_t)tile.row0 * hin_b;
+  const unsigned char* wbase = w + (int64_t)tile.ex * Hin * n_b + (int64_t)tile.n0 * E_;
+  const int nsteps = (int)cdiv64(hin_b, kKB);
+
+  // buffer b: activations at smem + b*(A+B), weights right after them
+  auto As = [&](int b) { return smem + b * (C::kLdsA + C::kLdsB); };
+  auto Bs = [&](int b) { return smem + b * (C::kLdsA + C::kLdsB) + C::kLdsA; };
+
+  uint4 ra[C::kAPT];
+  uint2 rb[C::kUPT][8];
+
+  auto gload = [&](int step) {
+    const int kb0 = step * kKB;  // byte offset into an activation row
+#pragma unroll
+    for (int i = 0; i < C::kAPT; ++i) {
+      const int c = tid + i * C::kNT;
+      const int row = c >> 3, kc = c & 7;
+      const int avail = (row < tile.rows) ? (int)min<int64_t>(hin_b - (kb0 + kc * 16), 16) : 0;
+      ra[i] = ld16<C::kAligned, E_>(abase + (int64_t)row * hin_b + kb0 + kc * 16, avail);
+    }
+    const int k0 = step * C::kKRows;  // weight row
+#pragma unroll
+    for (int u = 0; u < C::kUPT; ++u) {
+      const int unit = tid + u * C::kNT;
+      const int kb = unit % C::kKBlk, nq = unit / C::kKBlk;
+      const int nb = nq * 8;  // byte offset in the weight row (from n0)
+      const int avail_n = (int)min<int64_t>(n_b - ((int64_t)tile.n0 * E_ + nb), 8);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int k = k0 + kb * 8 + r;
+        rb[u][r] = ld8<C::kAligned, E_>(wbase + (int64_t)k * n_b + nb, k < Hin ? avail_n : 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::kAPT; ++i) {
+      const int c = tid + i * C::kNT;
+      const int row = c >> 3, kc = c & 7;
+      *reinterpret_cast<uint4*>(As(buf) + row * kPitch + kc * 16) = ra[i];
+    }
+#pragma unroll
+    for (int u = 0; u < C::kUPT; ++u) {
+      const int unit = tid + u * C::kNT;
+      const int kb = unit % C::kKBlk, nq = unit / C::kKBlk;
+      if (E_ == 2) {
+        uint4 cols[4];
+        transpose_8x4_bf16(rb[u], cols);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint4*>(Bs(buf) + (nq * 4 + j) * kPitch + kb * 16) = cols[j];
+      } else {
+        uint2 cols[8];
+        transpose_8x8_u8(rb[u], cols);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint2*>(Bs(buf) + (nq * 8 + j) * kPitch + kb * 8) = cols[j];
+      }
+    }
+  };
+
+  f32x4_t acc[C::kFI][C::kFJ];
+#pragma unroll
+  for (int i = 0; i < C::kFI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kFJ; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  const bool wave_active = (wm * C::kWM < tile.rows) && (tile.n0 + wn * C::kWN < N);
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    if (step + 1 < nsteps) gload(step + 1);
+    if (wave_active) {
+      const unsigned char* Ab = As(buf) + (wm * C::kWM + (lane & 15)) * kPitch;
+      const unsigned char* Bb = Bs(buf) + (wn * C::kWN + (lane & 15)) * kPitch;
+      if (E_ == 2) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int ko = kk * 64 + (lane >> 4) * 16;
+          bf16x8_t xa[C::kFI], wb[C::kFJ];
+#pragma unroll
+          for (int i = 0; i < C::kFI; ++i)
+            xa[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 16 * kPitch + ko);
+#pragma unroll
+          for (int j = 0; j < C::kFJ; ++j)
+            wb[j] = *reinterpret_cast<const bf16x8_t*>(Bb + j * 16 * kPitch + ko);
+#pragma unroll
+          for (int i = 0; i < C::kFI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kFJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[j], xa[i], acc[i][j], 0, 0, 0);
+        }
+      } else {
+        const int ko = (lane >> 4) * 32;
+        i32x8_t wb[C::kFJ];
+#pragma unroll
+        for (int j = 0; j < C::kFJ; ++j) wb[j] = *reinterpret_cast<const i32x8_t*>(Bb + j * 16 * kPitch + ko);
+#pragma unroll
+        for (int i = 0; i < C::kFI; ++i) {
+          const i32x8_t xa = *reinterpret_cast<const i32x8_t*>(Ab + i * 16 * kPitch + ko);
+#pragma unroll
+          for (int j = 0; j < C::kFJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[j], xa, acc[i][j], 0, 0, 0,
+                                                                         0, 0, 0);
+        }
+      }
+    }
+    if (step + 1 < nsteps) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+#pragma unroll
+  for (int i = 0; i < C::kFI; ++i) {
+    const int ml = wm * C::kWM + i * 16 + (lane & 15);
+    if (ml >= tile.rows) continue;
+    const int64_t m = tile.row0 + ml;
+#pragma unroll
+    for (int j = 0; j < C::kFJ; ++j) {
+      const int n = tile.n0 + wn * C::kWN + j * 16 + 4 * (lane >> 4);
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = acc[i][j][r] * sc;
+        if (relu) v[r] = v[r] > 0.f ? v[r] : 0.f;
+      }
+      if (C::kOutF32) {
+        float* o = reinterpret_cast<float*>(out) + m * N + n;
+        if (C::kAligned && n + 3 < N) {
+          *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) o[r] = v[r];
+        }
+      } else {
+        bf16_t* o = reinterpret_cast<bf16_t*>(out) + m * N + n;
+        if (C::kAligned && n + 3 < N) {
+          *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) o[r] = f32_to_bf16(v[r]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ streaming kernel (decode)
+
+template <int MB, bool AL>
+__global__ __launch_bounds__(256) void gmm_stream_kernel(
+    const bf16_t* __restrict__ a, const bf16_t* __restrict__ w, const float* __restrict__ a_scale,
+    const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int e, int A, int Hin,
+    int N, int relu, bf16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int ng = (N + 63) / 64;
+  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ex = task / ng;
+  if (ex >= e) return;
+  const int n0 = (task % ng) * 64;
+  int r0 = offsets[ex], r1 = offsets[ex + 1];
+  r0 = r0 < 0 ? 0 : (r0 > A ? A : r0);
+  r1 = r1 < r0 ? r0 : (r1 > A ? A : r1);
+  const int cnt = r1 - r0;
+  if (cnt == 0) return;
+  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+  const int kq = lane >> 4;  // k slice of the 32-wide step
+  const int ci = lane & 15;  // fragment row/column index
+  const int ncol = n0 + 4 * ci;
+  const int avail_n = (int)min(N - ncol, 4) * 2;  // bytes of this lane's 4 columns
+  const bf16_t* wex = w + (int64_t)ex * Hin * N;
+
+  for (int mc = 0; mc < cnt; mc += 16 * MB) {
+    f32x4_t acc[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[mb][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < Hin; k0 += 32) {
+      uint2 rows[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int k = k0 + kq * 8 + r;
+        rows[r] = ld8<AL, 2>(reinterpret_cast<const unsigned char*>(wex + (int64_t)k * N + ncol),
+                             k < Hin ? avail_n : 0);
+      }
+      bf16x8_t xa[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int ml = mc + mb * 16 + ci;
+        const int kk = k0 + kq * 8;
+        const int avail = (ml < cnt) ? min(Hin - kk, 8) * 2 : 0;
+        uint4 v = ld16<AL, 2>(reinterpret_cast<const unsigned char*>(a + (int64_t)(r0 + ml) * Hin + kk),
+                              ml < cnt ? avail : 0);
+        xa[mb] = *reinterpret_cast<bf16x8_t*>(&v);
+      }
+      uint4 cols[4];
+      transpose_8x4_bf16(rows, cols);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t wb = *reinterpret_cast<bf16x8_t*>(&cols[j]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xa[mb], acc[mb][j], 0, 0, 0);
+      }
+    }
+    // MFMA j, output row i = 4*kq + r  ->  column n0 + 4*i + j = n0 + 16*kq + 4r + j
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int ml = mc + mb * 16 + ci;
+      if (ml >= cnt) continue;
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float t = acc[mb][j][r] * sc;
+          v[4 * r + j] = (relu && t < 0.f) ? 0.f : t;
+        }
+      const int nb = n0 + 16 * kq;
+      bf16_t* o = out + (int64_t)(r0 + ml) * N + nb;
+      if (AL && nb + 15 < N) {
+        uint4 p0 = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        uint4 p1 = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                              pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+        reinterpret_cast<uint4*>(o)[0] = p0;
+        reinterpret_cast<uint4*>(o)[1] = p1;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (nb + q < N) o[q] = f32_to_bf16(v[q]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 kernel
+
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+
+__global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ a,
+                                                      const float* __restrict__ w,
+                                                      const float* __restrict__ a_scale,
+                                                      const float* __restrict__ w_scale,
+                                                      const int32_t* __restrict__ offsets, int e,
+                                                      int A, int Hin, int N, int relu,
+                                                      float* __restrict__ out) {
+  __shared__ int s_off[257];
+  __shared__ int s_pre[257];
+  __shared__ float As[kF32BK][kF32BM + 1];
+  __shared__ float Bs[kF32BK][kF32BN + 1];
+  load_tile_prefix<kF32BM>(offsets, e, A, s_off, s_pre);
+  Tile tile;
+  if (!pick_tile<kF32BM, kF32BN, 8>(s_off, s_pre, e, N, tile)) return;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  const float* wex = w + (int64_t)tile.ex * Hin * N;
+  for (int k0 = 0; k0 < Hin; k0 += kF32BK) {
+    for (int p = tid; p < kF32BM * kF32BK; p += 256) {
+      const int r = p / kF32BK, k = p % kF32BK;
+      As[k][r] = (r < tile.rows && k0 + k < Hin) ? a[(int64_t)(tile.row0 + r) * Hin + k0 + k] : 0.f;
+    }
+    for (int p = tid; p < kF32BK * kF32BN; p += 256) {
+      const int k = p / kF32BN, c = p % kF32BN;
+      const int n = tile.n0 + c;
+      Bs[k][c] = (k0 + k < Hin && n < N) ? wex[(int64_t)(k0 + k) * N + n] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kF32BK; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(As[k][ty * 4 + i], Bs[k][tx * 4 + j], acc[i][j]);
+    __syncthreads();
+  }
+  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty * 4 + i;
+    if (r >= tile.rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = tile.n0 + tx * 4 + j;
+      if (n >= N) continue;
+      float v = acc[i][j] * sc;
+      if (relu && v < 0.f) v = 0.f;
+      out[(int64_t)(tile.row0 + r) * N + n] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+template <class C>
+moe_status launch_tiled(const void* a, const float* as, const void* w, const float* ws,
+                        const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
+                        hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_tiled_kernel<C>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    attr_done = true;
+  }
+  const int64_t mt_max = cdiv64(A, C::kBM) + (e < A ? e : A);
+  const int64_t blocks = mt_max * cdiv64(N, C::kBN);
+  const int64_t grid = cdiv64(blocks, 8) * 8;
+  if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(gmm_tiled_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
+                     (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
+                     relu, (unsigned char*)out);
+  return launch_status();
+}
+
+template <int MB, bool AL>
+moe_status launch_stream(const void* a, const float* as, const void* w, const float* ws,
+                         const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
+                         hipStream_t s) {
+  const int64_t tasks = (int64_t)e * cdiv(N, 64);
+  hipLaunchKernelGGL((gmm_stream_kernel<MB, AL>), dim3((unsigned)cdiv64(tasks, 4)), dim3(256), 0, s,
+                     (const bf16_t*)a, (const bf16_t*)w, as, ws, offsets, e, A, Hin, N, relu,
+                     (bf16_t*)out);
+  return launch_status();
+}
+
+template <int MB>
+moe_status launch_stream_al(bool al, const void* a, const float* as, const void* w, const float* ws,
+                            const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
+                            hipStream_t s) {
+  return al ? launch_stream<MB, true>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s)
+            : launch_stream<MB, false>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s);
+}
+
+}  // namespace
+
+// Rows per expert at or below which the weight-streaming kernel is used.
+constexpr int kStreamMaxAvgRows = 48;
+
+moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
+                      const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
+                      moe_act act, void* out, moe_dtype out_dt, hipStream_t s) {
+  if (A == 0) return MOE_OK;
+  const int relu = act == MOE_ACT_RELU;
+  if (in_dt == MOE_F32) {
+    const int64_t blocks = (cdiv64(A, kF32BM) + (e < A ? e : A)) * cdiv64(N, kF32BN);
+    const int64_t grid = cdiv64(blocks, 8) * 8;
+    hipLaunchKernelGGL(gmm_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const float*)a,
+                       (const float*)w, a_scale, w_scale, offsets, e, A, Hin, N, relu, (float*)out);
+    return launch_status();
+  }
+  const int elem = in_dt == MOE_BF16 ? 2 : 1;
+  if (in_dt == MOE_BF16 && (int64_t)A <= (int64_t)kStreamMaxAvgRows * e) {
+    const bool al = (Hin % 8 == 0) && (N % 8 == 0);
+    const int avg = cdiv(A, e);
+    if (avg <= 8) return launch_stream_al<1>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+    if (avg <= 16) return launch_stream_al<2>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+    return launch_stream_al<4>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+  }
+  const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0);
+  if (elem == 2) {
+    typedef TiledCfg<2, 256, 256, 2, 4, true, false> CA;
+    typedef TiledCfg<2, 256, 256, 2, 4, false, false> CU;
+    return al ? launch_tiled<CA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s)
+              : launch_tiled<CU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+  }
+  typedef TiledCfg<1, 256, 256, 2, 4, true, false> FA;
+  typedef TiledCfg<1, 256, 256, 2, 4, false, false> FU;
+  return al ? launch_tiled<FA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s)
+            : launch_tiled<FU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+}
+
+}  // namespace moe

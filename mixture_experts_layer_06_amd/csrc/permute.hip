@@ -1,0 +1,225 @@
+// permute.hip — dispatch of (token, slot) pairs into per-expert contiguous row
+// blocks ("Advanced GPU Optimization ... Part 5", section 1.2, token dispatch;
+// per-expert counts as in the count arrays of
+// "aclnnQuantGroupedMatMulAlltoAllv"; offsets + perm_src are the CSC form of
+// the (T,E) activation mask of the SpMM page).
+//
+// Placement is stable: inside one expert's block rows follow ascending
+// flat index i = t*K + k. Ranks come from in-wave match masks (8 ballots on
+// the expert id bits) plus ordered per-chunk prefix sums, never from the
+// order in which atomics happen to land, so the result is deterministic.
+//
+// Index path, A = T*K pairs cut into chunks of kChunk:
+//   small A (<= kSmallA): one wave does count, scan and rank in one launch;
+//   otherwise: count per chunk (LDS histogram) -> one-block scan over
+//   (chunk, expert) -> per-chunk rank and write.
+// Data path: one block per token reads its row once (16-byte vectors when
+// the row pitch allows) and writes it to its K destination rows.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;   // pairs per chunk
+constexpr int kSmallA = 4096;  // single-wave path up to this many pairs
+
+__device__ __forceinline__ int clamp_e(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+// Lanes whose expert equals mine (among lanes with valid = true), via 8 ballots.
+__device__ __forceinline__ uint64_t match_mask(int e, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint64_t bal = __ballot(valid && ((e >> b) & 1));
+    m &= ((e >> b) & 1) ? bal : ~bal;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Ranks pairs [begin, end) into rows, starting from run[e] (LDS), by one wave.
+__device__ __forceinline__ void rank_range(const int32_t* __restrict__ idx, int begin, int end, int E,
+                                           int* run, int32_t* __restrict__ perm_src,
+                                           int32_t* __restrict__ perm_dst) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int base = begin; base < end; base += kWave) {
+    const int i = base + lane;
+    const bool valid = i < end;
+    const int e = valid ? clamp_e(idx[i], E) : 0;
+    const uint64_t m = match_mask(e, valid);
+    const int rank = __popcll(m & lanemask_lt());
+    int row = 0;
+    if (valid) row = run[e] + rank;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // the highest lane of each group advances the running row
+    if (valid && (m >> lane) == 1ull) run[e] += __popcll(m);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (valid) {
+      perm_dst[i] = row;
+      perm_src[row] = i;
+    }
+  }
+}
+
+// Single wave: whole index path for small A.
+__global__ __launch_bounds__(64) void permute_small_kernel(const int32_t* __restrict__ idx, int A,
+                                                           int E, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm_src,
+                                                           int32_t* __restrict__ perm_dst) {
+  __shared__ int hist[256];
+  __shared__ int run[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < 256; e += kWave) hist[e] = 0;
+  __syncthreads();
+  for (int i = lane; i < A; i += kWave) atomicAdd(&hist[clamp_e(idx[i], E)], 1);
+  __syncthreads();
+  // exclusive scan of hist[0:E] by lane 0 (E <= 256: a short serial loop)
+  if (lane == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      run[e] = acc;
+      acc += hist[e];
+    }
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += kWave) {
+    counts[e] = hist[e];
+    offsets[e] = run[e];
+  }
+  if (lane == 0) offsets[E] = A;
+  rank_range(idx, 0, A, E, run, perm_src, perm_dst);
+}
+
+__global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx, int A,
+                                                            int E, int32_t* __restrict__ chunk_counts) {
+  __shared__ int hist[256];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int begin = blockIdx.x * kChunk;
+  const int end = min(A, begin + kChunk);
+  for (int i = begin + threadIdx.x; i < end; i += blockDim.x) atomicAdd(&hist[clamp_e(idx[i], E)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One block, thread e: running sum over chunks, then exclusive scan over experts.
+__global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                           int nchunks, int E, int A,
+                                                           int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets) {
+  __shared__ int tot[256];
+  __shared__ int off[256];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      chunk_base[(int64_t)c * E + e] = run;
+      run += chunk_counts[(int64_t)c * E + e];
+    }
+  }
+  tot[e] = e < E ? run : 0;
+  __syncthreads();
+  if (e == 0) {
+    int acc = 0;
+    for (int q = 0; q < E; ++q) {
+      off[q] = acc;
+      acc += tot[q];
+    }
+  }
+  __syncthreads();
+  if (e < E) {
+    counts[e] = tot[e];
+    offsets[e] = off[e];
+    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off[e];
+  }
+  if (e == 0) offsets[E] = A;
+}
+
+__global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restrict__ idx, int A, int E,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          int32_t* __restrict__ perm_src,
+                                                          int32_t* __restrict__ perm_dst) {
+  __shared__ int run[256];
+  for (int e = threadIdx.x; e < E; e += kWave) run[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  const int begin = blockIdx.x * kChunk;
+  rank_range(idx, begin, min(A, begin + kChunk), E, run, perm_src, perm_dst);
+}
+
+// Row scatter: x_perm[perm_dst[t*K+k]] = x[t]. VB = bytes per access.
+template <int VB>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const unsigned char* __restrict__ x,
+                                                           int64_t row_bytes, int T, int K,
+                                                           const int32_t* __restrict__ perm_dst,
+                                                           unsigned char* __restrict__ xp) {
+  typedef typename std::conditional<VB == 16, uint4,
+          typename std::conditional<VB == 8, uint2,
+          typename std::conditional<VB == 4, uint32_t,
+          typename std::conditional<VB == 2, uint16_t, uint8_t>::type>::type>::type>::type V;
+  const int64_t nv = row_bytes / VB;
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    int dst[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k] = k < K ? perm_dst[(int64_t)t * K + k] : 0;
+    const V* src = reinterpret_cast<const V*>(x + (int64_t)t * row_bytes);
+    for (int64_t j = threadIdx.x; j < nv; j += blockDim.x) {
+      const V v = src[j];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < K) reinterpret_cast<V*>(xp + (int64_t)dst[k] * row_bytes)[j] = v;
+    }
+  }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int T, int E, int K) {
+  const int64_t A = (int64_t)T * K;
+  if (A <= kSmallA) return 0;
+  const int64_t nch = cdiv64(A, kChunk);
+  return (size_t)(2 * nch * E * sizeof(int32_t));
+}
+
+moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T, int H, int E, int K,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
+                          void* x_perm, void* ws, hipStream_t s) {
+  const int A = T * K;
+  if (A <= kSmallA) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(64), 0, s, idx, A, E, counts, offsets,
+                       perm_src, perm_dst);
+  } else {
+    const int nch = cdiv(A, kChunk);
+    int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);
+    int32_t* chunk_base = chunk_counts + (int64_t)nch * E;
+    hipLaunchKernelGGL(permute_count_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, A,
+                       chunk_base, counts, offsets);
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(nch), dim3(64), 0, s, idx, A, E, chunk_base,
+                       perm_src, perm_dst);
+  }
+  if (x && T > 0) {
+    const int64_t rb = (int64_t)H * dtype_size(dt);
+    const int grid = T < 65536 ? T : 65536;
+    const unsigned char* xs = (const unsigned char*)x;
+    unsigned char* xd = (unsigned char*)x_perm;
+    if (rb % 16 == 0)
+      hipLaunchKernelGGL(permute_rows_kernel<16>, dim3(grid), dim3(256), 0, s, xs, rb, T, K, perm_dst, xd);
+    else if (rb % 8 == 0)
+      hipLaunchKernelGGL(permute_rows_kernel<8>, dim3(grid), dim3(256), 0, s, xs, rb, T, K, perm_dst, xd);
+    else if (rb % 4 == 0)
+      hipLaunchKernelGGL(permute_rows_kernel<4>, dim3(grid), dim3(256), 0, s, xs, rb, T, K, perm_dst, xd);
+    else if (rb % 2 == 0)
+      hipLaunchKernelGGL(permute_rows_kernel<2>, dim3(grid), dim3(256), 0, s, xs, rb, T, K, perm_dst, xd);
+    else
+      hipLaunchKernelGGL(permute_rows_kernel<1>, dim3(grid), dim3(256), 0, s, xs, rb, T, K, perm_dst, xd);
+  }
+  return launch_status();
+}
+
+}  // namespace moe

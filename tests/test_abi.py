@@ -1,0 +1,214 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+entry point include/moe.h declares, and rejects bad arguments on the host
+before touching the device (every case below carries at least one invalid
+argument, so nothing is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_06_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x100000  # a 16-byte aligned non-NULL stand-in address (never dereferenced)
+MIS = 0x100004  # misaligned
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int|moe_status)\s+(moe_\w+)\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_entry_points()
+    for n in ("moe_route", "moe_permute", "moe_gmm", "moe_combine", "moe_layer",
+              "moe_permute_workspace_size", "moe_layer_workspace_size", "moe_status_string",
+              "moe_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for n in declared_entry_points():
+        assert hasattr(L, n), n
+    assert set(moe.EXPORTS) >= set(declared_entry_points())
+
+
+def test_version_and_status_strings():
+    assert moe.lib().moe_version() == 10000
+    seen = set()
+    for s in range(8):
+        msg = moe.status_string(s)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert moe.status_string(99) == "unknown status"
+
+
+L = None
+
+
+@pytest.fixture(autouse=True)
+def _lib():
+    global L
+    L = moe.lib()
+
+
+def route(x=P, wr=P, dt=moe.BF16, bias=None, T=16, H=64, E=8, K=2, idx=P, gate=P):
+    return L.moe_route(x, wr, dt, bias, T, H, E, K, idx, gate, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=moe.FP8_E4M3), moe.ERR_BAD_DTYPE),
+    (dict(dt=7), moe.ERR_BAD_DTYPE),
+    (dict(T=-1), moe.ERR_BAD_SHAPE),
+    (dict(H=0), moe.ERR_BAD_SHAPE),
+    (dict(H=65536), moe.ERR_BAD_SHAPE),
+    (dict(E=0), moe.ERR_BAD_SHAPE),
+    (dict(E=257), moe.ERR_BAD_SHAPE),
+    (dict(K=0), moe.ERR_BAD_SHAPE),
+    (dict(K=9, E=16), moe.ERR_BAD_SHAPE),
+    (dict(K=16, E=256, T=1024, H=128), moe.ERR_BAD_SHAPE),  # SpMM page's example shape: top-16
+    (dict(K=5, E=4), moe.ERR_BAD_SHAPE),
+    (dict(T=52428800 // 2, K=2), moe.ERR_BAD_SHAPE),
+    (dict(x=None), moe.ERR_NULL_POINTER),
+    (dict(wr=None), moe.ERR_NULL_POINTER),
+    (dict(idx=None), moe.ERR_NULL_POINTER),
+    (dict(gate=None), moe.ERR_NULL_POINTER),
+    (dict(x=MIS), moe.ERR_MISALIGNED),
+    (dict(bias=MIS), moe.ERR_MISALIGNED),
+    (dict(gate=MIS), moe.ERR_MISALIGNED),
+])
+def test_route_validation(kw, status):
+    assert route(**kw) == status
+
+
+def test_route_empty_batch_is_noop_without_pointers():
+    assert route(x=None, wr=None, idx=None, gate=None, T=0) == moe.OK
+
+
+def permute(idx=P, x=P, dt=moe.BF16, T=2000, H=64, E=8, K=4, counts=P, offsets=P, psrc=P, pdst=P,
+            xp=P, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        try:
+            ws_bytes = moe.permute_workspace_size(T, E, K)
+        except moe.MoeError:
+            ws_bytes = 0
+    return L.moe_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, ws, ws_bytes, None)
+
+
+def test_permute_workspace_size_small_and_chunked():
+    assert moe.permute_workspace_size(16, 128, 8) == 0
+    n = moe.permute_workspace_size(16384, 64, 6)
+    assert n >= 2 * 96 * 64 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=9), moe.ERR_BAD_DTYPE),
+    (dict(E=300), moe.ERR_BAD_SHAPE),
+    (dict(K=9), moe.ERR_BAD_SHAPE),
+    (dict(H=70000), moe.ERR_BAD_SHAPE),
+    (dict(x=None), moe.ERR_NULL_POINTER),   # x NULL but x_perm given
+    (dict(xp=None), moe.ERR_NULL_POINTER),  # x given but x_perm NULL
+    (dict(counts=None), moe.ERR_NULL_POINTER),
+    (dict(offsets=None), moe.ERR_NULL_POINTER),
+    (dict(psrc=None), moe.ERR_NULL_POINTER),
+    (dict(idx=None), moe.ERR_NULL_POINTER),
+    (dict(ws=None), moe.ERR_NULL_POINTER),
+    (dict(ws_bytes=16), moe.ERR_WORKSPACE_TOO_SMALL),
+    (dict(pdst=MIS), moe.ERR_MISALIGNED),
+    (dict(xp=MIS), moe.ERR_MISALIGNED),
+])
+def test_permute_validation(kw, status):
+    assert permute(**kw) == status
+
+
+def gmm(a=P, adt=moe.BF16, aq=0, asc=None, w=P, wdt=moe.BF16, wq=0, wsc=None, off=P, e=8, A=100,
+        Hin=64, N=64, act=moe.ACT_RELU, out=P, odt=moe.BF16):
+    return L.moe_gmm(a, adt, aq, asc, w, wdt, wq, wsc, off, e, A, Hin, N, act, out, odt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(adt=moe.F32), moe.ERR_BAD_DTYPE),                        # mixed input types
+    (dict(odt=moe.F32), moe.ERR_BAD_DTYPE),                        # bf16 -> f32 not offered
+    (dict(adt=moe.FP8_E4M3, wdt=moe.FP8_E4M3, odt=moe.FP8_E4M3, aq=1, wq=1, asc=P, wsc=P),
+     moe.ERR_BAD_DTYPE),
+    (dict(adt=moe.FP8_E4M3, wdt=moe.FP8_E4M3), moe.ERR_UNSUPPORTED),  # fp8 needs per-tensor scales
+    (dict(aq=2), moe.ERR_UNSUPPORTED),
+    (dict(wq=3), moe.ERR_UNSUPPORTED),
+    (dict(aq=4), moe.ERR_UNSUPPORTED),
+    (dict(aq=5), moe.ERR_UNSUPPORTED),
+    (dict(aq=6), moe.ERR_UNSUPPORTED),
+    (dict(wq=7), moe.ERR_UNSUPPORTED),
+    (dict(wq=8), moe.ERR_UNSUPPORTED),
+    (dict(act=2), moe.ERR_UNSUPPORTED),
+    (dict(e=0), moe.ERR_BAD_SHAPE),
+    (dict(e=257), moe.ERR_BAD_SHAPE),
+    (dict(A=-1), moe.ERR_BAD_SHAPE),
+    (dict(Hin=0), moe.ERR_BAD_SHAPE),
+    (dict(N=65536), moe.ERR_BAD_SHAPE),
+    (dict(aq=1), moe.ERR_NULL_POINTER),                             # per-tensor without a scale
+    (dict(a=None), moe.ERR_NULL_POINTER),
+    (dict(off=None), moe.ERR_NULL_POINTER),
+    (dict(out=None), moe.ERR_NULL_POINTER),
+    (dict(w=MIS), moe.ERR_MISALIGNED),
+    (dict(off=MIS), moe.ERR_MISALIGNED),
+])
+def test_gmm_validation(kw, status):
+    assert gmm(**kw) == status
+
+
+def test_gmm_zero_rows_is_noop():
+    assert gmm(a=None, w=None, off=None, out=None, A=0) == moe.OK
+
+
+def combine(y=P, dt=moe.BF16, pdst=P, gate=P, T=10, K=2, N=64, out=P, odt=moe.BF16):
+    return L.moe_combine(y, dt, pdst, gate, T, K, N, out, odt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=moe.FP8_E4M3, odt=moe.FP8_E4M3), moe.ERR_BAD_DTYPE),
+    (dict(odt=moe.F32), moe.ERR_BAD_DTYPE),
+    (dict(K=0), moe.ERR_BAD_SHAPE),
+    (dict(K=9), moe.ERR_BAD_SHAPE),
+    (dict(N=0), moe.ERR_BAD_SHAPE),
+    (dict(T=-3), moe.ERR_BAD_SHAPE),
+    (dict(y=None), moe.ERR_NULL_POINTER),
+    (dict(pdst=None), moe.ERR_NULL_POINTER),
+    (dict(out=None), moe.ERR_NULL_POINTER),
+    (dict(gate=MIS), moe.ERR_MISALIGNED),
+])
+def test_combine_validation(kw, status):
+    assert combine(**kw) == status
+
+
+def layer(x=P, wr=P, bias=None, w1=P, w2=P, dt=moe.BF16, T=32, H=64, E=8, K=2, F=96,
+          act=moe.ACT_RELU, y=P, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return L.moe_layer(x, wr, bias, w1, w2, dt, T, H, E, K, F, act, y, None, None, None, ws, ws_bytes,
+                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=moe.FP8_E4M3), moe.ERR_BAD_DTYPE),
+    (dict(F=0), moe.ERR_BAD_SHAPE),
+    (dict(K=3, E=2), moe.ERR_BAD_SHAPE),
+    (dict(act=3), moe.ERR_UNSUPPORTED),
+    (dict(w1=None), moe.ERR_NULL_POINTER),
+    (dict(ws=None), moe.ERR_NULL_POINTER),
+    (dict(ws_bytes=1024), moe.ERR_WORKSPACE_TOO_SMALL),
+    (dict(y=MIS), moe.ERR_MISALIGNED),
+])
+def test_layer_validation(kw, status):
+    assert layer(**kw) == status
+
+
+def test_layer_workspace_size_covers_buffers():
+    T, H, E, K, F = 4096, 4096, 8, 2, 14336
+    n = moe.layer_workspace_size(T, H, E, K, F, moe.BF16)
+    A = T * K
+    assert n >= A * H * 2 + A * F * 2 + 4 * A * 4
+    with pytest.raises(moe.MoeError) as ei:
+        moe.layer_workspace_size(T, H, E, 9, F, moe.BF16)
+    assert ei.value.status == moe.ERR_BAD_SHAPE

@@ -1,0 +1,273 @@
+"""GPU parity of each C-ABI entry point against the fp64 oracle.
+
+Both sides get the same seeded inputs from synth; nothing the GPU computes
+is fed back into the oracle. Sizes span several tiles and a ragged tail;
+edge cases cover empty experts, unaligned widths, K = 1, E = 256.
+Bar: bit-exact for indices/counts/offsets/permutations/copies; floating
+point within the normwise tolerances (fp32 1e-5, bf16 2e-2, fp8 6e-2).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_06_amd as moe
+import oracle
+import synth
+from synth import configs
+from tests.helpers import GAP, TOL, as_f64, normwise_err, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- route
+
+ROUTE_CASES = [
+    # (name, T, H, E, K, dtype, integer, bias)
+    ("tiny_f32", 64, 128, 8, 2, "f32", False, False),
+    ("tiny_f32_int", 64, 128, 8, 2, "f32", True, False),
+    ("tiny_bf16_int", 64, 128, 8, 2, "bf16", True, False),
+    ("mid_bf16_bias", 300, 520, 64, 6, "bf16", False, True),
+    ("ragged_bf16", 77, 100, 5, 2, "bf16", False, False),
+    ("e256_k8", 40, 256, 256, 8, "bf16", False, False),
+    ("decode_like", 64, 4096, 128, 8, "bf16", False, False),
+    ("k1", 50, 64, 16, 1, "bf16", False, False),
+    ("k_eq_e", 33, 96, 4, 4, "f32", False, False),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_parity(case):
+    name, T, H, E, K, dt, integer, use_bias = case
+    d = configs.layer_inputs("tiny", T=T, H=H, E=E, K=K, F=8, dtype=dt, integer=integer,
+                             bias=use_bias, wid=40 + len(name))
+    ridx, rgate, _, gap = oracle.route(d["x"], d["wr"], T, H, E, K, bias=d["bias"])
+    bias = to_dev(d["bias"]) if use_bias else None
+    idx, gate = moe.route(to_dev(d["x"]), to_dev(d["wr"]), K, bias=bias)
+    _sync()
+    idx, gate = to_host(idx), to_host(gate)
+    if integer:
+        # scores are exact integers in fp32: every token, ties included, matches
+        assert np.array_equal(idx, ridx)
+        np.testing.assert_allclose(gate, rgate, rtol=0, atol=2e-6)
+        return
+    ok = gap > GAP
+    assert ok.mean() > 0.9
+    assert np.array_equal(idx[ok], ridx[ok])
+    tol = 1e-5 if dt == "f32" else 2e-3  # bf16 scores: fp32 sums of exact products
+    assert np.abs(gate[ok] - rgate[ok]).max() <= tol
+    np.testing.assert_allclose(gate.sum(1), 1.0, atol=1e-6)
+
+
+# ---------------------------------------------------------------- permute
+
+def _check_permute_bitexact(idx_np, E, x_np):
+    T, K = idx_np.shape
+    x = to_dev(x_np) if x_np is not None else None
+    r = moe.permute(to_dev(idx_np), E, x=x)
+    _sync()
+    counts, offsets, psrc, pdst = oracle.permute(idx_np, E)
+    assert np.array_equal(to_host(r["counts"]), counts)
+    assert np.array_equal(to_host(r["offsets"]), offsets)
+    assert np.array_equal(to_host(r["perm_src"]), psrc)
+    assert np.array_equal(to_host(r["perm_dst"]), pdst)
+    if x_np is not None:
+        xp_ref = oracle.gather_rows(x_np, psrc, K)
+        assert np.array_equal(to_host(r["x_perm"]).view(np.uint8), xp_ref.view(np.uint8))
+
+
+def test_permute_small_path_bf16():
+    idx = synth.random_routing(101, 100, 8, 2)
+    x = synth.normal(102, (100, 128), dtype="bf16")
+    _check_permute_bitexact(idx, 8, x)
+
+
+def test_permute_chunked_path_skewed_with_empty_experts():
+    T, E, K = 3000, 64, 6
+    idx = synth.random_routing(103, T, E, K)
+    idx[idx >= 60] = 0          # experts 60..63 empty, expert 0 heavy
+    idx[idx % 7 == 3] = 1       # more skew
+    x = synth.normal(104, (T, 72), dtype="bf16")
+    _check_permute_bitexact(idx, E, x)
+
+
+def test_permute_duplicate_experts_in_a_token():
+    idx = synth.random_routing(105, 700, 6, 4)
+    idx[:, 1] = idx[:, 0]  # same expert twice in each token: still stable by (t, k)
+    _check_permute_bitexact(idx, 6, None)
+
+
+@pytest.mark.parametrize("H,kind", [(7, "fp8"), (5, "f32"), (33, "bf16"), (7168, "fp8")])
+def test_permute_row_widths(H, kind):
+    T, E, K = 130, 32, 8
+    idx = synth.random_routing(106, T, E, K)
+    if kind == "fp8":
+        x = synth.to_e4m3(synth.normal(107, (T, H)), 0.02)
+    elif kind == "f32":
+        x = synth.normal(107, (T, H))
+    else:
+        x = synth.normal(107, (T, H), dtype="bf16")
+    _check_permute_bitexact(idx, E, x)
+
+
+def test_permute_empty_batch():
+    E = 8
+    counts = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
+    L = moe.lib()
+    st = L.moe_permute(None, None, 0, 0, 1, E, 2, counts.data_ptr(), offsets.data_ptr(), None, None,
+                       None, None, 0, None)
+    _sync()
+    assert st == moe.OK
+    assert to_host(counts).tolist() == [0] * E and to_host(offsets).tolist() == [0] * (E + 1)
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+def _offsets(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def _gmm_case(counts, Hin, N, dt, seed, act=moe.ACT_NONE, integer=False, scales=None):
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    if dt == "fp8":
+        if integer:
+            af = synth.ints(seed, (A, Hin), -4, 4)
+            wf = synth.ints(seed + 1, (e, Hin, N), -4, 4)
+            a, w = synth.to_e4m3(af, 1.0), synth.to_e4m3(wf, 1.0)
+            sa, sw = scales or (0.5, 2.0)
+        else:
+            a, sa = synth.quantize_e4m3(synth.normal(seed, (A, Hin)))
+            w, sw = synth.quantize_e4m3(synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin)))
+        ref = oracle.gmm(a, w, off, act=act, a_scale=float(sa), w_scale=float(sw), nthreads=8)
+        out = moe.gmm(to_dev(a), to_dev(w), to_dev(off), act=act,
+                      a_scale=torch.tensor([sa], dtype=torch.float32, device="cuda"),
+                      w_scale=torch.tensor([sw], dtype=torch.float32, device="cuda"))
+    else:
+        if integer:
+            a = synth.ints(seed, (A, Hin), -2, 2, dt)
+            w = synth.ints(seed + 1, (e, Hin, N), -2, 2, dt)
+        else:
+            a = synth.normal(seed, (A, Hin), dtype=dt)
+            w = synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin), dtype=dt)
+        ref = oracle.gmm(a, w, off, act=act, nthreads=8)
+        out = moe.gmm(to_dev(a), to_dev(w), to_dev(off), act=act)
+    _sync()
+    return to_host(out), ref
+
+
+GMM_CASES = [
+    # (name, counts, Hin, N, dtype)
+    ("bf16_tiled_ragged", [300, 0, 1, 555], 640, 520, "bf16"),
+    ("bf16_tiled_unaligned", [270, 3, 0, 400], 300, 130, "bf16"),
+    ("bf16_tiled_ktail", [513], 200, 264, "bf16"),
+    ("bf16_stream", [5, 0, 17, 30, 1, 0, 9, 12, 3, 31, 0, 2, 8, 16, 4, 7], 512, 320, "bf16"),
+    ("bf16_stream_unaligned", [3, 0, 14, 6, 1, 9], 90, 100, "bf16"),
+    ("bf16_stream_overflow_rows", [2, 80, 1, 0, 3, 1, 2, 3], 256, 192, "bf16"),
+    ("fp8_tiled", [200, 0, 333], 256, 384, "fp8"),
+    ("fp8_tiled_unaligned", [100, 77], 200, 100, "fp8"),
+    ("f32_tiny", [20, 0, 17, 40, 1, 30, 12, 8], 128, 256, "f32"),
+    ("f32_ragged", [70, 5], 33, 45, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", GMM_CASES, ids=[c[0] for c in GMM_CASES])
+@pytest.mark.parametrize("act", [moe.ACT_NONE, moe.ACT_RELU], ids=["none", "relu"])
+def test_gmm_parity(case, act):
+    name, counts, Hin, N, dt = case
+    out, ref = _gmm_case(counts, Hin, N, dt, seed=200 + len(name), act=act)
+    err = normwise_err(out, ref)
+    assert err <= TOL[dt], f"{name}: normwise err {err:.3e}"
+    # a much tighter bound actually holds: one rounding of the output dominates
+    bound = {"f32": 2e-6, "bf16": 8e-3, "fp8": 8e-3}[dt]
+    assert err <= bound, f"{name}: normwise err {err:.3e} (> {bound})"
+
+
+@pytest.mark.parametrize("dt,counts,Hin,N", [
+    ("bf16", [300, 0, 1, 555], 512, 264),   # tiled
+    ("bf16", [5, 0, 17, 30, 2, 1], 256, 128),  # streaming
+    ("fp8", [200, 0, 333], 512, 256),       # tiled E4M3, power-of-two scales
+])
+def test_gmm_integer_inputs_bit_exact(dt, counts, Hin, N):
+    out, ref = _gmm_case(counts, Hin, N, dt, seed=300, integer=True, act=moe.ACT_RELU)
+    assert np.abs(ref).max() < 2 ** 24  # the fp32 sums are exact
+    assert np.array_equal(out, oracle.bf16_bits(ref))
+
+
+@pytest.mark.parametrize("rows", [[257, 0, 31], [3, 9, 0, 1]])
+def test_gmm_identity_weights_return_rows(rows):
+    H = 256
+    off = _offsets(rows)
+    a = synth.normal(400, (int(off[-1]), H), dtype="bf16")
+    w = synth.to_bf16(np.broadcast_to(np.eye(H, dtype=np.float32), (len(rows), H, H)).copy())
+    out = moe.gmm(to_dev(a), to_dev(w), to_dev(off))
+    _sync()
+    assert np.array_equal(to_host(out), a)
+
+
+def test_gmm_shared_expert_is_plain_gemm():
+    """e = 1 (the shared-expert MatMul): matches a plain fp64 matmul."""
+    M, Hin, N = 700, 384, 320
+    a = synth.normal(410, (M, Hin), dtype="bf16")
+    w = synth.normal(411, (1, Hin, N), math.sqrt(1 / Hin), dtype="bf16")
+    out = moe.gmm(to_dev(a), to_dev(w), to_dev(np.array([0, M], np.int32)))
+    _sync()
+    ref = as_f64(a) @ as_f64(w[0])
+    assert normwise_err(to_host(out), ref) <= 8e-3
+
+
+def test_gmm_deterministic():
+    counts = [300, 0, 1, 555]
+    off = _offsets(counts)
+    a = to_dev(synth.normal(420, (int(off[-1]), 640), dtype="bf16"))
+    w = to_dev(synth.normal(421, (4, 640, 520), 0.04, dtype="bf16"))
+    o1 = to_host(moe.gmm(a, w, to_dev(off)))
+    o2 = to_host(moe.gmm(a, w, to_dev(off)))
+    assert np.array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("dt,N", [("bf16", 264), ("bf16", 30), ("f32", 30), ("f32", 128)])
+def test_combine_weighted_parity(dt, N):
+    T, E, K = 200, 16, 6
+    idx = synth.random_routing(500, T, E, K)
+    _, _, psrc, pdst = oracle.permute(idx, E)
+    yp = synth.normal(501, (T * K, N), dtype=dt)
+    g = np.abs(synth.normal(502, (T, K))).astype(np.float32)
+    g /= g.sum(1, keepdims=True)
+    out = moe.combine(to_dev(yp), to_dev(pdst), to_dev(g), T, K)
+    _sync()
+    ref = oracle.combine(as_f64(yp), pdst, g.astype(np.float64), T, K)
+    err = normwise_err(to_host(out), ref)
+    assert err <= (1e-6 if dt == "f32" else 4e-3)
+
+
+def test_combine_one_hot_gates_is_exact_gather():
+    T, E, K, N = 150, 8, 4, 96
+    idx = synth.random_routing(510, T, E, K)
+    _, _, psrc, pdst = oracle.permute(idx, E)
+    yp = synth.normal(511, (T * K, N), dtype="bf16")
+    g = np.zeros((T, K), np.float32)
+    g[:, 2] = 1.0
+    out = moe.combine(to_dev(yp), to_dev(pdst), to_dev(g), T, K)
+    _sync()
+    assert np.array_equal(to_host(out), yp[pdst.reshape(T, K)[:, 2]])
+
+
+@pytest.mark.parametrize("dt,N", [("bf16", 2048), ("bf16", 7), ("f32", 5)])
+def test_unpermute_bit_exact(dt, N):
+    T, E, K = 300, 32, 8
+    idx = synth.random_routing(520, T, E, K)
+    _, _, psrc, pdst = oracle.permute(idx, E)
+    yp = synth.normal(521, (T * K, N), dtype=dt)
+    out = moe.combine(to_dev(yp), to_dev(pdst), None, T, K)
+    _sync()
+    assert np.array_equal(to_host(out).view(np.uint8), yp[pdst].view(np.uint8))
