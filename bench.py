@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-GPU MoE layer on MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+route -> permute -> GEMM 1 (ReLU) -> GEMM 2 -> weighted combine, each a
+C-ABI call on torch's current stream (the same launches moe_layer makes).
+Inputs are resident in HBM before the timed region. HIP events between the
+stages give per-kernel durations from the same timed steps; the dominant
+kernel (moe_gmm) is reported against its roofline.
+
+Prints ONE JSON line. Default workload: prefill (T=4096, H=4096, E=8, K=2,
+F=14336, bf16). Other workloads: --workload skewed|decode16|decode64|
+decode256|fp8gmm|tiny.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "MoE layer tokens/s; moe_gmm TFLOP/s and % of MFMA/HBM peak (1 GPU)"
+
+LAYER_WORKLOADS = {
+    # name: (recipe, T)
+    "prefill": ("prefill", 4096),
+    "skewed": ("skewed", 16384),
+    "decode16": ("decode", 16),
+    "decode64": ("decode", 64),
+    "decode256": ("decode", 256),
+    "tiny": ("tiny", 64),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def host_to_dev(a, dev):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def flops_bytes_gmm(counts, Hin, N, elem):
+    """Algorithmic work of one grouped-GEMM launch: 2*A*Hin*N flops; bytes =
+    weights of experts that received rows + activations in + outputs out."""
+    A = int(sum(counts))
+    used = sum(1 for c in counts if c > 0)
+    fl = 2.0 * A * Hin * N
+    by = used * Hin * N * elem + A * Hin * elem + A * N * 2
+    return fl, by
+
+
+def bench_layer(args, dev):
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_06_amd as moe
+    from synth import configs
+
+    recipe, T = LAYER_WORKLOADS[args.workload]
+    d = configs.layer_inputs(recipe, T=T)
+    H, E, K, F, dt = d["H"], d["E"], d["K"], d["F"], d["dtype"]
+    es = 4 if dt == "f32" else 2
+    A = T * K
+    x = host_to_dev(d["x"], dev)
+    wr = host_to_dev(d["wr"], dev)
+    w1 = host_to_dev(d["w1"], dev)
+    w2 = host_to_dev(d["w2"], dev)
+    bias = host_to_dev(d["bias"], dev) if d["bias"] is not None else None
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    bufs = {"counts": torch.empty((E,), dtype=torch.int32, device=dev),
+            "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+            "perm_src": torch.empty((A,), dtype=torch.int32, device=dev),
+            "perm_dst": torch.empty((A,), dtype=torch.int32, device=dev),
+            "x_perm": torch.empty((A, H), dtype=tdt, device=dev)}
+    hm = torch.empty((A, F), dtype=tdt, device=dev)
+    yp = torch.empty((A, H), dtype=tdt, device=dev)
+    y = torch.empty((T, H), dtype=tdt, device=dev)
+    pws_n = moe.permute_workspace_size(T, E, K)
+    pws = torch.empty((max(pws_n, 16),), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        moe.route(x, wr, K, bias=bias, topk_idx=idx, topk_gate=gate)
+        if ev is not None:
+            ev[1].record()
+        moe.permute(idx, E, x=x, ws=pws, out=bufs)
+        if ev is not None:
+            ev[2].record()
+        moe.gmm(bufs["x_perm"], w1, bufs["offsets"], act=moe.ACT_RELU, out=hm)
+        if ev is not None:
+            ev[3].record()
+        moe.gmm(hm, w2, bufs["offsets"], out=yp)
+        if ev is not None:
+            ev[4].record()
+        moe.combine(yp, bufs["perm_dst"], gate, T, K, out=y)
+        if ev is not None:
+            ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    names = ["route", "permute", "gmm1", "gmm2", "combine"]
+    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+
+    # the same step through the single moe_layer entry point (outside the timed region)
+    ws_layer = torch.empty((moe.layer_workspace_size(T, H, E, K, F, moe.dtype_code(x)),),
+                           dtype=torch.uint8, device=dev)
+    y2 = torch.empty_like(y)
+    for _ in range(2):
+        moe.layer(x, wr, w1, w2, K, bias=bias, y=y2, ws=ws_layer)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        moe.layer(x, wr, w1, w2, K, bias=bias, y=y2, ws=ws_layer)
+    e1.record()
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / args.steps
+
+    counts = bufs["counts"].cpu().numpy().tolist()
+    fl1, by1 = flops_bytes_gmm(counts, H, F, es)
+    fl2, by2 = flops_bytes_gmm(counts, F, H, es)
+    gmm_ms = (per["gmm1"] + per["gmm2"]) / 2.0  # one kernel, two launches of equal work
+    fl_launch, by_launch = (fl1 + fl2) / 2.0, (by1 + by2) / 2.0
+    hbm_bound = (fl_launch / by_launch) < (PEAK_BF16_TFLOPS / PEAK_HBM_GBS) * 1e3
+    if hbm_bound:
+        achieved = by_launch / (gmm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    else:
+        achieved = fl_launch / (gmm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+    bytes_stage = {
+        "route": T * H * es + H * E * es + T * K * 8,
+        "permute": T * K * 4 * 3 + T * H * es + A * H * es,
+        "combine": A * H * es + T * H * es + T * K * 8,
+    }
+    kernels = {n: {"ms": per[n]} for n in names}
+    for n, b in bytes_stage.items():
+        kernels[n]["GB/s"] = b / (per[n] * 1e-3) / 1e9
+    for n, fl, by in (("gmm1", fl1, by1), ("gmm2", fl2, by2)):
+        kernels[n]["TFLOP/s"] = fl / (per[n] * 1e-3) / 1e12
+        kernels[n]["GB/s"] = by / (per[n] * 1e-3) / 1e9
+    gmm_tflops = (fl1 + fl2) / ((per["gmm1"] + per["gmm2"]) * 1e-3) / 1e12
+    workload = (f"{args.workload}: T={T} H={H} E={E} K={K} F={F} ReLU {dt}"
+                + (" router bias -1.2ln(e+1)" if bias is not None else ""))
+    res = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens)",
+        "config": {"workload": workload, "T": T, "H": H, "E": E, "K": K, "F": F,
+                   "tokens_per_step": T, "parallelism": "single GPU"},
+        "roofline": dict(roof, kernel="moe_gmm (gmm_tiled_kernel / gmm_stream_kernel)",
+                         launches_per_step=2, flops_per_launch=fl_launch,
+                         bytes_per_launch=by_launch, avg_launch_ms=gmm_ms),
+        "moe_gmm_tflops": gmm_tflops,
+        "moe_gmm_frac_bf16_peak": gmm_tflops / PEAK_BF16_TFLOPS if dt != "f32" else None,
+        "kernels": kernels,
+        "moe_layer_call_ms": layer_ms,
+        "expert_counts": {"min": min(counts), "max": max(counts), "empty": counts.count(0)},
+    }
+    host = {"x": d["x"], "wr": d["wr"], "w1": d["w1"], "w2": d["w2"], "bias": d["bias"], "K": K}
+    return res, host
+
+
+def bench_fp8(args, dev):
+    """Page-2 form: fp8 grouped GEMM (per-tensor scales) + Unpermute, with the
+    bf16 shared-expert GEMM on a second stream, joined by events."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_06_amd as moe
+    import oracle
+    from synth import configs
+
+    d = configs.fp8_inputs()
+    T, e, K, A, H1, N1, H2, N2 = (d[k] for k in ("T", "e", "K", "A", "H1", "N1", "H2", "N2"))
+    # dispatch layout of the routed rows: computed once on the device by moe_permute
+    idx = host_to_dev(d["topk_idx"], dev)
+    perm = moe.permute(idx, e)
+    gx = host_to_dev(d["gmm_x"], dev)
+    gw = host_to_dev(d["gmm_w"], dev)
+    sx = torch.tensor([float(d["gmm_x_scale"])], dtype=torch.float32, device=dev)
+    sw = torch.tensor([float(d["gmm_w_scale"])], dtype=torch.float32, device=dev)
+    mx = host_to_dev(d["mm_x"], dev)
+    mw = host_to_dev(d["mm_w"], dev).view(1, H2, N2)
+    moff = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    gy = torch.empty((A, N1), dtype=torch.bfloat16, device=dev)
+    un = torch.empty((A, N1), dtype=torch.bfloat16, device=dev)
+    my = torch.empty((T, N2), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream(device=dev)
+
+    def step(ev=None):
+        main = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        if ev is not None:
+            ev[0].record(main)
+        with torch.cuda.stream(side):
+            if ev is not None:
+                ev[3].record(side)
+            moe.gmm(mx, mw, moff, out=my, stream=side)
+            if ev is not None:
+                ev[4].record(side)
+        moe.gmm(gx, gw, perm["offsets"], a_scale=sx, w_scale=sw, out=gy)
+        if ev is not None:
+            ev[1].record(main)
+        moe.combine(gy, perm["perm_dst"], None, T, K, out=un)
+        if ev is not None:
+            ev[2].record(main)
+        join = torch.cuda.Event()
+        join.record(side)
+        main.wait_event(join)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    gmm_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][1]) for s in range(args.steps)]))
+    un_ms = float(np.mean([evs[s][1].elapsed_time(evs[s][2]) for s in range(args.steps)]))
+    sh_ms = float(np.mean([evs[s][3].elapsed_time(evs[s][4]) for s in range(args.steps)]))
+    counts = perm["counts"].cpu().numpy().tolist()
+    fl, by = flops_bytes_gmm(counts, H1, N1, 1)
+    achieved = fl / (gmm_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
+        "config": {"workload": f"fp8gmm: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
+                               f"({T},{H2})x({H2},{N2}) bf16", "tokens_per_step": T},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
+                     "kernel": "moe_gmm E4M3 (gmm_tiled_kernel)", "flops_per_launch": fl,
+                     "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
+        "kernels": {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
+                    "unpermute": {"ms": un_ms, "GB/s": 2 * A * N1 * 2 / (un_ms * 1e-3) / 1e9},
+                    "shared_gemm_bf16": {"ms": sh_ms, "TFLOP/s": 2.0 * T * H2 * N2 / (sh_ms * 1e-3) / 1e12}},
+    }
+    return res, None
+
+
+def cpu_baseline_layer(host, target_s):
+    """The oracle (plain fp64 C) on the host cores: the whole layer on the
+    first n tokens of the same inputs, n grown until the run takes about
+    target_s seconds."""
+    import oracle
+    nth = cpu_threads()
+    T = host["x"].shape[0]
+    n = min(T, 8)
+    spent = 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.layer(host["x"][:n], host["wr"], host["w1"], host["w2"], host["K"], bias=host["bias"],
+                     nthreads=nth)
+        dt = time.perf_counter() - t0
+        spent += dt
+        if dt >= target_s / 3 or n >= T or spent > target_s:
+            break
+        n = min(T, max(n + 1, int(n * min(8.0, (target_s / 2) / max(dt, 1e-3)))))
+    return {"value": n / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+            "sample": f"whole layer on the first {n} of {T} tokens (full weights), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the "
+                                   "expert-parallel all-to-all across GPUs is not built)"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    import mixture_experts_layer_06_amd as moe
+    moe.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == "fp8gmm":
+        res, host = bench_fp8(args, dev)
+    else:
+        res, host = bench_layer(args, dev)
+    if not args.no_cpu and host is not None:
+        res["cpu_baseline"] = cpu_baseline_layer(host, args.cpu_seconds)
+    elif not args.no_cpu:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
