@@ -37,6 +37,12 @@
 
 #include "common.h"
 
+// Wave layout of the 256 x 256 tiled kernel (waves along rows x columns).
+#ifndef MOE_TILED_WAVES_M
+#define MOE_TILED_WAVES_M 2
+#define MOE_TILED_WAVES_N 4
+#endif
+
 namespace moe {
 namespace {
 
@@ -122,10 +128,12 @@ __device__ __forceinline__ bool pick_tile(const int* s_off, const int* s_pre, in
   const int gsz = min(GM, mt - grp * GM);
   const int nt = within / gsz;
   const int m = grp * GM + within % gsz;
-  t.ex = ex;
-  t.row0 = s_off[ex] + m * BM;
-  t.rows = min(BM, s_off[ex + 1] - t.row0);
-  t.n0 = nt * BN;
+  // every lane computed the same tile: say so, so that tile-derived bases and
+  // buffer descriptors live in scalar registers
+  t.ex = __builtin_amdgcn_readfirstlane(ex);
+  t.row0 = __builtin_amdgcn_readfirstlane(s_off[ex] + m * BM);
+  t.rows = __builtin_amdgcn_readfirstlane(min(BM, s_off[ex + 1] - (s_off[ex] + m * BM)));
+  t.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
   return true;
 }
 
@@ -227,8 +235,23 @@ __device__ __forceinline__ float ld_scale(const float* p) { return p ? *p : 1.0f
 
 // ------------------------------------------------------------------ tiled MFMA kernel
 
-constexpr int kKB = 128;    // K-slice bytes per tile step
-constexpr int kPitch = 144; // LDS row pitch (bytes)
+constexpr int kKB = 128;   // K-slice bytes per tile step (64 bf16 or 128 E4M3 values)
+constexpr int kRowB = 128; // LDS bytes per tile row (one K slice, no padding)
+
+// LDS byte offset of 16-byte chunk c (0..7) of tile row r. The chunk index is
+// XORed with s(r) = (r ^ (r >> 3)) & 7: sixteen consecutive rows read at the
+// same logical chunk land on sixteen distinct 16-byte bank groups, and so do
+// the eight chunks of one row plus the eight of the next row.
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * kRowB + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer, 32-bit data format; loads at offsets >= bytes return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset bias that puts a load out of range
 
 template <int ELEM, int BM, int BN, int WM_, int WN_, bool AL, bool OUT_F32>
 struct TiledCfg {
@@ -248,11 +271,14 @@ struct TiledCfg {
   static constexpr int kAPT = kAChunks / kNT;
   static constexpr bool kAligned = AL;
   static constexpr bool kOutF32 = OUT_F32;
-  static constexpr int kLdsA = BM * kPitch, kLdsB = BN * kPitch;
+  static constexpr int kLdsA = BM * kRowB, kLdsB = BN * kRowB;
   static constexpr int kLds = 2 * (kLdsA + kLdsB);
   static_assert(kUnits % kNT == 0 && kAChunks % kNT == 0, "load split");
 };
 
+// AL (16-byte aligned rows, both matrices under 2 GiB per expert): buffer
+// loads, the hardware returns zeros outside each tile's valid region.
+// !AL: element-wise loads with explicit bounds (odd shapes only).
 template <class C>
 __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
@@ -271,65 +297,120 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
-  const int64_t hin_b = (int64_t)Hin * E_;
-  const int64_t n_b = (int64_t)N * E_;
+  const int hin_b = Hin * E_;
+  const int n_b = N * E_;
+  const int n0b = tile.n0 * E_;
   const unsigned char* abase = a + (int64_t)tile.row0 * hin_b;
-  const unsigned char* wbase = w + (int64_t)tile.ex * Hin * n_b + (int64_t)tile.n0 * E_;
-  const int nsteps = (int)cdiv64(hin_b, kKB);
+  const unsigned char* wbase = w + (int64_t)tile.ex * Hin * n_b;
+  const int nsteps = (hin_b + kKB - 1) / kKB;
 
-  // buffer b: activations at smem + b*(A+B), weights right after them
+  // buffer: activations at smem + b*(A+B), weights right after them
   auto As = [&](int b) { return smem + b * (C::kLdsA + C::kLdsB); };
   auto Bs = [&](int b) { return smem + b * (C::kLdsA + C::kLdsB) + C::kLdsA; };
+
+  // ---- per-thread load descriptors, fixed for the tile
+  __amdgpu_buffer_rsrc_t arsrc, wrsrc;
+  if (C::kAligned) {
+    arsrc = make_rsrc(abase, (uint32_t)tile.rows * (uint32_t)hin_b);
+    wrsrc = make_rsrc(wbase, (uint32_t)Hin * (uint32_t)n_b);
+  }
+  uint32_t aoff[C::kAPT];
+  int alds[C::kAPT], akc[C::kAPT];
+#pragma unroll
+  for (int i = 0; i < C::kAPT; ++i) {
+    const int c = tid + i * C::kNT;
+    const int row = c >> 3, kc = c & 7;
+    aoff[i] = (uint32_t)row * (uint32_t)hin_b + kc * 16;  // beyond tile.rows -> out of range
+    akc[i] = kc * 16;
+    alds[i] = lds_off(row, kc);
+  }
+  uint32_t woff[C::kUPT];
+  int wkr[C::kUPT], wnq[C::kUPT], wkb[C::kUPT];
+#pragma unroll
+  for (int u = 0; u < C::kUPT; ++u) {
+    const int unit = tid + u * C::kNT;
+    const int kb = unit % C::kKBlk, nq = unit / C::kKBlk;
+    const int nb = n0b + nq * 8;
+    woff[u] = (uint32_t)(kb * 8) * (uint32_t)n_b + (uint32_t)nb + (nb < n_b ? 0u : kOOB);
+    wkr[u] = kb * 8;
+    wnq[u] = nq;
+    wkb[u] = kb;
+  }
 
   uint4 ra[C::kAPT];
   uint2 rb[C::kUPT][8];
 
   auto gload = [&](int step) {
-    const int kb0 = step * kKB;  // byte offset into an activation row
+    const int kb0 = step * kKB;
+    const int k0 = step * C::kKRows;
+    if (C::kAligned) {
 #pragma unroll
-    for (int i = 0; i < C::kAPT; ++i) {
-      const int c = tid + i * C::kNT;
-      const int row = c >> 3, kc = c & 7;
-      const int avail = (row < tile.rows) ? (int)min<int64_t>(hin_b - (kb0 + kc * 16), 16) : 0;
-      ra[i] = ld16<C::kAligned, E_>(abase + (int64_t)row * hin_b + kb0 + kc * 16, avail);
-    }
-    const int k0 = step * C::kKRows;  // weight row
+      for (int i = 0; i < C::kAPT; ++i) {
+        const uint32_t o = aoff[i] + kb0 + (kb0 + akc[i] < hin_b ? 0u : kOOB);
+        ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, o, 0, 0));
+      }
+      const uint32_t kstep = (uint32_t)k0 * (uint32_t)n_b;
 #pragma unroll
-    for (int u = 0; u < C::kUPT; ++u) {
-      const int unit = tid + u * C::kNT;
-      const int kb = unit % C::kKBlk, nq = unit / C::kKBlk;
-      const int nb = nq * 8;  // byte offset in the weight row (from n0)
-      const int avail_n = (int)min<int64_t>(n_b - ((int64_t)tile.n0 * E_ + nb), 8);
+      for (int u = 0; u < C::kUPT; ++u)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int k = k0 + kb * 8 + r;
-        rb[u][r] = ld8<C::kAligned, E_>(wbase + (int64_t)k * n_b + nb, k < Hin ? avail_n : 0);
+        for (int r = 0; r < 8; ++r)
+          rb[u][r] = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(wrsrc, woff[u] + kstep + r * n_b, 0, 0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kAPT; ++i) {
+        const int c = tid + i * C::kNT;
+        const int row = c >> 3;
+        const int rem = hin_b - (kb0 + akc[i]);
+        const int avail = row < tile.rows ? (rem < 16 ? rem : 16) : 0;
+        ra[i] = ld16<false, E_>(abase + (int64_t)row * hin_b + kb0 + akc[i], avail);
+      }
+#pragma unroll
+      for (int u = 0; u < C::kUPT; ++u) {
+        const int nb = n0b + wnq[u] * 8;
+        const int remn = n_b - nb;
+        const int avail_n = remn < 8 ? remn : 8;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int k = k0 + wkr[u] + r;
+          rb[u][r] = ld8<false, E_>(wbase + (int64_t)k * n_b + nb, k < Hin ? avail_n : 0);
+        }
       }
     }
   };
   auto lstore = [&](int buf) {
+    unsigned char* Ab = As(buf);
+    unsigned char* Bb = Bs(buf);
 #pragma unroll
-    for (int i = 0; i < C::kAPT; ++i) {
-      const int c = tid + i * C::kNT;
-      const int row = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4*>(As(buf) + row * kPitch + kc * 16) = ra[i];
-    }
+    for (int i = 0; i < C::kAPT; ++i) *reinterpret_cast<uint4*>(Ab + alds[i]) = ra[i];
 #pragma unroll
     for (int u = 0; u < C::kUPT; ++u) {
-      const int unit = tid + u * C::kNT;
-      const int kb = unit % C::kKBlk, nq = unit / C::kKBlk;
       if (E_ == 2) {
         uint4 cols[4];
         transpose_8x4_bf16(rb[u], cols);
+        // odd column groups write their four rows in the order 1,0,3,2 so that the
+        // two groups sharing a 16-lane phase touch rows of opposite parity
+        // (a bitwise select keeps the choice in registers; a ternary on array
+        // elements gets turned into a dynamically indexed array in scratch)
+        const int odd = wnq[u] & 1;
+        const uint32_t msk = 0u - (uint32_t)odd;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint4*>(Bs(buf) + (nq * 4 + j) * kPitch + kb * 16) = cols[j];
+        for (int j = 0; j < 4; ++j) {
+          const uint4 c0 = cols[j], c1 = cols[j ^ 1];
+          uint4 v;
+          v.x = c0.x ^ ((c0.x ^ c1.x) & msk);
+          v.y = c0.y ^ ((c0.y ^ c1.y) & msk);
+          v.z = c0.z ^ ((c0.z ^ c1.z) & msk);
+          v.w = c0.w ^ ((c0.w ^ c1.w) & msk);
+          *reinterpret_cast<uint4*>(Bb + lds_off(wnq[u] * 4 + (j ^ odd), wkb[u])) = v;
+        }
       } else {
         uint2 cols[8];
         transpose_8x8_u8(rb[u], cols);
+        // 8-byte half of 16-byte chunk (kb >> 1)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint2*>(Bs(buf) + (nq * 8 + j) * kPitch + kb * 8) = cols[j];
+          *reinterpret_cast<uint2*>(Bb + lds_off(wnq[u] * 8 + j, wkb[u] >> 1) + (wkb[u] & 1) * 8) = cols[j];
       }
     }
   };
@@ -341,6 +422,7 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     for (int j = 0; j < C::kFJ; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   const bool wave_active = (wm * C::kWM < tile.rows) && (tile.n0 + wn * C::kWN < N);
+  const int ci = lane & 15, kq = lane >> 4;
 
   gload(0);
   lstore(0);
@@ -349,19 +431,19 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     const int buf = step & 1;
     if (step + 1 < nsteps) gload(step + 1);
     if (wave_active) {
-      const unsigned char* Ab = As(buf) + (wm * C::kWM + (lane & 15)) * kPitch;
-      const unsigned char* Bb = Bs(buf) + (wn * C::kWN + (lane & 15)) * kPitch;
+      const unsigned char* Ab = As(buf);
+      const unsigned char* Bb = Bs(buf);
       if (E_ == 2) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const int ko = kk * 64 + (lane >> 4) * 16;
+          const int c = kk * 4 + kq;
           bf16x8_t xa[C::kFI], wb[C::kFJ];
 #pragma unroll
           for (int i = 0; i < C::kFI; ++i)
-            xa[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 16 * kPitch + ko);
+            xa[i] = *reinterpret_cast<const bf16x8_t*>(Ab + lds_off(wm * C::kWM + i * 16 + ci, c));
 #pragma unroll
           for (int j = 0; j < C::kFJ; ++j)
-            wb[j] = *reinterpret_cast<const bf16x8_t*>(Bb + j * 16 * kPitch + ko);
+            wb[j] = *reinterpret_cast<const bf16x8_t*>(Bb + lds_off(wn * C::kWN + j * 16 + ci, c));
 #pragma unroll
           for (int i = 0; i < C::kFI; ++i)
 #pragma unroll
@@ -369,13 +451,22 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[j], xa[i], acc[i][j], 0, 0, 0);
         }
       } else {
-        const int ko = (lane >> 4) * 32;
         i32x8_t wb[C::kFJ];
 #pragma unroll
-        for (int j = 0; j < C::kFJ; ++j) wb[j] = *reinterpret_cast<const i32x8_t*>(Bb + j * 16 * kPitch + ko);
+        for (int j = 0; j < C::kFJ; ++j) {
+          const int r = wn * C::kWN + j * 16 + ci;
+          const uint4 lo = *reinterpret_cast<const uint4*>(Bb + lds_off(r, 2 * kq));
+          const uint4 hi = *reinterpret_cast<const uint4*>(Bb + lds_off(r, 2 * kq + 1));
+          wb[j] = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
 #pragma unroll
         for (int i = 0; i < C::kFI; ++i) {
-          const i32x8_t xa = *reinterpret_cast<const i32x8_t*>(Ab + i * 16 * kPitch + ko);
+          const int r = wm * C::kWM + i * 16 + ci;
+          const uint4 lo = *reinterpret_cast<const uint4*>(Ab + lds_off(r, 2 * kq));
+          const uint4 hi = *reinterpret_cast<const uint4*>(Ab + lds_off(r, 2 * kq + 1));
+          const i32x8_t xa = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
           for (int j = 0; j < C::kFJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[j], xa, acc[i][j], 0, 0, 0,
@@ -391,12 +482,12 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
   const float sc = ld_scale(a_scale) * ld_scale(w_scale);
 #pragma unroll
   for (int i = 0; i < C::kFI; ++i) {
-    const int ml = wm * C::kWM + i * 16 + (lane & 15);
+    const int ml = wm * C::kWM + i * 16 + ci;
     if (ml >= tile.rows) continue;
     const int64_t m = tile.row0 + ml;
 #pragma unroll
     for (int j = 0; j < C::kFJ; ++j) {
-      const int n = tile.n0 + wn * C::kWN + j * 16 + 4 * (lane >> 4);
+      const int n = tile.n0 + wn * C::kWN + j * 16 + 4 * kq;
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -421,6 +512,225 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
           for (int r = 0; r < 4; ++r)
             if (n + r < N) o[r] = f32_to_bf16(v[r]);
         }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ LDS-DMA bf16 kernel
+//
+// Same tiles and scheduling as gmm_tiled_kernel, but global->LDS traffic goes
+// through buffer_load_dwordx4 ... lds (gfx950 LDS DMA): no staging registers,
+// so a ring of kDmaStages K slices (32 bf16 each) keeps kDmaStages-1 slices
+// in flight per block. The weight slice lands untransposed (k rows of BN
+// columns); each lane then reads 8 rows x 4 columns (ds_read_b64), transposes
+// them with v_perm_b32 and issues 4 MFMAs whose row i stands for column
+// 4i + j, which leaves each lane 16 consecutive output columns of one row.
+//
+// Stage layout (32 KB): activations BM rows x 64 B, 16-byte chunk c of row r
+// at r*64 + ((c ^ ((r >> 2) & 3)) << 4); weights 32 rows x BN*2 B, 128-byte
+// segment g of row k at k*BN*2 + ((g ^ ((k >> 3) & 3)) << 7). Both swizzles
+// make the MFMA operand reads bank-conflict free; every DMA instruction
+// writes one contiguous KB.
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDmaStages = 4;
+constexpr int kDmaKB = 64;  // K bytes per stage: 32 bf16
+
+__device__ __forceinline__ u32x4_t make_srd(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  u32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu;  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes);                          // loads past it read 0
+  r.w = 0x00020000u;                                                    // 32-bit data format
+  return r;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from buffer offset voff into LDS at lds_base + 16*lane
+// (lds_base wave-uniform). The compiler does not see these loads, so the
+// kernel waits for them itself with wait_vmcnt.
+__device__ __forceinline__ void dma16(u32x4_t srd, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(srd), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int WM_, int WN_>
+struct DmaCfg {
+  static constexpr int kBM = BM, kBN = BN;
+  static constexpr int kWavesM = WM_, kWavesN = WN_;
+  static constexpr int kNT = 64 * WM_ * WN_;
+  static constexpr int kWM = BM / WM_, kWN = BN / WN_;
+  static constexpr int kFI = kWM / 16;   // 16-row activation fragments per wave
+  static constexpr int kFG = kWN / 64;   // 64-column weight groups per wave
+  static constexpr int kLdsA = BM * kDmaKB;        // bytes of activations per stage
+  static constexpr int kLdsW = 32 * BN * 2;        // bytes of weights per stage
+  static constexpr int kStage = kLdsA + kLdsW;
+  static constexpr int kLds = kDmaStages * kStage;
+  static constexpr int kADma = kLdsA / 1024 / (kNT / 64);  // KB-sized DMA ops per wave per stage
+  static constexpr int kWDma = kLdsW / 1024 / (kNT / 64);
+  static constexpr int kPerStage = kADma + kWDma;          // vmcnt units per stage per thread
+  static_assert(kLdsA % (1024 * (kNT / 64)) == 0 && kLdsW % (1024 * (kNT / 64)) == 0, "dma split");
+  static_assert(kWN % 64 == 0, "weight groups");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::kNT) void gmm_dma_kernel(
+    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
+    const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+    const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
+    bf16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int s_off[257];
+  __shared__ int s_pre[257];
+  load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_pre);
+  Tile tile;
+  if (!pick_tile<C::kBM, C::kBN, 8>(s_off, s_pre, e, N, tile)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
+  const int hin_b = Hin * 2;
+  const int n_b = N * 2;
+  const int n0b = tile.n0 * 2;
+  const int nsteps = (hin_b + kDmaKB - 1) / kDmaKB;
+  const u32x4_t asrd = make_srd(a + (int64_t)tile.row0 * hin_b, (uint32_t)tile.rows * (uint32_t)hin_b);
+  const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * n_b, (uint32_t)Hin * (uint32_t)n_b);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  // ---- DMA descriptors: which global bytes this lane fetches for each KB it fills
+  uint32_t a_voff[C::kADma];
+  uint32_t a_kc[C::kADma];
+#pragma unroll
+  for (int q = 0; q < C::kADma; ++q) {
+    const int kb = (wave * C::kADma + q) * 1024 + lane * 16;  // byte within the stage's A part
+    const int row = kb >> 6, pc = (kb >> 4) & 3;
+    const int lc = pc ^ ((row >> 2) & 3);
+    a_voff[q] = (uint32_t)row * (uint32_t)hin_b + lc * 16;
+    a_kc[q] = lc * 16;
+  }
+  uint32_t w_voff[C::kWDma];
+#pragma unroll
+  for (int q = 0; q < C::kWDma; ++q) {
+    const int kb = (wave * C::kWDma + q) * 1024 + lane * 16;  // byte within the stage's W part
+    const int k = kb / (C::kBN * 2), pb = kb % (C::kBN * 2);
+    const int lseg = (pb >> 7) ^ ((k >> 3) & 3);
+    const int lb = (lseg << 7) + (pb & 127);
+    w_voff[q] = (uint32_t)k * (uint32_t)n_b + (uint32_t)(n0b + lb) + (n0b + lb < n_b ? 0u : kOOB);
+  }
+  auto issue = [&](int step) {
+    const uint32_t base = lds0 + (step % kDmaStages) * C::kStage;
+    const int kb0 = step * kDmaKB;
+#pragma unroll
+    for (int q = 0; q < C::kADma; ++q)
+      dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < hin_b ? 0u : kOOB),
+            __builtin_amdgcn_readfirstlane(base + (wave * C::kADma + q) * 1024));
+    const uint32_t kstep = (uint32_t)(step * 32) * (uint32_t)n_b;
+#pragma unroll
+    for (int q = 0; q < C::kWDma; ++q)
+      dma16(wsrd, w_voff[q] + kstep,
+            __builtin_amdgcn_readfirstlane(base + C::kLdsA + (wave * C::kWDma + q) * 1024));
+  };
+
+  f32x4_t acc[C::kFI][C::kFG][4];
+#pragma unroll
+  for (int i = 0; i < C::kFI; ++i)
+#pragma unroll
+    for (int g = 0; g < C::kFG; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][g][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  const bool wave_active = (wm * C::kWM < tile.rows) && (tile.n0 + wn * C::kWN < N);
+  const int ci = lane & 15, kq = lane >> 4;
+  // per-lane LDS read offsets within a stage
+  int xoff[C::kFI];
+#pragma unroll
+  for (int i = 0; i < C::kFI; ++i) {
+    const int m = wm * C::kWM + i * 16 + ci;
+    xoff[i] = m * kDmaKB + ((kq ^ ((m >> 2) & 3)) << 4);
+  }
+  int woff[C::kFG];
+#pragma unroll
+  for (int g = 0; g < C::kFG; ++g) {
+    const int cb = (wn * C::kWN + g * 64 + 4 * ci) * 2;  // byte of this lane's 4 columns
+    woff[g] = C::kLdsA + (kq * 8) * (C::kBN * 2) + (((cb >> 7) ^ kq) << 7) + (cb & 127);
+  }
+
+#pragma unroll
+  for (int s = 0; s < kDmaStages - 1; ++s)
+    if (s < nsteps) issue(s);
+  for (int step = 0; step < nsteps; ++step) {
+    const int ahead = nsteps - 1 - step;  // stages issued after this one
+    if (ahead >= 2) wait_vmcnt<2 * C::kPerStage>();
+    else if (ahead == 1) wait_vmcnt<C::kPerStage>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (step + kDmaStages - 1 < nsteps) issue(step + kDmaStages - 1);
+    if (wave_active) {
+      const unsigned char* st = smem + (step % kDmaStages) * C::kStage;
+      bf16x8_t xa[C::kFI];
+#pragma unroll
+      for (int i = 0; i < C::kFI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(st + xoff[i]);
+#pragma unroll
+      for (int g = 0; g < C::kFG; ++g) {
+        uint2 rows[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          rows[r] = *reinterpret_cast<const uint2*>(st + woff[g] + r * (C::kBN * 2));
+        uint4 cols[4];
+        transpose_8x4_bf16(rows, cols);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t wb = *reinterpret_cast<bf16x8_t*>(&cols[j]);
+#pragma unroll
+          for (int i = 0; i < C::kFI; ++i)
+            acc[i][g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xa[i], acc[i][g][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if (!wave_active) return;
+  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+#pragma unroll
+  for (int i = 0; i < C::kFI; ++i) {
+    const int ml = wm * C::kWM + i * 16 + ci;
+    if (ml >= tile.rows) continue;
+    const int64_t m = tile.row0 + ml;
+#pragma unroll
+    for (int g = 0; g < C::kFG; ++g) {
+      // MFMA j, output row 4*kq + r  ->  column nb + 4r + j
+      const int nb = tile.n0 + wn * C::kWN + g * 64 + 16 * kq;
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float t = acc[i][g][j][r] * sc;
+          v[4 * r + j] = (relu && t < 0.f) ? 0.f : t;
+        }
+      bf16_t* o = out + m * N + nb;
+      if (nb + 15 < N) {
+        reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                                                    pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (nb + q < N) o[q] = f32_to_bf16(v[q]);
       }
     }
   }
@@ -595,6 +905,26 @@ moe_status launch_tiled(const void* a, const float* as, const void* w, const flo
   return launch_status();
 }
 
+template <class C>
+moe_status launch_dma(const void* a, const float* as, const void* w, const float* ws,
+                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
+                      hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_dma_kernel<C>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    attr_done = true;
+  }
+  const int64_t mt_max = cdiv64(A, C::kBM) + (e < A ? e : A);
+  const int64_t blocks = mt_max * cdiv64(N, C::kBN);
+  const int64_t grid = cdiv64(blocks, 8) * 8;
+  if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(gmm_dma_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
+                     (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
+                     relu, (bf16_t*)out);
+  return launch_status();
+}
+
 template <int MB, bool AL>
 moe_status launch_stream(const void* a, const float* as, const void* w, const float* ws,
                          const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
@@ -639,15 +969,24 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
     if (avg <= 16) return launch_stream_al<2>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
     return launch_stream_al<4>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
   }
-  const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0);
+  // buffer-load path: 16-byte aligned rows and each expert's weight matrix under 2 GiB
+  const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0) &&
+                  ((int64_t)Hin * N * elem < (1ll << 31));
+  constexpr int WM = MOE_TILED_WAVES_M, WN = MOE_TILED_WAVES_N;
+#ifndef MOE_NO_DMA
+  if (elem == 2 && al && N % 16 == 0) {
+    typedef DmaCfg<256, 256, 2, 4> CD;
+    return launch_dma<CD>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+  }
+#endif
   if (elem == 2) {
-    typedef TiledCfg<2, 256, 256, 2, 4, true, false> CA;
-    typedef TiledCfg<2, 256, 256, 2, 4, false, false> CU;
+    typedef TiledCfg<2, 256, 256, WM, WN, true, false> CA;
+    typedef TiledCfg<2, 256, 256, WM, WN, false, false> CU;
     return al ? launch_tiled<CA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s)
               : launch_tiled<CU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
   }
-  typedef TiledCfg<1, 256, 256, 2, 4, true, false> FA;
-  typedef TiledCfg<1, 256, 256, 2, 4, false, false> FU;
+  typedef TiledCfg<1, 256, 256, WM, WN, true, false> FA;
+  typedef TiledCfg<1, 256, 256, WM, WN, false, false> FU;
   return al ? launch_tiled<FA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s)
             : launch_tiled<FU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
 }
