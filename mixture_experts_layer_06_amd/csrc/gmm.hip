@@ -37,6 +37,18 @@
 
 #include "common.h"
 
+// bf16 tiled path: 1 = LDS-DMA kernel, 0 = register-staged kernel.
+#ifndef MOE_GMM_BF16
+#define MOE_GMM_BF16 1
+#endif
+// Tile / wave layout / ring depth of the bf16 LDS-DMA kernel.
+#ifndef MOE_DMA_BM
+#define MOE_DMA_BM 256
+#define MOE_DMA_BN 256
+#define MOE_DMA_WM 2
+#define MOE_DMA_WN 4
+#define MOE_DMA_STAGES 4
+#endif
 // Wave layout of the 256 x 256 tiled kernel (waves along rows x columns).
 #ifndef MOE_TILED_WAVES_M
 #define MOE_TILED_WAVES_M 2
@@ -521,8 +533,8 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
 //
 // Same tiles and scheduling as gmm_tiled_kernel, but global->LDS traffic goes
 // through buffer_load_dwordx4 ... lds (gfx950 LDS DMA): no staging registers,
-// so a ring of kDmaStages K slices (32 bf16 each) keeps kDmaStages-1 slices
-// in flight per block. The weight slice lands untransposed (k rows of BN
+// so a ring of STAGES K slices (32 bf16 each) keeps STAGES-1 slices in
+// flight per block. The weight slice lands untransposed (k rows of BN
 // columns); each lane then reads 8 rows x 4 columns (ds_read_b64), transposes
 // them with v_perm_b32 and issues 4 MFMAs whose row i stands for column
 // 4i + j, which leaves each lane 16 consecutive output columns of one row.
@@ -535,7 +547,6 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kDmaStages = 4;
 constexpr int kDmaKB = 64;  // K bytes per stage: 32 bf16
 
 __device__ __forceinline__ u32x4_t make_srd(const void* base, uint32_t bytes) {
@@ -566,9 +577,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int WM_, int WN_>
+template <int BM, int BN, int WM_, int WN_, int STAGES>
 struct DmaCfg {
+  static constexpr int kStages = STAGES;
   static constexpr int kBM = BM, kBN = BN;
+  static constexpr int kSegMask = (BN * 2) / 128 - 1;  // 128-byte segments per weight row - 1
   static constexpr int kWavesM = WM_, kWavesN = WN_;
   static constexpr int kNT = 64 * WM_ * WN_;
   static constexpr int kWM = BM / WM_, kWN = BN / WN_;
@@ -577,16 +590,20 @@ struct DmaCfg {
   static constexpr int kLdsA = BM * kDmaKB;        // bytes of activations per stage
   static constexpr int kLdsW = 32 * BN * 2;        // bytes of weights per stage
   static constexpr int kStage = kLdsA + kLdsW;
-  static constexpr int kLds = kDmaStages * kStage;
+  static constexpr int kLds = STAGES * kStage;
   static constexpr int kADma = kLdsA / 1024 / (kNT / 64);  // KB-sized DMA ops per wave per stage
   static constexpr int kWDma = kLdsW / 1024 / (kNT / 64);
   static constexpr int kPerStage = kADma + kWDma;          // vmcnt units per stage per thread
   static_assert(kLdsA % (1024 * (kNT / 64)) == 0 && kLdsW % (1024 * (kNT / 64)) == 0, "dma split");
   static_assert(kWN % 64 == 0, "weight groups");
+  static_assert(STAGES >= 3 && STAGES <= 4, "ring depth");
 };
 
+// Two waves per SIMD: caps registers at 256 per lane, which also keeps the
+// accumulators in VGPRs (left to itself with one wave per SIMD the compiler
+// parks them in AGPRs and copies them back and forth every K slice).
 template <class C>
-__global__ __launch_bounds__(C::kNT) void gmm_dma_kernel(
+__global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) void gmm_dma_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
@@ -626,18 +643,18 @@ __global__ __launch_bounds__(C::kNT) void gmm_dma_kernel(
   for (int q = 0; q < C::kWDma; ++q) {
     const int kb = (wave * C::kWDma + q) * 1024 + lane * 16;  // byte within the stage's W part
     const int k = kb / (C::kBN * 2), pb = kb % (C::kBN * 2);
-    const int lseg = (pb >> 7) ^ ((k >> 3) & 3);
+    const int lseg = (pb >> 7) ^ ((k >> 3) & C::kSegMask);
     const int lb = (lseg << 7) + (pb & 127);
     w_voff[q] = (uint32_t)k * (uint32_t)n_b + (uint32_t)(n0b + lb) + (n0b + lb < n_b ? 0u : kOOB);
   }
   auto issue = [&](int step) {
-    const uint32_t base = lds0 + (step % kDmaStages) * C::kStage;
+    const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
     const int kb0 = step * kDmaKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
       dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < hin_b ? 0u : kOOB),
             __builtin_amdgcn_readfirstlane(base + (wave * C::kADma + q) * 1024));
-    const uint32_t kstep = (uint32_t)(step * 32) * (uint32_t)n_b;
+    const uint32_t kstep = step < nsteps ? (uint32_t)(step * 32) * (uint32_t)n_b : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
       dma16(wsrd, w_voff[q] + kstep,
@@ -665,42 +682,61 @@ __global__ __launch_bounds__(C::kNT) void gmm_dma_kernel(
 #pragma unroll
   for (int g = 0; g < C::kFG; ++g) {
     const int cb = (wn * C::kWN + g * 64 + 4 * ci) * 2;  // byte of this lane's 4 columns
-    woff[g] = C::kLdsA + (kq * 8) * (C::kBN * 2) + (((cb >> 7) ^ kq) << 7) + (cb & 127);
+    woff[g] = C::kLdsA + (kq * 8) * (C::kBN * 2) + (((cb >> 7) ^ (kq & C::kSegMask)) << 7) + (cb & 127);
   }
 
+  // Fragment registers, one set. Activation fragment i of slice s+1 is read
+  // into the registers of fragment i of slice s right after the last MFMA
+  // that uses them, so each LDS read overlaps the rest of the slice's MFMAs.
+  // The weight fragments are read and transposed after the multiplies.
+  bf16x8_t xa[C::kFI];
+  uint4 wc[C::kFG][4];
+  auto read_w = [&](int slice) {
+    const unsigned char* st = smem + (slice % C::kStages) * C::kStage;
 #pragma unroll
-  for (int s = 0; s < kDmaStages - 1; ++s)
-    if (s < nsteps) issue(s);
-  for (int step = 0; step < nsteps; ++step) {
-    const int ahead = nsteps - 1 - step;  // stages issued after this one
-    if (ahead >= 2) wait_vmcnt<2 * C::kPerStage>();
-    else if (ahead == 1) wait_vmcnt<C::kPerStage>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (step + kDmaStages - 1 < nsteps) issue(step + kDmaStages - 1);
-    if (wave_active) {
-      const unsigned char* st = smem + (step % kDmaStages) * C::kStage;
-      bf16x8_t xa[C::kFI];
+    for (int g = 0; g < C::kFG; ++g) {
+      uint2 wraw[8];
 #pragma unroll
-      for (int i = 0; i < C::kFI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(st + xoff[i]);
-#pragma unroll
-      for (int g = 0; g < C::kFG; ++g) {
-        uint2 rows[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          rows[r] = *reinterpret_cast<const uint2*>(st + woff[g] + r * (C::kBN * 2));
-        uint4 cols[4];
-        transpose_8x4_bf16(rows, cols);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8_t wb = *reinterpret_cast<bf16x8_t*>(&cols[j]);
-#pragma unroll
-          for (int i = 0; i < C::kFI; ++i)
-            acc[i][g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xa[i], acc[i][g][j], 0, 0, 0);
-        }
-      }
+      for (int r = 0; r < 8; ++r) wraw[r] = *reinterpret_cast<const uint2*>(st + woff[g] + r * (C::kBN * 2));
+      transpose_8x4_bf16(wraw, wc[g]);
     }
+  };
+  // Slice s: wait for slice s+1's DMA (the S-3 newer slices may stay in
+  // flight), barrier, refill the slot slice s-1 used, multiply slice s while
+  // reading slice s+1. Past-the-end slices are issued too (out-of-range
+  // loads write zeros), so every wait count is fixed.
+  auto step_fn = [&](int step) {
+    wait_vmcnt<(C::kStages - 3) * C::kPerStage>();
+    __syncthreads();
+    issue(step + C::kStages - 1);
+    if (wave_active) {
+      const unsigned char* nx = smem + ((step + 1) % C::kStages) * C::kStage;
+#pragma unroll
+      for (int i = 0; i < C::kFI; ++i) {
+#pragma unroll
+        for (int g = 0; g < C::kFG; ++g)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *reinterpret_cast<bf16x8_t*>(&wc[g][j]), xa[i], acc[i][g][j], 0, 0, 0);
+        xa[i] = *reinterpret_cast<const bf16x8_t*>(nx + xoff[i]);
+      }
+      read_w(step + 1);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < C::kStages - 1; ++s) issue(s);
+  wait_vmcnt<(C::kStages - 2) * C::kPerStage>();
+  __syncthreads();
+  if (wave_active) {
+    const unsigned char* st = smem;
+#pragma unroll
+    for (int i = 0; i < C::kFI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(st + xoff[i]);
+    read_w(0);
   }
+  for (int step = 0; step < nsteps; ++step) step_fn(step);
+  wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
 
   if (!wave_active) return;
   const float sc = ld_scale(a_scale) * ld_scale(w_scale);
@@ -973,9 +1009,9 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
   const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0) &&
                   ((int64_t)Hin * N * elem < (1ll << 31));
   constexpr int WM = MOE_TILED_WAVES_M, WN = MOE_TILED_WAVES_N;
-#ifndef MOE_NO_DMA
+#if MOE_GMM_BF16 == 1
   if (elem == 2 && al && N % 16 == 0) {
-    typedef DmaCfg<256, 256, 2, 4> CD;
+    typedef DmaCfg<MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_STAGES> CD;
     return launch_dma<CD>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
   }
 #endif
