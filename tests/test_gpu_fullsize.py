@@ -1,0 +1,175 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (moe_layer / moe_route / moe_permute / moe_gmm / moe_combine
+on the same shapes). The oracle computes sampled outputs one by one (the
+per-token form of the layer, single rows of the grouped GEMM); properties that
+hold at any size cover the rest. Inputs come from synth only.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_06_amd as moe
+import oracle
+import synth
+from synth import configs
+from tests.helpers import GAP, TOL, as_f64, normwise_err, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+NTH = synth.threads()
+
+
+@functools.lru_cache(maxsize=4)
+def _inputs(name, T):
+    return configs.layer_inputs(name, T=T)
+
+
+def _layer_on_gpu(d):
+    T, E, K = d["T"], d["E"], d["K"]
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    bias = to_dev(d["bias"]) if d["bias"] is not None else None
+    x, wr, w1, w2 = (to_dev(d[k]) for k in ("x", "wr", "w1", "w2"))
+    y = moe.layer(x, wr, w1, w2, K, bias=bias, topk_idx=idx, topk_gate=gate, counts=counts)
+    torch.cuda.synchronize()
+    del x, wr, w1, w2
+    return to_host(y), to_host(idx), to_host(gate), to_host(counts)
+
+
+def _sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    s = set([0, T - 1]) | set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    return np.array(sorted(s), np.int32)
+
+
+@pytest.mark.parametrize("name,T,nsample", [
+    ("prefill", 4096, 24),
+    ("skewed", 16384, 48),
+    ("decode", 16, 16),
+    ("decode", 64, 24),
+    ("decode", 256, 32),
+])
+def test_layer_full_size_sampled_tokens(name, T, nsample):
+    d = _inputs(name, T)
+    y, idx, gate, counts = _layer_on_gpu(d)
+    K, E = d["K"], d["E"]
+    assert counts.sum() == T * K
+    assert np.array_equal(np.bincount(idx.ravel(), minlength=E), counts)
+    toks = _sample_tokens(T, nsample, seed=T)
+    ref = oracle.layer_tokens(d["x"], d["wr"], d["w1"], d["w2"], K, toks, bias=d["bias"],
+                              nthreads=NTH)
+    ok = ref["gap"] > GAP
+    assert ok.mean() > 0.8
+    assert np.array_equal(idx[toks][ok], ref["idx"][ok])
+    np.testing.assert_allclose(gate[toks][ok], ref["gate"][ok], atol=2e-3)
+    err = normwise_err(y[toks][ok], ref["y"][ok])
+    assert err <= TOL["bf16"], f"{name} T={T}: {err:.3e}"
+    if name == "skewed":
+        # the router bias gives expert 0 the largest share and a long tail
+        assert counts.argmax() == 0 and counts[0] > 8 * np.median(counts)
+
+
+def test_route_full_size_all_tokens_decode_and_prefill():
+    for name, T in (("decode", 256), ("prefill", 4096)):
+        d = _inputs(name, T)
+        K = d["K"]
+        idx, gate = moe.route(to_dev(d["x"]), to_dev(d["wr"]), K)
+        torch.cuda.synchronize()
+        ridx, rgate, _, gap = oracle.route(d["x"], d["wr"], T, d["H"], d["E"], K)
+        ok = gap > GAP
+        assert np.array_equal(to_host(idx)[ok], ridx[ok])
+        assert np.abs(to_host(gate)[ok] - rgate[ok]).max() <= 2e-3
+
+
+@pytest.mark.parametrize("T,E,K,H", [(4096, 8, 2, 4096), (16384, 64, 6, 2048), (8192, 32, 8, 7168)])
+def test_permute_full_size_bit_exact(T, E, K, H):
+    idx = synth.random_routing(600 + E, T, E, K)
+    x = synth.normal(601, (T, H), dtype="bf16") if H <= 4096 else None
+    r = moe.permute(to_dev(idx), E, x=to_dev(x) if x is not None else None)
+    torch.cuda.synchronize()
+    counts, offsets, psrc, pdst = oracle.permute(idx, E)
+    assert np.array_equal(to_host(r["counts"]), counts)
+    assert np.array_equal(to_host(r["offsets"]), offsets)
+    assert np.array_equal(to_host(r["perm_src"]), psrc)
+    assert np.array_equal(to_host(r["perm_dst"]), pdst)
+    if x is not None:
+        xp = to_host(r["x_perm"])
+        rows = np.random.default_rng(1).choice(T * K, 512, replace=False)
+        assert np.array_equal(xp[rows], x[psrc[rows] // K])
+
+
+def _boundary_rows(offsets, extra, seed):
+    rows = set()
+    for e in range(len(offsets) - 1):
+        if offsets[e + 1] > offsets[e]:
+            rows |= {int(offsets[e]), int(offsets[e + 1] - 1)}
+    rng = np.random.default_rng(seed)
+    rows |= set(rng.choice(int(offsets[-1]), extra, replace=False).tolist())
+    return np.array(sorted(rows), np.int32)
+
+
+@pytest.mark.parametrize("which", ["w1", "w2"])
+def test_gmm_full_size_prefill_sampled_rows(which):
+    """moe_gmm on the prefill GEMM shapes (8192 rows, 8 experts) against
+    single-row oracle results, first/last row of every expert included."""
+    T, E, K, H, F = 4096, 8, 2, 4096, 14336
+    idx = synth.random_routing(610, T, E, K)
+    counts, offsets, _, _ = oracle.permute(idx, E)
+    Hin, N = (H, F) if which == "w1" else (F, H)
+    a = synth.normal(611, (T * K, Hin), dtype="bf16")
+    w = synth.normal(612, (E, Hin, N), (1.0 / Hin) ** 0.5, dtype="bf16")
+    act = moe.ACT_RELU if which == "w1" else moe.ACT_NONE
+    out = to_host(moe.gmm(to_dev(a), to_dev(w), to_dev(offsets), act=act))
+    rows = _boundary_rows(offsets, 16, 613)
+    ref = oracle.gmm(a, w, offsets, act=act, rows=rows, nthreads=NTH)
+    assert normwise_err(out[rows], ref) <= 8e-3
+
+
+def test_fp8_gmm_unpermute_and_shared_expert_full_size():
+    """The page-2 workload: E4M3 grouped GEMM (65536 x 7168 x 2048, 32 experts,
+    per-tensor scales) + Unpermute, and the bf16 shared-expert GEMM."""
+    d = configs.fp8_inputs()
+    T, e, K, A, H1, N1 = (d[k] for k in ("T", "e", "K", "A", "H1", "N1"))
+    counts, offsets, psrc, pdst = oracle.permute(d["topk_idx"], e)
+    perm = moe.permute(to_dev(d["topk_idx"]), e)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(perm["offsets"]), offsets)
+    sx = torch.tensor([float(d["gmm_x_scale"])], device="cuda")
+    sw = torch.tensor([float(d["gmm_w_scale"])], device="cuda")
+    gy = moe.gmm(to_dev(d["gmm_x"]), to_dev(d["gmm_w"]), perm["offsets"], a_scale=sx, w_scale=sw)
+    un = moe.combine(gy, perm["perm_dst"], None, T, K)
+    torch.cuda.synchronize()
+    gy_h, un_h = to_host(gy), to_host(un)
+    rows = _boundary_rows(offsets, 24, 620)
+    ref = oracle.gmm(d["gmm_x"], d["gmm_w"], offsets, a_scale=float(d["gmm_x_scale"]),
+                     w_scale=float(d["gmm_w_scale"]), rows=rows, nthreads=NTH)
+    assert normwise_err(gy_h[rows], ref) <= TOL["fp8"]
+    assert normwise_err(gy_h[rows], ref) <= 8e-3  # one bf16 rounding of an exact-input sum
+    # Unpermute: slot psrc[r] of the output holds row r (bit copy), at every sampled row
+    assert np.array_equal(un_h[psrc[rows]], gy_h[rows])
+    assert normwise_err(un_h[psrc[rows]], ref) <= 8e-3
+    # the whole unpermute is a bijection of rows
+    assert np.array_equal(un_h[psrc], gy_h)
+    # shared expert: e = 1 grouped GEMM == plain GEMM
+    mo = moe.gmm(to_dev(d["mm_x"]), to_dev(d["mm_w"]).view(1, d["H2"], d["N2"]),
+                 to_dev(np.array([0, T], np.int32)))
+    torch.cuda.synchronize()
+    srows = np.random.default_rng(621).choice(T, 12, replace=False).astype(np.int32)
+    sref = oracle.gmm(d["mm_x"], d["mm_w"].reshape(1, d["H2"], d["N2"]), np.array([0, T], np.int32),
+                      rows=srows, nthreads=NTH)
+    assert normwise_err(to_host(mo)[srows], sref) <= 8e-3
+
+
+def test_combine_full_size_prefill():
+    T, E, K, H = 4096, 8, 2, 4096
+    idx = synth.random_routing(630, T, E, K)
+    _, _, psrc, pdst = oracle.permute(idx, E)
+    yp = synth.normal(631, (T * K, H), dtype="bf16")
+    g = np.abs(synth.normal(632, (T, K))).astype(np.float32)
+    g /= g.sum(1, keepdims=True)
+    out = to_host(moe.combine(to_dev(yp), to_dev(pdst), to_dev(g), T, K))
+    ref = oracle.combine(as_f64(yp), pdst, g.astype(np.float64), T, K)
+    assert normwise_err(out, ref) <= 4e-3
