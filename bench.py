@@ -50,7 +50,45 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
+
+
+GMM_SRC = os.path.join(ROOT, "mixture_experts_layer_06_amd", "csrc", "gmm.hip")
+
+
+def source_digest(path=GMM_SRC) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per moe_gmm launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary is
+    missing or was taken on a different gmm.hip."""
+    path = os.path.join(ROOT, "profiles", f"moe_gmm_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("machine: "):
+            rec = json.loads(line[len("machine: "):])
+            if rec.get("gmm_source") == source_digest():
+                return rec.get("traffic_bytes_per_launch")
+    return None
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
 def cpu_threads() -> int:
@@ -169,11 +207,11 @@ def bench_layer(args, dev):
     if hbm_bound:
         achieved = by_launch / (gmm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
     else:
         achieved = fl_launch / (gmm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(args.workload)}
     bytes_stage = {
         "route": T * H * es + H * E * es + T * K * 8,
         "permute": T * K * 4 * 3 + T * H * es + A * H * es,
@@ -195,7 +233,8 @@ def bench_layer(args, dev):
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens)",
         "config": {"workload": workload, "T": T, "H": H, "E": E, "K": K, "F": F,
                    "tokens_per_step": T, "parallelism": "single GPU"},
-        "roofline": dict(roof, kernel="moe_gmm (gmm_tiled_kernel / gmm_stream_kernel)",
+        "roofline": dict(roof, kernel="moe_gmm (" + ("gmm_stream_kernel" if hbm_bound else "gmm_dma_kernel") + ")",
+                         gmm_source=source_digest(),
                          launches_per_step=2, flops_per_launch=fl_launch,
                          bytes_per_launch=by_launch, avg_launch_ms=gmm_ms),
         "moe_gmm_tflops": gmm_tflops,
@@ -282,8 +321,10 @@ def bench_fp8(args, dev):
         "config": {"workload": f"fp8gmm: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
                                f"({T},{H2})x({H2},{N2}) bf16", "tokens_per_step": T},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
-                     "kernel": "moe_gmm E4M3 (gmm_tiled_kernel)", "flops_per_launch": fl,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
+                     "traffic": measured_traffic("fp8gmm"),
+                     "kernel": "moe_gmm E4M3 (gmm_tiled_kernel)", "gmm_source": source_digest(),
+                     "flops_per_launch": fl,
                      "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
         "kernels": {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
                     "unpermute": {"ms": un_ms, "GB/s": 2 * A * N1 * 2 / (un_ms * 1e-3) / 1e9},
@@ -324,6 +365,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import mixture_experts_layer_06_amd as moe
     moe.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
