@@ -233,7 +233,7 @@ def bench_layer(args, dev):
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens)",
         "config": {"workload": workload, "T": T, "H": H, "E": E, "K": K, "F": F,
                    "tokens_per_step": T, "parallelism": "single GPU"},
-        "roofline": dict(roof, kernel="moe_gmm (" + ("gmm_stream_kernel" if hbm_bound else "gmm_dma_kernel") + ")",
+        "roofline": dict(roof, kernel="moe_gmm (" + ("gmm_stream_kernel" if hbm_bound else "gmm_pp_kernel") + ")",
                          gmm_source=source_digest(),
                          launches_per_step=2, flops_per_launch=fl_launch,
                          bytes_per_launch=by_launch, avg_launch_ms=gmm_ms),

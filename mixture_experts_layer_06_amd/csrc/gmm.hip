@@ -37,17 +37,16 @@
 
 #include "common.h"
 
-// bf16 tiled path: 1 = LDS-DMA kernel, 0 = register-staged kernel.
+// bf16 tiled path: 1 = LDS-DMA ping-pong kernel, 0 = register-staged kernel.
 #ifndef MOE_GMM_BF16
 #define MOE_GMM_BF16 1
 #endif
-// Tile / wave layout / ring depth of the bf16 LDS-DMA kernel.
-#ifndef MOE_DMA_BM
-#define MOE_DMA_BM 256
-#define MOE_DMA_BN 256
-#define MOE_DMA_WM 2
-#define MOE_DMA_WN 4
-#define MOE_DMA_STAGES 4
+// Tile / waves along columns / LDS ring slots of the bf16 ping-pong kernel.
+#ifndef MOE_PP_BM
+#define MOE_PP_BM 256
+#define MOE_PP_BN 256
+#define MOE_PP_WN 4
+#define MOE_PP_STAGES 4
 #endif
 // Wave layout of the 256 x 256 tiled kernel (waves along rows x columns).
 #ifndef MOE_TILED_WAVES_M
@@ -577,8 +576,47 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+
+// ------------------------------------------------------------------ ping-pong bf16 kernel
+//
+// 256 x 256 output tile, 8 waves of 128 x 64. The K dimension is walked in
+// 32-wide slices that stream through an S-slot LDS ring filled by
+// buffer_load ... lds (each wave moves an equal share of every slice:
+// activations 256 rows x 64 B, weights 32 rows x 512 B). Weights are read
+// untransposed (8 rows x 4 columns per lane) and transposed in registers, so
+// MFMA row i of fragment j is output column 4i+j and a lane ends with 16
+// consecutive output columns.
+//
+// LDS layout. gfx950 serves a 16-byte-per-lane LDS read over 64 four-byte
+// banks in four passes, each pass taking two groups of 8 lanes (lanes 0-7
+// with 16-23, 8-15 with 24-31, and so on; measured: a pattern that is
+// conflict-free under that pairing reads at the full 256 B/clk, the others
+// at half). An activation fragment read has lane l on row l%16, 16-byte
+// chunk l/16, so one pass covers rows r..r+7 and two adjacent chunks; with
+// 64-byte rows, rows r and r+4 share banks. The chunk index is therefore
+// XORed with (row/2)%4, which gives the four (row, chunk) pairs of each bank
+// group distinct banks. Weight rows (512 B) keep their 128-byte segments
+// XORed with (row/8)%4, so the 8-byte reads of the four 8-row groups of a
+// slice fall in distinct banks.
+//
+// The two row halves of the tile (waves 0-3 and 4-7: one wave of each on
+// every SIMD) run out of phase. Between two barriers one half multiplies a
+// whole K slice while the other reads its next fragments from LDS and issues
+// its share of the DMA; at the barrier they swap, so each SIMD's matrix pipe
+// is fed by one wave while its partner works on memory.
+//
+// Barrier k = 0, 1, ...: the first half reads slice u between barriers 2u
+// and 2u+1 and multiplies it between 2u+1 and 2u+2; the second half reads it
+// between 2u+1 and 2u+2 and multiplies it between 2u+2 and 2u+3. While
+// reading slice u each wave issues its share of slice u+S-1, which goes to
+// the slot of slice u-1, read by both halves before barrier 2u. Slice t must
+// have landed by barrier 2t: each wave waits for its share of t, leaving the
+// shares of t+1 .. t+S-2 in flight. Barriers and the ring never depend on
+// data, so a wave whose part of the tile is empty runs the same schedule
+// without reads or multiplies.
+
 template <int BM, int BN, int WM_, int WN_, int STAGES>
-struct DmaCfg {
+struct PpCfg {
   static constexpr int kStages = STAGES;
   static constexpr int kBM = BM, kBN = BN;
   static constexpr int kSegMask = (BN * 2) / 128 - 1;  // 128-byte segments per weight row - 1
@@ -587,37 +625,43 @@ struct DmaCfg {
   static constexpr int kWM = BM / WM_, kWN = BN / WN_;
   static constexpr int kFI = kWM / 16;   // 16-row activation fragments per wave
   static constexpr int kFG = kWN / 64;   // 64-column weight groups per wave
-  static constexpr int kLdsA = BM * kDmaKB;        // bytes of activations per stage
-  static constexpr int kLdsW = 32 * BN * 2;        // bytes of weights per stage
+  static constexpr int kLdsA = BM * kDmaKB;        // bytes of activations per slot
+  static constexpr int kLdsW = 32 * BN * 2;        // bytes of weights per slot
   static constexpr int kStage = kLdsA + kLdsW;
   static constexpr int kLds = STAGES * kStage;
-  static constexpr int kADma = kLdsA / 1024 / (kNT / 64);  // KB-sized DMA ops per wave per stage
+  static constexpr int kADma = kLdsA / 1024 / (kNT / 64);  // 1 KB DMA ops per wave per slot
   static constexpr int kWDma = kLdsW / 1024 / (kNT / 64);
-  static constexpr int kPerStage = kADma + kWDma;          // vmcnt units per stage per thread
+  static constexpr int kPerStage = kADma + kWDma;          // vmcnt units per slot per lane
   static_assert(kLdsA % (1024 * (kNT / 64)) == 0 && kLdsW % (1024 * (kNT / 64)) == 0, "dma split");
   static_assert(kWN % 64 == 0, "weight groups");
-  static_assert(STAGES >= 3 && STAGES <= 4, "ring depth");
+  static_assert(WM_ == 2, "two row halves");
+  static_assert(STAGES >= 3 && (STAGES - 2) * kPerStage <= 63, "ring depth");
+  static_assert(kLds >= 2 * 257 * 4, "tile prefix lives in the ring");
 };
 
-// Two waves per SIMD: caps registers at 256 per lane, which also keeps the
-// accumulators in VGPRs (left to itself with one wave per SIMD the compiler
-// parks them in AGPRs and copies them back and forth every K slice).
 template <class C>
-__global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) void gmm_dma_kernel(
+__global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
     bf16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ int s_off[257];
-  __shared__ int s_pre[257];
-  load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_pre);
+  // The ring takes all of LDS; the tile prefix borrows its first bytes
+  // before any DMA is issued.
+  {
+    int* s_off = reinterpret_cast<int*>(smem);
+    int* s_pre = s_off + 257;
+    load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_pre);
+  }
   Tile tile;
-  if (!pick_tile<C::kBM, C::kBN, 8>(s_off, s_pre, e, N, tile)) return;
+  if (!pick_tile<C::kBM, C::kBN, 8>(reinterpret_cast<const int*>(smem),
+                                     reinterpret_cast<const int*>(smem) + 257, e, N, tile))
+    return;
+  __syncthreads();  // every lane has its tile before the ring overwrites the prefix
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
   const int hin_b = Hin * 2;
   const int n_b = N * 2;
@@ -627,56 +671,56 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
   const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * n_b, (uint32_t)Hin * (uint32_t)n_b);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // ---- DMA descriptors: which global bytes this lane fetches for each KB it fills
+  // ---- DMA: which global bytes this lane fetches for each KB of a slot it fills
   uint32_t a_voff[C::kADma];
   uint32_t a_kc[C::kADma];
 #pragma unroll
   for (int q = 0; q < C::kADma; ++q) {
-    const int kb = (wave * C::kADma + q) * 1024 + lane * 16;  // byte within the stage's A part
+    const int kb = (wave * C::kADma + q) * 1024 + lane * 16;  // byte within the slot's activations
     const int row = kb >> 6, pc = (kb >> 4) & 3;
-    const int lc = pc ^ ((row >> 2) & 3);
+    const int lc = pc ^ ((row >> 1) & 3);
     a_voff[q] = (uint32_t)row * (uint32_t)hin_b + lc * 16;
     a_kc[q] = lc * 16;
   }
   uint32_t w_voff[C::kWDma];
 #pragma unroll
   for (int q = 0; q < C::kWDma; ++q) {
-    const int kb = (wave * C::kWDma + q) * 1024 + lane * 16;  // byte within the stage's W part
+    const int kb = (wave * C::kWDma + q) * 1024 + lane * 16;  // byte within the slot's weights
     const int k = kb / (C::kBN * 2), pb = kb % (C::kBN * 2);
     const int lseg = (pb >> 7) ^ ((k >> 3) & C::kSegMask);
     const int lb = (lseg << 7) + (pb & 127);
     w_voff[q] = (uint32_t)k * (uint32_t)n_b + (uint32_t)(n0b + lb) + (n0b + lb < n_b ? 0u : kOOB);
   }
+  // Past-the-end slices are issued too (out-of-range loads write zeros), so
+  // every wait count is fixed.
   auto issue = [&](int step) {
     const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
     const int kb0 = step * kDmaKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
       dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < hin_b ? 0u : kOOB),
-            __builtin_amdgcn_readfirstlane(base + (wave * C::kADma + q) * 1024));
+            base + (wave * C::kADma + q) * 1024);
     const uint32_t kstep = step < nsteps ? (uint32_t)(step * 32) * (uint32_t)n_b : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
-      dma16(wsrd, w_voff[q] + kstep,
-            __builtin_amdgcn_readfirstlane(base + C::kLdsA + (wave * C::kWDma + q) * 1024));
+      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
   };
-
-  f32x4_t acc[C::kFI][C::kFG][4];
-#pragma unroll
-  for (int i = 0; i < C::kFI; ++i)
-#pragma unroll
-    for (int g = 0; g < C::kFG; ++g)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][g][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  // The compiler may not move work across these barriers: the phases are the schedule.
+  auto bar = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int S = C::kStages;
+  constexpr int kInFlight = (S - 2) * C::kPerStage;  // a wave's ops still landing at a wait
 
   const bool wave_active = (wm * C::kWM < tile.rows) && (tile.n0 + wn * C::kWN < N);
   const int ci = lane & 15, kq = lane >> 4;
-  // per-lane LDS read offsets within a stage
   int xoff[C::kFI];
 #pragma unroll
   for (int i = 0; i < C::kFI; ++i) {
     const int m = wm * C::kWM + i * 16 + ci;
-    xoff[i] = m * kDmaKB + ((kq ^ ((m >> 2) & 3)) << 4);
+    xoff[i] = m * kDmaKB + ((kq ^ ((m >> 1) & 3)) << 4);
   }
   int woff[C::kFG];
 #pragma unroll
@@ -684,15 +728,12 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int cb = (wn * C::kWN + g * 64 + 4 * ci) * 2;  // byte of this lane's 4 columns
     woff[g] = C::kLdsA + (kq * 8) * (C::kBN * 2) + (((cb >> 7) ^ (kq & C::kSegMask)) << 7) + (cb & 127);
   }
-
-  // Fragment registers, one set. Activation fragment i of slice s+1 is read
-  // into the registers of fragment i of slice s right after the last MFMA
-  // that uses them, so each LDS read overlaps the rest of the slice's MFMAs.
-  // The weight fragments are read and transposed after the multiplies.
   bf16x8_t xa[C::kFI];
   uint4 wc[C::kFG][4];
-  auto read_w = [&](int slice) {
-    const unsigned char* st = smem + (slice % C::kStages) * C::kStage;
+  auto read_frags = [&](int slice) {
+    const unsigned char* st = smem + (slice % S) * C::kStage;
+#pragma unroll
+    for (int i = 0; i < C::kFI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(st + xoff[i]);
 #pragma unroll
     for (int g = 0; g < C::kFG; ++g) {
       uint2 wraw[8];
@@ -701,44 +742,83 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
       transpose_8x4_bf16(wraw, wc[g]);
     }
   };
-  // Slice s: wait for slice s+1's DMA (the S-3 newer slices may stay in
-  // flight), barrier, refill the slot slice s-1 used, multiply slice s while
-  // reading slice s+1. Past-the-end slices are issued too (out-of-range
-  // loads write zeros), so every wait count is fixed.
-  auto step_fn = [&](int step) {
-    wait_vmcnt<(C::kStages - 3) * C::kPerStage>();
-    __syncthreads();
-    issue(step + C::kStages - 1);
-    if (wave_active) {
-      const unsigned char* nx = smem + ((step + 1) % C::kStages) * C::kStage;
+  f32x4_t acc[C::kFI][C::kFG][4];
 #pragma unroll
-      for (int i = 0; i < C::kFI; ++i) {
+  for (int i = 0; i < C::kFI; ++i)
 #pragma unroll
-        for (int g = 0; g < C::kFG; ++g)
+    for (int g = 0; g < C::kFG; ++g)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                *reinterpret_cast<bf16x8_t*>(&wc[g][j]), xa[i], acc[i][g][j], 0, 0, 0);
-        xa[i] = *reinterpret_cast<const bf16x8_t*>(nx + xoff[i]);
-      }
-      read_w(step + 1);
-    }
+      for (int j = 0; j < 4; ++j) acc[i][g][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  auto multiply = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::kFI; ++i)
+#pragma unroll
+      for (int g = 0; g < C::kFG; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<bf16x8_t*>(&wc[g][j]), xa[i], acc[i][g][j], 0, 0, 0);
   };
 
 #pragma unroll
-  for (int s = 0; s < C::kStages - 1; ++s) issue(s);
-  wait_vmcnt<(C::kStages - 2) * C::kPerStage>();
-  __syncthreads();
-  if (wave_active) {
-    const unsigned char* st = smem;
-#pragma unroll
-    for (int i = 0; i < C::kFI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(st + xoff[i]);
-    read_w(0);
+  for (int t = 0; t < S - 1; ++t) issue(t);
+  wait_vmcnt<kInFlight>();
+  bar();  // barrier 0: slice 0 has landed
+  // Four straight-line loops (half x active), each with the same barriers and
+  // DMA as its partner, so no loop carries a branch.
+  if (wm == 0) {
+    if (wave_active) {
+      read_frags(0);
+      issue(S - 1);
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        multiply();
+        wait_vmcnt<kInFlight>();
+        bar();
+        read_frags(s + 1);
+        issue(s + S);
+        bar();
+      }
+    } else {
+      issue(S - 1);
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        wait_vmcnt<kInFlight>();
+        bar();
+        issue(s + S);
+        bar();
+      }
+    }
+    bar();  // matches the second half's last barrier
+  } else {
+    bar();
+    issue(S - 1);
+    if (wave_active) {
+      read_frags(0);
+      wait_vmcnt<kInFlight>();
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        multiply();
+        bar();
+        read_frags(s + 1);
+        issue(s + S);
+        wait_vmcnt<kInFlight>();
+        bar();
+      }
+    } else {
+      wait_vmcnt<kInFlight>();
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        bar();
+        issue(s + S);
+        wait_vmcnt<kInFlight>();
+        bar();
+      }
+    }
   }
-  for (int step = 0; step < nsteps; ++step) step_fn(step);
   wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
-
   if (!wave_active) return;
+
   const float sc = ld_scale(a_scale) * ld_scale(w_scale);
 #pragma unroll
   for (int i = 0; i < C::kFI; ++i) {
@@ -749,6 +829,7 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int g = 0; g < C::kFG; ++g) {
       // MFMA j, output row 4*kq + r  ->  column nb + 4r + j
       const int nb = tile.n0 + wn * C::kWN + g * 64 + 16 * kq;
+      if (nb >= N) continue;  // N is a multiple of 16 here: a lane's 16 columns are all in or all out
       float v[16];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -758,16 +839,10 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
           v[4 * r + j] = (relu && t < 0.f) ? 0.f : t;
         }
       bf16_t* o = out + m * N + nb;
-      if (nb + 15 < N) {
-        reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-        reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
-                                                    pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (nb + q < N) o[q] = f32_to_bf16(v[q]);
-      }
+      reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                                                  pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
     }
   }
 }
@@ -942,12 +1017,12 @@ moe_status launch_tiled(const void* a, const float* as, const void* w, const flo
 }
 
 template <class C>
-moe_status launch_dma(const void* a, const float* as, const void* w, const float* ws,
-                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                      hipStream_t s) {
+moe_status launch_pp(const void* a, const float* as, const void* w, const float* ws,
+                     const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
+                     hipStream_t s) {
   static bool attr_done = false;
   if (!attr_done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_dma_kernel<C>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp_kernel<C>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     attr_done = true;
   }
@@ -955,7 +1030,7 @@ moe_status launch_dma(const void* a, const float* as, const void* w, const float
   const int64_t blocks = mt_max * cdiv64(N, C::kBN);
   const int64_t grid = cdiv64(blocks, 8) * 8;
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL(gmm_dma_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
+  hipLaunchKernelGGL(gmm_pp_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
                      (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
                      relu, (bf16_t*)out);
   return launch_status();
@@ -1011,8 +1086,8 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
   constexpr int WM = MOE_TILED_WAVES_M, WN = MOE_TILED_WAVES_N;
 #if MOE_GMM_BF16 == 1
   if (elem == 2 && al && N % 16 == 0) {
-    typedef DmaCfg<MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_STAGES> CD;
-    return launch_dma<CD>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+    typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
+    return launch_pp<CP>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
   }
 #endif
   if (elem == 2) {
