@@ -148,11 +148,13 @@ def bench_layer(args, dev):
     y = torch.empty((T, H), dtype=tdt, device=dev)
     pws_n = moe.permute_workspace_size(T, E, K)
     pws = torch.empty((max(pws_n, 16),), dtype=torch.uint8, device=dev)
+    rws_n = moe.route_workspace_size(T, H, E, K, moe.dtype_code(x))
+    rws = torch.empty((max(rws_n, 16),), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        moe.route(x, wr, K, bias=bias, topk_idx=idx, topk_gate=gate)
+        moe.route(x, wr, K, bias=bias, topk_idx=idx, topk_gate=gate, ws=rws)
         if ev is not None:
             ev[1].record()
         moe.permute(idx, E, x=x, ws=pws, out=bufs)

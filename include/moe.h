@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10000 /* 1.0.0 */
+#define MOE_VERSION 10100 /* 1.1.0: moe_route takes a workspace */
 
 typedef enum {
   MOE_OK = 0,
@@ -96,10 +96,15 @@ int moe_version(void);
  *   topk_idx device (T,K) int32 out        experts by descending score; equal
  *                                          scores -> lower expert index first
  *   topk_gate device (T,K) fp32 out        g_k = exp(l_k - l_0) / sum_j exp(l_j - l_0)
+ *   ws, ws_bytes device scratch of at least moe_route_workspace_size() bytes
+ *                (may be NULL when that size is 0; with few tokens the router
+ *                splits H over several blocks and keeps partial scores there)
  * Scores are accumulated in fp32. T = 0 is a no-op.
  */
+moe_status moe_route_workspace_size(int T, int H, int E, int K, moe_dtype dt, size_t* bytes);
 moe_status moe_route(const void* x, const void* w_router, moe_dtype dt, const float* bias, int T,
-                     int H, int E, int K, int32_t* topk_idx, float* topk_gate, void* stream);
+                     int H, int E, int K, int32_t* topk_idx, float* topk_gate, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /*
  * moe_permute — dispatch: per-expert counts, their exclusive scan, and a

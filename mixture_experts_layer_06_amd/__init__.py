@@ -25,8 +25,9 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 QUANT_NONE, QUANT_PER_TENSOR = 0, 1
 ACT_NONE, ACT_RELU = 0, 1
 
-EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_permute_workspace_size",
-           "moe_permute", "moe_gmm", "moe_combine", "moe_layer_workspace_size", "moe_layer")
+EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
+           "moe_permute_workspace_size", "moe_permute", "moe_gmm", "moe_combine",
+           "moe_layer_workspace_size", "moe_layer")
 
 
 class MoeError(RuntimeError):
@@ -51,7 +52,8 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_version.argtypes = []
         L.moe_version.restype = i32
-        L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_route_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         L.moe_permute_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_permute.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_gmm.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, vp,
@@ -106,16 +108,28 @@ def _empty(shape, dtype, like):
 
 # ---------------------------------------------------------------- entry points
 
-def route(x, w_router, K, bias=None, topk_idx=None, topk_gate=None, stream=None):
-    """moe_route. Returns (topk_idx int32 (T,K), topk_gate fp32 (T,K))."""
+def route_workspace_size(T, H, E, K, dt) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_route_workspace_size(T, H, E, K, dt, ctypes.byref(n)), "moe_route_workspace_size")
+    return n.value
+
+
+def route(x, w_router, K, bias=None, topk_idx=None, topk_gate=None, ws=None, stream=None):
+    """moe_route. Returns (topk_idx int32 (T,K), topk_gate fp32 (T,K)). ws: a device
+    buffer of at least route_workspace_size() bytes, allocated here when None."""
     T, H = x.shape
     E = w_router.shape[1]
+    dt = dtype_code(x)
     if topk_idx is None:
         topk_idx = _empty((T, K), torch.int32, x)
     if topk_gate is None:
         topk_gate = _empty((T, K), torch.float32, x)
-    st = lib().moe_route(_ptr(x), _ptr(w_router), dtype_code(x), _ptr(bias), T, H, E, K,
-                         _ptr(topk_idx), _ptr(topk_gate), _stream(stream))
+    if ws is None:
+        n = route_workspace_size(T, H, E, K, dt)
+        ws = _empty((n,), torch.uint8, x) if n else None
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib().moe_route(_ptr(x), _ptr(w_router), dt, _ptr(bias), T, H, E, K,
+                         _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), nbytes, _stream(stream))
     _check(st, "moe_route")
     return topk_idx, topk_gate
 

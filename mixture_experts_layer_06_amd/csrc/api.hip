@@ -59,7 +59,9 @@ LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
   L.pdst = o; o += round256(A * 4);
   L.perm_ws = o; o += round256(permute_ws_bytes(T, E, K));
   L.xp = o; o += round256((size_t)A * H * es);  // permuted rows; reused for GEMM 2 output
-  L.hm = o; o += round256((size_t)A * F * es);  // hidden activations
+  // hidden activations; before GEMM 1 writes them the router's split-H partials live here
+  const size_t hm = (size_t)A * F * es, rws = route_ws_bytes(T, H, E, dt);
+  L.hm = o; o += round256(hm > rws ? hm : rws);
   L.total = o;
   return L;
 }
@@ -84,8 +86,17 @@ const char* moe_status_string(moe_status s) {
 
 int moe_version(void) { return MOE_VERSION; }
 
+moe_status moe_route_workspace_size(int T, int H, int E, int K, moe_dtype dt, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
+  MOE_TRY(check_route_shape(T, H, E, K));
+  *bytes = route_ws_bytes(T, H, E, dt);
+  return MOE_OK;
+}
+
 moe_status moe_route(const void* x, const void* w_router, moe_dtype dt, const float* bias, int T,
-                     int H, int E, int K, int32_t* topk_idx, float* topk_gate, void* stream) {
+                     int H, int E, int K, int32_t* topk_idx, float* topk_gate, void* ws,
+                     size_t ws_bytes, void* stream) {
   if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
   MOE_TRY(check_route_shape(T, H, E, K));
   if (T == 0) return MOE_OK;
@@ -93,12 +104,18 @@ moe_status moe_route(const void* x, const void* w_router, moe_dtype dt, const fl
   REQUIRE_PTR(w_router);
   REQUIRE_PTR(topk_idx);
   REQUIRE_PTR(topk_gate);
+  const size_t need = route_ws_bytes(T, H, E, dt);
+  if (need > 0) {
+    REQUIRE_PTR(ws);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
   REQUIRE_ALIGNED(x);
   REQUIRE_ALIGNED(w_router);
   REQUIRE_ALIGNED(bias);
   REQUIRE_ALIGNED(topk_idx);
   REQUIRE_ALIGNED(topk_gate);
-  return launch_route(x, w_router, dt, bias, T, H, E, K, topk_idx, topk_gate, (hipStream_t)stream);
+  REQUIRE_ALIGNED(ws);
+  return launch_route(x, w_router, dt, bias, T, H, E, K, topk_idx, topk_gate, ws, (hipStream_t)stream);
 }
 
 moe_status moe_permute_workspace_size(int T, int E, int K, size_t* bytes) {
@@ -235,7 +252,7 @@ moe_status moe_layer(const void* x, const void* w_router, const float* bias, con
   void* xp = base + L.xp;
   void* hm = base + L.hm;
   const int A = T * K;
-  MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, s));
+  MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s));
   MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
   MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, s));
   MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, s));

@@ -5,8 +5,10 @@
 //  unweighted: out[t*K+k] = y_perm[perm_dst[t*K+k]]
 //            (unpermuteOut = Unpermute(gmmY), "aclnnQuantGroupedMatMulAlltoAllv",
 //            section 计算公式).
-// Both are pure bandwidth kernels: one block per output token, 16-byte
-// vector accesses when the row pitch allows, every input row read once.
+// Both are pure bandwidth kernels: blocks over (output token, column
+// stripe), 16-byte vector accesses when the row pitch allows, every input
+// row read once. Few tokens (decode) get several column stripes per token,
+// so that each thread issues the loads of all K rows of one vector at once.
 #include "common.h"
 
 namespace moe {
@@ -29,7 +31,7 @@ __global__ __launch_bounds__(256) void combine_weighted_kernel(const void* __res
       src[k] = k < K ? perm_dst[(int64_t)t * K + k] : 0;
       g[k] = k < K ? gate[(int64_t)t * K + k] : 0.f;
     }
-    for (int j = threadIdx.x; j < nv; j += blockDim.x) {
+    for (int j = blockIdx.y * blockDim.x + threadIdx.x; j < nv; j += gridDim.y * blockDim.x) {
       float acc[VE];
 #pragma unroll
       for (int q = 0; q < VE; ++q) acc[q] = 0.f;
@@ -85,7 +87,8 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const unsigned char* __r
       const int64_t i = (int64_t)t * K + k;
       const V* src = reinterpret_cast<const V*>(yp + (int64_t)perm_dst[i] * row_bytes);
       V* dst = reinterpret_cast<V*>(out + i * row_bytes);
-      for (int64_t j = threadIdx.x; j < nv; j += blockDim.x) dst[j] = src[j];
+      for (int64_t j = blockIdx.y * blockDim.x + threadIdx.x; j < nv; j += gridDim.y * blockDim.x)
+        dst[j] = src[j];
     }
   }
 }
@@ -95,8 +98,15 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const unsigned char* __r
 moe_status launch_combine(const void* y_perm, moe_dtype dt, const int32_t* perm_dst,
                           const float* gate, int T, int K, int N, void* out, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  const int grid = T < 65536 ? T : 65536;
   const bool bf = dt == MOE_BF16;
+  // column stripes per token: one 256-vector stripe per block when tokens are few
+  const int64_t vecs = gate ? (bf ? N / 8 : N / 4) : (int64_t)N * (bf ? 2 : 4) / 16;
+  int stripes = 1;
+  if (T < 2048) {
+    const int64_t st = (vecs + 255) / 256;
+    stripes = st < 1 ? 1 : (st > 64 ? 64 : (int)st);
+  }
+  const dim3 grid(T < 65536 ? T : 65536, stripes);
   if (gate) {
     if (bf) {
       if (N % 8 == 0)

@@ -38,6 +38,40 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// bf16: rows r0..r7 of 4 columns (uint2 each) -> 4 columns of 8 rows (uint4 each).
+__device__ __forceinline__ void transpose_8x4_bf16(const uint2 in[8], uint4 out[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = (c >> 1) ? in[2 * p].y : in[2 * p].x;
+      const uint32_t b = (c >> 1) ? in[2 * p + 1].y : in[2 * p + 1].x;
+      d[p] = perm_b32(b, a, sel);
+    }
+    out[c] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer, 32-bit data format; loads at offsets >= bytes return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset bias that puts a load out of range
+
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -50,8 +84,9 @@ inline moe_status launch_status() {
 }
 
 // Launchers implemented by the kernel files. They assume validated arguments.
+size_t route_ws_bytes(int T, int H, int E, moe_dtype dt);
 moe_status launch_route(const void* x, const void* wr, moe_dtype dt, const float* bias, int T, int H,
-                        int E, int K, int32_t* idx, float* gate, hipStream_t s);
+                        int E, int K, int32_t* idx, float* gate, void* ws, hipStream_t s);
 size_t permute_ws_bytes(int T, int E, int K);
 moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T, int H, int E, int K,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,

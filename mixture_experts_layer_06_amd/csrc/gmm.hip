@@ -59,16 +59,6 @@ namespace {
 
 // ------------------------------------------------------------------ helpers
 
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
-
 // Expert offsets (clamped to [0, A]) and the running count of row tiles per
 // expert, in LDS: s_off[0..e], s_pre[0..e] (s_pre[q] = tiles before expert q).
 template <int BM>
@@ -200,22 +190,6 @@ __device__ __forceinline__ uint2 ld8(const unsigned char* p, int avail) {
   return make_uint2(w[0], w[1]);
 }
 
-// bf16: rows r0..r7 of 4 columns (uint2 each) -> 4 columns of 8 rows (uint4 each).
-__device__ __forceinline__ void transpose_8x4_bf16(const uint2 in[8], uint4 out[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t d[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = (c >> 1) ? in[2 * p].y : in[2 * p].x;
-      const uint32_t b = (c >> 1) ? in[2 * p + 1].y : in[2 * p + 1].x;
-      d[p] = perm_b32(b, a, sel);
-    }
-    out[c] = make_uint4(d[0], d[1], d[2], d[3]);
-  }
-}
-
 // E4M3: rows r0..r7 of 8 columns (uint2 each, one byte per column) ->
 // 8 columns of 8 rows (uint2 each, one byte per row).
 __device__ __forceinline__ void transpose_8x8_u8(const uint2 in[8], uint2 out[8]) {
@@ -257,12 +231,6 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return r * kRowB + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer, 32-bit data format; loads at offsets >= bytes return zero
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-constexpr uint32_t kOOB = 0x80000000u;  // offset bias that puts a load out of range
 
 template <int ELEM, int BM, int BN, int WM_, int WN_, bool AL, bool OUT_F32>
 struct TiledCfg {

@@ -9,10 +9,14 @@
 // the expert id bits) plus ordered per-chunk prefix sums, never from the
 // order in which atomics happen to land, so the result is deterministic.
 //
-// Index path, A = T*K pairs cut into chunks of kChunk:
-//   small A (<= kSmallA): one wave does count, scan and rank in one launch;
-//   otherwise: count per chunk (LDS histogram) -> one-block scan over
-//   (chunk, expert) -> per-chunk rank and write.
+// Index path, A = T*K pairs:
+//   A <= kBlockA: one block of up to 16 waves, one launch. Wave w owns the
+//   contiguous segment w of the pairs: it counts its segment per expert, a
+//   prefix over (wave, expert) gives every wave its first row per expert,
+//   and each wave ranks its own segment in order;
+//   otherwise: the same three steps over chunks of kChunk pairs in three
+//   launches (count per chunk -> one-block scan over (chunk, expert) ->
+//   per-chunk rank and write).
 // Data path: one block per token reads its row once (16-byte vectors when
 // the row pitch allows) and writes it to its K destination rows.
 #include "common.h"
@@ -21,7 +25,8 @@ namespace moe {
 namespace {
 
 constexpr int kChunk = 1024;   // pairs per chunk
-constexpr int kSmallA = 4096;  // single-wave path up to this many pairs
+constexpr int kBlockA = 16384;  // one-block path up to this many pairs
+constexpr int kBlockWaves = 16;
 
 __device__ __forceinline__ int clamp_e(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
@@ -65,34 +70,67 @@ __device__ __forceinline__ void rank_range(const int32_t* __restrict__ idx, int 
   }
 }
 
-// Single wave: whole index path for small A.
-__global__ __launch_bounds__(64) void permute_small_kernel(const int32_t* __restrict__ idx, int A,
-                                                           int E, int32_t* __restrict__ counts,
-                                                           int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ perm_src,
-                                                           int32_t* __restrict__ perm_dst) {
-  __shared__ int hist[256];
-  __shared__ int run[256];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < 256; e += kWave) hist[e] = 0;
+// One block: whole index path for A <= kBlockA (see the file header).
+__global__ __launch_bounds__(kBlockWaves * kWave) void permute_block_kernel(
+    const int32_t* __restrict__ idx, int A, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ perm_dst) {
+  __shared__ int hist[kBlockWaves][256];  // count, then first row, per (wave, expert)
+  __shared__ int tot[256];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const int seg = cdiv(A, nw);
+  const int begin = min(A, w * seg), end = min(A, begin + seg);
+  int* mine = hist[w];
+  for (int e = lane; e < 256; e += kWave) mine[e] = 0;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  for (int base = begin; base < end; base += kWave) {
+    const int i = base + lane;
+    const bool valid = i < end;
+    const int e = valid ? clamp_e(idx[i], E) : 0;
+    const uint64_t m = match_mask(e, valid);
+    // the highest lane of each group of equal experts adds the group's size
+    if (valid && (m >> lane) == 1ull) mine[e] += __popcll(m);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
   __syncthreads();
-  for (int i = lane; i < A; i += kWave) atomicAdd(&hist[clamp_e(idx[i], E)], 1);
-  __syncthreads();
-  // exclusive scan of hist[0:E] by lane 0 (E <= 256: a short serial loop)
-  if (lane == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      run[e] = acc;
-      acc += hist[e];
+  // thread e: prefix over waves (segment order), total per expert
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int q = 0; q < nw; ++q) {
+      const int v = hist[q][e];
+      hist[q][e] = run;
+      run += v;
     }
+    tot[e] = run;
   }
   __syncthreads();
-  for (int e = lane; e < E; e += kWave) {
-    counts[e] = hist[e];
-    offsets[e] = run[e];
+  // exclusive scan over experts by wave 0 (4 consecutive experts per lane)
+  if (w == 0) {
+    int c[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      c[j] = e < E ? tot[e] : 0;
+      local += c[j];
+    }
+    int run = wave_incl_scan(local) - local;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      if (e < E) {
+        counts[e] = c[j];
+        offsets[e] = run;
+        tot[e] = run;
+      }
+      run += c[j];
+    }
+    if (lane == 0) offsets[E] = A;
   }
-  if (lane == 0) offsets[E] = A;
-  rank_range(idx, 0, A, E, run, perm_src, perm_dst);
+  __syncthreads();
+  for (int e = lane; e < E; e += kWave) mine[e] += tot[e];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  rank_range(idx, begin, end, E, mine, perm_src, perm_dst);
 }
 
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx, int A,
@@ -181,7 +219,7 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const unsigned char* 
 
 size_t permute_ws_bytes(int T, int E, int K) {
   const int64_t A = (int64_t)T * K;
-  if (A <= kSmallA) return 0;
+  if (A <= kBlockA) return 0;
   const int64_t nch = cdiv64(A, kChunk);
   return (size_t)(2 * nch * E * sizeof(int32_t));
 }
@@ -190,9 +228,12 @@ moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
                           void* x_perm, void* ws, hipStream_t s) {
   const int A = T * K;
-  if (A <= kSmallA) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(64), 0, s, idx, A, E, counts, offsets,
-                       perm_src, perm_dst);
+  if (A <= kBlockA) {
+    // about 256 pairs per wave, at most kBlockWaves waves
+    int nw = cdiv(A, 256);
+    nw = nw < 1 ? 1 : (nw > kBlockWaves ? kBlockWaves : nw);
+    hipLaunchKernelGGL(permute_block_kernel, dim3(1), dim3(nw * kWave), 0, s, idx, A, E, counts,
+                       offsets, perm_src, perm_dst);
   } else {
     const int nch = cdiv(A, kChunk);
     int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);

@@ -23,8 +23,8 @@ def declared_entry_points():
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
     for n in ("moe_route", "moe_permute", "moe_gmm", "moe_combine", "moe_layer",
-              "moe_permute_workspace_size", "moe_layer_workspace_size", "moe_status_string",
-              "moe_version"):
+              "moe_route_workspace_size", "moe_permute_workspace_size", "moe_layer_workspace_size",
+              "moe_status_string", "moe_version"):
         assert n in names
 
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10000
+    assert moe.lib().moe_version() == 10100
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -54,8 +54,26 @@ def _lib():
     L = moe.lib()
 
 
-def route(x=P, wr=P, dt=moe.BF16, bias=None, T=16, H=64, E=8, K=2, idx=P, gate=P):
-    return L.moe_route(x, wr, dt, bias, T, H, E, K, idx, gate, None)
+def route(x=P, wr=P, dt=moe.BF16, bias=None, T=16, H=64, E=8, K=2, idx=P, gate=P, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        try:
+            ws_bytes = moe.route_workspace_size(T, H, E, K, dt)
+        except moe.MoeError:
+            ws_bytes = 0
+    return L.moe_route(x, wr, dt, bias, T, H, E, K, idx, gate, ws, ws_bytes, None)
+
+
+def test_route_workspace_size():
+    # few token tiles: H is split over blocks, partial scores need scratch
+    assert moe.route_workspace_size(16, 4096, 128, 8, moe.BF16) > 0
+    assert moe.route_workspace_size(256, 4096, 128, 8, moe.BF16) >= 256 * 128 * 4 * 2
+    # enough token tiles, or fp32: no scratch
+    assert moe.route_workspace_size(4096, 4096, 8, 2, moe.BF16) == 0
+    assert moe.route_workspace_size(16, 4096, 128, 8, moe.F32) == 0
+    assert moe.route_workspace_size(0, 4096, 128, 8, moe.BF16) == 0
+    with pytest.raises(moe.MoeError) as ei:
+        moe.route_workspace_size(16, 4096, 300, 8, moe.BF16)
+    assert ei.value.status == moe.ERR_BAD_SHAPE
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -70,6 +88,9 @@ def route(x=P, wr=P, dt=moe.BF16, bias=None, T=16, H=64, E=8, K=2, idx=P, gate=P
     (dict(K=9, E=16), moe.ERR_BAD_SHAPE),
     (dict(K=16, E=256, T=1024, H=128), moe.ERR_BAD_SHAPE),  # SpMM page's example shape: top-16
     (dict(K=5, E=4), moe.ERR_BAD_SHAPE),
+    (dict(H=4096, E=128, ws=None), moe.ERR_NULL_POINTER),       # split-H router needs scratch
+    (dict(H=4096, E=128, ws_bytes=16), moe.ERR_WORKSPACE_TOO_SMALL),
+    (dict(H=4096, E=128, ws=MIS), moe.ERR_MISALIGNED),
     (dict(T=52428800 // 2, K=2), moe.ERR_BAD_SHAPE),
     (dict(x=None), moe.ERR_NULL_POINTER),
     (dict(wr=None), moe.ERR_NULL_POINTER),
@@ -87,7 +108,7 @@ def test_route_empty_batch_is_noop_without_pointers():
     assert route(x=None, wr=None, idx=None, gate=None, T=0) == moe.OK
 
 
-def permute(idx=P, x=P, dt=moe.BF16, T=2000, H=64, E=8, K=4, counts=P, offsets=P, psrc=P, pdst=P,
+def permute(idx=P, x=P, dt=moe.BF16, T=5000, H=64, E=8, K=4, counts=P, offsets=P, psrc=P, pdst=P,
             xp=P, ws=P, ws_bytes=None):
     if ws_bytes is None:
         try:
@@ -99,6 +120,8 @@ def permute(idx=P, x=P, dt=moe.BF16, T=2000, H=64, E=8, K=4, counts=P, offsets=P
 
 def test_permute_workspace_size_small_and_chunked():
     assert moe.permute_workspace_size(16, 128, 8) == 0
+    assert moe.permute_workspace_size(4096, 8, 4) == 0    # 16384 pairs: one block, no scratch
+    assert moe.permute_workspace_size(4097, 8, 4) > 0     # chunked
     n = moe.permute_workspace_size(16384, 64, 6)
     assert n >= 2 * 96 * 64 * 4
 

@@ -38,6 +38,15 @@ ROUTE_CASES = [
     ("decode_like", 64, 4096, 128, 8, "bf16", False, False),
     ("k1", 50, 64, 16, 1, "bf16", False, False),
     ("k_eq_e", 33, 96, 4, 4, "f32", False, False),
+    # one case per router kernel instance: 64-expert groups 1/2/4, aligned or not
+    ("prefill_like", 48, 4096, 8, 2, "bf16", False, False),
+    ("e128_int_ties", 40, 256, 128, 8, "bf16", True, False),
+    ("e100_ragged_bias", 50, 90, 100, 4, "bf16", False, True),
+    ("e200_ragged", 20, 70, 200, 3, "bf16", False, False),
+    # many token tiles, aligned or not; H split with ragged rows
+    ("t16400_bias", 16400, 64, 40, 3, "bf16", False, True),
+    ("t16400_ragged", 16400, 65, 40, 2, "bf16", False, False),
+    ("split_ragged_bias", 30, 1001, 60, 4, "bf16", False, True),
 ]
 
 
@@ -94,6 +103,21 @@ def test_permute_chunked_path_skewed_with_empty_experts():
     idx[idx % 7 == 3] = 1       # more skew
     x = synth.normal(104, (T, 72), dtype="bf16")
     _check_permute_bitexact(idx, E, x)
+
+
+@pytest.mark.parametrize("T,E,K,skew", [
+    (1250, 256, 4, False),   # 5000 pairs: 16 waves, ragged last segment, E = 256
+    (513, 33, 3, True),      # 1539 pairs: 7 waves, empty experts
+    (4096, 4, 4, False),     # 16384 pairs: the largest one-block case, long equal runs
+    (4097, 4, 4, False),     # 16388 pairs: the smallest chunked case
+    (2048, 128, 8, False),   # decode T=256-like pair count x 8
+])
+def test_permute_block_and_chunked_boundary(T, E, K, skew):
+    idx = synth.random_routing(106 + T, T, E, K)
+    if skew:
+        idx[idx >= E - 5] = 1
+        idx[: T // 3, 0] = 0
+    _check_permute_bitexact(idx, E, None)
 
 
 def test_permute_duplicate_experts_in_a_token():
