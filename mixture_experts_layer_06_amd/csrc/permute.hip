@@ -46,6 +46,23 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Counts pairs [begin, end) per expert into hist[0:256] (LDS, zeroed here), by one wave.
+__device__ __forceinline__ void count_range(const int32_t* __restrict__ idx, int begin, int end, int E,
+                                            int* hist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int e = lane; e < 256; e += kWave) hist[e] = 0;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  for (int base = begin; base < end; base += kWave) {
+    const int i = base + lane;
+    const bool valid = i < end;
+    const int e = valid ? clamp_e(idx[i], E) : 0;
+    const uint64_t m = match_mask(e, valid);
+    // the highest lane of each group of equal experts adds the group's size
+    if (valid && (m >> lane) == 1ull) hist[e] += __popcll(m);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 // Ranks pairs [begin, end) into rows, starting from run[e] (LDS), by one wave.
 __device__ __forceinline__ void rank_range(const int32_t* __restrict__ idx, int begin, int end, int E,
                                            int* run, int32_t* __restrict__ perm_src,
@@ -82,17 +99,7 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void permute_block_kernel(
   const int seg = cdiv(A, nw);
   const int begin = min(A, w * seg), end = min(A, begin + seg);
   int* mine = hist[w];
-  for (int e = lane; e < 256; e += kWave) mine[e] = 0;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  for (int base = begin; base < end; base += kWave) {
-    const int i = base + lane;
-    const bool valid = i < end;
-    const int e = valid ? clamp_e(idx[i], E) : 0;
-    const uint64_t m = match_mask(e, valid);
-    // the highest lane of each group of equal experts adds the group's size
-    if (valid && (m >> lane) == 1ull) mine[e] += __popcll(m);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  }
+  count_range(idx, begin, end, E, mine);
   __syncthreads();
   // thread e: prefix over waves (segment order), total per expert
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -145,49 +152,75 @@ __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// One block, thread e: running sum over chunks, then exclusive scan over experts.
+// One block, thread e (E <= 256): total over chunks, exclusive scan over
+// experts, then the running prefix over chunks. Each pass issues the loads
+// of 16 chunks before adding them, in chunk order.
 __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __restrict__ chunk_counts,
                                                            int nchunks, int E, int A,
                                                            int32_t* __restrict__ chunk_base,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets) {
-  __shared__ int tot[256];
-  __shared__ int off[256];
+  constexpr int U = 16;
+  __shared__ int wsum[4];
   const int e = threadIdx.x;
-  int run = 0;
+  const int lane = e & (kWave - 1), w = e / kWave;
+  int tot = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      chunk_base[(int64_t)c * E + e] = run;
-      run += chunk_counts[(int64_t)c * E + e];
+    for (int c0 = 0; c0 < nchunks; c0 += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) tot += v[u];
     }
   }
-  tot[e] = e < E ? run : 0;
+  const int incl = wave_incl_scan(tot);
+  if (lane == kWave - 1) wsum[w] = incl;
   __syncthreads();
-  if (e == 0) {
-    int acc = 0;
-    for (int q = 0; q < E; ++q) {
-      off[q] = acc;
-      acc += tot[q];
-    }
-  }
-  __syncthreads();
+  int excl = incl - tot;
+  for (int q = 0; q < w; ++q) excl += wsum[q];
   if (e < E) {
-    counts[e] = tot[e];
-    offsets[e] = off[e];
-    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off[e];
+    counts[e] = tot;
+    offsets[e] = excl;
+    int run = excl;
+    for (int c0 = 0; c0 < nchunks; c0 += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + u < nchunks) chunk_base[(int64_t)(c0 + u) * E + e] = run;
+        run += v[u];
+      }
+    }
   }
   if (e == 0) offsets[E] = A;
 }
 
-__global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restrict__ idx, int A, int E,
-                                                          const int32_t* __restrict__ chunk_base,
-                                                          int32_t* __restrict__ perm_src,
-                                                          int32_t* __restrict__ perm_dst) {
-  __shared__ int run[256];
-  for (int e = threadIdx.x; e < E; e += kWave) run[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+// Chunk c: four waves count and rank its four quarters; the quarters' first
+// rows are the chunk's base plus the counts of the quarters before them.
+__global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __restrict__ idx, int A, int E,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ perm_src,
+                                                           int32_t* __restrict__ perm_dst) {
+  constexpr int kQuarter = kChunk / 4;
+  __shared__ int hist[4][256];
+  const int w = threadIdx.x / kWave;
+  const int begin = min(A, blockIdx.x * kChunk + w * kQuarter);
+  const int end = min(A, begin + kQuarter);
+  count_range(idx, begin, end, E, hist[w]);
   __syncthreads();
-  const int begin = blockIdx.x * kChunk;
-  rank_range(idx, begin, min(A, begin + kChunk), E, run, perm_src, perm_dst);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = chunk_base[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = hist[q][e];
+      hist[q][e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  rank_range(idx, begin, end, E, hist[w], perm_src, perm_dst);
 }
 
 // Row scatter: x_perm[perm_dst[t*K+k]] = x[t]. VB = bytes per access.
@@ -241,7 +274,7 @@ moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T
     hipLaunchKernelGGL(permute_count_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts);
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, A,
                        chunk_base, counts, offsets);
-    hipLaunchKernelGGL(permute_rank_kernel, dim3(nch), dim3(64), 0, s, idx, A, E, chunk_base,
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_base,
                        perm_src, perm_dst);
   }
   if (x && T > 0) {
