@@ -822,23 +822,44 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
     const bf16_t* __restrict__ a, const bf16_t* __restrict__ w, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int e, int A, int Hin,
     int N, int relu, bf16_t* __restrict__ out) {
+  // Tasks are (non-empty expert, 64 columns), numbered densely so that the
+  // waves with work are spread evenly over the CUs: s_pre[q] counts the
+  // non-empty experts before q (a "row tile" of 2^30 rows).
+  __shared__ int s_off[257];
+  __shared__ int s_pre[257];
+  load_tile_prefix<0x40000000>(offsets, e, A, s_off, s_pre);
   const int lane = threadIdx.x & 63;
   const int ng = (N + 63) / 64;
   const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int ex = task / ng;
-  if (ex >= e) return;
+  const int q = task / ng;
+  if (q >= s_pre[e]) return;
+  int lo = 0, hi = e - 1;  // largest expert with s_pre <= q: the q-th non-empty one
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= q) lo = mid;
+    else hi = mid - 1;
+  }
+  const int ex = lo;
   const int n0 = (task % ng) * 64;
-  int r0 = offsets[ex], r1 = offsets[ex + 1];
-  r0 = r0 < 0 ? 0 : (r0 > A ? A : r0);
-  r1 = r1 < r0 ? r0 : (r1 > A ? A : r1);
-  const int cnt = r1 - r0;
-  if (cnt == 0) return;
+  const int r0 = s_off[ex];
+  const int cnt = s_off[ex + 1] - r0;
   const float sc = ld_scale(a_scale) * ld_scale(w_scale);
   const int kq = lane >> 4;  // k slice of the 32-wide step
   const int ci = lane & 15;  // fragment row/column index
   const int ncol = n0 + 4 * ci;
   const int avail_n = (int)min(N - ncol, 4) * 2;  // bytes of this lane's 4 columns
   const bf16_t* wex = w + (int64_t)ex * Hin * N;
+  // AL: buffer loads (rows past Hin and columns past N read as zero); U
+  // k-steps per register set, the next set's loads all issued before the
+  // current set is multiplied.
+  constexpr int U = MB == 1 ? 1 : 2;  // measured: deeper sets only pay with 32+ rows per wave
+  const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(wex, (uint32_t)Hin * (uint32_t)N * 2u);
+  const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a + (int64_t)r0 * Hin, (uint32_t)cnt * (uint32_t)Hin * 2u);
+  const uint32_t woff = (uint32_t)(kq * 8) * (uint32_t)N * 2u + (uint32_t)ncol * 2u + (ncol < N ? 0u : kOOB);
+  struct Set {
+    uint2 w[U][8];
+    uint4 x[U][MB];
+  };
 
   for (int mc = 0; mc < cnt; mc += 16 * MB) {
     f32x4_t acc[MB][4];
@@ -846,6 +867,53 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[mb][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if (AL) {
+      uint32_t xoff[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xoff[mb] = (uint32_t)(mc + mb * 16 + ci) * (uint32_t)Hin * 2u + kq * 16;
+      auto load_set = [&](int k0, Set& st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int k = k0 + 32 * u;
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            st.w[u][r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                             wsrc, woff + (uint32_t)(k + r) * (uint32_t)N * 2u, 0, 0));
+          const uint32_t kx = (uint32_t)k * 2u + (k + kq * 8 < Hin ? 0u : kOOB);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            st.x[u][mb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[mb] + kx, 0, 0));
+        }
+      };
+      auto mul_set = [&](const Set& st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          uint4 cols[4];
+          transpose_8x4_bf16(st.w[u], cols);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, cols[j]), __builtin_bit_cast(bf16x8_t, st.x[u][mb]),
+                  acc[mb][j], 0, 0, 0);
+        }
+      };
+      Set sa, sb;
+      int k0 = 0;
+      load_set(0, sa);
+      while (k0 < Hin) {
+        load_set(k0 + 32 * U, sb);  // past the end: zeros
+        __builtin_amdgcn_sched_barrier(0);
+        mul_set(sa);
+        k0 += 32 * U;
+        if (k0 >= Hin) break;
+        load_set(k0 + 32 * U, sa);
+        __builtin_amdgcn_sched_barrier(0);
+        mul_set(sb);
+        k0 += 32 * U;
+      }
+    } else
     for (int k0 = 0; k0 < Hin; k0 += 32) {
       uint2 rows[8];
 #pragma unroll
@@ -1042,7 +1110,9 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
   }
   const int elem = in_dt == MOE_BF16 ? 2 : 1;
   if (in_dt == MOE_BF16 && (int64_t)A <= (int64_t)kStreamMaxAvgRows * e) {
-    const bool al = (Hin % 8 == 0) && (N % 8 == 0);
+    // aligned: buffer loads over each expert's weights and over the rows (both under 2 GiB)
+    const bool al = (Hin % 8 == 0) && (N % 8 == 0) && ((int64_t)Hin * N * 2 < (1ll << 31)) &&
+                    ((int64_t)A * Hin * 2 < (1ll << 31));
     const int avg = cdiv(A, e);
     if (avg <= 8) return launch_stream_al<1>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
     if (avg <= 16) return launch_stream_al<2>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
