@@ -325,7 +325,7 @@ def bench_fp8(args, dev):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
                      "traffic": measured_traffic("fp8gmm"),
-                     "kernel": "moe_gmm E4M3 (gmm_tiled_kernel)", "gmm_source": source_digest(),
+                     "kernel": "moe_gmm E4M3 (gmm_pp8_kernel)", "gmm_source": source_digest(),
                      "flops_per_launch": fl,
                      "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
         "kernels": {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},

@@ -11,22 +11,26 @@
 // v_perm_b32 on its way in.
 //
 // Kernels
-//  * gmm_tiled_kernel (bf16 / E4M3, many rows per expert): 256x256 output
-//    tiles, 8 waves (2 x 4, each 128 x 64), 128-byte K slices double-
-//    buffered in LDS (pitch 144 B so MFMA fragment reads are conflict
-//    free). The weight slice is transposed while being written to LDS.
-//    MFMA: v_mfma_f32_16x16x32_bf16 or v_mfma_f32_16x16x128_f8f6f4 with the
-//    weight fragment as the 16-row operand and the activation fragment as
-//    the 16-column operand, so each lane ends up with 4 consecutive output
-//    columns of one row (8-byte stores).
-//    Tiles: per expert ceil(rows/256) x ceil(N/256); the block index is
-//    remapped so each of the 8 XCDs gets a contiguous run of tiles, ordered
-//    in groups of 8 row-tiles so concurrently running tiles share weight and
-//    activation panels in that XCD's L2. The grid is an upper bound sized on
-//    the host; the real tile count is computed on the device from offsets,
-//    and surplus blocks exit at once.
+//  * gmm_pp_kernel (bf16, many rows per expert, aligned): 256 x 256 output
+//    tiles, 8 waves of 128 x 64, a 4-slot LDS ring of 32-deep K slices
+//    filled by LDS DMA, the two row halves of the tile alternating multiply
+//    and memory phases between barriers (ping-pong). Weights are read 8 rows
+//    x 4 columns per lane and transposed with v_perm_b32, so MFMA j's row i
+//    is output column 4i + j and each lane ends with 16 consecutive output
+//    columns (32-byte stores).
+//  * gmm_pp8_kernel (E4M3, aligned): the same scheme on 16x16x128 f8f6f4
+//    MFMAs with 256 x 128 tiles, 128-deep K slices and a 3-slot ring.
+//  * gmm_tiled_kernel (bf16 / E4M3 shapes the DMA kernels do not take:
+//    unaligned rows or columns): register-staged 256 x 256 tiles, 128-byte K
+//    slices double-buffered in LDS, weights transposed on their way in.
+//  * All tiled kernels: per expert ceil(rows/BM) x ceil(N/BN) tiles; the
+//    block index is remapped so each of the 8 XCDs gets a contiguous run of
+//    tiles, ordered in groups of 8 row tiles so concurrently running tiles
+//    share weight and activation panels in that XCD's L2. The grid is an
+//    upper bound sized on the host; the real tile count is computed on the
+//    device from offsets, and surplus blocks exit at once.
 //  * gmm_stream_kernel (bf16, few rows per expert: decode shapes): one wave
-//    per (expert, 64 output columns), no LDS. Lane l loads rows
+//    per (non-empty expert, 64 output columns), no LDS. Lane l loads rows
 //    k0+8*(l/16)..+7 of columns n0+4*(l%16)..+3 (8-byte loads), transposes
 //    them into 4 fragments and issues 4 MFMAs whose row i means column
 //    n0 + 4i + j; every weight byte is read from HBM exactly once and the
@@ -37,6 +41,10 @@
 
 #include "common.h"
 
+// E4M3 tiled path: 1 = LDS-DMA ping-pong kernel, 0 = register-staged kernel.
+#ifndef MOE_GMM_FP8
+#define MOE_GMM_FP8 1
+#endif
 // bf16 tiled path: 1 = LDS-DMA ping-pong kernel, 0 = register-staged kernel.
 #ifndef MOE_GMM_BF16
 #define MOE_GMM_BF16 1
@@ -496,21 +504,13 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
   }
 }
 
-// ------------------------------------------------------------------ LDS-DMA bf16 kernel
+// ------------------------------------------------------------------ LDS DMA helpers
 //
-// Same tiles and scheduling as gmm_tiled_kernel, but global->LDS traffic goes
-// through buffer_load_dwordx4 ... lds (gfx950 LDS DMA): no staging registers,
-// so a ring of STAGES K slices (32 bf16 each) keeps STAGES-1 slices in
-// flight per block. The weight slice lands untransposed (k rows of BN
-// columns); each lane then reads 8 rows x 4 columns (ds_read_b64), transposes
-// them with v_perm_b32 and issues 4 MFMAs whose row i stands for column
-// 4i + j, which leaves each lane 16 consecutive output columns of one row.
-//
-// Stage layout (32 KB): activations BM rows x 64 B, 16-byte chunk c of row r
-// at r*64 + ((c ^ ((r >> 2) & 3)) << 4); weights 32 rows x BN*2 B, 128-byte
-// segment g of row k at k*BN*2 + ((g ^ ((k >> 3) & 3)) << 7). Both swizzles
-// make the MFMA operand reads bank-conflict free; every DMA instruction
-// writes one contiguous KB.
+// gfx950 LDS DMA: buffer_load_dwordx4 ... lds moves 16 bytes per lane from
+// global memory straight into LDS at M0 + 16*lane, with no staging
+// registers; out-of-range buffer offsets write zeros. Every DMA instruction
+// of the ping-pong kernels fills one contiguous KB of a ring slot; the
+// swizzles live in which global bytes each lane fetches.
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -815,6 +815,254 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
+// ------------------------------------------------------------------ ping-pong E4M3 kernel
+//
+// The bf16 ping-pong design for E4M3 operands, on v_mfma_scale_f32_16x16x128
+// _f8f6f4 (unit scales, both operands E4M3). One MFMA reduces 128 values, so
+// a ring slot holds a 128-deep K slice: activations 256 rows x 128 B and
+// weights 128 rows x 128 B (a 256 x 128 output tile; three 48 KB slots fit
+// in LDS). 8 waves of 64 x 64: waves 0-3 hold rows 0-127, waves 4-7 rows
+// 128-255, and the two halves alternate multiply and memory phases between
+// barriers exactly as in gmm_pp_kernel (one phase = 16 MFMAs = 512 cycles).
+//
+// Weights are read 4 bytes (4 columns) per lane from 32 consecutive K rows
+// and byte-transposed in registers into four 32-byte fragments, so MFMA j's
+// row i is output column 4i + j and a lane ends with 16 consecutive output
+// columns. LDS layout (a bank model of the measured gfx950 rule gives no
+// conflicts for either read): activation row m holds its eight 16-byte
+// chunks at positions c ^ ((m/2)%2 + 4*((m/4)%2)); weight K row k sits at
+// LDS row k ^ ((k/32)%2) with its two 64-byte halves swapped when (k/64)%2.
+
+struct Pp8Cfg {
+  static constexpr int kBM = 256, kBN = 128;
+  static constexpr int kKB = 128;  // K values (bytes) per slot
+  static constexpr int kStages = 3;
+  static constexpr int kNT = 512;
+  static constexpr int kLdsA = kBM * kKB;  // 32 KB
+  static constexpr int kLdsW = kKB * kBN;  // 16 KB
+  static constexpr int kStage = kLdsA + kLdsW;
+  static constexpr int kLds = kStages * kStage;
+  static constexpr int kADma = kLdsA / 1024 / 8;  // 1 KB DMA ops per wave per slot
+  static constexpr int kWDma = kLdsW / 1024 / 8;
+  static constexpr int kPerStage = kADma + kWDma;
+};
+
+__device__ __forceinline__ int pp8_xswz(int m) { return ((m >> 1) & 1) | (((m >> 2) & 1) << 2); }
+
+// 4 rows x 4 bytes (d[r] = row r, byte c = column c) -> 4 columns x 4 rows.
+__device__ __forceinline__ void transpose_4x4_u8(const uint32_t d[4], uint32_t o[4]) {
+  const uint32_t a = perm_b32(d[1], d[0], 0x05010400u);  // d0[0] d1[0] d0[1] d1[1]
+  const uint32_t b = perm_b32(d[1], d[0], 0x07030602u);  // d0[2] d1[2] d0[3] d1[3]
+  const uint32_t c = perm_b32(d[3], d[2], 0x05010400u);
+  const uint32_t e = perm_b32(d[3], d[2], 0x07030602u);
+  o[0] = perm_b32(c, a, 0x05040100u);
+  o[1] = perm_b32(c, a, 0x07060302u);
+  o[2] = perm_b32(e, b, 0x05040100u);
+  o[3] = perm_b32(e, b, 0x07060302u);
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp8_kernel(
+    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
+    const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+    const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
+    bf16_t* __restrict__ out) {
+  typedef Pp8Cfg C;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  {
+    int* s_off = reinterpret_cast<int*>(smem);
+    load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_off + 257);
+  }
+  Tile tile;
+  if (!pick_tile<C::kBM, C::kBN, 8>(reinterpret_cast<const int*>(smem),
+                                     reinterpret_cast<const int*>(smem) + 257, e, N, tile))
+    return;
+  __syncthreads();  // every lane has its tile before the ring overwrites the prefix
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2, wm2 = (wave >> 1) & 1, wn = wave & 1;
+  const int nsteps = (Hin + C::kKB - 1) / C::kKB;
+  const u32x4_t asrd = make_srd(a + (int64_t)tile.row0 * Hin, (uint32_t)tile.rows * (uint32_t)Hin);
+  const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * N, (uint32_t)Hin * (uint32_t)N);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  uint32_t a_voff[C::kADma];
+  uint32_t a_kc[C::kADma];
+#pragma unroll
+  for (int q = 0; q < C::kADma; ++q) {
+    const int kb = (wave * C::kADma + q) * 1024 + lane * 16;
+    const int prow = kb >> 7, pc = (kb >> 4) & 7;
+    const int lc = pc ^ pp8_xswz(prow);
+    a_voff[q] = (uint32_t)prow * (uint32_t)Hin + lc * 16;
+    a_kc[q] = lc * 16;
+  }
+  uint32_t w_voff[C::kWDma];
+#pragma unroll
+  for (int q = 0; q < C::kWDma; ++q) {
+    const int kb = (wave * C::kWDma + q) * 1024 + lane * 16;
+    const int prow = kb >> 7, pc = (kb >> 4) & 7;
+    const int lrow = prow ^ ((prow >> 5) & 1);
+    const int lc = pc ^ (((lrow >> 6) & 1) << 2);
+    const int nb = tile.n0 + lc * 16;
+    w_voff[q] = (uint32_t)lrow * (uint32_t)N + (uint32_t)nb + (nb < N ? 0u : kOOB);
+  }
+  // Past-the-end slices are issued too (out-of-range loads write zeros).
+  auto issue = [&](int step) {
+    const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
+    const int kb0 = step * C::kKB;
+#pragma unroll
+    for (int q = 0; q < C::kADma; ++q)
+      dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < Hin ? 0u : kOOB),
+            base + (wave * C::kADma + q) * 1024);
+    const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : kOOB;
+#pragma unroll
+    for (int q = 0; q < C::kWDma; ++q)
+      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
+  };
+  auto bar = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int S = C::kStages;
+  constexpr int kInFlight = (S - 2) * C::kPerStage;
+
+  const bool wave_active = (half * 128 + wm2 * 64 < tile.rows) && (tile.n0 + wn * 64 < N);
+  const int ci = lane & 15, kq = lane >> 4;
+  int xoff[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = half * 128 + wm2 * 64 + i * 16 + ci;
+      xoff[i][h] = m * C::kKB + (((2 * kq + h) ^ pp8_xswz(m)) << 4);
+    }
+  // weight K row 32kq + r sits at LDS row 32kq + (r ^ (kq & 1)); its column
+  // dword wn*16 + ci moves to the other 64-byte half when kq >= 2
+  const int pdw = (wn * 16 + ci) ^ ((kq >> 1) << 4);
+  const int wrow0 = C::kLdsA + 32 * kq * C::kBN + pdw * 4;
+  const int wpar = (kq & 1) * C::kBN;
+  i32x8_t xa[4], wf[4];
+  auto read_frags = [&](int slice) {
+    const unsigned char* st = smem + (slice % S) * C::kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(st + xoff[i][0]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(st + xoff[i][1]);
+      xa[i] = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    const unsigned char* we = st + wrow0 + wpar;  // even r: LDS row 32kq + r + (kq & 1)
+    const unsigned char* wo = st + wrow0 - wpar;  // odd r:  LDS row 32kq + r - (kq & 1)
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      uint32_t d[4], o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 4 * g + r;
+        d[r] = *reinterpret_cast<const uint32_t*>(((rr & 1) ? wo : we) + rr * C::kBN);
+      }
+      transpose_4x4_u8(d, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[j][g] = (int)o[j];
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  auto multiply = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0, 0,
+                                                                     0, 0);
+  };
+
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue(t);
+  wait_vmcnt<kInFlight>();
+  bar();  // barrier 0: slice 0 has landed
+  if (half == 0) {
+    if (wave_active) {
+      read_frags(0);
+      issue(S - 1);
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        multiply();
+        wait_vmcnt<kInFlight>();
+        bar();
+        read_frags(s + 1);
+        issue(s + S);
+        bar();
+      }
+    } else {
+      issue(S - 1);
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        wait_vmcnt<kInFlight>();
+        bar();
+        issue(s + S);
+        bar();
+      }
+    }
+    bar();  // matches the second half's last barrier
+  } else {
+    bar();
+    issue(S - 1);
+    if (wave_active) {
+      read_frags(0);
+      wait_vmcnt<kInFlight>();
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        multiply();
+        bar();
+        read_frags(s + 1);
+        issue(s + S);
+        wait_vmcnt<kInFlight>();
+        bar();
+      }
+    } else {
+      wait_vmcnt<kInFlight>();
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        bar();
+        issue(s + S);
+        wait_vmcnt<kInFlight>();
+        bar();
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
+  if (!wave_active) return;
+
+  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
+    if (ml >= tile.rows) continue;
+    const int64_t m = tile.row0 + ml;
+    // MFMA j, output row 4*kq + r  ->  column nb + 4r + j
+    const int nb = tile.n0 + wn * 64 + 16 * kq;
+    if (nb >= N) continue;  // N is a multiple of 16 here
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float t = acc[i][j][r] * sc;
+        v[4 * r + j] = (relu && t < 0.f) ? 0.f : t;
+      }
+    bf16_t* o = out + m * N + nb;
+    reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                                                pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+  }
+}
+
 // ------------------------------------------------------------------ streaming kernel (decode)
 
 template <int MB, bool AL>
@@ -1072,6 +1320,26 @@ moe_status launch_pp(const void* a, const float* as, const void* w, const float*
   return launch_status();
 }
 
+moe_status launch_pp8(const void* a, const float* as, const void* w, const float* ws,
+                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
+                      hipStream_t s) {
+  typedef Pp8Cfg C;
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp8_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    attr_done = true;
+  }
+  const int64_t mt_max = cdiv64(A, C::kBM) + (e < A ? e : A);
+  const int64_t blocks = mt_max * cdiv64(N, C::kBN);
+  const int64_t grid = cdiv64(blocks, 8) * 8;
+  if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(gmm_pp8_kernel, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
+                     (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
+                     relu, (bf16_t*)out);
+  return launch_status();
+}
+
 template <int MB, bool AL>
 moe_status launch_stream(const void* a, const float* as, const void* w, const float* ws,
                          const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
@@ -1127,6 +1395,10 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
     typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
     return launch_pp<CP>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
   }
+#endif
+#if MOE_GMM_FP8 == 1
+  if (elem == 1 && al && N % 16 == 0)
+    return launch_pp8(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
 #endif
   if (elem == 2) {
     typedef TiledCfg<2, 256, 256, WM, WN, true, false> CA;

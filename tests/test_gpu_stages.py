@@ -197,6 +197,7 @@ GMM_CASES = [
     ("bf16_stream_overflow_rows", [2, 80, 1, 0, 3, 1, 2, 3], 256, 192, "bf16"),
     ("fp8_tiled", [200, 0, 333], 256, 384, "fp8"),
     ("fp8_tiled_unaligned", [100, 77], 200, 100, "fp8"),
+    ("fp8_ragged_k_and_n", [130, 5, 0, 260], 208, 400, "fp8"),  # last K slice 80 deep, 16-column tile
     ("f32_tiny", [20, 0, 17, 40, 1, 30, 12, 8], 128, 256, "f32"),
     ("f32_ragged", [70, 5], 33, 45, "f32"),
 ]
