@@ -49,6 +49,16 @@
 #ifndef MOE_GMM_BF16
 #define MOE_GMM_BF16 1
 #endif
+// Row tiles per group in the tile order of the bf16 and E4M3 ping-pong kernels
+// (measured: 8 for the 256 x 256 bf16 tiles; 4 for the 256 x 128 E4M3 tiles,
+// where the ~32 tiles an XCD runs at once then span 4 row x 8 column tiles,
+// the split that re-reads the fewest panel bytes).
+#ifndef MOE_PP_GM
+#define MOE_PP_GM 8
+#endif
+#ifndef MOE_PP8_GM
+#define MOE_PP8_GM 4
+#endif
 // Tile / waves along columns / LDS ring slots of the bf16 ping-pong kernel.
 #ifndef MOE_PP_BM
 #define MOE_PP_BM 256
@@ -622,7 +632,7 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_pre);
   }
   Tile tile;
-  if (!pick_tile<C::kBM, C::kBN, 8>(reinterpret_cast<const int*>(smem),
+  if (!pick_tile<C::kBM, C::kBN, MOE_PP_GM>(reinterpret_cast<const int*>(smem),
                                      reinterpret_cast<const int*>(smem) + 257, e, N, tile))
     return;
   __syncthreads();  // every lane has its tile before the ring overwrites the prefix
@@ -873,7 +883,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_off + 257);
   }
   Tile tile;
-  if (!pick_tile<C::kBM, C::kBN, 8>(reinterpret_cast<const int*>(smem),
+  if (!pick_tile<C::kBM, C::kBN, MOE_PP8_GM>(reinterpret_cast<const int*>(smem),
                                      reinterpret_cast<const int*>(smem) + 257, e, N, tile))
     return;
   __syncthreads();  // every lane has its tile before the ring overwrites the prefix
