@@ -150,6 +150,9 @@ def bench_layer(args, dev):
     pws = torch.empty((max(pws_n, 16),), dtype=torch.uint8, device=dev)
     rws_n = moe.route_workspace_size(T, H, E, K, moe.dtype_code(x))
     rws = torch.empty((max(rws_n, 16),), dtype=torch.uint8, device=dev)
+    gws_n = max(moe.gmm_workspace_size(moe.dtype_code(x), E, A, H, F),
+                moe.gmm_workspace_size(moe.dtype_code(x), E, A, F, H))
+    gws = torch.empty((max(gws_n, 16),), dtype=torch.uint8, device=dev)  # shared: one stream
 
     def step(ev=None):
         if ev is not None:
@@ -160,10 +163,10 @@ def bench_layer(args, dev):
         moe.permute(idx, E, x=x, ws=pws, out=bufs)
         if ev is not None:
             ev[2].record()
-        moe.gmm(bufs["x_perm"], w1, bufs["offsets"], act=moe.ACT_RELU, out=hm)
+        moe.gmm(bufs["x_perm"], w1, bufs["offsets"], act=moe.ACT_RELU, out=hm, ws=gws)
         if ev is not None:
             ev[3].record()
-        moe.gmm(hm, w2, bufs["offsets"], out=yp)
+        moe.gmm(hm, w2, bufs["offsets"], out=yp, ws=gws)
         if ev is not None:
             ev[4].record()
         moe.combine(yp, bufs["perm_dst"], gate, T, K, out=y)
@@ -275,6 +278,10 @@ def bench_fp8(args, dev):
     un = torch.empty((A, N1), dtype=torch.bfloat16, device=dev)
     my = torch.empty((T, N2), dtype=torch.bfloat16, device=dev)
     side = torch.cuda.Stream(device=dev)
+    sws_n = moe.gmm_workspace_size(moe.BF16, 1, T, H2, N2)   # shared expert, on the side stream
+    sws = torch.empty((max(sws_n, 16),), dtype=torch.uint8, device=dev)
+    gws_n = moe.gmm_workspace_size(moe.FP8_E4M3, e, A, H1, N1)
+    gws = torch.empty((max(gws_n, 16),), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         main = torch.cuda.current_stream()
@@ -286,10 +293,10 @@ def bench_fp8(args, dev):
         with torch.cuda.stream(side):
             if ev is not None:
                 ev[3].record(side)
-            moe.gmm(mx, mw, moff, out=my, stream=side)
+            moe.gmm(mx, mw, moff, out=my, ws=sws, stream=side)
             if ev is not None:
                 ev[4].record(side)
-        moe.gmm(gx, gw, perm["offsets"], a_scale=sx, w_scale=sw, out=gy)
+        moe.gmm(gx, gw, perm["offsets"], a_scale=sx, w_scale=sw, out=gy, ws=gws)
         if ev is not None:
             ev[1].record(main)
         moe.combine(gy, perm["perm_dst"], None, T, K, out=un)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10100 /* 1.1.0: moe_route takes a workspace */
+#define MOE_VERSION 10200 /* 1.2.0: moe_route and moe_gmm take workspaces */
 
 typedef enum {
   MOE_OK = 0,
@@ -146,15 +146,21 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int
  *            device; offsets outside [0, A] are clamped to it)
  *   act      MOE_ACT_NONE or MOE_ACT_RELU
  *   out      device (A,N) in out_dt
+ *   ws, ws_bytes device scratch of at least moe_gmm_workspace_size() bytes
+ *            (may be NULL when that size is 0). When the output tiles leave
+ *            a partial last round on the GPU, those tiles are split along
+ *            the reduction and their fp32 partial sums meet here; the parts
+ *            are added in a fixed order, so results do not depend on timing.
  * Supported types (a_dt, w_dt -> out_dt): F32,F32->F32; BF16,BF16->BF16;
  * FP8,FP8->BF16 (FP8 requires MOE_QUANT_PER_TENSOR on both sides).
  * Accumulation is fp32; the scales multiply the fp32 sum; one rounding to
  * out_dt. Experts with no rows cost nothing and write nothing.
  */
+moe_status moe_gmm_workspace_size(moe_dtype a_dt, int e, int A, int Hin, int N, size_t* bytes);
 moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
                    const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
                    const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
-                   moe_dtype out_dt, void* stream);
+                   moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine — back to token order.

@@ -26,8 +26,8 @@ QUANT_NONE, QUANT_PER_TENSOR = 0, 1
 ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
-           "moe_permute_workspace_size", "moe_permute", "moe_gmm", "moe_combine",
-           "moe_layer_workspace_size", "moe_layer")
+           "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
+           "moe_combine", "moe_layer_workspace_size", "moe_layer")
 
 
 class MoeError(RuntimeError):
@@ -56,8 +56,9 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         L.moe_permute_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_permute.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_gmm_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_gmm.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, vp,
-                              i32, vp]
+                              i32, vp, sz, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
         L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
@@ -166,9 +167,16 @@ def permute(topk_idx, E, x=None, ws=None, stream=None, out=None):
     return {"counts": counts, "offsets": offsets, "perm_src": psrc, "perm_dst": pdst, "x_perm": xp}
 
 
-def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, stream=None):
+def gmm_workspace_size(a_dt, e, A, Hin, N) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_gmm_workspace_size(a_dt, e, A, Hin, N, ctypes.byref(n)), "moe_gmm_workspace_size")
+    return n.value
+
+
+def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=None, stream=None):
     """moe_gmm over w (e,Hin,N). Scales (1-element fp32 device tensors) select
-    MOE_QUANT_PER_TENSOR. Output: fp32 for fp32 inputs, else bf16."""
+    MOE_QUANT_PER_TENSOR. Output: fp32 for fp32 inputs, else bf16. ws: a device
+    buffer of at least gmm_workspace_size() bytes, allocated here when None."""
     A, Hin = a.shape
     e, Hw, N = w.shape
     if Hw != Hin:
@@ -177,10 +185,15 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, strea
     odt = F32 if adt == F32 else BF16
     if out is None:
         out = _empty((A, N), torch.float32 if odt == F32 else torch.bfloat16, a)
+    if ws is None:
+        n = gmm_workspace_size(adt, e, A, Hin, N)
+        ws = _empty((n,), torch.uint8, a) if n else None
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     aq = QUANT_PER_TENSOR if a_scale is not None else QUANT_NONE
     wq = QUANT_PER_TENSOR if w_scale is not None else QUANT_NONE
     st = lib().moe_gmm(_ptr(a), adt, aq, _ptr(a_scale), _ptr(w), wdt, wq, _ptr(w_scale),
-                       _ptr(offsets), e, A, Hin, N, act, _ptr(out), odt, _stream(stream))
+                       _ptr(offsets), e, A, Hin, N, act, _ptr(out), odt, _ptr(ws), nbytes,
+                       _stream(stream))
     _check(st, "moe_gmm")
     return out
 

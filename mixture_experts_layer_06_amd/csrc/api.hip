@@ -43,7 +43,7 @@ bool any_dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt =
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct LayerWs {
-  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, xp, hm, total;
+  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, gmm_ws, xp, hm, total;
 };
 
 LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
@@ -58,6 +58,10 @@ LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
   L.psrc = o; o += round256(A * 4);
   L.pdst = o; o += round256(A * 4);
   L.perm_ws = o; o += round256(permute_ws_bytes(T, E, K));
+  {
+    const size_t g1 = gmm_ws_bytes(dt, E, (int)A, H, F), g2 = gmm_ws_bytes(dt, E, (int)A, F, H);
+    L.gmm_ws = o; o += round256(g1 > g2 ? g1 : g2);  // shared by the two GEMMs (same stream)
+  }
   L.xp = o; o += round256((size_t)A * H * es);  // permuted rows; reused for GEMM 2 output
   // hidden activations; before GEMM 1 writes them the router's split-H partials live here
   const size_t hm = (size_t)A * F * es, rws = route_ws_bytes(T, H, E, dt);
@@ -155,10 +159,19 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int
                         (hipStream_t)stream);
 }
 
+moe_status moe_gmm_workspace_size(moe_dtype a_dt, int e, int A, int Hin, int N, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  if (!any_dtype_ok(a_dt)) return MOE_ERR_BAD_DTYPE;
+  if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
+  if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
+  *bytes = gmm_ws_bytes(a_dt, e, A, Hin, N);
+  return MOE_OK;
+}
+
 moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
                    const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
                    const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
-                   moe_dtype out_dt, void* stream) {
+                   moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
   if (!any_dtype_ok(a_dt) || !any_dtype_ok(w_dt) || !any_dtype_ok(out_dt)) return MOE_ERR_BAD_DTYPE;
   const bool pair_ok = (a_dt == MOE_F32 && w_dt == MOE_F32 && out_dt == MOE_F32) ||
                        (a_dt == MOE_BF16 && w_dt == MOE_BF16 && out_dt == MOE_BF16) ||
@@ -178,14 +191,21 @@ moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const floa
   REQUIRE_PTR(w);
   REQUIRE_PTR(offsets);
   REQUIRE_PTR(out);
+  const size_t need = gmm_ws_bytes(a_dt, e, A, Hin, N);
+  if (need > 0) {
+    REQUIRE_PTR(ws);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
   REQUIRE_ALIGNED(a);
   REQUIRE_ALIGNED(w);
   REQUIRE_ALIGNED(offsets);
   REQUIRE_ALIGNED(out);
+  REQUIRE_ALIGNED(ws);
   // scales are 4-byte device scalars: natural alignment suffices
   const float* as = a_q == MOE_QUANT_PER_TENSOR ? a_scale : nullptr;
   const float* wsc = w_q == MOE_QUANT_PER_TENSOR ? w_scale : nullptr;
-  return launch_gmm(a, a_dt, as, w, wsc, offsets, e, A, Hin, N, act, out, out_dt, (hipStream_t)stream);
+  return launch_gmm(a, a_dt, as, w, wsc, offsets, e, A, Hin, N, act, out, out_dt, need > 0 ? ws : nullptr,
+                    (hipStream_t)stream);
 }
 
 moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_dst,
@@ -254,8 +274,11 @@ moe_status moe_layer(const void* x, const void* w_router, const float* bias, con
   const int A = T * K;
   MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s));
   MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
-  MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, s));
-  MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, s));
+  void* gws = base + L.gmm_ws;  // sized for whichever GEMM needs more (possibly none)
+  MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt,
+                     gmm_ws_bytes(dt, E, A, H, F) ? gws : nullptr, s));
+  MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt,
+                     gmm_ws_bytes(dt, E, A, F, H) ? gws : nullptr, s));
   MOE_TRY(launch_combine(xp, dt, pdst, gate, T, K, H, y, s));
   return MOE_OK;
 }

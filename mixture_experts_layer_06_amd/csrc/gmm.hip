@@ -41,6 +41,10 @@
 
 #include "common.h"
 
+// 1: the bf16 ping-pong kernel may split its last, partial round of tiles along K.
+#ifndef MOE_GMM_SPLIT
+#define MOE_GMM_SPLIT 1
+#endif
 // E4M3 tiled path: 1 = LDS-DMA ping-pong kernel, 0 = register-staged kernel.
 #ifndef MOE_GMM_FP8
 #define MOE_GMM_FP8 1
@@ -79,7 +83,17 @@ namespace {
 
 // Expert offsets (clamped to [0, A]) and the running count of row tiles per
 // expert, in LDS: s_off[0..e], s_pre[0..e] (s_pre[q] = tiles before expert q).
-template <int BM>
+// Row tiles of an expert with `rows` rows: ceil(rows / BM), except that a
+// last piece of at most FOLD rows rides on the tile before it (that tile
+// then has BM < rows <= BM + FOLD).
+template <int BM, int FOLD>
+__device__ __forceinline__ int row_tiles(int rows) {
+  const int t = (rows + BM - 1) / BM;
+  const int tail = rows - (t - 1) * BM;
+  return (FOLD > 0 && t > 1 && tail <= FOLD) ? t - 1 : t;
+}
+
+template <int BM, int FOLD = 0>
 __device__ __forceinline__ void load_tile_prefix(const int32_t* __restrict__ offsets, int e, int A,
                                                  int* s_off, int* s_pre) {
   for (int q = threadIdx.x; q <= e; q += blockDim.x) {
@@ -96,7 +110,7 @@ __device__ __forceinline__ void load_tile_prefix(const int32_t* __restrict__ off
       const int q = lane * 4 + i;
       int rows = q < e ? s_off[q + 1] - s_off[q] : 0;
       rows = rows < 0 ? 0 : rows;
-      c[i] = (rows + BM - 1) / BM;
+      c[i] = row_tiles<BM, FOLD>(rows);
       local += c[i];
     }
     const int incl = wave_incl_scan(local);
@@ -120,17 +134,11 @@ struct Tile {
 // XCD-aware: block p runs on XCD p % 8; XCD x takes logical tiles
 // [x*per, (x+1)*per). Inside an expert, tiles go in groups of GM row tiles:
 // group-major, then column tile, then row tile.
-template <int BM, int BN, int GM>
-__device__ __forceinline__ bool pick_tile(const int* s_off, const int* s_pre, int e, int N, Tile& t) {
-  const int ntn = (N + BN - 1) / BN;
-  const int total = s_pre[e] * ntn;
-  if (total == 0) return false;
-  const int p = blockIdx.x;
-  const int per = (total + 7) / 8;
-  const int slot = p >> 3;
-  if (slot >= per) return false;
-  const int L = (p & 7) * per + slot;
-  if (L >= total) return false;
+// Tile of logical index L (0 <= L < s_pre[e] * ntn). Inside an expert,
+// tiles go in groups of GM row tiles: group-major, then column tile, then
+// row tile.
+template <int BM, int BN, int GM, int FOLD = 0>
+__device__ __forceinline__ void tile_of(const int* s_off, const int* s_pre, int e, int ntn, int L, Tile& t) {
   const int g = L / ntn;  // global row-tile-major position among s_pre[e] row tiles
   // find expert ex with s_pre[ex] <= g < s_pre[ex+1] (binary search, s_pre non-decreasing)
   int lo = 0, hi = e - 1;
@@ -151,8 +159,68 @@ __device__ __forceinline__ bool pick_tile(const int* s_off, const int* s_pre, in
   // buffer descriptors live in scalar registers
   t.ex = __builtin_amdgcn_readfirstlane(ex);
   t.row0 = __builtin_amdgcn_readfirstlane(s_off[ex] + m * BM);
-  t.rows = __builtin_amdgcn_readfirstlane(min(BM, s_off[ex + 1] - (s_off[ex] + m * BM)));
+  const int left = s_off[ex + 1] - (s_off[ex] + m * BM);  // the last tile takes a folded tail
+  t.rows = __builtin_amdgcn_readfirstlane((FOLD > 0 && m == mt - 1) ? left : min(BM, left));
   t.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
+}
+
+// Logical tile for this block, or false if the block has no work.
+// XCD-aware: block p runs on XCD p % 8; XCD x takes logical tiles
+// [x*per, (x+1)*per).
+template <int BM, int BN, int GM, int FOLD = 0>
+__device__ __forceinline__ bool pick_tile(const int* s_off, const int* s_pre, int e, int N, Tile& t) {
+  const int ntn = (N + BN - 1) / BN;
+  const int total = s_pre[e] * ntn;
+  if (total == 0) return false;
+  const int p = blockIdx.x;
+  const int per = (total + 7) / 8;
+  const int slot = p >> 3;
+  if (slot >= per) return false;
+  const int L = (p & 7) * per + slot;
+  if (L >= total) return false;
+  tile_of<BM, BN, GM, FOLD>(s_off, s_pre, e, ntn, L, t);
+  return true;
+}
+
+// Work of one block when the last, partial round of tiles may be split
+// along K. With total tiles = rounds * ncu + rem and 0 < rem <= ncu/4, the
+// first rounds * ncu blocks take whole tiles (XCD-aware as in pick_tile)
+// and each of the rem remaining tiles is split over S = 4 blocks, part
+// `part` of tile `rtile` (0 <= rtile < rem) taking K slices
+// [part*nsteps/S, (part+1)*nsteps/S) (at least 4 each). Otherwise S = 1 and
+// this is pick_tile. Measured on the prefill GEMMs: 4-way splits of a
+// small remainder gain 12%; 2-way splits of a remainder near ncu/2 lose 2%.
+// The host sizes the grid for the extra blocks (at most 3*ncu/4).
+constexpr int kMaxSplit = 4;
+struct Work {
+  int S, part, rtile;
+};
+template <int BM, int BN, int GM, int FOLD = 0>
+__device__ __forceinline__ bool pick_work(const int* s_off, const int* s_pre, int e, int N, int nsteps,
+                                          int ncu, bool can_split, Tile& t, Work& wk) {
+  const int ntn = (N + BN - 1) / BN;
+  const int total = s_pre[e] * ntn;
+  wk.S = 1;
+  wk.part = 0;
+  wk.rtile = 0;
+  if (total == 0) return false;
+  const int rem = total % ncu;
+  const int S = kMaxSplit;
+  if (!can_split || rem == 0 || rem * S > ncu || nsteps < 4 * S) return pick_tile<BM, BN, GM, FOLD>(s_off, s_pre, e, N, t);
+  const int full = total - rem;  // a multiple of ncu, hence of 8
+  const int p = blockIdx.x;
+  int L;
+  if (p < full) {
+    L = (p & 7) * (full >> 3) + (p >> 3);
+  } else {
+    const int u = p - full;
+    if (u >= rem * S) return false;
+    L = full + u / S;
+    wk.S = S;
+    wk.part = u % S;
+    wk.rtile = u / S;
+  }
+  tile_of<BM, BN, GM, FOLD>(s_off, s_pre, e, ntn, L, t);
   return true;
 }
 
@@ -597,23 +665,26 @@ template <int BM, int BN, int WM_, int WN_, int STAGES>
 struct PpCfg {
   static constexpr int kStages = STAGES;
   static constexpr int kBM = BM, kBN = BN;
+  static constexpr int kFold = 32;  // tail rows an expert's last tile may carry beyond BM
   static constexpr int kSegMask = (BN * 2) / 128 - 1;  // 128-byte segments per weight row - 1
   static constexpr int kWavesM = WM_, kWavesN = WN_;
   static constexpr int kNT = 64 * WM_ * WN_;
   static constexpr int kWM = BM / WM_, kWN = BN / WN_;
   static constexpr int kFI = kWM / 16;   // 16-row activation fragments per wave
   static constexpr int kFG = kWN / 64;   // 64-column weight groups per wave
-  static constexpr int kLdsA = BM * kDmaKB;        // bytes of activations per slot
-  static constexpr int kLdsW = 32 * BN * 2;        // bytes of weights per slot
-  static constexpr int kStage = kLdsA + kLdsW;
-  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kLdsA = BM * kDmaKB;                 // activations per slot
+  static constexpr int kLdsX = (BM + kFold) * kDmaKB;       // ... with the folded tail rows
+  static constexpr int kLdsW = 32 * BN * 2;                 // weights per slot
+  static constexpr int kStage = kLdsX + kLdsW;
+  static constexpr int kDummy = STAGES * kStage;            // 1 KB that soaks up unused DMA
+  static constexpr int kLds = kDummy + 1024;
   static constexpr int kADma = kLdsA / 1024 / (kNT / 64);  // 1 KB DMA ops per wave per slot
   static constexpr int kWDma = kLdsW / 1024 / (kNT / 64);
   static constexpr int kPerStage = kADma + kWDma;          // vmcnt units per slot per lane
   static_assert(kLdsA % (1024 * (kNT / 64)) == 0 && kLdsW % (1024 * (kNT / 64)) == 0, "dma split");
   static_assert(kWN % 64 == 0, "weight groups");
-  static_assert(WM_ == 2, "two row halves");
-  static_assert(STAGES >= 3 && (STAGES - 2) * kPerStage <= 63, "ring depth");
+  static_assert(WM_ == 2 && kFold == 16 * WM_, "two row halves, one tail fragment each");
+  static_assert(STAGES >= 3 && (STAGES - 2) * (kPerStage + 1) <= 63, "ring depth");
   static_assert(kLds >= 2 * 257 * 4, "tile prefix lives in the ring");
 };
 
@@ -622,44 +693,65 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
-    bf16_t* __restrict__ out) {
+    bf16_t* __restrict__ out, float* __restrict__ split_ws, int* __restrict__ split_cnt, int ncu) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int s_last;
   // The ring takes all of LDS; the tile prefix borrows its first bytes
   // before any DMA is issued.
   {
     int* s_off = reinterpret_cast<int*>(smem);
     int* s_pre = s_off + 257;
-    load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_pre);
+    load_tile_prefix<C::kBM, C::kFold>(offsets, e, A, s_off, s_pre);
   }
+  const int hin_b = Hin * 2;
+  const int nsteps_all = (hin_b + kDmaKB - 1) / kDmaKB;
   Tile tile;
-  if (!pick_tile<C::kBM, C::kBN, MOE_PP_GM>(reinterpret_cast<const int*>(smem),
-                                     reinterpret_cast<const int*>(smem) + 257, e, N, tile))
+  Work wk;
+  if (!pick_work<C::kBM, C::kBN, MOE_PP_GM, C::kFold>(reinterpret_cast<const int*>(smem),
+                                                       reinterpret_cast<const int*>(smem) + 257, e, N,
+                                                       nsteps_all, ncu, split_ws != nullptr, tile, wk))
     return;
   __syncthreads();  // every lane has its tile before the ring overwrites the prefix
+  // K slices of this block: all of them, or part wk.part of wk.S
+  const int ks0 = wk.part * nsteps_all / wk.S;
+  const int ks1 = (wk.part + 1) * nsteps_all / wk.S;
+  const int kext_b = (hin_b < ks1 * kDmaKB ? hin_b : ks1 * kDmaKB) - ks0 * kDmaKB;  // K bytes of the range
+  // An expert's last tile may carry up to kFold tail rows beyond BM: then
+  // each row half multiplies one more 16-row fragment (rows BM + 16*wm ..).
+  const bool extra = tile.rows > C::kBM;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
-  const int hin_b = Hin * 2;
   const int n_b = N * 2;
   const int n0b = tile.n0 * 2;
-  const int nsteps = (hin_b + kDmaKB - 1) / kDmaKB;
-  const u32x4_t asrd = make_srd(a + (int64_t)tile.row0 * hin_b, (uint32_t)tile.rows * (uint32_t)hin_b);
-  const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * n_b, (uint32_t)Hin * (uint32_t)n_b);
+  const int nsteps = ks1 - ks0;
+  // descriptors start at the range's first K slice (rows past tile.rows and
+  // K rows past Hin stay out of range)
+  const u32x4_t asrd = make_srd(a + (int64_t)tile.row0 * hin_b + ks0 * kDmaKB,
+                                (uint32_t)tile.rows * (uint32_t)hin_b - (uint32_t)(ks0 * kDmaKB));
+  const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * n_b + (int64_t)ks0 * 32 * n_b,
+                                (uint32_t)(Hin - ks0 * 32) * (uint32_t)n_b);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // ---- DMA: which global bytes this lane fetches for each KB of a slot it fills
-  uint32_t a_voff[C::kADma];
-  uint32_t a_kc[C::kADma];
-#pragma unroll
-  for (int q = 0; q < C::kADma; ++q) {
-    const int kb = (wave * C::kADma + q) * 1024 + lane * 16;  // byte within the slot's activations
+  auto x_src = [&](int kb, uint32_t& voff, uint32_t& kc) {  // kb: byte within the slot's activations
     const int row = kb >> 6, pc = (kb >> 4) & 3;
     const int lc = pc ^ ((row >> 1) & 3);
-    a_voff[q] = (uint32_t)row * (uint32_t)hin_b + lc * 16;
-    a_kc[q] = lc * 16;
-  }
+    voff = (uint32_t)row * (uint32_t)hin_b + lc * 16;
+    kc = lc * 16;
+  };
+  uint32_t a_voff[C::kADma + 1];
+  uint32_t a_kc[C::kADma + 1];
+#pragma unroll
+  for (int q = 0; q < C::kADma; ++q) x_src((wave * C::kADma + q) * 1024 + lane * 16, a_voff[q], a_kc[q]);
+  // tail rows: waves 0 and 1 fetch rows BM..BM+15 and BM+16..BM+31; the
+  // other waves issue an out-of-range op into the dummy KB, so every wave
+  // counts the same number of ops per slice
+  const bool tail_dma = wave < C::kFold / 16;
+  x_src(C::kLdsA + wave * 1024 + lane * 16, a_voff[C::kADma], a_kc[C::kADma]);
+  if (!tail_dma) a_voff[C::kADma] = kOOB;
   uint32_t w_voff[C::kWDma];
 #pragma unroll
   for (int q = 0; q < C::kWDma; ++q) {
@@ -671,17 +763,20 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
   // Past-the-end slices are issued too (out-of-range loads write zeros), so
   // every wait count is fixed.
-  auto issue = [&](int step) {
+  auto issue = [&](int step, auto ex) {
     const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
     const int kb0 = step * kDmaKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
-      dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < hin_b ? 0u : kOOB),
+      dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < kext_b ? 0u : kOOB),
             base + (wave * C::kADma + q) * 1024);
+    if (decltype(ex)::value)
+      dma16(asrd, a_voff[C::kADma] + kb0 + (kb0 + (int)a_kc[C::kADma] < kext_b ? 0u : kOOB),
+            tail_dma ? base + C::kLdsA + wave * 1024 : lds0 + C::kDummy);
     const uint32_t kstep = step < nsteps ? (uint32_t)(step * 32) * (uint32_t)n_b : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
-      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
+      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsX + (wave * C::kWDma + q) * 1024);
   };
   // The compiler may not move work across these barriers: the phases are the schedule.
   auto bar = [] {
@@ -690,28 +785,27 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     __builtin_amdgcn_sched_barrier(0);
   };
   constexpr int S = C::kStages;
-  constexpr int kInFlight = (S - 2) * C::kPerStage;  // a wave's ops still landing at a wait
 
   const bool wave_active = (wm * C::kWM < tile.rows) && (tile.n0 + wn * C::kWN < N);
   const int ci = lane & 15, kq = lane >> 4;
+  auto xoff_of = [&](int m) { return m * kDmaKB + ((kq ^ ((m >> 1) & 3)) << 4); };
   int xoff[C::kFI];
 #pragma unroll
-  for (int i = 0; i < C::kFI; ++i) {
-    const int m = wm * C::kWM + i * 16 + ci;
-    xoff[i] = m * kDmaKB + ((kq ^ ((m >> 1) & 3)) << 4);
-  }
+  for (int i = 0; i < C::kFI; ++i) xoff[i] = xoff_of(wm * C::kWM + i * 16 + ci);
+  const int xoff_t = xoff_of(C::kBM + wm * 16 + ci);  // this half's tail fragment
   int woff[C::kFG];
 #pragma unroll
   for (int g = 0; g < C::kFG; ++g) {
     const int cb = (wn * C::kWN + g * 64 + 4 * ci) * 2;  // byte of this lane's 4 columns
-    woff[g] = C::kLdsA + (kq * 8) * (C::kBN * 2) + (((cb >> 7) ^ (kq & C::kSegMask)) << 7) + (cb & 127);
+    woff[g] = C::kLdsX + (kq * 8) * (C::kBN * 2) + (((cb >> 7) ^ (kq & C::kSegMask)) << 7) + (cb & 127);
   }
-  bf16x8_t xa[C::kFI];
+  bf16x8_t xa[C::kFI], xt;
   uint4 wc[C::kFG][4];
-  auto read_frags = [&](int slice) {
+  auto read_frags = [&](int slice, auto ex) {
     const unsigned char* st = smem + (slice % S) * C::kStage;
 #pragma unroll
     for (int i = 0; i < C::kFI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(st + xoff[i]);
+    if (decltype(ex)::value) xt = *reinterpret_cast<const bf16x8_t*>(st + xoff_t);
 #pragma unroll
     for (int g = 0; g < C::kFG; ++g) {
       uint2 wraw[8];
@@ -720,14 +814,16 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
       transpose_8x4_bf16(wraw, wc[g]);
     }
   };
-  f32x4_t acc[C::kFI][C::kFG][4];
+  f32x4_t acc[C::kFI][C::kFG][4], acct[C::kFG][4];
 #pragma unroll
-  for (int i = 0; i < C::kFI; ++i)
+  for (int g = 0; g < C::kFG; ++g)
 #pragma unroll
-    for (int g = 0; g < C::kFG; ++g)
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][g][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  auto multiply = [&]() {
+      for (int i = 0; i < C::kFI; ++i) acc[i][g][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      acct[g][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    }
+  auto multiply = [&](auto ex) {
 #pragma unroll
     for (int i = 0; i < C::kFI; ++i)
 #pragma unroll
@@ -736,91 +832,184 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int j = 0; j < 4; ++j)
           acc[i][g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               *reinterpret_cast<bf16x8_t*>(&wc[g][j]), xa[i], acc[i][g][j], 0, 0, 0);
+    if (decltype(ex)::value) {
+#pragma unroll
+      for (int g = 0; g < C::kFG; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acct[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<bf16x8_t*>(&wc[g][j]), xt, acct[g][j], 0, 0, 0);
+    }
   };
 
-#pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t);
-  wait_vmcnt<kInFlight>();
-  bar();  // barrier 0: slice 0 has landed
+  // The schedule; `ex` (compile time) adds the tail fragment and its DMA op.
   // Four straight-line loops (half x active), each with the same barriers and
   // DMA as its partner, so no loop carries a branch.
-  if (wm == 0) {
-    if (wave_active) {
-      read_frags(0);
-      issue(S - 1);
-      bar();
-      for (int s = 0; s < nsteps; ++s) {
-        multiply();
-        wait_vmcnt<kInFlight>();
+  auto run = [&](auto ex) {
+    constexpr int kInFlight = (S - 2) * (C::kPerStage + (decltype(ex)::value ? 1 : 0));
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) issue(t, ex);
+    wait_vmcnt<kInFlight>();
+    bar();  // barrier 0: slice 0 has landed
+    if (wm == 0) {
+      if (wave_active) {
+        read_frags(0, ex);
+        issue(S - 1, ex);
         bar();
-        read_frags(s + 1);
-        issue(s + S);
+        for (int s = 0; s < nsteps; ++s) {
+          multiply(ex);
+          wait_vmcnt<kInFlight>();
+          bar();
+          read_frags(s + 1, ex);
+          issue(s + S, ex);
+          bar();
+        }
+      } else {
+        issue(S - 1, ex);
         bar();
+        for (int s = 0; s < nsteps; ++s) {
+          wait_vmcnt<kInFlight>();
+          bar();
+          issue(s + S, ex);
+          bar();
+        }
       }
+      bar();  // matches the second half's last barrier
     } else {
-      issue(S - 1);
       bar();
-      for (int s = 0; s < nsteps; ++s) {
+      issue(S - 1, ex);
+      if (wave_active) {
+        read_frags(0, ex);
         wait_vmcnt<kInFlight>();
         bar();
-        issue(s + S);
+        for (int s = 0; s < nsteps; ++s) {
+          multiply(ex);
+          bar();
+          read_frags(s + 1, ex);
+          issue(s + S, ex);
+          wait_vmcnt<kInFlight>();
+          bar();
+        }
+      } else {
+        wait_vmcnt<kInFlight>();
         bar();
+        for (int s = 0; s < nsteps; ++s) {
+          bar();
+          issue(s + S, ex);
+          wait_vmcnt<kInFlight>();
+          bar();
+        }
       }
     }
-    bar();  // matches the second half's last barrier
-  } else {
-    bar();
-    issue(S - 1);
-    if (wave_active) {
-      read_frags(0);
-      wait_vmcnt<kInFlight>();
-      bar();
-      for (int s = 0; s < nsteps; ++s) {
-        multiply();
-        bar();
-        read_frags(s + 1);
-        issue(s + S);
-        wait_vmcnt<kInFlight>();
-        bar();
+  };
+  if (extra) run(std::true_type{});
+  else run(std::false_type{});
+  wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
+
+  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+  // Fragment f of this wave: 0 .. kFI-1 are rows wm*kWM + 16f + ci, kFI is
+  // the tail fragment (rows BM + 16*wm + ci).
+  auto frag_row = [&](int f) { return f < C::kFI ? wm * C::kWM + f * 16 + ci : C::kBM + wm * 16 + ci; };
+  auto frag_acc = [&](int f, int g, float* a16) {  // MFMA j, output row 4*kq + r -> column 4r + j
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a16[4 * r + j] = f < C::kFI ? acc[f][g][j][r] : acct[g][j][r];
+  };
+  auto store_out = [&](int f, int g, const float* acc16) {
+    const int ml = frag_row(f);
+    const int nb = tile.n0 + wn * C::kWN + g * 64 + 16 * kq;
+    if (ml >= tile.rows || nb >= N) return;  // N is a multiple of 16 here
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float t = acc16[q] * sc;
+      v[q] = (relu && t < 0.f) ? 0.f : t;
+    }
+    bf16_t* o = out + (tile.row0 + ml) * (int64_t)N + nb;
+    reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                                                pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+  };
+  if (wk.S == 1) {
+    if (!wave_active) return;
+#pragma unroll
+    for (int f = 0; f < C::kFI + 1; ++f) {
+      if (f == C::kFI && !extra) continue;  // compile-time f keeps the accumulators in registers
+#pragma unroll
+      for (int g = 0; g < C::kFG; ++g) {
+        float a16[16];
+        frag_acc(f, g, a16);
+        store_out(f, g, a16);
       }
-    } else {
-      wait_vmcnt<kInFlight>();
-      bar();
-      for (int s = 0; s < nsteps; ++s) {
-        bar();
-        issue(s + S);
-        wait_vmcnt<kInFlight>();
-        bar();
+    }
+    return;
+  }
+  // Split tile: every part stores its fp32 partial tile [BM + kFold][BN];
+  // the last part to arrive sums the S partials in part order (its own from
+  // registers), so the result does not depend on which part finished last.
+  // Partials are written through to memory and read back past L1/L2
+  // (system-scope cache policy): once a part's stores have completed it
+  // counts itself with a device-scope atomic, and the part that brings the
+  // count to S reads everything without the L2 writeback and invalidate a
+  // device-scope fence would cost every tile running on its XCD.
+  constexpr int kTileF = (C::kBM + C::kFold) * C::kBN;
+  constexpr int kSysScope = 17;  // cache policy sc0 | sc1
+  const __amdgpu_buffer_rsrc_t prsrc =
+      make_rsrc(split_ws + (int64_t)wk.rtile * wk.S * kTileF, (uint32_t)(wk.S * kTileF * 4));
+  auto part_off = [&](int q, int f, int g) {  // byte offset of a lane's 16 partial columns
+    return (uint32_t)((q * kTileF + frag_row(f) * C::kBN + wn * C::kWN + g * 64 + 16 * kq) * 4);
+  };
+  if (wave_active) {
+#pragma unroll
+    for (int f = 0; f < C::kFI + 1; ++f) {
+      if (f == C::kFI && !extra) continue;  // compile-time f keeps the accumulators in registers
+#pragma unroll
+      for (int g = 0; g < C::kFG; ++g) {
+        float a16[16];
+        frag_acc(f, g, a16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4_t v = {a16[4 * r], a16[4 * r + 1], a16[4 * r + 2], a16[4 * r + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), prsrc,
+                                                 part_off(wk.part, f, g) + r * 16, 0, kSysScope);
+        }
       }
     }
   }
-  wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
-  if (!wave_active) return;
-
-  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+  wait_vmcnt<0>();  // this wave's partials have reached memory
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(split_cnt + wk.rtile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             wk.S - 1;
+  __syncthreads();
+  if (!s_last || !wave_active) return;
 #pragma unroll
-  for (int i = 0; i < C::kFI; ++i) {
-    const int ml = wm * C::kWM + i * 16 + ci;
-    if (ml >= tile.rows) continue;
-    const int64_t m = tile.row0 + ml;
+  for (int f = 0; f < C::kFI + 1; ++f) {
+    if (f == C::kFI && !extra) continue;  // compile-time f keeps the accumulators in registers
 #pragma unroll
     for (int g = 0; g < C::kFG; ++g) {
-      // MFMA j, output row 4*kq + r  ->  column nb + 4r + j
-      const int nb = tile.n0 + wn * C::kWN + g * 64 + 16 * kq;
-      if (nb >= N) continue;  // N is a multiple of 16 here: a lane's 16 columns are all in or all out
-      float v[16];
+      float own[16], a16[16];
+      frag_acc(f, g, own);
+      for (int q = 0; q < wk.S; ++q) {
+        float p16[16];
+        if (q == wk.part) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+          for (int c = 0; c < 16; ++c) p16[c] = own[c];
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float t = acc[i][g][j][r] * sc;
-          v[4 * r + j] = (relu && t < 0.f) ? 0.f : t;
+          for (int r = 0; r < 4; ++r) {
+            const f32x4_t v = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prsrc, part_off(q, f, g) + r * 16, 0, kSysScope));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p16[4 * r + j] = v[j];
+          }
         }
-      bf16_t* o = out + m * N + nb;
-      reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-      reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
-                                                  pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+#pragma unroll
+        for (int c = 0; c < 16; ++c) a16[c] = q == 0 ? p16[c] : a16[c] + p16[c];
+      }
+      store_out(f, g, a16);
     }
   }
 }
@@ -1310,23 +1499,48 @@ moe_status launch_tiled(const void* a, const float* as, const void* w, const flo
   return launch_status();
 }
 
+// Split-K scratch of the bf16 ping-pong kernel: ncu fp32 partial tiles, then
+// ncu arrival counters.
+size_t split_ws_floats(int ncu) { return (size_t)ncu * (256 + 32) * 256; }  // tiles with folded tails
+
+__global__ void split_reset_kernel(int* __restrict__ cnt, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = 0;
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <class C>
 moe_status launch_pp(const void* a, const float* as, const void* w, const float* ws,
                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                     hipStream_t s) {
+                     void* split, hipStream_t s) {
+  static_assert(C::kBM == 256 && C::kBN == 256, "split scratch is sized for 256 x 256 tiles");
   static bool attr_done = false;
   if (!attr_done) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp_kernel<C>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     attr_done = true;
   }
+  const int ncu = device_cus();
+  float* sws = reinterpret_cast<float*>(split);
+  int* cnt = sws ? reinterpret_cast<int*>(sws + split_ws_floats(ncu)) : nullptr;
+  if (cnt) hipLaunchKernelGGL(split_reset_kernel, dim3(1), dim3(256), 0, s, cnt, ncu);
   const int64_t mt_max = cdiv64(A, C::kBM) + (e < A ? e : A);
-  const int64_t blocks = mt_max * cdiv64(N, C::kBN);
+  const int64_t blocks = mt_max * cdiv64(N, C::kBN) + (sws ? 3 * (int64_t)ncu / 4 : 0);
   const int64_t grid = cdiv64(blocks, 8) * 8;
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(gmm_pp_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
                      (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
-                     relu, (bf16_t*)out);
+                     relu, (bf16_t*)out, sws, cnt, ncu);
   return launch_status();
 }
 
@@ -1374,9 +1588,33 @@ moe_status launch_stream_al(bool al, const void* a, const float* as, const void*
 // Rows per expert at or below which the weight-streaming kernel is used.
 constexpr int kStreamMaxAvgRows = 48;
 
+// Kernel family moe_gmm uses for a shape.
+enum class GmmPath { F32, STREAM, PP, PP8, TILED };
+GmmPath gmm_path(moe_dtype in_dt, int e, int A, int Hin, int N) {
+  if (in_dt == MOE_F32) return GmmPath::F32;
+  const int elem = in_dt == MOE_BF16 ? 2 : 1;
+  if (in_dt == MOE_BF16 && (int64_t)A <= (int64_t)kStreamMaxAvgRows * e) return GmmPath::STREAM;
+  // buffer-load path: 16-byte aligned rows and each expert's weight matrix under 2 GiB
+  const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0) &&
+                  ((int64_t)Hin * N * elem < (1ll << 31));
+#if MOE_GMM_BF16 == 1
+  if (elem == 2 && al && N % 16 == 0) return GmmPath::PP;
+#endif
+#if MOE_GMM_FP8 == 1
+  if (elem == 1 && al && N % 16 == 0) return GmmPath::PP8;
+#endif
+  return GmmPath::TILED;
+}
+
+size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N) {
+  if (!MOE_GMM_SPLIT || A == 0 || gmm_path(in_dt, e, A, Hin, N) != GmmPath::PP) return 0;
+  const int ncu = device_cus();
+  return split_ws_floats(ncu) * sizeof(float) + (size_t)ncu * sizeof(int);
+}
+
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
-                      moe_act act, void* out, moe_dtype out_dt, hipStream_t s) {
+                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s) {
   if (A == 0) return MOE_OK;
   const int relu = act == MOE_ACT_RELU;
   if (in_dt == MOE_F32) {
@@ -1403,7 +1641,7 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
 #if MOE_GMM_BF16 == 1
   if (elem == 2 && al && N % 16 == 0) {
     typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
-    return launch_pp<CP>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+    return launch_pp<CP>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s);
   }
 #endif
 #if MOE_GMM_FP8 == 1

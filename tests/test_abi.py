@@ -23,7 +23,8 @@ def declared_entry_points():
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
     for n in ("moe_route", "moe_permute", "moe_gmm", "moe_combine", "moe_layer",
-              "moe_route_workspace_size", "moe_permute_workspace_size", "moe_layer_workspace_size",
+              "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
+              "moe_layer_workspace_size",
               "moe_status_string", "moe_version"):
         assert n in names
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10100
+    assert moe.lib().moe_version() == 10200
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -147,8 +148,27 @@ def test_permute_validation(kw, status):
 
 
 def gmm(a=P, adt=moe.BF16, aq=0, asc=None, w=P, wdt=moe.BF16, wq=0, wsc=None, off=P, e=8, A=100,
-        Hin=64, N=64, act=moe.ACT_RELU, out=P, odt=moe.BF16):
-    return L.moe_gmm(a, adt, aq, asc, w, wdt, wq, wsc, off, e, A, Hin, N, act, out, odt, None)
+        Hin=64, N=64, act=moe.ACT_RELU, out=P, odt=moe.BF16, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        try:
+            ws_bytes = moe.gmm_workspace_size(adt, e, A, Hin, N)
+        except moe.MoeError:
+            ws_bytes = 0
+    return L.moe_gmm(a, adt, aq, asc, w, wdt, wq, wsc, off, e, A, Hin, N, act, out, odt, ws, ws_bytes, None)
+
+
+def test_gmm_workspace_size():
+    # many rows per expert, bf16, aligned: the tiled kernel may split its last round
+    n = moe.gmm_workspace_size(moe.BF16, 8, 8192, 4096, 14336)
+    assert n >= 256 * 256 * 4 * 8       # room for several fp32 partial tiles
+    # streaming (few rows per expert), fp32 and E4M3 paths need none
+    assert moe.gmm_workspace_size(moe.BF16, 128, 2048, 4096, 1536) == 0
+    assert moe.gmm_workspace_size(moe.F32, 8, 8192, 128, 256) == 0
+    assert moe.gmm_workspace_size(moe.FP8_E4M3, 32, 65536, 7168, 2048) == 0
+    assert moe.gmm_workspace_size(moe.BF16, 8, 0, 4096, 14336) == 0
+    with pytest.raises(moe.MoeError) as ei:
+        moe.gmm_workspace_size(moe.BF16, 0, 8192, 4096, 14336)
+    assert ei.value.status == moe.ERR_BAD_SHAPE
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -176,6 +196,9 @@ def gmm(a=P, adt=moe.BF16, aq=0, asc=None, w=P, wdt=moe.BF16, wq=0, wsc=None, of
     (dict(out=None), moe.ERR_NULL_POINTER),
     (dict(w=MIS), moe.ERR_MISALIGNED),
     (dict(off=MIS), moe.ERR_MISALIGNED),
+    (dict(A=5000, ws=None), moe.ERR_NULL_POINTER),                  # tiled bf16 path needs scratch
+    (dict(A=5000, ws_bytes=16), moe.ERR_WORKSPACE_TOO_SMALL),
+    (dict(A=5000, ws=MIS), moe.ERR_MISALIGNED),
 ])
 def test_gmm_validation(kw, status):
     assert gmm(**kw) == status

@@ -192,6 +192,9 @@ GMM_CASES = [
     ("bf16_tiled_ragged", [300, 0, 1, 555], 640, 520, "bf16"),
     ("bf16_tiled_unaligned", [270, 3, 0, 400], 300, 130, "bf16"),
     ("bf16_tiled_ktail", [513], 200, 264, "bf16"),
+    # last row pieces of 1..32 rows ride on the tile before (257, 513, 800 = 768+32,
+    # 1055 = 1024+31, 288); 289 = 256+33 gets a tile of its own
+    ("bf16_fold_tails", [257, 513, 800, 1055, 288, 289], 256, 320, "bf16"),
     ("bf16_stream", [5, 0, 17, 30, 1, 0, 9, 12, 3, 31, 0, 2, 8, 16, 4, 7], 512, 320, "bf16"),
     ("bf16_stream_unaligned", [3, 0, 14, 6, 1, 9], 90, 100, "bf16"),
     ("bf16_stream_overflow_rows", [2, 80, 1, 0, 3, 1, 2, 3], 256, 192, "bf16"),
@@ -217,6 +220,7 @@ def test_gmm_parity(case, act):
 
 @pytest.mark.parametrize("dt,counts,Hin,N", [
     ("bf16", [300, 0, 1, 555], 512, 264),   # tiled
+    ("bf16", [257, 0, 800, 289], 256, 256),   # tiled, folded tails
     ("bf16", [5, 0, 17, 30, 2, 1], 256, 128),  # streaming
     ("fp8", [200, 0, 333], 512, 256),       # tiled E4M3, power-of-two scales
 ])
@@ -256,6 +260,51 @@ def test_gmm_deterministic():
     o1 = to_host(moe.gmm(a, w, to_dev(off)))
     o2 = to_host(moe.gmm(a, w, to_dev(off)))
     assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("act", [moe.ACT_NONE, moe.ACT_RELU], ids=["none", "relu"])
+def test_gmm_split_last_round(act):
+    """Two experts of 1900 rows (8 row tiles each, the last 108 rows), N = 5120:
+    320 tiles of 256 x 256 on 256 CUs leave 64 for a partial last round, which
+    the bf16 tiled kernel splits over 4 blocks along K (17 K slices: parts of
+    4, 4, 4 and 5). Rows of every row tile, last rows of both experts
+    included, against the oracle; a second run must be bit-identical."""
+    counts = [1900, 1900]
+    Hin, N = 544, 5120
+    off = _offsets(counts)
+    A = int(off[-1])
+    a = synth.normal(430, (A, Hin), dtype="bf16")
+    w = synth.normal(431, (2, Hin, N), math.sqrt(1.0 / Hin), dtype="bf16")
+    assert moe.gmm_workspace_size(moe.BF16, 2, A, Hin, N) > 0
+    rows = np.unique(np.concatenate([np.arange(0, A, 97), np.arange(0, A, 256) + 255,
+                                     [1899, 1900, A - 1]])).astype(np.int32)
+    rows = rows[rows < A]
+    ad, wd, od = to_dev(a), to_dev(w), to_dev(off)
+    o1 = to_host(moe.gmm(ad, wd, od, act=act))
+    o2 = to_host(moe.gmm(ad, wd, od, act=act))
+    assert np.array_equal(o1, o2)
+    ref = oracle.gmm(a, w, off, act=act, rows=rows, nthreads=8)
+    assert normwise_err(o1[rows], ref) <= 8e-3
+
+
+def test_gmm_fold_and_split():
+    """Experts of 7*256 + 20 rows: each last tile carries 276 rows; 14 row
+    tiles x 20 column tiles = 280 tiles leave 24 for a split last round, and
+    those are folded tiles of the second expert."""
+    counts = [1812, 1812]
+    Hin, N = 544, 5120
+    off = _offsets(counts)
+    A = int(off[-1])
+    a = synth.normal(440, (A, Hin), dtype="bf16")
+    w = synth.normal(441, (2, Hin, N), math.sqrt(1.0 / Hin), dtype="bf16")
+    rows = np.unique(np.concatenate([np.arange(1780, 1812), np.arange(A - 40, A),
+                                     np.arange(0, A, 131)])).astype(np.int32)
+    ad, wd, od = to_dev(a), to_dev(w), to_dev(off)
+    o1 = to_host(moe.gmm(ad, wd, od, act=moe.ACT_RELU))
+    o2 = to_host(moe.gmm(ad, wd, od, act=moe.ACT_RELU))
+    assert np.array_equal(o1, o2)
+    ref = oracle.gmm(a, w, off, act=moe.ACT_RELU, rows=rows, nthreads=8)
+    assert normwise_err(o1[rows], ref) <= 8e-3
 
 
 # ---------------------------------------------------------------- combine
