@@ -1024,13 +1024,19 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
 // 128-255, and the two halves alternate multiply and memory phases between
 // barriers exactly as in gmm_pp_kernel (one phase = 16 MFMAs = 512 cycles).
 //
-// Weights are read 4 bytes (4 columns) per lane from 32 consecutive K rows
-// and byte-transposed in registers into four 32-byte fragments, so MFMA j's
-// row i is output column 4i + j and a lane ends with 16 consecutive output
-// columns. LDS layout (a bank model of the measured gfx950 rule gives no
-// conflicts for either read): activation row m holds its eight 16-byte
-// chunks at positions c ^ ((m/2)%2 + 4*((m/4)%2)); weight K row k sits at
-// LDS row k ^ ((k/32)%2) with its two 64-byte halves swapped when (k/64)%2.
+// Weights go through gfx950's transposing LDS read (ds_read_b64_tr_b8). In
+// each group of 16 lanes, lane s names 8 bytes; the 16 x 8-byte pieces are
+// taken as 8 rows of 16 bytes (row b = the pieces of lanes 2b and 2b+1) and
+// lane l receives column l: byte b of its result is byte l of row b
+// (measured on the device). With lanes 2b, 2b+1 naming the two halves of
+// K row k0 + b over 16 consecutive output columns, lane l gets column l's K
+// values k0 .. k0+7, which is an MFMA fragment piece; four reads fill a
+// 32-byte fragment. MFMA j's row i is then output column 16j + i, and a
+// lane ends with 4 consecutive output columns per MFMA.
+// LDS layout: activation row m holds its eight 16-byte chunks at positions
+// c ^ ((m/2)%2 + 4*((m/4)%2)); weight K row k holds chunk c at position
+// c ^ ((k/2)%4 + 4*((k/32)%2)), so the 16 rows that lanes 0-31 (or 32-63)
+// of one transposing read touch fall in distinct banks.
 
 struct Pp8Cfg {
   static constexpr int kBM = 256, kBN = 128;
@@ -1047,18 +1053,7 @@ struct Pp8Cfg {
 };
 
 __device__ __forceinline__ int pp8_xswz(int m) { return ((m >> 1) & 1) | (((m >> 2) & 1) << 2); }
-
-// 4 rows x 4 bytes (d[r] = row r, byte c = column c) -> 4 columns x 4 rows.
-__device__ __forceinline__ void transpose_4x4_u8(const uint32_t d[4], uint32_t o[4]) {
-  const uint32_t a = perm_b32(d[1], d[0], 0x05010400u);  // d0[0] d1[0] d0[1] d1[1]
-  const uint32_t b = perm_b32(d[1], d[0], 0x07030602u);  // d0[2] d1[2] d0[3] d1[3]
-  const uint32_t c = perm_b32(d[3], d[2], 0x05010400u);
-  const uint32_t e = perm_b32(d[3], d[2], 0x07030602u);
-  o[0] = perm_b32(c, a, 0x05040100u);
-  o[1] = perm_b32(c, a, 0x07060302u);
-  o[2] = perm_b32(e, b, 0x05040100u);
-  o[3] = perm_b32(e, b, 0x07060302u);
-}
+__device__ __forceinline__ int pp8_wswz(int k) { return ((k >> 1) & 3) | (((k >> 5) & 1) << 2); }
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp8_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
@@ -1100,11 +1095,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
   for (int q = 0; q < C::kWDma; ++q) {
     const int kb = (wave * C::kWDma + q) * 1024 + lane * 16;
-    const int prow = kb >> 7, pc = (kb >> 4) & 7;
-    const int lrow = prow ^ ((prow >> 5) & 1);
-    const int lc = pc ^ (((lrow >> 6) & 1) << 2);
-    const int nb = tile.n0 + lc * 16;
-    w_voff[q] = (uint32_t)lrow * (uint32_t)N + (uint32_t)nb + (nb < N ? 0u : kOOB);
+    const int k = kb >> 7, pc = (kb >> 4) & 7;  // LDS row (= K row) and chunk position
+    const int nb = tile.n0 + (pc ^ pp8_wswz(k)) * 16;
+    w_voff[q] = (uint32_t)k * (uint32_t)N + (uint32_t)nb + (nb < N ? 0u : kOOB);
   }
   // Past-the-end slices are issued too (out-of-range loads write zeros).
   auto issue = [&](int step) {
@@ -1137,11 +1130,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
       const int m = half * 128 + wm2 * 64 + i * 16 + ci;
       xoff[i][h] = m * C::kKB + (((2 * kq + h) ^ pp8_xswz(m)) << 4);
     }
-  // weight K row 32kq + r sits at LDS row 32kq + (r ^ (kq & 1)); its column
-  // dword wn*16 + ci moves to the other 64-byte half when kq >= 2
-  const int pdw = (wn * 16 + ci) ^ ((kq >> 1) << 4);
-  const int wrow0 = C::kLdsA + 32 * kq * C::kBN + pdw * 4;
-  const int wpar = (kq & 1) * C::kBN;
+  // transposing weight reads: this lane names K row 32kq + 8t + ci/2 (t = 0..3),
+  // half ci%2 of output-column chunk 4wn + j
+  const int wk0 = 32 * kq + ci / 2;
+  const int wsw = pp8_wswz(wk0);  // the same for every t
+  const int wrow0 = C::kLdsA + wk0 * C::kBN + 8 * (ci & 1);
+  int wch[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wch[j] = ((4 * wn + j) ^ wsw) * 16;
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
   i32x8_t xa[4], wf[4];
   auto read_frags = [&](int slice) {
     const unsigned char* st = smem + (slice % S) * C::kStage;
@@ -1151,20 +1148,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
       const uint4 hi = *reinterpret_cast<const uint4*>(st + xoff[i][1]);
       xa[i] = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    const unsigned char* we = st + wrow0 + wpar;  // even r: LDS row 32kq + r + (kq & 1)
-    const unsigned char* wo = st + wrow0 - wpar;  // odd r:  LDS row 32kq + r - (kq & 1)
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      uint32_t d[4], o[4];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = 4 * g + r;
-        d[r] = *reinterpret_cast<const uint32_t*>(((rr & 1) ? wo : we) + rr * C::kBN);
+      for (int t = 0; t < 4; ++t) {
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(st + wrow0 + wch[j] + t * 8 * C::kBN));
+        wf[j][2 * t] = v.x;
+        wf[j][2 * t + 1] = v.y;
       }
-      transpose_4x4_u8(d, o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j][g] = (int)o[j];
-    }
   };
   f32x4_t acc[4][4];
 #pragma unroll
@@ -1243,22 +1235,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
     if (ml >= tile.rows) continue;
     const int64_t m = tile.row0 + ml;
-    // MFMA j, output row 4*kq + r  ->  column nb + 4r + j
-    const int nb = tile.n0 + wn * 64 + 16 * kq;
-    if (nb >= N) continue;  // N is a multiple of 16 here
-    float v[16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int j = 0; j < 4; ++j) {
+      // MFMA j, output row 4*kq + r  ->  column nb + r
+      const int nb = tile.n0 + wn * 64 + 16 * j + 4 * kq;
+      if (nb >= N) continue;  // N is a multiple of 16 here
+      float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int r = 0; r < 4; ++r) {
         const float t = acc[i][j][r] * sc;
-        v[4 * r + j] = (relu && t < 0.f) ? 0.f : t;
+        v[r] = (relu && t < 0.f) ? 0.f : t;
       }
-    bf16_t* o = out + m * N + nb;
-    reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
-                                                pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+      *reinterpret_cast<uint2*>(out + m * N + nb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
   }
 }
 
