@@ -7,8 +7,8 @@
 //
 // Weights arrive as (e, Hin, N) with N contiguous, the shape the page gives
 // for gmmWeight. MFMA wants both operands contiguous in the reduction
-// dimension, so every kernel transposes weight data in registers with
-// v_perm_b32 on its way in.
+// dimension, so weight data is transposed on its way in: in registers with
+// v_perm_b32, or (E4M3 ping-pong kernel) by the transposing LDS read.
 //
 // Kernels
 //  * gmm_pp_kernel (bf16, many rows per expert, aligned): 256 x 256 output
@@ -18,8 +18,11 @@
 //    x 4 columns per lane and transposed with v_perm_b32, so MFMA j's row i
 //    is output column 4i + j and each lane ends with 16 consecutive output
 //    columns (32-byte stores).
+//    An expert's last row piece of at most 32 rows rides on the tile before
+//    it, and a small last round of tiles is split 4 ways along K.
 //  * gmm_pp8_kernel (E4M3, aligned): the same scheme on 16x16x128 f8f6f4
-//    MFMAs with 256 x 128 tiles, 128-deep K slices and a 3-slot ring.
+//    MFMAs with 256 x 128 tiles, 128-deep K slices and a 3-slot ring;
+//    weight fragments come from ds_read_b64_tr_b8.
 //  * gmm_tiled_kernel (bf16 / E4M3 shapes the DMA kernels do not take:
 //    unaligned rows or columns): register-staged 256 x 256 tiles, 128-byte K
 //    slices double-buffered in LDS, weights transposed on their way in.
