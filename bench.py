@@ -141,8 +141,7 @@ def bench_layer(args, dev):
     bufs = {"counts": torch.empty((E,), dtype=torch.int32, device=dev),
             "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
             "perm_src": torch.empty((A,), dtype=torch.int32, device=dev),
-            "perm_dst": torch.empty((A,), dtype=torch.int32, device=dev),
-            "x_perm": torch.empty((A, H), dtype=tdt, device=dev)}
+            "perm_dst": torch.empty((A,), dtype=torch.int32, device=dev)}
     hm = torch.empty((A, F), dtype=tdt, device=dev)
     yp = torch.empty((A, H), dtype=tdt, device=dev)
     y = torch.empty((T, H), dtype=tdt, device=dev)
@@ -160,10 +159,11 @@ def bench_layer(args, dev):
         moe.route(x, wr, K, bias=bias, topk_idx=idx, topk_gate=gate, ws=rws)
         if ev is not None:
             ev[1].record()
-        moe.permute(idx, E, x=x, ws=pws, out=bufs)
+        moe.permute(idx, E, ws=pws, out=bufs)  # indices only: GEMM 1 gathers the token rows
         if ev is not None:
             ev[2].record()
-        moe.gmm(bufs["x_perm"], w1, bufs["offsets"], act=moe.ACT_RELU, out=hm, ws=gws)
+        moe.gmm(x, w1, bufs["offsets"], act=moe.ACT_RELU, out=hm, ws=gws, rows=bufs["perm_src"],
+                row_div=K)
         if ev is not None:
             ev[3].record()
         moe.gmm(hm, w2, bufs["offsets"], out=yp, ws=gws)
@@ -219,7 +219,7 @@ def bench_layer(args, dev):
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(args.workload)}
     bytes_stage = {
         "route": T * H * es + H * E * es + T * K * 8,
-        "permute": T * K * 4 * 3 + T * H * es + A * H * es,
+        "permute": T * K * 4 * 3,
         "combine": A * H * es + T * H * es + T * K * 8,
     }
     kernels = {n: {"ms": per[n]} for n in names}

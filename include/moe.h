@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10200 /* 1.2.0: moe_route and moe_gmm take workspaces */
+#define MOE_VERSION 10300 /* 1.3.0: moe_gmm_gather (grouped GEMM reading rows through an index) */
 
 typedef enum {
   MOE_OK = 0,
@@ -161,6 +161,27 @@ moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const floa
                    const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
                    const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
                    moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_gmm_gather — moe_gmm whose grouped row r is row row_src[r] / row_div of
+ * a, so the dispatch copy (x_perm[perm_dst[t*K+k]] = x[t], "Part 5",
+ * section 1.2 token dispatch) happens inside the GEMM's loads: with
+ * row_src = perm_src of moe_permute and row_div = K, grouped row r is token
+ * perm_src[r] / K, exactly the row moe_permute would have copied there.
+ *   a        device (a_rows,Hin) in a_dt; a_rows * Hin * element size must be
+ *            below 2^31 bytes (else MOE_ERR_UNSUPPORTED)
+ *   row_src  device (A) int32; an entry whose quotient is outside
+ *            [0, a_rows) (not checked on the host) reads as a zero row
+ *   row_div  >= 1
+ * Everything else (types, scales, offsets, act, out, workspace, errors) is
+ * as for moe_gmm, with the same workspace size; results equal moe_gmm on the
+ * gathered rows bit for bit.
+ */
+moe_status moe_gmm_gather(const void* a, int a_rows, const int32_t* row_src, int row_div, moe_dtype a_dt,
+                          moe_quant_mode a_q, const float* a_scale, const void* w, moe_dtype w_dt,
+                          moe_quant_mode w_q, const float* w_scale, const int32_t* offsets, int e, int A,
+                          int Hin, int N, moe_act act, void* out, moe_dtype out_dt, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * moe_combine — back to token order.

@@ -27,7 +27,7 @@ ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
-           "moe_combine", "moe_layer_workspace_size", "moe_layer")
+           "moe_gmm_gather", "moe_combine", "moe_layer_workspace_size", "moe_layer")
 
 
 class MoeError(RuntimeError):
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.moe_gmm_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_gmm.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, vp,
                               i32, vp, sz, vp]
+        L.moe_gmm_gather.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32,
+                                     i32, i32, i32, vp, i32, vp, sz, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
         L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
@@ -173,11 +175,16 @@ def gmm_workspace_size(a_dt, e, A, Hin, N) -> int:
     return n.value
 
 
-def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=None, stream=None):
+def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=None, stream=None,
+        rows=None, row_div=1):
     """moe_gmm over w (e,Hin,N). Scales (1-element fp32 device tensors) select
     MOE_QUANT_PER_TENSOR. Output: fp32 for fp32 inputs, else bf16. ws: a device
-    buffer of at least gmm_workspace_size() bytes, allocated here when None."""
+    buffer of at least gmm_workspace_size() bytes, allocated here when None.
+    rows (int32 device tensor, one entry per grouped row): moe_gmm_gather, grouped
+    row r is row rows[r] // row_div of a."""
     A, Hin = a.shape
+    if rows is not None:
+        A = rows.numel()
     e, Hw, N = w.shape
     if Hw != Hin:
         raise ValueError("a and w disagree on Hin")
@@ -191,6 +198,12 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=No
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     aq = QUANT_PER_TENSOR if a_scale is not None else QUANT_NONE
     wq = QUANT_PER_TENSOR if w_scale is not None else QUANT_NONE
+    if rows is not None:
+        st = lib().moe_gmm_gather(_ptr(a), a.shape[0], _ptr(rows), row_div, adt, aq, _ptr(a_scale),
+                                  _ptr(w), wdt, wq, _ptr(w_scale), _ptr(offsets), e, A, Hin, N, act,
+                                  _ptr(out), odt, _ptr(ws), nbytes, _stream(stream))
+        _check(st, "moe_gmm_gather")
+        return out
     st = lib().moe_gmm(_ptr(a), adt, aq, _ptr(a_scale), _ptr(w), wdt, wq, _ptr(w_scale),
                        _ptr(offsets), e, A, Hin, N, act, _ptr(out), odt, _ptr(ws), nbytes,
                        _stream(stream))

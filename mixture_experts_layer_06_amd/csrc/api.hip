@@ -168,10 +168,12 @@ moe_status moe_gmm_workspace_size(moe_dtype a_dt, int e, int A, int Hin, int N, 
   return MOE_OK;
 }
 
-moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
-                   const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
-                   const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
-                   moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// Shared argument checks and launch of moe_gmm / moe_gmm_gather.
+moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
+                       const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
+                       const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                       moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream, const Gather* gx) {
   if (!any_dtype_ok(a_dt) || !any_dtype_ok(w_dt) || !any_dtype_ok(out_dt)) return MOE_ERR_BAD_DTYPE;
   const bool pair_ok = (a_dt == MOE_F32 && w_dt == MOE_F32 && out_dt == MOE_F32) ||
                        (a_dt == MOE_BF16 && w_dt == MOE_BF16 && out_dt == MOE_BF16) ||
@@ -184,6 +186,11 @@ moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const floa
   if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
   if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
   if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
+  if (gx) {
+    if (gx->div < 1 || gx->rows < 0 || (A > 0 && gx->rows < 1)) return MOE_ERR_BAD_SHAPE;
+    // the gathered rows are addressed with 32-bit byte offsets
+    if ((int64_t)gx->rows * Hin * dtype_size(a_dt) >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  }
   if (a_q == MOE_QUANT_PER_TENSOR) REQUIRE_PTR(a_scale);
   if (w_q == MOE_QUANT_PER_TENSOR) REQUIRE_PTR(w_scale);
   if (A == 0) return MOE_OK;
@@ -191,6 +198,7 @@ moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const floa
   REQUIRE_PTR(w);
   REQUIRE_PTR(offsets);
   REQUIRE_PTR(out);
+  if (gx) REQUIRE_PTR(gx->src);
   const size_t need = gmm_ws_bytes(a_dt, e, A, Hin, N);
   if (need > 0) {
     REQUIRE_PTR(ws);
@@ -201,11 +209,31 @@ moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const floa
   REQUIRE_ALIGNED(offsets);
   REQUIRE_ALIGNED(out);
   REQUIRE_ALIGNED(ws);
+  if (gx) REQUIRE_ALIGNED(gx->src);
   // scales are 4-byte device scalars: natural alignment suffices
   const float* as = a_q == MOE_QUANT_PER_TENSOR ? a_scale : nullptr;
   const float* wsc = w_q == MOE_QUANT_PER_TENSOR ? w_scale : nullptr;
   return launch_gmm(a, a_dt, as, w, wsc, offsets, e, A, Hin, N, act, out, out_dt, need > 0 ? ws : nullptr,
-                    (hipStream_t)stream);
+                    (hipStream_t)stream, gx ? *gx : Gather{nullptr, 1, 0});
+}
+}  // namespace
+
+moe_status moe_gmm(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
+                   const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
+                   const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                   moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+  return gmm_checked(a, a_dt, a_q, a_scale, w, w_dt, w_q, w_scale, offsets, e, A, Hin, N, act, out,
+                     out_dt, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_gmm_gather(const void* a, int a_rows, const int32_t* row_src, int row_div, moe_dtype a_dt,
+                          moe_quant_mode a_q, const float* a_scale, const void* w, moe_dtype w_dt,
+                          moe_quant_mode w_q, const float* w_scale, const int32_t* offsets, int e, int A,
+                          int Hin, int N, moe_act act, void* out, moe_dtype out_dt, void* ws,
+                          size_t ws_bytes, void* stream) {
+  const Gather gx{row_src, row_div, a_rows};
+  return gmm_checked(a, a_dt, a_q, a_scale, w, w_dt, w_q, w_scale, offsets, e, A, Hin, N, act, out,
+                     out_dt, ws, ws_bytes, stream, &gx);
 }
 
 moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_dst,
@@ -273,10 +301,18 @@ moe_status moe_layer(const void* x, const void* w_router, const float* bias, con
   void* hm = base + L.hm;
   const int A = T * K;
   MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s));
-  MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
   void* gws = base + L.gmm_ws;  // sized for whichever GEMM needs more (possibly none)
-  MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt,
-                     gmm_ws_bytes(dt, E, A, H, F) ? gws : nullptr, s));
+  void* gws1 = gmm_ws_bytes(dt, E, A, H, F) ? gws : nullptr;
+  if ((int64_t)T * H * dtype_size(dt) < (1ll << 31)) {
+    // dispatch inside GEMM 1: its row r is token perm_src[r] / K
+    MOE_TRY(launch_permute(idx, nullptr, dt, T, H, E, K, counts, offsets, psrc, pdst, nullptr,
+                           base + L.perm_ws, s));
+    MOE_TRY(launch_gmm(x, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s,
+                       Gather{psrc, K, T}));
+  } else {
+    MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
+    MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s));
+  }
   MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt,
                      gmm_ws_bytes(dt, E, A, F, H) ? gws : nullptr, s));
   MOE_TRY(launch_combine(xp, dt, pdst, gate, T, K, H, y, s));

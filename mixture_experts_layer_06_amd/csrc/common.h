@@ -91,10 +91,18 @@ size_t permute_ws_bytes(int T, int E, int K);
 moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T, int H, int E, int K,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
                           void* x_perm, void* ws, hipStream_t s);
+// Row gather of a grouped GEMM's input: grouped row r reads row src[r] / div
+// of an input with `rows` rows; src == nullptr: row r itself.
+struct Gather {
+  const int32_t* src;
+  int div;
+  int rows;
+};
 size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N);
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
-                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s);
+                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s,
+                      Gather gx = Gather{nullptr, 1, 0});
 moe_status launch_combine(const void* y_perm, moe_dtype dt, const int32_t* perm_dst,
                           const float* gate, int T, int K, int N, void* out, hipStream_t s);
 

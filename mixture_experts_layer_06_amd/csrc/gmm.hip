@@ -133,6 +133,14 @@ struct Tile {
   int ex, row0, rows, n0;
 };
 
+// Source row of grouped row r under a gather (gx.src != nullptr), or -1 when
+// the entry's quotient falls outside [0, gx.rows).
+__device__ __forceinline__ int gather_src(const Gather& gx, int r) {
+  const int v = gx.src[r];
+  const int q = v >= 0 ? v / gx.div : -1;
+  return q < gx.rows ? q : -1;
+}
+
 // Logical tile for this block, or false if the block has no work.
 // XCD-aware: block p runs on XCD p % 8; XCD x takes logical tiles
 // [x*per, (x+1)*per). Inside an expert, tiles go in groups of GM row tiles:
@@ -352,7 +360,7 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
-    unsigned char* __restrict__ out) {
+    unsigned char* __restrict__ out, Gather gx) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_off[257];
   __shared__ int s_pre[257];
@@ -368,7 +376,9 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
   const int hin_b = Hin * E_;
   const int n_b = N * E_;
   const int n0b = tile.n0 * E_;
-  const unsigned char* abase = a + (int64_t)tile.row0 * hin_b;
+  // activation rows: relative to the tile's first row, or (gather) absolute rows of a
+  const bool gat = gx.src != nullptr;
+  const unsigned char* abase = gat ? a : a + (int64_t)tile.row0 * hin_b;
   const unsigned char* wbase = w + (int64_t)tile.ex * Hin * n_b;
   const int nsteps = (hin_b + kKB - 1) / kKB;
 
@@ -379,16 +389,18 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
   // ---- per-thread load descriptors, fixed for the tile
   __amdgpu_buffer_rsrc_t arsrc, wrsrc;
   if (C::kAligned) {
-    arsrc = make_rsrc(abase, (uint32_t)tile.rows * (uint32_t)hin_b);
+    arsrc = make_rsrc(abase, (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)hin_b);
     wrsrc = make_rsrc(wbase, (uint32_t)Hin * (uint32_t)n_b);
   }
   uint32_t aoff[C::kAPT];
-  int alds[C::kAPT], akc[C::kAPT];
+  int alds[C::kAPT], akc[C::kAPT], asrc[C::kAPT];
 #pragma unroll
   for (int i = 0; i < C::kAPT; ++i) {
     const int c = tid + i * C::kNT;
     const int row = c >> 3, kc = c & 7;
-    aoff[i] = (uint32_t)row * (uint32_t)hin_b + kc * 16;  // beyond tile.rows -> out of range
+    // source row, -1 when there is none (past tile.rows or an out-of-range gather entry)
+    asrc[i] = row >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + row) : row;
+    aoff[i] = (asrc[i] >= 0 ? (uint32_t)asrc[i] * (uint32_t)hin_b : kOOB) + kc * 16;
     akc[i] = kc * 16;
     alds[i] = lds_off(row, kc);
   }
@@ -414,7 +426,7 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     if (C::kAligned) {
 #pragma unroll
       for (int i = 0; i < C::kAPT; ++i) {
-        const uint32_t o = aoff[i] + kb0 + (kb0 + akc[i] < hin_b ? 0u : kOOB);
+        const uint32_t o = (aoff[i] + kb0) | (kb0 + akc[i] < hin_b ? 0u : kOOB);
         ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, o, 0, 0));
       }
       const uint32_t kstep = (uint32_t)k0 * (uint32_t)n_b;
@@ -427,11 +439,9 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     } else {
 #pragma unroll
       for (int i = 0; i < C::kAPT; ++i) {
-        const int c = tid + i * C::kNT;
-        const int row = c >> 3;
         const int rem = hin_b - (kb0 + akc[i]);
-        const int avail = row < tile.rows ? (rem < 16 ? rem : 16) : 0;
-        ra[i] = ld16<false, E_>(abase + (int64_t)row * hin_b + kb0 + akc[i], avail);
+        const int avail = asrc[i] >= 0 ? (rem < 16 ? rem : 16) : 0;
+        ra[i] = ld16<false, E_>(abase + (int64_t)(asrc[i] >= 0 ? asrc[i] : 0) * hin_b + kb0 + akc[i], avail);
       }
 #pragma unroll
       for (int u = 0; u < C::kUPT; ++u) {
@@ -696,7 +706,8 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
-    bf16_t* __restrict__ out, float* __restrict__ split_ws, int* __restrict__ split_cnt, int ncu) {
+    bf16_t* __restrict__ out, float* __restrict__ split_ws, int* __restrict__ split_cnt, int ncu,
+    Gather gx) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int s_last;
   // The ring takes all of LDS; the tile prefix borrows its first bytes
@@ -732,8 +743,11 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int nsteps = ks1 - ks0;
   // descriptors start at the range's first K slice (rows past tile.rows and
   // K rows past Hin stay out of range)
-  const u32x4_t asrd = make_srd(a + (int64_t)tile.row0 * hin_b + ks0 * kDmaKB,
-                                (uint32_t)tile.rows * (uint32_t)hin_b - (uint32_t)(ks0 * kDmaKB));
+  // activation rows: relative to the tile's first row, or (gather) absolute rows of a
+  const bool gat = gx.src != nullptr;
+  const u32x4_t asrd = make_srd(a + (gat ? 0 : (int64_t)tile.row0 * hin_b) + ks0 * kDmaKB,
+                                (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)hin_b -
+                                    (uint32_t)(ks0 * kDmaKB));
   const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * n_b + (int64_t)ks0 * 32 * n_b,
                                 (uint32_t)(Hin - ks0 * 32) * (uint32_t)n_b);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -742,7 +756,8 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
   auto x_src = [&](int kb, uint32_t& voff, uint32_t& kc) {  // kb: byte within the slot's activations
     const int row = kb >> 6, pc = (kb >> 4) & 3;
     const int lc = pc ^ ((row >> 1) & 3);
-    voff = (uint32_t)row * (uint32_t)hin_b + lc * 16;
+    const int src = row >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + row) : row;
+    voff = (src >= 0 ? (uint32_t)src * (uint32_t)hin_b : kOOB) + lc * 16;
     kc = lc * 16;
   };
   uint32_t a_voff[C::kADma + 1];
@@ -771,10 +786,10 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int kb0 = step * kDmaKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
-      dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < kext_b ? 0u : kOOB),
+      dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < kext_b ? 0u : kOOB),
             base + (wave * C::kADma + q) * 1024);
     if (decltype(ex)::value)
-      dma16(asrd, a_voff[C::kADma] + kb0 + (kb0 + (int)a_kc[C::kADma] < kext_b ? 0u : kOOB),
+      dma16(asrd, (a_voff[C::kADma] + kb0) | (kb0 + (int)a_kc[C::kADma] < kext_b ? 0u : kOOB),
             tail_dma ? base + C::kLdsA + wave * 1024 : lds0 + C::kDummy);
     const uint32_t kstep = step < nsteps ? (uint32_t)(step * 32) * (uint32_t)n_b : kOOB;
 #pragma unroll
@@ -1062,7 +1077,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
-    bf16_t* __restrict__ out) {
+    bf16_t* __restrict__ out, Gather gx) {
   typedef Pp8Cfg C;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   {
@@ -1080,7 +1095,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = wave >> 2, wm2 = (wave >> 1) & 1, wn = wave & 1;
   const int nsteps = (Hin + C::kKB - 1) / C::kKB;
-  const u32x4_t asrd = make_srd(a + (int64_t)tile.row0 * Hin, (uint32_t)tile.rows * (uint32_t)Hin);
+  // activation rows: relative to the tile's first row, or (gather) absolute rows of a
+  const bool gat = gx.src != nullptr;
+  const u32x4_t asrd = make_srd(a + (gat ? 0 : (int64_t)tile.row0 * Hin),
+                                (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)Hin);
   const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * N, (uint32_t)Hin * (uint32_t)N);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
@@ -1091,7 +1109,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int kb = (wave * C::kADma + q) * 1024 + lane * 16;
     const int prow = kb >> 7, pc = (kb >> 4) & 7;
     const int lc = pc ^ pp8_xswz(prow);
-    a_voff[q] = (uint32_t)prow * (uint32_t)Hin + lc * 16;
+    const int src = prow >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + prow) : prow;
+    a_voff[q] = (src >= 0 ? (uint32_t)src * (uint32_t)Hin : kOOB) + lc * 16;
     a_kc[q] = lc * 16;
   }
   uint32_t w_voff[C::kWDma];
@@ -1108,7 +1127,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int kb0 = step * C::kKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
-      dma16(asrd, a_voff[q] + kb0 + (kb0 + (int)a_kc[q] < Hin ? 0u : kOOB),
+      dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < Hin ? 0u : kOOB),
             base + (wave * C::kADma + q) * 1024);
     const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : kOOB;
 #pragma unroll
@@ -1260,7 +1279,7 @@ template <int MB, bool AL>
 __global__ __launch_bounds__(256) void gmm_stream_kernel(
     const bf16_t* __restrict__ a, const bf16_t* __restrict__ w, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int e, int A, int Hin,
-    int N, int relu, bf16_t* __restrict__ out) {
+    int N, int relu, bf16_t* __restrict__ out, Gather gx) {
   // Tasks are (non-empty expert, 64 columns), numbered densely so that the
   // waves with work are spread evenly over the CUs: s_pre[q] counts the
   // non-empty experts before q (a "row tile" of 2^30 rows).
@@ -1293,7 +1312,12 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
   // current set is multiplied.
   constexpr int U = MB == 1 ? 1 : 2;  // measured: deeper sets only pay with 32+ rows per wave
   const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(wex, (uint32_t)Hin * (uint32_t)N * 2u);
-  const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a + (int64_t)r0 * Hin, (uint32_t)cnt * (uint32_t)Hin * 2u);
+  // activation rows: relative to the expert's first row, or (gather) absolute rows of a
+  const bool gat = gx.src != nullptr;
+  const __amdgpu_buffer_rsrc_t xsrc =
+      make_rsrc(a + (gat ? 0 : (int64_t)r0 * Hin), (uint32_t)(gat ? gx.rows : cnt) * (uint32_t)Hin * 2u);
+  // source row of the expert's row ml, -1 when there is none
+  auto xrow = [&](int ml) { return ml >= cnt ? -1 : gat ? gather_src(gx, r0 + ml) : ml; };
   const uint32_t woff = (uint32_t)(kq * 8) * (uint32_t)N * 2u + (uint32_t)ncol * 2u + (ncol < N ? 0u : kOOB);
   struct Set {
     uint2 w[U][8];
@@ -1309,7 +1333,10 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
     if (AL) {
       uint32_t xoff[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) xoff[mb] = (uint32_t)(mc + mb * 16 + ci) * (uint32_t)Hin * 2u + kq * 16;
+      for (int mb = 0; mb < MB; ++mb) {
+        const int src = xrow(mc + mb * 16 + ci);
+        xoff[mb] = (src >= 0 ? (uint32_t)src * (uint32_t)Hin * 2u : kOOB) + kq * 16;
+      }
       auto load_set = [&](int k0, Set& st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1318,10 +1345,11 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
           for (int r = 0; r < 8; ++r)
             st.w[u][r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
                              wsrc, woff + (uint32_t)(k + r) * (uint32_t)N * 2u, 0, 0));
-          const uint32_t kx = (uint32_t)k * 2u + (k + kq * 8 < Hin ? 0u : kOOB);
+          const uint32_t kx = k + kq * 8 < Hin ? 0u : kOOB;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            st.x[u][mb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[mb] + kx, 0, 0));
+            st.x[u][mb] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, (xoff[mb] + (uint32_t)k * 2u) | kx, 0, 0));
         }
       };
       auto mul_set = [&](const Set& st) {
@@ -1352,33 +1380,37 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
         mul_set(sb);
         k0 += 32 * U;
       }
-    } else
-    for (int k0 = 0; k0 < Hin; k0 += 32) {
-      uint2 rows[8];
+    } else {
+      int xsr[MB];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int k = k0 + kq * 8 + r;
-        rows[r] = ld8<AL, 2>(reinterpret_cast<const unsigned char*>(wex + (int64_t)k * N + ncol),
-                             k < Hin ? avail_n : 0);
-      }
-      bf16x8_t xa[MB];
+      for (int mb = 0; mb < MB; ++mb) xsr[mb] = xrow(mc + mb * 16 + ci);
+      for (int k0 = 0; k0 < Hin; k0 += 32) {
+        uint2 rows[8];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int ml = mc + mb * 16 + ci;
-        const int kk = k0 + kq * 8;
-        const int avail = (ml < cnt) ? min(Hin - kk, 8) * 2 : 0;
-        uint4 v = ld16<AL, 2>(reinterpret_cast<const unsigned char*>(a + (int64_t)(r0 + ml) * Hin + kk),
-                              ml < cnt ? avail : 0);
-        xa[mb] = *reinterpret_cast<bf16x8_t*>(&v);
-      }
-      uint4 cols[4];
-      transpose_8x4_bf16(rows, cols);
+        for (int r = 0; r < 8; ++r) {
+          const int k = k0 + kq * 8 + r;
+          rows[r] = ld8<AL, 2>(reinterpret_cast<const unsigned char*>(wex + (int64_t)k * N + ncol),
+                               k < Hin ? avail_n : 0);
+        }
+        bf16x8_t xa[MB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t wb = *reinterpret_cast<bf16x8_t*>(&cols[j]);
+        for (int mb = 0; mb < MB; ++mb) {
+          const int kk = k0 + kq * 8;
+          const int src = xsr[mb];
+          const int avail = src >= 0 ? min(Hin - kk, 8) * 2 : 0;
+          const int64_t arow = src < 0 ? 0 : gat ? src : (int64_t)r0 + src;
+          uint4 v = ld16<AL, 2>(reinterpret_cast<const unsigned char*>(a + arow * Hin + kk), avail);
+          xa[mb] = *reinterpret_cast<bf16x8_t*>(&v);
+        }
+        uint4 cols[4];
+        transpose_8x4_bf16(rows, cols);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xa[mb], acc[mb][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t wb = *reinterpret_cast<bf16x8_t*>(&cols[j]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xa[mb], acc[mb][j], 0, 0, 0);
+        }
       }
     }
     // MFMA j, output row i = 4*kq + r  ->  column n0 + 4*i + j = n0 + 16*kq + 4r + j
@@ -1422,7 +1454,7 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ w_scale,
                                                       const int32_t* __restrict__ offsets, int e,
                                                       int A, int Hin, int N, int relu,
-                                                      float* __restrict__ out) {
+                                                      float* __restrict__ out, Gather gx) {
   __shared__ int s_off[257];
   __shared__ int s_pre[257];
   __shared__ float As[kF32BK][kF32BM + 1];
@@ -1434,10 +1466,20 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ 
   const int tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
   const float* wex = w + (int64_t)tile.ex * Hin * N;
+  // rows this thread loads (p = tid + 256 q: row p / kF32BK), as rows of a; -1: none
+  static_assert(kF32BM * kF32BK % 256 == 0, "load split");
+  int arow[kF32BM * kF32BK / 256];
+#pragma unroll
+  for (int q = 0; q < kF32BM * kF32BK / 256; ++q) {
+    const int r = (tid + 256 * q) / kF32BK;
+    arow[q] = r >= tile.rows ? -1 : gx.src ? gather_src(gx, tile.row0 + r) : tile.row0 + r;
+  }
   for (int k0 = 0; k0 < Hin; k0 += kF32BK) {
-    for (int p = tid; p < kF32BM * kF32BK; p += 256) {
+#pragma unroll
+    for (int q = 0; q < kF32BM * kF32BK / 256; ++q) {
+      const int p = tid + 256 * q;
       const int r = p / kF32BK, k = p % kF32BK;
-      As[k][r] = (r < tile.rows && k0 + k < Hin) ? a[(int64_t)(tile.row0 + r) * Hin + k0 + k] : 0.f;
+      As[k][r] = (arow[q] >= 0 && k0 + k < Hin) ? a[(int64_t)arow[q] * Hin + k0 + k] : 0.f;
     }
     for (int p = tid; p < kF32BK * kF32BN; p += 256) {
       const int k = p / kF32BN, c = p % kF32BN;
@@ -1474,7 +1516,7 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ 
 template <class C>
 moe_status launch_tiled(const void* a, const float* as, const void* w, const float* ws,
                         const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                        hipStream_t s) {
+                        hipStream_t s, Gather gx) {
   static bool attr_done = false;
   if (!attr_done) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_tiled_kernel<C>),
@@ -1487,7 +1529,7 @@ moe_status launch_tiled(const void* a, const float* as, const void* w, const flo
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(gmm_tiled_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
                      (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
-                     relu, (unsigned char*)out);
+                     relu, (unsigned char*)out, gx);
   return launch_status();
 }
 
@@ -1514,7 +1556,7 @@ int device_cus() {
 template <class C>
 moe_status launch_pp(const void* a, const float* as, const void* w, const float* ws,
                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                     void* split, hipStream_t s) {
+                     void* split, hipStream_t s, Gather gx) {
   static_assert(C::kBM == 256 && C::kBN == 256, "split scratch is sized for 256 x 256 tiles");
   static bool attr_done = false;
   if (!attr_done) {
@@ -1532,13 +1574,13 @@ moe_status launch_pp(const void* a, const float* as, const void* w, const float*
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(gmm_pp_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
                      (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
-                     relu, (bf16_t*)out, sws, cnt, ncu);
+                     relu, (bf16_t*)out, sws, cnt, ncu, gx);
   return launch_status();
 }
 
 moe_status launch_pp8(const void* a, const float* as, const void* w, const float* ws,
                       const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                      hipStream_t s) {
+                      hipStream_t s, Gather gx) {
   typedef Pp8Cfg C;
   static bool attr_done = false;
   if (!attr_done) {
@@ -1552,27 +1594,27 @@ moe_status launch_pp8(const void* a, const float* as, const void* w, const float
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(gmm_pp8_kernel, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
                      (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
-                     relu, (bf16_t*)out);
+                     relu, (bf16_t*)out, gx);
   return launch_status();
 }
 
 template <int MB, bool AL>
 moe_status launch_stream(const void* a, const float* as, const void* w, const float* ws,
                          const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                         hipStream_t s) {
+                         hipStream_t s, Gather gx) {
   const int64_t tasks = (int64_t)e * cdiv(N, 64);
   hipLaunchKernelGGL((gmm_stream_kernel<MB, AL>), dim3((unsigned)cdiv64(tasks, 4)), dim3(256), 0, s,
                      (const bf16_t*)a, (const bf16_t*)w, as, ws, offsets, e, A, Hin, N, relu,
-                     (bf16_t*)out);
+                     (bf16_t*)out, gx);
   return launch_status();
 }
 
 template <int MB>
 moe_status launch_stream_al(bool al, const void* a, const float* as, const void* w, const float* ws,
                             const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                            hipStream_t s) {
-  return al ? launch_stream<MB, true>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s)
-            : launch_stream<MB, false>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s);
+                            hipStream_t s, Gather gx) {
+  return al ? launch_stream<MB, true>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s, gx)
+            : launch_stream<MB, false>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s, gx);
 }
 
 }  // namespace
@@ -1606,25 +1648,26 @@ size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N) {
 
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
-                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s) {
+                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s, Gather gx) {
   if (A == 0) return MOE_OK;
   const int relu = act == MOE_ACT_RELU;
   if (in_dt == MOE_F32) {
     const int64_t blocks = (cdiv64(A, kF32BM) + (e < A ? e : A)) * cdiv64(N, kF32BN);
     const int64_t grid = cdiv64(blocks, 8) * 8;
     hipLaunchKernelGGL(gmm_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const float*)a,
-                       (const float*)w, a_scale, w_scale, offsets, e, A, Hin, N, relu, (float*)out);
+                       (const float*)w, a_scale, w_scale, offsets, e, A, Hin, N, relu, (float*)out, gx);
     return launch_status();
   }
   const int elem = in_dt == MOE_BF16 ? 2 : 1;
   if (in_dt == MOE_BF16 && (int64_t)A <= (int64_t)kStreamMaxAvgRows * e) {
     // aligned: buffer loads over each expert's weights and over the rows (both under 2 GiB)
+    const int64_t a_rows = gx.src ? gx.rows : A;  // rows the activation loads address
     const bool al = (Hin % 8 == 0) && (N % 8 == 0) && ((int64_t)Hin * N * 2 < (1ll << 31)) &&
-                    ((int64_t)A * Hin * 2 < (1ll << 31));
+                    (a_rows * Hin * 2 < (1ll << 31));
     const int avg = cdiv(A, e);
-    if (avg <= 8) return launch_stream_al<1>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
-    if (avg <= 16) return launch_stream_al<2>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
-    return launch_stream_al<4>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+    if (avg <= 8) return launch_stream_al<1>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
+    if (avg <= 16) return launch_stream_al<2>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
+    return launch_stream_al<4>(al, a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
   }
   // buffer-load path: 16-byte aligned rows and each expert's weight matrix under 2 GiB
   const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0) &&
@@ -1633,23 +1676,23 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
 #if MOE_GMM_BF16 == 1
   if (elem == 2 && al && N % 16 == 0) {
     typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
-    return launch_pp<CP>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s);
+    return launch_pp<CP>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s, gx);
   }
 #endif
 #if MOE_GMM_FP8 == 1
   if (elem == 1 && al && N % 16 == 0)
-    return launch_pp8(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+    return launch_pp8(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
 #endif
   if (elem == 2) {
     typedef TiledCfg<2, 256, 256, WM, WN, true, false> CA;
     typedef TiledCfg<2, 256, 256, WM, WN, false, false> CU;
-    return al ? launch_tiled<CA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s)
-              : launch_tiled<CU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+    return al ? launch_tiled<CA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx)
+              : launch_tiled<CU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
   }
   typedef TiledCfg<1, 256, 256, WM, WN, true, false> FA;
   typedef TiledCfg<1, 256, 256, WM, WN, false, false> FU;
-  return al ? launch_tiled<FA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s)
-            : launch_tiled<FU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s);
+  return al ? launch_tiled<FA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx)
+            : launch_tiled<FU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
 }
 
 }  // namespace moe

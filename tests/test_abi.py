@@ -22,7 +22,7 @@ def declared_entry_points():
 
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
-    for n in ("moe_route", "moe_permute", "moe_gmm", "moe_combine", "moe_layer",
+    for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_combine", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size",
               "moe_status_string", "moe_version"):
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10200
+    assert moe.lib().moe_version() == 10300
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -206,6 +206,44 @@ def test_gmm_validation(kw, status):
 
 def test_gmm_zero_rows_is_noop():
     assert gmm(a=None, w=None, off=None, out=None, A=0) == moe.OK
+
+
+def gmm_gather(a=P, a_rows=50, rows=P, div=2, adt=moe.BF16, aq=0, asc=None, w=P, wdt=moe.BF16, wq=0,
+               wsc=None, off=P, e=8, A=100, Hin=64, N=64, act=moe.ACT_RELU, out=P, odt=moe.BF16, ws=P,
+               ws_bytes=None):
+    if ws_bytes is None:
+        try:
+            ws_bytes = moe.gmm_workspace_size(adt, e, A, Hin, N)
+        except moe.MoeError:
+            ws_bytes = 0
+    return L.moe_gmm_gather(a, a_rows, rows, div, adt, aq, asc, w, wdt, wq, wsc, off, e, A, Hin, N, act,
+                            out, odt, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=None), moe.ERR_NULL_POINTER),
+    (dict(rows=MIS), moe.ERR_MISALIGNED),
+    (dict(div=0), moe.ERR_BAD_SHAPE),
+    (dict(div=-2), moe.ERR_BAD_SHAPE),
+    (dict(a_rows=0), moe.ERR_BAD_SHAPE),
+    (dict(a_rows=-1), moe.ERR_BAD_SHAPE),
+    (dict(a_rows=1 << 24, Hin=64), moe.ERR_UNSUPPORTED),         # 2 GiB of gathered bf16 rows
+    (dict(a_rows=1 << 24, Hin=128, adt=moe.FP8_E4M3, wdt=moe.FP8_E4M3, aq=1, wq=1, asc=P, wsc=P),
+     moe.ERR_UNSUPPORTED),
+    (dict(adt=moe.F32), moe.ERR_BAD_DTYPE),                          # same rules as moe_gmm
+    (dict(aq=2), moe.ERR_UNSUPPORTED),
+    (dict(e=0), moe.ERR_BAD_SHAPE),
+    (dict(a=None), moe.ERR_NULL_POINTER),
+    (dict(a=MIS), moe.ERR_MISALIGNED),
+    (dict(out=None), moe.ERR_NULL_POINTER),
+    (dict(A=5000, ws=None), moe.ERR_NULL_POINTER),
+])
+def test_gmm_gather_validation(kw, status):
+    assert gmm_gather(**kw) == status
+
+
+def test_gmm_gather_zero_rows_is_noop():
+    assert gmm_gather(a=None, rows=None, w=None, off=None, out=None, A=0, a_rows=0) == moe.OK
 
 
 def combine(y=P, dt=moe.BF16, pdst=P, gate=P, T=10, K=2, N=64, out=P, odt=moe.BF16):

@@ -307,6 +307,63 @@ def test_gmm_fold_and_split():
     assert normwise_err(o1[rows], ref) <= 8e-3
 
 
+GATHER_CASES = [
+    # (name, counts, Hin, N, dtype, K): one per kernel family, plus fold and split
+    ("bf16_pp_fold", [257, 513, 800, 1055, 0, 289], 256, 320, "bf16", 2),
+    ("bf16_pp_split", [1812, 1812], 544, 5120, "bf16", 4),
+    ("bf16_tiled_unaligned", [270, 3, 0, 400], 300, 130, "bf16", 2),
+    ("bf16_stream", [5, 0, 17, 30, 1, 0, 9, 12, 3, 31, 0, 2, 8, 16, 4, 7], 512, 320, "bf16", 8),
+    ("bf16_stream_unaligned", [3, 0, 14, 6, 1, 9], 90, 100, "bf16", 3),
+    ("bf16_stream_mb4", [40, 44, 0, 47, 33, 1], 256, 192, "bf16", 2),
+    ("fp8_pp8", [200, 0, 333, 129], 256, 384, "fp8", 8),
+    ("fp8_tiled_unaligned", [100, 77], 200, 100, "fp8", 2),
+    ("f32", [20, 0, 17, 40, 1, 30, 12, 8], 128, 256, "f32", 2),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_gmm_gather_equals_gmm_on_permuted_rows(case):
+    """moe_gmm_gather reading token rows through perm_src / K gives moe_gmm on
+    the permuted copy bit for bit (same tiles, same sums); both match the
+    oracle; index entries outside [0, T) read as zero rows."""
+    name, counts, Hin, N, dt, K = case
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    T = A // K + 7
+    rng = np.random.default_rng(len(name) * 31 + A)
+    psrc = rng.permutation(T * K)[:A].astype(np.int32)
+    bad = rng.choice(A, size=min(3, A), replace=False)
+    psrc[bad[0]] = -5
+    if len(bad) > 1:
+        psrc[bad[1]] = T * K + 3
+    if len(bad) > 2:
+        psrc[bad[2]] = T * K  # quotient T: one past the last row
+    seed = 700 + len(name)
+    kw = {}
+    if dt == "fp8":
+        x, sa = synth.quantize_e4m3(synth.normal(seed, (T, Hin)))
+        w, sw = synth.quantize_e4m3(synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin)))
+        kw = dict(a_scale=torch.tensor([sa], dtype=torch.float32, device="cuda"),
+                  w_scale=torch.tensor([sw], dtype=torch.float32, device="cuda"))
+        okw = dict(a_scale=float(sa), w_scale=float(sw))
+    else:
+        x = synth.normal(seed, (T, Hin), dtype=dt)
+        w = synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin), dtype=dt)
+        okw = {}
+    valid = (psrc >= 0) & (psrc < T * K)
+    xp = np.zeros((A, Hin), dtype=x.dtype)
+    xp[valid] = x[psrc[valid] // K]
+    wd, od = to_dev(w), to_dev(off)
+    for act in (moe.ACT_NONE, moe.ACT_RELU):
+        g = to_host(moe.gmm(to_dev(x), wd, od, act=act, rows=to_dev(psrc), row_div=K, **kw))
+        c = to_host(moe.gmm(to_dev(xp), wd, od, act=act, **kw))
+        assert np.array_equal(g, c), name
+        assert not g[~valid].any()
+    ref = oracle.gmm(xp, w, off, act=moe.ACT_RELU, nthreads=8, **okw)
+    assert normwise_err(g, ref) <= {"f32": 2e-6, "bf16": 8e-3, "fp8": 8e-3}[dt]
+
+
 # ---------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("dt,N", [("bf16", 264), ("bf16", 30), ("f32", 30), ("f32", 128)])
