@@ -43,8 +43,10 @@ LAYER_WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as fill 0.4 s, so the GPU's "
+                         "clocks have left their idle state; the count is reported)")
     ap.add_argument("--workload", default="prefill",
                     choices=sorted(LAYER_WORKLOADS) + ["fp8gmm"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -89,6 +91,24 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def warm_up(fn, count):
+    """Run fn `count` times, or (count None) until 0.4 s have passed; return the count."""
+    import torch
+    if count is not None:
+        for _ in range(count):
+            fn()
+        torch.cuda.synchronize()
+        return count
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= 0.4:
+                return n
 
 
 def cpu_threads() -> int:
@@ -173,35 +193,41 @@ def bench_layer(args, dev):
         if ev is not None:
             ev[5].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["route", "permute", "gmm1", "gmm2", "combine"]
-    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-           for i, n in enumerate(names)}
-
-    # the same step through the single moe_layer entry point (outside the timed region)
+    # The timed step is one moe_layer call (route, index permute, GEMM 1 gathering
+    # the token rows, GEMM 2, weighted combine: the whole path on one stream).
     ws_layer = torch.empty((moe.layer_workspace_size(T, H, E, K, F, moe.dtype_code(x)),),
                            dtype=torch.uint8, device=dev)
     y2 = torch.empty_like(y)
-    for _ in range(2):
+
+    def layer_step():
         moe.layer(x, wr, w1, w2, K, bias=bias, y=y2, ws=ws_layer)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+
+    def warm_step():
+        layer_step()
+        step()
+
+    warmup = warm_up(warm_step, args.warmup)
+    t0 = time.perf_counter()
     for _ in range(args.steps):
-        moe.layer(x, wr, w1, w2, K, bias=bias, y=y2, ws=ws_layer)
-    e1.record()
+        layer_step()
     torch.cuda.synchronize()
-    layer_ms = e0.elapsed_time(e1) / args.steps
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # The same path stage by stage through the separate entry points, with HIP
+    # events on the stream between them: per-kernel times (the grouped GEMM's
+    # launch time feeds the roofline).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    ts0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    ts1 = time.perf_counter()
+    ms_stages = (ts1 - ts0) * 1e3 / args.steps
+    names = ["route", "permute", "gmm1", "gmm2", "combine"]
+    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
 
     counts = bufs["counts"].cpu().numpy().tolist()
     fl1, by1 = flops_bytes_gmm(counts, H, F, es)
@@ -233,7 +259,7 @@ def bench_layer(args, dev):
                 + (" router bias -1.2ln(e+1)" if bias is not None else ""))
     res = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens)",
         "config": {"workload": workload, "T": T, "H": H, "E": E, "K": K, "F": F,
@@ -245,7 +271,7 @@ def bench_layer(args, dev):
         "moe_gmm_tflops": gmm_tflops,
         "moe_gmm_frac_bf16_peak": gmm_tflops / PEAK_BF16_TFLOPS if dt != "f32" else None,
         "kernels": kernels,
-        "moe_layer_call_ms": layer_ms,
+        "ms_per_step_stage_by_stage": ms_stages,
         "expert_counts": {"min": min(counts), "max": max(counts), "empty": counts.count(0)},
     }
     host = {"x": d["x"], "wr": d["wr"], "w1": d["w1"], "w2": d["w2"], "bias": d["bias"], "K": K}
@@ -306,9 +332,7 @@ def bench_fp8(args, dev):
         join.record(side)
         main.wait_event(join)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup = warm_up(step, args.warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -324,7 +348,7 @@ def bench_fp8(args, dev):
     achieved = fl / (gmm_ms * 1e-3) / 1e12
     res = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
         "data": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
         "config": {"workload": f"fp8gmm: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
