@@ -73,6 +73,11 @@
 #define MOE_PP_WN 4
 #define MOE_PP_STAGES 4
 #endif
+// 1: the streaming kernel's blocks share their activation rows through LDS
+// (32 or more rows per block, N a multiple of 256).
+#ifndef MOE_STREAM_XS
+#define MOE_STREAM_XS 1
+#endif
 // Wave layout of the 256 x 256 tiled kernel (waves along rows x columns).
 #ifndef MOE_TILED_WAVES_M
 #define MOE_TILED_WAVES_M 2
@@ -1275,7 +1280,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 
 // ------------------------------------------------------------------ streaming kernel (decode)
 
-template <int MB, bool AL>
+// XS: the block's 4 waves (one expert, 4 consecutive 64-column groups) share
+// their activation rows through LDS, 32 KB chunks of 32/MB k-steps filled by
+// LDS DMA and double-buffered, instead of each wave loading them itself.
+template <int MB, bool AL, bool XS>
 __global__ __launch_bounds__(256) void gmm_stream_kernel(
     const bf16_t* __restrict__ a, const bf16_t* __restrict__ w, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int e, int A, int Hin,
@@ -1324,13 +1332,112 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
     uint4 x[U][MB];
   };
 
+  static_assert(!XS || (AL && MB >= 2), "shared activation chunks: aligned, 32+ rows per block");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char xs_lds[];
+  const int wave = threadIdx.x >> 6;
+
   for (int mc = 0; mc < cnt; mc += 16 * MB) {
     f32x4_t acc[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[mb][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    if (AL) {
+    if constexpr (XS) {
+      // chunk ch holds k-steps ch*KC .. ch*KC+KC-1 of the block's 16*MB rows:
+      // row r at r*RB, its 16-byte piece c at position c ^ ((2r) % 16), so
+      // the 16 rows x 2 pieces one pass of a fragment read touches fall in
+      // distinct banks
+      constexpr int KC = 32 / MB;             // k-steps per chunk
+      constexpr int RB = KC * 64;             // bytes of one row in a chunk
+      constexpr int XB = 16 * MB * RB;        // 32 KB per buffer
+      constexpr int OPS = XB / 1024 / 4;      // 1 KB pieces (16 bytes per lane) per wave per chunk
+      constexpr int PPR = RB / 16;            // 16-byte pieces per row
+      static_assert(XB == 32768 && 1024 % RB == 0, "chunk shape");
+      // this lane's share of a chunk: piece `lane` of block rows wave*OPS + o
+      uint32_t dsrc[OPS], dpc[OPS];
+#pragma unroll
+      for (int o = 0; o < OPS; ++o) {
+        const int r = (wave * OPS + o) * (1024 / RB) + lane / PPR;  // block row
+        const int c = (lane % PPR) ^ ((2 * r) & 15);                  // piece stored at position lane % PPR
+        const int src = xrow(mc + r);
+        dsrc[o] = (src >= 0 ? (uint32_t)src * (uint32_t)Hin * 2u : kOOB) + (uint32_t)c * 16u;
+        dpc[o] = (uint32_t)c * 16u;
+      }
+      uint4 xst[OPS];
+      auto load_x = [&](int ch) {  // global -> registers
+        const uint32_t kb = (uint32_t)ch * RB;  // byte offset of the chunk within a row
+#pragma unroll
+        for (int o = 0; o < OPS; ++o)
+          xst[o] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       xsrc, (dsrc[o] + kb) | (kb + dpc[o] < (uint32_t)Hin * 2u ? 0u : kOOB), 0, 0));
+      };
+      auto store_x = [&](int ch) {  // registers -> LDS buffer ch % 2
+        unsigned char* xb = xs_lds + (ch & 1) * XB;
+#pragma unroll
+        for (int o = 0; o < OPS; ++o) *reinterpret_cast<uint4*>(xb + (wave * OPS + o) * 1024 + lane * 16) = xst[o];
+      };
+      int xoff[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xoff[mb] = (mb * 16 + ci) * RB;
+      const int xsw = (2 * ci) & 15;  // swizzle of rows mb*16 + ci (the same for every mb)
+      struct WSet {
+        uint2 w[U][8];
+      };
+      auto load_w = [&](int k0, WSet& st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            st.w[u][r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                             wsrc, woff + (uint32_t)(k0 + 32 * u + r) * (uint32_t)N * 2u, 0, 0));
+      };
+      auto mul_w = [&](const WSet& st, int k0) {
+        const int ch = k0 / (32 * KC);
+        const unsigned char* xb = xs_lds + (ch & 1) * XB;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int step = (k0 / 32 + u) % KC;
+          const int pos = ((4 * step + kq) ^ xsw) * 16;
+          bf16x8_t xv[MB];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) xv[mb] = *reinterpret_cast<const bf16x8_t*>(xb + xoff[mb] + pos);
+          uint4 cols[4];
+          transpose_8x4_bf16(st.w[u], cols);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cols[j]), xv[mb],
+                                                                   acc[mb][j], 0, 0, 0);
+        }
+      };
+      // Per chunk: the next chunk's activations go to registers before the
+      // chunk's last weight sets are loaded and to the other LDS buffer after
+      // its last multiply; the barrier then also tells every wave that the
+      // buffer of the chunk before is free again.
+      const int nch = (Hin + 32 * KC - 1) / (32 * KC);
+      WSet sa, sb;
+      load_x(0);
+      load_w(0, sa);
+      store_x(0);
+      __syncthreads();
+      for (int ch = 0; ch < nch; ++ch) {
+        const int kc0 = ch * 32 * KC;
+#pragma unroll 1
+        for (int t = 0; t < KC / U; t += 2) {
+          const int k0 = kc0 + t * 32 * U;
+          if (t + 2 >= KC / U && ch + 1 < nch) load_x(ch + 1);
+          load_w(k0 + 32 * U, sb);  // past Hin: zeros
+          __builtin_amdgcn_sched_barrier(0);
+          mul_w(sa, k0);
+          load_w(k0 + 64 * U, sa);
+          __builtin_amdgcn_sched_barrier(0);
+          mul_w(sb, k0 + 32 * U);
+        }
+        if (ch + 1 < nch) store_x(ch + 1);
+        __syncthreads();
+      }
+    } else if (AL) {
       uint32_t xoff[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -1603,9 +1710,25 @@ moe_status launch_stream(const void* a, const float* as, const void* w, const fl
                          const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
                          hipStream_t s, Gather gx) {
   const int64_t tasks = (int64_t)e * cdiv(N, 64);
-  hipLaunchKernelGGL((gmm_stream_kernel<MB, AL>), dim3((unsigned)cdiv64(tasks, 4)), dim3(256), 0, s,
-                     (const bf16_t*)a, (const bf16_t*)w, as, ws, offsets, e, A, Hin, N, relu,
-                     (bf16_t*)out, gx);
+  const dim3 grid((unsigned)cdiv64(tasks, 4));
+  if constexpr (AL && MB >= 2 && MOE_STREAM_XS) {
+    // a block's 4 waves share one expert's rows when the 64-column groups
+    // come in fours (N a multiple of 256)
+    if (N % 256 == 0) {
+      constexpr int kXsLds = 2 * 32768;
+      static bool attr_done = false;
+      if (!attr_done) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_stream_kernel<MB, AL, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kXsLds);
+        attr_done = true;
+      }
+      hipLaunchKernelGGL((gmm_stream_kernel<MB, AL, true>), grid, dim3(256), kXsLds, s, (const bf16_t*)a,
+                         (const bf16_t*)w, as, ws, offsets, e, A, Hin, N, relu, (bf16_t*)out, gx);
+      return launch_status();
+    }
+  }
+  hipLaunchKernelGGL((gmm_stream_kernel<MB, AL, false>), grid, dim3(256), 0, s, (const bf16_t*)a,
+                     (const bf16_t*)w, as, ws, offsets, e, A, Hin, N, relu, (bf16_t*)out, gx);
   return launch_status();
 }
 

@@ -198,6 +198,10 @@ GMM_CASES = [
     ("bf16_stream", [5, 0, 17, 30, 1, 0, 9, 12, 3, 31, 0, 2, 8, 16, 4, 7], 512, 320, "bf16"),
     ("bf16_stream_unaligned", [3, 0, 14, 6, 1, 9], 90, 100, "bf16"),
     ("bf16_stream_overflow_rows", [2, 80, 1, 0, 3, 1, 2, 3], 256, 192, "bf16"),
+    # 32 rows per block sharing activations through LDS: 40 rows = two row blocks,
+    # Hin = 1000 leaves a partial last 512-deep chunk
+    ("bf16_stream_shared_x", [12, 40, 0, 9, 16, 3, 20, 11], 1000, 512, "bf16"),
+    ("bf16_stream_shared_x_64rows", [30, 0, 45, 21, 33, 17], 264, 256, "bf16"),
     ("fp8_tiled", [200, 0, 333], 256, 384, "fp8"),
     ("fp8_tiled_unaligned", [100, 77], 200, 100, "fp8"),
     ("fp8_ragged_k_and_n", [130, 5, 0, 260], 208, 400, "fp8"),  # last K slice 80 deep, 16-column tile
@@ -315,6 +319,8 @@ GATHER_CASES = [
     ("bf16_stream", [5, 0, 17, 30, 1, 0, 9, 12, 3, 31, 0, 2, 8, 16, 4, 7], 512, 320, "bf16", 8),
     ("bf16_stream_unaligned", [3, 0, 14, 6, 1, 9], 90, 100, "bf16", 3),
     ("bf16_stream_mb4", [40, 44, 0, 47, 33, 1], 256, 192, "bf16", 2),
+    ("bf16_stream_shared_x", [12, 40, 0, 9, 16, 3, 20, 11], 1000, 512, "bf16", 4),
+    ("bf16_stream_shared_x_64rows", [30, 0, 45, 21, 33, 17], 264, 256, "bf16", 2),
     ("fp8_pp8", [200, 0, 333, 129], 256, 384, "fp8", 8),
     ("fp8_tiled_unaligned", [100, 77], 200, 100, "fp8", 2),
     ("f32", [20, 0, 17, 40, 1, 30, 12, 8], 128, 256, "f32", 2),
