@@ -236,18 +236,34 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(const float* __restr
   const int ntok = min(kTok, T - t0);
   const float* src = part_in + (int64_t)t0 * EP;
   const int64_t split = (int64_t)T * EP;
-  for (int p = threadIdx.x; p < ntok * EP; p += blockDim.x) {
-    float sc = 0.f;
-    for (int q0 = 0; q0 < S; q0 += 8) {
-      float v[8];
+  // each thread owns PPT (token, expert) columns; the loads of 16 splits of
+  // all of them are in flight before the adds, which go in split order
+  constexpr int PPT = kTok * EP / 1024;
+  static_assert(kTok * EP % 1024 == 0, "columns per thread");
+  float sc[PPT];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = q0 + u < S ? src[(q0 + u) * split + p] : 0.f;
+  for (int i = 0; i < PPT; ++i) sc[i] = 0.f;
+  for (int q0 = 0; q0 < S; q0 += 16) {
+    float v[PPT][16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sc += v[u];
+    for (int i = 0; i < PPT; ++i) {
+      const int p = threadIdx.x + 1024 * i;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[i][u] = (q0 + u < S && p < ntok * EP) ? src[(q0 + u) * split + p] : 0.f;
     }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sc[i] += v[i][u];
+  }
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = threadIdx.x + 1024 * i;
+    if (p >= ntok * EP) continue;
     const int e = p % EP;
-    if (bias && e < E) sc += bias[e];
-    lg[p] = sc;
+    float x = sc[i];
+    if (bias && e < E) x += bias[e];
+    lg[p] = x;
   }
   __syncthreads();
   const int w = threadIdx.x / kWave;
