@@ -111,6 +111,65 @@ def warm_up(fn, count):
                 return n
 
 
+def _time_ms(fn, iters):
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def reported_sclk():
+    """The shader clock rocm-smi reports right now (informational), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for line in r.stdout.splitlines():
+        if "sclk" in line.lower():
+            return line.split(":", 2)[-1].strip()
+    return None
+
+
+def achievable(dev, even_experts=None):
+    """What the GPU sustains on plain work of the same kind, outside the timed
+    region, on random data (informational, beside the published peaks): a
+    1 GiB device copy (read + write bytes), one dense bf16 GEMM of the prefill
+    GEMM 1 shape through the vendor BLAS (hipBLASLt), and optionally the
+    vendor's batched GEMM on even expert loads of the given shapes."""
+    import torch
+    res = {"sclk_reported_after_run": reported_sclk()}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = _time_ms(lambda: dst.copy_(src), 10)
+    res["hbm_copy_GBps"] = 2 * n / (ms * 1e-3) / 1e9
+    del src, dst
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    a = torch.randn(8192, 4096, device=dev, generator=g).to(torch.bfloat16)
+    b = (torch.randn(4096, 14336, device=dev, generator=g) * 4096 ** -0.5).to(torch.bfloat16)
+    ms = _time_ms(lambda: torch.matmul(a, b), 10)
+    res["vendor_dense_bf16_gemm_8192x4096x14336_TFLOPs"] = 2.0 * 8192 * 4096 * 14336 / (ms * 1e-3) / 1e12
+    del a, b
+    if even_experts is not None:
+        E, M, shapes = even_experts
+        for name, (Hin, N) in shapes.items():
+            a = torch.randn(E, M, Hin, device=dev, generator=g).to(torch.bfloat16)
+            b = (torch.randn(E, Hin, N, device=dev, generator=g) * Hin ** -0.5).to(torch.bfloat16)
+            ms = _time_ms(lambda: torch.bmm(a, b), 10)
+            res[f"vendor_bmm_bf16_{name}_{E}x{M}x{Hin}x{N}_TFLOPs"] = 2.0 * E * M * Hin * N / (ms * 1e-3) / 1e12
+            del a, b
+    return res
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -391,8 +450,8 @@ def cpu_baseline_layer(host, target_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the "
-                                   "expert-parallel all-to-all across GPUs is not built)"}))
+        print(json.dumps({"error": "the MoE layer here runs on one GPU; --gpus must be 1 (the "
+                                   "expert-parallel all-to-all across GPUs is not implemented)"}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -407,8 +466,14 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "fp8gmm":
         res, host = bench_fp8(args, dev)
+        res["achievable"] = achievable(dev)
     else:
         res, host = bench_layer(args, dev)
+        c = res["config"]
+        even = None
+        if args.workload == "prefill":  # the vendor's batched GEMM on even expert loads, for context
+            even = (c["E"], c["T"] * c["K"] // c["E"], {"gemm1": (c["H"], c["F"]), "gemm2": (c["F"], c["H"])})
+        res["achievable"] = achievable(dev, even)
     if not args.no_cpu and host is not None:
         res["cpu_baseline"] = cpu_baseline_layer(host, args.cpu_seconds)
     elif not args.no_cpu:
