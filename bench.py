@@ -2,15 +2,18 @@
 """Benchmark of the single-GPU MoE layer on MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-route -> permute -> GEMM 1 (ReLU) -> GEMM 2 -> weighted combine, each a
-C-ABI call on torch's current stream (the same launches moe_layer makes).
-Inputs are resident in HBM before the timed region. HIP events between the
-stages give per-kernel durations from the same timed steps; the dominant
-kernel (moe_gmm) is reported against its roofline.
+one moe_layer call (route -> index permute -> GEMM 1 gathering the token
+rows, ReLU -> GEMM 2 -> weighted combine) on torch's current stream. Inputs
+are resident in HBM before the timed region. The same path run stage by
+stage through the separate entry points, with HIP events between them, gives
+per-kernel durations; the dominant kernel (moe_gmm) is reported against its
+roofline. The fp8 workloads time the page-2 step instead: E4M3 grouped GEMM
+(per-tensor or MX block scales) + Unpermute, with the shared bf16 expert on
+a second stream.
 
 Prints ONE JSON line. Default workload: prefill (T=4096, H=4096, E=8, K=2,
 F=14336, bf16). Other workloads: --workload skewed|decode16|decode64|
-decode256|fp8gmm|tiny.
+decode256|fp8gmm|fp8mx|tiny.
 """
 from __future__ import annotations
 
@@ -48,7 +51,7 @@ def parse():
                     help="untimed warm-up steps (default: as many as fill 0.4 s, so the GPU's "
                          "clocks have left their idle state; the count is reported)")
     ap.add_argument("--workload", default="prefill",
-                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm"])
+                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -337,9 +340,10 @@ def bench_layer(args, dev):
     return res, host
 
 
-def bench_fp8(args, dev):
-    """Page-2 form: fp8 grouped GEMM (per-tensor scales) + Unpermute, with the
-    bf16 shared-expert GEMM on a second stream, joined by events."""
+def bench_fp8(args, dev, use_mx=False):
+    """Page-2 form: fp8 grouped GEMM (per-tensor scales, or mx: E8M0 block
+    scales) + Unpermute, with the bf16 shared-expert GEMM on a second stream,
+    joined by events."""
     import numpy as np
     import torch
 
@@ -347,15 +351,19 @@ def bench_fp8(args, dev):
     import oracle
     from synth import configs
 
-    d = configs.fp8_inputs()
+    d = configs.fp8_mx_inputs() if use_mx else configs.fp8_inputs()
     T, e, K, A, H1, N1, H2, N2 = (d[k] for k in ("T", "e", "K", "A", "H1", "N1", "H2", "N2"))
     # dispatch layout of the routed rows: computed once on the device by moe_permute
     idx = host_to_dev(d["topk_idx"], dev)
     perm = moe.permute(idx, e)
     gx = host_to_dev(d["gmm_x"], dev)
     gw = host_to_dev(d["gmm_w"], dev)
-    sx = torch.tensor([float(d["gmm_x_scale"])], dtype=torch.float32, device=dev)
-    sw = torch.tensor([float(d["gmm_w_scale"])], dtype=torch.float32, device=dev)
+    if use_mx:
+        sx = host_to_dev(d["gmm_x_scale"], dev)
+        sw = host_to_dev(d["gmm_w_scale"], dev)
+    else:
+        sx = torch.tensor([float(d["gmm_x_scale"])], dtype=torch.float32, device=dev)
+        sw = torch.tensor([float(d["gmm_w_scale"])], dtype=torch.float32, device=dev)
     mx = host_to_dev(d["mm_x"], dev)
     mw = host_to_dev(d["mm_w"], dev).view(1, H2, N2)
     moff = torch.tensor([0, T], dtype=torch.int32, device=dev)
@@ -381,7 +389,10 @@ def bench_fp8(args, dev):
             moe.gmm(mx, mw, moff, out=my, ws=sws, stream=side)
             if ev is not None:
                 ev[4].record(side)
-        moe.gmm(gx, gw, perm["offsets"], a_scale=sx, w_scale=sw, out=gy, ws=gws)
+        if use_mx:
+            moe.gmm_mx(gx, sx, gw, sw, perm["offsets"], out=gy)
+        else:
+            moe.gmm(gx, gw, perm["offsets"], a_scale=sx, w_scale=sw, out=gy, ws=gws)
         if ev is not None:
             ev[1].record(main)
         moe.combine(gy, perm["perm_dst"], None, T, K, out=un)
@@ -404,18 +415,24 @@ def bench_fp8(args, dev):
     sh_ms = float(np.mean([evs[s][3].elapsed_time(evs[s][4]) for s in range(args.steps)]))
     counts = perm["counts"].cpu().numpy().tolist()
     fl, by = flops_bytes_gmm(counts, H1, N1, 1)
+    if use_mx:  # E8M0 scales: one byte per 32 activation and weight elements
+        by += A * (H1 // 32) + sum(1 for c in counts if c > 0) * (H1 // 32) * N1
     achieved = fl / (gmm_ms * 1e-3) / 1e12
+    wl = "fp8mx" if use_mx else "fp8gmm"
     res = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
-        "data": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
-        "config": {"workload": f"fp8gmm: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
+        "data": ("synthetic (seeded; E4M3 with MX E8M0 scales per 32 elements, OCP recipe; "
+                 "random top-8 of 32 routing)" if use_mx else
+                 "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)"),
+        "config": {"workload": f"{wl}: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
                                f"({T},{H2})x({H2},{N2}) bf16", "tokens_per_step": T},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
-                     "traffic": measured_traffic("fp8gmm"),
-                     "kernel": "moe_gmm E4M3 (gmm_pp8_kernel)", "gmm_source": source_digest(),
+                     "traffic": measured_traffic(wl),
+                     "kernel": ("moe_gmm_mx E4M3 + E8M0 (gmm_pp8_kernel<true>)" if use_mx
+                                else "moe_gmm E4M3 (gmm_pp8_kernel)"), "gmm_source": source_digest(),
                      "flops_per_launch": fl,
                      "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
         "kernels": {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
@@ -464,8 +481,8 @@ def main():
     moe.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload == "fp8gmm":
-        res, host = bench_fp8(args, dev)
+    if args.workload in ("fp8gmm", "fp8mx"):
+        res, host = bench_fp8(args, dev, use_mx=args.workload == "fp8mx")
         res["achievable"] = achievable(dev)
     else:
         res, host = bench_layer(args, dev)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10300 /* 1.3.0: moe_gmm_gather (grouped GEMM reading rows through an index) */
+#define MOE_VERSION 10400 /* 1.4.0: moe_gmm_mx (E4M3 grouped GEMM with MX block scales) */
 
 typedef enum {
   MOE_OK = 0,
@@ -141,6 +141,7 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int
  *   w        device (e,Hin,N) in w_dt      N contiguous (shape of gmmWeight)
  *   a_q/w_q  MOE_QUANT_NONE (scale must be NULL) or MOE_QUANT_PER_TENSOR
  *            (scale = device pointer to one fp32); other modes: UNSUPPORTED
+ *            (MOE_QUANT_MX operands go through moe_gmm_mx)
  *   offsets  device (e+1) int32, non-decreasing, offsets[0] = 0 and
  *            offsets[e] = A (not checked on the host: the values live on the
  *            device; offsets outside [0, A] are clamped to it)
@@ -182,6 +183,29 @@ moe_status moe_gmm_gather(const void* a, int a_rows, const int32_t* row_src, int
                           moe_quant_mode w_q, const float* w_scale, const int32_t* offsets, int e, int A,
                           int Hin, int N, moe_act act, void* out, moe_dtype out_dt, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * moe_gmm_mx — grouped GEMM on MX block-scaled E4M3 operands (quant mode 6,
+ * "mx", of "aclnnQuantGroupedMatMulAlltoAllv": the interface description
+ * names per-tensor and mx as the supported quantisations). Every 32
+ * consecutive reduction elements of an activation row and of a weight column
+ * share one E8M0 scale byte s, value 2^(s-127) (255: NaN), the OCP MX
+ * reading of the page's mx mode:
+ *   out[r,n] = act( sum_b 2^(a_scale[r,b]-127) * 2^(w_scale[ex,b,n]-127)
+ *                   * sum_{32b <= h < 32b+32} a[r,h] * w[ex,h,n] )
+ * for offsets[ex] <= r < offsets[ex+1]; one rounding to bf16.
+ *   a        device (A,Hin) E4M3 bytes, rows grouped by expert
+ *   a_scale  device (A, Hin/32) E8M0 bytes
+ *   w        device (e,Hin,N) E4M3 bytes, N contiguous
+ *   w_scale  device (e, Hin/32, N) E8M0 bytes
+ *   offsets, e, A, act   as for moe_gmm
+ *   out      device (A,N) bf16
+ * Hin must be a multiple of 128 and N of 16 (else MOE_ERR_UNSUPPORTED). No
+ * workspace. Errors and validation as for moe_gmm.
+ */
+moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                      const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                      void* stream);
 
 /*
  * moe_combine — back to token order.

@@ -27,7 +27,7 @@ ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
-           "moe_gmm_gather", "moe_combine", "moe_layer_workspace_size", "moe_layer")
+           "moe_gmm_gather", "moe_gmm_mx", "moe_combine", "moe_layer_workspace_size", "moe_layer")
 
 
 class MoeError(RuntimeError):
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
                               i32, vp, sz, vp]
         L.moe_gmm_gather.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32,
                                      i32, i32, i32, vp, i32, vp, sz, vp]
+        L.moe_gmm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
         L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
@@ -208,6 +209,21 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=No
                        _ptr(offsets), e, A, Hin, N, act, _ptr(out), odt, _ptr(ws), nbytes,
                        _stream(stream))
     _check(st, "moe_gmm")
+    return out
+
+
+def gmm_mx(a, a_scale, w, w_scale, offsets, act=ACT_NONE, out=None, stream=None):
+    """moe_gmm_mx: E4M3 a (A,Hin) and w (e,Hin,N) with E8M0 block scales a_scale
+    (A,Hin/32) and w_scale (e,Hin/32,N) (uint8 device tensors); bf16 output."""
+    A, Hin = a.shape
+    e, Hw, N = w.shape
+    if Hw != Hin:
+        raise ValueError("a and w disagree on Hin")
+    if out is None:
+        out = _empty((A, N), torch.bfloat16, a)
+    st = lib().moe_gmm_mx(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(offsets), e, A, Hin, N,
+                          act, _ptr(out), _stream(stream))
+    _check(st, "moe_gmm_mx")
     return out
 
 

@@ -236,6 +236,31 @@ moe_status moe_gmm_gather(const void* a, int a_rows, const int32_t* row_src, int
                      out_dt, ws, ws_bytes, stream, &gx);
 }
 
+moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                      const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                      void* stream) {
+  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
+  if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
+  // 128-deep K slices of whole scale blocks, 16-byte column chunks, 32-bit offsets
+  if (Hin % 128 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)Hin * N >= (1ll << 31) || (int64_t)(Hin / 32) * N * e >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (A == 0) return MOE_OK;
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(a_scale);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(w_scale);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(out);
+  REQUIRE_ALIGNED(a);
+  REQUIRE_ALIGNED(a_scale);
+  REQUIRE_ALIGNED(w);
+  REQUIRE_ALIGNED(w_scale);
+  REQUIRE_ALIGNED(offsets);
+  REQUIRE_ALIGNED(out);
+  return launch_gmm_mx(a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out, (hipStream_t)stream);
+}
+
 moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_dst,
                        const float* topk_gate, int T, int K, int N, void* out, moe_dtype out_dt,
                        void* stream) {

@@ -103,6 +103,10 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                       moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s,
                       Gather gx = Gather{nullptr, 1, 0});
+// Grouped GEMM on MX (E8M0 block-scaled) E4M3 operands; Hin % 128 == 0, N % 16 == 0.
+moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void* w,
+                         const unsigned char* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
+                         moe_act act, void* out, hipStream_t s);
 moe_status launch_combine(const void* y_perm, moe_dtype dt, const int32_t* perm_dst,
                           const float* gate, int T, int K, int N, void* out, hipStream_t s);
 

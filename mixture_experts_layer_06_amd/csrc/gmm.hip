@@ -635,6 +635,17 @@ __device__ __forceinline__ void dma16(u32x4_t srd, uint32_t voff, uint32_t lds_b
 }
 #pragma clang diagnostic pop
 
+// 4 bytes per lane from buffer offset voff into LDS at lds_base + 4*lane.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(u32x4_t srd, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(srd), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -1061,6 +1072,7 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
 // c ^ ((k/2)%4 + 4*((k/32)%2)), so the 16 rows that lanes 0-31 (or 32-63)
 // of one transposing read touch fall in distinct banks.
 
+template <bool MX>
 struct Pp8Cfg {
   static constexpr int kBM = 256, kBN = 128;
   static constexpr int kKB = 128;  // K values (bytes) per slot
@@ -1068,22 +1080,36 @@ struct Pp8Cfg {
   static constexpr int kNT = 512;
   static constexpr int kLdsA = kBM * kKB;  // 32 KB
   static constexpr int kLdsW = kKB * kBN;  // 16 KB
-  static constexpr int kStage = kLdsA + kLdsW;
-  static constexpr int kLds = kStages * kStage;
+  // MX: the slot's E8M0 scales, activations [256 rows][4 blocks] then
+  // weights [4 blocks][128 columns]
+  static constexpr int kScA = kLdsA + kLdsW, kScW = kScA + kBM * 4;
+  static constexpr int kStage = kLdsA + kLdsW + (MX ? kBM * 4 + 4 * kBN : 0);
+  static constexpr int kDummy = kStages * kStage;  // 1 KB that soaks up the unused scale DMA (MX)
+  static constexpr int kLds = kDummy + (MX ? 1024 : 0);
   static constexpr int kADma = kLdsA / 1024 / 8;  // 1 KB DMA ops per wave per slot
   static constexpr int kWDma = kLdsW / 1024 / 8;
-  static constexpr int kPerStage = kADma + kWDma;
+  static constexpr int kPerStage = kADma + kWDma + (MX ? 1 : 0);  // + one 256-byte scale op
+  static_assert(kLds + 2 * 257 * 4 <= 160 * 1024 || kLds <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ int pp8_xswz(int m) { return ((m >> 1) & 1) | (((m >> 2) & 1) << 2); }
-__device__ __forceinline__ int pp8_wswz(int k) { return ((k >> 1) & 3) | (((k >> 5) & 1) << 2); }
+// Slot swizzles. The hardware's K order inside a 16x16x128 operand: lane
+// group g (lanes 16g .. 16g+15) register bytes 0-15 are K 16g .. 16g+15 and
+// bytes 16-31 are K 64+16g .. 64+16g+15 (measured with block scales: scale
+// lane group b covers K 32b .. 32b+31). Fragments are read in that order so
+// that K means the same thing in the data and in MX scale blocks: activation
+// row m holds 16-byte chunk c at position c ^ (2*((m/2)%4)), weight K row k
+// holds output-column chunk c at position c ^ ((k/2)%4 + 4*((k/16)%2)).
+__device__ __forceinline__ int pp8_xswz(int m) { return 2 * ((m >> 1) & 3); }
+__device__ __forceinline__ int pp8_wswz(int k) { return ((k >> 1) & 3) | (((k >> 4) & 1) << 2); }
 
+template <bool MX>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp8_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+    const unsigned char* __restrict__ a_mx, const unsigned char* __restrict__ w_mx,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
     bf16_t* __restrict__ out, Gather gx) {
-  typedef Pp8Cfg C;
+  typedef Pp8Cfg<MX> C;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   {
     int* s_off = reinterpret_cast<int*>(smem);
@@ -1106,6 +1132,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
                                 (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)Hin);
   const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * N, (uint32_t)Hin * (uint32_t)N);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  // MX scales (Hin a multiple of 128): 4 E8M0 blocks per row and slice.
+  // Waves 0-3 fetch the activation rows' scales (one row per lane), waves 4
+  // and 5 the weight columns' (32 lanes per block), waves 6 and 7 an
+  // out-of-range op into the dummy KB, so every wave counts one op per slice.
+  const int nbk = Hin / 32;
+  u32x4_t ssrd = {0u, 0u, 0u, 0u};
+  uint32_t s_voff = kOOB, s_lds = lds0 + C::kDummy, s_step = 0;
+  if (MX) {
+    if (wave < 4) {
+      const int m = 64 * wave + lane;
+      ssrd = make_srd(a_mx + (int64_t)tile.row0 * nbk, (uint32_t)tile.rows * (uint32_t)nbk);
+      s_voff = m < tile.rows ? (uint32_t)m * (uint32_t)nbk : kOOB;
+      s_lds = C::kScA + wave * 256;
+      s_step = 4;
+    } else if (wave < 6) {
+      const int bb = (64 * (wave - 4) + lane) / 32, col = tile.n0 + 4 * (lane % 32);
+      ssrd = make_srd(w_mx + (int64_t)tile.ex * nbk * N, (uint32_t)nbk * (uint32_t)N);
+      s_voff = (uint32_t)bb * (uint32_t)N + (uint32_t)col + (col < N ? 0u : kOOB);
+      s_lds = C::kScW + (wave - 4) * 256;
+      s_step = 4u * (uint32_t)N;
+    } else {
+      ssrd = make_srd(a_mx, 4u);
+    }
+  }
 
   uint32_t a_voff[C::kADma];
   uint32_t a_kc[C::kADma];
@@ -1134,10 +1184,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     for (int q = 0; q < C::kADma; ++q)
       dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < Hin ? 0u : kOOB),
             base + (wave * C::kADma + q) * 1024);
-    const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : kOOB;
+    const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : 0u;
+    const uint32_t kend = step < nsteps ? 0u : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
-      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
+      dma16(wsrd, (w_voff[q] + kstep) | kend, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
+    if (MX)
+      dma4(ssrd, (s_voff + (step < nsteps ? (uint32_t)step * s_step : 0u)) | kend,
+           wave < 6 ? base + s_lds : lds0 + C::kDummy);
   };
   auto bar = [] {
     __builtin_amdgcn_sched_barrier(0);
@@ -1149,17 +1203,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   const bool wave_active = (half * 128 + wm2 * 64 < tile.rows) && (tile.n0 + wn * 64 < N);
   const int ci = lane & 15, kq = lane >> 4;
+  // activation fragment i: chunks kq (register bytes 0-15) and 4 + kq (16-31)
   int xoff[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int m = half * 128 + wm2 * 64 + i * 16 + ci;
-      xoff[i][h] = m * C::kKB + (((2 * kq + h) ^ pp8_xswz(m)) << 4);
+      xoff[i][h] = m * C::kKB + (((4 * h + kq) ^ pp8_xswz(m)) << 4);
     }
-  // transposing weight reads: this lane names K row 32kq + 8t + ci/2 (t = 0..3),
+  // transposing weight reads: read t (= 0..3, register bytes 8t .. 8t+7) takes
+  // K rows 64*(t/2) + 16kq + 8*(t%2) + 0..7; this lane names row ... + ci/2,
   // half ci%2 of output-column chunk 4wn + j
-  const int wk0 = 32 * kq + ci / 2;
+  const int wk0 = 16 * kq + ci / 2;
   const int wsw = pp8_wswz(wk0);  // the same for every t
   const int wrow0 = C::kLdsA + wk0 * C::kBN + 8 * (ci & 1);
   int wch[4];
@@ -1167,6 +1223,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   for (int j = 0; j < 4; ++j) wch[j] = ((4 * wn + j) ^ wsw) * 16;
   typedef int i32x2_t __attribute__((ext_vector_type(2)));
   i32x8_t xa[4], wf[4];
+  int sxa[4], sxw[4];  // MX: this lane's E8M0 scales (block kq of the slice)
   auto read_frags = [&](int slice) {
     const unsigned char* st = smem + (slice % S) * C::kStage;
 #pragma unroll
@@ -1180,10 +1237,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2_t*)(st + wrow0 + wch[j] + t * 8 * C::kBN));
+            (__attribute__((address_space(3))) i32x2_t*)(st + wrow0 + wch[j] +
+                                                          (64 * (t >> 1) + 8 * (t & 1)) * C::kBN));
         wf[j][2 * t] = v.x;
         wf[j][2 * t + 1] = v.y;
       }
+    if (MX) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sxa[i] = st[C::kScA + (half * 128 + wm2 * 64 + i * 16 + ci) * 4 + kq];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sxw[j] = st[C::kScW + kq * C::kBN + wn * 64 + 16 * j + ci];
+    }
   };
   f32x4_t acc[4][4];
 #pragma unroll
@@ -1195,8 +1259,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0, 0,
-                                                                     0, 0);
+        acc[i][j] = MX ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0,
+                                                                          sxw[j], 0, sxa[i])
+                       : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0,
+                                                                          0, 0, 0);
   };
 
 #pragma unroll
@@ -1685,13 +1751,14 @@ moe_status launch_pp(const void* a, const float* as, const void* w, const float*
   return launch_status();
 }
 
+template <bool MX>
 moe_status launch_pp8(const void* a, const float* as, const void* w, const float* ws,
-                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                      hipStream_t s, Gather gx) {
-  typedef Pp8Cfg C;
+                      const unsigned char* a_mx, const unsigned char* w_mx, const int32_t* offsets, int e,
+                      int A, int Hin, int N, int relu, void* out, hipStream_t s, Gather gx) {
+  typedef Pp8Cfg<MX> C;
   static bool attr_done = false;
   if (!attr_done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp8_kernel),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp8_kernel<MX>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     attr_done = true;
   }
@@ -1699,9 +1766,9 @@ moe_status launch_pp8(const void* a, const float* as, const void* w, const float
   const int64_t blocks = mt_max * cdiv64(N, C::kBN);
   const int64_t grid = cdiv64(blocks, 8) * 8;
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL(gmm_pp8_kernel, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
-                     (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
-                     relu, (bf16_t*)out, gx);
+  hipLaunchKernelGGL(gmm_pp8_kernel<MX>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
+                     (const unsigned char*)a, (const unsigned char*)w, as, ws, a_mx, w_mx, offsets, e, A,
+                     Hin, N, relu, (bf16_t*)out, gx);
   return launch_status();
 }
 
@@ -1804,7 +1871,7 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
 #endif
 #if MOE_GMM_FP8 == 1
   if (elem == 1 && al && N % 16 == 0)
-    return launch_pp8(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
+    return launch_pp8<false>(a, a_scale, w, w_scale, nullptr, nullptr, offsets, e, A, Hin, N, relu, out, s, gx);
 #endif
   if (elem == 2) {
     typedef TiledCfg<2, 256, 256, WM, WN, true, false> CA;
@@ -1816,6 +1883,14 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
   typedef TiledCfg<1, 256, 256, WM, WN, false, false> FU;
   return al ? launch_tiled<FA>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx)
             : launch_tiled<FU>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
+}
+
+moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void* w,
+                         const unsigned char* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
+                         moe_act act, void* out, hipStream_t s) {
+  if (A == 0) return MOE_OK;
+  return launch_pp8<true>(a, nullptr, w, nullptr, a_scale, w_scale, offsets, e, A, Hin, N,
+                          act == MOE_ACT_RELU, out, s, Gather{nullptr, 1, 0});
 }
 
 }  // namespace moe

@@ -56,6 +56,9 @@ def lib():
         L.orc_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.orc_gather_rows.argtypes = [vp, i64, vp, i32, i32, vp]
         L.orc_gmm.argtypes = [vp, i32, dbl, vp, i32, dbl, vp, i32, i32, i32, i32, vp, i32, vp, i32]
+        L.orc_gmm_mx.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32]
+        L.orc_e8m0.argtypes = [i32]
+        L.orc_e8m0.restype = dbl
         L.orc_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.orc_expert_ffn.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.orc_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -63,7 +66,7 @@ def lib():
         L.orc_layer_tokens.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
                                        vp, vp, vp, vp, i32]
         L.orc_layer_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
-        for name in ("orc_decode_array", "orc_route", "orc_permute", "orc_gather_rows", "orc_gmm",
+        for name in ("orc_decode_array", "orc_route", "orc_permute", "orc_gather_rows", "orc_gmm", "orc_gmm_mx",
                      "orc_combine", "orc_expert_ffn", "orc_layer", "orc_layer_tokens",
                      "orc_layer_dense"):
             getattr(L, name).restype = i32
@@ -164,6 +167,36 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=1.0, w_scale=1.0, rows=None, nthrea
         prow, nrows = _p(rows), rows.size
     _check(lib().orc_gmm(pa, _code(a), float(a_scale), pw, _code(w), float(w_scale), poff, e, Hin,
                          N, act, prow, nrows, _p(out), int(nthreads)), "gmm")
+    return out
+
+
+def e8m0(s: int) -> float:
+    """Value of one E8M0 scale byte: 2**(s - 127); 255 is NaN."""
+    return lib().orc_e8m0(int(s))
+
+
+def gmm_mx(a, a_scale, w, w_scale, offsets, act=ACT_NONE, rows=None, nthreads=1):
+    """Grouped GEMM on MX block-scaled operands: a (A,Hin) and w (e,Hin,N) E4M3
+    (or any oracle encoding), a_scale (A, Hin/32) and w_scale (e, Hin/32, N)
+    E8M0 bytes (uint8); every 32-element reduction block is scaled by both of
+    its scales. fp64 result."""
+    a, pa = _c(a)
+    w, pw = _c(w)
+    sa, psa = _c(np.asarray(a_scale, np.uint8))
+    sw, psw = _c(np.asarray(w_scale, np.uint8))
+    off, poff = _c(np.asarray(offsets, np.int32))
+    e, Hin, N = w.shape
+    if a.shape[1] != Hin or Hin % 32 or sa.shape != (a.shape[0], Hin // 32) or sw.shape != (e, Hin // 32, N):
+        raise ValueError("gmm_mx: shapes disagree")
+    if rows is None:
+        out = np.empty((int(off[e]), N), np.float64)
+        prow, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, np.int32)
+        out = np.empty((rows.size, N), np.float64)
+        prow, nrows = _p(rows), rows.size
+    _check(lib().orc_gmm_mx(pa, _code(a), psa, pw, _code(w), psw, poff, e, Hin, N, act, prow, nrows, _p(out),
+                            int(nthreads)), "gmm_mx")
     return out
 
 

@@ -289,6 +289,83 @@ int orc_gmm(const void* a, int a_dt, double a_scale, const void* w, int w_dt, do
 }
 
 /* ------------------------------------------------------------------ */
+/* O7, MX form: block-scaled operands                                   */
+/* ------------------------------------------------------------------ */
+
+/* E8M0 scale byte: 2^(s - 127); 255 encodes NaN (OCP MX). */
+double orc_e8m0(int s) {
+  if (s < 0 || s > 255) return NAN;
+  return s == 255 ? NAN : ldexp(1.0, s - 127);
+}
+
+typedef struct {
+  const void* a;
+  int a_dt;
+  const uint8_t* a_scale;
+  const void* w;
+  int w_dt;
+  const uint8_t* w_scale;
+  const int32_t* offsets;
+  int e, Hin, N, act;
+  const int32_t* rows;
+  double* out;
+  int bad;
+} orc_gmm_mx_ctx;
+
+static void orc_gmm_mx_row(void* p, int64_t j) {
+  orc_gmm_mx_ctx* c = (orc_gmm_mx_ctx*)p;
+  int64_t r = c->rows ? c->rows[j] : j;
+  int ex = -1;
+  for (int q = 0; q < c->e; ++q)
+    if (c->offsets[q] <= r && r < c->offsets[q + 1]) {
+      ex = q;
+      break;
+    }
+  double* o = c->out + j * (int64_t)c->N;
+  double* blk = (double*)malloc(sizeof(double) * (size_t)c->N);
+  if (ex < 0 || !blk) {
+    c->bad = 1;
+    for (int n = 0; n < c->N; ++n) o[n] = NAN;
+    free(blk);
+    return;
+  }
+  const int nb = c->Hin / 32;
+  const int64_t wbase = (int64_t)ex * c->Hin * c->N;
+  for (int n = 0; n < c->N; ++n) o[n] = 0.0;
+  for (int b = 0; b < nb; ++b) {
+    /* the block's plain dot products, ascending h, then its two scales */
+    for (int n = 0; n < c->N; ++n) blk[n] = 0.0;
+    for (int h = 32 * b; h < 32 * b + 32; ++h) {
+      double av = orc_decode(c->a, c->a_dt, r * c->Hin + h);
+      for (int n = 0; n < c->N; ++n) blk[n] += av * orc_decode(c->w, c->w_dt, wbase + (int64_t)h * c->N + n);
+    }
+    double sa = orc_e8m0(c->a_scale[r * nb + b]);
+    const uint8_t* swr = c->w_scale + ((int64_t)ex * nb + b) * c->N;
+    for (int n = 0; n < c->N; ++n) o[n] += sa * orc_e8m0(swr[n]) * blk[n];
+  }
+  free(blk);
+  if (c->act == ORC_ACT_RELU)
+    for (int n = 0; n < c->N; ++n)
+      if (o[n] < 0.0) o[n] = 0.0;
+}
+
+int orc_gmm_mx(const void* a, int a_dt, const uint8_t* a_scale, const void* w, int w_dt,
+               const uint8_t* w_scale, const int32_t* offsets, int e, int Hin, int N, int act,
+               const int32_t* rows, int nrows, double* out, int nthreads) {
+  if (!a || !w || !a_scale || !w_scale || !offsets || !out || e <= 0 || Hin <= 0 || N <= 0) return -1;
+  if (Hin % 32 != 0) return -1;
+  if (act != ORC_ACT_NONE && act != ORC_ACT_RELU) return -1;
+  if (offsets[0] != 0) return -1;
+  for (int q = 0; q < e; ++q)
+    if (offsets[q + 1] < offsets[q]) return -1;
+  int64_t n_out = rows ? nrows : offsets[e];
+  if (n_out < 0) return -1;
+  orc_gmm_mx_ctx c = {a, a_dt, a_scale, w, w_dt, w_scale, offsets, e, Hin, N, act, rows, out, 0};
+  orc_parallel_for(n_out, nthreads, orc_gmm_mx_row, &c);
+  return c.bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* O8 combine / Unpermute                                              */
 /* ------------------------------------------------------------------ */
 

@@ -20,7 +20,8 @@
  *     "aclnnQuantGroupedMatMulAlltoAllv" (parameter constraints).
  *   - Grouped GEMM with per-tensor scales  gmmY = (gmmX @ gmmWeight) *
  *     gmmXScale * gmmWeightScale, and Unpermute
- *       ("aclnnQuantGroupedMatMulAlltoAllv", section 计算公式).
+ *       ("aclnnQuantGroupedMatMulAlltoAllv", section 计算公式), and with MX
+ *     (block-scaled) operands, the page's other supported quantisation.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - ties in top-k go to the lower expert index; the k slots are ordered by
@@ -92,6 +93,18 @@ int orc_gather_rows(const void* x, int64_t row_bytes, const int32_t* perm_src, i
 int orc_gmm(const void* a, int a_dt, double a_scale, const void* w, int w_dt, double w_scale,
             const int32_t* offsets, int e, int Hin, int N, int act, const int32_t* rows, int nrows,
             double* out, int nthreads);
+
+/* Grouped GEMM on MX block-scaled operands: every 32 consecutive reduction
+ * elements of an activation row (scales a_scale, (A, Hin/32) bytes) and of a
+ * weight column (w_scale, (e, Hin/32, N) bytes) share one E8M0 scale
+ * 2^(s-127), s = 255 being NaN; out = act(sum over blocks of both scales times
+ * the block's dot product). Quant mode 6 (mx) of
+ * "aclnnQuantGroupedMatMulAlltoAllv"; block size and scale format are the
+ * OCP MX reading. Hin must be a multiple of 32. */
+double orc_e8m0(int s);
+int orc_gmm_mx(const void* a, int a_dt, const uint8_t* a_scale, const void* w, int w_dt,
+               const uint8_t* w_scale, const int32_t* offsets, int e, int Hin, int N, int act,
+               const int32_t* rows, int nrows, double* out, int nthreads);
 
 /* O8: combine. gate != NULL: y[t,n] = sum_{k ascending} gate[t,k] * yp[perm_dst[t*K+k], n]
  * (out is (T,N)). gate == NULL: Unpermute, out[t*K+k, n] = yp[perm_dst[t*K+k], n]

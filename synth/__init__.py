@@ -129,6 +129,27 @@ def quantize_e4m3(a: np.ndarray):
     return to_e4m3(a, s), np.float32(s)
 
 
+def quantize_mx(a: np.ndarray, axis: int):
+    """MX input recipe (OCP microscaling, E4M3 elements): blocks of 32 along
+    `axis` share the power-of-two scale 2^(floor(log2 amax) - 8) (8 = E4M3's
+    largest exponent), stored as an E8M0 byte (exponent + 127); elements are
+    E4M3(a / scale). Returns (E4M3 bytes, same shape; scale bytes, `axis`
+    divided by 32)."""
+    a = np.moveaxis(np.asarray(a, np.float32), axis, -1)
+    shp = a.shape
+    if shp[-1] % 32:
+        raise ValueError("quantize_mx: axis length must be a multiple of 32")
+    blocks = a.reshape(shp[:-1] + (shp[-1] // 32, 32))
+    am = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(am > 0, np.floor(np.log2(np.where(am > 0, am, 1.0))) - 8, 0).astype(np.int32)
+    ex = np.clip(ex, -127, 127)
+    scaled = blocks / np.ldexp(np.float32(1.0), ex)[..., None].astype(np.float32)
+    q = to_e4m3(scaled.reshape(shp), 1.0)
+    sb = (ex + 127).astype(np.uint8)
+    return (np.ascontiguousarray(np.moveaxis(q, -1, axis)), np.ascontiguousarray(np.moveaxis(sb, -1, axis)))
+
+
 def random_routing(seed: int, T: int, E: int, K: int) -> np.ndarray:
     out = np.empty((T, K), np.int32)
     if lib().synth_random_routing(seed, T, E, K, _ptr(out)) != 0:

@@ -22,7 +22,7 @@ def declared_entry_points():
 
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
-    for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_combine", "moe_layer",
+    for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_gmm_mx", "moe_combine", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size",
               "moe_status_string", "moe_version"):
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10300
+    assert moe.lib().moe_version() == 10400
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -240,6 +240,33 @@ def gmm_gather(a=P, a_rows=50, rows=P, div=2, adt=moe.BF16, aq=0, asc=None, w=P,
 ])
 def test_gmm_gather_validation(kw, status):
     assert gmm_gather(**kw) == status
+
+
+def gmm_mx(a=P, sa=P, w=P, sw=P, off=P, e=8, A=100, Hin=256, N=64, act=moe.ACT_NONE, out=P):
+    return L.moe_gmm_mx(a, sa, w, sw, off, e, A, Hin, N, act, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hin=96), moe.ERR_UNSUPPORTED),       # K slices of 128
+    (dict(Hin=200), moe.ERR_UNSUPPORTED),
+    (dict(N=40), moe.ERR_UNSUPPORTED),
+    (dict(act=2), moe.ERR_UNSUPPORTED),
+    (dict(e=0), moe.ERR_BAD_SHAPE),
+    (dict(A=-1), moe.ERR_BAD_SHAPE),
+    (dict(Hin=65536), moe.ERR_BAD_SHAPE),
+    (dict(sa=None), moe.ERR_NULL_POINTER),
+    (dict(sw=None), moe.ERR_NULL_POINTER),
+    (dict(a=None), moe.ERR_NULL_POINTER),
+    (dict(out=None), moe.ERR_NULL_POINTER),
+    (dict(sa=MIS), moe.ERR_MISALIGNED),
+    (dict(w=MIS), moe.ERR_MISALIGNED),
+])
+def test_gmm_mx_validation(kw, status):
+    assert gmm_mx(**kw) == status
+
+
+def test_gmm_mx_zero_rows_is_noop():
+    assert gmm_mx(a=None, sa=None, w=None, sw=None, off=None, out=None, A=0) == moe.OK
 
 
 def test_gmm_gather_zero_rows_is_noop():

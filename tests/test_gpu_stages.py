@@ -370,6 +370,71 @@ def test_gmm_gather_equals_gmm_on_permuted_rows(case):
     assert normwise_err(g, ref) <= {"f32": 2e-6, "bf16": 8e-3, "fp8": 8e-3}[dt]
 
 
+MX_CASES = [
+    # (name, counts, Hin, N): E4M3 with E8M0 block scales
+    ("mx_ragged", [300, 0, 1, 555], 256, 400),
+    ("mx_deep_k", [513, 130], 1024, 128),
+    ("mx_partial_tiles", [257, 3, 0, 31], 128, 144),
+]
+
+
+def _mx_scales(rng, shape):
+    return rng.integers(122, 133, size=shape).astype(np.uint8)
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=[c[0] for c in MX_CASES])
+@pytest.mark.parametrize("act", [moe.ACT_NONE, moe.ACT_RELU], ids=["none", "relu"])
+def test_gmm_mx_parity(case, act):
+    name, counts, Hin, N = case
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    seed = 800 + len(name)
+    a, sa = synth.quantize_mx(synth.normal(seed, (A, Hin)), axis=1)
+    w, sw = synth.quantize_mx(synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin)), axis=1)
+    ref = oracle.gmm_mx(a, sa, w, sw, off, act=act, nthreads=8)
+    out = to_host(moe.gmm_mx(to_dev(a), to_dev(sa), to_dev(w), to_dev(sw), to_dev(off), act=act))
+    err = normwise_err(out, ref)
+    assert err <= TOL["fp8"] and err <= 8e-3, f"{name}: normwise err {err:.3e}"
+
+
+def test_gmm_mx_integer_inputs_bit_exact():
+    """Integer E4M3 values and power-of-two block scales: every fp32 sum is
+    exact, so the bf16 output equals the oracle's rounding bit for bit (a wrong
+    block-to-scale assignment cannot pass)."""
+    counts = [200, 0, 333, 40]
+    Hin, N = 384, 256
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    rng = np.random.default_rng(810)
+    a = synth.to_e4m3(synth.ints(811, (A, Hin), -4, 4), 1.0)
+    w = synth.to_e4m3(synth.ints(812, (e, Hin, N), -4, 4), 1.0)
+    sa = _mx_scales(rng, (A, Hin // 32))
+    sw = _mx_scales(rng, (e, Hin // 32, N))
+    ref = oracle.gmm_mx(a, sa, w, sw, off, act=moe.ACT_RELU, nthreads=8)
+    assert np.abs(ref).max() < 2 ** 24
+    out = to_host(moe.gmm_mx(to_dev(a), to_dev(sa), to_dev(w), to_dev(sw), to_dev(off), act=moe.ACT_RELU))
+    assert np.array_equal(out, oracle.bf16_bits(ref))
+
+
+def test_gmm_mx_unit_scales_match_per_tensor_path():
+    """All scales 127 (1.0): the MX kernel and the per-tensor kernel with unit
+    scales compute the same sums in the same MFMA order."""
+    counts = [260, 7, 0, 300]
+    Hin, N = 256, 192
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    a, _ = synth.quantize_e4m3(synth.normal(820, (A, Hin)))
+    w, _ = synth.quantize_e4m3(synth.normal(821, (e, Hin, N)))
+    sa = np.full((A, Hin // 32), 127, np.uint8)
+    sw = np.full((e, Hin // 32, N), 127, np.uint8)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    mx = to_host(moe.gmm_mx(to_dev(a), to_dev(sa), to_dev(w), to_dev(sw), to_dev(off)))
+    pt = to_host(moe.gmm(to_dev(a), to_dev(w), to_dev(off), a_scale=one, w_scale=one))
+    assert np.array_equal(mx, pt)
+
 # ---------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("dt,N", [("bf16", 264), ("bf16", 30), ("f32", 30), ("f32", 128)])

@@ -300,6 +300,87 @@ def test_gmm_e4m3_integer_inputs_exact_with_power_of_two_scales():
     assert np.array_equal(out, ref * 2.0)
 
 
+# ---- MX (block-scaled) grouped GEMM: quant mode 6 of the CANN interface, read
+# as OCP MX: 32-element reduction blocks, E8M0 scale bytes 2^(s-127).
+
+def test_e8m0_decoding():
+    for s in range(255):
+        assert oracle.e8m0(s) == math.ldexp(1.0, s - 127)
+    assert math.isnan(oracle.e8m0(255))
+
+
+def _mx_ints(seed, counts, Hin, N):
+    e = len(counts)
+    A = int(sum(counts))
+    a_f = synth.ints(seed, (A, Hin), -4, 4)
+    w_f = synth.ints(seed + 1, (e, Hin, N), -4, 4)
+    return a_f, w_f, synth.to_e4m3(a_f, 1.0), synth.to_e4m3(w_f, 1.0)
+
+
+def test_gmm_mx_unit_scales_equal_plain_grouped_gemm():
+    counts = [25, 0, 15]
+    a_f, w_f, a_q, w_q = _mx_ints(20, counts, 64, 24)
+    off = _offsets(counts)
+    sa = np.full((40, 2), 127, np.uint8)
+    sw = np.full((3, 2, 24), 127, np.uint8)
+    assert np.array_equal(oracle.gmm_mx(a_q, sa, w_q, sw, off), oracle.gmm(a_q, w_q, off))
+
+
+def test_gmm_mx_is_the_sum_of_scaled_block_products():
+    """Each 32-deep block enters with the scale of its activation row and of its
+    weight column: the result equals the sum over blocks of plain grouped GEMMs
+    on that block's slice, times 2^(sa-127) 2^(sw-127), exactly (integer
+    inputs, power-of-two scales)."""
+    counts = [20, 13]
+    Hin, N = 96, 10
+    a_f, w_f, a_q, w_q = _mx_ints(22, counts, Hin, N)
+    off = _offsets(counts)
+    rng = np.random.default_rng(23)
+    sa = rng.integers(121, 134, size=(33, Hin // 32)).astype(np.uint8)
+    sw = rng.integers(121, 134, size=(2, Hin // 32, N)).astype(np.uint8)
+    out = oracle.gmm_mx(a_q, sa, w_q, sw, off)
+    ref = np.zeros((33, N))
+    for ex in range(2):
+        r0, r1 = off[ex], off[ex + 1]
+        for b in range(Hin // 32):
+            blk = a_f[r0:r1, 32 * b:32 * b + 32].astype(np.float64) @ w_f[ex, 32 * b:32 * b + 32]
+            ref[r0:r1] += blk * np.exp2(sa[r0:r1, b].astype(np.float64) - 127)[:, None] \
+                * np.exp2(sw[ex, b].astype(np.float64) - 127)[None, :]
+    assert np.array_equal(out, ref)
+
+
+def test_gmm_mx_one_scale_moves_one_block_of_one_column():
+    counts = [12]
+    a_f, w_f, a_q, w_q = _mx_ints(24, counts, 64, 6)
+    off = _offsets(counts)
+    sa = np.full((12, 2), 127, np.uint8)
+    sw = np.full((1, 2, 6), 127, np.uint8)
+    base = oracle.gmm_mx(a_q, sa, w_q, sw, off)
+    sw2 = sw.copy()
+    sw2[0, 1, 4] = 129  # x4 on block 1 of column 4
+    out = oracle.gmm_mx(a_q, sa, w_q, sw2, off)
+    blk1 = a_f[:, 32:].astype(np.float64) @ w_f[0, 32:, 4]
+    assert np.array_equal(np.delete(out, 4, axis=1), np.delete(base, 4, axis=1))
+    assert np.array_equal(out[:, 4], base[:, 4] + 3 * blk1)
+    sa2 = sa.copy()
+    sa2[7, 0] = 255  # NaN scale poisons that row only
+    nan_out = oracle.gmm_mx(a_q, sa2, w_q, sw, off)
+    assert np.isnan(nan_out[7]).all() and not np.isnan(np.delete(nan_out, 7, axis=0)).any()
+
+
+def test_gmm_mx_recipe_roundtrip_close_to_source():
+    """The MX input recipe reproduces the fp32 source to within 2^-3 of the
+    largest magnitude: half an E4M3 step (2^-4 relative) below 1.75 * 2^8 times
+    the block scale, and saturation at 448 (at most 1/8 of a block maximum in
+    [1.75, 2) * 2^(e+8)) above it."""
+    x = synth.normal(25, (16, 128))
+    q, sc = synth.quantize_mx(x, axis=1)
+    qv = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()  # torch's E4M3 decoder
+    deq = qv.reshape(16, 4, 32) * np.exp2(sc.astype(np.float64) - 127)[..., None]
+    err = np.abs(deq.reshape(16, 128) - x).max() / np.abs(x).max()
+    assert err <= 2.0 ** -3
+
+
 def test_gmm_row_subset_equals_full():
     a = synth.normal(12, (50, 16), dtype="bf16")
     w = synth.normal(13, (3, 16, 8), dtype="bf16")
