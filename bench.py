@@ -129,15 +129,17 @@ def _time_ms(fn, iters):
 
 
 def reported_sclk():
-    """The shader clock rocm-smi reports right now (informational), or None."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-    except (OSError, subprocess.SubprocessError):
-        return None
-    for line in r.stdout.splitlines():
-        if "sclk" in line.lower():
-            return line.split(":", 2)[-1].strip()
+    """The shader clock level the driver marks as current in sysfs right now
+    (informational), or None. Read from a file: no child process."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            lines = open(path).read().splitlines()
+        except OSError:
+            continue
+        for line in lines:
+            if line.rstrip().endswith("*"):
+                return line.split(":", 1)[-1].strip(" *")
     return None
 
 
