@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10400 /* 1.4.0: moe_gmm_mx (E4M3 grouped GEMM with MX block scales) */
+#define MOE_VERSION 10500 /* 1.5.0: moe_gmm_scatter (unpermuting, gating stores), moe_sum_slots */
 
 typedef enum {
   MOE_OK = 0,
@@ -185,6 +185,33 @@ moe_status moe_gmm_gather(const void* a, int a_rows, const int32_t* row_src, int
                           size_t ws_bytes, void* stream);
 
 /*
+ * moe_gmm_scatter — moe_gmm whose grouped row r is stored as row row_dst[r]
+ * of out, times row_gate[row_dst[r]] when row_gate is not NULL:
+ *   out[row_dst[r], n] = g * act( (sum_h a[r,h] * w[ex,h,n]) * a_scale * w_scale ),
+ *   g = row_gate ? row_gate[row_dst[r]] : 1, fp32 product, one rounding.
+ * With row_dst = perm_src of moe_permute (grouped row r's (token, slot)
+ * index t*K+k), out is the GEMM's output already unpermuted into (t,k)
+ * order: unpermuteOut = Unpermute(gmmY) ("aclnnQuantGroupedMatMulAlltoAllv",
+ * section 计算公式) fused into the GEMM's stores. With row_gate = the (T,K)
+ * top-k gates as well, out row t*K+k holds g[t,k] * E_k(x_t) and
+ * moe_sum_slots completes y = sum_i g_i(x) E_i(x) (SpMM page, section
+ * "MoE 模型与专家选择的挑战").
+ *   row_dst  device (A) int32, required; each out row that should be written
+ *            must be named by exactly one grouped row. Entries outside
+ *            [0, A) (not checked on the host) are not stored.
+ *   row_gate device fp32 indexed by the destination row (A entries), or NULL
+ *   out      device (A,N) in out_dt; rows no entry names are left untouched
+ * Everything else (types, scales, offsets, act, workspace, errors) is as for
+ * moe_gmm, with the same workspace size; without a gate the stored rows equal
+ * moe_gmm's rows bit for bit.
+ */
+moe_status moe_gmm_scatter(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
+                           const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
+                           const int32_t* offsets, int e, int A, int Hin, int N, moe_act act,
+                           const int32_t* row_dst, const float* row_gate, void* out, moe_dtype out_dt,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_gmm_mx — grouped GEMM on MX block-scaled E4M3 operands (quant mode 6,
  * "mx", of "aclnnQuantGroupedMatMulAlltoAllv": the interface description
  * names per-tensor and mx as the supported quantisations). Every 32
@@ -222,6 +249,16 @@ moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, cons
 moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_dst,
                        const float* topk_gate, int T, int K, int N, void* out, moe_dtype out_dt,
                        void* stream);
+
+/*
+ * moe_sum_slots — y[t,n] = sum_{k=0..K-1} z[t*K+k, n], fp32 sum in ascending
+ * k, one rounding: the K-row sum after moe_gmm_scatter has stored every
+ * (token, slot) row already multiplied by its gate (y = sum_i g_i(x) E_i(x),
+ * SpMM page, section "MoE 模型与专家选择的挑战").
+ *   z device (T*K,N) in dt; out device (T,N) in dt; dt MOE_F32 or MOE_BF16.
+ * Errors: as moe_combine.
+ */
+moe_status moe_sum_slots(const void* z, moe_dtype dt, int T, int K, int N, void* out, void* stream);
 
 /*
  * moe_layer — the whole layer on one stream: route, permute, GEMM 1 with the

@@ -27,7 +27,8 @@ ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
-           "moe_gmm_gather", "moe_gmm_mx", "moe_combine", "moe_layer_workspace_size", "moe_layer")
+           "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx", "moe_combine", "moe_sum_slots",
+           "moe_layer_workspace_size", "moe_layer")
 
 
 class MoeError(RuntimeError):
@@ -61,8 +62,11 @@ def lib() -> ctypes.CDLL:
                               i32, vp, sz, vp]
         L.moe_gmm_gather.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32,
                                      i32, i32, i32, vp, i32, vp, sz, vp]
+        L.moe_gmm_scatter.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
+                                      vp, vp, vp, i32, vp, sz, vp]
         L.moe_gmm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
+        L.moe_sum_slots.argtypes = [vp, i32, i32, i32, i32, vp, vp]
         L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                 vp, vp, sz, vp]
@@ -177,12 +181,16 @@ def gmm_workspace_size(a_dt, e, A, Hin, N) -> int:
 
 
 def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=None, stream=None,
-        rows=None, row_div=1):
+        rows=None, row_div=1, dst=None, gate=None):
     """moe_gmm over w (e,Hin,N). Scales (1-element fp32 device tensors) select
     MOE_QUANT_PER_TENSOR. Output: fp32 for fp32 inputs, else bf16. ws: a device
     buffer of at least gmm_workspace_size() bytes, allocated here when None.
     rows (int32 device tensor, one entry per grouped row): moe_gmm_gather, grouped
-    row r is row rows[r] // row_div of a."""
+    row r is row rows[r] // row_div of a. dst (int32, one entry per grouped row):
+    moe_gmm_scatter, grouped row r is stored as out row dst[r], times gate[dst[r]]
+    when gate (fp32) is given."""
+    if dst is not None and rows is not None:
+        raise ValueError("gather (rows) and scatter (dst) are separate entry points")
     A, Hin = a.shape
     if rows is not None:
         A = rows.numel()
@@ -199,6 +207,12 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=No
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     aq = QUANT_PER_TENSOR if a_scale is not None else QUANT_NONE
     wq = QUANT_PER_TENSOR if w_scale is not None else QUANT_NONE
+    if dst is not None:
+        st = lib().moe_gmm_scatter(_ptr(a), adt, aq, _ptr(a_scale), _ptr(w), wdt, wq, _ptr(w_scale),
+                                   _ptr(offsets), e, A, Hin, N, act, _ptr(dst), _ptr(gate), _ptr(out),
+                                   odt, _ptr(ws), nbytes, _stream(stream))
+        _check(st, "moe_gmm_scatter")
+        return out
     if rows is not None:
         st = lib().moe_gmm_gather(_ptr(a), a.shape[0], _ptr(rows), row_div, adt, aq, _ptr(a_scale),
                                   _ptr(w), wdt, wq, _ptr(w_scale), _ptr(offsets), e, A, Hin, N, act,
@@ -237,6 +251,16 @@ def combine(y_perm, perm_dst, topk_gate, T, K, out=None, stream=None):
     st = lib().moe_combine(_ptr(y_perm), dt, _ptr(perm_dst), _ptr(topk_gate), T, K, N, _ptr(out),
                            dt, _stream(stream))
     _check(st, "moe_combine")
+    return out
+
+
+def sum_slots(z, T, K, out=None, stream=None):
+    """moe_sum_slots: y[t] = sum_k z[t*K+k] for z (T*K,N) -> (T,N)."""
+    N = z.shape[1]
+    dt = dtype_code(z)
+    if out is None:
+        out = _empty((T, N), z.dtype, z)
+    _check(lib().moe_sum_slots(_ptr(z), dt, T, K, N, _ptr(out), _stream(stream)), "moe_sum_slots")
     return out
 
 

@@ -4,7 +4,9 @@
 //            fp32 sum, one rounding to the output type;
 //  unweighted: out[t*K+k] = y_perm[perm_dst[t*K+k]]
 //            (unpermuteOut = Unpermute(gmmY), "aclnnQuantGroupedMatMulAlltoAllv",
-//            section 计算公式).
+//            section 计算公式);
+//  slot sum: y[t] = sum_{k ascending} z[t*K+k], the rows already in (t,k)
+//            order and gated (by the GEMM's scattering epilogue).
 // Both are pure bandwidth kernels: blocks over (output token, column
 // stripe), 16-byte vector accesses when the row pitch allows, every input
 // row read once. Few tokens (decode) get several column stripes per token,
@@ -28,8 +30,9 @@ __global__ __launch_bounds__(256) void combine_weighted_kernel(const void* __res
     float g[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      src[k] = k < K ? perm_dst[(int64_t)t * K + k] : 0;
-      g[k] = k < K ? gate[(int64_t)t * K + k] : 0.f;
+      // no permutation: rows t*K+k in place; no gate: weight 1
+      src[k] = k < K ? (perm_dst != nullptr ? perm_dst[(int64_t)t * K + k] : t * K + k) : 0;
+      g[k] = k < K ? (gate != nullptr ? gate[(int64_t)t * K + k] : 1.f) : 0.f;
     }
     for (int j = blockIdx.y * blockDim.x + threadIdx.x; j < nv; j += gridDim.y * blockDim.x) {
       float acc[VE];
@@ -96,18 +99,24 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const unsigned char* __r
 }  // namespace
 
 moe_status launch_combine(const void* y_perm, moe_dtype dt, const int32_t* perm_dst,
-                          const float* gate, int T, int K, int N, void* out, hipStream_t s) {
+                          const float* gate, int T, int K, int N, void* out, hipStream_t s,
+                          bool sum_slots) {
   if (T == 0) return MOE_OK;
   const bool bf = dt == MOE_BF16;
+  if (sum_slots) {
+    perm_dst = nullptr;
+    gate = nullptr;
+  }
+  const bool weighted = gate != nullptr || sum_slots;
   // column stripes per token: one 256-vector stripe per block when tokens are few
-  const int64_t vecs = gate ? (bf ? N / 8 : N / 4) : (int64_t)N * (bf ? 2 : 4) / 16;
+  const int64_t vecs = weighted ? (bf ? N / 8 : N / 4) : (int64_t)N * (bf ? 2 : 4) / 16;
   int stripes = 1;
   if (T < 2048) {
     const int64_t st = (vecs + 255) / 256;
     stripes = st < 1 ? 1 : (st > 64 ? 64 : (int)st);
   }
   const dim3 grid(T < 65536 ? T : 65536, stripes);
-  if (gate) {
+  if (weighted) {
     if (bf) {
       if (N % 8 == 0)
         hipLaunchKernelGGL((combine_weighted_kernel<true, 8>), dim3(grid), dim3(256), 0, s, y_perm,

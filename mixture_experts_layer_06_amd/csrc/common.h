@@ -91,23 +91,30 @@ size_t permute_ws_bytes(int T, int E, int K);
 moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T, int H, int E, int K,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
                           void* x_perm, void* ws, hipStream_t s);
-// Row gather of a grouped GEMM's input: grouped row r reads row src[r] / div
-// of an input with `rows` rows; src == nullptr: row r itself.
-struct Gather {
-  const int32_t* src;
-  int div;
-  int rows;
+// Row maps of a grouped GEMM. Input: grouped row r reads row src[r] / div of
+// an input with `rows` rows (src == nullptr: row r itself). Output: grouped
+// row r is stored as row dst[r] of out, multiplied by gate[dst[r]] when gate
+// is set (dst == nullptr: row r, no gate); destinations outside [0, A) are
+// not stored.
+struct RowMap {
+  const int32_t* src = nullptr;
+  int div = 1;
+  int rows = 0;
+  const int32_t* dst = nullptr;
+  const float* gate = nullptr;
 };
 size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N);
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                       moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s,
-                      Gather gx = Gather{nullptr, 1, 0});
+                      RowMap gx = RowMap{});
 // Grouped GEMM on MX (E8M0 block-scaled) E4M3 operands; Hin % 128 == 0, N % 16 == 0.
 moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void* w,
                          const unsigned char* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                          moe_act act, void* out, hipStream_t s);
+// sum_slots: y[t] = sum_k y_perm[t*K+k] (perm_dst and gate ignored).
 moe_status launch_combine(const void* y_perm, moe_dtype dt, const int32_t* perm_dst,
-                          const float* gate, int T, int K, int N, void* out, hipStream_t s);
+                          const float* gate, int T, int K, int N, void* out, hipStream_t s,
+                          bool sum_slots = false);
 
 }  // namespace moe

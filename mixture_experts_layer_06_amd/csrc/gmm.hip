@@ -140,10 +140,26 @@ struct Tile {
 
 // Source row of grouped row r under a gather (gx.src != nullptr), or -1 when
 // the entry's quotient falls outside [0, gx.rows).
-__device__ __forceinline__ int gather_src(const Gather& gx, int r) {
+__device__ __forceinline__ int gather_src(const RowMap& gx, int r) {
   const int v = gx.src[r];
   const int q = v >= 0 ? v / gx.div : -1;
   return q < gx.rows ? q : -1;
+}
+
+// Where grouped row m is stored (row m itself without an output map) and the
+// factor it is multiplied by (its gate, else 1); row -1: not stored (a
+// destination outside [0, A)).
+struct OutRow {
+  int64_t row;
+  float gate;
+};
+__device__ __forceinline__ OutRow out_row_of(const RowMap& rm, int64_t m, int d, int A) {
+  if (rm.dst == nullptr) return {m, 1.f};
+  if (d < 0 || d >= A) return {-1, 0.f};
+  return {d, rm.gate != nullptr ? rm.gate[d] : 1.f};
+}
+__device__ __forceinline__ OutRow out_row(const RowMap& rm, int64_t m, int A) {
+  return out_row_of(rm, m, rm.dst != nullptr ? rm.dst[m] : 0, A);
 }
 
 // Logical tile for this block, or false if the block has no work.
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
-    unsigned char* __restrict__ out, Gather gx) {
+    unsigned char* __restrict__ out, RowMap gx) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_off[257];
   __shared__ int s_pre[257];
@@ -567,7 +583,9 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
   for (int i = 0; i < C::kFI; ++i) {
     const int ml = wm * C::kWM + i * 16 + ci;
     if (ml >= tile.rows) continue;
-    const int64_t m = tile.row0 + ml;
+    const OutRow orow = out_row(gx, tile.row0 + ml, A);
+    if (orow.row < 0) continue;
+    const int64_t m = orow.row;
 #pragma unroll
     for (int j = 0; j < C::kFJ; ++j) {
       const int n = tile.n0 + wn * C::kWN + j * 16 + 4 * kq;
@@ -576,6 +594,7 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
       for (int r = 0; r < 4; ++r) {
         v[r] = acc[i][j][r] * sc;
         if (relu) v[r] = v[r] > 0.f ? v[r] : 0.f;
+        v[r] *= orow.gate;
       }
       if (C::kOutF32) {
         float* o = reinterpret_cast<float*>(out) + m * N + n;
@@ -723,7 +742,7 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
     bf16_t* __restrict__ out, float* __restrict__ split_ws, int* __restrict__ split_cnt, int ncu,
-    Gather gx) {
+    RowMap gx) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int s_last;
   // The ring takes all of LDS; the tile prefix borrows its first bytes
@@ -954,13 +973,15 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int ml = frag_row(f);
     const int nb = tile.n0 + wn * C::kWN + g * 64 + 16 * kq;
     if (ml >= tile.rows || nb >= N) return;  // N is a multiple of 16 here
+    const OutRow orow = out_row(gx, tile.row0 + ml, A);
+    if (orow.row < 0) return;
     float v[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const float t = acc16[q] * sc;
-      v[q] = (relu && t < 0.f) ? 0.f : t;
+      v[q] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
     }
-    bf16_t* o = out + (tile.row0 + ml) * (int64_t)N + nb;
+    bf16_t* o = out + orow.row * N + nb;
     reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
     reinterpret_cast<uint4*>(o)[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
@@ -1108,7 +1129,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const unsigned char* __restrict__ a_mx, const unsigned char* __restrict__ w_mx,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
-    bf16_t* __restrict__ out, Gather gx) {
+    bf16_t* __restrict__ out, RowMap gx) {
   typedef Pp8Cfg<MX> C;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   {
@@ -1203,6 +1224,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   const bool wave_active = (half * 128 + wm2 * 64 < tile.rows) && (tile.n0 + wn * 64 < N);
   const int ci = lane & 15, kq = lane >> 4;
+  // output map: this lane's destination rows, fetched now so that the
+  // epilogue does not wait for them
+  int dpre[4] = {0, 0, 0, 0};
+  if (gx.dst != nullptr && wave_active) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
+      dpre[i] = ml < tile.rows ? gx.dst[tile.row0 + ml] : -1;
+    }
+  }
   // activation fragment i: chunks kq (register bytes 0-15) and 4 + kq (16-31)
   int xoff[4][2];
 #pragma unroll
@@ -1327,7 +1358,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   for (int i = 0; i < 4; ++i) {
     const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
     if (ml >= tile.rows) continue;
-    const int64_t m = tile.row0 + ml;
+    const OutRow orow = out_row_of(gx, tile.row0 + ml, dpre[i], A);
+    if (orow.row < 0) continue;
+    const int64_t m = orow.row;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // MFMA j, output row 4*kq + r  ->  column nb + r
@@ -1337,7 +1370,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float t = acc[i][j][r] * sc;
-        v[r] = (relu && t < 0.f) ? 0.f : t;
+        v[r] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
       }
       *reinterpret_cast<uint2*>(out + m * N + nb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
@@ -1353,7 +1386,7 @@ template <int MB, bool AL, bool XS>
 __global__ __launch_bounds__(256) void gmm_stream_kernel(
     const bf16_t* __restrict__ a, const bf16_t* __restrict__ w, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int e, int A, int Hin,
-    int N, int relu, bf16_t* __restrict__ out, Gather gx) {
+    int N, int relu, bf16_t* __restrict__ out, RowMap gx) {
   // Tasks are (non-empty expert, 64 columns), numbered densely so that the
   // waves with work are spread evenly over the CUs: s_pre[q] counts the
   // non-empty experts before q (a "row tile" of 2^30 rows).
@@ -1591,16 +1624,18 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(
     for (int mb = 0; mb < MB; ++mb) {
       const int ml = mc + mb * 16 + ci;
       if (ml >= cnt) continue;
+      const OutRow orow = out_row(gx, r0 + ml, A);
+      if (orow.row < 0) continue;
       float v[16];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float t = acc[mb][j][r] * sc;
-          v[4 * r + j] = (relu && t < 0.f) ? 0.f : t;
+          v[4 * r + j] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
         }
       const int nb = n0 + 16 * kq;
-      bf16_t* o = out + (int64_t)(r0 + ml) * N + nb;
+      bf16_t* o = out + orow.row * N + nb;
       if (AL && nb + 15 < N) {
         uint4 p0 = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
@@ -1627,7 +1662,7 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ w_scale,
                                                       const int32_t* __restrict__ offsets, int e,
                                                       int A, int Hin, int N, int relu,
-                                                      float* __restrict__ out, Gather gx) {
+                                                      float* __restrict__ out, RowMap gx) {
   __shared__ int s_off[257];
   __shared__ int s_pre[257];
   __shared__ float As[kF32BK][kF32BM + 1];
@@ -1673,13 +1708,15 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ 
   for (int i = 0; i < 4; ++i) {
     const int r = ty * 4 + i;
     if (r >= tile.rows) continue;
+    const OutRow orow = out_row(gx, tile.row0 + r, A);
+    if (orow.row < 0) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = tile.n0 + tx * 4 + j;
       if (n >= N) continue;
       float v = acc[i][j] * sc;
       if (relu && v < 0.f) v = 0.f;
-      out[(int64_t)(tile.row0 + r) * N + n] = v;
+      out[orow.row * N + n] = v * orow.gate;
     }
   }
 }
@@ -1689,7 +1726,7 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ 
 template <class C>
 moe_status launch_tiled(const void* a, const float* as, const void* w, const float* ws,
                         const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                        hipStream_t s, Gather gx) {
+                        hipStream_t s, RowMap gx) {
   static bool attr_done = false;
   if (!attr_done) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_tiled_kernel<C>),
@@ -1729,7 +1766,7 @@ int device_cus() {
 template <class C>
 moe_status launch_pp(const void* a, const float* as, const void* w, const float* ws,
                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                     void* split, hipStream_t s, Gather gx) {
+                     void* split, hipStream_t s, RowMap gx) {
   static_assert(C::kBM == 256 && C::kBN == 256, "split scratch is sized for 256 x 256 tiles");
   static bool attr_done = false;
   if (!attr_done) {
@@ -1754,7 +1791,7 @@ moe_status launch_pp(const void* a, const float* as, const void* w, const float*
 template <bool MX>
 moe_status launch_pp8(const void* a, const float* as, const void* w, const float* ws,
                       const unsigned char* a_mx, const unsigned char* w_mx, const int32_t* offsets, int e,
-                      int A, int Hin, int N, int relu, void* out, hipStream_t s, Gather gx) {
+                      int A, int Hin, int N, int relu, void* out, hipStream_t s, RowMap gx) {
   typedef Pp8Cfg<MX> C;
   static bool attr_done = false;
   if (!attr_done) {
@@ -1775,7 +1812,7 @@ moe_status launch_pp8(const void* a, const float* as, const void* w, const float
 template <int MB, bool AL>
 moe_status launch_stream(const void* a, const float* as, const void* w, const float* ws,
                          const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                         hipStream_t s, Gather gx) {
+                         hipStream_t s, RowMap gx) {
   const int64_t tasks = (int64_t)e * cdiv(N, 64);
   const dim3 grid((unsigned)cdiv64(tasks, 4));
   if constexpr (AL && MB >= 2 && MOE_STREAM_XS) {
@@ -1802,7 +1839,7 @@ moe_status launch_stream(const void* a, const float* as, const void* w, const fl
 template <int MB>
 moe_status launch_stream_al(bool al, const void* a, const float* as, const void* w, const float* ws,
                             const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                            hipStream_t s, Gather gx) {
+                            hipStream_t s, RowMap gx) {
   return al ? launch_stream<MB, true>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s, gx)
             : launch_stream<MB, false>(a, as, w, ws, offsets, e, A, Hin, N, relu, out, s, gx);
 }
@@ -1838,7 +1875,7 @@ size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N) {
 
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
-                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s, Gather gx) {
+                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s, RowMap gx) {
   if (A == 0) return MOE_OK;
   const int relu = act == MOE_ACT_RELU;
   if (in_dt == MOE_F32) {
@@ -1890,7 +1927,7 @@ moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void
                          moe_act act, void* out, hipStream_t s) {
   if (A == 0) return MOE_OK;
   return launch_pp8<true>(a, nullptr, w, nullptr, a_scale, w_scale, offsets, e, A, Hin, N,
-                          act == MOE_ACT_RELU, out, s, Gather{nullptr, 1, 0});
+                          act == MOE_ACT_RELU, out, s, RowMap{});
 }
 
 }  // namespace moe

@@ -22,7 +22,8 @@ def declared_entry_points():
 
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
-    for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_gmm_mx", "moe_combine", "moe_layer",
+    for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx",
+              "moe_combine", "moe_sum_slots", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size",
               "moe_status_string", "moe_version"):
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10400
+    assert moe.lib().moe_version() == 10500
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -271,6 +272,62 @@ def test_gmm_mx_zero_rows_is_noop():
 
 def test_gmm_gather_zero_rows_is_noop():
     assert gmm_gather(a=None, rows=None, w=None, off=None, out=None, A=0, a_rows=0) == moe.OK
+
+
+def gmm_scatter(a=P, adt=moe.BF16, aq=0, asc=None, w=P, wdt=moe.BF16, wq=0, wsc=None, off=P, e=8, A=100,
+                Hin=64, N=64, act=moe.ACT_NONE, dst=P, gate=P, out=P, odt=moe.BF16, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        try:
+            ws_bytes = moe.gmm_workspace_size(adt, e, A, Hin, N)
+        except moe.MoeError:
+            ws_bytes = 0
+    return L.moe_gmm_scatter(a, adt, aq, asc, w, wdt, wq, wsc, off, e, A, Hin, N, act, dst, gate, out, odt,
+                             ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dst=None), moe.ERR_NULL_POINTER),
+    (dict(dst=MIS), moe.ERR_MISALIGNED),
+    (dict(gate=MIS), moe.ERR_MISALIGNED),
+    (dict(adt=moe.F32), moe.ERR_BAD_DTYPE),                          # same rules as moe_gmm
+    (dict(aq=3), moe.ERR_UNSUPPORTED),
+    (dict(act=5), moe.ERR_UNSUPPORTED),
+    (dict(e=0), moe.ERR_BAD_SHAPE),
+    (dict(N=0), moe.ERR_BAD_SHAPE),
+    (dict(a=None), moe.ERR_NULL_POINTER),
+    (dict(out=MIS), moe.ERR_MISALIGNED),
+    (dict(A=5000, ws=None), moe.ERR_NULL_POINTER),
+])
+def test_gmm_scatter_validation(kw, status):
+    assert gmm_scatter(**kw) == status
+
+
+def test_gmm_scatter_zero_rows_is_noop():
+    assert gmm_scatter(a=None, w=None, off=None, dst=None, gate=None, out=None, A=0) == moe.OK
+
+
+def sum_slots(z=P, dt=moe.BF16, T=10, K=2, N=64, out=P):
+    return L.moe_sum_slots(z, dt, T, K, N, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=moe.FP8_E4M3), moe.ERR_BAD_DTYPE),
+    (dict(dt=9), moe.ERR_BAD_DTYPE),
+    (dict(K=0), moe.ERR_BAD_SHAPE),
+    (dict(K=9), moe.ERR_BAD_SHAPE),
+    (dict(N=65536), moe.ERR_BAD_SHAPE),
+    (dict(T=-1), moe.ERR_BAD_SHAPE),
+    (dict(z=None), moe.ERR_NULL_POINTER),
+    (dict(out=None), moe.ERR_NULL_POINTER),
+    (dict(z=MIS), moe.ERR_MISALIGNED),
+    (dict(out=MIS), moe.ERR_MISALIGNED),
+])
+def test_sum_slots_validation(kw, status):
+    assert sum_slots(**kw) == status
+
+
+def test_sum_slots_empty_batch_is_noop():
+    assert sum_slots(z=None, out=None, T=0) == moe.OK
 
 
 def combine(y=P, dt=moe.BF16, pdst=P, gate=P, T=10, K=2, N=64, out=P, odt=moe.BF16):

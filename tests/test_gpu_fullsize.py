@@ -130,7 +130,8 @@ def test_gmm_full_size_prefill_sampled_rows(which):
 
 def test_fp8_gmm_unpermute_and_shared_expert_full_size():
     """The page-2 workload: E4M3 grouped GEMM (65536 x 7168 x 2048, 32 experts,
-    per-tensor scales) + Unpermute, and the bf16 shared-expert GEMM."""
+    per-tensor scales) + Unpermute, separate and fused, and the bf16
+    shared-expert GEMM."""
     d = configs.fp8_inputs()
     T, e, K, A, H1, N1 = (d[k] for k in ("T", "e", "K", "A", "H1", "N1"))
     counts, offsets, psrc, pdst = oracle.permute(d["topk_idx"], e)
@@ -153,6 +154,12 @@ def test_fp8_gmm_unpermute_and_shared_expert_full_size():
     assert normwise_err(un_h[psrc[rows]], ref) <= 8e-3
     # the whole unpermute is a bijection of rows
     assert np.array_equal(un_h[psrc], gy_h)
+    # Unpermute fused into the GEMM's stores (the launch the benchmark times) is
+    # the same bytes
+    fu = moe.gmm(to_dev(d["gmm_x"]), to_dev(d["gmm_w"]), perm["offsets"], a_scale=sx, w_scale=sw,
+                 dst=perm["perm_src"])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(fu), un_h)
     # shared expert: e = 1 grouped GEMM == plain GEMM
     mo = moe.gmm(to_dev(d["mm_x"]), to_dev(d["mm_w"]).view(1, d["H2"], d["N2"]),
                  to_dev(np.array([0, T], np.int32)))

@@ -370,6 +370,57 @@ def test_gmm_gather_equals_gmm_on_permuted_rows(case):
     assert normwise_err(g, ref) <= {"f32": 2e-6, "bf16": 8e-3, "fp8": 8e-3}[dt]
 
 
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_gmm_scatter_moves_rows_and_applies_gates(case):
+    """moe_gmm_scatter stores grouped row r as out row dst[r]: without a gate
+    the stored rows equal moe_gmm's bit for bit; destinations outside [0, A)
+    are dropped and the rows nobody names stay untouched; power-of-two gates
+    scale exactly; random gates match the oracle times the gate."""
+    name, counts, Hin, N, dt, K = case
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    rng = np.random.default_rng(len(name) * 17 + A)
+    dst = rng.permutation(A).astype(np.int32)
+    bad = rng.choice(A, size=min(3, A), replace=False)
+    unnamed = dst[bad].copy()
+    dst[bad[0]] = -2
+    if len(bad) > 1:
+        dst[bad[1]] = A
+    if len(bad) > 2:
+        dst[bad[2]] = A + 9
+    valid = (dst >= 0) & (dst < A)
+    seed = 900 + len(name)
+    kw, okw = {}, {}
+    if dt == "fp8":
+        x, sa = synth.quantize_e4m3(synth.normal(seed, (A, Hin)))
+        w, sw = synth.quantize_e4m3(synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin)))
+        kw = dict(a_scale=torch.tensor([sa], dtype=torch.float32, device="cuda"),
+                  w_scale=torch.tensor([sw], dtype=torch.float32, device="cuda"))
+        okw = dict(a_scale=float(sa), w_scale=float(sw))
+    else:
+        x = synth.normal(seed, (A, Hin), dtype=dt)
+        w = synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin), dtype=dt)
+    xd, wd, od, dd = to_dev(x), to_dev(w), to_dev(off), to_dev(dst)
+    odt = torch.float32 if dt == "f32" else torch.bfloat16
+    sentinel = torch.full((A, N), 3.0, dtype=odt, device="cuda")
+    pow2 = np.exp2(rng.integers(-2, 3, size=A)).astype(np.float32)
+    gates = rng.uniform(0.05, 1.0, size=A).astype(np.float32)
+    sent_h = to_host(sentinel)
+    for act in (moe.ACT_NONE, moe.ACT_RELU):
+        plain = to_host(moe.gmm(xd, wd, od, act=act, **kw))
+        s0 = to_host(moe.gmm(xd, wd, od, act=act, dst=dd, out=sentinel.clone(), **kw))
+        assert np.array_equal(s0[dst[valid]], plain[valid]), name
+        assert np.array_equal(s0[unnamed], sent_h[unnamed])
+        s1 = to_host(moe.gmm(xd, wd, od, act=act, dst=dd, gate=to_dev(pow2), out=sentinel.clone(), **kw))
+        scaled = as_f64(plain[valid]) * pow2[dst[valid]][:, None]  # exact: powers of two
+        exp = scaled.astype(np.float32) if dt == "f32" else synth.to_bf16(scaled.astype(np.float32))
+        assert np.array_equal(s1[dst[valid]], exp), name
+    s2 = to_host(moe.gmm(xd, wd, od, act=moe.ACT_RELU, dst=dd, gate=to_dev(gates), **kw))
+    ref = oracle.gmm(x, w, off, act=moe.ACT_RELU, nthreads=8, **okw) * gates[np.clip(dst, 0, A - 1)][:, None]
+    assert normwise_err(s2[dst[valid]], ref[valid]) <= {"f32": 2e-6, "bf16": 8e-3, "fp8": 8e-3}[dt]
+
+
 MX_CASES = [
     # (name, counts, Hin, N): E4M3 with E8M0 block scales
     ("mx_ragged", [300, 0, 1, 555], 256, 400),
@@ -462,6 +513,43 @@ def test_combine_one_hot_gates_is_exact_gather():
     out = moe.combine(to_dev(yp), to_dev(pdst), to_dev(g), T, K)
     _sync()
     assert np.array_equal(to_host(out), yp[pdst.reshape(T, K)[:, 2]])
+
+
+@pytest.mark.parametrize("dt,N", [("bf16", 4096), ("bf16", 30), ("f32", 30), ("f32", 128)])
+@pytest.mark.parametrize("T,K", [(200, 6), (3, 1), (40, 8)])
+def test_sum_slots_parity(dt, N, T, K):
+    """moe_sum_slots is the weighted combine with the identity permutation and
+    unit gates (the oracle's combine), and bit-exact for K = 1 (one rounding of
+    one value is the value)."""
+    z = synth.normal(530 + K, (T * K, N), dtype=dt)
+    out = to_host(moe.sum_slots(to_dev(z), T, K))
+    ref = oracle.combine(as_f64(z), np.arange(T * K, dtype=np.int32), np.ones((T, K)), T, K)
+    assert normwise_err(out, ref) <= (1e-6 if dt == "f32" else 4e-3)
+    if K == 1:
+        assert np.array_equal(out.view(np.uint8), z.view(np.uint8))
+
+
+def test_scatter_then_sum_slots_is_the_weighted_combine():
+    """GEMM 2 storing gated rows in (t,k) order followed by the slot sum equals
+    GEMM 2 in grouped order followed by the weighted combine, to one extra
+    rounding, and both match the oracle."""
+    T, E, K, Hin, N = 300, 16, 4, 256, 512
+    idx = synth.random_routing(540, T, E, K)
+    counts, off, psrc, pdst = oracle.permute(idx, E)
+    A = T * K
+    h = synth.normal(541, (A, Hin), dtype="bf16")
+    w = synth.normal(542, (E, Hin, N), math.sqrt(1.0 / Hin), dtype="bf16")
+    g = np.abs(synth.normal(543, (T, K))).astype(np.float32)
+    g /= g.sum(1, keepdims=True)
+    hd, wd, od = to_dev(h), to_dev(w), to_dev(off)
+    yp = moe.gmm(hd, wd, od)
+    y_a = to_host(moe.combine(yp, to_dev(pdst), to_dev(g), T, K))
+    z = moe.gmm(hd, wd, od, dst=to_dev(psrc), gate=to_dev(g.reshape(-1)))
+    y_b = to_host(moe.sum_slots(z, T, K))
+    ref = oracle.combine(oracle.gmm(h, w, off, nthreads=8), pdst, g.astype(np.float64), T, K)
+    assert normwise_err(y_a, ref) <= 8e-3
+    assert normwise_err(y_b, ref) <= 8e-3
+    assert normwise_err(y_b, as_f64(y_a)) <= 8e-3
 
 
 @pytest.mark.parametrize("dt,N", [("bf16", 2048), ("bf16", 7), ("f32", 5)])
