@@ -57,6 +57,12 @@ def lib():
         L.orc_gather_rows.argtypes = [vp, i64, vp, i32, i32, vp]
         L.orc_gmm.argtypes = [vp, i32, dbl, vp, i32, dbl, vp, i32, i32, i32, i32, vp, i32, vp, i32]
         L.orc_gmm_mx.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32]
+        L.orc_gmm_row_scaled.argtypes = [vp, i32, vp, vp, i32, dbl, vp, i32, i32, i32, i32, vp, i32, vp,
+                                         i32]
+        L.orc_e4m3_nearest.argtypes = [ctypes.c_float]
+        L.orc_e4m3_nearest.restype = ctypes.c_uint8
+        L.orc_e4m3_nearest_array.argtypes = [vp, i64, vp]
+        L.orc_quant_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp]
         L.orc_e8m0.argtypes = [i32]
         L.orc_e8m0.restype = dbl
         L.orc_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp]
@@ -67,6 +73,7 @@ def lib():
                                        vp, vp, vp, vp, i32]
         L.orc_layer_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         for name in ("orc_decode_array", "orc_route", "orc_permute", "orc_gather_rows", "orc_gmm", "orc_gmm_mx",
+                     "orc_gmm_row_scaled", "orc_e4m3_nearest_array", "orc_quant_rows",
                      "orc_combine", "orc_expert_ffn", "orc_layer", "orc_layer_tokens",
                      "orc_layer_dense"):
             getattr(L, name).restype = i32
@@ -151,7 +158,11 @@ def gather_rows(x, perm_src, K):
 
 
 def gmm(a, w, offsets, act=ACT_NONE, a_scale=1.0, w_scale=1.0, rows=None, nthreads=1):
-    """Grouped GEMM: a (A,Hin), w (e,Hin,N), offsets (e+1). fp64 result."""
+    """Grouped GEMM: a (A,Hin), w (e,Hin,N), offsets (e+1). fp64 result.
+    a_scale: one number, or one per grouped row (an array of A values: the
+    per-token scale of gmmX)."""
+    if np.ndim(a_scale) > 0:
+        return _gmm_row_scaled(a, w, offsets, act, a_scale, w_scale, rows, nthreads)
     a, pa = _c(a)
     w, pw = _c(w)
     off, poff = _c(np.asarray(offsets, np.int32))
@@ -168,6 +179,52 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=1.0, w_scale=1.0, rows=None, nthrea
     _check(lib().orc_gmm(pa, _code(a), float(a_scale), pw, _code(w), float(w_scale), poff, e, Hin,
                          N, act, prow, nrows, _p(out), int(nthreads)), "gmm")
     return out
+
+
+def _gmm_row_scaled(a, w, offsets, act, a_scale, w_scale, rows, nthreads):
+    a, pa = _c(a)
+    w, pw = _c(w)
+    rs, prs = _c(np.asarray(a_scale, np.float64).reshape(-1))
+    off, poff = _c(np.asarray(offsets, np.int32))
+    e, Hin, N = w.shape
+    if a.shape[1] != Hin or rs.size != a.shape[0]:
+        raise ValueError("gmm: a, w and the row scales disagree")
+    if rows is None:
+        out = np.empty((int(off[e]), N), np.float64)
+        prow, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, np.int32)
+        out = np.empty((rows.size, N), np.float64)
+        prow, nrows = _p(rows), rows.size
+    _check(lib().orc_gmm_row_scaled(pa, _code(a), prs, pw, _code(w), float(w_scale), poff, e, Hin, N, act,
+                                    prow, nrows, _p(out), int(nthreads)), "gmm (per-row scales)")
+    return out
+
+
+def e4m3_nearest(v) -> np.ndarray:
+    """E4M3 codes (uint8) of the finite E4M3 values nearest to the binary32
+    values v, ties to the even code, +-448 beyond the range."""
+    v, pv = _c(np.asarray(v, np.float32))
+    out = np.empty(v.shape, np.uint8)
+    _check(lib().orc_e4m3_nearest_array(pv, v.size, _p(out)), "e4m3_nearest")
+    return out
+
+
+def quant_rows(x, rows=None, div=1):
+    """Per-token dynamic E4M3 quantisation (binary32 arithmetic): for each
+    output row, the source row t = rows[r] // div (or r), scale = max|x[t]| / 448,
+    codes = nearest E4M3 of x[t] / scale. Returns (codes (R,H) uint8, scales (R,) float32)."""
+    x, px = _c(x)
+    n, H = x.shape
+    if rows is None:
+        R, pr = n, None
+    else:
+        rows = np.ascontiguousarray(rows, np.int32)
+        R, pr = rows.size, _p(rows)
+    q = np.empty((R, H), np.uint8)
+    sc = np.empty(R, np.float32)
+    _check(lib().orc_quant_rows(px, _code(x), n, H, pr, int(div), R, _p(q), _p(sc)), "quant_rows")
+    return q, sc
 
 
 def e8m0(s: int) -> float:

@@ -234,6 +234,7 @@ typedef struct {
   const void* a;
   int a_dt;
   double a_scale;
+  const double* a_row_scale; /* NULL: a_scale for every row */
   const void* w;
   int w_dt;
   double w_scale;
@@ -265,7 +266,7 @@ static void orc_gmm_row(void* p, int64_t j) {
     double av = orc_decode(c->a, c->a_dt, r * c->Hin + h);
     for (int n = 0; n < c->N; ++n) o[n] += av * orc_decode(c->w, c->w_dt, wbase + (int64_t)h * c->N + n);
   }
-  double sc = c->a_scale * c->w_scale;
+  double sc = (c->a_row_scale ? c->a_row_scale[r] : c->a_scale) * c->w_scale;
   for (int n = 0; n < c->N; ++n) {
     double v = o[n] * sc;
     if (c->act == ORC_ACT_RELU && v < 0.0) v = 0.0;
@@ -283,9 +284,94 @@ int orc_gmm(const void* a, int a_dt, double a_scale, const void* w, int w_dt, do
     if (offsets[q + 1] < offsets[q]) return -1;
   int64_t n_out = rows ? nrows : offsets[e];
   if (n_out < 0) return -1;
-  orc_gmm_ctx c = {a, a_dt, a_scale, w, w_dt, w_scale, offsets, e, Hin, N, act, rows, out, 0};
+  orc_gmm_ctx c = {a, a_dt, a_scale, NULL, w, w_dt, w_scale, offsets, e, Hin, N, act, rows, out, 0};
   orc_parallel_for(n_out, nthreads, orc_gmm_row, &c);
   return c.bad ? -1 : 0;
+}
+
+int orc_gmm_row_scaled(const void* a, int a_dt, const double* a_row_scale, const void* w, int w_dt,
+                       double w_scale, const int32_t* offsets, int e, int Hin, int N, int act,
+                       const int32_t* rows, int nrows, double* out, int nthreads) {
+  if (!a_row_scale || !a || !w || !offsets || !out || e <= 0 || Hin <= 0 || N <= 0) return -1;
+  if (act != ORC_ACT_NONE && act != ORC_ACT_RELU) return -1;
+  if (offsets[0] != 0) return -1;
+  for (int q = 0; q < e; ++q)
+    if (offsets[q + 1] < offsets[q]) return -1;
+  int64_t n_out = rows ? nrows : offsets[e];
+  if (n_out < 0) return -1;
+  orc_gmm_ctx c = {a, a_dt, 1.0, a_row_scale, w, w_dt, w_scale, offsets, e, Hin, N, act, rows, out, 0};
+  orc_parallel_for(n_out, nthreads, orc_gmm_row, &c);
+  return c.bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-token E4M3 quantisation                                          */
+/* ------------------------------------------------------------------ */
+
+/* Codes 0x00 .. 0x7e are the non-negative finite E4M3 values in increasing
+ * order (the exponent field sits above the mantissa field), so the nearest
+ * value is found by bisection over the codes. */
+uint8_t orc_e4m3_nearest(float v) {
+  if (isnan(v)) return 0x7f;
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs((double)v);
+  uint8_t one = 0;
+  if (a >= 448.0) return sign | 0x7e;
+  int lo = 0, hi = 0x7e; /* value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (dec_e4m3(&(uint8_t){(uint8_t)mid}, 0) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const double dl = a - dec_e4m3(&(uint8_t){(uint8_t)lo}, 0);
+  const double dh = dec_e4m3(&(uint8_t){(uint8_t)hi}, 0) - a;
+  if (dl < dh)
+    one = (uint8_t)lo;
+  else if (dh < dl)
+    one = (uint8_t)hi;
+  else
+    one = (uint8_t)((lo & 1) ? hi : lo); /* tie: the even code */
+  return sign | one;
+}
+
+int orc_e4m3_nearest_array(const float* v, int64_t n, uint8_t* out) {
+  if (!v || !out || n < 0) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_nearest(v[i]);
+  return 0;
+}
+
+int orc_quant_rows(const void* x, int x_dt, int x_rows, int H, const int32_t* src, int div, int rows,
+                   uint8_t* q, float* scale) {
+  if (!x || !q || !scale || x_rows < 0 || H <= 0 || rows < 0 || div < 1) return -1;
+  if (x_dt != ORC_F32 && x_dt != ORC_BF16) return -1;
+  for (int r = 0; r < rows; ++r) {
+    int64_t t = r;
+    if (src) t = src[r] >= 0 ? src[r] / div : -1;
+    uint8_t* qr = q + (int64_t)r * H;
+    if (t < 0 || t >= x_rows) {
+      memset(qr, 0, (size_t)H);
+      scale[r] = 0.0f;
+      continue;
+    }
+    float amax = 0.0f;
+    for (int h = 0; h < H; ++h) {
+      float xv = (float)orc_decode(x, x_dt, t * H + h); /* exact: bf16 and f32 are binary32 values */
+      if (fabsf(xv) > amax) amax = fabsf(xv);
+    }
+    const float s = amax / 448.0f;
+    scale[r] = s;
+    for (int h = 0; h < H; ++h) {
+      if (amax == 0.0f) {
+        qr[h] = 0;
+        continue;
+      }
+      float xv = (float)orc_decode(x, x_dt, t * H + h);
+      qr[h] = orc_e4m3_nearest(xv / s);
+    }
+  }
+  return 0;
 }
 
 /* ------------------------------------------------------------------ */

@@ -106,6 +106,26 @@ int orc_gmm_mx(const void* a, int a_dt, const uint8_t* a_scale, const void* w, i
                const uint8_t* w_scale, const int32_t* offsets, int e, int Hin, int N, int act,
                const int32_t* rows, int nrows, double* out, int nthreads);
 
+/* Per-token quantisation to E4M3 (quant modes 3 "pertoken" and 7 "pertoken
+ * dynamic" of "aclnnQuantGroupedMatMulAlltoAllv", 量化模式 enumeration; the
+ * formula there multiplies gmmX's scale back onto the product).
+ * orc_e4m3_nearest: the code of the finite E4M3 value nearest to v, ties to
+ * the even code (mantissa bit 0 clear); |v| above 448 gives +-448, NaN 0x7f.
+ * orc_quant_rows: row r of q is source row t = src ? src[r] / div : r of x
+ * (x_rows rows, H values each, in x_dt); in binary32 arithmetic: amax = the
+ * largest |x[t,h]|, scale[r] = amax / 448, q[r,h] = nearest(x[t,h] / scale[r]);
+ * amax == 0 or a source row outside [0, x_rows): all codes 0, scale 0. */
+uint8_t orc_e4m3_nearest(float v);
+int orc_e4m3_nearest_array(const float* v, int64_t n, uint8_t* out);
+int orc_quant_rows(const void* x, int x_dt, int x_rows, int H, const int32_t* src, int div, int rows,
+                   uint8_t* q, float* scale);
+
+/* O7 with a per-row activation scale: as orc_gmm with a_scale replaced by
+ * a_row_scale[r] for grouped row r (gmmXScale of shape (A,), per-token). */
+int orc_gmm_row_scaled(const void* a, int a_dt, const double* a_row_scale, const void* w, int w_dt,
+                       double w_scale, const int32_t* offsets, int e, int Hin, int N, int act,
+                       const int32_t* rows, int nrows, double* out, int nthreads);
+
 /* O8: combine. gate != NULL: y[t,n] = sum_{k ascending} gate[t,k] * yp[perm_dst[t*K+k], n]
  * (out is (T,N)). gate == NULL: Unpermute, out[t*K+k, n] = yp[perm_dst[t*K+k], n]
  * (out is (T*K,N)). */

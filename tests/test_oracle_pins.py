@@ -473,3 +473,113 @@ def test_layer_skew_bias_forced_empty_experts():
     res = oracle.layer(d["x"], d["wr"], d["w1"], d["w2"], d["K"], bias=b)
     assert res["counts"][6] == 0 and res["counts"][7] == 0
     assert res["counts"].sum() == d["T"] * d["K"]
+
+
+# ---- Per-token E4M3 quantisation (quant modes 3 / 7 of the CANN interface):
+# nearest E4M3 value with ties to the even code, scale = row amax / 448, all in
+# binary32.
+
+def _all_e4m3_values():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode(codes)
+    finite = ~np.isnan(vals)
+    return codes[finite], vals[finite]
+
+
+def test_e4m3_nearest_matches_torch_in_range():
+    """torch's float -> float8_e4m3fn conversion rounds to nearest even; inside
+    the finite range the oracle's codes must be the same, also on every exact
+    value and on every midpoint between neighbours (the ties)."""
+    rng = np.random.default_rng(40)
+    mag = np.exp2(rng.uniform(-12, math.log2(448.0), 20000))
+    v = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    _, vals = _all_e4m3_values()
+    pos = np.unique(vals[vals >= 0])
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (pos[1:] + pos[:-1]) / 2)  # midpoints are exact in binary32
+    v = np.concatenate([v, pos.astype(np.float32), mids, -mids])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_nearest(v), ref)
+
+
+def test_e4m3_nearest_is_the_nearest_value_by_brute_force():
+    rng = np.random.default_rng(41)
+    v = (rng.standard_normal(3000) * np.exp2(rng.integers(-10, 9, 3000))).astype(np.float32)
+    v = v[np.abs(v) < 448]
+    codes, vals = _all_e4m3_values()
+    got = oracle.decode(oracle.e4m3_nearest(v))
+    dist = np.abs(v.astype(np.float64)[:, None] - vals[None, :])
+    best = dist.min(axis=1)
+    assert np.array_equal(np.abs(got - v.astype(np.float64)), best)
+    # ties go to the even code: exactly half-way between 1 and 1.125 (codes 0x38, 0x39)
+    assert oracle.e4m3_nearest(np.float32(1.0625)) == 0x38
+    assert oracle.e4m3_nearest(np.float32(1.1875)) == 0x3A
+
+
+def test_e4m3_nearest_saturates_and_keeps_sign():
+    v = np.array([448.0, 449.0, 464.0, 1e30, -1e30, -448.0, np.nan, -0.0, -1e-10, 2 ** -10],
+                 np.float32)
+    got = oracle.e4m3_nearest(v)
+    assert list(got) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x80, 0x80, 0x00]
+
+
+def test_quant_rows_scale_and_error_bound():
+    rng = np.random.default_rng(42)
+    x = (rng.standard_normal((64, 300)) * np.exp2(rng.integers(-6, 6, (64, 1)))).astype(np.float32)
+    q, s = oracle.quant_rows(x)
+    amax = np.abs(x).max(axis=1)
+    assert np.array_equal(s, (amax / np.float32(448)).astype(np.float32))
+    # the largest element of each row lands on +-448
+    arg = np.abs(x).argmax(axis=1)
+    assert np.all((q[np.arange(64), arg] & 0x7F) == 0x7E)
+    # within half a step of the value grid: 2^-4 relative (normal), 2^-10 * scale (subnormal)
+    deq = oracle.decode(q) * s[:, None].astype(np.float64)
+    ratio = np.abs(x) / s[:, None]
+    bound = np.where(ratio >= 2 ** -6, np.abs(x) * 2 ** -4, s[:, None] * 2 ** -10) * (1 + 1e-6)
+    assert np.all(np.abs(deq - x) <= bound)
+
+
+def test_quant_rows_special_cases():
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((10, 64)).astype(np.float32)
+    x[3] = 0.0
+    q, s = oracle.quant_rows(x)
+    assert s[3] == 0 and not q[3].any()
+    # scaling a row by a power of two scales its scale and keeps its codes
+    q2, s2 = oracle.quant_rows(x * np.float32(8.0))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(8.0))
+    # gathering: output row r quantises source row rows[r] // div; out of range -> zero row
+    rows = np.array([5, 0, 19, -1, 40, 7], np.int32)
+    qg, sg = oracle.quant_rows(x, rows=rows, div=2)
+    src = rows // 2
+    for r, t in enumerate(src):
+        if 0 <= rows[r] and t < 10:
+            assert np.array_equal(qg[r], q[t]) and sg[r] == s[t]
+        else:
+            assert not qg[r].any() and sg[r] == 0
+    # bf16 input: the same as its binary32 values
+    xb = synth.to_bf16(x)
+    qb, sb = oracle.quant_rows(xb)
+    qf, sf = oracle.quant_rows(synth.bf16_to_f32(xb))
+    assert np.array_equal(qb, qf) and np.array_equal(sb, sf)
+
+
+def test_gmm_row_scales():
+    """Per-row activation scales: unit scales are the scale-free product, a
+    constant is the per-tensor scale, and each row's scale moves only its row."""
+    rng = np.random.default_rng(44)
+    counts = [5, 0, 9, 3]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    a = rng.integers(-3, 4, (A, 48)).astype(np.float32)
+    w = rng.integers(-2, 3, (4, 48, 20)).astype(np.float32)
+    base = oracle.gmm(a, w, off)
+    assert np.array_equal(oracle.gmm(a, w, off, a_scale=np.ones(A)), base)
+    assert np.array_equal(oracle.gmm(a, w, off, a_scale=np.full(A, 0.375), w_scale=2.0),
+                          oracle.gmm(a, w, off, a_scale=0.375, w_scale=2.0))
+    rs = np.ones(A)
+    rs[7] = 4.0
+    got = oracle.gmm(a, w, off, a_scale=rs, act=oracle.ACT_RELU)
+    ref = oracle.gmm(a, w, off, act=oracle.ACT_RELU)
+    assert np.array_equal(np.delete(got, 7, axis=0), np.delete(ref, 7, axis=0))
+    assert np.array_equal(got[7], 4.0 * ref[7])
