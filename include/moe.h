@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10500 /* 1.5.0: moe_gmm_scatter (unpermuting, gating stores), moe_sum_slots */
+#define MOE_VERSION 10600 /* 1.6.0: moe_quant_rows and per-token E4M3 activation scales */
 
 typedef enum {
   MOE_OK = 0,
@@ -140,8 +140,13 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int
  *   a        device (A,Hin) in a_dt        rows grouped by expert
  *   w        device (e,Hin,N) in w_dt      N contiguous (shape of gmmWeight)
  *   a_q/w_q  MOE_QUANT_NONE (scale must be NULL) or MOE_QUANT_PER_TENSOR
- *            (scale = device pointer to one fp32); other modes: UNSUPPORTED
- *            (MOE_QUANT_MX operands go through moe_gmm_mx)
+ *            (scale = device pointer to one fp32); for E4M3 activations also
+ *            a_q = MOE_QUANT_PER_TOKEN: a_scale = device fp32, one per row of
+ *            a (16-byte aligned), multiplying that row's products (gmmXScale
+ *            of shape (A,)); moe_quant_rows makes such rows. Other modes:
+ *            UNSUPPORTED (MOE_QUANT_MX operands go through moe_gmm_mx;
+ *            MOE_QUANT_PER_TOKEN_DYNAMIC is moe_quant_rows followed by
+ *            MOE_QUANT_PER_TOKEN)
  *   offsets  device (e+1) int32, non-decreasing, offsets[0] = 0 and
  *            offsets[e] = A (not checked on the host: the values live on the
  *            device; offsets outside [0, A] are clamped to it)
@@ -153,7 +158,8 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int
  *            the reduction and their fp32 partial sums meet here; the parts
  *            are added in a fixed order, so results do not depend on timing.
  * Supported types (a_dt, w_dt -> out_dt): F32,F32->F32; BF16,BF16->BF16;
- * FP8,FP8->BF16 (FP8 requires MOE_QUANT_PER_TENSOR on both sides).
+ * FP8,FP8->BF16 (FP8 requires MOE_QUANT_PER_TENSOR or, for a, MOE_QUANT_PER_TOKEN
+ * and MOE_QUANT_PER_TENSOR for w).
  * Accumulation is fp32; the scales multiply the fp32 sum; one rounding to
  * out_dt. Experts with no rows cost nothing and write nothing.
  */
@@ -259,6 +265,28 @@ moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_
  * Errors: as moe_combine.
  */
 moe_status moe_sum_slots(const void* z, moe_dtype dt, int T, int K, int N, void* out, void* stream);
+
+/*
+ * moe_quant_rows — per-token dynamic quantisation to E4M3 (quant modes 3
+ * "pertoken" and 7 "pertoken dynamic" of "aclnnQuantGroupedMatMulAlltoAllv",
+ * 量化模式 enumeration). Output row r quantises source row
+ * t = row_src ? row_src[r] / row_div : r of x, in binary32:
+ *   scale[r] = max_h |x[t,h]| / 448
+ *   q[r,h]   = the E4M3 value nearest to x[t,h] / scale[r], ties to the even
+ *              code, saturating at +-448 (OCP E4M3, no infinities)
+ * A zero row, or a source row outside [0, x_rows) (not checked on the host),
+ * gives codes 0 and scale 0. With row_src = perm_src of moe_permute and
+ * row_div = K the dispatch copy and the quantisation are one pass (gmmX in
+ * E4M3 with its per-row gmmXScale); with row_src = NULL the tokens are
+ * quantised once and moe_gmm_gather reads them (and their scales) by index.
+ *   x      device (x_rows,H) in x_dt (MOE_F32 or MOE_BF16), 16-byte aligned
+ *   row_src device (rows) int32 or NULL (then rows <= x_rows); row_div >= 1
+ *   q      device (rows,H) bytes, E4M3 codes; scale device (rows) fp32
+ * Errors: BAD_DTYPE, BAD_SHAPE (H outside (0,65536), rows < 0, row_div < 1,
+ * rows > x_rows without row_src), NULL_POINTER, MISALIGNED.
+ */
+moe_status moe_quant_rows(const void* x, moe_dtype x_dt, int x_rows, int H, const int32_t* row_src,
+                          int row_div, int rows, uint8_t* q, float* scale, void* stream);
 
 /*
  * moe_layer — the whole layer on one stream: route, permute, GEMM 1 with the

@@ -22,13 +22,13 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 OK, ERR_NULL_POINTER, ERR_BAD_SHAPE, ERR_BAD_DTYPE, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_DEVICE = 5, 6, 7
 F32, BF16, FP8_E4M3 = 0, 1, 2
-QUANT_NONE, QUANT_PER_TENSOR = 0, 1
+QUANT_NONE, QUANT_PER_TENSOR, QUANT_PER_TOKEN = 0, 1, 3
 ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
            "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx", "moe_combine", "moe_sum_slots",
-           "moe_layer_workspace_size", "moe_layer")
+           "moe_quant_rows", "moe_layer_workspace_size", "moe_layer")
 
 
 class MoeError(RuntimeError):
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.moe_gmm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
         L.moe_sum_slots.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        L.moe_quant_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp, vp]
         L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                 vp, vp, sz, vp]
@@ -181,14 +182,15 @@ def gmm_workspace_size(a_dt, e, A, Hin, N) -> int:
 
 
 def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=None, stream=None,
-        rows=None, row_div=1, dst=None, gate=None):
+        rows=None, row_div=1, dst=None, gate=None, per_token=False):
     """moe_gmm over w (e,Hin,N). Scales (1-element fp32 device tensors) select
     MOE_QUANT_PER_TENSOR. Output: fp32 for fp32 inputs, else bf16. ws: a device
     buffer of at least gmm_workspace_size() bytes, allocated here when None.
     rows (int32 device tensor, one entry per grouped row): moe_gmm_gather, grouped
     row r is row rows[r] // row_div of a. dst (int32, one entry per grouped row):
     moe_gmm_scatter, grouped row r is stored as out row dst[r], times gate[dst[r]]
-    when gate (fp32) is given."""
+    when gate (fp32) is given. per_token: a_scale holds one fp32 per row of a
+    (MOE_QUANT_PER_TOKEN, E4M3 activations)."""
     if dst is not None and rows is not None:
         raise ValueError("gather (rows) and scatter (dst) are separate entry points")
     A, Hin = a.shape
@@ -206,6 +208,8 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=No
         ws = _empty((n,), torch.uint8, a) if n else None
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     aq = QUANT_PER_TENSOR if a_scale is not None else QUANT_NONE
+    if per_token:
+        aq = QUANT_PER_TOKEN
     wq = QUANT_PER_TENSOR if w_scale is not None else QUANT_NONE
     if dst is not None:
         st = lib().moe_gmm_scatter(_ptr(a), adt, aq, _ptr(a_scale), _ptr(w), wdt, wq, _ptr(w_scale),
@@ -252,6 +256,22 @@ def combine(y_perm, perm_dst, topk_gate, T, K, out=None, stream=None):
                            dt, _stream(stream))
     _check(st, "moe_combine")
     return out
+
+
+def quant_rows(x, rows=None, row_div=1, n_out=None, q=None, scale=None, stream=None):
+    """moe_quant_rows: per-token dynamic E4M3 quantisation of x (f32/bf16,
+    (x_rows,H)); output row r quantises x[rows[r] // row_div] (or x[r]).
+    Returns (codes (R,H) float8_e4m3fn, scales (R,) fp32)."""
+    x_rows, H = x.shape
+    R = (rows.numel() if rows is not None else x_rows) if n_out is None else n_out
+    if q is None:
+        q = _empty((R, H), torch.float8_e4m3fn, x)
+    if scale is None:
+        scale = _empty((R,), torch.float32, x)
+    st = lib().moe_quant_rows(_ptr(x), dtype_code(x), x_rows, H, _ptr(rows), row_div, R, _ptr(q), _ptr(scale),
+                              _stream(stream))
+    _check(st, "moe_quant_rows")
+    return q, scale
 
 
 def sum_slots(z, T, K, out=None, stream=None):

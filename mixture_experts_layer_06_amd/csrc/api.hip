@@ -188,8 +188,11 @@ moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const 
                        (a_dt == MOE_FP8_E4M3 && w_dt == MOE_FP8_E4M3 && out_dt == MOE_BF16);
   if (!pair_ok) return MOE_ERR_BAD_DTYPE;
   if ((int)a_q < 0 || (int)a_q > 7 || (int)w_q < 0 || (int)w_q > 7) return MOE_ERR_UNSUPPORTED;
-  if (a_q > MOE_QUANT_PER_TENSOR || w_q > MOE_QUANT_PER_TENSOR) return MOE_ERR_UNSUPPORTED;
-  if (a_dt == MOE_FP8_E4M3 && (a_q != MOE_QUANT_PER_TENSOR || w_q != MOE_QUANT_PER_TENSOR))
+  // per-token activation scales: E4M3 activations with a per-tensor weight scale
+  const bool per_token = a_q == MOE_QUANT_PER_TOKEN;
+  if (per_token && (a_dt != MOE_FP8_E4M3 || w_q != MOE_QUANT_PER_TENSOR)) return MOE_ERR_UNSUPPORTED;
+  if ((a_q > MOE_QUANT_PER_TENSOR && !per_token) || w_q > MOE_QUANT_PER_TENSOR) return MOE_ERR_UNSUPPORTED;
+  if (a_dt == MOE_FP8_E4M3 && ((a_q != MOE_QUANT_PER_TENSOR && !per_token) || w_q != MOE_QUANT_PER_TENSOR))
     return MOE_ERR_UNSUPPORTED;
   if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
   if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
@@ -199,7 +202,7 @@ moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const 
     // the gathered rows are addressed with 32-bit byte offsets
     if ((int64_t)gx->rows * Hin * dtype_size(a_dt) >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   }
-  if (a_q == MOE_QUANT_PER_TENSOR) REQUIRE_PTR(a_scale);
+  if (a_q == MOE_QUANT_PER_TENSOR || per_token) REQUIRE_PTR(a_scale);
   if (w_q == MOE_QUANT_PER_TENSOR) REQUIRE_PTR(w_scale);
   if (A == 0) return MOE_OK;
   REQUIRE_PTR(a);
@@ -222,11 +225,16 @@ moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const 
   REQUIRE_ALIGNED(offsets);
   REQUIRE_ALIGNED(out);
   REQUIRE_ALIGNED(ws);
-  // scales are 4-byte device scalars: natural alignment suffices
+  // per-tensor scales are 4-byte device scalars: natural alignment suffices
   const float* as = a_q == MOE_QUANT_PER_TENSOR ? a_scale : nullptr;
   const float* wsc = w_q == MOE_QUANT_PER_TENSOR ? w_scale : nullptr;
+  RowMap rm = gx ? *gx : RowMap{};
+  if (per_token) {
+    REQUIRE_ALIGNED(a_scale);
+    rm.row_scale = a_scale;
+  }
   return launch_gmm(a, a_dt, as, w, wsc, offsets, e, A, Hin, N, act, out, out_dt, need > 0 ? ws : nullptr,
-                    (hipStream_t)stream, gx ? *gx : RowMap{});
+                    (hipStream_t)stream, rm);
 }
 }  // namespace
 
@@ -300,6 +308,22 @@ moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_
   REQUIRE_ALIGNED(topk_gate);
   REQUIRE_ALIGNED(out);
   return launch_combine(y_perm, in_dt, perm_dst, topk_gate, T, K, N, out, (hipStream_t)stream);
+}
+
+moe_status moe_quant_rows(const void* x, moe_dtype x_dt, int x_rows, int H, const int32_t* row_src,
+                          int row_div, int rows, uint8_t* q, float* scale, void* stream) {
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_BAD_DTYPE;
+  if (x_rows < 0 || rows < 0 || !dim_ok(H) || row_div < 1 || (int64_t)rows >= kMaxRows) return MOE_ERR_BAD_SHAPE;
+  if (row_src == nullptr && rows > x_rows) return MOE_ERR_BAD_SHAPE;
+  if (rows == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(scale);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(row_src);
+  REQUIRE_ALIGNED(q);
+  REQUIRE_ALIGNED(scale);
+  return launch_quant_rows(x, x_dt, x_rows, H, row_src, row_div, rows, q, scale, (hipStream_t)stream);
 }
 
 moe_status moe_sum_slots(const void* z, moe_dtype dt, int T, int K, int N, void* out, void* stream) {

@@ -92,16 +92,18 @@ moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
                           void* x_perm, void* ws, hipStream_t s);
 // Row maps of a grouped GEMM. Input: grouped row r reads row src[r] / div of
-// an input with `rows` rows (src == nullptr: row r itself). Output: grouped
-// row r is stored as row dst[r] of out, multiplied by gate[dst[r]] when gate
-// is set (dst == nullptr: row r, no gate); destinations outside [0, A) are
-// not stored.
+// an input with `rows` rows (src == nullptr: row r itself); row_scale, when
+// set (E4M3 inputs), is a per-row activation scale indexed like the rows of
+// the input. Output: grouped row r is stored as row dst[r] of out, multiplied
+// by gate[dst[r]] when gate is set (dst == nullptr: row r, no gate);
+// destinations outside [0, A) are not stored.
 struct RowMap {
   const int32_t* src = nullptr;
   int div = 1;
   int rows = 0;
   const int32_t* dst = nullptr;
   const float* gate = nullptr;
+  const float* row_scale = nullptr;
 };
 size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N);
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
@@ -113,6 +115,9 @@ moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void
                          const unsigned char* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                          moe_act act, void* out, hipStream_t s);
 // sum_slots: y[t] = sum_k y_perm[t*K+k] (perm_dst and gate ignored).
+// Per-token E4M3 quantisation of the rows src[r] / div (or r) of x.
+moe_status launch_quant_rows(const void* x, moe_dtype dt, int x_rows, int H, const int32_t* src, int div,
+                             int rows, uint8_t* q, float* scale, hipStream_t s);
 moe_status launch_combine(const void* y_perm, moe_dtype dt, const int32_t* perm_dst,
                           const float* gate, int T, int K, int N, void* out, hipStream_t s,
                           bool sum_slots = false);

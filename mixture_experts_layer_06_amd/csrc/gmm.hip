@@ -162,6 +162,15 @@ __device__ __forceinline__ OutRow out_row(const RowMap& rm, int64_t m, int A) {
   return out_row_of(rm, m, rm.dst != nullptr ? rm.dst[m] : 0, A);
 }
 
+// Per-row activation scale of grouped row m (1 without one); a gathered row
+// whose index is out of range reads as a zero row, scale 0.
+__device__ __forceinline__ float row_scale_of(const RowMap& rm, int m) {
+  if (rm.row_scale == nullptr) return 1.f;
+  if (rm.src == nullptr) return rm.row_scale[m];
+  const int t = gather_src(rm, m);
+  return t >= 0 ? rm.row_scale[t] : 0.f;
+}
+
 // Logical tile for this block, or false if the block has no work.
 // XCD-aware: block p runs on XCD p % 8; XCD x takes logical tiles
 // [x*per, (x+1)*per). Inside an expert, tiles go in groups of GM row tiles:
@@ -586,13 +595,14 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
     const OutRow orow = out_row(gx, tile.row0 + ml, A);
     if (orow.row < 0) continue;
     const int64_t m = orow.row;
+    const float rsc = gx.row_scale != nullptr ? row_scale_of(gx, tile.row0 + ml) * sc : sc;
 #pragma unroll
     for (int j = 0; j < C::kFJ; ++j) {
       const int n = tile.n0 + wn * C::kWN + j * 16 + 4 * kq;
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = acc[i][j][r] * sc;
+        v[r] = acc[i][j][r] * rsc;
         if (relu) v[r] = v[r] > 0.f ? v[r] : 0.f;
         v[r] *= orow.gate;
       }
@@ -1234,6 +1244,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
       dpre[i] = ml < tile.rows ? gx.dst[tile.row0 + ml] : -1;
     }
   }
+  // per-row activation scales (per-token quantised input), fetched now too
+  float rpre[4] = {1.f, 1.f, 1.f, 1.f};
+  if (gx.row_scale != nullptr && wave_active) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
+      rpre[i] = ml < tile.rows ? row_scale_of(gx, tile.row0 + ml) : 0.f;
+    }
+  }
   // activation fragment i: chunks kq (register bytes 0-15) and 4 + kq (16-31)
   int xoff[4][2];
 #pragma unroll
@@ -1361,6 +1380,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const OutRow orow = out_row_of(gx, tile.row0 + ml, dpre[i], A);
     if (orow.row < 0) continue;
     const int64_t m = orow.row;
+    const float rsc = gx.row_scale != nullptr ? rpre[i] * sc : sc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // MFMA j, output row 4*kq + r  ->  column nb + r
@@ -1369,7 +1389,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float t = acc[i][j][r] * sc;
+        const float t = acc[i][j][r] * rsc;
         v[r] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
       }
       *reinterpret_cast<uint2*>(out + m * N + nb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));

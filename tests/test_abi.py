@@ -23,7 +23,7 @@ def declared_entry_points():
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
     for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx",
-              "moe_combine", "moe_sum_slots", "moe_layer",
+              "moe_combine", "moe_sum_slots", "moe_quant_rows", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size",
               "moe_status_string", "moe_version"):
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10500
+    assert moe.lib().moe_version() == 10600
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -304,6 +304,45 @@ def test_gmm_scatter_validation(kw, status):
 
 def test_gmm_scatter_zero_rows_is_noop():
     assert gmm_scatter(a=None, w=None, off=None, dst=None, gate=None, out=None, A=0) == moe.OK
+
+
+def quant_rows(x=P, dt=moe.BF16, x_rows=10, H=64, src=None, div=1, rows=10, q=P, sc=P):
+    return L.moe_quant_rows(x, dt, x_rows, H, src, div, rows, q, sc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=moe.FP8_E4M3), moe.ERR_BAD_DTYPE),
+    (dict(dt=7), moe.ERR_BAD_DTYPE),
+    (dict(H=0), moe.ERR_BAD_SHAPE),
+    (dict(H=65536), moe.ERR_BAD_SHAPE),
+    (dict(rows=-1), moe.ERR_BAD_SHAPE),
+    (dict(x_rows=-1), moe.ERR_BAD_SHAPE),
+    (dict(rows=11), moe.ERR_BAD_SHAPE),               # more rows than x without an index
+    (dict(src=P, div=0), moe.ERR_BAD_SHAPE),
+    (dict(x=None), moe.ERR_NULL_POINTER),
+    (dict(q=None), moe.ERR_NULL_POINTER),
+    (dict(sc=None), moe.ERR_NULL_POINTER),
+    (dict(x=MIS), moe.ERR_MISALIGNED),
+    (dict(src=MIS, rows=40), moe.ERR_MISALIGNED),
+    (dict(sc=MIS), moe.ERR_MISALIGNED),
+])
+def test_quant_rows_validation(kw, status):
+    assert quant_rows(**kw) == status
+
+
+def test_quant_rows_no_rows_is_noop():
+    assert quant_rows(x=None, q=None, sc=None, rows=0, x_rows=0) == moe.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(aq=3), moe.ERR_UNSUPPORTED),                                    # per-token needs E4M3
+    (dict(adt=moe.FP8_E4M3, wdt=moe.FP8_E4M3, aq=3, wq=0), moe.ERR_UNSUPPORTED),
+    (dict(adt=moe.FP8_E4M3, wdt=moe.FP8_E4M3, aq=7, wq=1, asc=P, wsc=P), moe.ERR_UNSUPPORTED),
+    (dict(adt=moe.FP8_E4M3, wdt=moe.FP8_E4M3, aq=3, wq=1, asc=None, wsc=P), moe.ERR_NULL_POINTER),
+    (dict(adt=moe.FP8_E4M3, wdt=moe.FP8_E4M3, aq=3, wq=1, asc=MIS, wsc=P), moe.ERR_MISALIGNED),
+])
+def test_gmm_per_token_validation(kw, status):
+    assert gmm_scatter(**kw) == status
 
 
 def sum_slots(z=P, dt=moe.BF16, T=10, K=2, N=64, out=P):

@@ -421,6 +421,105 @@ def test_gmm_scatter_moves_rows_and_applies_gates(case):
     assert normwise_err(s2[dst[valid]], ref[valid]) <= {"f32": 2e-6, "bf16": 8e-3, "fp8": 8e-3}[dt]
 
 
+# ---------------------------------------------------------------- per-token E4M3
+
+def _rows_with_spread(seed, shape, dt):
+    """N(0,1) rows with per-row magnitudes 2^-6 .. 2^6, one all-zero row and one
+    row holding a single nonzero value."""
+    x = synth.normal(seed, shape).astype(np.float32)
+    x *= np.exp2(np.arange(shape[0]) % 13 - 6).astype(np.float32)[:, None]
+    x[min(3, shape[0] - 1)] = 0.0
+    if shape[0] > 5:
+        x[5] = 0.0
+        x[5, shape[1] // 2] = -2.5
+    return synth.to_bf16(x) if dt == "bf16" else x
+
+
+@pytest.mark.parametrize("dt,T,H", [("bf16", 300, 7168), ("bf16", 70, 36), ("f32", 129, 100),
+                                    ("f32", 64, 2048), ("bf16", 5, 8)])
+def test_quant_rows_bit_exact(dt, T, H):
+    """Codes and scales equal the oracle's bit for bit (same binary32 steps)."""
+    x = _rows_with_spread(800 + H, (T, H), dt)
+    q, sc = moe.quant_rows(to_dev(x))
+    rq, rs = oracle.quant_rows(x)
+    assert np.array_equal(to_host(q), rq)
+    assert np.array_equal(to_host(sc).view(np.uint32), rs.view(np.uint32))
+
+
+def test_quant_rows_gather_is_the_permute():
+    """Gathering through perm_src / K quantises the dispatched rows: equal to
+    quantising the permuted copy; entries out of range give zero rows."""
+    T, E, K, H = 500, 16, 4, 1024
+    idx = synth.random_routing(810, T, E, K)
+    _, off, psrc, pdst = oracle.permute(idx, E)
+    psrc = psrc.copy()
+    psrc[7] = -1
+    psrc[11] = T * K + 2
+    x = _rows_with_spread(811, (T, H), "bf16")
+    q, sc = moe.quant_rows(to_dev(x), rows=to_dev(psrc), row_div=K)
+    rq, rs = oracle.quant_rows(x, rows=psrc, div=K)
+    assert np.array_equal(to_host(q), rq)
+    assert np.array_equal(to_host(sc), rs)
+    assert not rq[7].any() and not rq[11].any() and rs[7] == 0 and rs[11] == 0
+
+
+PER_TOKEN_CASES = [
+    # (name, counts, Hin, N): the E4M3 ping-pong kernel and the tiled kernel
+    ("pt_pp8", [200, 0, 333, 129], 512, 384),
+    ("pt_tiled_unaligned", [100, 77, 0, 3], 200, 100),
+]
+
+
+@pytest.mark.parametrize("case", PER_TOKEN_CASES, ids=[c[0] for c in PER_TOKEN_CASES])
+def test_gmm_per_token_scales(case):
+    """gmmY = (gmmX @ W) * gmmXScale[row] * wScale with dynamically quantised
+    rows: parity with the oracle; the gathering form (tokens quantised once,
+    rows and scales read through perm_src / K) equals the direct form on the
+    permuted rows bit for bit."""
+    name, counts, Hin, N = case
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    K = 2
+    T = A // K + 5
+    rng = np.random.default_rng(820 + A)
+    psrc = rng.permutation(T * K)[:A].astype(np.int32)
+    x = _rows_with_spread(821, (T, Hin), "bf16")
+    w, sw = synth.quantize_e4m3(synth.normal(822, (e, Hin, N), math.sqrt(1.0 / Hin)))
+    swd = torch.tensor([sw], dtype=torch.float32, device="cuda")
+    qt, st = oracle.quant_rows(x)                      # tokens
+    qp, sp = oracle.quant_rows(x, rows=psrc, div=K)    # dispatched rows
+    wd, od = to_dev(w), to_dev(off)
+    for act in (moe.ACT_NONE, moe.ACT_RELU):
+        direct = to_host(moe.gmm(to_dev(qp), wd, od, act=act, a_scale=to_dev(sp), w_scale=swd, per_token=True))
+        gath = to_host(moe.gmm(to_dev(qt), wd, od, act=act, a_scale=to_dev(st), w_scale=swd, per_token=True,
+                               rows=to_dev(psrc), row_div=K))
+        assert np.array_equal(direct, gath), name
+    ref = oracle.gmm(qp, w, off, act=moe.ACT_RELU, a_scale=sp.astype(np.float64), w_scale=float(sw), nthreads=8)
+    assert normwise_err(direct, ref) <= 8e-3
+    # and against the unquantised product: the quantisation error stays within the fp8 bar
+    xf = synth.bf16_to_f32(x)[psrc // K]
+    wf = oracle.decode(w) * sw
+    exact = np.maximum(np.concatenate([xf[off[i]:off[i + 1]].astype(np.float64) @ wf[i] for i in range(e)]), 0)
+    assert normwise_err(direct, exact) <= TOL["fp8"]
+
+
+def test_gmm_per_token_integer_inputs_bit_exact():
+    """Integer E4M3 codes with power-of-two row scales: exact fp32 sums, so the
+    bf16 outputs equal the oracle's rounding bit for bit."""
+    counts = [200, 0, 333, 129]
+    off = _offsets(counts)
+    A, Hin, N, e = int(off[-1]), 256, 256, len(counts)
+    a = synth.to_e4m3(synth.ints(830, (A, Hin), -4, 4), 1.0)
+    w = synth.to_e4m3(synth.ints(831, (e, Hin, N), -4, 4), 1.0)
+    rs = np.exp2(np.random.default_rng(832).integers(-3, 4, A)).astype(np.float32)
+    out = to_host(moe.gmm(to_dev(a), to_dev(w), to_dev(off), act=moe.ACT_RELU, a_scale=to_dev(rs), per_token=True,
+                          w_scale=torch.tensor([0.5], dtype=torch.float32, device="cuda")))
+    ref = oracle.gmm(a, w, off, act=moe.ACT_RELU, a_scale=rs.astype(np.float64), w_scale=0.5, nthreads=8)
+    assert np.abs(ref).max() < 2 ** 24
+    assert np.array_equal(out, oracle.bf16_bits(ref))
+
+
 MX_CASES = [
     # (name, counts, Hin, N): E4M3 with E8M0 block scales
     ("mx_ragged", [300, 0, 1, 555], 256, 400),
