@@ -9,11 +9,11 @@ stage through the separate entry points, with HIP events between them, gives
 per-kernel durations; the dominant kernel (moe_gmm) is reported against its
 roofline. The fp8 workloads time the page-2 step instead: E4M3 grouped GEMM
 (per-tensor or MX block scales) + Unpermute, with the shared bf16 expert on
-a second stream.
+a second stream (fp8dyn: gmmX quantised per row on the device first).
 
 Prints ONE JSON line. Default workload: prefill (T=4096, H=4096, E=8, K=2,
 F=14336, bf16). Other workloads: --workload skewed|decode16|decode64|
-decode256|fp8gmm|fp8mx|tiny.
+decode256|fp8gmm|fp8mx|fp8dyn|tiny.
 """
 from __future__ import annotations
 
@@ -51,7 +51,7 @@ def parse():
                     help="untimed warm-up steps (default: as many as fill 0.4 s, so the GPU's "
                          "clocks have left their idle state; the count is reported)")
     ap.add_argument("--workload", default="prefill",
-                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx"])
+                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx", "fp8dyn"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -342,18 +342,21 @@ def bench_layer(args, dev):
     return res, host
 
 
-def bench_fp8(args, dev, use_mx=False):
-    """Page-2 form: fp8 grouped GEMM (per-tensor scales, or mx: E8M0 block
-    scales) + Unpermute, with the bf16 shared-expert GEMM on a second stream,
-    joined by events."""
+def bench_fp8(args, dev, mode="pt"):
+    """Page-2 form: fp8 grouped GEMM + Unpermute, with the bf16 shared-expert
+    GEMM on a second stream, joined by events. mode "pt": per-tensor scales,
+    the Unpermute fused into the GEMM's stores; "mx": E8M0 block scales, then
+    the Unpermute kernel; "dyn": gmmX arrives in bf16 and is quantised per row
+    on the device (per-token dynamic), then the per-token-scaled GEMM with the
+    fused Unpermute."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_06_amd as moe
-    import oracle
     from synth import configs
 
-    d = configs.fp8_mx_inputs() if use_mx else configs.fp8_inputs()
+    use_mx, dyn = mode == "mx", mode == "dyn"
+    d = (configs.fp8_mx_inputs() if use_mx else configs.fp8_dyn_inputs() if dyn else configs.fp8_inputs())
     T, e, K, A, H1, N1, H2, N2 = (d[k] for k in ("T", "e", "K", "A", "H1", "N1", "H2", "N2"))
     # dispatch layout of the routed rows: computed once on the device by moe_permute
     idx = host_to_dev(d["topk_idx"], dev)
@@ -363,11 +366,16 @@ def bench_fp8(args, dev, use_mx=False):
     if use_mx:
         sx = host_to_dev(d["gmm_x_scale"], dev)
         sw = host_to_dev(d["gmm_w_scale"], dev)
+    elif dyn:
+        qx = torch.empty((A, H1), dtype=torch.float8_e4m3fn, device=dev)
+        sx = torch.empty((A,), dtype=torch.float32, device=dev)
+        sw = torch.tensor([float(d["gmm_w_scale"])], dtype=torch.float32, device=dev)
     else:
         sx = torch.tensor([float(d["gmm_x_scale"])], dtype=torch.float32, device=dev)
         sw = torch.tensor([float(d["gmm_w_scale"])], dtype=torch.float32, device=dev)
     mx = host_to_dev(d["mm_x"], dev)
     mw = host_to_dev(d["mm_w"], dev).view(1, H2, N2)
+    del d
     moff = torch.tensor([0, T], dtype=torch.int32, device=dev)
     gy = torch.empty((A, N1), dtype=torch.bfloat16, device=dev)
     un = torch.empty((A, N1), dtype=torch.bfloat16, device=dev)
@@ -378,6 +386,8 @@ def bench_fp8(args, dev, use_mx=False):
     gws_n = moe.gmm_workspace_size(moe.FP8_E4M3, e, A, H1, N1)
     gws = torch.empty((max(gws_n, 16),), dtype=torch.uint8, device=dev)
 
+    # events: 0 start, 5 after the quantisation (dyn), 1 after the GEMM, 2 after
+    # the Unpermute (mx), 3/4 around the shared expert on the side stream
     def step(ev=None):
         main = torch.cuda.current_stream()
         fork = torch.cuda.Event()
@@ -392,13 +402,22 @@ def bench_fp8(args, dev, use_mx=False):
             if ev is not None:
                 ev[4].record(side)
         if use_mx:
+            if ev is not None:
+                ev[5].record(main)
             moe.gmm_mx(gx, sx, gw, sw, perm["offsets"], out=gy)
             if ev is not None:
                 ev[1].record(main)
             moe.combine(gy, perm["perm_dst"], None, T, K, out=un)
         else:
+            a, asc = gx, sx
+            if dyn:
+                moe.quant_rows(gx, q=qx, scale=sx)
+                a = qx
+            if ev is not None:
+                ev[5].record(main)
             # Unpermute fused into the GEMM's stores: grouped row r lands in row perm_src[r]
-            moe.gmm(gx, gw, perm["offsets"], a_scale=sx, w_scale=sw, out=un, ws=gws, dst=perm["perm_src"])
+            moe.gmm(a, gw, perm["offsets"], a_scale=asc, w_scale=sw, out=un, ws=gws, dst=perm["perm_src"],
+                    per_token=dyn)
             if ev is not None:
                 ev[1].record(main)
         if ev is not None:
@@ -408,42 +427,52 @@ def bench_fp8(args, dev, use_mx=False):
         main.wait_event(join)
 
     warmup = warm_up(step, args.warmup)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    gmm_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][1]) for s in range(args.steps)]))
-    un_ms = float(np.mean([evs[s][1].elapsed_time(evs[s][2]) for s in range(args.steps)]))
-    sh_ms = float(np.mean([evs[s][3].elapsed_time(evs[s][4]) for s in range(args.steps)]))
+
+    def span(i, j):
+        return float(np.mean([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)]))
+
+    q_ms, gmm_ms, un_ms, sh_ms = span(0, 5), span(5, 1), span(1, 2), span(3, 4)
     counts = perm["counts"].cpu().numpy().tolist()
     fl, by = flops_bytes_gmm(counts, H1, N1, 1)
     if use_mx:  # E8M0 scales: one byte per 32 activation and weight elements
         by += A * (H1 // 32) + sum(1 for c in counts if c > 0) * (H1 // 32) * N1
+    if dyn:  # one fp32 scale per activation row
+        by += A * 4
     achieved = fl / (gmm_ms * 1e-3) / 1e12
-    wl = "fp8mx" if use_mx else "fp8gmm"
+    wl = {"pt": "fp8gmm", "mx": "fp8mx", "dyn": "fp8dyn"}[mode]
+    data = {"pt": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
+            "mx": "synthetic (seeded; E4M3 with MX E8M0 scales per 32 elements, OCP recipe; "
+                  "random top-8 of 32 routing)",
+            "dyn": "synthetic (seeded; bf16 gmmX quantised per row on the device, E4M3 weights with a "
+                   "per-tensor scale; random top-8 of 32 routing)"}[mode]
+    kernel = {"pt": "moe_gmm_scatter E4M3 (gmm_pp8_kernel, Unpermute fused into its stores)",
+              "mx": "moe_gmm_mx E4M3 + E8M0 (gmm_pp8_kernel<true>)",
+              "dyn": "moe_gmm_scatter E4M3, per-token scales (gmm_pp8_kernel, Unpermute fused)"}[mode]
+    kernels = {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
+               "unpermute": ({"ms": un_ms, "GB/s": 2 * A * N1 * 2 / (un_ms * 1e-3) / 1e9} if use_mx
+                             else "fused into the grouped GEMM's stores"),
+               "shared_gemm_bf16": {"ms": sh_ms, "TFLOP/s": 2.0 * T * H2 * N2 / (sh_ms * 1e-3) / 1e12}}
+    if dyn:  # bf16 rows read once, codes and scales written
+        kernels["quant_rows"] = {"ms": q_ms, "GB/s": (A * H1 * 3 + A * 4) / (q_ms * 1e-3) / 1e9}
     res = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
-        "data": ("synthetic (seeded; E4M3 with MX E8M0 scales per 32 elements, OCP recipe; "
-                 "random top-8 of 32 routing)" if use_mx else
-                 "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)"),
+        "data": data,
         "config": {"workload": f"{wl}: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
                                f"({T},{H2})x({H2},{N2}) bf16", "tokens_per_step": T},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
-                     "traffic": measured_traffic(wl),
-                     "kernel": ("moe_gmm_mx E4M3 + E8M0 (gmm_pp8_kernel<true>)" if use_mx
-                                else "moe_gmm_scatter E4M3 (gmm_pp8_kernel, Unpermute fused into its stores)"), "gmm_source": source_digest(),
-                     "flops_per_launch": fl,
-                     "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
-        "kernels": {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
-                    "unpermute": ({"ms": un_ms, "GB/s": 2 * A * N1 * 2 / (un_ms * 1e-3) / 1e9} if use_mx
-                                  else "fused into the grouped GEMM's stores"),
-                    "shared_gemm_bf16": {"ms": sh_ms, "TFLOP/s": 2.0 * T * H2 * N2 / (sh_ms * 1e-3) / 1e12}},
+                     "traffic": measured_traffic(wl), "kernel": kernel, "gmm_source": source_digest(),
+                     "flops_per_launch": fl, "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
+        "kernels": kernels,
     }
     return res, None
 
@@ -487,8 +516,8 @@ def main():
     moe.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload in ("fp8gmm", "fp8mx"):
-        res, host = bench_fp8(args, dev, use_mx=args.workload == "fp8mx")
+    if args.workload in ("fp8gmm", "fp8mx", "fp8dyn"):
+        res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8mx": "mx", "fp8dyn": "dyn"}[args.workload])
         res["achievable"] = achievable(dev)
     else:
         res, host = bench_layer(args, dev)

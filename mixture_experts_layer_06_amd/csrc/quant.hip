@@ -3,40 +3,30 @@
 // 量化模式 enumeration; its formula multiplies gmmX's scale back onto the
 // product). For every output row r, with source row t = src[r] / div (or r):
 //   scale[r] = max_h |x[t,h]| / 448          (binary32 division)
-//   q[r,h]   = nearest E4M3 value of x[t,h] / scale[r]   (binary32 division,
-//              ties to the even code, saturating at +-448)
+//   q[r,h]   = nearest E4M3 value of x[t,h] * (448 / max_h |x[t,h]|)
+//              (binary32: one division per row, then products; ties to the
+//              even code, saturating at +-448)
 // An all-zero row, or a source row outside [0, x_rows), gives codes 0 and
 // scale 0. With src = perm_src of the dispatch and div = K this is the
 // permute and the quantisation in one pass (x_perm in E4M3 plus its
 // per-row scales, the form gmmX and gmmXScale take on that page).
 //
-// HBM-bound: one wave per output row reads the row twice (the second pass
-// hits L2), writes one byte per element and one scale.
+// HBM-bound: one wave per output row reads the row once (rows up to 7168
+// bf16 or 4096 fp32 values stay in registers; longer ones are read again from
+// L2), writes one byte per element and one scale.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-// Code of the finite E4M3 value nearest to v, ties to the even code; |v| at
-// or above 448 saturates, NaN gives 0x7f. Built from the format: subnormal
-// steps of 2^-9 below 2^-6, else 3 mantissa bits per binade (exponent bias 7).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const float a = __uint_as_float(b & 0x7fffffffu);
-  if (!(a == a)) return 0x7fu;
-  if (a >= 448.f) return sign | 0x7eu;
-  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
-    const float m = rintf(a * 512.f);        // exact scaling; rint ties to even
-    return sign | (uint32_t)m;               // m == 8 is 2^-6, code 0x08
-  }
-  int e = (int)((b >> 23) & 0xffu) - 127;    // -6 .. 8
-  uint32_t m = (uint32_t)rintf(__builtin_ldexpf(a, 3 - e));  // 8 .. 16
-  if (m == 16u) {
-    m = 8u;
-    ++e;
-  }
-  return sign | ((uint32_t)(e + 7) << 3) | (m - 8u);  // a < 448 keeps it at or below 0x7e
+// E4M3 codes of two binary32 values, written into byte pair HI of `old`:
+// gfx950's conversion rounds to the nearest E4M3 value, ties to the even
+// code (OCP E4M3, as the MFMAs read it). Inputs here are at most 448 in
+// magnitude up to one rounding of x * (448 / amax), so they never overflow;
+// non-finite inputs give unspecified codes.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -70,24 +60,65 @@ __device__ __forceinline__ void load8(const void* x, int64_t i, float v[8]) {
   }
 }
 
-// VEC: H % 8 == 0 and 16-byte aligned rows (8 elements per access).
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int x_rows, int H,
-                                                         const int32_t* __restrict__ src, int div, int rows,
-                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+// Codes of 8 values, packed little-endian into two words.
+__device__ __forceinline__ uint2 e4m3_pack8(const float v[8], float inv) {
+  uint32_t lo = e4m3_pair<false>(v[0] * inv, v[1] * inv, 0u);
+  lo = e4m3_pair<true>(v[2] * inv, v[3] * inv, lo);
+  uint32_t hi = e4m3_pair<false>(v[4] * inv, v[5] * inv, 0u);
+  hi = e4m3_pair<true>(v[6] * inv, v[7] * inv, hi);
+  return make_uint2(lo, hi);
+}
+
+// Source row of output row r, or -1 (zero row).
+__device__ __forceinline__ int quant_src_row(const int32_t* src, int div, int x_rows, int r) {
   int t = r;
   if (src != nullptr) {
     const int v = src[r];
     t = v >= 0 ? v / div : -1;
   }
+  return t < x_rows ? t : -1;
+}
+
+// One wave per output row. VEC (H % 8 == 0, rows 16-byte aligned): 8
+// elements per access; rows of at most kCh * 512 elements are held in
+// registers (one HBM read, all loads in flight at once), longer rows are
+// read twice (the second pass from L2). Otherwise one element per access.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int x_rows, int H,
+                                                         const int32_t* __restrict__ src, int div, int rows,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
+  constexpr int kCh = BF16 ? 14 : 8;  // register-held chunks of 8 elements per lane
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int t = quant_src_row(src, div, x_rows, r);
   uint8_t* qr = q + (int64_t)r * H;
-  const bool valid = t >= 0 && t < x_rows;
-  const int64_t base = (int64_t)(valid ? t : 0) * H;
+  const int64_t base = (int64_t)(t >= 0 ? t : 0) * H;
+  if (VEC && H <= kCh * 512) {
+    float v[kCh][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      const int h = (c * 64 + lane) * 8;
+      if (t >= 0 && h < H) {
+        load8<BF16>(x, base + h, v[c]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[c][k]));
+      }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) scale[r] = amax / 448.f;
+    const float inv = 448.f / amax;
+    const bool zero = !(amax > 0.f);
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      const int h = (c * 64 + lane) * 8;
+      if (h < H) *reinterpret_cast<uint2*>(qr + h) = zero ? make_uint2(0u, 0u) : e4m3_pack8(v[c], inv);
+    }
+    return;
+  }
   float amax = 0.f;
-  if (valid) {
+  if (t >= 0) {
     if (VEC) {
       for (int h = lane * 8; h < H; h += 64 * 8) {
         float v[8];
@@ -100,26 +131,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     }
     amax = wave_max(amax);
   }
-  const float s = amax / 448.f;
-  if (lane == 0) scale[r] = s;
+  if (lane == 0) scale[r] = amax / 448.f;
+  const float inv = 448.f / amax;
   const bool zero = !(amax > 0.f);
   if (VEC) {
     for (int h = lane * 8; h < H; h += 64 * 8) {
-      uint32_t lo = 0, hi = 0;
+      uint2 o = make_uint2(0u, 0u);
       if (!zero) {
         float v[8];
         load8<BF16>(x, base + h, v);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          lo |= e4m3_code(v[k] / s) << (8 * k);
-          hi |= e4m3_code(v[k + 4] / s) << (8 * k);
-        }
+        o = e4m3_pack8(v, inv);
       }
-      *reinterpret_cast<uint2*>(qr + h) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(qr + h) = o;
     }
   } else {
     for (int h = lane; h < H; h += 64)
-      qr[h] = zero ? 0 : (uint8_t)e4m3_code(load_elem<BF16>(x, base + h) / s);
+      qr[h] = zero ? 0 : (uint8_t)(e4m3_pair<false>(load_elem<BF16>(x, base + h) * inv, 0.f, 0u) & 0xffu);
   }
 }
 

@@ -213,7 +213,8 @@ def e4m3_nearest(v) -> np.ndarray:
 def quant_rows(x, rows=None, div=1):
     """Per-token dynamic E4M3 quantisation (binary32 arithmetic): for each
     output row, the source row t = rows[r] // div (or r), scale = max|x[t]| / 448,
-    codes = nearest E4M3 of x[t] / scale. Returns (codes (R,H) uint8, scales (R,) float32)."""
+    codes = nearest E4M3 of x[t] * (448 / max|x[t]|). Returns (codes (R,H)
+    uint8, scales (R,) float32)."""
     x, px = _c(x)
     n, H = x.shape
     if rows is None:

@@ -360,15 +360,15 @@ int orc_quant_rows(const void* x, int x_dt, int x_rows, int H, const int32_t* sr
       float xv = (float)orc_decode(x, x_dt, t * H + h); /* exact: bf16 and f32 are binary32 values */
       if (fabsf(xv) > amax) amax = fabsf(xv);
     }
-    const float s = amax / 448.0f;
-    scale[r] = s;
+    scale[r] = amax / 448.0f;
+    const float inv = 448.0f / amax; /* the inverse scale, one division per row */
     for (int h = 0; h < H; ++h) {
       if (amax == 0.0f) {
         qr[h] = 0;
         continue;
       }
       float xv = (float)orc_decode(x, x_dt, t * H + h);
-      qr[h] = orc_e4m3_nearest(xv / s);
+      qr[h] = orc_e4m3_nearest(xv * inv);
     }
   }
   return 0;

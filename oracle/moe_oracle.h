@@ -113,7 +113,9 @@ int orc_gmm_mx(const void* a, int a_dt, const uint8_t* a_scale, const void* w, i
  * the even code (mantissa bit 0 clear); |v| above 448 gives +-448, NaN 0x7f.
  * orc_quant_rows: row r of q is source row t = src ? src[r] / div : r of x
  * (x_rows rows, H values each, in x_dt); in binary32 arithmetic: amax = the
- * largest |x[t,h]|, scale[r] = amax / 448, q[r,h] = nearest(x[t,h] / scale[r]);
+ * largest |x[t,h]|, scale[r] = amax / 448, q[r,h] = nearest(x[t,h] * inv) with
+ * the inverse scale inv = 448 / amax (the pages name the mode but give no
+ * formula; one division per row, then products, is the reading taken);
  * amax == 0 or a source row outside [0, x_rows): all codes 0, scale 0. */
 uint8_t orc_e4m3_nearest(float v);
 int orc_e4m3_nearest_array(const float* v, int64_t n, uint8_t* out);

@@ -186,6 +186,29 @@ def test_fp8_mx_gmm_full_size_sampled_rows():
     assert normwise_err(to_host(gy)[rows], ref) <= 8e-3
 
 
+def test_fp8_dynamic_per_token_full_size_sampled_rows():
+    """The fp8 workload with gmmX in bf16, quantised per row on the device
+    (65536 x 7168), then the per-token-scaled GEMM with the Unpermute fused
+    into its stores, as the benchmark runs it: codes and scales of sampled rows
+    bit-exact, outputs of sampled rows against the oracle."""
+    d = configs.fp8_dyn_inputs(with_shared=False)
+    e, A = d["e"], d["A"]
+    counts, offsets, psrc, _ = oracle.permute(d["topk_idx"], e)
+    perm = moe.permute(to_dev(d["topk_idx"]), e)
+    q, sc = moe.quant_rows(to_dev(d["gmm_x"]))
+    sw = float(d["gmm_w_scale"])
+    un = moe.gmm(q, to_dev(d["gmm_w"]), perm["offsets"], a_scale=sc, per_token=True,
+                 w_scale=torch.tensor([sw], dtype=torch.float32, device="cuda"), dst=perm["perm_src"])
+    torch.cuda.synchronize()
+    rows = _boundary_rows(offsets, 24, 650)
+    rq, rs = oracle.quant_rows(d["gmm_x"][rows])
+    q_h, sc_h = to_host(q), to_host(sc)
+    assert np.array_equal(q_h[rows], rq) and np.array_equal(sc_h[rows], rs)
+    ref = oracle.gmm(q_h, d["gmm_w"], offsets, a_scale=sc_h.astype(np.float64), w_scale=sw, rows=rows,
+                     nthreads=NTH)
+    assert normwise_err(to_host(un)[psrc[rows]], ref) <= 8e-3
+
+
 def test_combine_full_size_prefill():
     T, E, K, H = 4096, 8, 2, 4096
     idx = synth.random_routing(630, T, E, K)

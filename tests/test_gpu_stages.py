@@ -436,7 +436,8 @@ def _rows_with_spread(seed, shape, dt):
 
 
 @pytest.mark.parametrize("dt,T,H", [("bf16", 300, 7168), ("bf16", 70, 36), ("f32", 129, 100),
-                                    ("f32", 64, 2048), ("bf16", 5, 8)])
+                                    ("f32", 64, 2048), ("bf16", 5, 8),
+                                    ("bf16", 33, 8200), ("f32", 20, 4104)])  # rows read twice
 def test_quant_rows_bit_exact(dt, T, H):
     """Codes and scales equal the oracle's bit for bit (same binary32 steps)."""
     x = _rows_with_spread(800 + H, (T, H), dt)
@@ -444,6 +445,39 @@ def test_quant_rows_bit_exact(dt, T, H):
     rq, rs = oracle.quant_rows(x)
     assert np.array_equal(to_host(q), rq)
     assert np.array_equal(to_host(sc).view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("dt,pad", [("f32", 0), ("f32", 3), ("bf16", 0), ("bf16", 5)])
+def test_quant_rows_ties_and_grid_points(dt, pad):
+    """Rows whose largest value is 448 (so the inverse scale is exactly 1):
+    every E4M3 value, every midpoint between neighbours (ties to the even
+    code), the binary32 neighbours of each midpoint, and the subnormal range;
+    vector (pad 0) and element-wise (H not a multiple of 8) paths."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode(codes)
+    pos = np.unique(vals[~np.isnan(vals) & (vals >= 0)])
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    near = [mids, pos.astype(np.float32)]
+    if dt == "f32":
+        near += [np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0))]
+    row = np.concatenate([np.array([448.0], np.float32)] + near)
+    row = np.concatenate([row, -row[1:]])
+    H = ((row.size + 7) // 8) * 8 + pad
+    x = np.zeros((4, H), np.float32)
+    x[0, :row.size] = row
+    x[1, :row.size] = row[::-1]
+    x[2] = np.resize(row, H)
+    x[3, 0] = -448.0
+    x[3, 1:row.size] = row[1:] / np.float32(2.0)
+    if dt == "bf16":
+        xb = synth.to_bf16(x)
+        assert np.array_equal(synth.bf16_to_f32(xb), x)  # the grid points are bf16 values
+        x = xb
+    q, sc = moe.quant_rows(to_dev(x))
+    rq, rs = oracle.quant_rows(x)
+    assert np.all(rs == np.float32(1.0))
+    assert np.array_equal(to_host(q), rq)
+    assert np.array_equal(to_host(sc), rs)
 
 
 def test_quant_rows_gather_is_the_permute():
