@@ -63,6 +63,9 @@ def lib():
         L.orc_e4m3_nearest.restype = ctypes.c_uint8
         L.orc_e4m3_nearest_array.argtypes = [vp, i64, vp]
         L.orc_quant_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp]
+        L.orc_gmm_mx4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32]
+        L.orc_e2m1.argtypes = [i32]
+        L.orc_e2m1.restype = dbl
         L.orc_e8m0.argtypes = [i32]
         L.orc_e8m0.restype = dbl
         L.orc_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp]
@@ -73,7 +76,7 @@ def lib():
                                        vp, vp, vp, vp, i32]
         L.orc_layer_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         for name in ("orc_decode_array", "orc_route", "orc_permute", "orc_gather_rows", "orc_gmm", "orc_gmm_mx",
-                     "orc_gmm_row_scaled", "orc_e4m3_nearest_array", "orc_quant_rows",
+                     "orc_gmm_row_scaled", "orc_e4m3_nearest_array", "orc_quant_rows", "orc_gmm_mx4",
                      "orc_combine", "orc_expert_ffn", "orc_layer", "orc_layer_tokens",
                      "orc_layer_dense"):
             getattr(L, name).restype = i32
@@ -255,6 +258,37 @@ def gmm_mx(a, a_scale, w, w_scale, offsets, act=ACT_NONE, rows=None, nthreads=1)
         prow, nrows = _p(rows), rows.size
     _check(lib().orc_gmm_mx(pa, _code(a), psa, pw, _code(w), psw, poff, e, Hin, N, act, prow, nrows, _p(out),
                             int(nthreads)), "gmm_mx")
+    return out
+
+
+def e2m1(code: int) -> float:
+    """Value of one E2M1 (OCP FP4) code 0..15."""
+    return lib().orc_e2m1(int(code))
+
+
+def gmm_mx4(a, a_scale, w, w_scale, offsets, act=ACT_NONE, rows=None, nthreads=1):
+    """Grouped GEMM on MX operands with E2M1 elements: a (A, Hin/2) and w
+    (e, Hin/2, N) packed bytes (two elements per byte along Hin, the even one
+    in the low nibble), a_scale (A, Hin/32) and w_scale (e, Hin/32, N) E8M0
+    bytes. fp64 result."""
+    a, pa = _c(np.asarray(a, np.uint8))
+    w, pw = _c(np.asarray(w, np.uint8))
+    sa, psa = _c(np.asarray(a_scale, np.uint8))
+    sw, psw = _c(np.asarray(w_scale, np.uint8))
+    off, poff = _c(np.asarray(offsets, np.int32))
+    e, Hh, N = w.shape
+    Hin = 2 * Hh
+    if a.shape[1] != Hh or Hin % 32 or sa.shape != (a.shape[0], Hin // 32) or sw.shape != (e, Hin // 32, N):
+        raise ValueError("gmm_mx4: shapes disagree")
+    if rows is None:
+        out = np.empty((int(off[e]), N), np.float64)
+        prow, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, np.int32)
+        out = np.empty((rows.size, N), np.float64)
+        prow, nrows = _p(rows), rows.size
+    _check(lib().orc_gmm_mx4(pa, psa, pw, psw, poff, e, Hin, N, act, prow, nrows, _p(out), int(nthreads)),
+           "gmm_mx4")
     return out
 
 

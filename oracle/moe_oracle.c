@@ -451,6 +451,83 @@ int orc_gmm_mx(const void* a, int a_dt, const uint8_t* a_scale, const void* w, i
   return c.bad ? -1 : 0;
 }
 
+/* MX with E2M1 (OCP FP4) elements: 1 sign, 2 exponent bits (bias 1), 1
+ * mantissa bit; exponent 0 is subnormal (m * 0.5); largest value 6. Two
+ * elements per byte along the reduction index, the even index in the low
+ * nibble: a (A, Hin/2) bytes; w (e, Hin/2, N) bytes, byte (ex, h/2, n)
+ * holding rows h (low nibble, h even) and h+1 of column n. */
+double orc_e2m1(int code) {
+  const int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  const double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+static double dec_e2m1_at(const uint8_t* buf, int64_t byte, int hi) {
+  return orc_e2m1(hi ? (buf[byte] >> 4) : (buf[byte] & 15));
+}
+
+typedef struct {
+  const uint8_t *a, *a_scale, *w, *w_scale;
+  const int32_t* offsets;
+  int e, Hin, N, act;
+  const int32_t* rows;
+  double* out;
+  int bad;
+} orc_gmm_mx4_ctx;
+
+static void orc_gmm_mx4_row(void* p, int64_t j) {
+  orc_gmm_mx4_ctx* c = (orc_gmm_mx4_ctx*)p;
+  int64_t r = c->rows ? c->rows[j] : j;
+  int ex = -1;
+  for (int q = 0; q < c->e; ++q)
+    if (c->offsets[q] <= r && r < c->offsets[q + 1]) {
+      ex = q;
+      break;
+    }
+  double* o = c->out + j * (int64_t)c->N;
+  double* blk = (double*)malloc(sizeof(double) * (size_t)c->N);
+  if (ex < 0 || !blk) {
+    c->bad = 1;
+    for (int n = 0; n < c->N; ++n) o[n] = NAN;
+    free(blk);
+    return;
+  }
+  const int nb = c->Hin / 32, hb = c->Hin / 2;
+  for (int n = 0; n < c->N; ++n) o[n] = 0.0;
+  for (int b = 0; b < nb; ++b) {
+    /* the block's plain dot products, ascending h, then its two scales */
+    for (int n = 0; n < c->N; ++n) blk[n] = 0.0;
+    for (int h = 32 * b; h < 32 * b + 32; ++h) {
+      const double av = dec_e2m1_at(c->a, r * hb + h / 2, h & 1);
+      const int64_t wrow = ((int64_t)ex * hb + h / 2) * c->N;
+      for (int n = 0; n < c->N; ++n) blk[n] += av * dec_e2m1_at(c->w, wrow + n, h & 1);
+    }
+    const double sa = orc_e8m0(c->a_scale[r * nb + b]);
+    const uint8_t* swr = c->w_scale + ((int64_t)ex * nb + b) * c->N;
+    for (int n = 0; n < c->N; ++n) o[n] += sa * orc_e8m0(swr[n]) * blk[n];
+  }
+  free(blk);
+  if (c->act == ORC_ACT_RELU)
+    for (int n = 0; n < c->N; ++n)
+      if (o[n] < 0.0) o[n] = 0.0;
+}
+
+int orc_gmm_mx4(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
+                const int32_t* offsets, int e, int Hin, int N, int act, const int32_t* rows, int nrows,
+                double* out, int nthreads) {
+  if (!a || !w || !a_scale || !w_scale || !offsets || !out || e <= 0 || Hin <= 0 || N <= 0) return -1;
+  if (Hin % 32 != 0) return -1;
+  if (act != ORC_ACT_NONE && act != ORC_ACT_RELU) return -1;
+  if (offsets[0] != 0) return -1;
+  for (int q = 0; q < e; ++q)
+    if (offsets[q + 1] < offsets[q]) return -1;
+  int64_t n_out = rows ? nrows : offsets[e];
+  if (n_out < 0) return -1;
+  orc_gmm_mx4_ctx c = {a, a_scale, w, w_scale, offsets, e, Hin, N, act, rows, out, 0};
+  orc_parallel_for(n_out, nthreads, orc_gmm_mx4_row, &c);
+  return c.bad ? -1 : 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* O8 combine / Unpermute                                              */
 /* ------------------------------------------------------------------ */

@@ -106,6 +106,16 @@ int orc_gmm_mx(const void* a, int a_dt, const uint8_t* a_scale, const void* w, i
                const uint8_t* w_scale, const int32_t* offsets, int e, int Hin, int N, int act,
                const int32_t* rows, int nrows, double* out, int nthreads);
 
+/* MX with E2M1 (OCP FP4) elements, packed two per byte along the reduction
+ * index (even index in the low nibble): a (A, Hin/2) bytes, w (e, Hin/2, N)
+ * bytes (byte (ex, k, n) holds rows 2k and 2k+1 of column n); scales as for
+ * orc_gmm_mx. orc_e2m1: value of one 4-bit code (s ee m, bias 1, exponent 0
+ * subnormal: m/2; largest 6). */
+double orc_e2m1(int code);
+int orc_gmm_mx4(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
+                const int32_t* offsets, int e, int Hin, int N, int act, const int32_t* rows, int nrows,
+                double* out, int nthreads);
+
 /* Per-token quantisation to E4M3 (quant modes 3 "pertoken" and 7 "pertoken
  * dynamic" of "aclnnQuantGroupedMatMulAlltoAllv", 量化模式 enumeration; the
  * formula there multiplies gmmX's scale back onto the product).

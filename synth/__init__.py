@@ -150,6 +150,52 @@ def quantize_mx(a: np.ndarray, axis: int):
     return (np.ascontiguousarray(np.moveaxis(q, -1, axis)), np.ascontiguousarray(np.moveaxis(sb, -1, axis)))
 
 
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # OCP FP4 magnitudes, codes 0..7
+
+
+def to_e2m1(a: np.ndarray) -> np.ndarray:
+    """E2M1 codes (0..15, sign in bit 3) of a: nearest magnitude on the FP4
+    grid, ties to the even code, saturating at 6."""
+    a = np.asarray(a, np.float64)
+    mag = np.abs(a)
+    d = np.abs(mag[..., None] - _E2M1_GRID)
+    best = d.min(axis=-1, keepdims=True)
+    # among the nearest grid points (at most two neighbours) prefer the even code
+    pref = (d == best) * (2 - (np.arange(8) % 2))
+    code = pref.argmax(axis=-1).astype(np.uint8)
+    return code | (np.signbit(a).astype(np.uint8) << 3)
+
+
+def pack_e2m1(codes: np.ndarray, axis: int) -> np.ndarray:
+    """Two E2M1 codes per byte along `axis` (even index in the low nibble)."""
+    c = np.moveaxis(np.asarray(codes, np.uint8), axis, -1)
+    if c.shape[-1] % 2:
+        raise ValueError("pack_e2m1: axis length must be even")
+    packed = (c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4)
+    return np.ascontiguousarray(np.moveaxis(packed.astype(np.uint8), -1, axis))
+
+
+def quantize_mx4(a: np.ndarray, axis: int):
+    """MX input recipe with E2M1 elements (OCP microscaling): blocks of 32
+    along `axis` share the scale 2^(floor(log2 amax) - 2) (2 = E2M1's largest
+    exponent), stored as an E8M0 byte; elements E2M1(a / scale), packed two
+    per byte along `axis`. Returns (packed bytes, scale bytes)."""
+    a = np.moveaxis(np.asarray(a, np.float32), axis, -1)
+    shp = a.shape
+    if shp[-1] % 32:
+        raise ValueError("quantize_mx4: axis length must be a multiple of 32")
+    blocks = a.reshape(shp[:-1] + (shp[-1] // 32, 32))
+    am = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(am > 0, np.floor(np.log2(np.where(am > 0, am, 1.0))) - 2, 0).astype(np.int32)
+    ex = np.clip(ex, -127, 127)
+    scaled = blocks / np.ldexp(np.float32(1.0), ex)[..., None].astype(np.float32)
+    codes = to_e2m1(scaled.reshape(shp))
+    packed = pack_e2m1(codes, -1)
+    sb = (ex + 127).astype(np.uint8)
+    return (np.ascontiguousarray(np.moveaxis(packed, -1, axis)), np.ascontiguousarray(np.moveaxis(sb, -1, axis)))
+
+
 def random_routing(seed: int, T: int, E: int, K: int) -> np.ndarray:
     out = np.empty((T, K), np.int32)
     if lib().synth_random_routing(seed, T, E, K, _ptr(out)) != 0:

@@ -583,3 +583,77 @@ def test_gmm_row_scales():
     ref = oracle.gmm(a, w, off, act=oracle.ACT_RELU)
     assert np.array_equal(np.delete(got, 7, axis=0), np.delete(ref, 7, axis=0))
     assert np.array_equal(got[7], 4.0 * ref[7])
+
+
+# ---- MX with E2M1 (OCP FP4) elements, packed two per byte along the reduction.
+
+def test_e2m1_format_properties():
+    vals = np.array([oracle.e2m1(c) for c in range(16)])
+    assert np.array_equal(vals[8:], -vals[:8]) and vals[0] == 0.0
+    assert np.all(np.diff(vals[:8]) > 0)
+    # one mantissa bit per binade above the subnormal code: value(e+1, m) = 2 value(e, m)
+    for e in range(1, 3):
+        for m in range(2):
+            assert vals[2 * (e + 1) + m] == 2 * vals[2 * e + m]
+    assert vals[1] == vals[2] / 2  # the subnormal code is half the smallest normal value
+    # the input encoder picks the nearest value, ties to the even code, saturating
+    rng = np.random.default_rng(50)
+    v = rng.uniform(-8, 8, 5000)
+    got = np.array([oracle.e2m1(c) for c in synth.to_e2m1(v)])
+    dist = np.abs(v[:, None] - vals[None, :])
+    assert np.allclose(np.abs(got - v), dist.min(axis=1))
+
+
+def _e2m1_grid_case(seed, counts, Hin, N):
+    rng = np.random.default_rng(seed)
+    e = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    af = rng.choice(grid, (A, Hin)) * rng.choice([-1, 1], (A, Hin))
+    wf = rng.choice(grid, (e, Hin, N)) * rng.choice([-1, 1], (e, Hin, N))
+    a = synth.pack_e2m1(synth.to_e2m1(af), 1)
+    w = synth.pack_e2m1(synth.to_e2m1(wf), 1)
+    return off, af, wf, a, w
+
+
+def test_gmm_mx4_unit_scales_equal_numpy_matmul():
+    """Grid values with unit scales: the packed FP4 GEMM equals numpy's matmul
+    of the unpacked values exactly (this pins the decoding and both packings)."""
+    counts = [7, 0, 12, 5]
+    off, af, wf, a, w = _e2m1_grid_case(51, counts, 64, 24)
+    A, e = af.shape[0], len(counts)
+    sa = np.full((A, 2), 127, np.uint8)
+    sw = np.full((e, 2, 24), 127, np.uint8)
+    out = oracle.gmm_mx4(a, sa, w, sw, off)
+    ref = np.concatenate([af[off[i]:off[i + 1]] @ wf[i] for i in range(e)])
+    assert np.array_equal(out, ref)
+
+
+def test_gmm_mx4_block_scales_by_brute_force():
+    counts = [5, 9]
+    off, af, wf, a, w = _e2m1_grid_case(52, counts, 96, 10)
+    A, e, nb = af.shape[0], len(counts), 3
+    rng = np.random.default_rng(53)
+    sa = rng.integers(120, 135, (A, nb)).astype(np.uint8)
+    sw = rng.integers(120, 135, (e, nb, 10)).astype(np.uint8)
+    out = oracle.gmm_mx4(a, sa, w, sw, off, act=oracle.ACT_RELU)
+    ref = np.zeros((A, 10))
+    for r in range(A):
+        ex = int(np.searchsorted(off, r, side="right") - 1)
+        for b in range(nb):
+            dot = af[r, 32 * b:32 * b + 32] @ wf[ex, 32 * b:32 * b + 32]
+            ref[r] += 2.0 ** (int(sa[r, b]) - 127) * 2.0 ** (sw[ex, b].astype(int) - 127) * dot
+    assert np.allclose(out, np.maximum(ref, 0), rtol=1e-15, atol=0)
+
+
+def test_quantize_mx4_recipe_roundtrip():
+    rng = np.random.default_rng(54)
+    x = (rng.standard_normal((16, 128)) * np.exp2(rng.integers(-5, 5, (16, 1)))).astype(np.float32)
+    q, sc = synth.quantize_mx4(x, axis=1)
+    lo, hi = q & 15, q >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(16, 128)
+    vals = np.array([oracle.e2m1(c) for c in range(16)])[codes]
+    step = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=1)
+    deq = vals * step
+    assert np.all(np.abs(deq - x) <= 0.25 * np.abs(x) + 0.25 * step + 1e-30)
