@@ -13,7 +13,7 @@ a second stream (fp8dyn: gmmX quantised per row on the device first).
 
 Prints ONE JSON line. Default workload: prefill (T=4096, H=4096, E=8, K=2,
 F=14336, bf16). Other workloads: --workload skewed|decode16|decode64|
-decode256|fp8gmm|fp8mx|fp8dyn|tiny.
+decode256|fp8gmm|fp8mx|fp8dyn|fp4mx|tiny.
 """
 from __future__ import annotations
 
@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP4_TFLOPS = 10100.0  # dense E2M1 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer tokens/s; moe_gmm TFLOP/s and % of MFMA/HBM peak (1 GPU)"
 
@@ -51,7 +52,7 @@ def parse():
                     help="untimed warm-up steps (default: as many as fill 0.4 s, so the GPU's "
                          "clocks have left their idle state; the count is reported)")
     ap.add_argument("--workload", default="prefill",
-                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx", "fp8dyn"])
+                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx", "fp8dyn", "fp4mx"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -355,8 +356,10 @@ def bench_fp8(args, dev, mode="pt"):
     import mixture_experts_layer_06_amd as moe
     from synth import configs
 
-    use_mx, dyn = mode == "mx", mode == "dyn"
-    d = (configs.fp8_mx_inputs() if use_mx else configs.fp8_dyn_inputs() if dyn else configs.fp8_inputs())
+    fp4 = mode == "mx4"
+    use_mx, dyn = mode in ("mx", "mx4"), mode == "dyn"
+    d = (configs.fp4_mx_inputs() if fp4 else configs.fp8_mx_inputs() if use_mx else
+         configs.fp8_dyn_inputs() if dyn else configs.fp8_inputs())
     T, e, K, A, H1, N1, H2, N2 = (d[k] for k in ("T", "e", "K", "A", "H1", "N1", "H2", "N2"))
     # dispatch layout of the routed rows: computed once on the device by moe_permute
     idx = host_to_dev(d["topk_idx"], dev)
@@ -404,7 +407,10 @@ def bench_fp8(args, dev, mode="pt"):
         if use_mx:
             if ev is not None:
                 ev[5].record(main)
-            moe.gmm_mx(gx, sx, gw, sw, perm["offsets"], out=gy)
+            if fp4:
+                moe.gmm_mxfp4(gx, sx, gw, sw, perm["offsets"], out=gy)
+            else:
+                moe.gmm_mx(gx, sx, gw, sw, perm["offsets"], out=gy)
             if ev is not None:
                 ev[1].record(main)
             moe.combine(gy, perm["perm_dst"], None, T, K, out=un)
@@ -441,20 +447,26 @@ def bench_fp8(args, dev, mode="pt"):
     q_ms, gmm_ms, un_ms, sh_ms = span(0, 5), span(5, 1), span(1, 2), span(3, 4)
     counts = perm["counts"].cpu().numpy().tolist()
     fl, by = flops_bytes_gmm(counts, H1, N1, 1)
+    if fp4:  # half a byte per activation and weight element
+        by -= (A * H1 + sum(1 for c in counts if c > 0) * H1 * N1) // 2
     if use_mx:  # E8M0 scales: one byte per 32 activation and weight elements
         by += A * (H1 // 32) + sum(1 for c in counts if c > 0) * (H1 // 32) * N1
     if dyn:  # one fp32 scale per activation row
         by += A * 4
     achieved = fl / (gmm_ms * 1e-3) / 1e12
-    wl = {"pt": "fp8gmm", "mx": "fp8mx", "dyn": "fp8dyn"}[mode]
+    peak = PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS
+    wl = {"pt": "fp8gmm", "mx": "fp8mx", "dyn": "fp8dyn", "mx4": "fp4mx"}[mode]
     data = {"pt": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
             "mx": "synthetic (seeded; E4M3 with MX E8M0 scales per 32 elements, OCP recipe; "
                   "random top-8 of 32 routing)",
             "dyn": "synthetic (seeded; bf16 gmmX quantised per row on the device, E4M3 weights with a "
-                   "per-tensor scale; random top-8 of 32 routing)"}[mode]
+                   "per-tensor scale; random top-8 of 32 routing)",
+            "mx4": "synthetic (seeded; E2M1 with MX E8M0 scales per 32 elements, OCP recipe; "
+                   "random top-8 of 32 routing)"}[mode]
     kernel = {"pt": "moe_gmm_scatter E4M3 (gmm_pp8_kernel, Unpermute fused into its stores)",
               "mx": "moe_gmm_mx E4M3 + E8M0 (gmm_pp8_kernel<true>)",
-              "dyn": "moe_gmm_scatter E4M3, per-token scales (gmm_pp8_kernel, Unpermute fused)"}[mode]
+              "dyn": "moe_gmm_scatter E4M3, per-token scales (gmm_pp8_kernel, Unpermute fused)",
+              "mx4": "moe_gmm_mxfp4 E2M1 + E8M0 (gmm_pp8_kernel<true, true>)"}[mode]
     kernels = {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
                "unpermute": ({"ms": un_ms, "GB/s": 2 * A * N1 * 2 / (un_ms * 1e-3) / 1e9} if use_mx
                              else "fused into the grouped GEMM's stores"),
@@ -464,12 +476,12 @@ def bench_fp8(args, dev, mode="pt"):
     res = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
-        "data": data,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4_e2m1" if fp4 else "fp8_e4m3", "data": data,
         "config": {"workload": f"{wl}: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
                                f"({T},{H2})x({H2},{N2}) bf16", "tokens_per_step": T},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": measured_traffic(wl), "kernel": kernel, "gmm_source": source_digest(),
                      "flops_per_launch": fl, "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
         "kernels": kernels,
@@ -516,8 +528,9 @@ def main():
     moe.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload in ("fp8gmm", "fp8mx", "fp8dyn"):
-        res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8mx": "mx", "fp8dyn": "dyn"}[args.workload])
+    if args.workload in ("fp8gmm", "fp8mx", "fp8dyn", "fp4mx"):
+        res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8mx": "mx", "fp8dyn": "dyn",
+                                               "fp4mx": "mx4"}[args.workload])
         res["achievable"] = achievable(dev)
     else:
         res, host = bench_layer(args, dev)

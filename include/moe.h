@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10600 /* 1.6.0: moe_quant_rows and per-token E4M3 activation scales */
+#define MOE_VERSION 10700 /* 1.7.0: moe_gmm_mxfp4 (MX block-scaled E2M1 grouped GEMM) */
 
 typedef enum {
   MOE_OK = 0,
@@ -239,6 +239,24 @@ moe_status moe_gmm_scatter(const void* a, moe_dtype a_dt, moe_quant_mode a_q, co
 moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
                       const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
                       void* stream);
+
+/*
+ * moe_gmm_mxfp4 — moe_gmm_mx with E2M1 (OCP FP4: sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) elements, the
+ * other element type of the page's mx mode ("aclnnQuantGroupedMatMulAlltoAllv",
+ * quant-mode enumeration, mode 6; OCP MXFP4). Two elements per byte along the
+ * reduction index, the even one in the low nibble:
+ *   a       device (A, Hin/2) bytes: byte (r, k) holds a[r,2k] and a[r,2k+1]
+ *   w       device (e, Hin/2, N) bytes: byte (ex, k, n) holds w[ex,2k,n] and
+ *           w[ex,2k+1,n]
+ *   a_scale device (A, Hin/32) E8M0 bytes; w_scale device (e, Hin/32, N)
+ *   out     device (A,N) bf16
+ * Hin must be a multiple of 256 and N of 16 (else MOE_ERR_UNSUPPORTED).
+ * Arithmetic, offsets, act and errors as moe_gmm_mx.
+ */
+moe_status moe_gmm_mxfp4(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                         const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                         void* stream);
 
 /*
  * moe_combine — back to token order.

@@ -27,7 +27,7 @@ ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
-           "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx", "moe_combine", "moe_sum_slots",
+           "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
            "moe_quant_rows", "moe_layer_workspace_size", "moe_layer")
 
 
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.moe_gmm_scatter.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
                                       vp, vp, vp, i32, vp, sz, vp]
         L.moe_gmm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+        L.moe_gmm_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
         L.moe_sum_slots.argtypes = [vp, i32, i32, i32, i32, vp, vp]
         L.moe_quant_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp, vp]
@@ -242,6 +243,22 @@ def gmm_mx(a, a_scale, w, w_scale, offsets, act=ACT_NONE, out=None, stream=None)
     st = lib().moe_gmm_mx(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(offsets), e, A, Hin, N,
                           act, _ptr(out), _stream(stream))
     _check(st, "moe_gmm_mx")
+    return out
+
+
+def gmm_mxfp4(a, a_scale, w, w_scale, offsets, act=ACT_NONE, out=None, stream=None):
+    """moe_gmm_mxfp4: E2M1 a (A, Hin/2) and w (e, Hin/2, N) packed bytes (two
+    values per byte along Hin), E8M0 scales a_scale (A, Hin/32) and w_scale
+    (e, Hin/32, N) (uint8 device tensors); bf16 output."""
+    A, Hh = a.shape
+    e, Hw, N = w.shape
+    if Hw != Hh:
+        raise ValueError("a and w disagree on Hin")
+    if out is None:
+        out = _empty((A, N), torch.bfloat16, a)
+    st = lib().moe_gmm_mxfp4(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(offsets), e, A, 2 * Hh, N,
+                             act, _ptr(out), _stream(stream))
+    _check(st, "moe_gmm_mxfp4")
     return out
 
 

@@ -326,6 +326,32 @@ moe_status moe_quant_rows(const void* x, moe_dtype x_dt, int x_rows, int H, cons
   return launch_quant_rows(x, x_dt, x_rows, H, row_src, row_div, rows, q, scale, (hipStream_t)stream);
 }
 
+moe_status moe_gmm_mxfp4(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                         const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                         void* stream) {
+  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
+  if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
+  // 256-deep K slices (128 bytes) of whole scale blocks, 16-byte column chunks, 32-bit offsets
+  if (Hin % 256 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)(Hin / 2) * N >= (1ll << 31) || (int64_t)(Hin / 32) * N * e >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (A == 0) return MOE_OK;
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(a_scale);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(w_scale);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(out);
+  REQUIRE_ALIGNED(a);
+  REQUIRE_ALIGNED(a_scale);
+  REQUIRE_ALIGNED(w);
+  REQUIRE_ALIGNED(w_scale);
+  REQUIRE_ALIGNED(offsets);
+  REQUIRE_ALIGNED(out);
+  return launch_gmm_mx(a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out, (hipStream_t)stream, true);
+}
+
 moe_status moe_sum_slots(const void* z, moe_dtype dt, int T, int K, int N, void* out, void* stream) {
   if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
   if (T < 0 || K < 1 || K > kMaxK || !dim_ok(N) || (int64_t)T * K >= kMaxRows) return MOE_ERR_BAD_SHAPE;

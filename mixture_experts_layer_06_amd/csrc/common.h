@@ -110,10 +110,11 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                       moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s,
                       RowMap gx = RowMap{});
-// Grouped GEMM on MX (E8M0 block-scaled) E4M3 operands; Hin % 128 == 0, N % 16 == 0.
+// Grouped GEMM on MX (E8M0 block-scaled) operands: E4M3 (Hin % 128 == 0) or,
+// fp4, E2M1 packed two per byte along K (Hin % 256 == 0); N % 16 == 0.
 moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void* w,
                          const unsigned char* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
-                         moe_act act, void* out, hipStream_t s);
+                         moe_act act, void* out, hipStream_t s, bool fp4 = false);
 // sum_slots: y[t] = sum_k y_perm[t*K+k] (perm_dst and gate ignored).
 // Per-token E4M3 quantisation of the rows src[r] / div (or r) of x.
 moe_status launch_quant_rows(const void* x, moe_dtype dt, int x_rows, int H, const int32_t* src, int div,

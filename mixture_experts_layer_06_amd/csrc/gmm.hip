@@ -1103,23 +1103,28 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
 // c ^ ((k/2)%4 + 4*((k/32)%2)), so the 16 rows that lanes 0-31 (or 32-63)
 // of one transposing read touch fall in distinct banks.
 
-template <bool MX>
+// FP4 (MX only): E2M1 elements, two per byte along K, so a slot's 128 bytes
+// per row hold 256 K values, two MFMA K steps of 128, and 8 scale blocks.
+template <bool MX, bool FP4 = false>
 struct Pp8Cfg {
+  static_assert(MX || !FP4, "E2M1 operands come with MX block scales");
   static constexpr int kBM = 256, kBN = 128;
-  static constexpr int kKB = 128;  // K values (bytes) per slot
+  static constexpr int kKB = 128;  // bytes per activation row (= weight K rows) per slot
   static constexpr int kStages = 3;
   static constexpr int kNT = 512;
   static constexpr int kLdsA = kBM * kKB;  // 32 KB
   static constexpr int kLdsW = kKB * kBN;  // 16 KB
-  // MX: the slot's E8M0 scales, activations [256 rows][4 blocks] then
-  // weights [4 blocks][128 columns]
-  static constexpr int kScA = kLdsA + kLdsW, kScW = kScA + kBM * 4;
-  static constexpr int kStage = kLdsA + kLdsW + (MX ? kBM * 4 + 4 * kBN : 0);
+  static constexpr int kBlk = FP4 ? 8 : 4;  // MX scale blocks per slot
+  // MX: the slot's E8M0 scales, activations [kBlk/4][256 rows][4 blocks]
+  // then weights [kBlk blocks][128 columns]
+  static constexpr int kScA = kLdsA + kLdsW, kScW = kScA + kBM * kBlk;
+  static constexpr int kStage = kLdsA + kLdsW + (MX ? kBM * kBlk + kBlk * kBN : 0);
   static constexpr int kDummy = kStages * kStage;  // 1 KB that soaks up the unused scale DMA (MX)
   static constexpr int kLds = kDummy + (MX ? 1024 : 0);
   static constexpr int kADma = kLdsA / 1024 / 8;  // 1 KB DMA ops per wave per slot
   static constexpr int kWDma = kLdsW / 1024 / 8;
-  static constexpr int kPerStage = kADma + kWDma + (MX ? 1 : 0);  // + one 256-byte scale op
+  static constexpr int kSDma = MX ? kBlk / 4 : 0;  // 256-byte scale ops per wave per slot
+  static constexpr int kPerStage = kADma + kWDma + kSDma;
   static_assert(kLds + 2 * 257 * 4 <= 160 * 1024 || kLds <= 160 * 1024, "LDS budget");
 };
 
@@ -1133,14 +1138,14 @@ struct Pp8Cfg {
 __device__ __forceinline__ int pp8_xswz(int m) { return 2 * ((m >> 1) & 3); }
 __device__ __forceinline__ int pp8_wswz(int k) { return ((k >> 1) & 3) | (((k >> 4) & 1) << 2); }
 
-template <bool MX>
+template <bool MX, bool FP4 = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp8_kernel(
     const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const unsigned char* __restrict__ a_mx, const unsigned char* __restrict__ w_mx,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
     bf16_t* __restrict__ out, RowMap gx) {
-  typedef Pp8Cfg<MX> C;
+  typedef Pp8Cfg<MX, FP4> C;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   {
     int* s_off = reinterpret_cast<int*>(smem);
@@ -1156,33 +1161,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = wave >> 2, wm2 = (wave >> 1) & 1, wn = wave & 1;
-  const int nsteps = (Hin + C::kKB - 1) / C::kKB;
+  // bytes per activation row = weight K rows per expert (E2M1: two K values per byte)
+  const int rowb = FP4 ? Hin / 2 : Hin;
+  const int nsteps = (rowb + C::kKB - 1) / C::kKB;
   // activation rows: relative to the tile's first row, or (gather) absolute rows of a
   const bool gat = gx.src != nullptr;
-  const u32x4_t asrd = make_srd(a + (gat ? 0 : (int64_t)tile.row0 * Hin),
-                                (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)Hin);
-  const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * Hin * N, (uint32_t)Hin * (uint32_t)N);
+  const u32x4_t asrd = make_srd(a + (gat ? 0 : (int64_t)tile.row0 * rowb),
+                                (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)rowb);
+  const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * rowb * N, (uint32_t)rowb * (uint32_t)N);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // MX scales (Hin a multiple of 128): 4 E8M0 blocks per row and slice.
-  // Waves 0-3 fetch the activation rows' scales (one row per lane), waves 4
-  // and 5 the weight columns' (32 lanes per block), waves 6 and 7 an
-  // out-of-range op into the dummy KB, so every wave counts one op per slice.
+  // MX scales (whole slices): kBlk E8M0 blocks per row and slice. Waves 0-3
+  // fetch the activation rows' scales (one row per lane, 4 blocks per op),
+  // the next kBlk/2 waves the weight columns' (32 lanes per block, 2 blocks
+  // per op); every other op is an out-of-range one into the dummy KB, so
+  // that every wave counts kSDma ops per slice.
   const int nbk = Hin / 32;
   u32x4_t ssrd = {0u, 0u, 0u, 0u};
   uint32_t s_voff = kOOB, s_lds = lds0 + C::kDummy, s_step = 0;
+  bool s_real = false;
   if (MX) {
     if (wave < 4) {
       const int m = 64 * wave + lane;
       ssrd = make_srd(a_mx + (int64_t)tile.row0 * nbk, (uint32_t)tile.rows * (uint32_t)nbk);
       s_voff = m < tile.rows ? (uint32_t)m * (uint32_t)nbk : kOOB;
       s_lds = C::kScA + wave * 256;
-      s_step = 4;
-    } else if (wave < 6) {
+      s_step = C::kBlk;
+      s_real = true;
+    } else if (wave < 4 + C::kBlk / 2) {
       const int bb = (64 * (wave - 4) + lane) / 32, col = tile.n0 + 4 * (lane % 32);
       ssrd = make_srd(w_mx + (int64_t)tile.ex * nbk * N, (uint32_t)nbk * (uint32_t)N);
       s_voff = (uint32_t)bb * (uint32_t)N + (uint32_t)col + (col < N ? 0u : kOOB);
       s_lds = C::kScW + (wave - 4) * 256;
-      s_step = 4u * (uint32_t)N;
+      s_step = (uint32_t)C::kBlk * (uint32_t)N;
+      s_real = true;
     } else {
       ssrd = make_srd(a_mx, 4u);
     }
@@ -1196,7 +1207,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int prow = kb >> 7, pc = (kb >> 4) & 7;
     const int lc = pc ^ pp8_xswz(prow);
     const int src = prow >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + prow) : prow;
-    a_voff[q] = (src >= 0 ? (uint32_t)src * (uint32_t)Hin : kOOB) + lc * 16;
+    a_voff[q] = (src >= 0 ? (uint32_t)src * (uint32_t)rowb : kOOB) + lc * 16;
     a_kc[q] = lc * 16;
   }
   uint32_t w_voff[C::kWDma];
@@ -1213,16 +1224,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int kb0 = step * C::kKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
-      dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < Hin ? 0u : kOOB),
+      dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < rowb ? 0u : kOOB),
             base + (wave * C::kADma + q) * 1024);
     const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : 0u;
     const uint32_t kend = step < nsteps ? 0u : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
       dma16(wsrd, (w_voff[q] + kstep) | kend, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
-    if (MX)
-      dma4(ssrd, (s_voff + (step < nsteps ? (uint32_t)step * s_step : 0u)) | kend,
-           wave < 6 ? base + s_lds : lds0 + C::kDummy);
+    if (MX) {
+      const uint32_t soff = (s_voff + (step < nsteps ? (uint32_t)step * s_step : 0u)) | kend;
+      dma4(ssrd, soff, s_real ? base + s_lds : lds0 + C::kDummy);
+      if (FP4) {  // activation blocks 4..7 of the slice, or a filler op
+        if (wave < 4)
+          dma4(ssrd, soff + 4u, base + s_lds + C::kBM * 4);
+        else
+          dma4(ssrd, kOOB, lds0 + C::kDummy);
+      }
+    }
   };
   auto bar = [] {
     __builtin_amdgcn_sched_barrier(0);
@@ -1273,7 +1291,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   for (int j = 0; j < 4; ++j) wch[j] = ((4 * wn + j) ^ wsw) * 16;
   typedef int i32x2_t __attribute__((ext_vector_type(2)));
   i32x8_t xa[4], wf[4];
-  int sxa[4], sxw[4];  // MX: this lane's E8M0 scales (block kq of the slice)
+  int sxa[C::kBlk / 4][4], sxw[C::kBlk / 4][4];  // MX: this lane's E8M0 scales (block kq of each K step)
   auto read_frags = [&](int slice) {
     const unsigned char* st = smem + (slice % S) * C::kStage;
 #pragma unroll
@@ -1294,9 +1312,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
       }
     if (MX) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sxa[i] = st[C::kScA + (half * 128 + wm2 * 64 + i * 16 + ci) * 4 + kq];
+      for (int u = 0; u < C::kBlk / 4; ++u) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sxw[j] = st[C::kScW + kq * C::kBN + wn * 64 + 16 * j + ci];
+        for (int i = 0; i < 4; ++i)
+          sxa[u][i] = st[C::kScA + u * C::kBM * 4 + (half * 128 + wm2 * 64 + i * 16 + ci) * 4 + kq];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sxw[u][j] = st[C::kScW + (4 * u + kq) * C::kBN + wn * 64 + 16 * j + ci];
+      }
     }
   };
   f32x4_t acc[4][4];
@@ -1305,12 +1327,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   auto multiply = [&]() {
+    if (FP4) {
+      // E2M1: each 32-byte fragment holds two K steps of 16 bytes per lane;
+      // lane group g's 16 bytes are scale block g of the step (measured)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const i32x8_t wv = u ? __builtin_shufflevector(wf[j], wf[j], 4, 5, 6, 7, 4, 5, 6, 7) : wf[j];
+            const i32x8_t xv = u ? __builtin_shufflevector(xa[i], xa[i], 4, 5, 6, 7, 4, 5, 6, 7) : xa[i];
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, xv, acc[i][j], 4, 4, 0,
+                                                                         sxw[u % (C::kBlk / 4)][j], 0,
+                                                                         sxa[u % (C::kBlk / 4)][i]);
+          }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = MX ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0,
-                                                                          sxw[j], 0, sxa[i])
+                                                                          sxw[0][j], 0, sxa[0][i])
                        : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0,
                                                                           0, 0, 0);
   };
@@ -1808,14 +1847,14 @@ moe_status launch_pp(const void* a, const float* as, const void* w, const float*
   return launch_status();
 }
 
-template <bool MX>
+template <bool MX, bool FP4 = false>
 moe_status launch_pp8(const void* a, const float* as, const void* w, const float* ws,
                       const unsigned char* a_mx, const unsigned char* w_mx, const int32_t* offsets, int e,
                       int A, int Hin, int N, int relu, void* out, hipStream_t s, RowMap gx) {
-  typedef Pp8Cfg<MX> C;
+  typedef Pp8Cfg<MX, FP4> C;
   static bool attr_done = false;
   if (!attr_done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp8_kernel<MX>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp8_kernel<MX, FP4>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     attr_done = true;
   }
@@ -1823,7 +1862,7 @@ moe_status launch_pp8(const void* a, const float* as, const void* w, const float
   const int64_t blocks = mt_max * cdiv64(N, C::kBN);
   const int64_t grid = cdiv64(blocks, 8) * 8;
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL(gmm_pp8_kernel<MX>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
+  hipLaunchKernelGGL((gmm_pp8_kernel<MX, FP4>), dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
                      (const unsigned char*)a, (const unsigned char*)w, as, ws, a_mx, w_mx, offsets, e, A,
                      Hin, N, relu, (bf16_t*)out, gx);
   return launch_status();
@@ -1944,8 +1983,11 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
 
 moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void* w,
                          const unsigned char* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
-                         moe_act act, void* out, hipStream_t s) {
+                         moe_act act, void* out, hipStream_t s, bool fp4) {
   if (A == 0) return MOE_OK;
+  if (fp4)
+    return launch_pp8<true, true>(a, nullptr, w, nullptr, a_scale, w_scale, offsets, e, A, Hin, N,
+                                  act == MOE_ACT_RELU, out, s, RowMap{});
   return launch_pp8<true>(a, nullptr, w, nullptr, a_scale, w_scale, offsets, e, A, Hin, N,
                           act == MOE_ACT_RELU, out, s, RowMap{});
 }

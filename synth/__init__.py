@@ -158,11 +158,10 @@ def to_e2m1(a: np.ndarray) -> np.ndarray:
     grid, ties to the even code, saturating at 6."""
     a = np.asarray(a, np.float64)
     mag = np.abs(a)
-    d = np.abs(mag[..., None] - _E2M1_GRID)
-    best = d.min(axis=-1, keepdims=True)
-    # among the nearest grid points (at most two neighbours) prefer the even code
-    pref = (d == best) * (2 - (np.arange(8) % 2))
-    code = pref.argmax(axis=-1).astype(np.uint8)
+    mids = (_E2M1_GRID[1:] + _E2M1_GRID[:-1]) / 2  # 0.25 0.75 1.25 1.75 2.5 3.5 5
+    code = np.searchsorted(mids, mag, side="right").astype(np.uint8)  # a midpoint goes up ...
+    down = (mag == 0.25) | (mag == 1.25) | (mag == 2.5) | (mag == 5.0)  # ... unless the even code is below
+    code -= down.astype(np.uint8)
     return code | (np.signbit(a).astype(np.uint8) << 3)
 
 

@@ -18,7 +18,7 @@ import math
 
 import numpy as np
 
-from . import (amax, bf16_to_f32, ints, normal, quantize_e4m3, quantize_mx, random_routing, seed_for,
+from . import (amax, bf16_to_f32, ints, normal, quantize_e4m3, quantize_mx, quantize_mx4, random_routing, seed_for,
                to_bf16, to_e4m3)
 
 LAYER_SHAPES = {
@@ -124,6 +124,27 @@ def fp8_mx_inputs(wid: int = 2, with_shared: bool = True, **shape) -> dict:
     return out
 
 
+def fp4_mx_inputs(wid: int = 2, with_shared: bool = True, **shape) -> dict:
+    """The fp8 workload with MXFP4 operands: the same fp32 sources (same seeds)
+    quantised to E2M1 in 32-element blocks along H1 (per row of gmmX, per
+    column of gmmWeight), packed two per byte along H1: gmm_x (A, H1/2),
+    gmm_w (e, H1/2, N1); E8M0 scales gmm_x_scale (A, H1/32), gmm_w_scale
+    (e, H1/32, N1)."""
+    d = dict(FP8_SHAPE)
+    d.update({k: v for k, v in shape.items() if v is not None})
+    T, e, K, H1, N1, H2, N2 = d["T"], d["e"], d["K"], d["H1"], d["N1"], d["H2"], d["N2"]
+    A = T * K
+    idx = random_routing(seed_for(wid, 0), T, e, K)
+    gx_q, sx = quantize_mx4(normal(seed_for(wid, 1), (A, H1), 1.0), axis=1)
+    gw_q, sw = quantize_mx4(normal(seed_for(wid, 2), (e, H1, N1), math.sqrt(1.0 / H1)), axis=1)
+    out = dict(T=T, e=e, K=K, A=A, H1=H1, N1=N1, H2=H2, N2=N2, topk_idx=idx, gmm_x=gx_q,
+               gmm_x_scale=sx, gmm_w=gw_q, gmm_w_scale=sw)
+    if with_shared:
+        out["mm_x"] = normal(seed_for(wid, 3), (T, H2), 1.0, dtype="bf16")
+        out["mm_w"] = normal(seed_for(wid, 4), (H2, N2), math.sqrt(1.0 / H2), dtype="bf16")
+    return out
+
+
 def fp8_dyn_inputs(wid: int = 2, with_shared: bool = True, **shape) -> dict:
     """The fp8 workload for per-token dynamic quantisation: the same sources
     (same seeds) with gmmX left in bf16 (A, H1), to be quantised per row on the
@@ -144,5 +165,5 @@ def fp8_dyn_inputs(wid: int = 2, with_shared: bool = True, **shape) -> dict:
 
 
 __all__ = ["LAYER_SHAPES", "FP8_SHAPE", "skew_bias", "layer_inputs", "identity_ffn", "fp8_inputs", "fp8_mx_inputs",
-           "fp8_dyn_inputs",
+           "fp8_dyn_inputs", "fp4_mx_inputs",
            "bf16_to_f32", "amax", "to_e4m3"]

@@ -23,6 +23,7 @@ def declared_entry_points():
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
     for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx",
+              "moe_gmm_mxfp4",
               "moe_combine", "moe_sum_slots", "moe_quant_rows", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size",
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10600
+    assert moe.lib().moe_version() == 10700
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -264,6 +265,32 @@ def gmm_mx(a=P, sa=P, w=P, sw=P, off=P, e=8, A=100, Hin=256, N=64, act=moe.ACT_N
 ])
 def test_gmm_mx_validation(kw, status):
     assert gmm_mx(**kw) == status
+
+
+def gmm_mxfp4(a=P, sa=P, w=P, sw=P, off=P, e=8, A=100, Hin=512, N=64, act=moe.ACT_NONE, out=P):
+    return L.moe_gmm_mxfp4(a, sa, w, sw, off, e, A, Hin, N, act, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hin=128), moe.ERR_UNSUPPORTED),       # K slices of 256
+    (dict(Hin=384), moe.ERR_UNSUPPORTED),
+    (dict(N=40), moe.ERR_UNSUPPORTED),
+    (dict(act=2), moe.ERR_UNSUPPORTED),
+    (dict(e=0), moe.ERR_BAD_SHAPE),
+    (dict(A=-1), moe.ERR_BAD_SHAPE),
+    (dict(N=65536), moe.ERR_BAD_SHAPE),
+    (dict(sa=None), moe.ERR_NULL_POINTER),
+    (dict(w=None), moe.ERR_NULL_POINTER),
+    (dict(off=None), moe.ERR_NULL_POINTER),
+    (dict(sw=MIS), moe.ERR_MISALIGNED),
+    (dict(a=MIS), moe.ERR_MISALIGNED),
+])
+def test_gmm_mxfp4_validation(kw, status):
+    assert gmm_mxfp4(**kw) == status
+
+
+def test_gmm_mxfp4_zero_rows_is_noop():
+    assert gmm_mxfp4(a=None, sa=None, w=None, sw=None, off=None, out=None, A=0) == moe.OK
 
 
 def test_gmm_mx_zero_rows_is_noop():

@@ -209,6 +209,22 @@ def test_fp8_dynamic_per_token_full_size_sampled_rows():
     assert normwise_err(to_host(un)[psrc[rows]], ref) <= 8e-3
 
 
+def test_fp4_mx_gmm_full_size_sampled_rows():
+    """The fp8 workload's shapes with MXFP4 operands (65536 x 7168 x 2048, 32
+    experts): sampled rows, the first and last of every expert, against the oracle."""
+    d = configs.fp4_mx_inputs(with_shared=False)
+    e = d["e"]
+    counts, offsets, _, _ = oracle.permute(d["topk_idx"], e)
+    perm = moe.permute(to_dev(d["topk_idx"]), e)
+    gy = moe.gmm_mxfp4(to_dev(d["gmm_x"]), to_dev(d["gmm_x_scale"]), to_dev(d["gmm_w"]),
+                       to_dev(d["gmm_w_scale"]), perm["offsets"])
+    torch.cuda.synchronize()
+    rows = _boundary_rows(offsets, 24, 660)
+    ref = oracle.gmm_mx4(d["gmm_x"], d["gmm_x_scale"], d["gmm_w"], d["gmm_w_scale"], offsets, rows=rows,
+                         nthreads=NTH)
+    assert normwise_err(to_host(gy)[rows], ref) <= 8e-3
+
+
 def test_combine_full_size_prefill():
     T, E, K, H = 4096, 8, 2, 4096
     idx = synth.random_routing(630, T, E, K)

@@ -619,6 +619,60 @@ def test_gmm_mx_unit_scales_match_per_tensor_path():
     pt = to_host(moe.gmm(to_dev(a), to_dev(w), to_dev(off), a_scale=one, w_scale=one))
     assert np.array_equal(mx, pt)
 
+# ---------------------------------------------------------------- MX FP4
+
+MX4_CASES = [
+    # (name, counts, Hin, N): E2M1 with E8M0 block scales
+    ("mx4_ragged", [300, 0, 1, 555], 256, 400),
+    ("mx4_deep_k", [513, 130], 1024, 128),
+    ("mx4_partial_tiles", [257, 3, 0, 31], 512, 144),
+]
+
+
+def _mx4_case(name, counts, Hin, N, seed):
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    a, sa = synth.quantize_mx4(synth.normal(seed, (A, Hin)), axis=1)
+    w, sw = synth.quantize_mx4(synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin)), axis=1)
+    return off, a, sa, w, sw
+
+
+@pytest.mark.parametrize("case", MX4_CASES, ids=[c[0] for c in MX4_CASES])
+@pytest.mark.parametrize("act", [moe.ACT_NONE, moe.ACT_RELU], ids=["none", "relu"])
+def test_gmm_mxfp4_parity(case, act):
+    name, counts, Hin, N = case
+    off, a, sa, w, sw = _mx4_case(name, counts, Hin, N, 860 + len(name))
+    out = to_host(moe.gmm_mxfp4(to_dev(a), to_dev(sa), to_dev(w), to_dev(sw), to_dev(off), act=act))
+    ref = oracle.gmm_mx4(a, sa, w, sw, off, act=act, nthreads=8)
+    assert normwise_err(out, ref) <= 8e-3, name
+
+
+def test_gmm_mxfp4_grid_values_bit_exact_and_equal_to_fp8_mx():
+    """E2M1 grid values with block scales: exact fp32 sums, so bf16 outputs
+    equal the oracle's rounding bit for bit, and the E4M3 MX kernel on the same
+    values (every E2M1 value is an E4M3 value) gives the same bits."""
+    counts = [200, 0, 333, 129]
+    e, Hin, N = len(counts), 512, 256
+    off = _offsets(counts)
+    A = int(off[-1])
+    rng = np.random.default_rng(870)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    af = rng.choice(grid, (A, Hin)) * rng.choice([-1, 1], (A, Hin))
+    wf = rng.choice(grid, (e, Hin, N)) * rng.choice([-1, 1], (e, Hin, N))
+    a4 = synth.pack_e2m1(synth.to_e2m1(af), 1)
+    w4 = synth.pack_e2m1(synth.to_e2m1(wf), 1)
+    sa = rng.integers(125, 130, (A, Hin // 32)).astype(np.uint8)
+    sw = rng.integers(125, 130, (e, Hin // 32, N)).astype(np.uint8)
+    od = to_dev(off)
+    out4 = to_host(moe.gmm_mxfp4(to_dev(a4), to_dev(sa), to_dev(w4), to_dev(sw), od, act=moe.ACT_RELU))
+    ref = oracle.gmm_mx4(a4, sa, w4, sw, off, act=moe.ACT_RELU, nthreads=8)
+    assert np.array_equal(out4, oracle.bf16_bits(ref))
+    a8, w8 = synth.to_e4m3(af, 1.0), synth.to_e4m3(wf, 1.0)
+    out8 = to_host(moe.gmm_mx(to_dev(a8), to_dev(sa), to_dev(w8), to_dev(sw), od, act=moe.ACT_RELU))
+    assert np.array_equal(out4, out8)
+
+
 # ---------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("dt,N", [("bf16", 264), ("bf16", 30), ("f32", 30), ("f32", 128)])
