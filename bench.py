@@ -13,7 +13,7 @@ a second stream (fp8dyn: gmmX quantised per row on the device first).
 
 Prints ONE JSON line. Default workload: prefill (T=4096, H=4096, E=8, K=2,
 F=14336, bf16). Other workloads: --workload skewed|decode16|decode64|
-decode256|fp8gmm|fp8mx|fp8dyn|fp4mx|tiny.
+decode256|fp8gmm|fp8mx|fp8dyn|fp4mx|prefill_fp8|tiny.
 """
 from __future__ import annotations
 
@@ -52,7 +52,7 @@ def parse():
                     help="untimed warm-up steps (default: as many as fill 0.4 s, so the GPU's "
                          "clocks have left their idle state; the count is reported)")
     ap.add_argument("--workload", default="prefill",
-                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx", "fp8dyn", "fp4mx"])
+                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx", "fp8dyn", "fp4mx", "prefill_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -489,6 +489,110 @@ def bench_fp8(args, dev, mode="pt"):
     return res, None
 
 
+def bench_layer_fp8(args, dev):
+    """The E4M3 layer on the prefill shapes: one moe_layer_fp8 call per step
+    (route, index permute, per-token quantisation of the tokens, GEMM 1
+    gathering the quantised tokens, per-row quantisation of the hidden rows,
+    GEMM 2, weighted combine); the same path stage by stage for per-kernel times."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_06_amd as moe
+    from synth import configs
+
+    d = configs.layer_fp8_inputs("prefill")
+    T, H, E, K, F = d["T"], d["H"], d["E"], d["K"], d["F"]
+    A = T * K
+    x, wr = host_to_dev(d["x"], dev), host_to_dev(d["wr"], dev)
+    w1, w2 = host_to_dev(d["w1"], dev), host_to_dev(d["w2"], dev)
+    s1 = torch.tensor([float(d["w1_scale"])], dtype=torch.float32, device=dev)
+    s2 = torch.tensor([float(d["w2_scale"])], dtype=torch.float32, device=dev)
+    ws = torch.empty((moe.layer_fp8_workspace_size(T, H, E, K, F),), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    bufs = {"counts": torch.empty((E,), dtype=torch.int32, device=dev),
+            "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+            "perm_src": torch.empty((A,), dtype=torch.int32, device=dev),
+            "perm_dst": torch.empty((A,), dtype=torch.int32, device=dev)}
+    xq = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev)
+    xs = torch.empty((T,), dtype=torch.float32, device=dev)
+    hm = torch.empty((A, F), dtype=torch.bfloat16, device=dev)
+    hq = torch.empty((A, F), dtype=torch.float8_e4m3fn, device=dev)
+    hs = torch.empty((A,), dtype=torch.float32, device=dev)
+    yp = torch.empty((A, H), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty_like(y)
+    pws = torch.empty((max(moe.permute_workspace_size(T, E, K), 16),), dtype=torch.uint8, device=dev)
+    rws = torch.empty((max(moe.route_workspace_size(T, H, E, K, moe.BF16), 16),), dtype=torch.uint8, device=dev)
+    gws = torch.empty((max(moe.gmm_workspace_size(moe.FP8_E4M3, E, A, H, F),
+                           moe.gmm_workspace_size(moe.FP8_E4M3, E, A, F, H), 16),), dtype=torch.uint8, device=dev)
+
+    def layer_step():
+        moe.layer_fp8(x, wr, w1, s1, w2, s2, K, y=y, ws=ws)
+
+    names = ["route", "permute", "quant_x", "gmm1", "quant_h", "gmm2", "combine"]
+
+    def step(ev):
+        ev[0].record()
+        moe.route(x, wr, K, topk_idx=idx, topk_gate=gate, ws=rws)
+        ev[1].record()
+        moe.permute(idx, E, ws=pws, out=bufs)
+        ev[2].record()
+        moe.quant_rows(x, q=xq, scale=xs)
+        ev[3].record()
+        moe.gmm(xq, w1, bufs["offsets"], act=moe.ACT_RELU, a_scale=xs, per_token=True, w_scale=s1, out=hm,
+                ws=gws, rows=bufs["perm_src"], row_div=K)
+        ev[4].record()
+        moe.quant_rows(hm, q=hq, scale=hs)
+        ev[5].record()
+        moe.gmm(hq, w2, bufs["offsets"], a_scale=hs, per_token=True, w_scale=s2, out=yp, ws=gws)
+        ev[6].record()
+        moe.combine(yp, bufs["perm_dst"], gate, T, K, out=y2)
+        ev[7].record()
+
+    warmup = warm_up(layer_step, args.warmup)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer_step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+    counts = bufs["counts"].cpu().numpy().tolist()
+    fl1, by1 = flops_bytes_gmm(counts, H, F, 1)
+    fl2, by2 = flops_bytes_gmm(counts, F, H, 1)
+    gmm_ms = (per["gmm1"] + per["gmm2"]) / 2.0
+    fl_launch = (fl1 + fl2) / 2.0
+    achieved = fl_launch / (gmm_ms * 1e-3) / 1e12
+    kernels = {n: {"ms": per[n]} for n in names}
+    kernels["gmm1"]["TFLOP/s"] = fl1 / (per["gmm1"] * 1e-3) / 1e12
+    kernels["gmm2"]["TFLOP/s"] = fl2 / (per["gmm2"] * 1e-3) / 1e12
+    kernels["quant_x"]["GB/s"] = (T * H * 3 + T * 4) / (per["quant_x"] * 1e-3) / 1e9
+    kernels["quant_h"]["GB/s"] = (A * F * 3 + A * 4) / (per["quant_h"] * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded; bf16 N(0,1) tokens and router; N(0,1/fan_in) expert weights quantised "
+                "per tensor to E4M3; activations quantised per token on the device)",
+        "config": {"workload": f"prefill_fp8: T={T} H={H} E={E} K={K} F={F} ReLU, E4M3 experts, per-token "
+                               "dynamic activation quantisation", "T": T, "H": H, "E": E, "K": K, "F": F,
+                   "tokens_per_step": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
+                     "kernel": "moe_gmm E4M3, per-token scales (gmm_pp8_kernel)", "gmm_source": source_digest(),
+                     "launches_per_step": 2, "flops_per_launch": fl_launch,
+                     "bytes_per_launch": (by1 + by2) / 2.0, "avg_launch_ms": gmm_ms},
+        "kernels": kernels,
+        "ms_per_step_stage_by_stage": sum(per.values()),
+    }
+    return res, None
+
+
 def cpu_baseline_layer(host, target_s):
     """The oracle (plain fp64 C) on the host cores: the whole layer on the
     first n tokens of the same inputs, n grown until the run takes about
@@ -528,7 +632,10 @@ def main():
     moe.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload in ("fp8gmm", "fp8mx", "fp8dyn", "fp4mx"):
+    if args.workload == "prefill_fp8":
+        res, host = bench_layer_fp8(args, dev)
+        res["achievable"] = achievable(dev)
+    elif args.workload in ("fp8gmm", "fp8mx", "fp8dyn", "fp4mx"):
         res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8mx": "mx", "fp8dyn": "dyn",
                                                "fp4mx": "mx4"}[args.workload])
         res["achievable"] = achievable(dev)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10700 /* 1.7.0: moe_gmm_mxfp4 (MX block-scaled E2M1 grouped GEMM) */
+#define MOE_VERSION 10800 /* 1.8.0: moe_layer_fp8 (E4M3 experts, per-token dynamic activation quantisation) */
 
 typedef enum {
   MOE_OK = 0,
@@ -320,6 +320,25 @@ moe_status moe_layer(const void* x, const void* w_router, const float* bias, con
                      const void* w2, moe_dtype dt, int T, int H, int E, int K, int F, moe_act act,
                      void* y, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_fp8 — the layer with E4M3 experts: route on the bf16 tokens,
+ * permute, then each expert GEMM on E4M3 activations quantised per token on
+ * the fly (quant mode 7, per-token dynamic, of "aclnnQuantGroupedMatMulAlltoAllv",
+ * with per-tensor weight scales: gmmY = (gmmX @ gmmWeight) * gmmXScale *
+ * gmmWeightScale, section 计算公式): the tokens are quantised once and GEMM 1
+ * gathers them through the dispatch index; the bf16 hidden rows are
+ * quantised per row before GEMM 2; the weighted combine as moe_layer.
+ *   x (T,H) bf16, w_router (H,E) bf16, bias (E) fp32 or NULL
+ *   w1 (E,H,F) and w2 (E,F,H) E4M3 bytes; w1_scale, w2_scale: one fp32 each
+ *   (device); y (T,H) bf16; topk/counts outputs and errors as moe_layer
+ *   ws, ws_bytes: device scratch of at least moe_layer_fp8_workspace_size().
+ */
+moe_status moe_layer_fp8_workspace_size(int T, int H, int E, int K, int F, size_t* bytes);
+moe_status moe_layer_fp8(const void* x, const void* w_router, const float* bias, const uint8_t* w1,
+                         const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T, int H, int E,
+                         int K, int F, moe_act act, void* y, int32_t* topk_idx_out, float* topk_gate_out,
+                         int32_t* counts_out, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

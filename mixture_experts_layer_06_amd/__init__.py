@@ -28,7 +28,8 @@ ACT_NONE, ACT_RELU = 0, 1
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
            "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
-           "moe_quant_rows", "moe_layer_workspace_size", "moe_layer")
+           "moe_quant_rows", "moe_layer_workspace_size", "moe_layer", "moe_layer_fp8_workspace_size",
+           "moe_layer_fp8")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                 vp, vp, sz, vp]
+        L.moe_layer_fp8_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.moe_layer_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                    vp, sz, vp]
         for n in EXPORTS[2:]:
             getattr(L, n).restype = i32
         _lib = L
@@ -323,4 +327,28 @@ def layer(x, w_router, w1, w2, K, bias=None, act=ACT_RELU, y=None, ws=None, topk
                          act, _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
                          ws.numel(), _stream(stream))
     _check(st, "moe_layer")
+    return y
+
+
+def layer_fp8_workspace_size(T, H, E, K, F) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_layer_fp8_workspace_size(T, H, E, K, F, ctypes.byref(n)), "moe_layer_fp8_workspace_size")
+    return n.value
+
+
+def layer_fp8(x, w_router, w1, w1_scale, w2, w2_scale, K, bias=None, act=ACT_RELU, y=None, ws=None,
+              topk_idx=None, topk_gate=None, counts=None, stream=None):
+    """moe_layer_fp8: bf16 tokens x (T,H) and router (H,E); E4M3 experts w1
+    (E,H,F), w2 (E,F,H) with one fp32 device scale each; bf16 y (T,H)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    F = w1.shape[2]
+    if y is None:
+        y = _empty((T, H), torch.bfloat16, x)
+    if ws is None:
+        ws = _empty((layer_fp8_workspace_size(T, H, E, K, F),), torch.uint8, x)
+    st = lib().moe_layer_fp8(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1), _ptr(w1_scale), _ptr(w2),
+                             _ptr(w2_scale), T, H, E, K, F, act, _ptr(y), _ptr(topk_idx), _ptr(topk_gate),
+                             _ptr(counts), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_layer_fp8")
     return y

@@ -70,6 +70,41 @@ LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
   return L;
 }
 
+// E4M3 layer: bf16 tokens and router, E4M3 experts with per-tensor scales,
+// activations quantised per token on the way into each GEMM.
+struct LayerFp8Ws {
+  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, gmm_ws, xq, xs, hm, hq, hs, yp, total;
+};
+
+LayerFp8Ws layer_fp8_ws_layout(int T, int H, int E, int K, int F) {
+  const int64_t A = (int64_t)T * K;
+  // tokens are quantised once and gathered (rows of up to 2^31 bytes), else
+  // quantised through the dispatch index into A rows
+  const int64_t qrows = (int64_t)T * H < (1ll << 31) ? T : A;
+  LayerFp8Ws L;
+  size_t o = 0;
+  L.idx = o; o += round256(A * 4);
+  L.gate = o; o += round256(A * 4);
+  L.counts = o; o += round256((size_t)E * 4);
+  L.offsets = o; o += round256((size_t)(E + 1) * 4);
+  L.psrc = o; o += round256(A * 4);
+  L.pdst = o; o += round256(A * 4);
+  L.perm_ws = o; o += round256(permute_ws_bytes(T, E, K));
+  {
+    const size_t g1 = gmm_ws_bytes(MOE_FP8_E4M3, E, (int)A, H, F), g2 = gmm_ws_bytes(MOE_FP8_E4M3, E, (int)A, F, H);
+    L.gmm_ws = o; o += round256(g1 > g2 ? g1 : g2);
+  }
+  L.xq = o; o += round256((size_t)qrows * H);
+  L.xs = o; o += round256((size_t)qrows * 4);
+  const size_t hm = (size_t)A * F * 2, rws = route_ws_bytes(T, H, E, MOE_BF16);
+  L.hm = o; o += round256(hm > rws ? hm : rws);
+  L.hq = o; o += round256((size_t)A * F);
+  L.hs = o; o += round256((size_t)A * 4);
+  L.yp = o; o += round256((size_t)A * H * 2);
+  L.total = o;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -436,6 +471,85 @@ moe_status moe_layer(const void* x, const void* w_router, const float* bias, con
     MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, gws2, s));
     MOE_TRY(launch_combine(xp, dt, pdst, gate, T, K, H, y, s));
   }
+  return MOE_OK;
+}
+
+moe_status moe_layer_fp8_workspace_size(int T, int H, int E, int K, int F, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  MOE_TRY(check_route_shape(T, H, E, K));
+  if (!dim_ok(F)) return MOE_ERR_BAD_SHAPE;
+  *bytes = layer_fp8_ws_layout(T, H, E, K, F).total;
+  return MOE_OK;
+}
+
+moe_status moe_layer_fp8(const void* x, const void* w_router, const float* bias, const uint8_t* w1,
+                         const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T, int H, int E,
+                         int K, int F, moe_act act, void* y, int32_t* topk_idx_out, float* topk_gate_out,
+                         int32_t* counts_out, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_route_shape(T, H, E, K));
+  if (!dim_ok(F)) return MOE_ERR_BAD_SHAPE;
+  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w1_scale);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(w2_scale);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(ws);
+  const LayerFp8Ws L = layer_fp8_ws_layout(T, H, E, K, F);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(w_router);
+  REQUIRE_ALIGNED(bias);
+  REQUIRE_ALIGNED(w1);
+  REQUIRE_ALIGNED(w2);
+  REQUIRE_ALIGNED(y);
+  REQUIRE_ALIGNED(topk_idx_out);
+  REQUIRE_ALIGNED(topk_gate_out);
+  REQUIRE_ALIGNED(counts_out);
+  REQUIRE_ALIGNED(ws);
+
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char* base = (unsigned char*)ws;
+  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(base + L.idx);
+  float* gate = topk_gate_out ? topk_gate_out : (float*)(base + L.gate);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* psrc = (int32_t*)(base + L.psrc);
+  int32_t* pdst = (int32_t*)(base + L.pdst);
+  uint8_t* xq = base + L.xq;
+  float* xs = (float*)(base + L.xs);
+  void* hm = base + L.hm;
+  uint8_t* hq = base + L.hq;
+  float* hs = (float*)(base + L.hs);
+  void* yp = base + L.yp;
+  const int A = T * K;
+  void* gws = base + L.gmm_ws;
+  MOE_TRY(launch_route(x, w_router, MOE_BF16, bias, T, H, E, K, idx, gate, hm, s));
+  MOE_TRY(launch_permute(idx, nullptr, MOE_BF16, T, H, E, K, counts, offsets, psrc, pdst, nullptr,
+                         base + L.perm_ws, s));
+  RowMap r1;
+  r1.row_scale = xs;
+  if ((int64_t)T * H < (1ll << 31)) {
+    // tokens quantised once; GEMM 1 reads row r as token perm_src[r] / K with its scale
+    MOE_TRY(launch_quant_rows(x, MOE_BF16, T, H, nullptr, 1, T, xq, xs, s));
+    r1.src = psrc;
+    r1.div = K;
+    r1.rows = T;
+  } else {
+    // dispatch and quantisation in one pass into A rows
+    MOE_TRY(launch_quant_rows(x, MOE_BF16, T, H, psrc, K, A, xq, xs, s));
+  }
+  MOE_TRY(launch_gmm(xq, MOE_FP8_E4M3, nullptr, w1, w1_scale, offsets, E, A, H, F, act, hm, MOE_BF16,
+                     gmm_ws_bytes(MOE_FP8_E4M3, E, A, H, F) ? gws : nullptr, s, r1));
+  MOE_TRY(launch_quant_rows(hm, MOE_BF16, A, F, nullptr, 1, A, hq, hs, s));
+  RowMap r2;
+  r2.row_scale = hs;
+  MOE_TRY(launch_gmm(hq, MOE_FP8_E4M3, nullptr, w2, w2_scale, offsets, E, A, F, H, MOE_ACT_NONE, yp, MOE_BF16,
+                     gmm_ws_bytes(MOE_FP8_E4M3, E, A, F, H) ? gws : nullptr, s, r2));
+  MOE_TRY(launch_combine(yp, MOE_BF16, pdst, gate, T, K, H, y, s));
   return MOE_OK;
 }
 

@@ -331,6 +331,32 @@ def layer(x, wr, w1, w2, K, bias=None, act=ACT_RELU, nthreads=1):
     return {"y": y, "idx": idx, "gate": gate, "gap": gap, "counts": counts}
 
 
+def layer_fp8(x, wr, w1, w1_scale, w2, w2_scale, K, bias=None, act=ACT_RELU, tokens=None, nthreads=1):
+    """The layer with E4M3 experts and per-token dynamic quantisation
+    ("aclnnQuantGroupedMatMulAlltoAllv": quant mode 7 for the activations,
+    per-tensor weight scales, gmmY = (gmmX @ W) * gmmXScale * wScale), composed
+    from the functions above: route the bf16 tokens, permute, quantise each
+    token, GEMM 1 on the dispatched codes with their tokens' scales, the hidden
+    rows rounded to bf16 (the layer type) and quantised per row, GEMM 2, the
+    weighted combine. Every token is independent, so `tokens` (indices)
+    computes just those tokens. Returns dict with y, idx, gate, gap, counts."""
+    x = np.asarray(x)
+    if tokens is not None:
+        x = x[np.asarray(tokens)]
+    T, H = x.shape
+    E = w1.shape[0]
+    idx, gate, _, gap = route(x, wr, T, H, E, K, bias=bias)
+    counts, off, psrc, pdst = permute(idx, E)
+    xq, xs = quant_rows(x)
+    tok = psrc // K
+    hm = gmm(xq[tok], w1, off, act=act, a_scale=xs[tok].astype(np.float64), w_scale=float(w1_scale),
+             nthreads=nthreads)
+    hq, hs = quant_rows(bf16_bits(hm))
+    yp = gmm(hq, w2, off, a_scale=hs.astype(np.float64), w_scale=float(w2_scale), nthreads=nthreads)
+    y = combine(yp, pdst, gate, T, K)
+    return {"y": y, "idx": idx, "gate": gate, "gap": gap, "counts": counts}
+
+
 def layer_tokens(x, wr, w1, w2, K, tokens, bias=None, act=ACT_RELU, nthreads=1):
     """Per-token form on a subset of tokens. Returns dict with y, idx, gate, gap."""
     x, px = _c(x)

@@ -66,6 +66,18 @@ def layer_inputs(name: str, T: int | None = None, integer: bool = False, H=None,
     return dict(name=name, T=T, H=H, E=E, K=K, F=F, dtype=dt, x=x, wr=wr, w1=w1, w2=w2, bias=b)
 
 
+def layer_fp8_inputs(name: str, **shape) -> dict:
+    """Inputs of the E4M3 layer on a whole-layer workload's shapes: the same
+    seeds, tokens and router in bf16, expert weights drawn in fp32 and
+    quantised per tensor to E4M3 (scale = amax / 448)."""
+    d = layer_inputs(name, dtype="f32", **shape)
+    d["x"], d["wr"] = to_bf16(d["x"]), to_bf16(d["wr"])
+    d["w1"], d["w1_scale"] = quantize_e4m3(d["w1"])
+    d["w2"], d["w2_scale"] = quantize_e4m3(d["w2"])
+    d["dtype"] = "fp8"
+    return d
+
+
 def identity_ffn(H: int, E: int, dtype: str = "f32"):
     """W1 = [I | -I] (H, 2H) and W2 = [I ; -I] (2H, H) for every expert, so
     relu(x) - relu(-x) = x: each expert returns its input."""
@@ -165,5 +177,5 @@ def fp8_dyn_inputs(wid: int = 2, with_shared: bool = True, **shape) -> dict:
 
 
 __all__ = ["LAYER_SHAPES", "FP8_SHAPE", "skew_bias", "layer_inputs", "identity_ffn", "fp8_inputs", "fp8_mx_inputs",
-           "fp8_dyn_inputs", "fp4_mx_inputs",
+           "fp8_dyn_inputs", "fp4_mx_inputs", "layer_fp8_inputs",
            "bf16_to_f32", "amax", "to_e4m3"]

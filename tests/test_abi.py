@@ -26,7 +26,7 @@ def test_header_declares_expected_entry_points():
               "moe_gmm_mxfp4",
               "moe_combine", "moe_sum_slots", "moe_quant_rows", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
-              "moe_layer_workspace_size",
+              "moe_layer_workspace_size", "moe_layer_fp8", "moe_layer_fp8_workspace_size",
               "moe_status_string", "moe_version"):
         assert n in names
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10700
+    assert moe.lib().moe_version() == 10800
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -446,3 +446,35 @@ def test_layer_workspace_size_covers_buffers():
     with pytest.raises(moe.MoeError) as ei:
         moe.layer_workspace_size(T, H, E, 9, F, moe.BF16)
     assert ei.value.status == moe.ERR_BAD_SHAPE
+
+
+def layer_fp8(x=P, wr=P, bias=None, w1=P, s1=P, w2=P, s2=P, T=32, H=64, E=8, K=2, F=96, act=moe.ACT_RELU, y=P,
+              ws=P, ws_bytes=1 << 40):
+    return L.moe_layer_fp8(x, wr, bias, w1, s1, w2, s2, T, H, E, K, F, act, y, None, None, None, ws, ws_bytes,
+                           None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(F=0), moe.ERR_BAD_SHAPE),
+    (dict(K=3, E=2), moe.ERR_BAD_SHAPE),
+    (dict(H=65536), moe.ERR_BAD_SHAPE),
+    (dict(act=3), moe.ERR_UNSUPPORTED),
+    (dict(w1=None), moe.ERR_NULL_POINTER),
+    (dict(s1=None), moe.ERR_NULL_POINTER),
+    (dict(s2=None), moe.ERR_NULL_POINTER),
+    (dict(ws=None), moe.ERR_NULL_POINTER),
+    (dict(ws_bytes=1024), moe.ERR_WORKSPACE_TOO_SMALL),
+    (dict(w2=MIS), moe.ERR_MISALIGNED),
+    (dict(bias=MIS), moe.ERR_MISALIGNED),
+])
+def test_layer_fp8_validation(kw, status):
+    assert layer_fp8(**kw) == status
+
+
+def test_layer_fp8_empty_batch_and_workspace_size():
+    assert layer_fp8(x=None, wr=None, w1=None, s1=None, w2=None, s2=None, y=None, ws=None, T=0) == moe.OK
+    T, H, E, K, F = 4096, 4096, 8, 2, 14336
+    A = T * K
+    n = moe.layer_fp8_workspace_size(T, H, E, K, F)
+    assert n >= T * H + A * F * 3 + A * H * 2 + 4 * A * 4
+

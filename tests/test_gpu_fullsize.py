@@ -225,6 +225,24 @@ def test_fp4_mx_gmm_full_size_sampled_rows():
     assert normwise_err(to_host(gy)[rows], ref) <= 8e-3
 
 
+def test_layer_fp8_full_size_prefill_sampled_tokens():
+    """The E4M3 layer on the prefill shapes (T=4096, H=4096, E=8, K=2, F=14336):
+    sampled tokens against the oracle's E4M3 layer on those tokens."""
+    d = configs.layer_fp8_inputs("prefill")
+    T, K = d["T"], d["K"]
+    sc = lambda v: torch.tensor([float(v)], dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    y = moe.layer_fp8(to_dev(d["x"]), to_dev(d["wr"]), to_dev(d["w1"]), sc(d["w1_scale"]), to_dev(d["w2"]),
+                      sc(d["w2_scale"]), K, topk_idx=idx)
+    torch.cuda.synchronize()
+    tokens = np.random.default_rng(670).choice(T, 12, replace=False)
+    ref = oracle.layer_fp8(d["x"], d["wr"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"], K, tokens=tokens,
+                           nthreads=NTH)
+    ok = ref["gap"] > GAP
+    assert np.array_equal(to_host(idx)[tokens][ok], ref["idx"][ok])
+    assert normwise_err(to_host(y)[tokens][ok], ref["y"][ok]) <= 2e-2
+
+
 def test_combine_full_size_prefill():
     T, E, K, H = 4096, 8, 2, 4096
     idx = synth.random_routing(630, T, E, K)

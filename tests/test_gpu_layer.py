@@ -10,6 +10,7 @@ import torch
 
 import mixture_experts_layer_06_amd as moe
 import oracle
+import synth
 from synth import configs
 from tests.helpers import GAP, TOL, normwise_err, to_dev, to_host
 
@@ -101,3 +102,40 @@ def test_layer_deterministic():
     y1 = run_layer(d)[0]
     y2 = run_layer(d)[0]
     assert np.array_equal(y1, y2)
+
+
+# ---------------------------------------------------------------- E4M3 layer
+
+def _run_layer_fp8(d):
+    T, E, K = d["T"], d["E"], d["K"]
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    sc = lambda v: torch.tensor([float(v)], dtype=torch.float32, device="cuda")
+    y = moe.layer_fp8(to_dev(d["x"]), to_dev(d["wr"]), to_dev(d["w1"]), sc(d["w1_scale"]), to_dev(d["w2"]),
+                      sc(d["w2_scale"]), K, bias=None if d["bias"] is None else to_dev(d["bias"]),
+                      topk_idx=idx, topk_gate=gate, counts=counts)
+    torch.cuda.synchronize()
+    return to_host(y), to_host(idx), to_host(gate), to_host(counts)
+
+
+@pytest.mark.parametrize("name,shape", [("tiny", dict(T=64)), ("prefill", dict(T=300, H=512, F=1024)),
+                                        ("skewed", dict(T=400, H=256, F=384)),
+                                        ("decode", dict(T=16, H=512, F=256))])
+def test_layer_fp8_parity(name, shape):
+    """E4M3 experts with per-token dynamic quantisation: routing as the
+    oracle's (where the gap decides it), y against the oracle's E4M3 layer,
+    and against the unquantised layer on the same weights within the fp8 bar."""
+    d = configs.layer_fp8_inputs(name, **shape)
+    y, idx, gate, counts = _run_layer_fp8(d)
+    ref = oracle.layer_fp8(d["x"], d["wr"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"], d["K"],
+                           bias=d["bias"], nthreads=8)
+    ok = ref["gap"] > GAP
+    assert np.array_equal(idx[ok], ref["idx"][ok])
+    assert normwise_err(y[ok], ref["y"][ok]) <= 2e-2
+    w1f = oracle.decode(d["w1"]) * float(d["w1_scale"])
+    w2f = oracle.decode(d["w2"]) * float(d["w2_scale"])
+    plain = oracle.layer(synth.bf16_to_f32(d["x"]), synth.bf16_to_f32(d["wr"]), w1f.astype(np.float32),
+                         w2f.astype(np.float32), d["K"], bias=d["bias"], nthreads=8)
+    assert normwise_err(y[ok], plain["y"][ok]) <= TOL["fp8"]
+

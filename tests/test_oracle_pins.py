@@ -657,3 +657,19 @@ def test_quantize_mx4_recipe_roundtrip():
     step = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=1)
     deq = vals * step
     assert np.all(np.abs(deq - x) <= 0.25 * np.abs(x) + 0.25 * step + 1e-30)
+
+
+def test_layer_fp8_composition():
+    """The E4M3 layer: token subsets give the same rows as the whole batch
+    (every step is per token), and the result stays within the fp8 bar of the
+    unquantised layer on the same (dequantised) weights."""
+    d = configs.layer_fp8_inputs("tiny", T=48)
+    full = oracle.layer_fp8(d["x"], d["wr"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"], d["K"])
+    sub = np.array([3, 17, 40, 0])
+    part = oracle.layer_fp8(d["x"], d["wr"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"], d["K"], tokens=sub)
+    assert np.array_equal(part["y"], full["y"][sub]) and np.array_equal(part["idx"], full["idx"][sub])
+    w1f = (oracle.decode(d["w1"]) * float(d["w1_scale"])).astype(np.float32)
+    w2f = (oracle.decode(d["w2"]) * float(d["w2_scale"])).astype(np.float32)
+    plain = oracle.layer(synth.bf16_to_f32(d["x"]), synth.bf16_to_f32(d["wr"]), w1f, w2f, d["K"])
+    err = np.abs(full["y"] - plain["y"]).max() / np.abs(plain["y"]).max()
+    assert err <= 6e-2
