@@ -11,9 +11,9 @@
 // permute and the quantisation in one pass (x_perm in E4M3 plus its
 // per-row scales, the form gmmX and gmmXScale take on that page).
 //
-// HBM-bound: one wave per output row reads the row once (rows up to 7168
-// bf16 or 4096 fp32 values stay in registers; longer ones are read again from
-// L2), writes one byte per element and one scale.
+// HBM-bound: one wave per output row reads the row once (rows up to 14336
+// bf16 or 4096 fp32 values stay in registers in their input encoding; longer
+// ones are read again from L2), writes one byte per element and one scale.
 #include "common.h"
 
 namespace moe {
@@ -41,23 +41,39 @@ __device__ __forceinline__ float load_elem(const void* x, int64_t i) {
   return reinterpret_cast<const float*>(x)[i];
 }
 
-// 8 consecutive elements starting at i (i a multiple of 8, 16-byte aligned rows)
+// 8 consecutive elements starting at i (i a multiple of 8, 16-byte aligned
+// rows), as raw words: bf16 fills raw[0], fp32 raw[0] and raw[1].
 template <bool BF16>
-__device__ __forceinline__ void load8(const void* x, int64_t i, float v[8]) {
+__device__ __forceinline__ void load8_raw(const void* x, int64_t i, uint4 raw[2]) {
   if (BF16) {
-    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(x) + i);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    raw[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(x) + i);
+  } else {
+    raw[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + i);
+    raw[1] = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + i + 4);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const uint4 raw[2], float v[8]) {
+  if (BF16) {
+    const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       v[2 * k] = __uint_as_float(w[k] << 16);
       v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
     }
   } else {
-    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i);
-    const float4 c = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(w[k]);
   }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* x, int64_t i, float v[8]) {
+  uint4 raw[2];
+  load8_raw<BF16>(x, i, raw);
+  unpack8<BF16>(raw, v);
 }
 
 // Codes of 8 values, packed little-endian into two words.
@@ -87,7 +103,7 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int x_rows, int H,
                                                          const int32_t* __restrict__ src, int div, int rows,
                                                          uint8_t* __restrict__ q, float* __restrict__ scale) {
-  constexpr int kCh = BF16 ? 14 : 8;  // register-held chunks of 8 elements per lane
+  constexpr int kCh = BF16 ? 28 : 8;  // register-held chunks of 8 elements per lane
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -95,15 +111,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
   uint8_t* qr = q + (int64_t)r * H;
   const int64_t base = (int64_t)(t >= 0 ? t : 0) * H;
   if (VEC && H <= kCh * 512) {
-    float v[kCh][8];
+    uint4 raw[kCh][BF16 ? 1 : 2];  // the row in its input encoding
     float amax = 0.f;
 #pragma unroll
     for (int c = 0; c < kCh; ++c) {
       const int h = (c * 64 + lane) * 8;
       if (t >= 0 && h < H) {
-        load8<BF16>(x, base + h, v[c]);
+        uint4 r2[2];
+        load8_raw<BF16>(x, base + h, r2);
+        raw[c][0] = r2[0];
+        if (!BF16) raw[c][BF16 ? 0 : 1] = r2[1];
+        float v[8];
+        unpack8<BF16>(r2, v);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[c][k]));
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
       }
     }
     amax = wave_max(amax);
@@ -113,7 +134,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 #pragma unroll
     for (int c = 0; c < kCh; ++c) {
       const int h = (c * 64 + lane) * 8;
-      if (h < H) *reinterpret_cast<uint2*>(qr + h) = zero ? make_uint2(0u, 0u) : e4m3_pack8(v[c], inv);
+      if (h < H) {
+        uint2 o = make_uint2(0u, 0u);
+        if (!zero) {
+          uint4 r2[2];
+          r2[0] = raw[c][0];
+          if (!BF16) r2[1] = raw[c][BF16 ? 0 : 1];
+          float v[8];
+          unpack8<BF16>(r2, v);
+          o = e4m3_pack8(v, inv);
+        }
+        *reinterpret_cast<uint2*>(qr + h) = o;
+      }
     }
     return;
   }

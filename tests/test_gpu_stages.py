@@ -437,7 +437,8 @@ def _rows_with_spread(seed, shape, dt):
 
 @pytest.mark.parametrize("dt,T,H", [("bf16", 300, 7168), ("bf16", 70, 36), ("f32", 129, 100),
                                     ("f32", 64, 2048), ("bf16", 5, 8),
-                                    ("bf16", 33, 8200), ("f32", 20, 4104)])  # rows read twice
+                                    ("bf16", 33, 14336), ("bf16", 9, 14400),
+                                    ("f32", 20, 4104)])  # the last two: rows read twice
 def test_quant_rows_bit_exact(dt, T, H):
     """Codes and scales equal the oracle's bit for bit (same binary32 steps)."""
     x = _rows_with_spread(800 + H, (T, H), dt)
