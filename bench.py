@@ -565,6 +565,7 @@ def bench_layer_fp8(args, dev):
     counts = bufs["counts"].cpu().numpy().tolist()
     fl1, by1 = flops_bytes_gmm(counts, H, F, 1)
     fl2, by2 = flops_bytes_gmm(counts, F, H, 1)
+    by1, by2 = by1 + A * 4, by2 + A * 4  # one fp32 scale per activation row
     gmm_ms = (per["gmm1"] + per["gmm2"]) / 2.0
     fl_launch = (fl1 + fl2) / 2.0
     achieved = fl_launch / (gmm_ms * 1e-3) / 1e12
@@ -583,7 +584,7 @@ def bench_layer_fp8(args, dev):
                                "dynamic activation quantisation", "T": T, "H": H, "E": E, "K": K, "F": F,
                    "tokens_per_step": T, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": measured_traffic("prefill_fp8"),
                      "kernel": "moe_gmm E4M3, per-token scales (gmm_pp8_kernel)", "gmm_source": source_digest(),
                      "launches_per_step": 2, "flops_per_launch": fl_launch,
                      "bytes_per_launch": (by1 + by2) / 2.0, "avg_launch_ms": gmm_ms},
