@@ -354,6 +354,7 @@ def bench_fp8(args, dev, mode="pt"):
     import torch
 
     import mixture_experts_layer_06_amd as moe
+    import synth
     from synth import configs
 
     fp4 = mode == "mx4"
@@ -367,7 +368,7 @@ def bench_fp8(args, dev, mode="pt"):
     gx = host_to_dev(d["gmm_x"], dev)
     gw = host_to_dev(d["gmm_w"], dev)
     if use_mx:
-        sx = host_to_dev(d["gmm_x_scale"], dev)
+        sx = host_to_dev(synth.mx_scales_slice_major(d["gmm_x_scale"], 8 if fp4 else 4), dev)
         sw = host_to_dev(d["gmm_w_scale"], dev)
     elif dyn:
         qx = torch.empty((A, H1), dtype=torch.float8_e4m3fn, device=dev)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10800 /* 1.8.0: moe_layer_fp8 (E4M3 experts, per-token dynamic activation quantisation) */
+#define MOE_VERSION 10900 /* 1.9.0: MX activation scales stored slice-major */
 
 typedef enum {
   MOE_OK = 0,
@@ -224,11 +224,14 @@ moe_status moe_gmm_scatter(const void* a, moe_dtype a_dt, moe_quant_mode a_q, co
  * consecutive reduction elements of an activation row and of a weight column
  * share one E8M0 scale byte s, value 2^(s-127) (255: NaN), the OCP MX
  * reading of the page's mx mode:
- *   out[r,n] = act( sum_b 2^(a_scale[r,b]-127) * 2^(w_scale[ex,b,n]-127)
+ *   out[r,n] = act( sum_b 2^(sa(r,b)-127) * 2^(w_scale[ex,b,n]-127)
  *                   * sum_{32b <= h < 32b+32} a[r,h] * w[ex,h,n] )
  * for offsets[ex] <= r < offsets[ex+1]; one rounding to bf16.
  *   a        device (A,Hin) E4M3 bytes, rows grouped by expert
- *   a_scale  device (A, Hin/32) E8M0 bytes
+ *   a_scale  device E8M0 bytes, slice-major: sa(r,b) is byte
+ *            ((b/4)*A + r)*4 + b%4, i.e. (Hin/128, A, 4): for each 128-deep
+ *            slice of the reduction, every row's 4 block scales, rows
+ *            consecutive (the kernel then fetches contiguous bytes)
  *   w        device (e,Hin,N) E4M3 bytes, N contiguous
  *   w_scale  device (e, Hin/32, N) E8M0 bytes
  *   offsets, e, A, act   as for moe_gmm
@@ -249,7 +252,9 @@ moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, cons
  *   a       device (A, Hin/2) bytes: byte (r, k) holds a[r,2k] and a[r,2k+1]
  *   w       device (e, Hin/2, N) bytes: byte (ex, k, n) holds w[ex,2k,n] and
  *           w[ex,2k+1,n]
- *   a_scale device (A, Hin/32) E8M0 bytes; w_scale device (e, Hin/32, N)
+ *   a_scale device E8M0 bytes, slice-major with 256-deep slices: sa(r,b) is
+ *           byte ((b/8)*A + r)*8 + b%8, i.e. (Hin/256, A, 8)
+ *   w_scale device (e, Hin/32, N) E8M0 bytes
  *   out     device (A,N) bf16
  * Hin must be a multiple of 256 and N of 16 (else MOE_ERR_UNSUPPORTED).
  * Arithmetic, offsets, act and errors as moe_gmm_mx.

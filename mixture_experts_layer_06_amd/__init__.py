@@ -237,7 +237,8 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=No
 
 def gmm_mx(a, a_scale, w, w_scale, offsets, act=ACT_NONE, out=None, stream=None):
     """moe_gmm_mx: E4M3 a (A,Hin) and w (e,Hin,N) with E8M0 block scales a_scale
-    (A,Hin/32) and w_scale (e,Hin/32,N) (uint8 device tensors); bf16 output."""
+    (slice-major, (Hin/128, A, 4)) and w_scale (e,Hin/32,N) (uint8 device
+    tensors); bf16 output."""
     A, Hin = a.shape
     e, Hw, N = w.shape
     if Hw != Hin:
@@ -252,8 +253,8 @@ def gmm_mx(a, a_scale, w, w_scale, offsets, act=ACT_NONE, out=None, stream=None)
 
 def gmm_mxfp4(a, a_scale, w, w_scale, offsets, act=ACT_NONE, out=None, stream=None):
     """moe_gmm_mxfp4: E2M1 a (A, Hin/2) and w (e, Hin/2, N) packed bytes (two
-    values per byte along Hin), E8M0 scales a_scale (A, Hin/32) and w_scale
-    (e, Hin/32, N) (uint8 device tensors); bf16 output."""
+    values per byte along Hin), E8M0 scales a_scale (slice-major, (Hin/256, A,
+    8)) and w_scale (e, Hin/32, N) (uint8 device tensors); bf16 output."""
     A, Hh = a.shape
     e, Hw, N = w.shape
     if Hw != Hh:

@@ -1170,11 +1170,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
                                 (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)rowb);
   const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * rowb * N, (uint32_t)rowb * (uint32_t)N);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // MX scales (whole slices): kBlk E8M0 blocks per row and slice. Waves 0-3
-  // fetch the activation rows' scales (one row per lane, 4 blocks per op),
-  // the next kBlk/2 waves the weight columns' (32 lanes per block, 2 blocks
-  // per op); every other op is an out-of-range one into the dummy KB, so
-  // that every wave counts kSDma ops per slice.
+  // MX scales (whole slices): kBlk E8M0 blocks per row and slice. Activation
+  // scales are stored slice-major, (Hin/32/kBlk, A, kBlk): a slice's scales
+  // of consecutive rows are consecutive, so waves 0-3 (one row per lane, 4
+  // blocks per op) each read 256 contiguous bytes; the next kBlk/2 waves
+  // fetch the weight columns' (32 lanes per block, 2 blocks per op); every
+  // other op is an out-of-range one into the dummy KB, so that every wave
+  // counts kSDma ops per slice.
   const int nbk = Hin / 32;
   u32x4_t ssrd = {0u, 0u, 0u, 0u};
   uint32_t s_voff = kOOB, s_lds = lds0 + C::kDummy, s_step = 0;
@@ -1182,10 +1184,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   if (MX) {
     if (wave < 4) {
       const int m = 64 * wave + lane;
-      ssrd = make_srd(a_mx + (int64_t)tile.row0 * nbk, (uint32_t)tile.rows * (uint32_t)nbk);
-      s_voff = m < tile.rows ? (uint32_t)m * (uint32_t)nbk : kOOB;
+      ssrd = make_srd(a_mx, (uint32_t)A * (uint32_t)nbk);
+      s_voff = m < tile.rows ? (uint32_t)(tile.row0 + m) * (uint32_t)C::kBlk : kOOB;
       s_lds = C::kScA + wave * 256;
-      s_step = C::kBlk;
+      s_step = (uint32_t)A * (uint32_t)C::kBlk;
       s_real = true;
     } else if (wave < 4 + C::kBlk / 2) {
       const int bb = (64 * (wave - 4) + lane) / 32, col = tile.n0 + 4 * (lane % 32);

@@ -195,6 +195,16 @@ def quantize_mx4(a: np.ndarray, axis: int):
     return (np.ascontiguousarray(np.moveaxis(packed, -1, axis)), np.ascontiguousarray(np.moveaxis(sb, -1, axis)))
 
 
+def mx_scales_slice_major(sa: np.ndarray, per_slice: int) -> np.ndarray:
+    """Rearrange activation block scales (A, nb) into the slice-major order the
+    MX grouped GEMMs read: (nb/per_slice, A, per_slice), every row's scales of
+    one reduction slice adjacent and rows consecutive."""
+    A, nb = sa.shape
+    if nb % per_slice:
+        raise ValueError("mx_scales_slice_major: blocks per row must be a multiple of the slice")
+    return np.ascontiguousarray(np.asarray(sa, np.uint8).reshape(A, nb // per_slice, per_slice).transpose(1, 0, 2))
+
+
 def random_routing(seed: int, T: int, E: int, K: int) -> np.ndarray:
     out = np.empty((T, K), np.int32)
     if lib().synth_random_routing(seed, T, E, K, _ptr(out)) != 0:

@@ -177,7 +177,7 @@ def test_fp8_mx_gmm_full_size_sampled_rows():
     e = d["e"]
     counts, offsets, _, _ = oracle.permute(d["topk_idx"], e)
     perm = moe.permute(to_dev(d["topk_idx"]), e)
-    gy = moe.gmm_mx(to_dev(d["gmm_x"]), to_dev(d["gmm_x_scale"]), to_dev(d["gmm_w"]),
+    gy = moe.gmm_mx(to_dev(d["gmm_x"]), to_dev(synth.mx_scales_slice_major(d["gmm_x_scale"], 4)), to_dev(d["gmm_w"]),
                     to_dev(d["gmm_w_scale"]), perm["offsets"])
     torch.cuda.synchronize()
     rows = _boundary_rows(offsets, 24, 640)
@@ -216,7 +216,8 @@ def test_fp4_mx_gmm_full_size_sampled_rows():
     e = d["e"]
     counts, offsets, _, _ = oracle.permute(d["topk_idx"], e)
     perm = moe.permute(to_dev(d["topk_idx"]), e)
-    gy = moe.gmm_mxfp4(to_dev(d["gmm_x"]), to_dev(d["gmm_x_scale"]), to_dev(d["gmm_w"]),
+    gy = moe.gmm_mxfp4(to_dev(d["gmm_x"]), to_dev(synth.mx_scales_slice_major(d["gmm_x_scale"], 8)),
+                       to_dev(d["gmm_w"]),
                        to_dev(d["gmm_w_scale"]), perm["offsets"])
     torch.cuda.synchronize()
     rows = _boundary_rows(offsets, 24, 660)
