@@ -139,3 +139,21 @@ def test_layer_fp8_parity(name, shape):
                          w2f.astype(np.float32), d["K"], bias=d["bias"], nthreads=8)
     assert normwise_err(y[ok], plain["y"][ok]) <= TOL["fp8"]
 
+
+
+def test_layer_fp8_forced_empty_experts_odd_batch_and_determinism():
+    """E4M3 layer with experts 5.. forced empty by the bias, a batch that is not
+    a multiple of the 16-token tiles, and two runs bit-identical."""
+    d = configs.layer_fp8_inputs("tiny", T=37)
+    b = np.zeros(d["E"], np.float32)
+    b[5:] = -1e4
+    d["bias"] = b
+    y1, idx, gate, counts = _run_layer_fp8(d)
+    y2, _, _, _ = _run_layer_fp8(d)
+    assert counts[5:].sum() == 0 and counts.sum() == d["T"] * d["K"]
+    assert np.array_equal(y1, y2)
+    ref = oracle.layer_fp8(d["x"], d["wr"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"], d["K"], bias=b,
+                           nthreads=8)
+    ok = ref["gap"] > GAP
+    assert np.array_equal(idx[ok], ref["idx"][ok])
+    assert normwise_err(y1[ok], ref["y"][ok]) <= 2e-2
