@@ -1136,6 +1136,10 @@ struct Pp8Cfg {
 // row m holds 16-byte chunk c at position c ^ (2*((m/2)%4)), weight K row k
 // holds output-column chunk c at position c ^ ((k/2)%4 + 4*((k/16)%2)).
 __device__ __forceinline__ int pp8_xswz(int m) { return 2 * ((m >> 1) & 3); }
+// Tile row held by LDS activation row q: within each 64-row group, LDS row
+// 16i + c (fragment i, lane c) holds tile row 4c + i, so the four rows a
+// lane multiplies are adjacent (one 16-byte read then fetches their scales).
+__device__ __forceinline__ int pp8_trow(int q) { return (q & ~63) | ((q & 15) << 2) | ((q >> 4) & 3); }
 __device__ __forceinline__ int pp8_wswz(int k) { return ((k >> 1) & 3) | (((k >> 4) & 1) << 2); }
 
 template <bool MX, bool FP4 = false>
@@ -1208,7 +1212,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int kb = (wave * C::kADma + q) * 1024 + lane * 16;
     const int prow = kb >> 7, pc = (kb >> 4) & 7;
     const int lc = pc ^ pp8_xswz(prow);
-    const int src = prow >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + prow) : prow;
+    const int trow = pp8_trow(prow);
+    const int src = trow >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + trow) : trow;
     a_voff[q] = (src >= 0 ? (uint32_t)src * (uint32_t)rowb : kOOB) + lc * 16;
     a_kc[q] = lc * 16;
   }
@@ -1260,7 +1265,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   if (gx.dst != nullptr && wave_active) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
+      const int ml = half * 128 + wm2 * 64 + 4 * ci + i;
       dpre[i] = ml < tile.rows ? gx.dst[tile.row0 + ml] : -1;
     }
   }
@@ -1269,7 +1274,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   if (gx.row_scale != nullptr && wave_active) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
+      const int ml = half * 128 + wm2 * 64 + 4 * ci + i;
       rpre[i] = ml < tile.rows ? row_scale_of(gx, tile.row0 + ml) : 0.f;
     }
   }
@@ -1315,9 +1320,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     if (MX) {
 #pragma unroll
       for (int u = 0; u < C::kBlk / 4; ++u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sxa[u][i] = st[C::kScA + u * C::kBM * 4 + (half * 128 + wm2 * 64 + i * 16 + ci) * 4 + kq];
+        {  // this lane's four rows are adjacent: one 16-byte read, then block kq of each
+          const uint4 r4 = *reinterpret_cast<const uint4*>(st + C::kScA + u * C::kBM * 4 +
+                                                           (half * 128 + wm2 * 64 + 4 * ci) * 4);
+          sxa[u][0] = (int)(r4.x >> (8 * kq));
+          sxa[u][1] = (int)(r4.y >> (8 * kq));
+          sxa[u][2] = (int)(r4.z >> (8 * kq));
+          sxa[u][3] = (int)(r4.w >> (8 * kq));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) sxw[u][j] = st[C::kScW + (4 * u + kq) * C::kBN + wn * 64 + 16 * j + ci];
       }
@@ -1416,7 +1426,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const float sc = ld_scale(a_scale) * ld_scale(w_scale);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ml = half * 128 + wm2 * 64 + i * 16 + ci;
+    const int ml = half * 128 + wm2 * 64 + 4 * ci + i;
     if (ml >= tile.rows) continue;
     const OutRow orow = out_row_of(gx, tile.row0 + ml, dpre[i], A);
     if (orow.row < 0) continue;
