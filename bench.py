@@ -369,7 +369,7 @@ def bench_fp8(args, dev, mode="pt"):
     gw = host_to_dev(d["gmm_w"], dev)
     if use_mx:
         sx = host_to_dev(synth.mx_scales_slice_major(d["gmm_x_scale"], 8 if fp4 else 4), dev)
-        sw = host_to_dev(d["gmm_w_scale"], dev)
+        sw = host_to_dev(synth.mx_weight_scales_interleaved(d["gmm_w_scale"]), dev)
     elif dyn:
         qx = torch.empty((A, H1), dtype=torch.float8_e4m3fn, device=dev)
         sx = torch.empty((A,), dtype=torch.float32, device=dev)

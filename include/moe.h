@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10900 /* 1.9.0: MX activation scales stored slice-major */
+#define MOE_VERSION 11000 /* 1.10.0: MX weight scales in interleaved column order */
 
 typedef enum {
   MOE_OK = 0,
@@ -224,7 +224,7 @@ moe_status moe_gmm_scatter(const void* a, moe_dtype a_dt, moe_quant_mode a_q, co
  * consecutive reduction elements of an activation row and of a weight column
  * share one E8M0 scale byte s, value 2^(s-127) (255: NaN), the OCP MX
  * reading of the page's mx mode:
- *   out[r,n] = act( sum_b 2^(sa(r,b)-127) * 2^(w_scale[ex,b,n]-127)
+ *   out[r,n] = act( sum_b 2^(sa(r,b)-127) * 2^(sw(ex,b,n)-127)
  *                   * sum_{32b <= h < 32b+32} a[r,h] * w[ex,h,n] )
  * for offsets[ex] <= r < offsets[ex+1]; one rounding to bf16.
  *   a        device (A,Hin) E4M3 bytes, rows grouped by expert
@@ -233,7 +233,11 @@ moe_status moe_gmm_scatter(const void* a, moe_dtype a_dt, moe_quant_mode a_q, co
  *            slice of the reduction, every row's 4 block scales, rows
  *            consecutive (the kernel then fetches contiguous bytes)
  *   w        device (e,Hin,N) E4M3 bytes, N contiguous
- *   w_scale  device (e, Hin/32, N) E8M0 bytes
+ *   w_scale  device E8M0 bytes (e, Hin/32, N64), N64 = N rounded up to a
+ *            multiple of 64, columns interleaved within each group of 64:
+ *            sw(ex,b,n) is byte (ex*(Hin/32) + b)*N64 + (n & ~63) + 4*(n%16)
+ *            + (n%64)/16, so the scales of columns c, c+16, c+32, c+48 are
+ *            adjacent (the padding bytes are not read)
  *   offsets, e, A, act   as for moe_gmm
  *   out      device (A,N) bf16
  * Hin must be a multiple of 128 and N of 16 (else MOE_ERR_UNSUPPORTED). No
@@ -254,7 +258,7 @@ moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, cons
  *           w[ex,2k+1,n]
  *   a_scale device E8M0 bytes, slice-major with 256-deep slices: sa(r,b) is
  *           byte ((b/8)*A + r)*8 + b%8, i.e. (Hin/256, A, 8)
- *   w_scale device (e, Hin/32, N) E8M0 bytes
+ *   w_scale device E8M0 bytes, the interleaved (e, Hin/32, N64) order of moe_gmm_mx
  *   out     device (A,N) bf16
  * Hin must be a multiple of 256 and N of 16 (else MOE_ERR_UNSUPPORTED).
  * Arithmetic, offsets, act and errors as moe_gmm_mx.

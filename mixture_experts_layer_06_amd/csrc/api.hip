@@ -312,7 +312,7 @@ moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, cons
   if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
   // 128-deep K slices of whole scale blocks, 16-byte column chunks, 32-bit offsets
   if (Hin % 128 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)Hin * N >= (1ll << 31) || (int64_t)(Hin / 32) * N * e >= (1ll << 31) ||
+  if ((int64_t)Hin * N >= (1ll << 31) || (int64_t)(Hin / 32) * ((N + 63) & ~63) * e >= (1ll << 31) ||
       (int64_t)(Hin / 32) * A >= (1ll << 31))
     return MOE_ERR_UNSUPPORTED;
   if (A == 0) return MOE_OK;
@@ -371,7 +371,7 @@ moe_status moe_gmm_mxfp4(const void* a, const uint8_t* a_scale, const void* w, c
   if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
   // 256-deep K slices (128 bytes) of whole scale blocks, 16-byte column chunks, 32-bit offsets
   if (Hin % 256 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)(Hin / 2) * N >= (1ll << 31) || (int64_t)(Hin / 32) * N * e >= (1ll << 31) ||
+  if ((int64_t)(Hin / 2) * N >= (1ll << 31) || (int64_t)(Hin / 32) * ((N + 63) & ~63) * e >= (1ll << 31) ||
       (int64_t)(Hin / 32) * A >= (1ll << 31))
     return MOE_ERR_UNSUPPORTED;
   if (A == 0) return MOE_OK;

@@ -1194,11 +1194,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
       s_step = (uint32_t)A * (uint32_t)C::kBlk;
       s_real = true;
     } else if (wave < 4 + C::kBlk / 2) {
+      // weight scales in interleaved column order, rows of N64 = N rounded
+      // up to 64: position 4c + j of a 64-column group holds column 16j + c
+      const int n64 = (N + 63) & ~63;
       const int bb = (64 * (wave - 4) + lane) / 32, col = tile.n0 + 4 * (lane % 32);
-      ssrd = make_srd(w_mx + (int64_t)tile.ex * nbk * N, (uint32_t)nbk * (uint32_t)N);
-      s_voff = (uint32_t)bb * (uint32_t)N + (uint32_t)col + (col < N ? 0u : kOOB);
+      ssrd = make_srd(w_mx + (int64_t)tile.ex * nbk * n64, (uint32_t)nbk * (uint32_t)n64);
+      s_voff = (uint32_t)bb * (uint32_t)n64 + (uint32_t)col + (col < n64 ? 0u : kOOB);
       s_lds = C::kScW + (wave - 4) * 256;
-      s_step = (uint32_t)C::kBlk * (uint32_t)N;
+      s_step = (uint32_t)C::kBlk * (uint32_t)n64;
       s_real = true;
     } else {
       ssrd = make_srd(a_mx, 4u);
@@ -1328,8 +1331,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
           sxa[u][2] = (int)(r4.z >> (8 * kq));
           sxa[u][3] = (int)(r4.w >> (8 * kq));
         }
+        {  // columns 16j + ci (j = 0..3) of block kq: one 4-byte read of the interleaved row
+          const uint32_t c4 = *reinterpret_cast<const uint32_t*>(st + C::kScW + (4 * u + kq) * C::kBN + wn * 64 + 4 * ci);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sxw[u][j] = st[C::kScW + (4 * u + kq) * C::kBN + wn * 64 + 16 * j + ci];
+          for (int j = 0; j < 4; ++j) sxw[u][j] = (int)(c4 >> (8 * j));
+        }
       }
     }
   };

@@ -205,6 +205,18 @@ def mx_scales_slice_major(sa: np.ndarray, per_slice: int) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(sa, np.uint8).reshape(A, nb // per_slice, per_slice).transpose(1, 0, 2))
 
 
+def mx_weight_scales_interleaved(sw: np.ndarray) -> np.ndarray:
+    """Rearrange weight block scales (e, nb, N) into the order the MX grouped
+    GEMMs read: N padded to N64 (a multiple of 64) and, within each group of
+    64 columns, column 16j + c stored at position 4c + j."""
+    e, nb, N = sw.shape
+    n64 = (N + 63) // 64 * 64
+    pad = np.zeros((e, nb, n64), np.uint8)
+    pad[:, :, :N] = sw
+    g = pad.reshape(e, nb, n64 // 64, 4, 16)           # [.., group, j, c]
+    return np.ascontiguousarray(g.transpose(0, 1, 2, 4, 3).reshape(e, nb, n64))  # position 4c + j
+
+
 def random_routing(seed: int, T: int, E: int, K: int) -> np.ndarray:
     out = np.empty((T, K), np.int32)
     if lib().synth_random_routing(seed, T, E, K, _ptr(out)) != 0:

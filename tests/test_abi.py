@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 10900
+    assert moe.lib().moe_version() == 11000
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)

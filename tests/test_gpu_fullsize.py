@@ -178,7 +178,7 @@ def test_fp8_mx_gmm_full_size_sampled_rows():
     counts, offsets, _, _ = oracle.permute(d["topk_idx"], e)
     perm = moe.permute(to_dev(d["topk_idx"]), e)
     gy = moe.gmm_mx(to_dev(d["gmm_x"]), to_dev(synth.mx_scales_slice_major(d["gmm_x_scale"], 4)), to_dev(d["gmm_w"]),
-                    to_dev(d["gmm_w_scale"]), perm["offsets"])
+                    to_dev(synth.mx_weight_scales_interleaved(d["gmm_w_scale"])), perm["offsets"])
     torch.cuda.synchronize()
     rows = _boundary_rows(offsets, 24, 640)
     ref = oracle.gmm_mx(d["gmm_x"], d["gmm_x_scale"], d["gmm_w"], d["gmm_w_scale"], offsets, rows=rows,
@@ -218,7 +218,7 @@ def test_fp4_mx_gmm_full_size_sampled_rows():
     perm = moe.permute(to_dev(d["topk_idx"]), e)
     gy = moe.gmm_mxfp4(to_dev(d["gmm_x"]), to_dev(synth.mx_scales_slice_major(d["gmm_x_scale"], 8)),
                        to_dev(d["gmm_w"]),
-                       to_dev(d["gmm_w_scale"]), perm["offsets"])
+                       to_dev(synth.mx_weight_scales_interleaved(d["gmm_w_scale"])), perm["offsets"])
     torch.cuda.synchronize()
     rows = _boundary_rows(offsets, 24, 660)
     ref = oracle.gmm_mx4(d["gmm_x"], d["gmm_x_scale"], d["gmm_w"], d["gmm_w_scale"], offsets, rows=rows,

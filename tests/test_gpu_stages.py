@@ -578,7 +578,7 @@ def test_gmm_mx_parity(case, act):
     a, sa = synth.quantize_mx(synth.normal(seed, (A, Hin)), axis=1)
     w, sw = synth.quantize_mx(synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin)), axis=1)
     ref = oracle.gmm_mx(a, sa, w, sw, off, act=act, nthreads=8)
-    out = to_host(moe.gmm_mx(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w), to_dev(sw), to_dev(off), act=act))
+    out = to_host(moe.gmm_mx(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w), to_dev(synth.mx_weight_scales_interleaved(sw)), to_dev(off), act=act))
     err = normwise_err(out, ref)
     assert err <= TOL["fp8"] and err <= 8e-3, f"{name}: normwise err {err:.3e}"
 
@@ -599,7 +599,7 @@ def test_gmm_mx_integer_inputs_bit_exact():
     sw = _mx_scales(rng, (e, Hin // 32, N))
     ref = oracle.gmm_mx(a, sa, w, sw, off, act=moe.ACT_RELU, nthreads=8)
     assert np.abs(ref).max() < 2 ** 24
-    out = to_host(moe.gmm_mx(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w), to_dev(sw), to_dev(off), act=moe.ACT_RELU))
+    out = to_host(moe.gmm_mx(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w), to_dev(synth.mx_weight_scales_interleaved(sw)), to_dev(off), act=moe.ACT_RELU))
     assert np.array_equal(out, oracle.bf16_bits(ref))
 
 
@@ -616,7 +616,7 @@ def test_gmm_mx_unit_scales_match_per_tensor_path():
     sa = np.full((A, Hin // 32), 127, np.uint8)
     sw = np.full((e, Hin // 32, N), 127, np.uint8)
     one = torch.ones(1, dtype=torch.float32, device="cuda")
-    mx = to_host(moe.gmm_mx(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w), to_dev(sw), to_dev(off)))
+    mx = to_host(moe.gmm_mx(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w), to_dev(synth.mx_weight_scales_interleaved(sw)), to_dev(off)))
     pt = to_host(moe.gmm(to_dev(a), to_dev(w), to_dev(off), a_scale=one, w_scale=one))
     assert np.array_equal(mx, pt)
 
@@ -644,7 +644,7 @@ def _mx4_case(name, counts, Hin, N, seed):
 def test_gmm_mxfp4_parity(case, act):
     name, counts, Hin, N = case
     off, a, sa, w, sw = _mx4_case(name, counts, Hin, N, 860 + len(name))
-    out = to_host(moe.gmm_mxfp4(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 8)), to_dev(w), to_dev(sw), to_dev(off), act=act))
+    out = to_host(moe.gmm_mxfp4(to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 8)), to_dev(w), to_dev(synth.mx_weight_scales_interleaved(sw)), to_dev(off), act=act))
     ref = oracle.gmm_mx4(a, sa, w, sw, off, act=act, nthreads=8)
     assert normwise_err(out, ref) <= 8e-3, name
 
@@ -666,11 +666,11 @@ def test_gmm_mxfp4_grid_values_bit_exact_and_equal_to_fp8_mx():
     sa = rng.integers(125, 130, (A, Hin // 32)).astype(np.uint8)
     sw = rng.integers(125, 130, (e, Hin // 32, N)).astype(np.uint8)
     od = to_dev(off)
-    out4 = to_host(moe.gmm_mxfp4(to_dev(a4), to_dev(synth.mx_scales_slice_major(sa, 8)), to_dev(w4), to_dev(sw), od, act=moe.ACT_RELU))
+    out4 = to_host(moe.gmm_mxfp4(to_dev(a4), to_dev(synth.mx_scales_slice_major(sa, 8)), to_dev(w4), to_dev(synth.mx_weight_scales_interleaved(sw)), od, act=moe.ACT_RELU))
     ref = oracle.gmm_mx4(a4, sa, w4, sw, off, act=moe.ACT_RELU, nthreads=8)
     assert np.array_equal(out4, oracle.bf16_bits(ref))
     a8, w8 = synth.to_e4m3(af, 1.0), synth.to_e4m3(wf, 1.0)
-    out8 = to_host(moe.gmm_mx(to_dev(a8), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w8), to_dev(sw), od, act=moe.ACT_RELU))
+    out8 = to_host(moe.gmm_mx(to_dev(a8), to_dev(synth.mx_scales_slice_major(sa, 4)), to_dev(w8), to_dev(synth.mx_weight_scales_interleaved(sw)), od, act=moe.ACT_RELU))
     assert np.array_equal(out4, out8)
 
 
