@@ -1150,6 +1150,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
     bf16_t* __restrict__ out, RowMap gx) {
   typedef Pp8Cfg<MX, FP4> C;
+  // MX: LDS activation rows in the pp8_trow order, so that one 16-byte read
+  // fetches the scales of a lane's four fragment rows
+  constexpr bool kRowPerm = MX;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   {
     int* s_off = reinterpret_cast<int*>(smem);
@@ -1215,7 +1218,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int kb = (wave * C::kADma + q) * 1024 + lane * 16;
     const int prow = kb >> 7, pc = (kb >> 4) & 7;
     const int lc = pc ^ pp8_xswz(prow);
-    const int trow = pp8_trow(prow);
+    const int trow = kRowPerm ? pp8_trow(prow) : prow;
     const int src = trow >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + trow) : trow;
     a_voff[q] = (src >= 0 ? (uint32_t)src * (uint32_t)rowb : kOOB) + lc * 16;
     a_kc[q] = lc * 16;
@@ -1262,13 +1265,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   const bool wave_active = (half * 128 + wm2 * 64 < tile.rows) && (tile.n0 + wn * 64 < N);
   const int ci = lane & 15, kq = lane >> 4;
+  // tile row (within the wave's 64) of fragment i, lane ci
+  auto frow = [&](int i) { return kRowPerm ? 4 * ci + i : 16 * i + ci; };
   // output map: this lane's destination rows, fetched now so that the
   // epilogue does not wait for them
   int dpre[4] = {0, 0, 0, 0};
   if (gx.dst != nullptr && wave_active) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ml = half * 128 + wm2 * 64 + 4 * ci + i;
+      const int ml = half * 128 + wm2 * 64 + frow(i);
       dpre[i] = ml < tile.rows ? gx.dst[tile.row0 + ml] : -1;
     }
   }
@@ -1277,7 +1282,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   if (gx.row_scale != nullptr && wave_active) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ml = half * 128 + wm2 * 64 + 4 * ci + i;
+      const int ml = half * 128 + wm2 * 64 + frow(i);
       rpre[i] = ml < tile.rows ? row_scale_of(gx, tile.row0 + ml) : 0.f;
     }
   }
@@ -1432,7 +1437,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const float sc = ld_scale(a_scale) * ld_scale(w_scale);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ml = half * 128 + wm2 * 64 + 4 * ci + i;
+    const int ml = half * 128 + wm2 * 64 + frow(i);
     if (ml >= tile.rows) continue;
     const OutRow orow = out_row_of(gx, tile.row0 + ml, dpre[i], A);
     if (orow.row < 0) continue;
