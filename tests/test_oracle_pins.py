@@ -673,3 +673,17 @@ def test_layer_fp8_composition():
     plain = oracle.layer(synth.bf16_to_f32(d["x"]), synth.bf16_to_f32(d["wr"]), w1f, w2f, d["K"])
     err = np.abs(full["y"] - plain["y"]).max() / np.abs(plain["y"]).max()
     assert err <= 6e-2
+
+
+def test_gmm_row_scales_on_sampled_rows():
+    """Per-row scales follow the grouped row, also when only listed rows are computed."""
+    rng = np.random.default_rng(45)
+    counts = [6, 3, 9]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    a = rng.integers(-3, 4, (A, 32)).astype(np.float32)
+    w = rng.integers(-2, 3, (3, 32, 8)).astype(np.float32)
+    rs = np.exp2(rng.integers(-2, 3, A)).astype(np.float64)
+    full = oracle.gmm(a, w, off, a_scale=rs)
+    rows = np.array([17, 2, 9, 0, 11], np.int32)
+    assert np.array_equal(oracle.gmm(a, w, off, a_scale=rs, rows=rows), full[rows])
