@@ -13,7 +13,7 @@ a second stream (fp8dyn: gmmX quantised per row on the device first).
 
 Prints ONE JSON line. Default workload: prefill (T=4096, H=4096, E=8, K=2,
 F=14336, bf16). Other workloads: --workload skewed|decode16|decode64|
-decode256|fp8gmm|fp8mx|fp8dyn|fp4mx|prefill_fp8|tiny.
+decode256|fp8gmm|fp8gmm_one|fp8mx|fp8dyn|fp4mx|prefill_fp8|tiny.
 """
 from __future__ import annotations
 
@@ -52,7 +52,8 @@ def parse():
                     help="untimed warm-up steps (default: as many as fill 0.4 s, so the GPU's "
                          "clocks have left their idle state; the count is reported)")
     ap.add_argument("--workload", default="prefill",
-                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8mx", "fp8dyn", "fp4mx", "prefill_fp8"])
+                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8gmm_one", "fp8mx", "fp8dyn", "fp4mx",
+                                                       "prefill_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -349,7 +350,8 @@ def bench_fp8(args, dev, mode="pt"):
     the Unpermute fused into the GEMM's stores; "mx": E8M0 block scales, then
     the Unpermute kernel; "dyn": gmmX arrives in bf16 and is quantised per row
     on the device (per-token dynamic), then the per-token-scaled GEMM with the
-    fused Unpermute."""
+    fused Unpermute; "one": as "pt", with the routed and the shared GEMM in
+    one launch (moe_gmm_routed_shared) instead of two streams."""
     import numpy as np
     import torch
 
@@ -392,6 +394,15 @@ def bench_fp8(args, dev, mode="pt"):
 
     # events: 0 start, 5 after the quantisation (dyn), 1 after the GEMM, 2 after
     # the Unpermute (mx), 3/4 around the shared expert on the side stream
+    def step_one(ev=None):
+        if ev is not None:
+            ev[0].record()
+            ev[5].record()
+        moe.gmm_routed_shared(gx, gw, perm["offsets"], sx, sw, mx, mw, moff, dst=perm["perm_src"], out=un, ys=my)
+        if ev is not None:
+            ev[1].record()
+            ev[2].record()
+
     def step(ev=None):
         main = torch.cuda.current_stream()
         fork = torch.cuda.Event()
@@ -433,6 +444,9 @@ def bench_fp8(args, dev, mode="pt"):
         join.record(side)
         main.wait_event(join)
 
+    one = mode == "one"
+    if one:
+        step = step_one
     warmup = warm_up(step, args.warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -445,7 +459,8 @@ def bench_fp8(args, dev, mode="pt"):
     def span(i, j):
         return float(np.mean([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)]))
 
-    q_ms, gmm_ms, un_ms, sh_ms = span(0, 5), span(5, 1), span(1, 2), span(3, 4)
+    q_ms, gmm_ms, un_ms = span(0, 5), span(5, 1), span(1, 2)
+    sh_ms = None if one else span(3, 4)
     counts = perm["counts"].cpu().numpy().tolist()
     fl, by = flops_bytes_gmm(counts, H1, N1, 1)
     if fp4:  # half a byte per activation and weight element
@@ -454,10 +469,16 @@ def bench_fp8(args, dev, mode="pt"):
         by += A * (H1 // 32) + sum(1 for c in counts if c > 0) * (H1 // 32) * N1
     if dyn:  # one fp32 scale per activation row
         by += A * 4
-    achieved = fl / (gmm_ms * 1e-3) / 1e12
     peak = PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS
-    wl = {"pt": "fp8gmm", "mx": "fp8mx", "dyn": "fp8dyn", "mx4": "fp4mx"}[mode]
+    if one:  # the launch also runs the bf16 shared GEMM: its flops, at the bf16 peak
+        fl_s = 2.0 * T * H2 * N2
+        by += 2 * (T * H2 + H2 * N2 + T * N2)
+        peak = (fl + fl_s) / (fl / (PEAK_FP8_TFLOPS * 1e12) + fl_s / (PEAK_BF16_TFLOPS * 1e12)) / 1e12
+        fl += fl_s
+    achieved = fl / (gmm_ms * 1e-3) / 1e12
+    wl = {"pt": "fp8gmm", "one": "fp8gmm_one", "mx": "fp8mx", "dyn": "fp8dyn", "mx4": "fp4mx"}[mode]
     data = {"pt": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
+            "one": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
             "mx": "synthetic (seeded; E4M3 with MX E8M0 scales per 32 elements, OCP recipe; "
                   "random top-8 of 32 routing)",
             "dyn": "synthetic (seeded; bf16 gmmX quantised per row on the device, E4M3 weights with a "
@@ -465,13 +486,16 @@ def bench_fp8(args, dev, mode="pt"):
             "mx4": "synthetic (seeded; E2M1 with MX E8M0 scales per 32 elements, OCP recipe; "
                    "random top-8 of 32 routing)"}[mode]
     kernel = {"pt": "moe_gmm_scatter E4M3 (gmm_pp8_kernel, Unpermute fused into its stores)",
+              "one": "moe_gmm_routed_shared (gmm_pair_kernel: E4M3 routed tiles, Unpermute fused into their "
+                     "stores, and bf16 shared-expert tiles in one launch)",
               "mx": "moe_gmm_mx E4M3 + E8M0 (gmm_pp8_kernel<true>)",
               "dyn": "moe_gmm_scatter E4M3, per-token scales (gmm_pp8_kernel, Unpermute fused)",
               "mx4": "moe_gmm_mxfp4 E2M1 + E8M0 (gmm_pp8_kernel<true, true>)"}[mode]
     kernels = {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
                "unpermute": ({"ms": un_ms, "GB/s": 2 * A * N1 * 2 / (un_ms * 1e-3) / 1e9} if use_mx
                              else "fused into the grouped GEMM's stores"),
-               "shared_gemm_bf16": {"ms": sh_ms, "TFLOP/s": 2.0 * T * H2 * N2 / (sh_ms * 1e-3) / 1e12}}
+               "shared_gemm_bf16": ({"ms": sh_ms, "TFLOP/s": 2.0 * T * H2 * N2 / (sh_ms * 1e-3) / 1e12}
+                                    if sh_ms is not None else "in the same launch")}
     if dyn:  # bf16 rows read once, codes and scales written
         kernels["quant_rows"] = {"ms": q_ms, "GB/s": (A * H1 * 3 + A * 4) / (q_ms * 1e-3) / 1e9}
     res = {
@@ -637,8 +661,8 @@ def main():
     if args.workload == "prefill_fp8":
         res, host = bench_layer_fp8(args, dev)
         res["achievable"] = achievable(dev)
-    elif args.workload in ("fp8gmm", "fp8mx", "fp8dyn", "fp4mx"):
-        res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8mx": "mx", "fp8dyn": "dyn",
+    elif args.workload in ("fp8gmm", "fp8gmm_one", "fp8mx", "fp8dyn", "fp4mx"):
+        res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8gmm_one": "one", "fp8mx": "mx", "fp8dyn": "dyn",
                                                "fp4mx": "mx4"}[args.workload])
         res["achievable"] = achievable(dev)
     else:

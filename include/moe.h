@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 11000 /* 1.10.0: MX weight scales in interleaved column order */
+#define MOE_VERSION 11100 /* 1.11.0: moe_gmm_routed_shared */
 
 typedef enum {
   MOE_OK = 0,
@@ -216,6 +216,42 @@ moe_status moe_gmm_scatter(const void* a, moe_dtype a_dt, moe_quant_mode a_q, co
                            const int32_t* offsets, int e, int A, int Hin, int N, moe_act act,
                            const int32_t* row_dst, const float* row_gate, void* out, moe_dtype out_dt,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_gmm_routed_shared — the routed experts' E4M3 grouped GEMM and the
+ * shared expert's bf16 GEMM of one layer step in a single launch: the page's
+ * two formulas, gmmY = (gmmX @ gmmWeight) * gmmXScale * gmmWeightScale and
+ * mmY = (mmX @ mmWeight) * mmXScaleOptional * mmWeightScaleOptional
+ * ("aclnnQuantGroupedMatMulAlltoAllv", section 计算公式), computed side by side
+ * as its interface description (接口功能) has the routed GEMM run in parallel
+ * with the shared expert's MatMul.
+ *   routed:  a, a_q, a_scale, w, w_scale, offsets, e, A, Hin, N, act,
+ *            row_dst, row_gate, out exactly as for moe_gmm_scatter with
+ *            a_dt = w_dt = MOE_FP8_E4M3, w_q = MOE_QUANT_PER_TENSOR and
+ *            out_dt = MOE_BF16, except that row_dst may be NULL (then grouped
+ *            row r is stored as row r, as by moe_gmm)
+ *   shared:  xs, ws_w, offsets_s, e_s, T, Hs, Ns, act_s, ys exactly as
+ *            a, w, offsets, e, A, Hin, N, act, out of moe_gmm with all three
+ *            types MOE_BF16 and no scales (mmX and mmWeight in bf16, the
+ *            optional scales left out). The shared expert is e_s = 1,
+ *            offsets_s = {0, T}: ys[t,n] = act_s( sum_h xs[t,h] * ws_w[h,n] ),
+ *            xs (T,Hs) = mmX, ws_w (Hs,Ns) = mmWeight, ys (T,Ns) = mmY.
+ * Either part may be empty (A = 0 or T = 0). One launch when both parts take
+ * the tiled DMA kernels (E4M3: Hin and N multiples of 16; bf16: more than 48
+ * rows per group on average, Hs % 8 == 0, Ns % 16 == 0; every expert's
+ * weight matrix under 2 GiB); otherwise the two GEMMs are launched one after
+ * the other on the stream. Either way out equals moe_gmm_scatter's (moe_gmm's)
+ * result and ys equals moe_gmm's, bit for bit, whenever that moe_gmm call does
+ * not split its last round of tiles along K: this call never splits, so it
+ * takes no workspace. out and ys must not overlap each other or any input.
+ * Errors: those of moe_gmm_scatter and moe_gmm for the two parts (no
+ * workspace errors).
+ */
+moe_status moe_gmm_routed_shared(const void* a, moe_quant_mode a_q, const float* a_scale, const void* w,
+                                 const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
+                                 moe_act act, const int32_t* row_dst, const float* row_gate, void* out,
+                                 const void* xs, const void* ws_w, const int32_t* offsets_s, int e_s, int T,
+                                 int Hs, int Ns, moe_act act_s, void* ys, void* stream);
 
 /*
  * moe_gmm_mx — grouped GEMM on MX block-scaled E4M3 operands (quant mode 6,

@@ -27,7 +27,7 @@ ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
-           "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
+           "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_routed_shared", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
            "moe_quant_rows", "moe_layer_workspace_size", "moe_layer", "moe_layer_fp8_workspace_size",
            "moe_layer_fp8")
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
                                      i32, i32, i32, vp, i32, vp, sz, vp]
         L.moe_gmm_scatter.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
                                       vp, vp, vp, i32, vp, sz, vp]
+        L.moe_gmm_routed_shared.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp,
+                                            vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_gmm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_gmm_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
@@ -233,6 +235,30 @@ def gmm(a, w, offsets, act=ACT_NONE, a_scale=None, w_scale=None, out=None, ws=No
                        _stream(stream))
     _check(st, "moe_gmm")
     return out
+
+
+def gmm_routed_shared(a, w, offsets, a_scale, w_scale, xs, ws_w, offsets_s, act=ACT_NONE, act_s=ACT_NONE,
+                      dst=None, gate=None, per_token=False, out=None, ys=None, stream=None):
+    """moe_gmm_routed_shared: the E4M3 grouped GEMM over w (e,Hin,N) (per-tensor
+    scales, or per_token: one a_scale per row of a; stored through dst, times
+    gate, when dst is given) and the bf16 grouped GEMM xs @ ws_w (e_s,Hs,Ns)
+    over offsets_s in one launch. Returns (out, ys), both bf16."""
+    A, Hin = a.shape
+    e, Hw, N = w.shape
+    T, Hs = xs.shape
+    e_s, Hw2, Ns = ws_w.shape
+    if Hw != Hin or Hw2 != Hs:
+        raise ValueError("activations and weights disagree on the reduction size")
+    if out is None:
+        out = _empty((A, N), torch.bfloat16, a)
+    if ys is None:
+        ys = _empty((T, Ns), torch.bfloat16, xs)
+    aq = QUANT_PER_TOKEN if per_token else QUANT_PER_TENSOR
+    st = lib().moe_gmm_routed_shared(_ptr(a), aq, _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(offsets), e, A,
+                                     Hin, N, act, _ptr(dst), _ptr(gate), _ptr(out), _ptr(xs), _ptr(ws_w),
+                                     _ptr(offsets_s), e_s, T, Hs, Ns, act_s, _ptr(ys), _stream(stream))
+    _check(st, "moe_gmm_routed_shared")
+    return out, ys
 
 
 def gmm_mx(a, a_scale, w, w_scale, offsets, act=ACT_NONE, out=None, stream=None):

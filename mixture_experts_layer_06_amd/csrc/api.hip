@@ -212,11 +212,14 @@ moe_status moe_gmm_workspace_size(moe_dtype a_dt, int e, int A, int Hin, int N, 
 #endif
 
 namespace {
-// Shared argument checks and launch of moe_gmm / moe_gmm_gather.
-moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
+// Shared argument checks of moe_gmm / moe_gmm_gather / moe_gmm_scatter; on
+// MOE_OK, call holds launch_gmm's arguments and *ws_use the workspace to pass
+// (no_split: no workspace is taken or required; the launch then never splits).
+moe_status gmm_prepare(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
                        const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
                        const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
-                       moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream, const RowMap* gx) {
+                       moe_dtype out_dt, void* ws, size_t ws_bytes, const RowMap* gx, GmmCall& call,
+                       void** ws_use, bool no_split = false) {
   if (!any_dtype_ok(a_dt) || !any_dtype_ok(w_dt) || !any_dtype_ok(out_dt)) return MOE_ERR_BAD_DTYPE;
   const bool pair_ok = (a_dt == MOE_F32 && w_dt == MOE_F32 && out_dt == MOE_F32) ||
                        (a_dt == MOE_BF16 && w_dt == MOE_BF16 && out_dt == MOE_BF16) ||
@@ -239,6 +242,8 @@ moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const 
   }
   if (a_q == MOE_QUANT_PER_TENSOR || per_token) REQUIRE_PTR(a_scale);
   if (w_q == MOE_QUANT_PER_TENSOR) REQUIRE_PTR(w_scale);
+  call = GmmCall{a, nullptr, w, nullptr, offsets, e, A, Hin, N, act, out, gx ? *gx : RowMap{}};
+  *ws_use = nullptr;
   if (A == 0) return MOE_OK;
   REQUIRE_PTR(a);
   REQUIRE_PTR(w);
@@ -250,7 +255,7 @@ moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const 
     REQUIRE_ALIGNED(gx->dst);
     REQUIRE_ALIGNED(gx->gate);
   }
-  const size_t need = gmm_ws_bytes(a_dt, e, A, Hin, N);
+  const size_t need = no_split ? 0 : gmm_ws_bytes(a_dt, e, A, Hin, N);
   if (need > 0) {
     REQUIRE_PTR(ws);
     if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -261,15 +266,28 @@ moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const 
   REQUIRE_ALIGNED(out);
   REQUIRE_ALIGNED(ws);
   // per-tensor scales are 4-byte device scalars: natural alignment suffices
-  const float* as = a_q == MOE_QUANT_PER_TENSOR ? a_scale : nullptr;
-  const float* wsc = w_q == MOE_QUANT_PER_TENSOR ? w_scale : nullptr;
-  RowMap rm = gx ? *gx : RowMap{};
+  call.a_scale = a_q == MOE_QUANT_PER_TENSOR ? a_scale : nullptr;
+  call.w_scale = w_q == MOE_QUANT_PER_TENSOR ? w_scale : nullptr;
   if (per_token) {
     REQUIRE_ALIGNED(a_scale);
-    rm.row_scale = a_scale;
+    call.gx.row_scale = a_scale;
   }
-  return launch_gmm(a, a_dt, as, w, wsc, offsets, e, A, Hin, N, act, out, out_dt, need > 0 ? ws : nullptr,
-                    (hipStream_t)stream, rm);
+  *ws_use = need > 0 ? ws : nullptr;
+  return MOE_OK;
+}
+
+// Checks and launch of moe_gmm / moe_gmm_gather / moe_gmm_scatter.
+moe_status gmm_checked(const void* a, moe_dtype a_dt, moe_quant_mode a_q, const float* a_scale,
+                       const void* w, moe_dtype w_dt, moe_quant_mode w_q, const float* w_scale,
+                       const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                       moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream, const RowMap* gx) {
+  GmmCall c;
+  void* ws_use = nullptr;
+  MOE_TRY(gmm_prepare(a, a_dt, a_q, a_scale, w, w_dt, w_q, w_scale, offsets, e, A, Hin, N, act, out, out_dt, ws,
+                      ws_bytes, gx, c, &ws_use));
+  if (A == 0) return MOE_OK;
+  return launch_gmm(c.a, a_dt, c.a_scale, c.w, c.w_scale, c.offsets, c.e, c.A, c.Hin, c.N, c.act, c.out, out_dt,
+                    ws_use, (hipStream_t)stream, c.gx);
 }
 }  // namespace
 
@@ -302,6 +320,24 @@ moe_status moe_gmm_scatter(const void* a, moe_dtype a_dt, moe_quant_mode a_q, co
   if (A > 0 && row_dst == nullptr) return MOE_ERR_NULL_POINTER;
   return gmm_checked(a, a_dt, a_q, a_scale, w, w_dt, w_q, w_scale, offsets, e, A, Hin, N, act, out,
                      out_dt, ws, ws_bytes, stream, &gx);
+}
+
+moe_status moe_gmm_routed_shared(const void* a, moe_quant_mode a_q, const float* a_scale, const void* w,
+                                 const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
+                                 moe_act act, const int32_t* row_dst, const float* row_gate, void* out,
+                                 const void* xs, const void* ws_w, const int32_t* offsets_s, int e_s, int T,
+                                 int Hs, int Ns, moe_act act_s, void* ys, void* stream) {
+  RowMap gx;
+  gx.dst = row_dst;
+  gx.gate = row_gate;
+  GmmCall f, b;
+  void* ws_use = nullptr;
+  MOE_TRY(gmm_prepare(a, MOE_FP8_E4M3, a_q, a_scale, w, MOE_FP8_E4M3, MOE_QUANT_PER_TENSOR, w_scale, offsets, e,
+                      A, Hin, N, act, out, MOE_BF16, nullptr, 0, row_dst ? &gx : nullptr, f, &ws_use, true));
+  MOE_TRY(gmm_prepare(xs, MOE_BF16, MOE_QUANT_NONE, nullptr, ws_w, MOE_BF16, MOE_QUANT_NONE, nullptr, offsets_s,
+                      e_s, T, Hs, Ns, act_s, ys, MOE_BF16, nullptr, 0, nullptr, b, &ws_use, true));
+  if (A == 0 && T == 0) return MOE_OK;
+  return launch_gmm_pair(f, b, (hipStream_t)stream);
 }
 
 moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,

@@ -110,6 +110,23 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                       moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s,
                       RowMap gx = RowMap{});
+// One grouped GEMM's operands (the arguments of launch_gmm).
+struct GmmCall {
+  const void* a;
+  const float* a_scale;
+  const void* w;
+  const float* w_scale;
+  const int32_t* offsets;
+  int e, A, Hin, N;
+  moe_act act;
+  void* out;
+  RowMap gx;
+};
+// An E4M3 grouped GEMM f and a bf16 grouped GEMM b (bf16 out for both) in
+// one launch when both take the ping-pong kernels, else as two launch_gmm
+// calls without a workspace; either way each result equals its own
+// launch_gmm with no workspace.
+moe_status launch_gmm_pair(const GmmCall& f, const GmmCall& b, hipStream_t s);
 // Grouped GEMM on MX (E8M0 block-scaled) operands: E4M3 (Hin % 128 == 0) or,
 // fp4, E2M1 packed two per byte along K (Hin % 256 == 0); N % 16 == 0.
 moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void* w,

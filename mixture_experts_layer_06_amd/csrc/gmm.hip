@@ -209,11 +209,10 @@ __device__ __forceinline__ void tile_of(const int* s_off, const int* s_pre, int 
 // XCD-aware: block p runs on XCD p % 8; XCD x takes logical tiles
 // [x*per, (x+1)*per).
 template <int BM, int BN, int GM, int FOLD = 0>
-__device__ __forceinline__ bool pick_tile(const int* s_off, const int* s_pre, int e, int N, Tile& t) {
+__device__ __forceinline__ bool pick_tile(const int* s_off, const int* s_pre, int e, int N, int p, Tile& t) {
   const int ntn = (N + BN - 1) / BN;
   const int total = s_pre[e] * ntn;
   if (total == 0) return false;
-  const int p = blockIdx.x;
   const int per = (total + 7) / 8;
   const int slot = p >> 3;
   if (slot >= per) return false;
@@ -238,7 +237,7 @@ struct Work {
 };
 template <int BM, int BN, int GM, int FOLD = 0>
 __device__ __forceinline__ bool pick_work(const int* s_off, const int* s_pre, int e, int N, int nsteps,
-                                          int ncu, bool can_split, Tile& t, Work& wk) {
+                                          int ncu, bool can_split, int p, Tile& t, Work& wk) {
   const int ntn = (N + BN - 1) / BN;
   const int total = s_pre[e] * ntn;
   wk.S = 1;
@@ -247,9 +246,8 @@ __device__ __forceinline__ bool pick_work(const int* s_off, const int* s_pre, in
   if (total == 0) return false;
   const int rem = total % ncu;
   const int S = kMaxSplit;
-  if (!can_split || rem == 0 || rem * S > ncu || nsteps < 4 * S) return pick_tile<BM, BN, GM, FOLD>(s_off, s_pre, e, N, t);
+  if (!can_split || rem == 0 || rem * S > ncu || nsteps < 4 * S) return pick_tile<BM, BN, GM, FOLD>(s_off, s_pre, e, N, p, t);
   const int full = total - rem;  // a multiple of ncu, hence of 8
-  const int p = blockIdx.x;
   int L;
   if (p < full) {
     L = (p & 7) * (full >> 3) + (p >> 3);
@@ -396,7 +394,7 @@ __global__ __launch_bounds__(C::kNT) void gmm_tiled_kernel(
   __shared__ int s_pre[257];
   load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_pre);
   Tile tile;
-  if (!pick_tile<C::kBM, C::kBN, 8>(s_off, s_pre, e, N, tile)) return;
+  if (!pick_tile<C::kBM, C::kBN, 8>(s_off, s_pre, e, N, blockIdx.x, tile)) return;
 
   constexpr int E_ = C::kElem;
   const int tid = threadIdx.x;
@@ -746,15 +744,15 @@ struct PpCfg {
   static_assert(kLds >= 2 * 257 * 4, "tile prefix lives in the ring");
 };
 
+// The kernel's work for block p (smem: the dynamic LDS ring; s_last: an LDS
+// flag of the block).
 template <class C>
-__global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp_kernel(
-    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
-    const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+__device__ __forceinline__ void pp_block(
+    unsigned char* smem, int& s_last, int p, const unsigned char* __restrict__ a,
+    const unsigned char* __restrict__ w, const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
     bf16_t* __restrict__ out, float* __restrict__ split_ws, int* __restrict__ split_cnt, int ncu,
-    RowMap gx) {
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ int s_last;
+    const RowMap& gx) {
   // The ring takes all of LDS; the tile prefix borrows its first bytes
   // before any DMA is issued.
   {
@@ -768,7 +766,7 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
   Work wk;
   if (!pick_work<C::kBM, C::kBN, MOE_PP_GM, C::kFold>(reinterpret_cast<const int*>(smem),
                                                        reinterpret_cast<const int*>(smem) + 257, e, N,
-                                                       nsteps_all, ncu, split_ws != nullptr, tile, wk))
+                                                       nsteps_all, ncu, split_ws != nullptr, p, tile, wk))
     return;
   __syncthreads();  // every lane has its tile before the ring overwrites the prefix
   // K slices of this block: all of them, or part wk.part of wk.S
@@ -1079,6 +1077,19 @@ __global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
+template <class C>
+__global__ __launch_bounds__(C::kNT) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp_kernel(
+    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
+    const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+    const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
+    bf16_t* __restrict__ out, float* __restrict__ split_ws, int* __restrict__ split_cnt, int ncu,
+    RowMap gx) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int s_last;
+  pp_block<C>(smem, s_last, blockIdx.x, a, w, a_scale, w_scale, offsets, e, A, Hin, N, relu, out, split_ws,
+              split_cnt, ncu, gx);
+}
+
 // ------------------------------------------------------------------ ping-pong E4M3 kernel
 //
 // The bf16 ping-pong design for E4M3 operands, on v_mfma_scale_f32_16x16x128
@@ -1142,25 +1153,25 @@ __device__ __forceinline__ int pp8_xswz(int m) { return 2 * ((m >> 1) & 3); }
 __device__ __forceinline__ int pp8_trow(int q) { return (q & ~63) | ((q & 15) << 2) | ((q >> 4) & 3); }
 __device__ __forceinline__ int pp8_wswz(int k) { return ((k >> 1) & 3) | (((k >> 4) & 1) << 2); }
 
-template <bool MX, bool FP4 = false>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp8_kernel(
-    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
+// The kernel's work for block p (smem: the dynamic LDS ring).
+template <bool MX, bool FP4>
+__device__ __forceinline__ void pp8_block(
+    unsigned char* smem, int p, const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
     const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     const unsigned char* __restrict__ a_mx, const unsigned char* __restrict__ w_mx,
     const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
-    bf16_t* __restrict__ out, RowMap gx) {
+    bf16_t* __restrict__ out, const RowMap& gx) {
   typedef Pp8Cfg<MX, FP4> C;
   // MX: LDS activation rows in the pp8_trow order, so that one 16-byte read
   // fetches the scales of a lane's four fragment rows
   constexpr bool kRowPerm = MX;
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   {
     int* s_off = reinterpret_cast<int*>(smem);
     load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_off + 257);
   }
   Tile tile;
   if (!pick_tile<C::kBM, C::kBN, MOE_PP8_GM>(reinterpret_cast<const int*>(smem),
-                                     reinterpret_cast<const int*>(smem) + 257, e, N, tile))
+                                     reinterpret_cast<const int*>(smem) + 257, e, N, p, tile))
     return;
   __syncthreads();  // every lane has its tile before the ring overwrites the prefix
 
@@ -1459,6 +1470,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
 }
 
+template <bool MX, bool FP4 = false>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp8_kernel(
+    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w,
+    const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+    const unsigned char* __restrict__ a_mx, const unsigned char* __restrict__ w_mx,
+    const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
+    bf16_t* __restrict__ out, RowMap gx) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  pp8_block<MX, FP4>(smem, blockIdx.x, a, w, a_scale, w_scale, a_mx, w_mx, offsets, e, A, Hin, N, relu, out, gx);
+}
+
+// Two grouped GEMMs in one launch: a bf16 one on the ping-pong kernel's
+// 256 x 256 tiles (blocks [0, nb_b)) and an E4M3 one on the E4M3 kernel's
+// 256 x 128 tiles (the blocks after them), each block running exactly what
+// its own kernel runs for that tile. The bf16 tiles, about four times as
+// long, are handed out first; nb_b is a multiple of 8, so both keep their
+// XCD-aware tile order. The bf16 GEMM is never split along K here.
+struct GroupArgs {
+  const unsigned char* a;
+  const unsigned char* w;
+  const float* a_scale;
+  const float* w_scale;
+  const int32_t* offsets;
+  int e, A, Hin, N, relu;
+  bf16_t* out;
+  RowMap gx;
+};
+
+template <class C>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pair_kernel(GroupArgs b,
+                                                                                               GroupArgs f,
+                                                                                               int nb_b) {
+  static_assert(C::kNT == 512, "both halves run 8 waves");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int s_last;
+  const int p = blockIdx.x;
+  if (p < nb_b)
+    pp_block<C>(smem, s_last, p, b.a, b.w, b.a_scale, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.relu, b.out,
+                nullptr, nullptr, 0, b.gx);
+  else
+    pp8_block<false, false>(smem, p - nb_b, f.a, f.w, f.a_scale, f.w_scale, nullptr, nullptr, f.offsets, f.e,
+                            f.A, f.Hin, f.N, f.relu, f.out, f.gx);
+}
+
 // ------------------------------------------------------------------ streaming kernel (decode)
 
 // XS: the block's 4 waves (one expert, 4 consecutive 64-column groups) share
@@ -1751,7 +1806,7 @@ __global__ __launch_bounds__(256) void gmm_f32_kernel(const float* __restrict__ 
   __shared__ float Bs[kF32BK][kF32BN + 1];
   load_tile_prefix<kF32BM>(offsets, e, A, s_off, s_pre);
   Tile tile;
-  if (!pick_tile<kF32BM, kF32BN, 8>(s_off, s_pre, e, N, tile)) return;
+  if (!pick_tile<kF32BM, kF32BN, 8>(s_off, s_pre, e, N, blockIdx.x, tile)) return;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
@@ -2013,6 +2068,39 @@ moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void
                                   act == MOE_ACT_RELU, out, s, RowMap{});
   return launch_pp8<true>(a, nullptr, w, nullptr, a_scale, w_scale, offsets, e, A, Hin, N,
                           act == MOE_ACT_RELU, out, s, RowMap{});
+}
+
+
+moe_status launch_gmm_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
+  const bool fuse = f.A > 0 && b.A > 0 && gmm_path(MOE_FP8_E4M3, f.e, f.A, f.Hin, f.N) == GmmPath::PP8 &&
+                    gmm_path(MOE_BF16, b.e, b.A, b.Hin, b.N) == GmmPath::PP;
+  if (!fuse) {
+    moe_status st = launch_gmm(f.a, MOE_FP8_E4M3, f.a_scale, f.w, f.w_scale, f.offsets, f.e, f.A, f.Hin, f.N,
+                               f.act, f.out, MOE_BF16, nullptr, s, f.gx);
+    if (st != MOE_OK) return st;
+    return launch_gmm(b.a, MOE_BF16, b.a_scale, b.w, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.act, b.out,
+                      MOE_BF16, nullptr, s, b.gx);
+  }
+  typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
+  typedef Pp8Cfg<false> C8;
+  constexpr int kLds = CP::kLds > C8::kLds ? CP::kLds : C8::kLds;
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pair_kernel<CP>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    attr_done = true;
+  }
+  // grid upper bounds as in the two kernels' own launches (surplus blocks exit)
+  const int64_t nb_b = cdiv64((cdiv64(b.A, CP::kBM) + (b.e < b.A ? b.e : b.A)) * cdiv64(b.N, CP::kBN), 8) * 8;
+  const int64_t nb_f = cdiv64((cdiv64(f.A, C8::kBM) + (f.e < f.A ? f.e : f.A)) * cdiv64(f.N, C8::kBN), 8) * 8;
+  if (nb_b + nb_f > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  const GroupArgs ga_b{(const unsigned char*)b.a, (const unsigned char*)b.w, b.a_scale, b.w_scale, b.offsets,
+                       b.e, b.A, b.Hin, b.N, b.act == MOE_ACT_RELU, (bf16_t*)b.out, b.gx};
+  const GroupArgs ga_f{(const unsigned char*)f.a, (const unsigned char*)f.w, f.a_scale, f.w_scale, f.offsets,
+                       f.e, f.A, f.Hin, f.N, f.act == MOE_ACT_RELU, (bf16_t*)f.out, f.gx};
+  hipLaunchKernelGGL(gmm_pair_kernel<CP>, dim3((unsigned)(nb_b + nb_f)), dim3(512), kLds, s, ga_b, ga_f,
+                     (int)nb_b);
+  return launch_status();
 }
 
 }  // namespace moe

@@ -23,7 +23,7 @@ def declared_entry_points():
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
     for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx",
-              "moe_gmm_mxfp4",
+              "moe_gmm_mxfp4", "moe_gmm_routed_shared",
               "moe_combine", "moe_sum_slots", "moe_quant_rows", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size", "moe_layer_fp8", "moe_layer_fp8_workspace_size",
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 11000
+    assert moe.lib().moe_version() == 11100
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -331,6 +331,42 @@ def test_gmm_scatter_validation(kw, status):
 
 def test_gmm_scatter_zero_rows_is_noop():
     assert gmm_scatter(a=None, w=None, off=None, dst=None, gate=None, out=None, A=0) == moe.OK
+
+
+def gmm_routed_shared(a=P, aq=1, asc=P, w=P, wsc=P, off=P, e=8, A=100, Hin=128, N=64, act=moe.ACT_NONE,
+                      dst=P, gate=None, out=P, xs=P, ws_w=P, off_s=P, e_s=1, T=64, Hs=128, Ns=64,
+                      act_s=moe.ACT_NONE, ys=P):
+    return L.moe_gmm_routed_shared(a, aq, asc, w, wsc, off, e, A, Hin, N, act, dst, gate, out, xs, ws_w, off_s,
+                                   e_s, T, Hs, Ns, act_s, ys, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(asc=None), moe.ERR_NULL_POINTER),                           # routed part: moe_gmm_scatter's rules
+    (dict(wsc=None), moe.ERR_NULL_POINTER),
+    (dict(aq=0), moe.ERR_UNSUPPORTED),                                # E4M3 needs its scales
+    (dict(aq=6), moe.ERR_UNSUPPORTED),
+    (dict(act=5), moe.ERR_UNSUPPORTED),
+    (dict(e=0), moe.ERR_BAD_SHAPE),
+    (dict(N=0), moe.ERR_BAD_SHAPE),
+    (dict(a=None), moe.ERR_NULL_POINTER),
+    (dict(dst=MIS), moe.ERR_MISALIGNED),
+    (dict(out=MIS), moe.ERR_MISALIGNED),
+    (dict(xs=None), moe.ERR_NULL_POINTER),                            # shared part: moe_gmm's rules
+    (dict(ys=MIS), moe.ERR_MISALIGNED),
+    (dict(off_s=None), moe.ERR_NULL_POINTER),
+    (dict(ws_w=MIS), moe.ERR_MISALIGNED),
+    (dict(e_s=0), moe.ERR_BAD_SHAPE),
+    (dict(T=-1), moe.ERR_BAD_SHAPE),
+    (dict(Ns=65536), moe.ERR_BAD_SHAPE),
+    (dict(act_s=2), moe.ERR_UNSUPPORTED),
+])
+def test_gmm_routed_shared_validation(kw, status):
+    assert gmm_routed_shared(**kw) == status
+
+
+def test_gmm_routed_shared_empty_parts_are_noop():
+    assert gmm_routed_shared(a=None, w=None, off=None, dst=None, out=None, A=0, xs=None, ws_w=None, off_s=None,
+                             ys=None, T=0) == moe.OK
 
 
 def quant_rows(x=P, dt=moe.BF16, x_rows=10, H=64, src=None, div=1, rows=10, q=P, sc=P):
