@@ -1516,7 +1516,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int q = first ? p : p - nb0;
   if (first == (MOE_PAIR_BF16_FIRST != 0))
     pp_block<C>(smem, s_last, q, b.a, b.w, b.a_scale, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.relu, b.out,
-                nullptr, nullptr, 0, b.gx);
+                nullptr, nullptr, 1, b.gx);  // no split workspace: ncu is not used
   else
     pp8_block<false, false>(smem, q, f.a, f.w, f.a_scale, f.w_scale, nullptr, nullptr, f.offsets, f.e,
                             f.A, f.Hin, f.N, f.relu, f.out, f.gx);
