@@ -13,7 +13,7 @@ a second stream (fp8dyn: gmmX quantised per row on the device first).
 
 Prints ONE JSON line. Default workload: prefill (T=4096, H=4096, E=8, K=2,
 F=14336, bf16). Other workloads: --workload skewed|decode16|decode64|
-decode256|fp8gmm|fp8gmm_one|fp8mx|fp8dyn|fp4mx|prefill_fp8|tiny.
+decode256|fp8gmm|fp8gmm_one|fp8mx|fp8mx_one|fp8dyn|fp4mx|fp4mx_one|prefill_fp8|tiny.
 """
 from __future__ import annotations
 
@@ -52,8 +52,8 @@ def parse():
                     help="untimed warm-up steps (default: as many as fill 0.4 s, so the GPU's "
                          "clocks have left their idle state; the count is reported)")
     ap.add_argument("--workload", default="prefill",
-                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8gmm_one", "fp8mx", "fp8dyn", "fp4mx",
-                                                       "prefill_fp8"])
+                    choices=sorted(LAYER_WORKLOADS) + ["fp8gmm", "fp8gmm_one", "fp8mx", "fp8mx_one", "fp8dyn",
+                                                       "fp4mx", "fp4mx_one", "prefill_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -351,7 +351,8 @@ def bench_fp8(args, dev, mode="pt"):
     the Unpermute kernel; "dyn": gmmX arrives in bf16 and is quantised per row
     on the device (per-token dynamic), then the per-token-scaled GEMM with the
     fused Unpermute; "one": as "pt", with the routed and the shared GEMM in
-    one launch (moe_gmm_routed_shared) instead of two streams."""
+    one launch (moe_gmm_routed_shared) instead of two streams; "mx_one" and
+    "mx4_one": as "mx" and "mx4", with moe_gmm_mx_routed_shared."""
     import numpy as np
     import torch
 
@@ -359,8 +360,9 @@ def bench_fp8(args, dev, mode="pt"):
     import synth
     from synth import configs
 
-    fp4 = mode == "mx4"
-    use_mx, dyn = mode in ("mx", "mx4"), mode == "dyn"
+    one = mode in ("one", "mx_one", "mx4_one")
+    fp4 = mode in ("mx4", "mx4_one")
+    use_mx, dyn = mode in ("mx", "mx4", "mx_one", "mx4_one"), mode == "dyn"
     d = (configs.fp4_mx_inputs() if fp4 else configs.fp8_mx_inputs() if use_mx else
          configs.fp8_dyn_inputs() if dyn else configs.fp8_inputs())
     T, e, K, A, H1, N1, H2, N2 = (d[k] for k in ("T", "e", "K", "A", "H1", "N1", "H2", "N2"))
@@ -398,9 +400,16 @@ def bench_fp8(args, dev, mode="pt"):
         if ev is not None:
             ev[0].record()
             ev[5].record()
-        moe.gmm_routed_shared(gx, gw, perm["offsets"], sx, sw, mx, mw, moff, dst=perm["perm_src"], out=un, ys=my)
+        if use_mx:
+            moe.gmm_mx_routed_shared(gx, sx, gw, sw, perm["offsets"], mx, mw, moff, fp4=fp4, out=gy, ys=my)
+        else:
+            moe.gmm_routed_shared(gx, gw, perm["offsets"], sx, sw, mx, mw, moff, dst=perm["perm_src"], out=un,
+                                  ys=my)
         if ev is not None:
             ev[1].record()
+        if use_mx:
+            moe.combine(gy, perm["perm_dst"], None, T, K, out=un)
+        if ev is not None:
             ev[2].record()
 
     def step(ev=None):
@@ -444,7 +453,6 @@ def bench_fp8(args, dev, mode="pt"):
         join.record(side)
         main.wait_event(join)
 
-    one = mode == "one"
     if one:
         step = step_one
     warmup = warm_up(step, args.warmup)
@@ -473,10 +481,11 @@ def bench_fp8(args, dev, mode="pt"):
     if one:  # the launch also runs the bf16 shared GEMM: its flops, at the bf16 peak
         fl_s = 2.0 * T * H2 * N2
         by += 2 * (T * H2 + H2 * N2 + T * N2)
-        peak = (fl + fl_s) / (fl / (PEAK_FP8_TFLOPS * 1e12) + fl_s / (PEAK_BF16_TFLOPS * 1e12)) / 1e12
+        peak = (fl + fl_s) / (fl / (peak * 1e12) + fl_s / (PEAK_BF16_TFLOPS * 1e12)) / 1e12
         fl += fl_s
     achieved = fl / (gmm_ms * 1e-3) / 1e12
-    wl = {"pt": "fp8gmm", "one": "fp8gmm_one", "mx": "fp8mx", "dyn": "fp8dyn", "mx4": "fp4mx"}[mode]
+    wl = {"pt": "fp8gmm", "one": "fp8gmm_one", "mx": "fp8mx", "mx_one": "fp8mx_one", "dyn": "fp8dyn",
+          "mx4": "fp4mx", "mx4_one": "fp4mx_one"}[mode]
     data = {"pt": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
             "one": "synthetic (seeded; E4M3 per-tensor scales amax/448; random top-8 of 32 routing)",
             "mx": "synthetic (seeded; E4M3 with MX E8M0 scales per 32 elements, OCP recipe; "
@@ -484,13 +493,17 @@ def bench_fp8(args, dev, mode="pt"):
             "dyn": "synthetic (seeded; bf16 gmmX quantised per row on the device, E4M3 weights with a "
                    "per-tensor scale; random top-8 of 32 routing)",
             "mx4": "synthetic (seeded; E2M1 with MX E8M0 scales per 32 elements, OCP recipe; "
-                   "random top-8 of 32 routing)"}[mode]
+                   "random top-8 of 32 routing)"}[mode.replace("_one", "") if mode != "one" else mode]
     kernel = {"pt": "moe_gmm_scatter E4M3 (gmm_pp8_kernel, Unpermute fused into its stores)",
               "one": "moe_gmm_routed_shared (gmm_pair_kernel: E4M3 routed tiles, Unpermute fused into their "
                      "stores, and bf16 shared-expert tiles in one launch)",
               "mx": "moe_gmm_mx E4M3 + E8M0 (gmm_pp8_kernel<true>)",
               "dyn": "moe_gmm_scatter E4M3, per-token scales (gmm_pp8_kernel, Unpermute fused)",
-              "mx4": "moe_gmm_mxfp4 E2M1 + E8M0 (gmm_pp8_kernel<true, true>)"}[mode]
+              "mx4": "moe_gmm_mxfp4 E2M1 + E8M0 (gmm_pp8_kernel<true, true>)",
+              "mx_one": "moe_gmm_mx_routed_shared E4M3 + E8M0 (gmm_pair_kernel<.., true, false>: MX routed "
+                        "tiles and bf16 shared-expert tiles in one launch)",
+              "mx4_one": "moe_gmm_mx_routed_shared E2M1 + E8M0 (gmm_pair_kernel<.., true, true>: MX routed "
+                         "tiles and bf16 shared-expert tiles in one launch)"}[mode]
     kernels = {"gmm_fp8": {"ms": gmm_ms, "TFLOP/s": achieved},
                "unpermute": ({"ms": un_ms, "GB/s": 2 * A * N1 * 2 / (un_ms * 1e-3) / 1e9} if use_mx
                              else "fused into the grouped GEMM's stores"),
@@ -661,9 +674,10 @@ def main():
     if args.workload == "prefill_fp8":
         res, host = bench_layer_fp8(args, dev)
         res["achievable"] = achievable(dev)
-    elif args.workload in ("fp8gmm", "fp8gmm_one", "fp8mx", "fp8dyn", "fp4mx"):
-        res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8gmm_one": "one", "fp8mx": "mx", "fp8dyn": "dyn",
-                                               "fp4mx": "mx4"}[args.workload])
+    elif args.workload in ("fp8gmm", "fp8gmm_one", "fp8mx", "fp8mx_one", "fp8dyn", "fp4mx", "fp4mx_one"):
+        res, host = bench_fp8(args, dev, mode={"fp8gmm": "pt", "fp8gmm_one": "one", "fp8mx": "mx",
+                                               "fp8mx_one": "mx_one", "fp8dyn": "dyn", "fp4mx": "mx4",
+                                               "fp4mx_one": "mx4_one"}[args.workload])
         res["achievable"] = achievable(dev)
     else:
         res, host = bench_layer(args, dev)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 11100 /* 1.11.0: moe_gmm_routed_shared */
+#define MOE_VERSION 11200 /* 1.12.0: moe_gmm_routed_shared, moe_gmm_mx_routed_shared */
 
 typedef enum {
   MOE_OK = 0,
@@ -318,6 +318,28 @@ moe_status moe_gmm_mxfp4(const void* a, const uint8_t* a_scale, const void* w, c
 moe_status moe_combine(const void* y_perm, moe_dtype in_dt, const int32_t* perm_dst,
                        const float* topk_gate, int T, int K, int N, void* out, moe_dtype out_dt,
                        void* stream);
+
+/*
+ * moe_gmm_mx_routed_shared — moe_gmm_mx (fp4 = 0) or moe_gmm_mxfp4 (fp4 = 1)
+ * for the routed experts and the shared expert's bf16 GEMM in one launch, as
+ * moe_gmm_routed_shared does for per-tensor E4M3 (the page's routed and
+ * shared formulas, "aclnnQuantGroupedMatMulAlltoAllv" sections 计算公式 and
+ * 接口功能, with its mx quant mode for the routed experts).
+ *   routed:  a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out exactly
+ *            as for moe_gmm_mx (fp4 = 0) or moe_gmm_mxfp4 (fp4 = 1)
+ *   shared:  xs, ws_w, offsets_s, e_s, T, Hs, Ns, act_s, ys as for
+ *            moe_gmm_routed_shared
+ * One launch when the shared part takes the tiled DMA kernel (more than 48
+ * rows per group on average, Hs % 8 == 0, Ns % 16 == 0) and A > 0; otherwise
+ * two launches on the stream. out equals moe_gmm_mx's (moe_gmm_mxfp4's) and
+ * ys moe_gmm's result bit for bit whenever that moe_gmm call does not split
+ * along K. Errors: those of moe_gmm_mx / moe_gmm_mxfp4 and of moe_gmm for the
+ * two parts; MOE_ERR_UNSUPPORTED for fp4 outside {0, 1}.
+ */
+moe_status moe_gmm_mx_routed_shared(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                                    const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, int fp4,
+                                    void* out, const void* xs, const void* ws_w, const int32_t* offsets_s,
+                                    int e_s, int T, int Hs, int Ns, moe_act act_s, void* ys, void* stream);
 
 /*
  * moe_sum_slots — y[t,n] = sum_{k=0..K-1} z[t*K+k, n], fp32 sum in ascending

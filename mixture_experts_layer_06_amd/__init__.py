@@ -27,7 +27,7 @@ ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
-           "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_routed_shared", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
+           "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_routed_shared", "moe_gmm_mx_routed_shared", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
            "moe_quant_rows", "moe_layer_workspace_size", "moe_layer", "moe_layer_fp8_workspace_size",
            "moe_layer_fp8")
 
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
                                       vp, vp, vp, i32, vp, sz, vp]
         L.moe_gmm_routed_shared.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                             vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+        L.moe_gmm_mx_routed_shared.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                               vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_gmm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_gmm_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp]
@@ -258,6 +260,29 @@ def gmm_routed_shared(a, w, offsets, a_scale, w_scale, xs, ws_w, offsets_s, act=
                                      Hin, N, act, _ptr(dst), _ptr(gate), _ptr(out), _ptr(xs), _ptr(ws_w),
                                      _ptr(offsets_s), e_s, T, Hs, Ns, act_s, _ptr(ys), _stream(stream))
     _check(st, "moe_gmm_routed_shared")
+    return out, ys
+
+
+def gmm_mx_routed_shared(a, a_scale, w, w_scale, offsets, xs, ws_w, offsets_s, fp4=False, act=ACT_NONE,
+                         act_s=ACT_NONE, out=None, ys=None, stream=None):
+    """moe_gmm_mx_routed_shared: gmm_mx (fp4 False) or gmm_mxfp4 (fp4 True)
+    and the bf16 grouped GEMM xs @ ws_w (e_s,Hs,Ns) over offsets_s in one
+    launch. Returns (out, ys), both bf16."""
+    A, Hb = a.shape
+    Hin = 2 * Hb if fp4 else Hb
+    e, Hw, N = w.shape
+    T, Hs = xs.shape
+    e_s, Hw2, Ns = ws_w.shape
+    if Hw != Hb or Hw2 != Hs:
+        raise ValueError("activations and weights disagree on the reduction size")
+    if out is None:
+        out = _empty((A, N), torch.bfloat16, a)
+    if ys is None:
+        ys = _empty((T, Ns), torch.bfloat16, xs)
+    st = lib().moe_gmm_mx_routed_shared(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(offsets), e, A, Hin,
+                                        N, act, int(bool(fp4)), _ptr(out), _ptr(xs), _ptr(ws_w), _ptr(offsets_s),
+                                        e_s, T, Hs, Ns, act_s, _ptr(ys), _stream(stream))
+    _check(st, "moe_gmm_mx_routed_shared")
     return out, ys
 
 

@@ -340,16 +340,19 @@ moe_status moe_gmm_routed_shared(const void* a, moe_quant_mode a_q, const float*
   return launch_gmm_pair(f, b, (hipStream_t)stream);
 }
 
-moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
-                      const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
-                      void* stream) {
+namespace {
+// Argument checks of the MX grouped GEMMs (fp4: E2M1 operands packed two per
+// byte along K, else E4M3).
+moe_status mx_checked(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                      const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out, bool fp4) {
   if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
   if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
   if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
-  // 128-deep K slices of whole scale blocks, 16-byte column chunks, 32-bit offsets
-  if (Hin % 128 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)Hin * N >= (1ll << 31) || (int64_t)(Hin / 32) * ((N + 63) & ~63) * e >= (1ll << 31) ||
-      (int64_t)(Hin / 32) * A >= (1ll << 31))
+  // whole K slices (128 bytes: 128 E4M3 or 256 E2M1 values) of whole scale
+  // blocks, 16-byte column chunks, 32-bit offsets
+  if (Hin % (fp4 ? 256 : 128) != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)(fp4 ? Hin / 2 : Hin) * N >= (1ll << 31) ||
+      (int64_t)(Hin / 32) * ((N + 63) & ~63) * e >= (1ll << 31) || (int64_t)(Hin / 32) * A >= (1ll << 31))
     return MOE_ERR_UNSUPPORTED;
   if (A == 0) return MOE_OK;
   REQUIRE_PTR(a);
@@ -364,6 +367,15 @@ moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, cons
   REQUIRE_ALIGNED(w_scale);
   REQUIRE_ALIGNED(offsets);
   REQUIRE_ALIGNED(out);
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_gmm_mx(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                      const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
+                      void* stream) {
+  MOE_TRY(mx_checked(a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out, false));
+  if (A == 0) return MOE_OK;
   return launch_gmm_mx(a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out, (hipStream_t)stream);
 }
 
@@ -402,28 +414,24 @@ moe_status moe_quant_rows(const void* x, moe_dtype x_dt, int x_rows, int H, cons
 moe_status moe_gmm_mxfp4(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
                          const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, void* out,
                          void* stream) {
-  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
-  if (e < 1 || e > kMaxExperts) return MOE_ERR_BAD_SHAPE;
-  if (A < 0 || (int64_t)A >= kMaxRows || !dim_ok(Hin) || !dim_ok(N)) return MOE_ERR_BAD_SHAPE;
-  // 256-deep K slices (128 bytes) of whole scale blocks, 16-byte column chunks, 32-bit offsets
-  if (Hin % 256 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)(Hin / 2) * N >= (1ll << 31) || (int64_t)(Hin / 32) * ((N + 63) & ~63) * e >= (1ll << 31) ||
-      (int64_t)(Hin / 32) * A >= (1ll << 31))
-    return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(mx_checked(a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out, true));
   if (A == 0) return MOE_OK;
-  REQUIRE_PTR(a);
-  REQUIRE_PTR(a_scale);
-  REQUIRE_PTR(w);
-  REQUIRE_PTR(w_scale);
-  REQUIRE_PTR(offsets);
-  REQUIRE_PTR(out);
-  REQUIRE_ALIGNED(a);
-  REQUIRE_ALIGNED(a_scale);
-  REQUIRE_ALIGNED(w);
-  REQUIRE_ALIGNED(w_scale);
-  REQUIRE_ALIGNED(offsets);
-  REQUIRE_ALIGNED(out);
   return launch_gmm_mx(a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out, (hipStream_t)stream, true);
+}
+
+moe_status moe_gmm_mx_routed_shared(const void* a, const uint8_t* a_scale, const void* w, const uint8_t* w_scale,
+                                    const int32_t* offsets, int e, int A, int Hin, int N, moe_act act, int fp4,
+                                    void* out, const void* xs, const void* ws_w, const int32_t* offsets_s,
+                                    int e_s, int T, int Hs, int Ns, moe_act act_s, void* ys, void* stream) {
+  if (fp4 != 0 && fp4 != 1) return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(mx_checked(a, a_scale, w, w_scale, offsets, e, A, Hin, N, act, out, fp4 != 0));
+  GmmCall f{a, nullptr, w, nullptr, offsets, e, A, Hin, N, act, out, RowMap{}, a_scale, w_scale, fp4 ? 2 : 1};
+  GmmCall b;
+  void* ws_use = nullptr;
+  MOE_TRY(gmm_prepare(xs, MOE_BF16, MOE_QUANT_NONE, nullptr, ws_w, MOE_BF16, MOE_QUANT_NONE, nullptr, offsets_s,
+                      e_s, T, Hs, Ns, act_s, ys, MOE_BF16, nullptr, 0, nullptr, b, &ws_use, true));
+  if (A == 0 && T == 0) return MOE_OK;
+  return launch_gmm_pair(f, b, (hipStream_t)stream);
 }
 
 moe_status moe_sum_slots(const void* z, moe_dtype dt, int T, int K, int N, void* out, void* stream) {

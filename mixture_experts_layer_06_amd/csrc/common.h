@@ -121,11 +121,14 @@ struct GmmCall {
   moe_act act;
   void* out;
   RowMap gx;
+  const unsigned char* a_mx = nullptr;  // E8M0 block scales when mx != 0
+  const unsigned char* w_mx = nullptr;
+  int mx = 0;  // 0: E4M3 with per-tensor / per-row scales; 1: MX E4M3; 2: MX E2M1
 };
-// An E4M3 grouped GEMM f and a bf16 grouped GEMM b (bf16 out for both) in
-// one launch when both take the ping-pong kernels, else as two launch_gmm
-// calls without a workspace; either way each result equals its own
-// launch_gmm with no workspace.
+// An E4M3 (or MX E4M3 / E2M1) grouped GEMM f and a bf16 grouped GEMM b
+// (bf16 out for both) in one launch when both take the ping-pong kernels,
+// else as two launches (launch_gmm_mx / launch_gmm, no workspace); either
+// way each result equals its own launch with no workspace.
 moe_status launch_gmm_pair(const GmmCall& f, const GmmCall& b, hipStream_t s);
 // Grouped GEMM on MX (E8M0 block-scaled) operands: E4M3 (Hin % 128 == 0) or,
 // fp4, E2M1 packed two per byte along K (Hin % 256 == 0); N % 16 == 0.

@@ -1498,13 +1498,15 @@ struct GroupArgs {
   const unsigned char* w;
   const float* a_scale;
   const float* w_scale;
+  const unsigned char* a_mx;  // E8M0 block scales (MX E4M3 / E2M1 groups)
+  const unsigned char* w_mx;
   const int32_t* offsets;
   int e, A, Hin, N, relu;
   bf16_t* out;
   RowMap gx;
 };
 
-template <class C>
+template <class C, bool MX, bool FP4>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pair_kernel(GroupArgs b,
                                                                                                GroupArgs f,
                                                                                                int nb0) {
@@ -1518,7 +1520,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
     pp_block<C>(smem, s_last, q, b.a, b.w, b.a_scale, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.relu, b.out,
                 nullptr, nullptr, 1, b.gx);  // no split workspace: ncu is not used
   else
-    pp8_block<false, false>(smem, q, f.a, f.w, f.a_scale, f.w_scale, nullptr, nullptr, f.offsets, f.e,
+    pp8_block<MX, FP4>(smem, q, f.a, f.w, f.a_scale, f.w_scale, f.a_mx, f.w_mx, f.offsets, f.e,
                             f.A, f.Hin, f.N, f.relu, f.out, f.gx);
 }
 
@@ -2079,22 +2081,14 @@ moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void
 }
 
 
-moe_status launch_gmm_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
-  const bool fuse = f.A > 0 && b.A > 0 && gmm_path(MOE_FP8_E4M3, f.e, f.A, f.Hin, f.N) == GmmPath::PP8 &&
-                    gmm_path(MOE_BF16, b.e, b.A, b.Hin, b.N) == GmmPath::PP;
-  if (!fuse) {
-    moe_status st = launch_gmm(f.a, MOE_FP8_E4M3, f.a_scale, f.w, f.w_scale, f.offsets, f.e, f.A, f.Hin, f.N,
-                               f.act, f.out, MOE_BF16, nullptr, s, f.gx);
-    if (st != MOE_OK) return st;
-    return launch_gmm(b.a, MOE_BF16, b.a_scale, b.w, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.act, b.out,
-                      MOE_BF16, nullptr, s, b.gx);
-  }
+template <bool MX, bool FP4>
+moe_status launch_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
   typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
-  typedef Pp8Cfg<false> C8;
+  typedef Pp8Cfg<MX, FP4> C8;
   constexpr int kLds = CP::kLds > C8::kLds ? CP::kLds : C8::kLds;
   static bool attr_done = false;
   if (!attr_done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pair_kernel<CP>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pair_kernel<CP, MX, FP4>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     attr_done = true;
   }
@@ -2102,13 +2096,30 @@ moe_status launch_gmm_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
   const int64_t nb_b = cdiv64((cdiv64(b.A, CP::kBM) + (b.e < b.A ? b.e : b.A)) * cdiv64(b.N, CP::kBN), 8) * 8;
   const int64_t nb_f = cdiv64((cdiv64(f.A, C8::kBM) + (f.e < f.A ? f.e : f.A)) * cdiv64(f.N, C8::kBN), 8) * 8;
   if (nb_b + nb_f > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  const GroupArgs ga_b{(const unsigned char*)b.a, (const unsigned char*)b.w, b.a_scale, b.w_scale, b.offsets,
-                       b.e, b.A, b.Hin, b.N, b.act == MOE_ACT_RELU, (bf16_t*)b.out, b.gx};
-  const GroupArgs ga_f{(const unsigned char*)f.a, (const unsigned char*)f.w, f.a_scale, f.w_scale, f.offsets,
-                       f.e, f.A, f.Hin, f.N, f.act == MOE_ACT_RELU, (bf16_t*)f.out, f.gx};
-  hipLaunchKernelGGL(gmm_pair_kernel<CP>, dim3((unsigned)(nb_b + nb_f)), dim3(512), kLds, s, ga_b, ga_f,
-                     (int)(MOE_PAIR_BF16_FIRST ? nb_b : nb_f));
+  const GroupArgs ga_b{(const unsigned char*)b.a, (const unsigned char*)b.w, b.a_scale, b.w_scale, nullptr,
+                       nullptr, b.offsets, b.e, b.A, b.Hin, b.N, b.act == MOE_ACT_RELU, (bf16_t*)b.out, b.gx};
+  const GroupArgs ga_f{(const unsigned char*)f.a, (const unsigned char*)f.w, f.a_scale, f.w_scale, f.a_mx,
+                       f.w_mx, f.offsets, f.e, f.A, f.Hin, f.N, f.act == MOE_ACT_RELU, (bf16_t*)f.out, f.gx};
+  hipLaunchKernelGGL((gmm_pair_kernel<CP, MX, FP4>), dim3((unsigned)(nb_b + nb_f)), dim3(512), kLds, s, ga_b,
+                     ga_f, (int)(MOE_PAIR_BF16_FIRST ? nb_b : nb_f));
   return launch_status();
+}
+
+moe_status launch_gmm_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
+  const bool f_ok = f.mx != 0 || gmm_path(MOE_FP8_E4M3, f.e, f.A, f.Hin, f.N) == GmmPath::PP8;
+  const bool fuse = f.A > 0 && b.A > 0 && f_ok && gmm_path(MOE_BF16, b.e, b.A, b.Hin, b.N) == GmmPath::PP;
+  if (!fuse) {
+    moe_status st = f.mx != 0 ? launch_gmm_mx(f.a, f.a_mx, f.w, f.w_mx, f.offsets, f.e, f.A, f.Hin, f.N, f.act,
+                                              f.out, s, f.mx == 2)
+                              : launch_gmm(f.a, MOE_FP8_E4M3, f.a_scale, f.w, f.w_scale, f.offsets, f.e, f.A,
+                                           f.Hin, f.N, f.act, f.out, MOE_BF16, nullptr, s, f.gx);
+    if (st != MOE_OK) return st;
+    return launch_gmm(b.a, MOE_BF16, b.a_scale, b.w, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.act, b.out,
+                      MOE_BF16, nullptr, s, b.gx);
+  }
+  if (f.mx == 2) return launch_pair<true, true>(f, b, s);
+  if (f.mx == 1) return launch_pair<true, false>(f, b, s);
+  return launch_pair<false, false>(f, b, s);
 }
 
 }  // namespace moe

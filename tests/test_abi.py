@@ -23,7 +23,7 @@ def declared_entry_points():
 def test_header_declares_expected_entry_points():
     names = declared_entry_points()
     for n in ("moe_route", "moe_permute", "moe_gmm", "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_mx",
-              "moe_gmm_mxfp4", "moe_gmm_routed_shared",
+              "moe_gmm_mxfp4", "moe_gmm_routed_shared", "moe_gmm_mx_routed_shared",
               "moe_combine", "moe_sum_slots", "moe_quant_rows", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size", "moe_layer_fp8", "moe_layer_fp8_workspace_size",
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.lib().moe_version() == 11100
+    assert moe.lib().moe_version() == 11200
     seen = set()
     for s in range(8):
         msg = moe.status_string(s)
@@ -367,6 +367,35 @@ def test_gmm_routed_shared_validation(kw, status):
 def test_gmm_routed_shared_empty_parts_are_noop():
     assert gmm_routed_shared(a=None, w=None, off=None, dst=None, out=None, A=0, xs=None, ws_w=None, off_s=None,
                              ys=None, T=0) == moe.OK
+
+
+def gmm_mx_routed_shared(a=P, sa=P, w=P, sw=P, off=P, e=8, A=100, Hin=256, N=64, act=moe.ACT_NONE, fp4=0, out=P,
+                         xs=P, ws_w=P, off_s=P, e_s=1, T=64, Hs=128, Ns=64, act_s=moe.ACT_NONE, ys=P):
+    return L.moe_gmm_mx_routed_shared(a, sa, w, sw, off, e, A, Hin, N, act, fp4, out, xs, ws_w, off_s, e_s, T, Hs,
+                                      Ns, act_s, ys, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fp4=2), moe.ERR_UNSUPPORTED),
+    (dict(Hin=192), moe.ERR_UNSUPPORTED),                             # routed part: moe_gmm_mx's rules
+    (dict(Hin=384, fp4=1), moe.ERR_UNSUPPORTED),                      # ... and moe_gmm_mxfp4's
+    (dict(N=40), moe.ERR_UNSUPPORTED),
+    (dict(sa=None), moe.ERR_NULL_POINTER),
+    (dict(sw=MIS), moe.ERR_MISALIGNED),
+    (dict(act=4), moe.ERR_UNSUPPORTED),
+    (dict(e=300), moe.ERR_BAD_SHAPE),
+    (dict(xs=None), moe.ERR_NULL_POINTER),                            # shared part: moe_gmm's rules
+    (dict(ys=MIS), moe.ERR_MISALIGNED),
+    (dict(Hs=0), moe.ERR_BAD_SHAPE),
+    (dict(act_s=3), moe.ERR_UNSUPPORTED),
+])
+def test_gmm_mx_routed_shared_validation(kw, status):
+    assert gmm_mx_routed_shared(**kw) == status
+
+
+def test_gmm_mx_routed_shared_empty_parts_are_noop():
+    assert gmm_mx_routed_shared(a=None, sa=None, w=None, sw=None, off=None, out=None, A=0, xs=None, ws_w=None,
+                                off_s=None, ys=None, T=0) == moe.OK
 
 
 def quant_rows(x=P, dt=moe.BF16, x_rows=10, H=64, src=None, div=1, rows=10, q=P, sc=P):

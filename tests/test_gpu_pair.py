@@ -144,3 +144,48 @@ def test_routed_shared_full_size_fp8_workload():
     sref = oracle.gmm(d["mm_x"], d["mm_w"].reshape(1, H2, N2), np.array([0, T], np.int32), rows=srows,
                       nthreads=16)
     assert normwise_err(my_h[srows], sref) <= 8e-3
+
+
+# (name, routed expert counts, Hin, N, shared T, Hs, Ns, fp4)
+MX_CASES = [
+    ("mx_e4m3", [300, 0, 17, 513, 256, 95], 384, 272, 700, 384, 400, False),
+    ("mx_e2m1", [129, 640, 0, 255, 77], 512, 400, 513, 256, 256, True),
+    ("mx_e2m1_shared_streams", [200, 0, 333], 256, 128, 40, 256, 256, True),   # T <= 48: two launches
+    ("mx_e4m3_routed_empty", [0, 0], 256, 128, 300, 256, 256, False),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=[c[0] for c in MX_CASES])
+def test_mx_routed_shared_equals_separate_calls_and_oracle(case):
+    """The MX variant: the routed part equals moe_gmm_mx / moe_gmm_mxfp4 and the
+    shared part moe_gmm, bit for bit, and both match the oracle."""
+    name, counts, Hin, N, T, Hs, Ns, fp4 = case
+    e = len(counts)
+    off = _offsets(counts)
+    A = int(off[-1])
+    seed = 1300 + 7 * len(name) + A
+    quant = synth.quantize_mx4 if fp4 else synth.quantize_mx
+    if A:
+        a, sa = quant(synth.normal(seed, (A, Hin)), axis=1)
+    else:
+        a, sa = np.zeros((0, Hin // 2 if fp4 else Hin), np.uint8), np.zeros((0, Hin // 32), np.uint8)
+    w, sw = quant(synth.normal(seed + 1, (e, Hin, N), math.sqrt(1.0 / Hin)), axis=1)
+    xs = synth.normal(seed + 2, (T, Hs), dtype="bf16")
+    wsw = synth.normal(seed + 3, (1, Hs, Ns), math.sqrt(1.0 / Hs), dtype="bf16")
+    ad, sad = to_dev(a), to_dev(synth.mx_scales_slice_major(sa, 8 if fp4 else 4))
+    wd, swd, od = to_dev(w), to_dev(synth.mx_weight_scales_interleaved(sw)), to_dev(off)
+    xsd, wswd, osd = to_dev(xs), to_dev(wsw), to_dev(np.array([0, T], np.int32))
+    print(f"case {name}: A={A} Hin={Hin} N={N} T={T} Hs={Hs} Ns={Ns} fp4={fp4}", flush=True)
+    out, ys = moe.gmm_mx_routed_shared(ad, sad, wd, swd, od, xsd, wswd, osd, fp4=fp4, act=moe.ACT_RELU,
+                                       act_s=moe.ACT_RELU)
+    torch.cuda.synchronize()
+    out_h, ys_h = to_host(out), to_host(ys)
+    if A:
+        sep = (moe.gmm_mxfp4 if fp4 else moe.gmm_mx)(ad, sad, wd, swd, od, act=moe.ACT_RELU)
+        assert np.array_equal(out_h, to_host(sep)), name
+        ref = (oracle.gmm_mx4 if fp4 else oracle.gmm_mx)(a, sa, w, sw, off, act=moe.ACT_RELU, nthreads=8)
+        assert normwise_err(out_h, ref) <= 8e-3, name
+    sep_s = moe.gmm(xsd, wswd, osd, act=moe.ACT_RELU)
+    assert np.array_equal(ys_h, to_host(sep_s)), name
+    sref = oracle.gmm(xs, wsw, np.array([0, T], np.int32), act=moe.ACT_RELU, nthreads=8)
+    assert normwise_err(ys_h, sref) <= 8e-3, name
