@@ -54,7 +54,7 @@ typedef enum {
   MOE_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
   MOE_ERR_BAD_SHAPE = 2,           /* a size is out of range or inconsistent */
   MOE_ERR_BAD_DTYPE = 3,           /* an element-type code is unknown or not allowed here */
-  MOE_ERR_UNSUPPORTED = 4,         /* a valid mode this build does not implement */
+  MOE_ERR_UNSUPPORTED = 4,         /* a valid mode the library does not implement */
   MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes below the *_workspace_size answer */
   MOE_ERR_MISALIGNED = 6,          /* a device pointer is not 16-byte aligned */
   MOE_ERR_DEVICE = 7               /* the HIP runtime reported an error */
