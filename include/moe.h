@@ -64,8 +64,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
 /* Quantisation modes, numbered as in "aclnnQuantGroupedMatMulAlltoAllv"
  * (parameter list): 0 none, 1 per-tensor, 2 per-channel, 3 per-token,
- * 4 per-group, 5 per-block, 6 mx, 7 dynamic per-token. Modes 2..7 return
- * MOE_ERR_UNSUPPORTED. */
+ * 4 per-group, 5 per-block, 6 mx, 7 dynamic per-token. moe_gmm and its
+ * variants take modes 0 and 1, and mode 3 for the activations of an E4M3
+ * product (per-row scales); mode 6 has entry points of its own
+ * (moe_gmm_mx, moe_gmm_mxfp4); mode 7 is moe_quant_rows followed by mode 3.
+ * Modes 2, 4, 5 and 7 passed to moe_gmm, and mode 3 for the weights or for a
+ * product that is not E4M3, return MOE_ERR_UNSUPPORTED. */
 typedef enum {
   MOE_QUANT_NONE = 0,
   MOE_QUANT_PER_TENSOR = 1,
@@ -354,13 +358,16 @@ moe_status moe_sum_slots(const void* z, moe_dtype dt, int T, int K, int N, void*
 /*
  * moe_quant_rows — per-token dynamic quantisation to E4M3 (quant modes 3
  * "pertoken" and 7 "pertoken dynamic" of "aclnnQuantGroupedMatMulAlltoAllv",
- * 量化模式 enumeration). Output row r quantises source row
- * t = row_src ? row_src[r] / row_div : r of x, in binary32:
- *   scale[r] = max_h |x[t,h]| / 448
- *   q[r,h]   = the E4M3 value nearest to x[t,h] / scale[r], ties to the even
- *              code, saturating at +-448 (OCP E4M3, no infinities)
- * A zero row, or a source row outside [0, x_rows) (not checked on the host),
- * gives codes 0 and scale 0. With row_src = perm_src of moe_permute and
+ * 量化模式 enumeration; the page gives no formula, this is the plain
+ * reading). Output row r quantises source row
+ * t = row_src ? row_src[r] / row_div : r of x:
+ *   scale[r] = max_h |x[t,h]| / 448, one binary32 division rounded to nearest
+ *   q[r,h]   = the E4M3 value nearest to the exact quotient x[t,h] / scale[r],
+ *              ties to the even code, saturating at +-448 (OCP E4M3, no
+ *              infinities)
+ * A zero row, a row whose max / 448 rounds to zero in binary32, or a source
+ * row outside [0, x_rows) (not checked on the host), gives codes 0 and scale
+ * 0. Non-finite inputs give unspecified codes. With row_src = perm_src of moe_permute and
  * row_div = K the dispatch copy and the quantisation are one pass (gmmX in
  * E4M3 with its per-row gmmXScale); with row_src = NULL the tokens are
  * quantised once and moe_gmm_gather reads them (and their scales) by index.

@@ -53,6 +53,7 @@ def lib():
         L.orc_bf16_bits.argtypes = [dbl]
         L.orc_bf16_bits.restype = ctypes.c_uint16
         L.orc_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp]
+        L.orc_route_given.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.orc_gather_rows.argtypes = [vp, i64, vp, i32, i32, vp]
         L.orc_gmm.argtypes = [vp, i32, dbl, vp, i32, dbl, vp, i32, i32, i32, i32, vp, i32, vp, i32]
@@ -61,6 +62,10 @@ def lib():
                                          i32]
         L.orc_e4m3_nearest.argtypes = [ctypes.c_float]
         L.orc_e4m3_nearest.restype = ctypes.c_uint8
+        L.orc_e4m3_nearest_ratio.argtypes = [dbl, dbl]
+        L.orc_e4m3_nearest_ratio.restype = ctypes.c_uint8
+        L.orc_div448_f32.argtypes = [dbl]
+        L.orc_div448_f32.restype = ctypes.c_float
         L.orc_e4m3_nearest_array.argtypes = [vp, i64, vp]
         L.orc_quant_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp]
         L.orc_gmm_mx4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32]
@@ -74,8 +79,11 @@ def lib():
                                 vp, i32]
         L.orc_layer_tokens.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
                                        vp, vp, vp, vp, i32]
+        L.orc_layer_tokens_given.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
+                                             vp, vp, vp, vp, vp, i32]
         L.orc_layer_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
-        for name in ("orc_decode_array", "orc_route", "orc_permute", "orc_gather_rows", "orc_gmm", "orc_gmm_mx",
+        for name in ("orc_decode_array", "orc_route", "orc_route_given", "orc_layer_tokens_given",
+                     "orc_permute", "orc_gather_rows", "orc_gmm", "orc_gmm_mx",
                      "orc_gmm_row_scaled", "orc_e4m3_nearest_array", "orc_quant_rows", "orc_gmm_mx4",
                      "orc_combine", "orc_expert_ffn", "orc_layer", "orc_layer_tokens",
                      "orc_layer_dense"):
@@ -136,6 +144,23 @@ def route(x, wr, T, H, E, K, bias=None):
     gap = np.empty(T, np.float64)
     _check(lib().orc_route(px, pw, _code(x), _p(b), T, H, E, K, _p(idx), _p(gate), _p(logits),
                            _p(gap)), "route")
+    return idx, gate, logits, gap
+
+
+def route_given(x, wr, T, H, E, K, given, bias=None):
+    """Router scores with the K experts of each token given ((T,K), e.g. a
+    selection made elsewhere): gates over the given experts' scores in the
+    given slot order. Returns (idx, gate, logits, gap); gap is the full sort's."""
+    x, px = _c(x)
+    wr, pw = _c(wr)
+    gv, pg = _c(np.asarray(given, np.int32).reshape(T, K))
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), np.float64)
+    logits = np.empty((T, E), np.float64)
+    gap = np.empty(T, np.float64)
+    _check(lib().orc_route_given(px, pw, _code(x), _p(b), T, H, E, K, pg, _p(idx), _p(gate), _p(logits),
+                                 _p(gap)), "route_given")
     return idx, gate, logits, gap
 
 
@@ -213,11 +238,23 @@ def e4m3_nearest(v) -> np.ndarray:
     return out
 
 
+def e4m3_nearest_ratio(num: float, den: float) -> int:
+    """E4M3 code of the value nearest to the exact quotient num / den (den a
+    positive binary32 number), by exact comparisons; ties to the even code."""
+    return int(lib().orc_e4m3_nearest_ratio(float(num), float(den)))
+
+
+def div448_f32(amax: float) -> np.float32:
+    """amax / 448 rounded to the nearest binary32 number (ties to even)."""
+    return np.float32(lib().orc_div448_f32(float(amax)))
+
+
 def quant_rows(x, rows=None, div=1):
-    """Per-token dynamic E4M3 quantisation (binary32 arithmetic): for each
-    output row, the source row t = rows[r] // div (or r), scale = max|x[t]| / 448,
-    codes = nearest E4M3 of x[t] * (448 / max|x[t]|). Returns (codes (R,H)
-    uint8, scales (R,) float32)."""
+    """Per-token dynamic E4M3 quantisation: for each output row, the source row
+    t = rows[r] // div (or r), scale = max|x[t]| / 448 rounded to binary32,
+    codes = the E4M3 values nearest to the exact quotients x[t] / scale (ties
+    to even). x in binary32, bfloat16 (uint16) or binary64. Returns (codes
+    (R,H) uint8, scales (R,) float32)."""
     x, px = _c(x)
     n, H = x.shape
     if rows is None:
@@ -331,34 +368,46 @@ def layer(x, wr, w1, w2, K, bias=None, act=ACT_RELU, nthreads=1):
     return {"y": y, "idx": idx, "gate": gate, "gap": gap, "counts": counts}
 
 
-def layer_fp8(x, wr, w1, w1_scale, w2, w2_scale, K, bias=None, act=ACT_RELU, tokens=None, nthreads=1):
+def layer_fp8(x, wr, w1, w1_scale, w2, w2_scale, K, bias=None, act=ACT_RELU, tokens=None, given=None,
+              hidden="f64", nthreads=1):
     """The layer with E4M3 experts and per-token dynamic quantisation
     ("aclnnQuantGroupedMatMulAlltoAllv": quant mode 7 for the activations,
     per-tensor weight scales, gmmY = (gmmX @ W) * gmmXScale * wScale), composed
     from the functions above: route the bf16 tokens, permute, quantise each
-    token, GEMM 1 on the dispatched codes with their tokens' scales, the hidden
-    rows rounded to bf16 (the layer type) and quantised per row, GEMM 2, the
-    weighted combine. Every token is independent, so `tokens` (indices)
-    computes just those tokens. Returns dict with y, idx, gate, gap, counts."""
+    token, GEMM 1 on the dispatched codes with their tokens' scales, the fp64
+    hidden rows quantised per row, GEMM 2, the weighted combine. Every token is
+    independent, so `tokens` (indices) computes just those tokens. `given`
+    ((T,K), or (len(tokens),K)) replaces the router's selection by the given
+    experts (gates over their scores). hidden="bf16" rounds the hidden rows to
+    bfloat16 before quantising them, as a layer that stores them in bf16 does
+    (a diagnostic mirror of that storage step; the default keeps them in
+    fp64). Returns dict with y, idx, gate, gap, counts."""
     x = np.asarray(x)
     if tokens is not None:
         x = x[np.asarray(tokens)]
     T, H = x.shape
     E = w1.shape[0]
-    idx, gate, _, gap = route(x, wr, T, H, E, K, bias=bias)
+    if given is None:
+        idx, gate, _, gap = route(x, wr, T, H, E, K, bias=bias)
+    else:
+        idx, gate, _, gap = route_given(x, wr, T, H, E, K, given, bias=bias)
     counts, off, psrc, pdst = permute(idx, E)
     xq, xs = quant_rows(x)
     tok = psrc // K
     hm = gmm(xq[tok], w1, off, act=act, a_scale=xs[tok].astype(np.float64), w_scale=float(w1_scale),
              nthreads=nthreads)
-    hq, hs = quant_rows(bf16_bits(hm))
+    if hidden not in ("f64", "bf16"):
+        raise ValueError("hidden must be 'f64' or 'bf16'")
+    hq, hs = quant_rows(hm if hidden == "f64" else bf16_bits(hm))
     yp = gmm(hq, w2, off, a_scale=hs.astype(np.float64), w_scale=float(w2_scale), nthreads=nthreads)
     y = combine(yp, pdst, gate, T, K)
     return {"y": y, "idx": idx, "gate": gate, "gap": gap, "counts": counts}
 
 
-def layer_tokens(x, wr, w1, w2, K, tokens, bias=None, act=ACT_RELU, nthreads=1):
-    """Per-token form on a subset of tokens. Returns dict with y, idx, gate, gap."""
+def layer_tokens(x, wr, w1, w2, K, tokens, bias=None, act=ACT_RELU, given=None, nthreads=1):
+    """Per-token form on a subset of tokens. `given` ((len(tokens),K))
+    replaces the router's selection by the given experts (gates over their
+    scores). Returns dict with y, idx, gate, gap."""
     x, px = _c(x)
     wr, pwr = _c(wr)
     w1, p1 = _c(w1)
@@ -368,12 +417,13 @@ def layer_tokens(x, wr, w1, w2, K, tokens, bias=None, act=ACT_RELU, nthreads=1):
     tok, ptok = _c(np.asarray(tokens, np.int32))
     b = None if bias is None else np.ascontiguousarray(bias, np.float32)
     n = tok.size
+    gv = None if given is None else np.ascontiguousarray(np.asarray(given, np.int32).reshape(n, K))
     y = np.empty((n, H), np.float64)
     idx = np.empty((n, K), np.int32)
     gate = np.empty((n, K), np.float64)
     gap = np.empty(n, np.float64)
-    _check(lib().orc_layer_tokens(px, pwr, _p(b), p1, p2, _code(x), T, H, E, K, F, act, ptok, n,
-                                  _p(y), _p(idx), _p(gate), _p(gap), int(nthreads)), "layer_tokens")
+    _check(lib().orc_layer_tokens_given(px, pwr, _p(b), p1, p2, _code(x), T, H, E, K, F, act, ptok, n, _p(gv),
+                                        _p(y), _p(idx), _p(gate), _p(gap), int(nthreads)), "layer_tokens")
     return {"y": y, "idx": idx, "gate": gate, "gap": gap}
 
 

@@ -151,10 +151,19 @@ static int orc_score_cmp(const void* pa, const void* pb) {
   return (a->e > b->e) - (a->e < b->e);
 }
 
+/* O1 for token t (scores into sc[E], bias added), then either O2 (full
+ * sort) or, when `given` holds K expert indices, that selection as it
+ * stands; O3 over the selected scores in slot order. gap: the K-th minus the
+ * (K+1)-th largest score of the full sort, in both cases. */
 static int route_one(const void* x, const void* wr, int dt, const float* bias, int t, int H, int E,
-                     int K, int32_t* idx, double* gate, double* logits, double* gap) {
+                     int K, const int32_t* given, int32_t* idx, double* gate, double* logits, double* gap) {
   orc_score* s = (orc_score*)malloc(sizeof(orc_score) * (size_t)E);
-  if (!s) return -2;
+  double* sc = (double*)malloc(sizeof(double) * (size_t)E);
+  if (!s || !sc) {
+    free(s);
+    free(sc);
+    return -2;
+  }
   for (int e = 0; e < E; ++e) {
     double acc = 0.0;
     for (int h = 0; h < H; ++h)
@@ -162,27 +171,39 @@ static int route_one(const void* x, const void* wr, int dt, const float* bias, i
     if (bias) acc += (double)bias[e];
     s[e].v = acc;
     s[e].e = e;
+    sc[e] = acc;
     if (logits) logits[(int64_t)t * E + e] = acc;
   }
   qsort(s, (size_t)E, sizeof(orc_score), orc_score_cmp); /* brute-force full sort */
-  double denom = 0.0;
-  for (int k = 0; k < K; ++k) denom += exp(s[k].v - s[0].v);
+  int rc = 0;
   for (int k = 0; k < K; ++k) {
-    idx[k] = s[k].e;
-    gate[k] = exp(s[k].v - s[0].v) / denom;
+    idx[k] = given ? given[k] : s[k].e;
+    if (idx[k] < 0 || idx[k] >= E) rc = -1;
+  }
+  if (rc == 0) {
+    double denom = 0.0;
+    for (int k = 0; k < K; ++k) denom += exp(sc[idx[k]] - sc[idx[0]]);
+    for (int k = 0; k < K; ++k) gate[k] = exp(sc[idx[k]] - sc[idx[0]]) / denom;
   }
   if (gap) *gap = (K < E) ? (s[K - 1].v - s[K].v) : INFINITY;
   free(s);
-  return 0;
+  free(sc);
+  return rc;
 }
 
 int orc_route(const void* x, const void* wr, int dt, const float* bias, int T, int H, int E, int K,
               int32_t* topk_idx, double* topk_gate, double* logits, double* gap) {
+  return orc_route_given(x, wr, dt, bias, T, H, E, K, NULL, topk_idx, topk_gate, logits, gap);
+}
+
+int orc_route_given(const void* x, const void* wr, int dt, const float* bias, int T, int H, int E, int K,
+                    const int32_t* given, int32_t* topk_idx, double* topk_gate, double* logits,
+                    double* gap) {
   if (!x || !wr || !topk_idx || !topk_gate) return -1;
   if (T < 0 || H <= 0 || E <= 0 || K <= 0 || K > E) return -1;
   for (int t = 0; t < T; ++t) {
-    int rc = route_one(x, wr, dt, bias, t, H, E, K, topk_idx + (int64_t)t * K,
-                       topk_gate + (int64_t)t * K, logits, gap ? gap + t : NULL);
+    int rc = route_one(x, wr, dt, bias, t, H, E, K, given ? given + (int64_t)t * K : NULL,
+                       topk_idx + (int64_t)t * K, topk_gate + (int64_t)t * K, logits, gap ? gap + t : NULL);
     if (rc) return rc;
   }
   return 0;
@@ -308,33 +329,45 @@ int orc_gmm_row_scaled(const void* a, int a_dt, const double* a_row_scale, const
 /* Per-token E4M3 quantisation                                          */
 /* ------------------------------------------------------------------ */
 
-/* Codes 0x00 .. 0x7e are the non-negative finite E4M3 values in increasing
- * order (the exponent field sits above the mantissa field), so the nearest
- * value is found by bisection over the codes. */
-uint8_t orc_e4m3_nearest(float v) {
-  if (isnan(v)) return 0x7f;
-  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
-  const double a = fabs((double)v);
-  uint8_t one = 0;
-  if (a >= 448.0) return sign | 0x7e;
-  int lo = 0, hi = 0x7e; /* value(lo) <= a < value(hi) */
+static double e4m3_value(int code) {
+  const uint8_t b = (uint8_t)code;
+  return dec_e4m3(&b, 0);
+}
+
+/* The finite E4M3 value nearest to num/den, decided without forming the
+ * quotient: |num| is compared with v*den for the E4M3 values v and with
+ * m*den for the midpoints m between neighbours. E4M3 values have at most 4
+ * significant bits and midpoints 5, so with den a binary32 number (24 bits)
+ * every such product is exact in binary64 and every comparison is exact.
+ * Codes 0x00 .. 0x7e are the non-negative finite values in increasing order
+ * (the exponent field sits above the mantissa field), so a bisection over
+ * the codes brackets |num|. Ties go to the even code (mantissa bit 0 clear);
+ * |num/den| at or above 448 gives +-448; NaN gives 0x7f. */
+uint8_t orc_e4m3_nearest_ratio(double num, double den) {
+  if (isnan(num) || !(den > 0.0)) return 0x7f;
+  const uint8_t sign = signbit(num) ? 0x80 : 0x00;
+  const double a = fabs(num);
+  if (a >= 448.0 * den) return sign | 0x7e;
+  int lo = 0, hi = 0x7e; /* value(lo) * den <= a < value(hi) * den */
   while (hi - lo > 1) {
-    int mid = (lo + hi) / 2;
-    if (dec_e4m3(&(uint8_t){(uint8_t)mid}, 0) <= a)
+    const int mid = (lo + hi) / 2;
+    if (e4m3_value(mid) * den <= a)
       lo = mid;
     else
       hi = mid;
   }
-  const double dl = a - dec_e4m3(&(uint8_t){(uint8_t)lo}, 0);
-  const double dh = dec_e4m3(&(uint8_t){(uint8_t)hi}, 0) - a;
-  if (dl < dh)
-    one = (uint8_t)lo;
-  else if (dh < dl)
-    one = (uint8_t)hi;
+  const double m = 0.5 * (e4m3_value(lo) + e4m3_value(hi)) * den;
+  int one;
+  if (a < m)
+    one = lo;
+  else if (a > m)
+    one = hi;
   else
-    one = (uint8_t)((lo & 1) ? hi : lo); /* tie: the even code */
-  return sign | one;
+    one = (lo & 1) ? hi : lo; /* tie: the even code */
+  return sign | (uint8_t)one;
 }
+
+uint8_t orc_e4m3_nearest(float v) { return orc_e4m3_nearest_ratio((double)v, 1.0); }
 
 int orc_e4m3_nearest_array(const float* v, int64_t n, uint8_t* out) {
   if (!v || !out || n < 0) return -1;
@@ -342,10 +375,37 @@ int orc_e4m3_nearest_array(const float* v, int64_t n, uint8_t* out) {
   return 0;
 }
 
+static uint32_t f32_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+/* amax / 448 rounded to the nearest binary32 number, ties to even. A first
+ * guess from one binary64 division is moved to whichever neighbour is nearer,
+ * judged by comparing amax with 448 times the midpoint between two adjacent
+ * binary32 numbers (25 significant bits times 3: exact in binary64). */
+float orc_div448_f32(double amax) {
+  float s = (float)(amax / 448.0);
+  for (int guard = 0; guard < 4; ++guard) {
+    const float up = nextafterf(s, INFINITY), dn = nextafterf(s, 0.0f);
+    const double mu = 0.5 * ((double)s + (double)up) * 448.0;
+    const double md = 0.5 * ((double)s + (double)dn) * 448.0;
+    const int odd = (int)(f32_bits(s) & 1u);
+    if (amax > mu || (amax == mu && odd))
+      s = up;
+    else if (dn != s && (amax < md || (amax == md && odd)))
+      s = dn;
+    else
+      break;
+  }
+  return s;
+}
+
 int orc_quant_rows(const void* x, int x_dt, int x_rows, int H, const int32_t* src, int div, int rows,
                    uint8_t* q, float* scale) {
   if (!x || !q || !scale || x_rows < 0 || H <= 0 || rows < 0 || div < 1) return -1;
-  if (x_dt != ORC_F32 && x_dt != ORC_BF16) return -1;
+  if (x_dt != ORC_F32 && x_dt != ORC_BF16 && x_dt != ORC_F64) return -1;
   for (int r = 0; r < rows; ++r) {
     int64_t t = r;
     if (src) t = src[r] >= 0 ? src[r] / div : -1;
@@ -355,21 +415,15 @@ int orc_quant_rows(const void* x, int x_dt, int x_rows, int H, const int32_t* sr
       scale[r] = 0.0f;
       continue;
     }
-    float amax = 0.0f;
+    double amax = 0.0;
     for (int h = 0; h < H; ++h) {
-      float xv = (float)orc_decode(x, x_dt, t * H + h); /* exact: bf16 and f32 are binary32 values */
-      if (fabsf(xv) > amax) amax = fabsf(xv);
+      const double v = fabs(orc_decode(x, x_dt, t * H + h));
+      if (v > amax) amax = v;
     }
-    scale[r] = amax / 448.0f;
-    const float inv = 448.0f / amax; /* the inverse scale, one division per row */
-    for (int h = 0; h < H; ++h) {
-      if (amax == 0.0f) {
-        qr[h] = 0;
-        continue;
-      }
-      float xv = (float)orc_decode(x, x_dt, t * H + h);
-      qr[h] = orc_e4m3_nearest(xv * inv);
-    }
+    const float s = orc_div448_f32(amax);
+    scale[r] = s;
+    for (int h = 0; h < H; ++h)
+      qr[h] = (s > 0.0f) ? orc_e4m3_nearest_ratio(orc_decode(x, x_dt, t * H + h), (double)s) : 0;
   }
   return 0;
 }
@@ -617,6 +671,7 @@ typedef struct {
   const float* bias;
   int dt, T, H, E, K, F, act;
   const int32_t* tokens;
+  const int32_t* given;
   double* y;
   int32_t* idx;
   double* gate;
@@ -637,8 +692,8 @@ static void orc_token_task(void* p, int64_t j) {
     free(xv); free(eo);
     return;
   }
-  if (route_one(c->x, c->wr, c->dt, c->bias, t, c->H, c->E, c->K, idx, gate, NULL,
-                c->gap ? c->gap + j : NULL)) {
+  if (route_one(c->x, c->wr, c->dt, c->bias, t, c->H, c->E, c->K, c->given ? c->given + j * c->K : NULL,
+                idx, gate, NULL, c->gap ? c->gap + j : NULL)) {
     c->bad = 1;
   }
   for (int h = 0; h < c->H; ++h) {
@@ -657,12 +712,20 @@ int orc_layer_tokens(const void* x, const void* wr, const float* bias, const voi
                      int dt, int T, int H, int E, int K, int F, int act, const int32_t* tokens,
                      int ntok, double* y, int32_t* topk_idx, double* topk_gate, double* gap,
                      int nthreads) {
+  return orc_layer_tokens_given(x, wr, bias, w1, w2, dt, T, H, E, K, F, act, tokens, ntok, NULL, y, topk_idx,
+                                topk_gate, gap, nthreads);
+}
+
+int orc_layer_tokens_given(const void* x, const void* wr, const float* bias, const void* w1, const void* w2,
+                           int dt, int T, int H, int E, int K, int F, int act, const int32_t* tokens,
+                           int ntok, const int32_t* given, double* y, int32_t* topk_idx, double* topk_gate,
+                           double* gap, int nthreads) {
   if (!x || !wr || !w1 || !w2 || !tokens || !y || ntok < 0) return -1;
   if (T <= 0 || H <= 0 || E <= 0 || K <= 0 || K > E || F <= 0) return -1;
   int32_t* idx = topk_idx ? topk_idx : (int32_t*)malloc(sizeof(int32_t) * (size_t)ntok * K + 1);
   double* g = topk_gate ? topk_gate : (double*)malloc(sizeof(double) * (size_t)ntok * K + 1);
   if (!idx || !g) return -2;
-  orc_tok_ctx c = {x, wr, w1, w2, bias, dt, T, H, E, K, F, act, tokens, y, idx, g, gap, 0};
+  orc_tok_ctx c = {x, wr, w1, w2, bias, dt, T, H, E, K, F, act, tokens, given, y, idx, g, gap, 0};
   orc_parallel_for(ntok, nthreads, orc_token_task, &c);
   if (!topk_idx) free(idx);
   if (!topk_gate) free(g);

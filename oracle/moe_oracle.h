@@ -29,7 +29,8 @@
  *   - the softmax is max-subtracted, no temperature;
  *   - the optional router bias is added before both selection and softmax;
  *   - the expert FFN is act(x . W1[e]) . W2[e] with no biases;
- *   - the hidden activation is kept in fp64 here;
+ *   - the hidden activation is kept in fp64 here (also where it is
+ *     quantised per row before the second GEMM);
  *   - the scaled GEMM applies the activation after the scales:
  *     act(acc * xScale * wScale);
  *   - rows are placed stably: inside one expert's block, rows appear in
@@ -73,6 +74,14 @@ uint16_t orc_bf16_bits(double v);
  *   the (k+1)-th largest score (+inf when K == E). */
 int orc_route(const void* x, const void* wr, int dt, const float* bias, int T, int H, int E, int K,
               int32_t* topk_idx, double* topk_gate, double* logits, double* gap);
+/* The same scores, with the K experts of each token taken from `given`
+ * (T,K) instead of the sort (each index in [0,E), else -1): the gates are O3
+ * over the given experts' scores in the given slot order, and gap is still
+ * that of the full sort. Used to evaluate a selection made elsewhere on
+ * tokens whose k-th and (k+1)-th scores nearly tie. */
+int orc_route_given(const void* x, const void* wr, int dt, const float* bias, int T, int H, int E, int K,
+                    const int32_t* given, int32_t* topk_idx, double* topk_gate, double* logits,
+                    double* gap);
 
 /* O4-O5: counts[E], offsets[E+1] (exclusive scan), and the stable row map.
  *   perm_src[row] = t*K + k ; perm_dst[t*K + k] = row. */
@@ -118,17 +127,26 @@ int orc_gmm_mx4(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, cons
 
 /* Per-token quantisation to E4M3 (quant modes 3 "pertoken" and 7 "pertoken
  * dynamic" of "aclnnQuantGroupedMatMulAlltoAllv", 量化模式 enumeration; the
- * formula there multiplies gmmX's scale back onto the product).
- * orc_e4m3_nearest: the code of the finite E4M3 value nearest to v, ties to
- * the even code (mantissa bit 0 clear); |v| above 448 gives +-448, NaN 0x7f.
- * orc_quant_rows: row r of q is source row t = src ? src[r] / div : r of x
- * (x_rows rows, H values each, in x_dt); in binary32 arithmetic: amax = the
- * largest |x[t,h]|, scale[r] = amax / 448, q[r,h] = nearest(x[t,h] * inv) with
- * the inverse scale inv = 448 / amax (the pages name the mode but give no
- * formula; one division per row, then products, is the reading taken);
- * amax == 0 or a source row outside [0, x_rows): all codes 0, scale 0. */
+ * formula there multiplies gmmX's scale back onto the product, so the codes
+ * are the row divided by its scale). The page names the modes and gives no
+ * formula; the plain reading taken here:
+ *   amax     = max_h |x[t,h]|                          (exact)
+ *   scale[r] = amax / 448 rounded to binary32          (448: E4M3's largest value)
+ *   q[r,h]   = the E4M3 value nearest to the exact quotient x[t,h] / scale[r],
+ *              ties to the even code
+ * for output row r with source row t = src ? src[r] / div : r (x_rows rows,
+ * H values each, in x_dt: binary32, bfloat16 or binary64). A source row
+ * outside [0, x_rows), an all-zero row, or a row whose amax / 448 rounds to
+ * zero in binary32 gives codes 0 and scale 0.
+ * orc_e4m3_nearest_ratio: the code of the finite E4M3 value nearest to
+ * num / den (den > 0 with at most 24 significant bits, e.g. a binary32
+ * number), decided by exact comparisons; |num / den| >= 448 gives +-448, NaN
+ * 0x7f. orc_e4m3_nearest(v) is the same with den = 1.
+ * orc_div448_f32: amax / 448 rounded to the nearest binary32 number. */
+uint8_t orc_e4m3_nearest_ratio(double num, double den);
 uint8_t orc_e4m3_nearest(float v);
 int orc_e4m3_nearest_array(const float* v, int64_t n, uint8_t* out);
+float orc_div448_f32(double amax);
 int orc_quant_rows(const void* x, int x_dt, int x_rows, int H, const int32_t* src, int div, int rows,
                    uint8_t* q, float* scale);
 
@@ -162,6 +180,12 @@ int orc_layer_tokens(const void* x, const void* wr, const float* bias, const voi
                      int dt, int T, int H, int E, int K, int F, int act, const int32_t* tokens,
                      int ntok, double* y, int32_t* topk_idx, double* topk_gate, double* gap,
                      int nthreads);
+/* The same with each listed token's experts given ((ntok,K), as for
+ * orc_route_given); NULL given is orc_layer_tokens. */
+int orc_layer_tokens_given(const void* x, const void* wr, const float* bias, const void* w1, const void* w2,
+                           int dt, int T, int H, int E, int K, int F, int act, const int32_t* tokens,
+                           int ntok, const int32_t* given, double* y, int32_t* topk_idx, double* topk_gate,
+                           double* gap, int nthreads);
 
 /* O9: dense masked sum, every expert on every token:
  * y[t] = sum_{e<E} m[t,e] * G[t,e] * E_e(x_t), with m the binary activation

@@ -14,7 +14,7 @@ import mixture_experts_layer_06_amd as moe
 import oracle
 import synth
 from synth import configs
-from tests.helpers import GAP, TOL, as_f64, normwise_err, to_dev, to_host
+from tests.helpers import TOL, as_f64, check_selection, layer_check, normwise_err, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -61,12 +61,8 @@ def test_layer_full_size_sampled_tokens(name, T, nsample):
     toks = _sample_tokens(T, nsample, seed=T)
     ref = oracle.layer_tokens(d["x"], d["wr"], d["w1"], d["w2"], K, toks, bias=d["bias"],
                               nthreads=NTH)
-    ok = ref["gap"] > GAP
-    assert ok.mean() > 0.8
-    assert np.array_equal(idx[toks][ok], ref["idx"][ok])
-    np.testing.assert_allclose(gate[toks][ok], ref["gate"][ok], atol=2e-3)
-    err = normwise_err(y[toks][ok], ref["y"][ok])
-    assert err <= TOL["bf16"], f"{name} T={T}: {err:.3e}"
+    err, n_alt = layer_check(y, idx, gate, d, ref, tokens=toks, tol=TOL["bf16"], nthreads=NTH)
+    print(f"{name} T={T}: {len(toks)} sampled tokens, normwise error {err:.2e}, {n_alt} near ties")
     if name == "skewed":
         # the router bias gives expert 0 the largest share and a long tail
         assert counts.argmax() == 0 and counts[0] > 8 * np.median(counts)
@@ -78,10 +74,17 @@ def test_route_full_size_all_tokens_decode_and_prefill():
         K = d["K"]
         idx, gate = moe.route(to_dev(d["x"]), to_dev(d["wr"]), K)
         torch.cuda.synchronize()
-        ridx, rgate, _, gap = oracle.route(d["x"], d["wr"], T, d["H"], d["E"], K)
-        ok = gap > GAP
-        assert np.array_equal(to_host(idx)[ok], ridx[ok])
-        assert np.abs(to_host(gate)[ok] - rgate[ok]).max() <= 2e-3
+        idx, gate = to_host(idx), to_host(gate)
+        ridx, rgate, logits, gap = oracle.route(d["x"], d["wr"], T, d["H"], d["E"], K)
+        diff = check_selection(idx, ridx, logits, K)
+        if diff.any():
+            _, g2, _, _ = oracle.route_given(d["x"][diff], d["wr"], int(diff.sum()), d["H"], d["E"], K,
+                                             idx[diff])
+            rgate = rgate.copy()
+            rgate[diff] = g2
+        assert np.abs(gate - rgate).max() <= 2e-3
+        print(f"{name} T={T}: every token checked, {int((gap <= 1e-3).sum())} near ties, "
+              f"{int(diff.sum())} selections differ from the oracle's")
 
 
 @pytest.mark.parametrize("T,E,K,H", [(4096, 8, 2, 4096), (16384, 64, 6, 2048), (8192, 32, 8, 7168)])
@@ -233,15 +236,16 @@ def test_layer_fp8_full_size_prefill_sampled_tokens():
     T, K = d["T"], d["K"]
     sc = lambda v: torch.tensor([float(v)], dtype=torch.float32, device="cuda")
     idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
     y = moe.layer_fp8(to_dev(d["x"]), to_dev(d["wr"]), to_dev(d["w1"]), sc(d["w1_scale"]), to_dev(d["w2"]),
-                      sc(d["w2_scale"]), K, topk_idx=idx)
+                      sc(d["w2_scale"]), K, topk_idx=idx, topk_gate=gate)
     torch.cuda.synchronize()
     tokens = np.random.default_rng(670).choice(T, 12, replace=False)
     ref = oracle.layer_fp8(d["x"], d["wr"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"], K, tokens=tokens,
                            nthreads=NTH)
-    ok = ref["gap"] > GAP
-    assert np.array_equal(to_host(idx)[tokens][ok], ref["idx"][ok])
-    assert normwise_err(to_host(y)[tokens][ok], ref["y"][ok]) <= 2e-2
+    err, _ = layer_check(to_host(y), to_host(idx), to_host(gate), d, ref, tokens=tokens, tol=TOL["fp8"], fp8=True,
+                         nthreads=NTH)
+    print(f"E4M3 layer, prefill shapes, 12 sampled tokens: normwise error {err:.2e} against the oracle")
 
 
 def test_combine_full_size_prefill():

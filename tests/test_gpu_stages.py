@@ -16,7 +16,7 @@ import mixture_experts_layer_06_amd as moe
 import oracle
 import synth
 from synth import configs
-from tests.helpers import GAP, TOL, as_f64, normwise_err, to_dev, to_host
+from tests.helpers import TOL, as_f64, check_selection, normwise_err, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_route_parity(case):
     name, T, H, E, K, dt, integer, use_bias = case
     d = configs.layer_inputs("tiny", T=T, H=H, E=E, K=K, F=8, dtype=dt, integer=integer,
                              bias=use_bias, wid=40 + len(name))
-    ridx, rgate, _, gap = oracle.route(d["x"], d["wr"], T, H, E, K, bias=d["bias"])
+    ridx, rgate, logits, gap = oracle.route(d["x"], d["wr"], T, H, E, K, bias=d["bias"])
     bias = to_dev(d["bias"]) if use_bias else None
     idx, gate = moe.route(to_dev(d["x"]), to_dev(d["wr"]), K, bias=bias)
     _sync()
@@ -65,11 +65,17 @@ def test_route_parity(case):
         assert np.array_equal(idx, ridx)
         np.testing.assert_allclose(gate, rgate, rtol=0, atol=2e-6)
         return
-    ok = gap > GAP
-    assert ok.mean() > 0.9
-    assert np.array_equal(idx[ok], ridx[ok])
+    # every token: the oracle's experts where its k-th and (k+1)-th scores are
+    # more than 1e-3 apart, a valid top-k within 1e-3 where they nearly tie;
+    # gates against the oracle's gates for the GPU's own experts
+    diff = check_selection(idx, ridx, logits, K)
+    if diff.any():
+        _, g2, _, _ = oracle.route_given(d["x"][diff], d["wr"], int(diff.sum()), H, E, K, idx[diff],
+                                         bias=d["bias"])
+        rgate = rgate.copy()
+        rgate[diff] = g2
     tol = 1e-5 if dt == "f32" else 2e-3  # bf16 scores: fp32 sums of exact products
-    assert np.abs(gate[ok] - rgate[ok]).max() <= tol
+    assert np.abs(gate - rgate).max() <= tol
     np.testing.assert_allclose(gate.sum(1), 1.0, atol=1e-6)
 
 
@@ -479,6 +485,66 @@ def test_quant_rows_ties_and_grid_points(dt, pad):
     assert np.all(rs == np.float32(1.0))
     assert np.array_equal(to_host(q), rq)
     assert np.array_equal(to_host(sc), rs)
+
+
+def _near_midpoint_rows(dt, seed):
+    """Rows whose elements put the exact quotient x / scale on or within a few
+    binary32 ulps of E4M3 midpoints, with general (24-bit) scales: binary32
+    rows take the nearest binary32 numbers to midpoint * scale and their
+    neighbours; bfloat16 rows take elements amax * m / 448 that are bfloat16
+    numbers (the scale amax / 448 is then rounded, so the quotient sits a
+    rounding away from m). Plus a row of 1e-37 values (subnormal scale) and
+    one whose max / 448 rounds to zero."""
+    rng = np.random.default_rng(seed)
+    pos = np.unique(oracle.decode(np.arange(0x7F, dtype=np.uint8)))
+    mids = (pos[1:] + pos[:-1]) / 2
+    H = 256
+    rows = []
+    for k in range(24):
+        amax = np.float32(rng.uniform(1, 2) * 2.0 ** rng.integers(-30, 30))
+        if dt == "bf16":
+            amax = synth.bf16_to_f32(synth.to_bf16(np.array([amax], np.float32)))[0]
+            cand = np.float32(amax * np.concatenate([mids, -mids]) / 448.0)
+            cand = cand[synth.bf16_to_f32(synth.to_bf16(cand)) == cand]
+        else:
+            s = np.float32(amax / np.float32(448.0))
+            near = np.float32(rng.choice(mids, 40) * float(s) * rng.choice([-1.0, 1.0], 40))
+            cand = np.concatenate([near, np.nextafter(near, np.float32(np.inf)),
+                                   np.nextafter(near, np.float32(-np.inf))])
+        cand = cand[np.abs(cand) < amax]
+        row = np.zeros(H, np.float32)
+        row[0] = -amax
+        n = min(H - 1, cand.size)
+        row[1:1 + n] = cand[:n]
+        row[1 + n:] = np.float32(rng.standard_normal(H - 1 - n) * amax / 5)
+        rows.append(row)
+    rows.append(np.float32(rng.standard_normal(H) * 1e-37))
+    rows.append(np.float32(np.r_[1e-45, -1e-45, np.zeros(H - 2)]))
+    x = np.stack(rows)
+    return synth.to_bf16(x) if dt == "bf16" else x
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_quant_rows_near_midpoints_and_tiny_rows(dt):
+    """Codes equal the oracle's (nearest E4M3 value of the exact quotient) also
+    where a quotient formed in binary32 would round to the other neighbour,
+    and on rows with a subnormal or vanishing scale (no NaN codes); scales bit
+    for bit."""
+    x = _near_midpoint_rows(dt, 830 if dt == "f32" else 831)
+    q, sc = moe.quant_rows(to_dev(x))
+    rq, rs = oracle.quant_rows(x)
+    xf = synth.bf16_to_f32(x) if dt == "bf16" else x
+    # the inputs do reach elements where the binary32 product x * (1/scale)
+    # lands on the other side of a midpoint
+    inv = np.float32(1.0) / np.maximum(rs, np.float32(1e-38))
+    naive = oracle.e4m3_nearest(xf * inv[:, None])
+    flips = int((naive[:-2] != rq[:-2]).sum())
+    print(f"{dt}: {flips} elements whose binary32 product quotient rounds differently")
+    assert flips > 0
+    assert np.array_equal(to_host(sc).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(to_host(q), rq)
+    assert rs[-1] == 0 and not rq[-1].any() and rs[-2] > 0
+    assert not np.isnan(oracle.decode(to_host(q))).any()
 
 
 def test_quant_rows_gather_is_the_permute():

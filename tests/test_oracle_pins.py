@@ -687,3 +687,161 @@ def test_gmm_row_scales_on_sampled_rows():
     full = oracle.gmm(a, w, off, a_scale=rs)
     rows = np.array([17, 2, 9, 0, 11], np.int32)
     assert np.array_equal(oracle.gmm(a, w, off, a_scale=rs, rows=rows), full[rows])
+
+
+# ---------------------------------------------------------------- per-token quantisation, exact quotient
+# The pins below hold the quantiser to its plain definition, scale =
+# binary32(amax / 448) and codes = nearest E4M3 value of the exact quotient
+# x / scale, by means other than the oracle's own comparisons: exact rational
+# arithmetic (fractions), and torch's E4M3 conversion where the quotient is a
+# binary32 number.
+
+from fractions import Fraction
+
+
+def _e4m3_table():
+    codes = np.arange(0x7F, dtype=np.uint8)  # 0x00 .. 0x7e: the non-negative finite values
+    return codes, [Fraction(float(v)) for v in oracle.decode(codes)]
+
+
+def _nearest_code_exact(q: Fraction, table) -> int:
+    """Code (sign bit clear) of the non-negative finite E4M3 value nearest to
+    |q|, by exact distances to all of them; ties to the even code."""
+    codes, vals = table
+    a = abs(q)
+    best, bestd = None, None
+    for c, v in zip(codes, vals):
+        d = abs(a - v)
+        if bestd is None or d < bestd or (d == bestd and int(c) % 2 == 0):
+            best, bestd = int(c), d
+    return best
+
+
+def _f32_nearest_exact(q: Fraction) -> np.float32:
+    """binary32 number nearest to the rational q (q >= 0), ties to even, from
+    exact distances to the binary32 neighbours of a first guess."""
+    g = np.float32(float(q))
+    cands = [np.nextafter(g, np.float32(-np.inf)), g, np.nextafter(g, np.float32(np.inf))]
+    cands = [c for c in cands if c >= 0]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - q), int(np.float32(c).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_div448_is_correctly_rounded():
+    rng = np.random.default_rng(50)
+    vals = list(np.abs(rng.standard_normal(300)) * np.exp2(rng.integers(-140, 120, 300)))
+    vals += [float(np.float32(v)) for v in vals[:100]]                 # binary32 amax
+    vals += [448.0 * float(np.float32(v)) for v in vals[:50]]          # exact quotients
+    # amax exactly half-way between 448 s and 448 next(s): ties to even
+    for s in np.float32([1.0, 1.5, 3.0e-5, 2.0 ** -130]):
+        up = np.nextafter(s, np.float32(np.inf))
+        vals.append(float((Fraction(float(s)) + Fraction(float(up))) / 2 * 448))
+    # binary64 amax one or two ulps from such a tie (the fp64 hidden rows of
+    # the E4M3 layer are binary64)
+    for s in np.float32(rng.uniform(1, 2, 200) * np.exp2(rng.integers(-60, 60, 200))):
+        up = np.nextafter(s, np.float32(np.inf))
+        tie = float((Fraction(float(s)) + Fraction(float(up))) / 2 * 448)
+        for step in (-2, -1, 1, 2):
+            v = tie
+            for _ in range(abs(step)):
+                v = np.nextafter(v, np.inf if step > 0 else -np.inf)
+            vals.append(float(v))
+    for v in vals:
+        assert oracle.div448_f32(v) == _f32_nearest_exact(Fraction(v) / 448), v
+
+
+def test_quant_rows_codes_are_nearest_to_the_exact_quotient():
+    """Random rows, rows with a subnormal or vanishing scale, and elements
+    placed on and next to every E4M3 midpoint times the row's scale (where a
+    quotient formed in binary32 arithmetic can round to the wrong side): each
+    code is the E4M3 value nearest to x / scale in exact rational arithmetic."""
+    rng = np.random.default_rng(51)
+    table = _e4m3_table()
+    pos = np.unique(oracle.decode(np.arange(0x7F, dtype=np.uint8)))
+    mids = (pos[1:] + pos[:-1]) / 2
+    rows = []
+    for k in range(6):
+        r = (rng.standard_normal(64) * np.exp2(rng.integers(-20, 20))).astype(np.float32)
+        s = np.float32(oracle.div448_f32(float(np.abs(r).max())))
+        # the binary32 numbers nearest to midpoint * scale, and their neighbours
+        m = rng.choice(mids, 20)
+        sign = rng.choice([-1.0, 1.0], 20)
+        near = np.float32(m * float(s) * sign)
+        extra = np.concatenate([near, np.nextafter(near, np.float32(np.inf)),
+                                np.nextafter(near, np.float32(-np.inf))])
+        rows.append(np.concatenate([r, extra[np.abs(extra) < np.abs(r).max()]]))
+    tiny = (rng.standard_normal(40) * 1e-37).astype(np.float32)        # subnormal scale
+    rows.append(tiny)
+    rows.append(np.float32([1e-45, -1e-45, 0.0] + [0.0] * 5))          # amax / 448 rounds to 0
+    rows.append(np.float32([448.0 * 2.0 ** -140, 3.0 * 2.0 ** -149, -2.0 ** -145] + [0.0] * 5))
+    Hmax = max(r.size for r in rows)
+    x = np.zeros((len(rows), Hmax), np.float32)
+    for i, r in enumerate(rows):
+        x[i, :r.size] = r
+    q, s = oracle.quant_rows(x)
+    for i in range(x.shape[0]):
+        amax = np.abs(x[i]).max()
+        assert s[i] == _f32_nearest_exact(Fraction(float(amax)) / 448)
+        if s[i] == 0:
+            assert not q[i].any()
+            continue
+        for h in range(Hmax):
+            want = _nearest_code_exact(Fraction(float(x[i, h])) / Fraction(float(s[i])), table)
+            if x[i, h] < 0 or (x[i, h] == 0 and np.signbit(x[i, h])):
+                want |= 0x80
+            assert q[i, h] == want, (i, h, x[i, h], s[i])
+    assert s[-2] == 0 and s[-1] > 0 and not np.isnan(oracle.decode(q)).any()
+
+
+def test_quant_rows_codes_equal_torch_where_the_quotient_is_binary32():
+    """Rows whose scale is a power of two (amax = 448 * 2^k): the quotient
+    x / scale is a binary32 number, so torch's binary32 -> float8_e4m3fn
+    conversion (round to nearest even) gives the exact answer; elsewhere
+    torch's conversion of the binary32-rounded quotient agrees except where a
+    midpoint lies within one binary32 rounding, where the oracle's code is one
+    of the two neighbours."""
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((40, 256)).astype(np.float32)
+    k = rng.integers(-30, 30, 40)
+    x /= np.abs(x).max(axis=1, keepdims=True)
+    x = (x * np.float32(448.0) * np.exp2(k)[:, None]).astype(np.float32)
+    pw = np.abs(x).max(axis=1) == np.float32(448.0) * np.exp2(k).astype(np.float32)
+    q, s = oracle.quant_rows(x)
+    assert pw.sum() >= 30
+    exact = (x[pw] / s[pw, None]).astype(np.float32)
+    assert np.array_equal(exact.astype(np.float64) * s[pw, None].astype(np.float64), x[pw].astype(np.float64))
+    ref = torch.from_numpy(exact).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q[pw], ref)
+    # general scales: binary32 quotients, compared away from the midpoints
+    y = (rng.standard_normal((30, 512)) * np.exp2(rng.integers(-10, 10, (30, 1)))).astype(np.float32)
+    qy, sy = oracle.quant_rows(y)
+    quo = (y.astype(np.float64) / sy[:, None].astype(np.float64)).astype(np.float32)
+    ref = torch.from_numpy(quo).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    differ = qy != ref
+    if differ.any():
+        lo = np.minimum(oracle.decode(qy[differ]), oracle.decode(ref[differ]))
+        hi = np.maximum(oracle.decode(qy[differ]), oracle.decode(ref[differ]))
+        mid = (lo + hi) / 2
+        assert np.all(np.abs(np.abs(quo[differ]) - np.abs(mid)) <= np.abs(mid) * 2.0 ** -23)
+    assert differ.mean() < 1e-3
+
+
+def test_quant_rows_binary64_input():
+    """Binary64 rows (the fp64 hidden activation of the E4M3 layer): the scale
+    is amax / 448 rounded once to binary32 and the codes follow the exact
+    quotient, also where a binary32 copy of the row would round differently."""
+    table = _e4m3_table()
+    rng = np.random.default_rng(53)
+    x = rng.standard_normal((4, 48))
+    x[1, 5] = 448.0 * (1 + 2.0 ** -30)          # amax not a binary32 value
+    x[2, :3] = [1.0625 * (1 + 2.0 ** -40), -1.0625 * (1 + 2.0 ** -40), 448.0]   # just past a tie
+    q, s = oracle.quant_rows(x)
+    for i in range(4):
+        amax = Fraction(float(np.abs(x[i]).max()))
+        assert s[i] == _f32_nearest_exact(amax / 448)
+        for h in range(48):
+            want = _nearest_code_exact(Fraction(float(x[i, h])) / Fraction(float(s[i])), table)
+            if x[i, h] < 0:
+                want |= 0x80
+            assert q[i, h] == want
+    assert s[2] == 1.0 and q[2, 0] == 0x39 and q[2, 1] == 0xB9  # binary32 would give the tie's even code 0x38
