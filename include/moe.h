@@ -103,7 +103,10 @@ int moe_version(void);
  *   ws, ws_bytes device scratch of at least moe_route_workspace_size() bytes
  *                (may be NULL when that size is 0; with few tokens the router
  *                splits H over several blocks and keeps partial scores there)
- * Scores are accumulated in fp32. T = 0 is a no-op.
+ * Scores are accumulated in fp32. T = 0 is a no-op. Non-finite inputs are
+ * outside the contract: a NaN score counts as -inf for selection, so the
+ * indices always hold K distinct experts in [0, E); that token's gates are
+ * then unspecified.
  */
 moe_status moe_route_workspace_size(int T, int H, int E, int K, moe_dtype dt, size_t* bytes);
 moe_status moe_route(const void* x, const void* w_router, moe_dtype dt, const float* bias, int T,

@@ -48,7 +48,10 @@ __device__ __forceinline__ void wave_argmax(float& v, int& e) {
 }
 
 // Top-k + sparse softmax for one token whose E scores sit in LDS row `lg`.
-// Called by a whole wave; lane k < K writes slot k.
+// Called by a whole wave; lane k < K writes slot k. A NaN score (from
+// non-finite inputs) counts as -inf, so every round picks an unselected
+// expert and the indices stay in [0, E); the gates of such a token are
+// then unspecified.
 __device__ __forceinline__ void topk_softmax_token(const float* lg, int E, int K, int32_t* idx_out,
                                                    float* gate_out) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -57,7 +60,8 @@ __device__ __forceinline__ void topk_softmax_token(const float* lg, int E, int K
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int e = lane + kWave * i;
-    cand[i] = e < E ? lg[e] : -INFINITY;
+    const float v = e < E ? lg[e] : -INFINITY;
+    cand[i] = v == v ? v : -INFINITY;
     taken[i] = e >= E;
   }
   float sel_v[8];

@@ -79,6 +79,26 @@ def test_route_parity(case):
     np.testing.assert_allclose(gate.sum(1), 1.0, atol=1e-6)
 
 
+@pytest.mark.parametrize("T,H,E,K", [(48, 512, 8, 2), (64, 4096, 128, 8), (40, 256, 256, 8)])
+def test_route_nan_scores_keep_valid_indices(T, H, E, K):
+    """Tokens whose scores are NaN (a NaN in the token row): every slot still
+    names a distinct expert in [0, E) (NaN counts as -inf); the other tokens
+    are unaffected. Covers the one-block and the split-H (finish kernel) paths."""
+    d = configs.layer_inputs("tiny", T=T, H=H, E=E, K=K, F=8, dtype="bf16", wid=47)
+    x = d["x"].copy()
+    nan_rows = [0, 5, T - 1]
+    for t in nan_rows:
+        x[t, 3] = 0x7FC0  # bf16 NaN
+    idx, gate = moe.route(to_dev(x), to_dev(d["wr"]), K)
+    _sync()
+    idx, gate = to_host(idx), to_host(gate)
+    assert ((idx >= 0) & (idx < E)).all()
+    assert (np.diff(np.sort(idx, axis=1), axis=1) != 0).all()
+    clean = np.setdiff1d(np.arange(T), nan_rows)
+    ridx, rgate, logits, _ = oracle.route(d["x"][clean], d["wr"], clean.size, H, E, K)
+    check_selection(idx[clean], ridx, logits, K)
+
+
 # ---------------------------------------------------------------- permute
 
 def _check_permute_bitexact(idx_np, E, x_np):
