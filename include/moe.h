@@ -57,7 +57,9 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 4,         /* a valid mode the library does not implement */
   MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes below the *_workspace_size answer */
   MOE_ERR_MISALIGNED = 6,          /* a device pointer is not 16-byte aligned */
-  MOE_ERR_DEVICE = 7               /* the HIP runtime reported an error */
+  MOE_ERR_DEVICE = 7,              /* the HIP runtime reported an error */
+  MOE_ERR_SCRATCH_LIMIT = 8        /* moe_layer_noalloc: the call needs more than
+                                      MOE_NOALLOC_SCRATCH_BYTES of scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -397,6 +399,30 @@ moe_status moe_layer(const void* x, const void* w_router, const float* bias, con
                      const void* w2, moe_dtype dt, int T, int H, int E, int K, int F, moe_act act,
                      void* y, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_noalloc — moe_layer for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results, bit for bit, without
+ * the workspace. Its scratch memory is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one copy per GPU,
+ * held until the process ends; its address on a device is looked up on the
+ * first call made with that device current. The call allocates nothing.
+ *   A call whose moe_layer_workspace_size() exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *   returns MOE_ERR_SCRATCH_LIMIT and enqueues nothing (32 MiB holds, e.g.,
+ *   every decode-shaped call up to T*K = 2048 rows at H = 4096, F = 1536).
+ *   The stream must belong to the current device.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by the
+ * caller; calls on one stream are ordered by it. Errors: as moe_layer, plus
+ * MOE_ERR_SCRATCH_LIMIT, and MOE_ERR_DEVICE if the array's address cannot be
+ * obtained.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_layer_noalloc(const void* x, const void* w_router, const float* bias, const void* w1,
+                             const void* w2, moe_dtype dt, int T, int H, int E, int K, int F, moe_act act,
+                             void* y, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                             void* stream);
 
 /*
  * moe_layer_fp8 — the layer with E4M3 experts: route on the bf16 tokens,

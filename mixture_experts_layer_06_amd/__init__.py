@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 # moe.h enums
 OK, ERR_NULL_POINTER, ERR_BAD_SHAPE, ERR_BAD_DTYPE, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
-ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_DEVICE = 5, 6, 7
+ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_DEVICE, ERR_SCRATCH_LIMIT = 5, 6, 7, 8
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 F32, BF16, FP8_E4M3 = 0, 1, 2
 QUANT_NONE, QUANT_PER_TENSOR, QUANT_PER_TOKEN = 0, 1, 3
 ACT_NONE, ACT_RELU = 0, 1
@@ -29,7 +30,7 @@ EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
            "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_routed_shared", "moe_gmm_mx_routed_shared", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
            "moe_quant_rows", "moe_layer_workspace_size", "moe_layer", "moe_layer_fp8_workspace_size",
-           "moe_layer_fp8")
+           "moe_layer_fp8", "moe_layer_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                 vp, vp, sz, vp]
+        L.moe_layer_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                        vp, vp]
         L.moe_layer_fp8_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_layer_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                     vp, sz, vp]
@@ -379,6 +382,22 @@ def layer(x, w_router, w1, w2, K, bias=None, act=ACT_RELU, y=None, ws=None, topk
                          act, _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
                          ws.numel(), _stream(stream))
     _check(st, "moe_layer")
+    return y
+
+
+def layer_noalloc(x, w_router, w1, w2, K, bias=None, act=ACT_RELU, y=None, topk_idx=None, topk_gate=None,
+                  counts=None, stream=None):
+    """moe_layer_noalloc: moe_layer with its scratch in the library's static
+    device buffer (no workspace argument, nothing allocated by the call
+    itself beyond y when y is None). Returns y."""
+    T, H = x.shape
+    E, _, F = w1.shape
+    dt = dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib().moe_layer_noalloc(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1), _ptr(w2), dt, T, H, E, K, F,
+                                 act, _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _stream(stream))
+    _check(st, "moe_layer_noalloc")
     return y
 
 

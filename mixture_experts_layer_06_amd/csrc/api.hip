@@ -5,6 +5,8 @@
 // "aclnnQuantGroupedMatMulAlltoAllv": the first stage checks parameters and
 // sizes the workspace, the second runs on a stream). The shape limits are
 // that page's constraints, adapted to one GPU that holds every expert.
+#include <mutex>
+
 #include "common.h"
 
 using namespace moe;
@@ -105,6 +107,94 @@ LayerFp8Ws layer_fp8_ws_layout(int T, int H, int E, int K, int F) {
   return L;
 }
 
+// Host-side checks shared by moe_layer and moe_layer_noalloc (everything but
+// the workspace).
+moe_status layer_check(const void* x, const void* w_router, const float* bias, const void* w1, const void* w2,
+                       moe_dtype dt, int T, int H, int E, int K, int F, moe_act act, const void* y,
+                       const int32_t* topk_idx_out, const float* topk_gate_out, const int32_t* counts_out) {
+  if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
+  MOE_TRY(check_route_shape(T, H, E, K));
+  if (!dim_ok(F)) return MOE_ERR_BAD_SHAPE;
+  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(y);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(w_router);
+  REQUIRE_ALIGNED(bias);
+  REQUIRE_ALIGNED(w1);
+  REQUIRE_ALIGNED(w2);
+  REQUIRE_ALIGNED(y);
+  REQUIRE_ALIGNED(topk_idx_out);
+  REQUIRE_ALIGNED(topk_gate_out);
+  REQUIRE_ALIGNED(counts_out);
+  return MOE_OK;
+}
+
+// The layer's launches on a checked workspace `base` laid out as L.
+moe_status layer_run(const void* x, const void* w_router, const float* bias, const void* w1, const void* w2,
+                     moe_dtype dt, int T, int H, int E, int K, int F, moe_act act, void* y, int32_t* topk_idx_out,
+                     float* topk_gate_out, int32_t* counts_out, unsigned char* base, const LayerWs& L,
+                     hipStream_t s) {
+  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(base + L.idx);
+  float* gate = topk_gate_out ? topk_gate_out : (float*)(base + L.gate);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* psrc = (int32_t*)(base + L.psrc);
+  int32_t* pdst = (int32_t*)(base + L.pdst);
+  void* xp = base + L.xp;
+  void* hm = base + L.hm;
+  const int A = T * K;
+  MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s));
+  void* gws = base + L.gmm_ws;  // sized for whichever GEMM needs more (possibly none)
+  void* gws1 = gmm_ws_bytes(dt, E, A, H, F) ? gws : nullptr;
+  if ((int64_t)T * H * dtype_size(dt) < (1ll << 31)) {
+    // dispatch inside GEMM 1: its row r is token perm_src[r] / K
+    MOE_TRY(launch_permute(idx, nullptr, dt, T, H, E, K, counts, offsets, psrc, pdst, nullptr,
+                           base + L.perm_ws, s));
+    MOE_TRY(launch_gmm(x, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s,
+                       RowMap{psrc, K, T}));
+  } else {
+    MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
+    MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s));
+  }
+  void* gws2 = gmm_ws_bytes(dt, E, A, F, H) ? gws : nullptr;
+  // GEMM 2 into the grouped rows, then the weighted combine (gates applied
+  // once, in fp32, in the combine; storing gated rows from GEMM 2's epilogue
+  // and summing K rows moves the same bytes and measured 1-5% slower)
+  MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, gws2, s));
+  MOE_TRY(launch_combine(xp, dt, pdst, gate, T, K, H, y, s));
+  return MOE_OK;
+}
+
+
+// Scratch memory of moe_layer_noalloc: moe_layer's workspace in a static
+// device array, one copy per GPU, held until the process ends. Host code
+// never uses the array's name as an address: the address on each device is
+// looked up once (with that device current) and kept.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kMaxDevices] = {};
+
+moe_status scratch_on_current_device(unsigned char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_DEVICE;
+    g_scratch[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,6 +208,8 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "mode not implemented (quantisation mode or activation)";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
     case MOE_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch memory than the allocation-free entry point's static buffer holds";
     case MOE_ERR_DEVICE: return "HIP runtime error while enqueuing work";
   }
   return "unknown status";
@@ -202,14 +294,6 @@ moe_status moe_gmm_workspace_size(moe_dtype a_dt, int e, int A, int Hin, int N, 
   *bytes = gmm_ws_bytes(a_dt, e, A, Hin, N);
   return MOE_OK;
 }
-
-// moe_layer's GEMM 2: 1 = stores gated rows in (token, slot) order and sums
-// K rows per token; 0 = stores grouped rows, then the gathering weighted
-// combine. Both move the same bytes; 0 measured 1-5% faster on GEMM 2 (the
-// gated stores wait for an index and then a gate load per row).
-#ifndef MOE_LAYER_GATED_STORES
-#define MOE_LAYER_GATED_STORES 0
-#endif
 
 namespace {
 // Shared argument checks of moe_gmm / moe_gmm_gather / moe_gmm_scatter; on
@@ -458,67 +542,30 @@ moe_status moe_layer(const void* x, const void* w_router, const float* bias, con
                      const void* w2, moe_dtype dt, int T, int H, int E, int K, int F, moe_act act,
                      void* y, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                      void* ws, size_t ws_bytes, void* stream) {
-  if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;
-  MOE_TRY(check_route_shape(T, H, E, K));
-  if (!dim_ok(F)) return MOE_ERR_BAD_SHAPE;
-  if (act != MOE_ACT_NONE && act != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(layer_check(x, w_router, bias, w1, w2, dt, T, H, E, K, F, act, y, topk_idx_out, topk_gate_out,
+                      counts_out));
   if (T == 0) return MOE_OK;
-  REQUIRE_PTR(x);
-  REQUIRE_PTR(w_router);
-  REQUIRE_PTR(w1);
-  REQUIRE_PTR(w2);
-  REQUIRE_PTR(y);
   REQUIRE_PTR(ws);
   const LayerWs L = layer_ws_layout(T, H, E, K, F, dt);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  REQUIRE_ALIGNED(x);
-  REQUIRE_ALIGNED(w_router);
-  REQUIRE_ALIGNED(bias);
-  REQUIRE_ALIGNED(w1);
-  REQUIRE_ALIGNED(w2);
-  REQUIRE_ALIGNED(y);
-  REQUIRE_ALIGNED(topk_idx_out);
-  REQUIRE_ALIGNED(topk_gate_out);
-  REQUIRE_ALIGNED(counts_out);
   REQUIRE_ALIGNED(ws);
+  return layer_run(x, w_router, bias, w1, w2, dt, T, H, E, K, F, act, y, topk_idx_out, topk_gate_out, counts_out,
+                   (unsigned char*)ws, L, (hipStream_t)stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  unsigned char* base = (unsigned char*)ws;
-  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(base + L.idx);
-  float* gate = topk_gate_out ? topk_gate_out : (float*)(base + L.gate);
-  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
-  int32_t* offsets = (int32_t*)(base + L.offsets);
-  int32_t* psrc = (int32_t*)(base + L.psrc);
-  int32_t* pdst = (int32_t*)(base + L.pdst);
-  void* xp = base + L.xp;
-  void* hm = base + L.hm;
-  const int A = T * K;
-  MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s));
-  void* gws = base + L.gmm_ws;  // sized for whichever GEMM needs more (possibly none)
-  void* gws1 = gmm_ws_bytes(dt, E, A, H, F) ? gws : nullptr;
-  if ((int64_t)T * H * dtype_size(dt) < (1ll << 31)) {
-    // dispatch inside GEMM 1: its row r is token perm_src[r] / K
-    MOE_TRY(launch_permute(idx, nullptr, dt, T, H, E, K, counts, offsets, psrc, pdst, nullptr,
-                           base + L.perm_ws, s));
-    MOE_TRY(launch_gmm(x, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s,
-                       RowMap{psrc, K, T}));
-  } else {
-    MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
-    MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s));
-  }
-  void* gws2 = gmm_ws_bytes(dt, E, A, F, H) ? gws : nullptr;
-  if (MOE_LAYER_GATED_STORES) {
-    // GEMM 2 stores g[t,k] * E_k(x_t) as row t*K+k; then the K-row sum
-    RowMap sx;
-    sx.dst = psrc;
-    sx.gate = gate;
-    MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, gws2, s, sx));
-    MOE_TRY(launch_combine(xp, dt, nullptr, nullptr, T, K, H, y, s, true));
-  } else {
-    MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, gws2, s));
-    MOE_TRY(launch_combine(xp, dt, pdst, gate, T, K, H, y, s));
-  }
-  return MOE_OK;
+moe_status moe_layer_noalloc(const void* x, const void* w_router, const float* bias, const void* w1,
+                             const void* w2, moe_dtype dt, int T, int H, int E, int K, int F, moe_act act,
+                             void* y, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                             void* stream) {
+  MOE_TRY(layer_check(x, w_router, bias, w1, w2, dt, T, H, E, K, F, act, y, topk_idx_out, topk_gate_out,
+                      counts_out));
+  if (T == 0) return MOE_OK;
+  const LayerWs L = layer_ws_layout(T, H, E, K, F, dt);
+  if (L.total > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  unsigned char* base = nullptr;
+  MOE_TRY(scratch_on_current_device(&base));
+  return layer_run(x, w_router, bias, w1, w2, dt, T, H, E, K, F, act, y, topk_idx_out, topk_gate_out, counts_out,
+                   base, L, (hipStream_t)stream);
 }
 
 moe_status moe_layer_fp8_workspace_size(int T, int H, int E, int K, int F, size_t* bytes) {

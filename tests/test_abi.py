@@ -27,7 +27,7 @@ def test_header_declares_expected_entry_points():
               "moe_combine", "moe_sum_slots", "moe_quant_rows", "moe_layer",
               "moe_route_workspace_size", "moe_permute_workspace_size", "moe_gmm_workspace_size",
               "moe_layer_workspace_size", "moe_layer_fp8", "moe_layer_fp8_workspace_size",
-              "moe_status_string", "moe_version"):
+              "moe_layer_noalloc", "moe_status_string", "moe_version"):
         assert n in names
 
 
@@ -543,3 +543,33 @@ def test_layer_fp8_empty_batch_and_workspace_size():
     n = moe.layer_fp8_workspace_size(T, H, E, K, F)
     assert n >= T * H + A * F * 3 + A * H * 2 + 4 * A * 4
 
+
+
+def layer_noalloc(x=P, wr=P, bias=None, w1=P, w2=P, dt=moe.BF16, T=32, H=64, E=8, K=2, F=96,
+                  act=moe.ACT_RELU, y=P):
+    return L.moe_layer_noalloc(x, wr, bias, w1, w2, dt, T, H, E, K, F, act, y, None, None, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=moe.FP8_E4M3), moe.ERR_BAD_DTYPE),
+    (dict(K=9), moe.ERR_BAD_SHAPE),
+    (dict(F=0), moe.ERR_BAD_SHAPE),
+    (dict(act=2), moe.ERR_UNSUPPORTED),
+    (dict(x=None), moe.ERR_NULL_POINTER),
+    (dict(y=None), moe.ERR_NULL_POINTER),
+    (dict(w1=MIS), moe.ERR_MISALIGNED),
+    # prefill-sized calls need about 360 MiB of scratch: refused before any device call
+    (dict(T=4096, H=4096, E=8, K=2, F=14336), moe.ERR_SCRATCH_LIMIT),
+    (dict(T=1024, H=4096, E=128, K=8, F=1536), moe.ERR_SCRATCH_LIMIT),
+    (dict(T=0, x=None, wr=None, w1=None, w2=None, y=None), moe.OK),
+])
+def test_layer_noalloc_validation(kw, status):
+    assert layer_noalloc(**kw) == status
+
+
+def test_layer_noalloc_limit_matches_the_workspace_query():
+    """The static buffer holds every decode-shaped call up to T*K = 2048 rows
+    at H = 4096, F = 1536, and the status string names the limit."""
+    assert moe.layer_workspace_size(256, 4096, 128, 8, 1536, moe.BF16) <= moe.NOALLOC_SCRATCH_BYTES
+    assert moe.layer_workspace_size(512, 4096, 128, 8, 1536, moe.BF16) > moe.NOALLOC_SCRATCH_BYTES
+    assert b"static buffer" in L.moe_status_string(moe.ERR_SCRATCH_LIMIT)
