@@ -116,6 +116,29 @@ def warm_up(fn, count):
                 return n
 
 
+FLUSH_BYTES = 1 << 30  # written before every timed step: evicts the 256 MB MALL and the L2s
+
+
+class Flush:
+    """A 1 GiB device buffer written (a fill kernel) before each timed step,
+    outside the step's events, so every step starts from cold caches."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xFF)
+
+
+def median_min(values):
+    import numpy as np
+    v = np.asarray(values, np.float64)
+    return float(np.median(v)), float(v.min())
+
+
 def _time_ms(fn, iters):
     import torch
     for _ in range(3):
@@ -177,12 +200,44 @@ def achievable(dev, even_experts=None):
     return res
 
 
-def cpu_threads() -> int:
+def cpu_share():
+    """(CPUs this process may run on, CPUs its cgroup quota grants or None)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
+    quota = None
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = max(1, int(math.ceil(int(q) / int(period))))
+    except (OSError, ValueError):
+        pass
+    return n, quota
+
+
+def cpu_threads() -> int:
+    """Oracle threads: every CPU granted to this process, at most 16 (the
+    host CPU share that goes with one GPU on the measurement boxes)."""
+    n, quota = cpu_share()
+    if quota is not None:
+        n = min(n, quota)
     return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_info(nth):
+    n, quota = cpu_share()
+    return {"cores": nth, "cpu_model": cpu_model(), "cpus_visible": n, "cgroup_cpu_quota": quota}
 
 
 def host_to_dev(a, dev):
@@ -272,28 +327,42 @@ def bench_layer(args, dev):
         layer_step()
         step()
 
+    flush = Flush(dev)
     warmup = warm_up(warm_step, args.warmup)
+    sclk_start = reported_sclk()
+    # Timed: every step after a 1 GiB write (outside its events), between two
+    # events on the stream; median and min over the steps.
+    lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        flush()
+        lev[s][0].record()
+        layer_step()
+        lev[s][1].record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_step, ms_min = median_min([e[0].elapsed_time(e[1]) for e in lev])
+    # The same steps back to back, no flush (informational).
     t0 = time.perf_counter()
     for _ in range(args.steps):
         layer_step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_b2b = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # The same path stage by stage through the separate entry points, with HIP
-    # events on the stream between them: per-kernel times (the grouped GEMM's
-    # launch time feeds the roofline).
+    # events on the stream between them, each step after a flush: per-kernel
+    # times (the grouped GEMM's launch time feeds the roofline).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    ts0 = time.perf_counter()
     for s in range(args.steps):
+        flush()
         step(evs[s])
     torch.cuda.synchronize()
-    ts1 = time.perf_counter()
-    ms_stages = (ts1 - ts0) * 1e3 / args.steps
     names = ["route", "permute", "gmm1", "gmm2", "combine"]
-    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+    per = {n: median_min([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)])[0]
            for i, n in enumerate(names)}
+    ms_stages = sum(per.values())
 
     counts = bufs["counts"].cpu().numpy().tolist()
     fl1, by1 = flops_bytes_gmm(counts, H, F, es)
@@ -328,6 +397,7 @@ def bench_layer(args, dev):
         "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens)",
+        "timing": timing_record(ms_step, ms_min, ms_b2b, wall_s, args.steps, sclk_start),
         "config": {"workload": workload, "T": T, "H": H, "E": E, "K": K, "F": F,
                    "tokens_per_step": T, "parallelism": "single GPU"},
         "roofline": dict(roof, kernel="moe_gmm (" + ("gmm_stream_kernel" if hbm_bound else "gmm_pp_kernel") + ")",
@@ -383,7 +453,7 @@ def bench_fp8(args, dev, mode="pt"):
         sw = torch.tensor([float(d["gmm_w_scale"])], dtype=torch.float32, device=dev)
     mx = host_to_dev(d["mm_x"], dev)
     mw = host_to_dev(d["mm_w"], dev).view(1, H2, N2)
-    del d
+    host = {"d": d, "mode": "mx4" if fp4 else "mx" if use_mx else "dyn" if dyn else "pt"}
     moff = torch.tensor([0, T], dtype=torch.int32, device=dev)
     gy = torch.empty((A, N1), dtype=torch.bfloat16, device=dev)
     un = torch.empty((A, N1), dtype=torch.bfloat16, device=dev)
@@ -411,6 +481,7 @@ def bench_fp8(args, dev, mode="pt"):
             moe.combine(gy, perm["perm_dst"], None, T, K, out=un)
         if ev is not None:
             ev[2].record()
+            ev[6].record()
 
     def step(ev=None):
         main = torch.cuda.current_stream()
@@ -452,23 +523,36 @@ def bench_fp8(args, dev, mode="pt"):
         join = torch.cuda.Event()
         join.record(side)
         main.wait_event(join)
+        if ev is not None:
+            ev[6].record(main)  # both streams joined: the step's end
 
     if one:
         step = step_one
+    flush = Flush(dev)
     warmup = warm_up(step, args.warmup)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    sclk_start = reported_sclk()
+    # Timed: every step after a 1 GiB write (outside its events); the step
+    # runs from its first launch on either stream to the join of both.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        flush()
         step(evs[s])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    wall_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_b2b = (time.perf_counter() - t0) * 1e3 / args.steps
 
     def span(i, j):
-        return float(np.mean([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)]))
+        return median_min([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)])
 
-    q_ms, gmm_ms, un_ms = span(0, 5), span(5, 1), span(1, 2)
-    sh_ms = None if one else span(3, 4)
+    ms_step, ms_min = span(0, 6)
+    q_ms, gmm_ms, un_ms = span(0, 5)[0], span(5, 1)[0], span(1, 2)[0]
+    sh_ms = None if one else span(3, 4)[0]
     counts = perm["counts"].cpu().numpy().tolist()
     fl, by = flops_bytes_gmm(counts, H1, N1, 1)
     if fp4:  # half a byte per activation and weight element
@@ -516,6 +600,7 @@ def bench_fp8(args, dev, mode="pt"):
         "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp4_e2m1" if fp4 else "fp8_e4m3", "data": data,
+        "timing": timing_record(ms_step, ms_min, ms_b2b, wall_s, args.steps, sclk_start),
         "config": {"workload": f"{wl}: T={T} e={e} K={K} A={A} H1={H1} N1={N1} + shared "
                                f"({T},{H2})x({H2},{N2}) bf16", "tokens_per_step": T},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
@@ -524,7 +609,7 @@ def bench_fp8(args, dev, mode="pt"):
                      "flops_per_launch": fl, "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
         "kernels": kernels,
     }
-    return res, None
+    return res, host
 
 
 def bench_layer_fp8(args, dev):
@@ -588,17 +673,31 @@ def bench_layer_fp8(args, dev):
         moe.combine(yp, bufs["perm_dst"], gate, T, K, out=y2)
         ev[7].record()
 
+    flush = Flush(dev)
     warmup = warm_up(layer_step, args.warmup)
+    sclk_start = reported_sclk()
+    lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        flush()
+        lev[s][0].record()
+        layer_step()
+        lev[s][1].record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_step, ms_min = median_min([e[0].elapsed_time(e[1]) for e in lev])
     t0 = time.perf_counter()
     for _ in range(args.steps):
         layer_step()
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_b2b = (time.perf_counter() - t0) * 1e3 / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
     for s in range(args.steps):
+        flush()
         step(evs[s])
     torch.cuda.synchronize()
-    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+    per = {n: median_min([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)])[0]
            for i, n in enumerate(names)}
     counts = bufs["counts"].cpu().numpy().tolist()
     fl1, by1 = flops_bytes_gmm(counts, H, F, 1)
@@ -616,6 +715,7 @@ def bench_layer_fp8(args, dev):
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "timing": timing_record(ms_step, ms_min, ms_b2b, wall_s, args.steps, sclk_start),
         "data": "synthetic (seeded; bf16 N(0,1) tokens and router; N(0,1/fan_in) expert weights quantised "
                 "per tensor to E4M3; activations quantised per token on the device)",
         "config": {"workload": f"prefill_fp8: T={T} H={H} E={E} K={K} F={F} ReLU, E4M3 experts, per-token "
@@ -629,29 +729,96 @@ def bench_layer_fp8(args, dev):
         "kernels": kernels,
         "ms_per_step_stage_by_stage": sum(per.values()),
     }
-    return res, None
+    host = {k: d[k] for k in ("x", "wr", "w1", "w1_scale", "w2", "w2_scale", "K")}
+    return res, host
 
 
-def cpu_baseline_layer(host, target_s):
-    """The oracle (plain fp64 C) on the host cores: the whole layer on the
-    first n tokens of the same inputs, n grown until the run takes about
-    target_s seconds."""
-    import oracle
+def timing_record(ms_med, ms_min, ms_b2b, wall_s, steps, sclk_start):
+    return {"ms_per_step_median": ms_med, "ms_per_step_min": ms_min, "ms_per_step_back_to_back": ms_b2b,
+            "timed_loop_wall_s": wall_s, "steps": steps, "sclk_reported_at_start": sclk_start,
+            "protocol": "each step after a 1 GiB device write (outside its events), timed with HIP events "
+                        "on its stream; value from the median step"}
+
+
+def cpu_baseline_tokens(run, T, target_s, what):
+    """Time run(n, threads) -- the oracle on the first n tokens of the
+    workload -- with n grown until one run takes about a third of target_s
+    (or all T tokens); tokens/s of the last run."""
     nth = cpu_threads()
-    T = host["x"].shape[0]
-    n = min(T, 8)
+    n = min(T, 4)
     spent = 0.0
     while True:
         t0 = time.perf_counter()
-        oracle.layer(host["x"][:n], host["wr"], host["w1"], host["w2"], host["K"], bias=host["bias"],
-                     nthreads=nth)
+        run(n, nth)
         dt = time.perf_counter() - t0
         spent += dt
         if dt >= target_s / 3 or n >= T or spent > target_s:
             break
         n = min(T, max(n + 1, int(n * min(8.0, (target_s / 2) / max(dt, 1e-3)))))
-    return {"value": n / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
-            "sample": f"whole layer on the first {n} of {T} tokens (full weights), {dt:.1f} s"}
+    return dict(cpu_info(nth), value=n / dt, unit="tokens/s", kind="oracle",
+                sample=f"{what} on the first {n} of {T} tokens, {dt:.1f} s")
+
+
+def cpu_baseline_layer(host, target_s):
+    """The oracle (plain fp64 C) on the host cores: the whole layer on the
+    first n tokens of the same inputs (full weights)."""
+    import oracle
+    T = host["x"].shape[0]
+
+    def run(n, nth):
+        oracle.layer(host["x"][:n], host["wr"], host["w1"], host["w2"], host["K"], bias=host["bias"],
+                     nthreads=nth)
+
+    return cpu_baseline_tokens(run, T, target_s, "whole layer (route, permute, both GEMMs, combine)")
+
+
+def cpu_baseline_layer_fp8(host, target_s):
+    """The oracle's E4M3 layer on the first n tokens (full weights)."""
+    import numpy as np
+
+    import oracle
+    T = host["x"].shape[0]
+
+    def run(n, nth):
+        oracle.layer_fp8(host["x"], host["wr"], host["w1"], host["w1_scale"], host["w2"], host["w2_scale"],
+                         host["K"], tokens=np.arange(n), nthreads=nth)
+
+    return cpu_baseline_tokens(run, T, target_s, "whole E4M3 layer (per-token quantisation, both GEMMs)")
+
+
+def cpu_baseline_page2(host, target_s):
+    """The oracle on the page-2 step of the first n tokens: their K routed rows
+    through the grouped GEMM in the workload's quantisation (per-tensor, MX,
+    MXFP4, or per-token after the oracle's own quantisation), the Unpermute of
+    those rows, and their rows of the shared bf16 expert."""
+    import numpy as np
+
+    import oracle
+    d, mode = host["d"], host["mode"]
+    T, e, K = d["T"], d["e"], d["K"]
+    _, off, _, pdst = oracle.permute(d["topk_idx"], e)
+
+    def run(n, nth):
+        grouped = pdst[: n * K]
+        rows = np.sort(grouped)
+        ex = np.searchsorted(off, rows, side="right") - 1
+        sub_off = np.concatenate([[0], np.cumsum(np.bincount(ex, minlength=e))]).astype(np.int32)
+        if mode in ("mx", "mx4"):
+            f = oracle.gmm_mx4 if mode == "mx4" else oracle.gmm_mx
+            y = f(d["gmm_x"][rows], d["gmm_x_scale"][rows], d["gmm_w"], d["gmm_w_scale"], sub_off, nthreads=nth)
+        elif mode == "dyn":
+            q, sc = oracle.quant_rows(d["gmm_x"], rows=rows)
+            y = oracle.gmm(q, d["gmm_w"], sub_off, a_scale=sc.astype(np.float64), w_scale=float(d["gmm_w_scale"]),
+                           nthreads=nth)
+        else:
+            y = oracle.gmm(d["gmm_x"][rows], d["gmm_w"], sub_off, a_scale=float(d["gmm_x_scale"]),
+                           w_scale=float(d["gmm_w_scale"]), nthreads=nth)
+        local = np.searchsorted(rows, grouped).astype(np.int32)
+        oracle.combine(y, local, None, n, K)  # Unpermute into (token, slot) order
+        oracle.gmm(d["mm_x"][:n], d["mm_w"].reshape(1, d["H2"], d["N2"]), np.array([0, n], np.int32),
+                   nthreads=nth)
+
+    return cpu_baseline_tokens(run, T, target_s, "routed grouped GEMM + Unpermute + shared expert")
 
 
 def main():
@@ -686,10 +853,13 @@ def main():
         if args.workload == "prefill":  # the vendor's batched GEMM on even expert loads, for context
             even = (c["E"], c["T"] * c["K"] // c["E"], {"gemm1": (c["H"], c["F"]), "gemm2": (c["F"], c["H"])})
         res["achievable"] = achievable(dev, even)
-    if not args.no_cpu and host is not None:
-        res["cpu_baseline"] = cpu_baseline_layer(host, args.cpu_seconds)
-    elif not args.no_cpu:
-        res["cpu_baseline"] = None
+    if not args.no_cpu:
+        if args.workload == "prefill_fp8":
+            res["cpu_baseline"] = cpu_baseline_layer_fp8(host, args.cpu_seconds)
+        elif "d" in host:
+            res["cpu_baseline"] = cpu_baseline_page2(host, args.cpu_seconds)
+        else:
+            res["cpu_baseline"] = cpu_baseline_layer(host, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
