@@ -46,16 +46,35 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// The experts of pairs [begin, end) into registers, by one wave: pair
+// begin + 64j + lane in ev[j] (j < PL); all loads are issued before any is
+// used. end - begin <= 64 * PL.
+template <int PL>
+__device__ __forceinline__ void load_range(const int32_t* __restrict__ idx, int begin, int end, int E,
+                                           int ev[PL]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int raw[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int i = begin + 64 * j + lane;
+    raw[j] = i < end ? idx[i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < PL; ++j) ev[j] = clamp_e(raw[j], E);
+}
+
 // Counts pairs [begin, end) per expert into hist[0:256] (LDS, zeroed here), by one wave.
-__device__ __forceinline__ void count_range(const int32_t* __restrict__ idx, int begin, int end, int E,
-                                            int* hist) {
+template <int PL>
+__device__ __forceinline__ void count_regs(const int ev[PL], int begin, int end, int* hist) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int e = lane; e < 256; e += kWave) hist[e] = 0;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  for (int base = begin; base < end; base += kWave) {
-    const int i = base + lane;
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int i = begin + 64 * j + lane;
+    if (begin + 64 * j >= end) break;
     const bool valid = i < end;
-    const int e = valid ? clamp_e(idx[i], E) : 0;
+    const int e = ev[j];
     const uint64_t m = match_mask(e, valid);
     // the highest lane of each group of equal experts adds the group's size
     if (valid && (m >> lane) == 1ull) hist[e] += __popcll(m);
@@ -64,14 +83,16 @@ __device__ __forceinline__ void count_range(const int32_t* __restrict__ idx, int
 }
 
 // Ranks pairs [begin, end) into rows, starting from run[e] (LDS), by one wave.
-__device__ __forceinline__ void rank_range(const int32_t* __restrict__ idx, int begin, int end, int E,
-                                           int* run, int32_t* __restrict__ perm_src,
-                                           int32_t* __restrict__ perm_dst) {
+template <int PL>
+__device__ __forceinline__ void rank_regs(const int ev[PL], int begin, int end, int* run,
+                                          int32_t* __restrict__ perm_src, int32_t* __restrict__ perm_dst) {
   const int lane = threadIdx.x & (kWave - 1);
-  for (int base = begin; base < end; base += kWave) {
-    const int i = base + lane;
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int i = begin + 64 * j + lane;
+    if (begin + 64 * j >= end) break;
     const bool valid = i < end;
-    const int e = valid ? clamp_e(idx[i], E) : 0;
+    const int e = ev[j];
     const uint64_t m = match_mask(e, valid);
     const int rank = __popcll(m & lanemask_lt());
     int row = 0;
@@ -91,6 +112,7 @@ __device__ __forceinline__ void rank_range(const int32_t* __restrict__ idx, int 
 __global__ __launch_bounds__(kBlockWaves * kWave) void permute_block_kernel(
     const int32_t* __restrict__ idx, int A, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ perm_dst) {
+  constexpr int PL = kBlockA / kBlockWaves / kWave;  // pairs per lane (segments of <= kBlockA / nw)
   __shared__ int hist[kBlockWaves][256];  // count, then first row, per (wave, expert)
   __shared__ int tot[256];
   const int lane = threadIdx.x & (kWave - 1);
@@ -99,7 +121,9 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void permute_block_kernel(
   const int seg = cdiv(A, nw);
   const int begin = min(A, w * seg), end = min(A, begin + seg);
   int* mine = hist[w];
-  count_range(idx, begin, end, E, mine);
+  int ev[PL];
+  load_range<PL>(idx, begin, end, E, ev);
+  count_regs<PL>(ev, begin, end, mine);
   __syncthreads();
   // thread e: prefix over waves (segment order), total per expert
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -137,42 +161,72 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void permute_block_kernel(
   __syncthreads();
   for (int e = lane; e < E; e += kWave) mine[e] += tot[e];
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  rank_range(idx, begin, end, E, mine, perm_src, perm_dst);
+  rank_regs<PL>(ev, begin, end, mine, perm_src, perm_dst);
 }
 
+// Chunk c: per-expert counts of its kChunk pairs (LDS atomics: counts only,
+// so the order in which they land does not matter).
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx, int A,
                                                             int E, int32_t* __restrict__ chunk_counts) {
+  constexpr int PT = kChunk / 256;
   __shared__ int hist[256];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-  __syncthreads();
   const int begin = blockIdx.x * kChunk;
-  const int end = min(A, begin + kChunk);
-  for (int i = begin + threadIdx.x; i < end; i += blockDim.x) atomicAdd(&hist[clamp_e(idx[i], E)], 1);
+  int ev[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int i = begin + 256 * u + threadIdx.x;
+    ev[u] = i < A ? clamp_e(idx[i], E) : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < PT; ++u)
+    if (ev[u] >= 0) atomicAdd(&hist[ev[u]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
 // One block, thread e (E <= 256): total over chunks, exclusive scan over
-// experts, then the running prefix over chunks. Each pass issues the loads
-// of 16 chunks before adding them, in chunk order.
+// experts, then the running prefix over chunks. The (chunk, expert) counts
+// pass through LDS in tiles of kScanInts, loaded by all threads at once; when
+// they fit in one tile the second pass reuses it.
+constexpr int kScanInts = 12288;
+__device__ __forceinline__ void load_scan_tile(const int32_t* __restrict__ src, int n, int* cc) {
+  constexpr int U = 16;
+  for (int p0 = 0; p0 < n; p0 += 256 * U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 256 * u + threadIdx.x;
+      v[u] = p < n ? src[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 256 * u + threadIdx.x;
+      if (p < n) cc[p] = v[u];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __restrict__ chunk_counts,
                                                            int nchunks, int E, int A,
                                                            int32_t* __restrict__ chunk_base,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets) {
-  constexpr int U = 16;
+  __shared__ int cc[kScanInts];
   __shared__ int wsum[4];
   const int e = threadIdx.x;
   const int lane = e & (kWave - 1), w = e / kWave;
+  const int ct = kScanInts / E;  // chunks per tile
+  const bool resident = nchunks <= ct;
   int tot = 0;
-  if (e < E) {
-    for (int c0 = 0; c0 < nchunks; c0 += U) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u) tot += v[u];
-    }
+  for (int c0 = 0; c0 < nchunks; c0 += ct) {
+    const int nc = min(ct, nchunks - c0);
+    __syncthreads();
+    load_scan_tile(chunk_counts + (int64_t)c0 * E, nc * E, cc);
+    __syncthreads();
+    if (e < E)
+      for (int c = 0; c < nc; ++c) tot += cc[c * E + e];
   }
   const int incl = wave_incl_scan(tot);
   if (lane == kWave - 1) wsum[w] = incl;
@@ -182,17 +236,20 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __rest
   if (e < E) {
     counts[e] = tot;
     offsets[e] = excl;
-    int run = excl;
-    for (int c0 = 0; c0 < nchunks; c0 += U) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (c0 + u < nchunks) chunk_base[(int64_t)(c0 + u) * E + e] = run;
-        run += v[u];
-      }
+  }
+  int run = excl;
+  for (int c0 = 0; c0 < nchunks; c0 += ct) {
+    const int nc = min(ct, nchunks - c0);
+    if (!resident) {
+      __syncthreads();
+      load_scan_tile(chunk_counts + (int64_t)c0 * E, nc * E, cc);
+      __syncthreads();
     }
+    if (e < E)
+      for (int c = 0; c < nc; ++c) {
+        chunk_base[(int64_t)(c0 + c) * E + e] = run;
+        run += cc[c * E + e];
+      }
   }
   if (e == 0) offsets[E] = A;
 }
@@ -204,11 +261,14 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ perm_src,
                                                            int32_t* __restrict__ perm_dst) {
   constexpr int kQuarter = kChunk / 4;
+  constexpr int PL = kQuarter / kWave;
   __shared__ int hist[4][256];
   const int w = threadIdx.x / kWave;
   const int begin = min(A, blockIdx.x * kChunk + w * kQuarter);
   const int end = min(A, begin + kQuarter);
-  count_range(idx, begin, end, E, hist[w]);
+  int ev[PL];
+  load_range<PL>(idx, begin, end, E, ev);
+  count_regs<PL>(ev, begin, end, hist[w]);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = chunk_base[(int64_t)blockIdx.x * E + e];
@@ -220,7 +280,7 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
     }
   }
   __syncthreads();
-  rank_range(idx, begin, end, E, hist[w], perm_src, perm_dst);
+  rank_regs<PL>(ev, begin, end, hist[w], perm_src, perm_dst);
 }
 
 // Row scatter: x_perm[perm_dst[t*K+k]] = x[t]. VB = bytes per access.

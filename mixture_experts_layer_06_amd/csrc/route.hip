@@ -8,23 +8,29 @@
 //
 // gfx950 design. bf16: the router GEMM runs on v_mfma_f32_16x16x32_bf16
 // with the router weights as the row operand (64 experts per group of four
-// MFMAs) and the token rows as the column operand. Weights are loaded
-// straight from global memory in MFMA layout: a lane reads 8 consecutive h
-// of 4 adjacent experts (8 bytes per row) and transposes them in registers
-// into four fragments, MFMA j's row i being expert 4i+j; token fragments
-// are 16-byte loads. No LDS staging, so every wave keeps the loads of a
-// whole 32-wide chunk in flight.
+// MFMAs) and the token rows as the column operand. A block owns 16, 32 or
+// 64 tokens (more when there are many experts and many tokens, so that the
+// weights are read once for more rows) and a range of H. It copies the
+// router weights of its range into LDS with 16-byte loads, in slabs when
+// they do not fit; its waves take interleaved 32-wide chunks of the range,
+// keep the 16-byte token loads of several chunks in flight, read the
+// weight rows of a chunk from LDS (8 consecutive h of 4 adjacent experts
+// per lane) and transpose them in registers into four fragments, MFMA j's
+// row i being expert 4i+j. The waves' partial scores are summed in a fixed
+// order in LDS. Loading the weights per chunk from global memory instead
+// made the address unit the bottleneck (8 weight loads per token load).
 //
-// A block owns 16 tokens and a range of H; its
-// waves take interleaved 32-wide chunks of the range and their partial
-// scores are summed in a fixed order in LDS. With few token tiles (decode)
-// H is split over S blocks per tile so that W_r streams through many CUs:
-// each block writes its fp32 partial scores to the workspace and a second
-// kernel sums the S partials in split order before selection. fp32: plain
-// FMA dot products (the fp32 layer is a small-shape correctness
-// configuration). Top-k is K rounds of a wave-wide argmax butterfly on
-// (score, expert) pairs: larger score wins, equal scores go to the lower
-// expert index.
+// With few token tiles (decode) H is split over S blocks per tile so that
+// W_r streams through many CUs: each block writes its fp32 partial scores
+// to the workspace and a second kernel sums the S partials in split order
+// before selection, one wave per token. fp32: plain FMA dot products (the
+// fp32 layer is a small-shape correctness configuration).
+//
+// Top-k is K rounds of a register-only argmax: the largest score among the
+// experts not yet taken (DPP max across the lanes) and, among the experts
+// holding it, the lowest index, so larger score wins and equal scores go to
+// the lower expert index. With at most 64 experts a wave selects four
+// tokens at once, one per 16-lane row.
 #include "common.h"
 
 
@@ -35,100 +41,225 @@ constexpr int kTok = 16;   // tokens per block
 constexpr int kWaves = 4;  // waves per block
 constexpr int kChunk = 32; // h per MFMA step
 
-// Argmax butterfly: (v,e) is better than (w,f) if v > w, or v == w and e < f.
-__device__ __forceinline__ void wave_argmax(float& v, int& e) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off, kWave);
-    int oe = __shfl_xor(e, off, kWave);
-    bool take = (ov > v) || (ov == v && oe < e);
-    v = take ? ov : v;
-    e = take ? oe : e;
-  }
+// Wave-wide max / min through DPP lane moves (quad permutes, row mirrors,
+// then the row broadcasts of lanes 15 and 31), read from lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp_mov<0xB1, 0xf>(__float_as_int(v))));   // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(dpp_mov<0x4E, 0xf>(__float_as_int(v))));   // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(dpp_mov<0x141, 0xf>(__float_as_int(v))));  // row_half_mirror
+  v = fmaxf(v, __int_as_float(dpp_mov<0x140, 0xf>(__float_as_int(v))));  // row_mirror
+  v = fmaxf(v, __int_as_float(dpp_mov<0x142, 0xa>(__float_as_int(v))));  // row_bcast:15
+  v = fmaxf(v, __int_as_float(dpp_mov<0x143, 0xc>(__float_as_int(v))));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_min(int v) {
+  v = min(v, dpp_mov<0xB1, 0xf>(v));
+  v = min(v, dpp_mov<0x4E, 0xf>(v));
+  v = min(v, dpp_mov<0x141, 0xf>(v));
+  v = min(v, dpp_mov<0x140, 0xf>(v));
+  v = min(v, dpp_mov<0x142, 0xa>(v));
+  v = min(v, dpp_mov<0x143, 0xc>(v));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Top-k + sparse softmax for one token whose E scores sit in LDS row `lg`.
-// Called by a whole wave; lane k < K writes slot k. A NaN score (from
-// non-finite inputs) counts as -inf, so every round picks an unselected
-// expert and the indices stay in [0, E); the gates of such a token are
-// then unspecified.
-__device__ __forceinline__ void topk_softmax_token(const float* lg, int E, int K, int32_t* idx_out,
-                                                   float* gate_out) {
+// Top-k + sparse softmax for one token whose E scores sit in LDS row `lg`,
+// by a whole wave. Lane l holds experts l + 64i (i < G). K rounds: the
+// largest score among the experts not yet taken (wave max), and among the
+// experts holding it the lowest index, which goes to the next slot. A NaN
+// score (from non-finite inputs) counts as -inf, so every slot names an
+// unselected expert in [0, E); the gates of such a token are then
+// unspecified. Gates: p_k = exp(v_k - v_0), summed in slot order, times the
+// reciprocal of the sum.
+__device__ __forceinline__ float nan_to_ninf(float v) { return v == v ? v : -INFINITY; }
+
+template <int G>
+__device__ __forceinline__ void topk_softmax_token(const float* lg, int E, int K, bool hb, const float (&bv)[G],
+                                                   int32_t* idx_out, float* gate_out) {
   const int lane = threadIdx.x & (kWave - 1);
-  float cand[4];
-  bool taken[4];
+  float v[G];
+  bool alive[G];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int e = lane + kWave * i;
-    const float v = e < E ? lg[e] : -INFINITY;
-    cand[i] = v == v ? v : -INFINITY;
-    taken[i] = e >= E;
+  for (int i = 0; i < G; ++i) {
+    const int e = lane + kWave * i;
+    alive[i] = e < E;
+    v[i] = alive[i] ? nan_to_ninf(hb ? lg[e] + bv[i] : lg[e]) : -INFINITY;
   }
-  float sel_v[8];
-  int sel_e[8];
+  float sv[8];
+  int se[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sv[k] = -INFINITY;
+    se[k] = 0;
+    if (k < K) {
+      // this lane's best live expert (its lowest index among equal scores)
+      float best = -INFINITY;
+      int bi = -1;
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        if (alive[i] && (bi < 0 || v[i] > best)) {
+          best = v[i];
+          bi = i;
+        }
+      const float m = wave_max(best);
+      const bool hit = bi >= 0 && best == m;
+      int eb;
+      if (G == 1) {
+        eb = __ffsll((unsigned long long)__ballot(hit)) - 1;  // lane = expert
+      } else {
+        eb = wave_min(hit ? lane + kWave * bi : 0x7fffffff);
+      }
+      sv[k] = m;
+      se[k] = eb;
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        if (lane + kWave * i == eb) alive[i] = false;
+    }
+  }
+  const float m = sv[0];
+  float s = 0.f, mine = 0.f;
+  int my_e = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if (k < K) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int e = lane + kWave * i;
-        bool better = !taken[i] && ((cand[i] > bv) || (cand[i] == bv && e < be));
-        bv = better ? cand[i] : bv;
-        be = better ? e : be;
+      const float p = expf(sv[k] - m);
+      s += p;
+      if (k == lane) {
+        mine = p;
+        my_e = se[k];
       }
-      wave_argmax(bv, be);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + kWave * i == be) taken[i] = true;
-      sel_v[k] = bv;
-      sel_e[k] = be;
-    } else {
-      sel_v[k] = -INFINITY;
-      sel_e[k] = 0;
     }
-  }
-  const float m = sel_v[0];
-  float p[8];
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    p[k] = k < K ? expf(sel_v[k] - m) : 0.f;
-    s += p[k];
   }
   const float inv = 1.0f / s;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if (k < K && lane == k) {
-      idx_out[k] = sel_e[k];
-      gate_out[k] = p[k] * inv;
-    }
+  if (lane < K) {
+    idx_out[lane] = my_e;
+    gate_out[lane] = mine * inv;
   }
 }
 
-// G = 64-expert groups (E <= 64*G).
-// AL: H % 8 == 0, E % 4 == 0 and aligned rows, so a lane's 16-byte token
-// loads and 8-byte weight loads never straddle a row end and can be buffer
-// loads (out-of-range reads give 0). Grid: (token tiles, S). S == 1: the
-// block selects; S > 1: it writes its partial scores to part[s][t][64*G].
-// Dynamic LDS: partial scores [waves][16][64*G] fp32.
-template <int G, bool AL>
-__global__ __launch_bounds__(G <= 2 ? 1024 : 512) void route_bf16_kernel(const bf16_t* __restrict__ x,
-                                                          const bf16_t* __restrict__ wr,
-                                                          const float* __restrict__ bias, int T,
-                                                          int H, int E, int K,
-                                                          int32_t* __restrict__ idx,
-                                                          float* __restrict__ gate,
-                                                          float* __restrict__ part_out) {
+// The same for four tokens at once, E <= 64: 16-lane row r of the wave
+// takes token r (rows at lg + r * stride, present when r < nrow); lane j of
+// a row holds experts j + 16i (i < 4). Row max / min through the in-row DPP
+// moves only.
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp_mov<0xB1, 0xf>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_mov<0x4E, 0xf>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_mov<0x141, 0xf>(__float_as_int(v))));
+  return fmaxf(v, __int_as_float(dpp_mov<0x140, 0xf>(__float_as_int(v))));
+}
+__device__ __forceinline__ int row_min(int v) {
+  v = min(v, dpp_mov<0xB1, 0xf>(v));
+  v = min(v, dpp_mov<0x4E, 0xf>(v));
+  v = min(v, dpp_mov<0x141, 0xf>(v));
+  return min(v, dpp_mov<0x140, 0xf>(v));
+}
+
+__device__ __forceinline__ void topk_softmax_rows(const float* lg, int stride, int nrow, int E, int K, bool hb,
+                                                  const float (&bv)[4], int32_t* idx_out, float* gate_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane >> 4, j = lane & 15;
+  const bool live = r < nrow;
+  const float* row = lg + (live ? r : 0) * stride;
+  float v[4];
+  bool alive[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = j + 16 * i;
+    alive[i] = e < E;
+    v[i] = alive[i] ? nan_to_ninf(hb ? row[e] + bv[i] : row[e]) : -INFINITY;
+  }
+  float sv[8];
+  int se[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sv[k] = -INFINITY;
+    se[k] = 0;
+    if (k < K) {
+      float best = -INFINITY;
+      int bi = -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (alive[i] && (bi < 0 || v[i] > best)) {
+          best = v[i];
+          bi = i;
+        }
+      const float m = row_max(best);
+      const int eb = row_min(bi >= 0 && best == m ? j + 16 * bi : 0x7fffffff);
+      sv[k] = m;
+      se[k] = eb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j + 16 * i == eb) alive[i] = false;
+    }
+  }
+  const float m = sv[0];
+  float s = 0.f, mine = 0.f;
+  int my_e = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k < K) {
+      const float p = expf(sv[k] - m);
+      s += p;
+      if (k == j) {
+        mine = p;
+        my_e = se[k];
+      }
+    }
+  }
+  const float inv = 1.0f / s;
+  if (live && j < K) {
+    idx_out[r * K + j] = my_e;
+    gate_out[r * K + j] = mine * inv;
+  }
+}
+
+// Fixed-order sum of the nw wave slices (stride `slice` floats) of element p.
+__device__ __forceinline__ float sum_slices(const float* part, int p, int nw, int slice) {
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = q < nw ? part[q * slice + p] : 0.f;
+  float sc = v[0];
+#pragma unroll
+  for (int q = 1; q < 16; ++q)
+    if (q < nw) sc += v[q];
+  return sc;
+}
+
+// G = 64-expert groups (E <= 64*G); TF = 16-token fragments per block.
+// AL: H % 8 == 0, E % 4 == 0 and aligned rows. Then the block copies the
+// router weights of its H range into LDS in slabs of `slab_rows` rows (one
+// slab when they fit), with 16-byte loads, and the multiply loop reads them
+// from there: its only global loads are the token rows, 16 bytes per lane,
+// D chunks of them in flight per wave. Otherwise (unaligned shapes) each
+// wave loads its weight fragments with element loads, one chunk at a time.
+// Out-of-range buffer loads give 0. Grid: (token tiles of 16*TF, S).
+// S == 1: the block selects; S > 1 (TF == 1 only): it writes its partial
+// scores to part[s][t][64*G].
+// Dynamic LDS: the weight slab during the multiply loop, then the partial
+// scores [waves][16*TF][64*G + 4] fp32.
+template <int G, int TF, bool AL>
+constexpr int route_depth() { return !AL ? 1 : (TF * G == 1 ? 5 : (TF == 4 ? 3 : 2)); }
+
+template <int G, int TF, bool AL>
+__global__ __launch_bounds__(G * TF <= 2 ? 1024 : 512) void route_bf16_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias, int T, int H,
+    int E, int K, int slab_rows, int32_t* __restrict__ idx, float* __restrict__ gate,
+    float* __restrict__ part_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int EP = 64 * G;
+  constexpr int EPS = EP + 4;    // LDS row stride of the partial scores (16 rows per store spread over the banks)
+  constexpr int NT = kTok * TF;  // tokens per block
+  static_assert(G * TF <= 4, "register budget");
+  constexpr int D = route_depth<G, TF, AL>();
   float* part = reinterpret_cast<float*>(smem);
   const int nw = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t0 = blockIdx.x * kTok;
-  const int ntok = min(kTok, T - t0);
+  const int t0 = blockIdx.x * NT;
+  const int ntok = min(NT, T - t0);
   const int ci = lane & 15, kq = lane >> 4;
   const int nch = cdiv(H, kChunk);
   const int S = gridDim.y;
@@ -137,36 +268,36 @@ __global__ __launch_bounds__(G <= 2 ? 1024 : 512) void route_bf16_kernel(const b
 
   const __amdgpu_buffer_rsrc_t xs = make_rsrc(x + (int64_t)t0 * H, (uint32_t)ntok * (uint32_t)H * 2u);
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(wr, (uint32_t)H * (uint32_t)E * 2u);
-  uint32_t wo[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int e0 = 64 * g + 4 * ci;
-    wo[g] = (uint32_t)(kq * 8) * (uint32_t)E * 2u + (uint32_t)e0 * 2u + (e0 < E ? 0u : kOOB);
-  }
 
-  // Token fragment of chunk c: token ci, h = 32c + 8kq .. +7.
-  auto load_x = [&](int c) -> uint4 {
+  // Token fragment f of chunk c: token 16f + ci, h = 32c + 8kq .. +7; zeros
+  // unless c < cend.
+  auto load_x = [&](int c, int f, int cend) -> uint4 {
     const int h = c * kChunk + 8 * kq;
+    const bool in = c < cend && h < H;
     if (AL) return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       xs, (uint32_t)ci * (uint32_t)H * 2u + (uint32_t)h * 2u + (h < H ? 0u : kOOB), 0, 0));
+                       xs, ((uint32_t)(16 * f + ci) * (uint32_t)H * 2u + (uint32_t)h * 2u) | (in ? 0u : kOOB), 0, 0));
     uint32_t v[4];
+    const int tt = 16 * f + ci;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok0 = ci < ntok && h + 2 * i < H, ok1 = ci < ntok && h + 2 * i + 1 < H;
-      const bf16_t* p = x + (int64_t)(t0 + ci) * H + h + 2 * i;
+      const bool ok0 = in && tt < ntok && h + 2 * i < H, ok1 = in && tt < ntok && h + 2 * i + 1 < H;
+      const bf16_t* p = x + (int64_t)(t0 + tt) * H + h + 2 * i;
       v[i] = (ok0 ? (uint32_t)p[0] : 0u) | ((ok1 ? (uint32_t)p[1] : 0u) << 16);
     }
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
-  // Weight rows h = 32c + 8kq + r (r < 8) of experts 64g + 4ci .. +3.
-  auto load_w = [&](int c, int g, uint2 raw[8]) {
+  // Weight rows h = 32c + 8kq + r (r < 8) of experts 64g + 4ci .. +3: from the
+  // LDS slab holding rows [hs, he) (AL), else from global memory.
+  auto load_w = [&](int c, int g, int hs, int he, uint2 raw[8]) {
+    const int e0 = 64 * g + 4 * ci;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
+      const int h = c * kChunk + 8 * kq + r;
       if (AL) {
-        raw[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                     ws, wo[g] + (uint32_t)(c * kChunk + r) * (uint32_t)E * 2u, 0, 0));
+        raw[r] = (e0 < E && h < he)
+                     ? *reinterpret_cast<const uint2*>(smem + ((size_t)(h - hs) * E + e0) * 2)
+                     : make_uint2(0u, 0u);
       } else {
-        const int h = c * kChunk + 8 * kq + r, e0 = 64 * g + 4 * ci;
         uint32_t v[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -179,100 +310,162 @@ __global__ __launch_bounds__(G <= 2 ? 1024 : 512) void route_bf16_kernel(const b
     }
   };
 
-  f32x4_t acc[G][4];
+  f32x4_t acc[G][4][TF];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[g][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  for (int c = c_begin + w; c < c_end; c += nw) {
-    uint2 raw[G][8];
-    const uint4 xr = load_x(c);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int g = 0; g < G; ++g) load_w(c, g, raw[g]);
+      for (int f = 0; f < TF; ++f) acc[g][j][f] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  // Slabs of the H range (AL: slab_rows is a multiple of 32; otherwise one
+  // slab). In each, this wave's chunks are cs + w, cs + w + nw, ...; the token
+  // loads of D of them are in flight while the oldest is multiplied.
+  const int h0 = c_begin * kChunk, h1 = min(H, c_end * kChunk);
+  const int step = AL ? slab_rows : (h1 > h0 ? h1 - h0 : 1);
+  for (int hs = h0; hs < h1; hs += step) {
+    const int he = min(h1, hs + step);
+    const int cs = hs / kChunk, ce = cdiv(he, kChunk);
+    uint4 xr[D][TF];
+    const int c0 = cs + w;
+    const int nmine = c0 < ce ? cdiv(ce - c0, nw) : 0;
+    auto issue = [&](int i, int slot) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      uint4 wc[4];
-      transpose_8x4_bf16(raw[g], wc);
+      for (int f = 0; f < TF; ++f) xr[slot][f] = load_x(c0 + i * nw, f, ce);
+    };
+    // the first token loads are in flight while the slab is copied
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, wc[j]), __builtin_bit_cast(bf16x8_t, xr), acc[g][j], 0, 0, 0);
+    for (int i = 0; i < D - 1; ++i) issue(i, i);
+    if (AL) {
+      // copy rows [hs, he) (contiguous in global memory) into the slab
+      constexpr int U = 4;
+      const int npiece = cdiv((he - hs) * E * 2, 16);
+      const uint32_t gbase = (uint32_t)hs * (uint32_t)E * 2u;
+      __syncthreads();  // every wave is done with the previous slab
+      for (int p0 = 0; p0 < npiece; p0 += U * (int)blockDim.x) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int p = p0 + u * (int)blockDim.x + (int)threadIdx.x;
+          v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     ws, (gbase + (uint32_t)p * 16u) | (p < npiece ? 0u : kOOB), 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int p = p0 + u * (int)blockDim.x + (int)threadIdx.x;
+          if (p < npiece) *reinterpret_cast<uint4*>(smem + (size_t)p * 16) = v[u];
+        }
+      }
+      __syncthreads();
+    }
+    for (int i0 = 0; i0 < nmine; i0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        issue(i0 + u + D - 1, (u + D - 1) % D);
+        if (i0 + u < nmine) {
+          const int c = c0 + (i0 + u) * nw;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            uint2 raw[8];
+            load_w(c, g, hs, he, raw);
+            uint4 wc[4];
+            transpose_8x4_bf16(raw, wc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int f = 0; f < TF; ++f)
+                acc[g][j][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, wc[j]), __builtin_bit_cast(bf16x8_t, xr[u][f]), acc[g][j][f], 0,
+                    0, 0);
+          }
+        }
+      }
     }
   }
-  // acc[g][j][r]: token ci, expert 64g + 16kq + 4r + j (this wave's chunks).
+  if (AL) __syncthreads();  // the partial scores overwrite the slab
+  // acc[g][j][f][r]: token 16f + ci, expert 64g + 16kq + 4r + j (this wave's chunks).
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int f = 0; f < TF; ++f)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<f32x4_t*>(part + (w * kTok + ci) * EP + 64 * g + 16 * kq + 4 * r) =
-          (f32x4_t){acc[g][0][r], acc[g][1][r], acc[g][2][r], acc[g][3][r]};
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<f32x4_t*>(part + (w * NT + 16 * f + ci) * EPS + 64 * g + 16 * kq + 4 * r) =
+            (f32x4_t){acc[g][0][f][r], acc[g][1][f][r], acc[g][2][f][r], acc[g][3][f][r]};
   __syncthreads();
   // Fixed-order sum over waves into the first wave's slice; with S > 1 it
-  // goes to the workspace instead (bias is added once, after the splits).
+  // goes to the workspace instead (the bias is added at the selection, or
+  // after the splits).
   for (int p = threadIdx.x; p < ntok * EP; p += blockDim.x) {
-    float sc = part[p];
-    for (int q = 1; q < nw; ++q) sc += part[q * kTok * EP + p];
-    if (S > 1) {
-      part_out[((int64_t)blockIdx.y * T + t0) * EP + p] = sc;
-    } else {
-      const int e = p % EP;
-      if (bias && e < E) sc += bias[e];
-      part[p] = sc;
-    }
+    const int e = p % EP, pl = (p / EP) * EPS + e;
+    float sc = sum_slices(part, pl, nw, NT * EPS);
+    if (S > 1) part_out[((int64_t)blockIdx.y * T + t0) * EP + p] = sc;
+    else part[pl] = sc;
   }
   if (S > 1) return;
   __syncthreads();
-  for (int tt = w; tt < ntok; tt += nw)
-    topk_softmax_token(part + tt * EP, E, K, idx + (int64_t)(t0 + tt) * K, gate + (int64_t)(t0 + tt) * K);
+  // selection (the bias, if any, is added to the sums here)
+  const bool hb = bias != nullptr;
+  if (G == 1) {
+    float bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = (lane & 15) + 16 * i;
+      bv[i] = (hb && e < E) ? bias[e] : 0.f;
+    }
+    for (int tt = 4 * w; tt < ntok; tt += 4 * nw)
+      topk_softmax_rows(part + tt * EPS, EPS, min(4, ntok - tt), E, K, hb, bv, idx + (int64_t)(t0 + tt) * K,
+                        gate + (int64_t)(t0 + tt) * K);
+  } else {
+    float bv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int e = lane + kWave * i;
+      bv[i] = (hb && e < E) ? bias[e] : 0.f;
+    }
+    for (int tt = w; tt < ntok; tt += nw)
+      topk_softmax_token<G>(part + tt * EPS, E, K, hb, bv, idx + (int64_t)(t0 + tt) * K,
+                            gate + (int64_t)(t0 + tt) * K);
+  }
 }
 
-// Sum of the S partial score rows of 16 tokens (split order), bias, selection.
-// Each thread sums whole (token, expert) columns; the loads of 8 splits are
-// issued before they are added, in split order.
+// Sum of the S partial score rows of a token (split order), bias, selection:
+// one wave per token, lane l owning experts l + 64i. The loads of 16 splits
+// are in flight before they are added, in split order.
 template <int G>
-__global__ __launch_bounds__(1024) void route_finish_kernel(const float* __restrict__ part_in, int S,
-                                                            const float* __restrict__ bias, int T,
-                                                            int E, int K, int32_t* __restrict__ idx,
-                                                            float* __restrict__ gate) {
+__global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ part_in, int S,
+                                                           const float* __restrict__ bias, int T,
+                                                           int E, int K, int32_t* __restrict__ idx,
+                                                           float* __restrict__ gate) {
   constexpr int EP = 64 * G;
-  __shared__ float lg[kTok * EP];
-  const int t0 = blockIdx.x * kTok;
-  const int ntok = min(kTok, T - t0);
-  const float* src = part_in + (int64_t)t0 * EP;
+  __shared__ float lg[4][EP];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * 4 + w;
+  const bool live = t < T;
+  const float* src = part_in + (int64_t)(live ? t : 0) * EP;
   const int64_t split = (int64_t)T * EP;
-  // each thread owns PPT (token, expert) columns; the loads of 16 splits of
-  // all of them are in flight before the adds, which go in split order
-  constexpr int PPT = kTok * EP / 1024;
-  static_assert(kTok * EP % 1024 == 0, "columns per thread");
-  float sc[PPT];
+  float sc[G];
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) sc[i] = 0.f;
+  for (int i = 0; i < G; ++i) sc[i] = 0.f;
   for (int q0 = 0; q0 < S; q0 += 16) {
-    float v[PPT][16];
+    float v[G][16];
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = threadIdx.x + 1024 * i;
+    for (int i = 0; i < G; ++i)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[i][u] = (q0 + u < S && p < ntok * EP) ? src[(q0 + u) * split + p] : 0.f;
-    }
+      for (int u = 0; u < 16; ++u) v[i][u] = (live && q0 + u < S) ? src[(q0 + u) * split + lane + 64 * i] : 0.f;
 #pragma unroll
-    for (int i = 0; i < PPT; ++i)
+    for (int i = 0; i < G; ++i)
 #pragma unroll
       for (int u = 0; u < 16; ++u) sc[i] += v[i][u];
   }
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int p = threadIdx.x + 1024 * i;
-    if (p >= ntok * EP) continue;
-    const int e = p % EP;
-    float x = sc[i];
-    if (bias && e < E) x += bias[e];
-    lg[p] = x;
+  for (int i = 0; i < G; ++i) {
+    const int e = lane + 64 * i;
+    lg[w][e] = (bias && e < E) ? sc[i] + bias[e] : sc[i];
   }
   __syncthreads();
-  const int w = threadIdx.x / kWave;
-  for (int tt = w; tt < ntok; tt += (int)(blockDim.x / kWave))
-    topk_softmax_token(lg + tt * EP, E, K, idx + (int64_t)(t0 + tt) * K, gate + (int64_t)(t0 + tt) * K);
+  const float nob[G] = {};
+  if (live) topk_softmax_token<G>(lg[w], E, K, false, nob, idx + (int64_t)t * K, gate + (int64_t)t * K);
 }
 
 // fp32: one thread per (token, expert) pair, sequential fp32 FMA over h.
@@ -297,57 +490,90 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
   }
   __syncthreads();
   const int w = threadIdx.x / kWave;
+  const float nob[4] = {};
   for (int tt = w; tt < kTok; tt += kWaves) {
     const int t = t0 + tt;
-    if (t < T) topk_softmax_token(lg + tt * E, E, K, idx + (int64_t)t * K, gate + (int64_t)t * K);
+    if (t < T) topk_softmax_token<4>(lg + tt * E, E, K, false, nob, idx + (int64_t)t * K, gate + (int64_t)t * K);
   }
 }
 
 // Launch shape of the bf16 router for (T, H, E).
 struct RoutePlan {
-  int G, S, nw;
+  int G, TF, S, nw;
+  size_t lds;     // dynamic LDS bytes
+  int slab_rows;  // W_r rows per LDS slab (aligned path)
 };
 
 RoutePlan route_plan(int T, int H, int E) {
   RoutePlan p;
   p.G = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
-  const int tiles = cdiv(T, kTok);
+  const int tiles16 = cdiv(T, kTok);
+  // With many experts the router weights (H x E) outweigh a 16-token block's
+  // rows: blocks of 32 or 64 tokens read them once for more tokens, while
+  // there are still at least as many blocks as CUs.
+  p.TF = 1;
+  if (E > 16) p.TF = tiles16 >= 4 * 256 ? 4 : (tiles16 >= 2 * 256 ? 2 : 1);
+  if (p.TF * p.G > 4) p.TF = 4 / p.G;  // register budget
+  const int tiles = cdiv(T, kTok * p.TF);
   const int nch = cdiv(H, kChunk);
   // Fewer token tiles than CUs: split H (powers of two) until there are
   // about as many blocks as CUs, keeping at least 4 chunks per block.
   p.S = 1;
   if (tiles < 256)
     while (tiles * p.S < 256 && nch / (2 * p.S) >= 4) p.S *= 2;
-  // waves: one chunk each up to the cap; LDS holds waves * 16 * 64*G floats (<= 128 KB)
-  const int cap = p.G <= 2 ? 16 : 8;
+  // waves: one chunk each up to the cap; the partial scores take waves * 16TF * (64G + 4) floats (<= 139 KB)
+  const int lds_cap = 32 / (p.TF * p.G);
+  const int thr_cap = (p.G * p.TF <= 2 ? 1024 : 512) / kWave;
+  const int cap = lds_cap < thr_cap ? lds_cap : thr_cap;
   int nw = cdiv(nch, p.S);
   p.nw = nw < 1 ? 1 : (nw > cap ? cap : nw);
+  // LDS: the partial scores, or the weight slab if larger (<= 128 KB); a
+  // slab holds whole 32-row chunks of W_r (E * 2 bytes per row)
+  const size_t part_bytes = (size_t)p.nw * kTok * p.TF * (64 * p.G + 4) * 4;
+  const size_t row_b = (size_t)E * 2;
+  const int range_rows = cdiv(nch, p.S) * kChunk;
+  size_t slab = (size_t)range_rows * row_b;
+  if (slab > 128 * 1024) slab = 128 * 1024;
+  p.lds = part_bytes > slab ? part_bytes : slab;
+  p.slab_rows = (int)(p.lds / row_b) / kChunk * kChunk;
   return p;
 }
 
-template <int G, bool AL>
+template <int G, int TF, bool AL>
 void launch_bf16(const RoutePlan& p, const void* x, const void* wr, const float* bias, int T, int H,
                  int E, int K, int32_t* idx, float* gate, float* part, hipStream_t s) {
-  const size_t lds = (size_t)p.nw * kTok * 64 * G * 4;
+  const size_t lds = AL ? p.lds : (size_t)p.nw * kTok * TF * (64 * G + 4) * 4;
   static bool attr_done = false;
   if (!attr_done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_bf16_kernel<G, AL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_bf16_kernel<G, TF, AL>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_done = true;
   }
-  hipLaunchKernelGGL((route_bf16_kernel<G, AL>), dim3(cdiv(T, kTok), p.S), dim3(p.nw * kWave),
-                     lds, s, (const bf16_t*)x, (const bf16_t*)wr, bias, T, H, E, K, idx, gate, part);
+  hipLaunchKernelGGL((route_bf16_kernel<G, TF, AL>), dim3(cdiv(T, kTok * TF), p.S), dim3(p.nw * kWave),
+                     lds, s, (const bf16_t*)x, (const bf16_t*)wr, bias, T, H, E, K, p.slab_rows, idx, gate, part);
   if (p.S > 1)
-    hipLaunchKernelGGL((route_finish_kernel<G>), dim3(cdiv(T, kTok)), dim3(1024), 0, s, part, p.S, bias,
-                       T, E, K, idx, gate);
+    hipLaunchKernelGGL((route_finish_kernel<G>), dim3(cdiv(T, 4)), dim3(256), 0, s, part, p.S, bias, T, E, K,
+                       idx, gate);
+}
+
+template <int G, bool AL>
+void launch_bf16_tf(const RoutePlan& p, const void* x, const void* wr, const float* bias, int T, int H,
+                    int E, int K, int32_t* idx, float* gate, float* part, hipStream_t s) {
+  if constexpr (G == 4) {
+    launch_bf16<G, 1, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+  } else {
+    if (p.TF == 1) launch_bf16<G, 1, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+    else if (p.TF == 2) launch_bf16<G, 2, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+    else launch_bf16<G, 4 / G, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+  }
 }
 
 template <bool AL>
 void launch_bf16_e(const RoutePlan& p, const void* x, const void* wr, const float* bias, int T, int H,
                    int E, int K, int32_t* idx, float* gate, float* part, hipStream_t s) {
-  if (p.G == 1) launch_bf16<1, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
-  else if (p.G == 2) launch_bf16<2, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
-  else launch_bf16<4, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+  if (p.G == 1) launch_bf16_tf<1, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+  else if (p.G == 2) launch_bf16_tf<2, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+  else launch_bf16_tf<4, AL>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
 }
 
 }  // namespace
@@ -368,7 +594,7 @@ moe_status launch_route(const void* x, const void* wr, moe_dtype dt, const float
     if (al) launch_bf16_e<true>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
     else launch_bf16_e<false>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
   } else {
-    hipLaunchKernelGGL(route_f32_kernel, dim3(cdiv(T, kTok)), dim3(256), (size_t)kTok * E * 4, s,
+    hipLaunchKernelGGL(route_f32_kernel, dim3(cdiv(T, kTok)), dim3(kWaves * kWave), (size_t)kTok * E * 4, s,
                        (const float*)x, (const float*)wr, bias, T, H, E, K, idx, gate);
   }
   return launch_status();

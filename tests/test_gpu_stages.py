@@ -47,6 +47,10 @@ ROUTE_CASES = [
     ("t16400_bias", 16400, 64, 40, 3, "bf16", False, True),
     ("t16400_ragged", 16400, 65, 40, 2, "bf16", False, False),
     ("split_ragged_bias", 30, 1001, 60, 4, "bf16", False, True),
+    # 32- and 64-token blocks (many tokens, more than 16 experts), aligned or not
+    ("t8200_e40", 8200, 128, 40, 4, "bf16", False, False),
+    ("t16400_e128_bias", 16400, 256, 128, 8, "bf16", False, True),
+    ("t8200_e72_ragged", 8200, 66, 72, 3, "bf16", False, False),
 ]
 
 
