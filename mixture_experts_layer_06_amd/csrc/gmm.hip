@@ -44,54 +44,24 @@
 
 #include "common.h"
 
-// 1: the bf16 ping-pong kernel may split its last, partial round of tiles along K.
-#ifndef MOE_GMM_SPLIT
-#define MOE_GMM_SPLIT 1
-#endif
-// Pair launch: 1 = the bf16 group's tiles are handed out first, 0 = last
-// (measured on the E4M3 workload with its bf16 shared expert: last is 0.3%
-// faster, 3 of 3 pairs on one box).
-#ifndef MOE_PAIR_BF16_FIRST
-#define MOE_PAIR_BF16_FIRST 0
-#endif
-// E4M3 tiled path: 1 = LDS-DMA ping-pong kernel, 0 = register-staged kernel.
-#ifndef MOE_GMM_FP8
-#define MOE_GMM_FP8 1
-#endif
-// bf16 tiled path: 1 = LDS-DMA ping-pong kernel, 0 = register-staged kernel.
-#ifndef MOE_GMM_BF16
-#define MOE_GMM_BF16 1
-#endif
-// Row tiles per group in the tile order of the bf16 and E4M3 ping-pong kernels
-// (measured: 8 for the 256 x 256 bf16 tiles; 4 for the 256 x 128 E4M3 tiles,
-// where the ~32 tiles an XCD runs at once then span 4 row x 8 column tiles,
-// the split that re-reads the fewest panel bytes).
-#ifndef MOE_PP_GM
-#define MOE_PP_GM 8
-#endif
-#ifndef MOE_PP8_GM
-#define MOE_PP8_GM 4
-#endif
-// Tile / waves along columns / LDS ring slots of the bf16 ping-pong kernel.
-#ifndef MOE_PP_BM
-#define MOE_PP_BM 256
-#define MOE_PP_BN 256
-#define MOE_PP_WN 4
-#define MOE_PP_STAGES 4
-#endif
-// 1: the streaming kernel's blocks share their activation rows through LDS
-// (32 or more rows per block, N a multiple of 256).
-#ifndef MOE_STREAM_XS
-#define MOE_STREAM_XS 1
-#endif
-// Wave layout of the 256 x 256 tiled kernel (waves along rows x columns).
-#ifndef MOE_TILED_WAVES_M
-#define MOE_TILED_WAVES_M 2
-#define MOE_TILED_WAVES_N 4
-#endif
-
 namespace moe {
 namespace {
+
+// Launch-shape constants (each the measured best of the alternatives named).
+// Row tiles per group in the tile order of the bf16 and E4M3 ping-pong
+// kernels: 8 for the 256 x 256 bf16 tiles; 4 for the 256 x 128 E4M3 tiles,
+// where the ~32 tiles an XCD runs at once then span 4 row x 8 column tiles,
+// the split that re-reads the fewest panel bytes.
+constexpr int kPpGroup = 8;
+constexpr int kPp8Group = 4;
+// Pair launch: the E4M3 group's tiles are handed out first, the bf16 group's
+// last (on the E4M3 workload with its bf16 shared expert: 0.3% faster than
+// the other order, 3 of 3 pairs on one box).
+constexpr bool kPairBf16First = false;
+// Wave layout of the 256 x 256 register-staged tiled kernel (waves along
+// rows x columns).
+constexpr int kTiledWavesM = 2, kTiledWavesN = 4;
+
 
 // ------------------------------------------------------------------ helpers
 
@@ -749,6 +719,8 @@ struct PpCfg {
   static_assert(STAGES >= 3 && (STAGES - 2) * (kPerStage + 1) <= 63, "ring depth");
   static_assert(kLds >= 2 * 257 * 4, "tile prefix lives in the ring");
 };
+// The bf16 configuration: 256 x 256 tiles, 2 x 4 waves, a 4-slot ring.
+typedef PpCfg<256, 256, 2, 4, 4> PpBf16;
 
 // The kernel's work for block p (smem: the dynamic LDS ring; s_last: an LDS
 // flag of the block).
@@ -770,7 +742,7 @@ __device__ __forceinline__ void pp_block(
   const int nsteps_all = (hin_b + kDmaKB - 1) / kDmaKB;
   Tile tile;
   Work wk;
-  if (!pick_work<C::kBM, C::kBN, MOE_PP_GM, C::kFold>(reinterpret_cast<const int*>(smem),
+  if (!pick_work<C::kBM, C::kBN, kPpGroup, C::kFold>(reinterpret_cast<const int*>(smem),
                                                        reinterpret_cast<const int*>(smem) + 257, e, N,
                                                        nsteps_all, ncu, split_ws != nullptr, p, tile, wk))
     return;
@@ -1176,7 +1148,7 @@ __device__ __forceinline__ void pp8_block(
     load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_off + 257);
   }
   Tile tile;
-  if (!pick_tile<C::kBM, C::kBN, MOE_PP8_GM>(reinterpret_cast<const int*>(smem),
+  if (!pick_tile<C::kBM, C::kBN, kPp8Group>(reinterpret_cast<const int*>(smem),
                                      reinterpret_cast<const int*>(smem) + 257, e, N, p, tile))
     return;
   __syncthreads();  // every lane has its tile before the ring overwrites the prefix
@@ -1490,7 +1462,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 // Two grouped GEMMs in one launch: a bf16 one on the ping-pong kernel's
 // 256 x 256 tiles and an E4M3 one on the E4M3 kernel's 256 x 128 tiles,
 // each block running exactly what its own kernel runs for that tile. The
-// first nb0 blocks serve the group handed out first (MOE_PAIR_BF16_FIRST
+// first nb0 blocks serve the group handed out first (kPairBf16First
 // says which), the rest the other; nb0 is a multiple of 8, so both keep
 // their XCD-aware tile order. The bf16 GEMM is never split along K here.
 struct GroupArgs {
@@ -1516,7 +1488,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int p = blockIdx.x;
   const bool first = p < nb0;
   const int q = first ? p : p - nb0;
-  if (first == (MOE_PAIR_BF16_FIRST != 0))
+  if (first == kPairBf16First)
     pp_block<C>(smem, s_last, q, b.a, b.w, b.a_scale, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.relu, b.out,
                 nullptr, nullptr, 1, b.gx);  // no split workspace: ncu is not used
   else
@@ -1962,7 +1934,7 @@ moe_status launch_stream(const void* a, const float* as, const void* w, const fl
                          hipStream_t s, RowMap gx) {
   const int64_t tasks = (int64_t)e * cdiv(N, 64);
   const dim3 grid((unsigned)cdiv64(tasks, 4));
-  if constexpr (AL && MB >= 2 && MOE_STREAM_XS) {
+  if constexpr (AL && MB >= 2) {
     // a block's 4 waves share one expert's rows when the 64-column groups
     // come in fours (N a multiple of 256)
     if (N % 256 == 0) {
@@ -2005,17 +1977,13 @@ GmmPath gmm_path(moe_dtype in_dt, int e, int A, int Hin, int N) {
   // buffer-load path: 16-byte aligned rows and each expert's weight matrix under 2 GiB
   const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0) &&
                   ((int64_t)Hin * N * elem < (1ll << 31));
-#if MOE_GMM_BF16 == 1
   if (elem == 2 && al && N % 16 == 0) return GmmPath::PP;
-#endif
-#if MOE_GMM_FP8 == 1
   if (elem == 1 && al && N % 16 == 0) return GmmPath::PP8;
-#endif
   return GmmPath::TILED;
 }
 
 size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N) {
-  if (!MOE_GMM_SPLIT || A == 0 || gmm_path(in_dt, e, A, Hin, N) != GmmPath::PP) return 0;
+  if (A == 0 || gmm_path(in_dt, e, A, Hin, N) != GmmPath::PP) return 0;
   const int ncu = device_cus();
   return split_ws_floats(ncu) * sizeof(float) + (size_t)ncu * sizeof(int);
 }
@@ -2046,17 +2014,11 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
   // buffer-load path: 16-byte aligned rows and each expert's weight matrix under 2 GiB
   const bool al = ((int64_t)Hin * elem % 16 == 0) && ((int64_t)N * elem % 16 == 0) &&
                   ((int64_t)Hin * N * elem < (1ll << 31));
-  constexpr int WM = MOE_TILED_WAVES_M, WN = MOE_TILED_WAVES_N;
-#if MOE_GMM_BF16 == 1
-  if (elem == 2 && al && N % 16 == 0) {
-    typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
-    return launch_pp<CP>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s, gx);
-  }
-#endif
-#if MOE_GMM_FP8 == 1
+  constexpr int WM = kTiledWavesM, WN = kTiledWavesN;
+  if (elem == 2 && al && N % 16 == 0)
+    return launch_pp<PpBf16>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s, gx);
   if (elem == 1 && al && N % 16 == 0)
     return launch_pp8<false>(a, a_scale, w, w_scale, nullptr, nullptr, offsets, e, A, Hin, N, relu, out, s, gx);
-#endif
   if (elem == 2) {
     typedef TiledCfg<2, 256, 256, WM, WN, true, false> CA;
     typedef TiledCfg<2, 256, 256, WM, WN, false, false> CU;
@@ -2083,7 +2045,7 @@ moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void
 
 template <bool MX, bool FP4>
 moe_status launch_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
-  typedef PpCfg<MOE_PP_BM, MOE_PP_BN, 2, MOE_PP_WN, MOE_PP_STAGES> CP;
+  typedef PpBf16 CP;
   typedef Pp8Cfg<MX, FP4> C8;
   constexpr int kLds = CP::kLds > C8::kLds ? CP::kLds : C8::kLds;
   static bool attr_done = false;
@@ -2101,7 +2063,7 @@ moe_status launch_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
   const GroupArgs ga_f{(const unsigned char*)f.a, (const unsigned char*)f.w, f.a_scale, f.w_scale, f.a_mx,
                        f.w_mx, f.offsets, f.e, f.A, f.Hin, f.N, f.act == MOE_ACT_RELU, (bf16_t*)f.out, f.gx};
   hipLaunchKernelGGL((gmm_pair_kernel<CP, MX, FP4>), dim3((unsigned)(nb_b + nb_f)), dim3(512), kLds, s, ga_b,
-                     ga_f, (int)(MOE_PAIR_BF16_FIRST ? nb_b : nb_f));
+                     ga_f, (int)(kPairBf16First ? nb_b : nb_f));
   return launch_status();
 }
 
