@@ -1459,9 +1459,273 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   pp8_block<MX, FP4>(smem, blockIdx.x, a, w, a_scale, w_scale, a_mx, w_mx, offsets, e, A, Hin, N, relu, out, gx);
 }
 
+// ------------------------------------------------------------------ wide ping-pong E4M3 kernel
+//
+// E4M3 with per-tensor or per-row scales (no block scales) on 256 x 256
+// tiles: the bf16 ping-pong kernel's ring geometry with E4M3 operands. A
+// slot holds a 64-deep K slice, activations 256 rows x 64 B and weights 64
+// K rows x 256 B (32 KB; four slots), so a slice brings 32 KB for 2048
+// MFMA cycles per SIMD pair, the same bytes per MFMA cycle as the bf16
+// kernel; the 256 x 128 E4M3 kernel needs half as many MFMA cycles per byte
+// fetched. 8 waves of 128 x 64 on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+// scales): waves 0-3 hold rows 0-127, waves 4-7 rows 128-255, the two
+// halves alternating multiply and memory phases as in gmm_pp_kernel.
+// MFMA operands: the weights are the row operand (row i = output column),
+// the activations the column operand (column j = tile row). Lane l holds
+// row / column l % 32 and K values 32 (l / 32) .. +31 in order: activation
+// fragments are two 16-byte LDS reads, weight fragments four transposing
+// reads (ds_read_b64_tr_b8, each 8 K rows of 16 columns per 16 lanes).
+// Accumulator register r of lane l is output column 8 (r / 4) + 4 (l / 32)
+// + r % 4 of the 32 x 32 block, tile row l % 32.
+// LDS layout: activation row m keeps its four 16-byte chunks at positions
+// c ^ ((m / 4) % 4), so 16 consecutive rows cover all banks; weight K row k
+// keeps its sixteen 16-column chunks at c ^ (2 (k % 8)), so the 8 rows x 2
+// chunks of a transposing read by 32 lanes fall in distinct banks.
+struct Pp8wCfg {
+  static constexpr int kBM = 256, kBN = 256, kStages = 4, kNT = 512;
+  static constexpr int kKB = 64;                 // K bytes (E4M3 values) per slot
+  static constexpr int kLdsA = kBM * kKB;        // 16 KB
+  static constexpr int kLdsW = kKB * kBN;        // 16 KB
+  static constexpr int kStage = kLdsA + kLdsW;
+  static constexpr int kLds = kStages * kStage;  // 128 KB
+  static constexpr int kADma = kLdsA / 1024 / 8;  // 1 KB DMA ops per wave per slot
+  static constexpr int kWDma = kLdsW / 1024 / 8;
+  static constexpr int kPerStage = kADma + kWDma;
+  static_assert(kLds >= 2 * 257 * 4, "tile prefix lives in the ring");
+};
+__device__ __forceinline__ int pp8w_xpos(int m, int c) { return c ^ ((m >> 2) & 3); }
+__device__ __forceinline__ int pp8w_wpos(int k, int c) { return c ^ (2 * (k & 7)); }
+
+__device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const unsigned char* __restrict__ a,
+                                           const unsigned char* __restrict__ w, const float* __restrict__ a_scale,
+                                           const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
+                                           int e, int A, int Hin, int N, int relu, bf16_t* __restrict__ out,
+                                           const RowMap& gx) {
+  typedef Pp8wCfg C;
+  {
+    int* s_off = reinterpret_cast<int*>(smem);
+    load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_off + 257);
+  }
+  Tile tile;
+  if (!pick_tile<C::kBM, C::kBN, kPpGroup>(reinterpret_cast<const int*>(smem),
+                                           reinterpret_cast<const int*>(smem) + 257, e, N, p, tile))
+    return;
+  __syncthreads();  // every lane has its tile before the ring overwrites the prefix
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int rowb = Hin;  // bytes per activation row = weight K rows
+  const int nsteps = (rowb + C::kKB - 1) / C::kKB;
+  const bool gat = gx.src != nullptr;
+  const u32x4_t asrd = make_srd(a + (gat ? 0 : (int64_t)tile.row0 * rowb),
+                                (uint32_t)(gat ? gx.rows : tile.rows) * (uint32_t)rowb);
+  const u32x4_t wsrd = make_srd(w + (int64_t)tile.ex * rowb * N, (uint32_t)rowb * (uint32_t)N);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  // ---- DMA: which global bytes this lane fetches for each KB of a slot it fills
+  uint32_t a_voff[C::kADma], a_kc[C::kADma];
+#pragma unroll
+  for (int q = 0; q < C::kADma; ++q) {
+    const int kb = (wave * C::kADma + q) * 1024 + lane * 16;  // byte within the slot's activations
+    const int row = kb >> 6, lc = pp8w_xpos(row, (kb >> 4) & 3);
+    const int src = row >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + row) : row;
+    a_voff[q] = (src >= 0 ? (uint32_t)src * (uint32_t)rowb : kOOB) + lc * 16;
+    a_kc[q] = lc * 16;
+  }
+  uint32_t w_voff[C::kWDma];
+#pragma unroll
+  for (int q = 0; q < C::kWDma; ++q) {
+    const int kb = (wave * C::kWDma + q) * 1024 + lane * 16;  // byte within the slot's weights
+    const int k = kb >> 8, lc = pp8w_wpos(k, (kb >> 4) & 15);
+    const int nb = tile.n0 + lc * 16;
+    w_voff[q] = (uint32_t)k * (uint32_t)N + (uint32_t)nb + (nb < N ? 0u : kOOB);
+  }
+  // Past-the-end slices are issued too (out-of-range loads write zeros); K
+  // rows past Hin lie past the weight descriptor's end.
+  auto issue = [&](int step) {
+    const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
+    const int kb0 = step * C::kKB;
+#pragma unroll
+    for (int q = 0; q < C::kADma; ++q)
+      dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < rowb ? 0u : kOOB), base + (wave * C::kADma + q) * 1024);
+    const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : kOOB;
+#pragma unroll
+    for (int q = 0; q < C::kWDma; ++q)
+      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
+  };
+  auto bar = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int S = C::kStages;
+  constexpr int kInFlight = (S - 2) * C::kPerStage;
+
+  const bool wave_active = (wm * 128 < tile.rows) && (tile.n0 + wn * 64 < N);
+  const int l32 = lane & 31, g = lane >> 5;
+  // output map and per-row scales of this lane's four tile rows, fetched now
+  int dpre[4] = {0, 0, 0, 0};
+  float rpre[4] = {1.f, 1.f, 1.f, 1.f};
+  if (wave_active) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ml = wm * 128 + 32 * i + l32;
+      if (gx.dst != nullptr) dpre[i] = ml < tile.rows ? gx.dst[tile.row0 + ml] : -1;
+      if (gx.row_scale != nullptr) rpre[i] = ml < tile.rows ? row_scale_of(gx, tile.row0 + ml) : 0.f;
+    }
+  }
+  // activation fragment i: tile row wm*128 + 32i + l32, K chunks 2g and 2g+1
+  int xoff[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = wm * 128 + 32 * i + l32;
+      xoff[i][h] = m * C::kKB + (pp8w_xpos(m, 2 * g + h) << 4);
+    }
+  // weight fragment j (columns wn*64 + 32j .. +31): in each 16-lane group,
+  // lanes 2b, 2b+1 name the halves of K row 32g + 8t + b of the group's 16
+  // columns (t = 0..3 for the four reads)
+  const int s16 = lane & 15, grp = lane >> 4;
+  const int wk0 = 32 * g + (s16 >> 1);  // K row of read t = 0 (k % 8 = s16 / 2 for every t)
+  int woff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    woff[j] = C::kLdsA + wk0 * C::kBN + (pp8w_wpos(wk0, 4 * wn + 2 * j + (grp & 1)) << 4) + 8 * (s16 & 1);
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  i32x8_t xa[4], wf[2];
+  auto read_frags = [&](int slice) {
+    const unsigned char* st = smem + (slice % S) * C::kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(st + xoff[i][0]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(st + xoff[i][1]);
+      xa[i] = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(st + woff[j] + t * 8 * C::kBN));
+        wf[j][2 * t] = v.x;
+        wf[j][2 * t + 1] = v.y;
+      }
+  };
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto multiply = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
+
+  // The schedule: gmm_pp_kernel's, without a tail fragment.
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue(t);
+  wait_vmcnt<kInFlight>();
+  bar();  // barrier 0: slice 0 has landed
+  if (wm == 0) {
+    if (wave_active) {
+      read_frags(0);
+      issue(S - 1);
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        multiply();
+        wait_vmcnt<kInFlight>();
+        bar();
+        read_frags(s + 1);
+        issue(s + S);
+        bar();
+      }
+    } else {
+      issue(S - 1);
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        wait_vmcnt<kInFlight>();
+        bar();
+        issue(s + S);
+        bar();
+      }
+    }
+    bar();  // matches the second half's last barrier
+  } else {
+    bar();
+    issue(S - 1);
+    if (wave_active) {
+      read_frags(0);
+      wait_vmcnt<kInFlight>();
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        multiply();
+        bar();
+        read_frags(s + 1);
+        issue(s + S);
+        wait_vmcnt<kInFlight>();
+        bar();
+      }
+    } else {
+      wait_vmcnt<kInFlight>();
+      bar();
+      for (int s = 0; s < nsteps; ++s) {
+        bar();
+        issue(s + S);
+        wait_vmcnt<kInFlight>();
+        bar();
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
+  if (!wave_active) return;
+
+  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ml = wm * 128 + 32 * i + l32;
+    if (ml >= tile.rows) continue;
+    const OutRow orow = out_row_of(gx, tile.row0 + ml, dpre[i], A);
+    if (orow.row < 0) continue;
+    const float rsc = gx.row_scale != nullptr ? rpre[i] * sc : sc;
+    bf16_t* orow_p = out + orow.row * N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // registers 4q .. 4q+3: output columns 8q + 4g .. +3 of the block
+        const int nb = tile.n0 + wn * 64 + 32 * j + 8 * q + 4 * g;
+        if (nb >= N) continue;  // N is a multiple of 16 here
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t = acc[i][j][4 * q + r] * rsc;
+          v[r] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
+        }
+        *reinterpret_cast<uint2*>(orow_p + nb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+  }
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gmm_pp8w_kernel(
+    const unsigned char* __restrict__ a, const unsigned char* __restrict__ w, const float* __restrict__ a_scale,
+    const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int e, int A, int Hin, int N, int relu,
+    bf16_t* __restrict__ out, RowMap gx) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  pp8w_block(smem, blockIdx.x, a, w, a_scale, w_scale, offsets, e, A, Hin, N, relu, out, gx);
+}
+
 // Two grouped GEMMs in one launch: a bf16 one on the ping-pong kernel's
-// 256 x 256 tiles and an E4M3 one on the E4M3 kernel's 256 x 128 tiles,
-// each block running exactly what its own kernel runs for that tile. The
+// 256 x 256 tiles and an E4M3 one on the wide E4M3 kernel's 256 x 256 tiles
+// (with MX block scales: the E4M3 kernel's 256 x 128 tiles), each block
+// running exactly what its own kernel runs for that tile. The
 // first nb0 blocks serve the group handed out first (kPairBf16First
 // says which), the rest the other; nb0 is a multiple of 8, so both keep
 // their XCD-aware tile order. The bf16 GEMM is never split along K here.
@@ -1491,9 +1755,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   if (first == kPairBf16First)
     pp_block<C>(smem, s_last, q, b.a, b.w, b.a_scale, b.w_scale, b.offsets, b.e, b.A, b.Hin, b.N, b.relu, b.out,
                 nullptr, nullptr, 1, b.gx);  // no split workspace: ncu is not used
-  else
+  else if constexpr (MX)
     pp8_block<MX, FP4>(smem, q, f.a, f.w, f.a_scale, f.w_scale, f.a_mx, f.w_mx, f.offsets, f.e,
                             f.A, f.Hin, f.N, f.relu, f.out, f.gx);
+  else
+    pp8w_block(smem, q, f.a, f.w, f.a_scale, f.w_scale, f.offsets, f.e, f.A, f.Hin, f.N, f.relu, f.out, f.gx);
 }
 
 // ------------------------------------------------------------------ streaming kernel (decode)
@@ -1928,6 +2194,24 @@ moe_status launch_pp8(const void* a, const float* as, const void* w, const float
   return launch_status();
 }
 
+moe_status launch_pp8w(const void* a, const float* as, const void* w, const float* ws, const int32_t* offsets,
+                       int e, int A, int Hin, int N, int relu, void* out, hipStream_t s, RowMap gx) {
+  typedef Pp8wCfg C;
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gmm_pp8w_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    attr_done = true;
+  }
+  const int64_t mt_max = cdiv64(A, C::kBM) + (e < A ? e : A);
+  const int64_t blocks = mt_max * cdiv64(N, C::kBN);
+  const int64_t grid = cdiv64(blocks, 8) * 8;
+  if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(gmm_pp8w_kernel, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s, (const unsigned char*)a,
+                     (const unsigned char*)w, as, ws, offsets, e, A, Hin, N, relu, (bf16_t*)out, gx);
+  return launch_status();
+}
+
 template <int MB, bool AL>
 moe_status launch_stream(const void* a, const float* as, const void* w, const float* ws,
                          const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
@@ -2018,7 +2302,7 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
   if (elem == 2 && al && N % 16 == 0)
     return launch_pp<PpBf16>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s, gx);
   if (elem == 1 && al && N % 16 == 0)
-    return launch_pp8<false>(a, a_scale, w, w_scale, nullptr, nullptr, offsets, e, A, Hin, N, relu, out, s, gx);
+    return launch_pp8w(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
   if (elem == 2) {
     typedef TiledCfg<2, 256, 256, WM, WN, true, false> CA;
     typedef TiledCfg<2, 256, 256, WM, WN, false, false> CU;
@@ -2046,7 +2330,7 @@ moe_status launch_gmm_mx(const void* a, const unsigned char* a_scale, const void
 template <bool MX, bool FP4>
 moe_status launch_pair(const GmmCall& f, const GmmCall& b, hipStream_t s) {
   typedef PpBf16 CP;
-  typedef Pp8Cfg<MX, FP4> C8;
+  typedef typename std::conditional<MX, Pp8Cfg<MX, FP4>, Pp8wCfg>::type C8;
   constexpr int kLds = CP::kLds > C8::kLds ? CP::kLds : C8::kLds;
   static bool attr_done = false;
   if (!attr_done) {

@@ -234,7 +234,10 @@ GMM_CASES = [
     ("bf16_stream_shared_x_64rows", [30, 0, 45, 21, 33, 17], 264, 256, "bf16"),
     ("fp8_tiled", [200, 0, 333], 256, 384, "fp8"),
     ("fp8_tiled_unaligned", [100, 77], 200, 100, "fp8"),
-    ("fp8_ragged_k_and_n", [130, 5, 0, 260], 208, 400, "fp8"),  # last K slice 80 deep, 16-column tile
+    ("fp8_ragged_k_and_n", [130, 5, 0, 260], 208, 400, "fp8"),  # last K slice 16 deep, 144-column tile
+    # 256 x 256 E4M3 tiles: three row tiles of one expert, a 1-row expert, 5 K slices
+    ("fp8_wide_tiles", [600, 0, 1, 257], 320, 512, "fp8"),
+    ("fp8_wide_16_column_tail", [300, 45], 128, 272, "fp8"),
     ("f32_tiny", [20, 0, 17, 40, 1, 30, 12, 8], 128, 256, "f32"),
     ("f32_ragged", [70, 5], 33, 45, "f32"),
 ]
