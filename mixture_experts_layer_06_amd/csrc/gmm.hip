@@ -1481,17 +1481,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 // c ^ ((m / 4) % 4), so 16 consecutive rows cover all banks; weight K row k
 // keeps its sixteen 16-column chunks at c ^ (2 (k % 8)), so the 8 rows x 2
 // chunks of a transposing read by 32 lanes fall in distinct banks.
+// Epilogue: the accumulators (4 columns per lane and register group) go to
+// an LDS copy of the bf16 output tile (rows padded to 528 bytes), which is
+// then written out a whole 512-byte row per 32 lanes.
+// An expert's last row piece of at most 32 rows rides on the tile before it
+// (as in gmm_pp_kernel): then each row half multiplies one more 32 x 32
+// block whose column j is tail row 16 * half + j % 16 (lanes j and j + 16
+// read the same row; only the first is stored).
 struct Pp8wCfg {
   static constexpr int kBM = 256, kBN = 256, kStages = 4, kNT = 512;
+  static constexpr int kFold = 32;               // tail rows an expert's last tile may carry beyond BM
   static constexpr int kKB = 64;                 // K bytes (E4M3 values) per slot
   static constexpr int kLdsA = kBM * kKB;        // 16 KB
+  static constexpr int kLdsX = (kBM + kFold) * kKB;  // ... with the folded tail rows
   static constexpr int kLdsW = kKB * kBN;        // 16 KB
-  static constexpr int kStage = kLdsA + kLdsW;
-  static constexpr int kLds = kStages * kStage;  // 128 KB
+  static constexpr int kStage = kLdsX + kLdsW;
+  static constexpr int kDummy = kStages * kStage;  // 1 KB that soaks up unused tail DMA
+  static constexpr int kRing = kDummy + 1024;      // 137 KB
+  static constexpr int kOutRow = kBN * 2 + 16;     // bytes per row of the staged output tile
+  static constexpr int kOut = (kBM + kFold) * kOutRow;
+  static constexpr int kLds = kRing > kOut ? kRing : kOut;  // 148.5 KB
   static constexpr int kADma = kLdsA / 1024 / 8;  // 1 KB DMA ops per wave per slot
   static constexpr int kWDma = kLdsW / 1024 / 8;
   static constexpr int kPerStage = kADma + kWDma;
   static_assert(kLds >= 2 * 257 * 4, "tile prefix lives in the ring");
+  static_assert(kFold * kKB == 2 * 1024, "waves 0 and 1 fetch the tail rows");
 };
 __device__ __forceinline__ int pp8w_xpos(int m, int c) { return c ^ ((m >> 2) & 3); }
 __device__ __forceinline__ int pp8w_wpos(int k, int c) { return c ^ (2 * (k & 7)); }
@@ -1504,13 +1518,14 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
   typedef Pp8wCfg C;
   {
     int* s_off = reinterpret_cast<int*>(smem);
-    load_tile_prefix<C::kBM>(offsets, e, A, s_off, s_off + 257);
+    load_tile_prefix<C::kBM, C::kFold>(offsets, e, A, s_off, s_off + 257);
   }
   Tile tile;
-  if (!pick_tile<C::kBM, C::kBN, kPpGroup>(reinterpret_cast<const int*>(smem),
-                                           reinterpret_cast<const int*>(smem) + 257, e, N, p, tile))
+  if (!pick_tile<C::kBM, C::kBN, kPpGroup, C::kFold>(reinterpret_cast<const int*>(smem),
+                                                     reinterpret_cast<const int*>(smem) + 257, e, N, p, tile))
     return;
   __syncthreads();  // every lane has its tile before the ring overwrites the prefix
+  const bool extra = tile.rows > C::kBM;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1525,15 +1540,21 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // ---- DMA: which global bytes this lane fetches for each KB of a slot it fills
-  uint32_t a_voff[C::kADma], a_kc[C::kADma];
-#pragma unroll
-  for (int q = 0; q < C::kADma; ++q) {
-    const int kb = (wave * C::kADma + q) * 1024 + lane * 16;  // byte within the slot's activations
+  auto x_src = [&](int kb, uint32_t& voff, uint32_t& kc) {  // kb: byte within the slot's activations
     const int row = kb >> 6, lc = pp8w_xpos(row, (kb >> 4) & 3);
     const int src = row >= tile.rows ? -1 : gat ? gather_src(gx, tile.row0 + row) : row;
-    a_voff[q] = (src >= 0 ? (uint32_t)src * (uint32_t)rowb : kOOB) + lc * 16;
-    a_kc[q] = lc * 16;
-  }
+    voff = (src >= 0 ? (uint32_t)src * (uint32_t)rowb : kOOB) + lc * 16;
+    kc = lc * 16;
+  };
+  uint32_t a_voff[C::kADma + 1], a_kc[C::kADma + 1];
+#pragma unroll
+  for (int q = 0; q < C::kADma; ++q) x_src((wave * C::kADma + q) * 1024 + lane * 16, a_voff[q], a_kc[q]);
+  // tail rows: waves 0 and 1 fetch rows BM..BM+15 and BM+16..BM+31; the
+  // other waves issue an out-of-range op into the dummy KB, so every wave
+  // counts the same number of ops per slice
+  const bool tail_dma = wave < C::kFold * C::kKB / 1024;
+  x_src(C::kLdsA + wave * 1024 + lane * 16, a_voff[C::kADma], a_kc[C::kADma]);
+  if (!tail_dma) a_voff[C::kADma] = kOOB;
   uint32_t w_voff[C::kWDma];
 #pragma unroll
   for (int q = 0; q < C::kWDma; ++q) {
@@ -1544,16 +1565,19 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
   }
   // Past-the-end slices are issued too (out-of-range loads write zeros); K
   // rows past Hin lie past the weight descriptor's end.
-  auto issue = [&](int step) {
+  auto issue = [&](int step, auto ex) {
     const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
     const int kb0 = step * C::kKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
       dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < rowb ? 0u : kOOB), base + (wave * C::kADma + q) * 1024);
+    if (decltype(ex)::value)
+      dma16(asrd, (a_voff[C::kADma] + kb0) | (kb0 + (int)a_kc[C::kADma] < rowb ? 0u : kOOB),
+            tail_dma ? base + C::kLdsA + wave * 1024 : lds0 + C::kDummy);
     const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
-      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsA + (wave * C::kWDma + q) * 1024);
+      dma16(wsrd, w_voff[q] + kstep, base + C::kLdsX + (wave * C::kWDma + q) * 1024);
   };
   auto bar = [] {
     __builtin_amdgcn_sched_barrier(0);
@@ -1561,30 +1585,21 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
     __builtin_amdgcn_sched_barrier(0);
   };
   constexpr int S = C::kStages;
-  constexpr int kInFlight = (S - 2) * C::kPerStage;
 
   const bool wave_active = (wm * 128 < tile.rows) && (tile.n0 + wn * 64 < N);
   const int l32 = lane & 31, g = lane >> 5;
   // output map and per-row scales of this lane's four tile rows, fetched now
-  int dpre[4] = {0, 0, 0, 0};
-  float rpre[4] = {1.f, 1.f, 1.f, 1.f};
-  if (wave_active) {
+  // tile row of block i's column l32 (block 4: this half's tail rows)
+  auto blk_row = [&](int i) { return i < 4 ? wm * 128 + 32 * i + l32 : C::kBM + 16 * wm + (l32 & 15); };
+  // activation fragment i: row blk_row(i), K chunks 2g and 2g+1; the chunk
+  // positions depend on the row only through l32 % 16 / 4, the same for
+  // every block, so blocks 1-3 are block 0 plus 32i rows
+  int xoff0[2], xofft[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ml = wm * 128 + 32 * i + l32;
-      if (gx.dst != nullptr) dpre[i] = ml < tile.rows ? gx.dst[tile.row0 + ml] : -1;
-      if (gx.row_scale != nullptr) rpre[i] = ml < tile.rows ? row_scale_of(gx, tile.row0 + ml) : 0.f;
-    }
+  for (int h = 0; h < 2; ++h) {
+    xoff0[h] = blk_row(0) * C::kKB + (pp8w_xpos(blk_row(0), 2 * g + h) << 4);
+    xofft[h] = blk_row(4) * C::kKB + (pp8w_xpos(blk_row(4), 2 * g + h) << 4);
   }
-  // activation fragment i: tile row wm*128 + 32i + l32, K chunks 2g and 2g+1
-  int xoff[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int m = wm * 128 + 32 * i + l32;
-      xoff[i][h] = m * C::kKB + (pp8w_xpos(m, 2 * g + h) << 4);
-    }
   // weight fragment j (columns wn*64 + 32j .. +31): in each 16-lane group,
   // lanes 2b, 2b+1 name the halves of K row 32g + 8t + b of the group's 16
   // columns (t = 0..3 for the four reads)
@@ -1593,15 +1608,18 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
   int woff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    woff[j] = C::kLdsA + wk0 * C::kBN + (pp8w_wpos(wk0, 4 * wn + 2 * j + (grp & 1)) << 4) + 8 * (s16 & 1);
+    woff[j] = C::kLdsX + wk0 * C::kBN + (pp8w_wpos(wk0, 4 * wn + 2 * j + (grp & 1)) << 4) + 8 * (s16 & 1);
   typedef int i32x2_t __attribute__((ext_vector_type(2)));
-  i32x8_t xa[4], wf[2];
-  auto read_frags = [&](int slice) {
+  i32x8_t xa[5], wf[2];
+  auto read_frags = [&](int slice, auto ex) {
     const unsigned char* st = smem + (slice % S) * C::kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(st + xoff[i][0]);
-      const uint4 hi = *reinterpret_cast<const uint4*>(st + xoff[i][1]);
+    for (int i = 0; i < 5; ++i) {
+      if (i == 4 && !decltype(ex)::value) continue;
+      const int o0 = i < 4 ? xoff0[0] + i * 32 * C::kKB : xofft[0];
+      const int o1 = i < 4 ? xoff0[1] + i * 32 * C::kKB : xofft[1];
+      const uint4 lo = *reinterpret_cast<const uint4*>(st + o0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(st + o1);
       xa[i] = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
@@ -1614,103 +1632,139 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
         wf[j][2 * t + 1] = v.y;
       }
   };
-  f32x16_t acc[4][2];
+  f32x16_t acc[5][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 5; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto multiply = [&]() {
+  auto multiply = [&](auto ex) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 5; ++i) {
+      if (i == 4 && !decltype(ex)::value) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xa[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
   };
 
-  // The schedule: gmm_pp_kernel's, without a tail fragment.
+  // The schedule: gmm_pp_kernel's; `ex` (compile time) adds the tail block
+  // and its DMA op.
+  auto run = [&](auto ex) {
+    constexpr int kInFlight = (S - 2) * (C::kPerStage + (decltype(ex)::value ? 1 : 0));
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t);
-  wait_vmcnt<kInFlight>();
-  bar();  // barrier 0: slice 0 has landed
-  if (wm == 0) {
-    if (wave_active) {
-      read_frags(0);
-      issue(S - 1);
-      bar();
-      for (int s = 0; s < nsteps; ++s) {
-        multiply();
-        wait_vmcnt<kInFlight>();
+    for (int t = 0; t < S - 1; ++t) issue(t, ex);
+    wait_vmcnt<kInFlight>();
+    bar();  // barrier 0: slice 0 has landed
+    if (wm == 0) {
+      if (wave_active) {
+        read_frags(0, ex);
+        issue(S - 1, ex);
         bar();
-        read_frags(s + 1);
-        issue(s + S);
+        for (int s = 0; s < nsteps; ++s) {
+          multiply(ex);
+          wait_vmcnt<kInFlight>();
+          bar();
+          read_frags(s + 1, ex);
+          issue(s + S, ex);
+          bar();
+        }
+      } else {
+        issue(S - 1, ex);
         bar();
+        for (int s = 0; s < nsteps; ++s) {
+          wait_vmcnt<kInFlight>();
+          bar();
+          issue(s + S, ex);
+          bar();
+        }
       }
+      bar();  // matches the second half's last barrier
     } else {
-      issue(S - 1);
       bar();
-      for (int s = 0; s < nsteps; ++s) {
+      issue(S - 1, ex);
+      if (wave_active) {
+        read_frags(0, ex);
         wait_vmcnt<kInFlight>();
         bar();
-        issue(s + S);
+        for (int s = 0; s < nsteps; ++s) {
+          multiply(ex);
+          bar();
+          read_frags(s + 1, ex);
+          issue(s + S, ex);
+          wait_vmcnt<kInFlight>();
+          bar();
+        }
+      } else {
+        wait_vmcnt<kInFlight>();
         bar();
+        for (int s = 0; s < nsteps; ++s) {
+          bar();
+          issue(s + S, ex);
+          wait_vmcnt<kInFlight>();
+          bar();
+        }
       }
     }
-    bar();  // matches the second half's last barrier
-  } else {
-    bar();
-    issue(S - 1);
-    if (wave_active) {
-      read_frags(0);
-      wait_vmcnt<kInFlight>();
-      bar();
-      for (int s = 0; s < nsteps; ++s) {
-        multiply();
-        bar();
-        read_frags(s + 1);
-        issue(s + S);
-        wait_vmcnt<kInFlight>();
-        bar();
-      }
-    } else {
-      wait_vmcnt<kInFlight>();
-      bar();
-      for (int s = 0; s < nsteps; ++s) {
-        bar();
-        issue(s + S);
-        wait_vmcnt<kInFlight>();
-        bar();
-      }
+  };
+  if (extra) run(std::true_type{});
+  else run(std::false_type{});
+  // output map and per-row scales of this lane's rows, fetched while the
+  // past-the-end DMA drains
+  int dpre[5] = {0, 0, 0, 0, 0};
+  float rpre[5] = {1.f, 1.f, 1.f, 1.f, 1.f};
+  if (wave_active) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int ml = blk_row(i);
+      if (gx.dst != nullptr) dpre[i] = ml < tile.rows ? gx.dst[tile.row0 + ml] : -1;
+      if (gx.row_scale != nullptr) rpre[i] = ml < tile.rows ? row_scale_of(gx, tile.row0 + ml) : 0.f;
     }
   }
   wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
-  if (!wave_active) return;
+  __syncthreads();  // every wave is done with the ring
 
-  const float sc = ld_scale(a_scale) * ld_scale(w_scale);
+  if (wave_active) {
+    const float sc = ld_scale(a_scale) * ld_scale(w_scale);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ml = wm * 128 + 32 * i + l32;
-    if (ml >= tile.rows) continue;
-    const OutRow orow = out_row_of(gx, tile.row0 + ml, dpre[i], A);
-    if (orow.row < 0) continue;
-    const float rsc = gx.row_scale != nullptr ? rpre[i] * sc : sc;
-    bf16_t* orow_p = out + orow.row * N;
+    for (int i = 0; i < 5; ++i) {
+      if (i == 4 && (!extra || l32 >= 16)) continue;  // tail rows: lanes 0-15 of each half
+      const int ml = blk_row(i);
+      if (ml >= tile.rows) continue;
+      const OutRow orow = out_row_of(gx, tile.row0 + ml, dpre[i], A);
+      if (orow.row < 0) continue;
+      const float rsc = gx.row_scale != nullptr ? rpre[i] * sc : sc;
+      unsigned char* lrow = smem + ml * C::kOutRow;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // registers 4q .. 4q+3: output columns 8q + 4g .. +3 of the block
-        const int nb = tile.n0 + wn * 64 + 32 * j + 8 * q + 4 * g;
-        if (nb >= N) continue;  // N is a multiple of 16 here
-        float v[4];
+        for (int q = 0; q < 4; ++q) {
+          // registers 4q .. 4q+3: columns 8q + 4g .. +3 of the 32-column block
+          const int c = wn * 64 + 32 * j + 8 * q + 4 * g;
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float t = acc[i][j][4 * q + r] * rsc;
-          v[r] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
+          for (int r = 0; r < 4; ++r) {
+            const float t = acc[i][j][4 * q + r] * rsc;
+            v[r] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
+          }
+          *reinterpret_cast<uint2*>(lrow + c * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
-        *reinterpret_cast<uint2*>(orow_p + nb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
+    }
+  }
+  __syncthreads();
+  // 32 lanes per tile row, 16 bytes (8 columns) each; rows past the tile's
+  // rows, rows without a destination and columns past N are skipped
+  constexpr int kPasses = (C::kBM + C::kFold) * 32 / C::kNT;
+#pragma unroll 4
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int idx = ps * C::kNT + tid;
+    const int ml = idx >> 5, c = (idx & 31) * 8;
+    if (ml >= tile.rows || tile.n0 + c >= N) continue;  // N is a multiple of 16 here
+    const OutRow orow = out_row(gx, tile.row0 + ml, A);
+    if (orow.row < 0) continue;
+    *reinterpret_cast<uint4*>(out + orow.row * N + tile.n0 + c) =
+        *reinterpret_cast<const uint4*>(smem + ml * C::kOutRow + c * 2);
   }
 }
 

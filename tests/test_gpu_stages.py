@@ -238,6 +238,9 @@ GMM_CASES = [
     # 256 x 256 E4M3 tiles: three row tiles of one expert, a 1-row expert, 5 K slices
     ("fp8_wide_tiles", [600, 0, 1, 257], 320, 512, "fp8"),
     ("fp8_wide_16_column_tail", [300, 45], 128, 272, "fp8"),
+    # E4M3 tails of 1..32 rows ride on the tile before (257 = 256+1, 800 = 768+32,
+    # 1055 = 1024+31, 288); 289 = 256+33 gets a tile of its own
+    ("fp8_wide_fold_tails", [257, 513, 800, 1055, 288, 289], 256, 320, "fp8"),
     ("f32_tiny", [20, 0, 17, 40, 1, 30, 12, 8], 128, 256, "f32"),
     ("f32_ragged", [70, 5], 33, 45, "f32"),
 ]
