@@ -168,12 +168,38 @@ def reported_sclk():
     return None
 
 
+def cu_read_rate(dev):
+    """Bytes per shader clock one CU reads (moe_fetch_probe: one block of 8
+    waves per CU, 8 KB in flight per wave), from a 2 MiB window every CU
+    shares (stays in L2) and from a private 1/ncu slice of 1 GiB each (HBM);
+    LDS DMA as the GEMM kernels fetch, and plain vector loads. A 256 x 256
+    ping-pong GEMM tile needs 32 bytes per clock per CU at full MFMA use, so
+    the DMA rate from L2 over 32 bounds its MFMA busy fraction."""
+    import torch
+    import mixture_experts_layer_06_amd as moe
+    out = {"unit": "bytes per shader clock per CU (mean over CUs)"}
+    for name, nbytes, shared, kb in (("l2_2MiB", 2 << 20, True, 2048), ("hbm_1GiB", 1 << 30, False, 2048)):
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        for mode, mname in ((0, "lds_dma"), (1, "vector")):
+            best = None
+            for _ in range(3):
+                cyc, per_cu = moe.fetch_probe(buf, mode, shared, kb)
+                torch.cuda.synchronize()
+                r = per_cu / cyc.double().mean().item()
+                best = r if best is None or r > best else best
+            out[f"{name}_{mname}"] = best
+        del buf
+    out["mfma_bound_256x256_tile"] = min(1.0, out["l2_2MiB_lds_dma"] / 32.0)
+    return out
+
+
 def achievable(dev, even_experts=None):
     """What the GPU sustains on plain work of the same kind, outside the timed
     region, on random data (informational, beside the published peaks): a
     1 GiB device copy (read + write bytes), one dense bf16 GEMM of the prefill
-    GEMM 1 shape through the vendor BLAS (hipBLASLt), and optionally the
-    vendor's batched GEMM on even expert loads of the given shapes."""
+    GEMM 1 shape through the vendor BLAS (hipBLASLt), the read rate of one CU
+    (cu_read_rate), and optionally the vendor's batched GEMM on even expert
+    loads of the given shapes."""
     import torch
     res = {"sclk_reported_after_run": reported_sclk()}
     n = 1 << 30
@@ -189,6 +215,7 @@ def achievable(dev, even_experts=None):
     ms = _time_ms(lambda: torch.matmul(a, b), 10)
     res["vendor_dense_bf16_gemm_8192x4096x14336_TFLOPs"] = 2.0 * 8192 * 4096 * 14336 / (ms * 1e-3) / 1e12
     del a, b
+    res["cu_read_rate"] = cu_read_rate(dev)
     if even_experts is not None:
         E, M, shapes = even_experts
         for name, (Hin, N) in shapes.items():
@@ -400,7 +427,8 @@ def bench_layer(args, dev):
         "timing": timing_record(ms_step, ms_min, ms_b2b, wall_s, args.steps, sclk_start),
         "config": {"workload": workload, "T": T, "H": H, "E": E, "K": K, "F": F,
                    "tokens_per_step": T, "parallelism": "single GPU"},
-        "roofline": dict(roof, kernel="moe_gmm (" + ("gmm_stream_kernel" if hbm_bound else "gmm_pp_kernel") + ")",
+        "roofline": dict(roof, kernel="moe_gmm (" + ("gmm_f32_kernel" if dt == "f32" else "gmm_stream_kernel"
+                                                    if hbm_bound else "gmm_pp_kernel") + ")",
                          gmm_source=source_digest(),
                          launches_per_step=2, flops_per_launch=fl_launch,
                          bytes_per_launch=by_launch, avg_launch_ms=gmm_ms),
@@ -547,6 +575,29 @@ def bench_fp8(args, dev, mode="pt"):
     torch.cuda.synchronize()
     ms_b2b = (time.perf_counter() - t0) * 1e3 / args.steps
 
+    # The routed grouped GEMM launched alone (no shared GEMM beside it), each
+    # launch after a flush: its own rate, which the in-step time (shared with
+    # the side stream's GEMM) understates.
+    alone_ms = None
+    if not one:
+        def routed():
+            if use_mx:
+                if fp4:
+                    moe.gmm_mxfp4(gx, sx, gw, sw, perm["offsets"], out=gy)
+                else:
+                    moe.gmm_mx(gx, sx, gw, sw, perm["offsets"], out=gy)
+            else:
+                moe.gmm(qx if dyn else gx, gw, perm["offsets"], a_scale=sx, w_scale=sw, out=un, ws=gws,
+                        dst=perm["perm_src"], per_token=dyn)
+        lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            flush()
+            lev[s][0].record()
+            routed()
+            lev[s][1].record()
+        torch.cuda.synchronize()
+        alone_ms = median_min([e0.elapsed_time(e1) for e0, e1 in lev])[0]
+
     def span(i, j):
         return median_min([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)])
 
@@ -578,11 +629,11 @@ def bench_fp8(args, dev, mode="pt"):
                    "per-tensor scale; random top-8 of 32 routing)",
             "mx4": "synthetic (seeded; E2M1 with MX E8M0 scales per 32 elements, OCP recipe; "
                    "random top-8 of 32 routing)"}[mode.replace("_one", "") if mode != "one" else mode]
-    kernel = {"pt": "moe_gmm_scatter E4M3 (gmm_pp8_kernel, Unpermute fused into its stores)",
+    kernel = {"pt": "moe_gmm_scatter E4M3 (gmm_pp8w_kernel, Unpermute fused into its stores)",
               "one": "moe_gmm_routed_shared (gmm_pair_kernel: E4M3 routed tiles, Unpermute fused into their "
                      "stores, and bf16 shared-expert tiles in one launch)",
               "mx": "moe_gmm_mx E4M3 + E8M0 (gmm_pp8_kernel<true>)",
-              "dyn": "moe_gmm_scatter E4M3, per-token scales (gmm_pp8_kernel, Unpermute fused)",
+              "dyn": "moe_gmm_scatter E4M3, per-token scales (gmm_pp8w_kernel, Unpermute fused)",
               "mx4": "moe_gmm_mxfp4 E2M1 + E8M0 (gmm_pp8_kernel<true, true>)",
               "mx_one": "moe_gmm_mx_routed_shared E4M3 + E8M0 (gmm_pair_kernel<.., true, false>: MX routed "
                         "tiles and bf16 shared-expert tiles in one launch)",
@@ -609,6 +660,9 @@ def bench_fp8(args, dev, mode="pt"):
                      "flops_per_launch": fl, "bytes_per_launch": by, "avg_launch_ms": gmm_ms},
         "kernels": kernels,
     }
+    if alone_ms is not None:
+        res["roofline"]["launch_alone"] = {"ms": alone_ms, "TFLOP/s": fl / (alone_ms * 1e-3) / 1e12,
+                                           "frac": fl / (alone_ms * 1e-3) / 1e12 / peak}
     return res, host
 
 
@@ -723,7 +777,7 @@ def bench_layer_fp8(args, dev):
                    "tokens_per_step": T, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP8_TFLOPS, "traffic": measured_traffic("prefill_fp8"),
-                     "kernel": "moe_gmm E4M3, per-token scales (gmm_pp8_kernel)", "gmm_source": source_digest(),
+                     "kernel": "moe_gmm E4M3, per-token scales (gmm_pp8w_kernel)", "gmm_source": source_digest(),
                      "launches_per_step": 2, "flops_per_launch": fl_launch,
                      "bytes_per_launch": (by1 + by2) / 2.0, "avg_launch_ms": gmm_ms},
         "kernels": kernels,

@@ -443,6 +443,30 @@ moe_status moe_layer_fp8(const void* x, const void* w_router, const float* bias,
                          int K, int F, moe_act act, void* y, int32_t* topk_idx_out, float* topk_gate_out,
                          int32_t* counts_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- diagnostics (not steps of the layer) --------------------------------
+ *
+ * moe_fetch_probe: measures how many bytes per shader clock one compute unit
+ * reads from device memory, the rate that bounds the grouped GEMM's tiles
+ * (each 256 x 256 ping-pong tile fetches 32 bytes per MFMA cycle of its CU
+ * at full MFMA use). One block of 8 waves runs on every compute unit; each
+ * wave reads kb_per_wave KB in 1 KB instructions, 8 in flight.
+ *   buf     device, bytes long, 16-byte aligned (its contents are not used)
+ *   bytes   multiple of 1024, below 2^31; shared_window != 0: every block
+ *           reads the first `bytes` bytes (>= 64 KB; a size that stays in
+ *           L2, e.g. 2 MB, measures L2 -> CU); shared_window == 0: block b
+ *           reads its own bytes / ncu slice (>= 1 KB each; measures HBM)
+ *   mode    0: LDS DMA (buffer_load_dwordx4 ... lds, as the GEMM kernels
+ *           fetch), 1: 16-byte vector loads into registers
+ *   kb_per_wave  multiple of 8 in [8, 2^20]
+ *   cycles  device, one uint64 per compute unit of the device
+ *           (hipDeviceAttributeMultiprocessorCount): the shader-clock cycles
+ *           block b spent reading; bytes per clock per CU = 8 * kb_per_wave *
+ *           1024 / cycles[b].
+ * Errors: NULL_POINTER, MISALIGNED, UNSUPPORTED (mode), BAD_SHAPE; DEVICE.
+ */
+moe_status moe_fetch_probe(const void* buf, size_t bytes, int mode, int shared_window, int kb_per_wave,
+                           uint64_t* cycles, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -529,6 +529,21 @@ moe_status moe_sum_slots(const void* z, moe_dtype dt, int T, int K, int N, void*
   return launch_combine(z, dt, nullptr, nullptr, T, K, N, out, (hipStream_t)stream, true);
 }
 
+moe_status moe_fetch_probe(const void* buf, size_t bytes, int mode, int shared_window, int kb_per_wave,
+                           uint64_t* cycles, void* stream) {
+  REQUIRE_PTR(buf);
+  REQUIRE_PTR(cycles);
+  REQUIRE_ALIGNED(buf);
+  if (mode != 0 && mode != 1) return MOE_ERR_UNSUPPORTED;
+  if (bytes % 1024 != 0 || bytes > 0x7fffffffu) return MOE_ERR_BAD_SHAPE;
+  if (kb_per_wave < 8 || kb_per_wave % 8 != 0 || kb_per_wave > (1 << 20)) return MOE_ERR_BAD_SHAPE;
+  const int ncu = probe_device_cus();
+  if (ncu <= 0) return MOE_ERR_DEVICE;
+  if (bytes < (shared_window ? (size_t)65536 : (size_t)1024 * ncu)) return MOE_ERR_BAD_SHAPE;
+  return launch_fetch_probe(buf, bytes, mode, shared_window, kb_per_wave, (unsigned long long*)cycles, ncu,
+                            (hipStream_t)stream);
+}
+
 moe_status moe_layer_workspace_size(int T, int H, int E, int K, int F, moe_dtype dt, size_t* bytes) {
   REQUIRE_PTR(bytes);
   if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;

@@ -573,3 +573,23 @@ def test_layer_noalloc_limit_matches_the_workspace_query():
     assert moe.layer_workspace_size(256, 4096, 128, 8, 1536, moe.BF16) <= moe.NOALLOC_SCRATCH_BYTES
     assert moe.layer_workspace_size(512, 4096, 128, 8, 1536, moe.BF16) > moe.NOALLOC_SCRATCH_BYTES
     assert b"static buffer" in L.moe_status_string(moe.ERR_SCRATCH_LIMIT)
+
+
+def fetch_probe(buf=P, nbytes=2 << 20, mode=0, shared=1, kb=64, cycles=P):
+    return L.moe_fetch_probe(buf, nbytes, mode, shared, kb, cycles, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(buf=None), moe.ERR_NULL_POINTER),
+    (dict(cycles=None), moe.ERR_NULL_POINTER),
+    (dict(buf=MIS), moe.ERR_MISALIGNED),
+    (dict(mode=2), moe.ERR_UNSUPPORTED),
+    (dict(mode=-1), moe.ERR_UNSUPPORTED),
+    (dict(nbytes=(2 << 20) + 16), moe.ERR_BAD_SHAPE),   # not whole KB
+    (dict(nbytes=1 << 31), moe.ERR_BAD_SHAPE),          # past a 32-bit buffer descriptor
+    (dict(kb=4), moe.ERR_BAD_SHAPE),
+    (dict(kb=12), moe.ERR_BAD_SHAPE),
+    (dict(kb=(1 << 20) + 8), moe.ERR_BAD_SHAPE),
+])
+def test_fetch_probe_validation(kw, status):
+    assert fetch_probe(**kw) == status
