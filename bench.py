@@ -120,17 +120,20 @@ FLUSH_BYTES = 1 << 30  # written before every timed step: evicts the 256 MB MALL
 
 
 class Flush:
-    """A 1 GiB device buffer written (a fill kernel) before each timed step,
-    outside the step's events, so every step starts from cold caches."""
+    """A 1 GiB device buffer read (a sum over it) before each timed step,
+    outside the step's events, so every step starts from cold caches: the
+    read evicts the 256 MB MALL and the L2s without leaving dirty lines
+    behind, whose write-back a written buffer would charge to the step's
+    first kernel."""
 
     def __init__(self, dev):
         import torch
-        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-        self.n = 0
+        self.buf = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+        self.sink = torch.empty((), dtype=torch.int64, device=dev)
 
     def __call__(self):
-        self.n += 1
-        self.buf.fill_(self.n & 0xFF)
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def median_min(values):
@@ -357,7 +360,7 @@ def bench_layer(args, dev):
     flush = Flush(dev)
     warmup = warm_up(warm_step, args.warmup)
     sclk_start = reported_sclk()
-    # Timed: every step after a 1 GiB write (outside its events), between two
+    # Timed: every step after a 1 GiB read (outside its events), between two
     # events on the stream; median and min over the steps.
     lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -559,7 +562,7 @@ def bench_fp8(args, dev, mode="pt"):
     flush = Flush(dev)
     warmup = warm_up(step, args.warmup)
     sclk_start = reported_sclk()
-    # Timed: every step after a 1 GiB write (outside its events); the step
+    # Timed: every step after a 1 GiB read (outside its events); the step
     # runs from its first launch on either stream to the join of both.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -790,7 +793,7 @@ def bench_layer_fp8(args, dev):
 def timing_record(ms_med, ms_min, ms_b2b, wall_s, steps, sclk_start):
     return {"ms_per_step_median": ms_med, "ms_per_step_min": ms_min, "ms_per_step_back_to_back": ms_b2b,
             "timed_loop_wall_s": wall_s, "steps": steps, "sclk_reported_at_start": sclk_start,
-            "protocol": "each step after a 1 GiB device write (outside its events), timed with HIP events "
+            "protocol": "each step after a 1 GiB device read (outside its events), timed with HIP events "
                         "on its stream; value from the median step"}
 
 

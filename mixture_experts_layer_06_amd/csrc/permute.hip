@@ -14,9 +14,11 @@
 //   contiguous segment w of the pairs: it counts its segment per expert, a
 //   prefix over (wave, expert) gives every wave its first row per expert,
 //   and each wave ranks its own segment in order;
-//   otherwise: the same three steps over chunks of kChunk pairs in three
-//   launches (count per chunk -> one-block scan over (chunk, expert) ->
-//   per-chunk rank and write).
+//   otherwise: the same three steps over chunks of kChunk pairs: counts per
+//   chunk, then per-chunk rank and write, where every chunk block stages all
+//   (chunk, expert) counts in LDS and scans them for its own offsets (two
+//   launches); with more counts than one LDS stage holds, a one-block scan
+//   launch sits between the two instead.
 // Data path: one block per token reads its row once (16-byte vectors when
 // the row pitch allows) and writes it to its K destination rows.
 #include "common.h"
@@ -25,8 +27,9 @@ namespace moe {
 namespace {
 
 constexpr int kChunk = 1024;   // pairs per chunk
-constexpr int kBlockA = 16384;  // one-block path up to this many pairs
+constexpr int kBlockA = 4096;   // one-block path up to this many pairs
 constexpr int kBlockWaves = 16;
+constexpr int kScanInts = 12288;  // (chunk, expert) counts a block stages in LDS at once
 
 __device__ __forceinline__ int clamp_e(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
@@ -190,7 +193,6 @@ __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __res
 // experts, then the running prefix over chunks. The (chunk, expert) counts
 // pass through LDS in tiles of kScanInts, loaded by all threads at once; when
 // they fit in one tile the second pass reuses it.
-constexpr int kScanInts = 12288;
 __device__ __forceinline__ void load_scan_tile(const int32_t* __restrict__ src, int n, int* cc) {
   constexpr int U = 16;
   for (int p0 = 0; p0 < n; p0 += 256 * U) {
@@ -283,6 +285,77 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
   rank_regs<PL>(ev, begin, end, hist[w], perm_src, perm_dst);
 }
 
+// Chunk c when all (chunk, expert) counts fit in LDS: the scan of
+// permute_scan_kernel done by every block for itself. The block stages the
+// counts, thread e sums expert e over all chunks (its total) and over the
+// chunks before c (its prefix), an exclusive scan over experts gives the
+// expert offsets, and block 0 writes counts and offsets; then the four waves
+// count and rank the chunk's quarters as permute_rank_kernel does.
+__global__ __launch_bounds__(256) void permute_rank_scan_kernel(const int32_t* __restrict__ idx, int A, int E,
+                                                                const int32_t* __restrict__ chunk_counts,
+                                                                int nchunks, int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ perm_src,
+                                                                int32_t* __restrict__ perm_dst) {
+  constexpr int kQuarter = kChunk / 4;
+  constexpr int PL = kQuarter / kWave;
+  __shared__ int cc[kScanInts];
+  __shared__ int hist[4][256];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x;
+  const int w = tid / kWave, lane = tid & (kWave - 1);
+  const int c = blockIdx.x;
+  const int begin = min(A, c * kChunk + w * kQuarter);
+  const int end = min(A, begin + kQuarter);
+  int ev[PL];
+  load_range<PL>(idx, begin, end, E, ev);  // in flight while the counts are staged
+  load_scan_tile(chunk_counts, nchunks * E, cc);
+  __syncthreads();
+  int tot = 0, pre = 0;
+  if (tid < E) {
+    int c0 = 0;
+    for (; c0 + 8 <= nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cc[(c0 + u) * E + tid];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        tot += v[u];
+        pre += c0 + u < c ? v[u] : 0;
+      }
+    }
+    for (; c0 < nchunks; ++c0) {
+      const int v = cc[c0 * E + tid];
+      tot += v;
+      pre += c0 < c ? v : 0;
+    }
+  }
+  const int incl = wave_incl_scan(tot);
+  if (lane == kWave - 1) wsum[w] = incl;
+  count_regs<PL>(ev, begin, end, hist[w]);
+  __syncthreads();
+  int excl = incl - tot;
+  for (int q = 0; q < w; ++q) excl += wsum[q];
+  if (c == 0) {
+    if (tid < E) {
+      counts[tid] = tot;
+      offsets[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = A;
+  }
+  if (tid < E) {
+    int run = excl + pre;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = hist[q][tid];
+      hist[q][tid] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  rank_regs<PL>(ev, begin, end, hist[w], perm_src, perm_dst);
+}
+
 // Row scatter: x_perm[perm_dst[t*K+k]] = x[t]. VB = bytes per access.
 template <int VB>
 __global__ __launch_bounds__(256) void permute_rows_kernel(const unsigned char* __restrict__ x,
@@ -332,10 +405,16 @@ moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T
     int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);
     int32_t* chunk_base = chunk_counts + (int64_t)nch * E;
     hipLaunchKernelGGL(permute_count_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts);
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, A,
-                       chunk_base, counts, offsets);
-    hipLaunchKernelGGL(permute_rank_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_base,
-                       perm_src, perm_dst);
+    if ((int64_t)nch * E <= kScanInts) {
+      // every chunk block scans the (staged) counts itself: two launches
+      hipLaunchKernelGGL(permute_rank_scan_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts, nch,
+                         counts, offsets, perm_src, perm_dst);
+    } else {
+      hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, A,
+                         chunk_base, counts, offsets);
+      hipLaunchKernelGGL(permute_rank_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_base,
+                         perm_src, perm_dst);
+    }
   }
   if (x && T > 0) {
     const int64_t rb = (int64_t)H * dtype_size(dt);

@@ -123,8 +123,8 @@ def permute(idx=P, x=P, dt=moe.BF16, T=5000, H=64, E=8, K=4, counts=P, offsets=P
 
 def test_permute_workspace_size_small_and_chunked():
     assert moe.permute_workspace_size(16, 128, 8) == 0
-    assert moe.permute_workspace_size(4096, 8, 4) == 0    # 16384 pairs: one block, no scratch
-    assert moe.permute_workspace_size(4097, 8, 4) > 0     # chunked
+    assert moe.permute_workspace_size(1024, 8, 4) == 0    # 4096 pairs: one block, no scratch
+    assert moe.permute_workspace_size(1025, 8, 4) > 0     # chunked
     n = moe.permute_workspace_size(16384, 64, 6)
     assert n >= 2 * 96 * 64 * 4
 

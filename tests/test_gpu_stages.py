@@ -136,11 +136,13 @@ def test_permute_chunked_path_skewed_with_empty_experts():
 
 
 @pytest.mark.parametrize("T,E,K,skew", [
-    (1250, 256, 4, False),   # 5000 pairs: 16 waves, ragged last segment, E = 256
+    (1024, 256, 4, False),   # 4096 pairs: the largest one-block case, 16 waves, E = 256
     (513, 33, 3, True),      # 1539 pairs: 7 waves, empty experts
-    (4096, 4, 4, False),     # 16384 pairs: the largest one-block case, long equal runs
-    (4097, 4, 4, False),     # 16388 pairs: the smallest chunked case
+    (1025, 4, 4, False),     # 4100 pairs: the smallest chunked case (two launches), long equal runs
+    (4096, 8, 2, False),     # 8192 pairs: the prefill pair count, 8 chunks
+    (1250, 256, 4, False),   # 5000 pairs: chunked, ragged last chunk, E = 256
     (2048, 128, 8, False),   # decode T=256-like pair count x 8
+    (12800, 256, 4, False),  # 51200 pairs x 256 experts: more counts than one LDS stage (three launches)
 ])
 def test_permute_block_and_chunked_boundary(T, E, K, skew):
     idx = synth.random_routing(106 + T, T, E, K)
