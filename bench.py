@@ -116,7 +116,7 @@ def warm_up(fn, count):
                 return n
 
 
-FLUSH_BYTES = 1 << 30  # written before every timed step: evicts the 256 MB MALL and the L2s
+FLUSH_BYTES = 1 << 30  # read before every timed step: evicts the 256 MB MALL and the L2s
 
 
 class Flush:
@@ -171,28 +171,61 @@ def reported_sclk():
     return None
 
 
-def cu_read_rate(dev):
-    """Bytes per shader clock one CU reads (moe_fetch_probe: one block of 8
-    waves per CU, 8 KB in flight per wave), from a 2 MiB window every CU
+def cu_read_rate(dev, mfma=None):
+    """What one CU reads per second (moe_fetch_probe: one block of 8 waves per
+    CU, 8 KB in flight per wave; timed with HIP events, since the probe's own
+    s_memtime ticks do not run at a fixed rate), from a 2 MiB window every CU
     shares (stays in L2) and from a private 1/ncu slice of 1 GiB each (HBM);
     LDS DMA as the GEMM kernels fetch, and plain vector loads. A 256 x 256
-    ping-pong GEMM tile needs 32 bytes per clock per CU at full MFMA use, so
-    the DMA rate from L2 over 32 bounds its MFMA busy fraction."""
+    ping-pong GEMM tile reads 32 KB per 4.19 MFLOP (bf16); at the MFMA-only
+    rate of one CU (mfma) that is the read rate it needs, and the DMA rate
+    from L2 over it bounds the tile's share of that MFMA rate."""
     import torch
     import mixture_experts_layer_06_amd as moe
-    out = {"unit": "bytes per shader clock per CU (mean over CUs)"}
+    out = {"unit": "GB/s per CU (mean over the launch)"}
     for name, nbytes, shared, kb in (("l2_2MiB", 2 << 20, True, 2048), ("hbm_1GiB", 1 << 30, False, 2048)):
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         for mode, mname in ((0, "lds_dma"), (1, "vector")):
             best = None
             for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
                 cyc, per_cu = moe.fetch_probe(buf, mode, shared, kb)
+                e1.record()
                 torch.cuda.synchronize()
-                r = per_cu / cyc.double().mean().item()
+                r = per_cu / (e0.elapsed_time(e1) * 1e-3) / 1e9
                 best = r if best is None or r > best else best
             out[f"{name}_{mname}"] = best
         del buf
-    out["mfma_bound_256x256_tile"] = min(1.0, out["l2_2MiB_lds_dma"] / 32.0)
+    if mfma is not None:
+        ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+        per_cu_flops = mfma["bf16"]["TFLOP/s"] * 1e12 / ncu
+        need = 32768.0 / (256 * 256 * 32 * 2) * per_cu_flops / 1e9
+        out["bf16_tile_need_at_mfma_only_rate"] = need
+        out["mfma_bound_256x256_tile"] = min(1.0, out["l2_2MiB_lds_dma"] / need)
+    return out
+
+
+def mfma_only(dev):
+    """MFMA rate without memory traffic (moe_mfma_probe, every CU, 8 waves,
+    long enough that the launch gap does not count), by HIP events; and the
+    shader clock that rate implies at the MFMA issue peak (bf16 4096, E4M3
+    8192 flops per clock per CU)."""
+    import torch
+    import mixture_experts_layer_06_amd as moe
+    out = {}
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    for name, fp8, iters, per_clk in (("bf16", False, 8192, 4096.0), ("fp8_e4m3", True, 4096, 8192.0)):
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            cyc, fl = moe.mfma_probe(fp8, iters, device=dev)
+            e1.record()
+            torch.cuda.synchronize()
+            tf = fl * ncu / (e0.elapsed_time(e1) * 1e-3) / 1e12
+            best = tf if best is None or tf > best else best
+        out[name] = {"TFLOP/s": best, "implied_clock_GHz_at_full_issue": best * 1e12 / ncu / per_clk / 1e9}
     return out
 
 
@@ -201,8 +234,9 @@ def achievable(dev, even_experts=None):
     region, on random data (informational, beside the published peaks): a
     1 GiB device copy (read + write bytes), one dense bf16 GEMM of the prefill
     GEMM 1 shape through the vendor BLAS (hipBLASLt), the read rate of one CU
-    (cu_read_rate), and optionally the vendor's batched GEMM on even expert
-    loads of the given shapes."""
+    (cu_read_rate), the MFMA rate without memory traffic (mfma_only), and
+    optionally the vendor's batched GEMM on even expert loads of the given
+    shapes."""
     import torch
     res = {"sclk_reported_after_run": reported_sclk()}
     n = 1 << 30
@@ -218,7 +252,8 @@ def achievable(dev, even_experts=None):
     ms = _time_ms(lambda: torch.matmul(a, b), 10)
     res["vendor_dense_bf16_gemm_8192x4096x14336_TFLOPs"] = 2.0 * 8192 * 4096 * 14336 / (ms * 1e-3) / 1e12
     del a, b
-    res["cu_read_rate"] = cu_read_rate(dev)
+    res["mfma_only"] = mfma_only(dev)
+    res["cu_read_rate"] = cu_read_rate(dev, res["mfma_only"])
     if even_experts is not None:
         E, M, shapes = even_experts
         for name, (Hin, N) in shapes.items():

@@ -445,11 +445,14 @@ moe_status moe_layer_fp8(const void* x, const void* w_router, const float* bias,
 
 /* ---- diagnostics (not steps of the layer) --------------------------------
  *
- * moe_fetch_probe: measures how many bytes per shader clock one compute unit
- * reads from device memory, the rate that bounds the grouped GEMM's tiles
- * (each 256 x 256 ping-pong tile fetches 32 bytes per MFMA cycle of its CU
- * at full MFMA use). One block of 8 waves runs on every compute unit; each
- * wave reads kb_per_wave KB in 1 KB instructions, 8 in flight.
+ * moe_fetch_probe: measures how fast one compute unit reads from device
+ * memory, the rate that bounds the grouped GEMM's tiles (each 256 x 256
+ * ping-pong tile fetches 32 bytes per MFMA cycle of its CU at full MFMA
+ * use). One block of 8 waves runs on every compute unit; each wave reads
+ * kb_per_wave KB in 1 KB instructions, 8 in flight. Time the launch with
+ * stream events for a rate per second: the per-block counts below come from
+ * s_memtime, whose tick rate was seen to differ from the shader clock and
+ * to vary between kernels, so they show the spread across CUs, not a rate.
  *   buf     device, bytes long, 16-byte aligned (its contents are not used)
  *   bytes   multiple of 1024, below 2^31; shared_window != 0: every block
  *           reads the first `bytes` bytes (>= 64 KB; a size that stays in
@@ -459,13 +462,26 @@ moe_status moe_layer_fp8(const void* x, const void* w_router, const float* bias,
  *           fetch), 1: 16-byte vector loads into registers
  *   kb_per_wave  multiple of 8 in [8, 2^20]
  *   cycles  device, one uint64 per compute unit of the device
- *           (hipDeviceAttributeMultiprocessorCount): the shader-clock cycles
- *           block b spent reading; bytes per clock per CU = 8 * kb_per_wave *
- *           1024 / cycles[b].
+ *           (hipDeviceAttributeMultiprocessorCount): the s_memtime ticks
+ *           block b spent reading 8 * kb_per_wave * 1024 bytes.
  * Errors: NULL_POINTER, MISALIGNED, UNSUPPORTED (mode), BAD_SHAPE; DEVICE.
  */
 moe_status moe_fetch_probe(const void* buf, size_t bytes, int mode, int shared_window, int kb_per_wave,
                            uint64_t* cycles, void* stream);
+
+/* moe_mfma_probe: the MFMA rate with no memory traffic, the achievable side of
+ * the MFMA peak. One block of 8 waves runs on every compute unit; each wave
+ * issues `iters` rounds of 8 independent MFMAs on register operands
+ * (MOE_BF16: v_mfma_f32_16x16x32_bf16, 16384 flops each; MOE_FP8_E4M3:
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales, 131072 flops each).
+ *   iters   in [1, 2^24]
+ *   sink    device, 512 floats per compute unit (results, kept so the work runs)
+ *   cycles  device, one uint64 per compute unit: s_memtime ticks of block b
+ * Flops per CU = 8 waves * 8 * iters * flops per MFMA; time the launch with
+ * stream events for the rate.
+ * Errors: NULL_POINTER, BAD_DTYPE, BAD_SHAPE; DEVICE.
+ */
+moe_status moe_mfma_probe(moe_dtype dt, int iters, float* sink, uint64_t* cycles, void* stream);
 
 #ifdef __cplusplus
 }

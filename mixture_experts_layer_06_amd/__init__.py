@@ -30,7 +30,7 @@ EXPORTS = ("moe_status_string", "moe_version", "moe_route_workspace_size", "moe_
            "moe_permute_workspace_size", "moe_permute", "moe_gmm_workspace_size", "moe_gmm",
            "moe_gmm_gather", "moe_gmm_scatter", "moe_gmm_routed_shared", "moe_gmm_mx_routed_shared", "moe_gmm_mx", "moe_gmm_mxfp4", "moe_combine", "moe_sum_slots",
            "moe_quant_rows", "moe_layer_workspace_size", "moe_layer", "moe_layer_fp8_workspace_size",
-           "moe_layer_fp8", "moe_layer_noalloc", "moe_fetch_probe")
+           "moe_layer_fp8", "moe_layer_noalloc", "moe_fetch_probe", "moe_mfma_probe")
 
 
 class MoeError(RuntimeError):
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                     vp, sz, vp]
         L.moe_fetch_probe.argtypes = [vp, sz, i32, i32, i32, vp, vp]
+        L.moe_mfma_probe.argtypes = [i32, i32, vp, vp, vp]
         for n in EXPORTS[2:]:
             getattr(L, n).restype = i32
         _lib = L
@@ -428,10 +429,22 @@ def layer_fp8(x, w_router, w1, w1_scale, w2, w2_scale, K, bias=None, act=ACT_REL
 
 def fetch_probe(buf, mode, shared_window, kb_per_wave, stream=None):
     """moe_fetch_probe over the uint8 device tensor buf (mode 0: LDS DMA, 1:
-    vector loads). Returns the per-compute-unit shader-clock cycles (int64
-    device tensor, one entry per CU) and the bytes each CU read."""
+    vector loads). Returns the per-compute-unit s_memtime ticks (int64
+    device tensor, one entry per CU) and the bytes each CU read; time the
+    call with stream events for a rate."""
     ncu = torch.cuda.get_device_properties(buf.device).multi_processor_count
     cycles = torch.zeros((ncu,), dtype=torch.int64, device=buf.device)
     _check(lib().moe_fetch_probe(_ptr(buf), buf.numel(), mode, 1 if shared_window else 0, kb_per_wave,
                                  _ptr(cycles), _stream(stream)), "moe_fetch_probe")
     return cycles, 8 * kb_per_wave * 1024
+
+
+def mfma_probe(fp8, iters, device="cuda", stream=None):
+    """moe_mfma_probe: per-CU s_memtime ticks (int64 device tensor) and the
+    flops each CU issued; time the call with stream events for a rate."""
+    ncu = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+    cycles = torch.zeros((ncu,), dtype=torch.int64, device=device)
+    sink = torch.empty((ncu * 512,), dtype=torch.float32, device=device)
+    _check(lib().moe_mfma_probe(FP8_E4M3 if fp8 else BF16, iters, _ptr(sink), _ptr(cycles), _stream(stream)),
+           "moe_mfma_probe")
+    return cycles, 8 * 8 * iters * (131072 if fp8 else 16384)

@@ -544,6 +544,16 @@ moe_status moe_fetch_probe(const void* buf, size_t bytes, int mode, int shared_w
                             (hipStream_t)stream);
 }
 
+moe_status moe_mfma_probe(moe_dtype dt, int iters, float* sink, uint64_t* cycles, void* stream) {
+  REQUIRE_PTR(sink);
+  REQUIRE_PTR(cycles);
+  if (dt != MOE_BF16 && dt != MOE_FP8_E4M3) return MOE_ERR_BAD_DTYPE;
+  if (iters < 1 || iters > (1 << 24)) return MOE_ERR_BAD_SHAPE;
+  const int ncu = probe_device_cus();
+  if (ncu <= 0) return MOE_ERR_DEVICE;
+  return launch_mfma_probe(dt == MOE_FP8_E4M3, iters, sink, (unsigned long long*)cycles, ncu, (hipStream_t)stream);
+}
+
 moe_status moe_layer_workspace_size(int T, int H, int E, int K, int F, moe_dtype dt, size_t* bytes) {
   REQUIRE_PTR(bytes);
   if (!layer_dtype_ok(dt)) return MOE_ERR_BAD_DTYPE;

@@ -110,6 +110,7 @@ size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N);
 int probe_device_cus();  // compute units of the current device (0 when the query fails)
 moe_status launch_fetch_probe(const void* buf, size_t bytes, int mode, int shared_window, int kb_per_wave,
                               unsigned long long* cycles, int ncu, hipStream_t s);
+moe_status launch_mfma_probe(int fp8, int iters, float* sink, unsigned long long* cycles, int ncu, hipStream_t s);
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                       moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s,

@@ -1,14 +1,16 @@
-// probe.hip — read rate of one CU from device memory, a diagnostic for the
-// grouped GEMM's ceiling (not a step of the MoE layer).
+// probe.hip — read rate of one CU from device memory and the MFMA issue
+// rate without memory traffic: diagnostics for the grouped GEMM's ceiling
+// (not steps of the MoE layer).
 //
 // The ping-pong GEMM kernels fetch a 32 KB K slice per 1024 MFMA cycles per
-// CU, so how many bytes one CU can pull per clock bounds their MFMA use.
+// CU, so how fast one CU can pull bytes bounds their MFMA use.
 // This kernel measures it: one block of 8 waves per CU (128 KB of dynamic
 // LDS keeps a second block off the CU), each wave streaming `kb_per_wave`
 // KB in 1 KB instructions with 8 of them in flight, either as LDS DMA
 // (buffer_load_dwordx4 ... lds, what the GEMM kernels use) or as 16-byte
-// vector loads into registers. Every block times its reads with the shader
-// clock (s_memtime). Shared window: every block reads the first `bytes`
+// vector loads into registers. Every block also counts s_memtime ticks
+// across its reads (the spread across CUs; the rate comes from timing the
+// launch, as these ticks do not keep the shader clock's pace). Shared window: every block reads the first `bytes`
 // bytes (a size that stays in L2 measures the L2-to-CU path); private: block
 // b reads its own 1/ncu of the buffer (the HBM path).
 #include "common.h"
@@ -80,7 +82,67 @@ __global__ __launch_bounds__(kProbeWaves * kWave) void fetch_probe_kernel(const 
   if (threadIdx.x == 0) cycles[b] = t1 - t0;
 }
 
+// MFMA issue rate with no memory traffic: 8 waves per CU, each running
+// `iters` rounds of 8 independent MFMAs on register operands (bf16:
+// v_mfma_f32_16x16x32_bf16; E4M3: v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// scales), with s_memtime ticks per block. The accumulators are
+// stored once so the work is kept.
+template <bool FP8>
+__global__ __launch_bounds__(kProbeWaves * kWave) void mfma_probe_kernel(int iters, float* __restrict__ sink,
+                                                                         unsigned long long* __restrict__ cycles) {
+  const int lane = threadIdx.x & (kWave - 1);
+  __syncthreads();
+  const unsigned long long t0 = clock64();
+  float keep = 0.f;
+  if (FP8) {
+    i32x8_t a, b;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      a[q] = 0x38383838 ^ (lane << q);  // E4M3 bytes around 1.0
+      b[q] = 0x30303030 ^ (q << 8);
+    }
+    f32x16_t acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[m], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) keep += acc[m][lane & 15];
+  } else {
+    bf16x8_t a, b;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      a[q] = (__bf16)(1.0f + 0.001f * (float)(lane + q));
+      b[q] = (__bf16)(0.5f - 0.001f * (float)q);
+    }
+    f32x4_t acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) keep += acc[m][lane & 3];
+  }
+  const unsigned long long t1 = clock64();
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = keep;
+  __syncthreads();
+  if (threadIdx.x == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
 }  // namespace
+
+moe_status launch_mfma_probe(int fp8, int iters, float* sink, unsigned long long* cycles, int ncu, hipStream_t s) {
+  if (fp8)
+    hipLaunchKernelGGL((mfma_probe_kernel<true>), dim3(ncu), dim3(kProbeWaves * kWave), 0, s, iters, sink, cycles);
+  else
+    hipLaunchKernelGGL((mfma_probe_kernel<false>), dim3(ncu), dim3(kProbeWaves * kWave), 0, s, iters, sink, cycles);
+  return launch_status();
+}
 
 int probe_device_cus() {
   int dev = 0, n = 0;

@@ -593,3 +593,16 @@ def fetch_probe(buf=P, nbytes=2 << 20, mode=0, shared=1, kb=64, cycles=P):
 ])
 def test_fetch_probe_validation(kw, status):
     assert fetch_probe(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sink=None), moe.ERR_NULL_POINTER),
+    (dict(cycles=None), moe.ERR_NULL_POINTER),
+    (dict(dt=moe.F32), moe.ERR_BAD_DTYPE),
+    (dict(iters=0), moe.ERR_BAD_SHAPE),
+    (dict(iters=(1 << 24) + 1), moe.ERR_BAD_SHAPE),
+])
+def test_mfma_probe_validation(kw, status):
+    a = dict(dt=moe.BF16, iters=16, sink=P, cycles=P)
+    a.update(kw)
+    assert L.moe_mfma_probe(a["dt"], a["iters"], a["sink"], a["cycles"], None) == status
