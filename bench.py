@@ -183,14 +183,17 @@ def cu_read_rate(dev, mfma=None):
     import torch
     import mixture_experts_layer_06_amd as moe
     out = {"unit": "GB/s per CU (mean over the launch)"}
-    for name, nbytes, shared, kb in (("l2_2MiB", 2 << 20, True, 2048), ("hbm_1GiB", 1 << 30, False, 2048)):
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    cycles = torch.zeros((ncu,), dtype=torch.int64, device=dev)
+    for name, nbytes, shared, kb in (("l2_2MiB", 2 << 20, True, 4096), ("hbm_1GiB", 1 << 30, False, 2048)):
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         for mode, mname in ((0, "lds_dma"), (1, "vector")):
+            moe.fetch_probe(buf, mode, shared, 64, cycles=cycles)  # warm
             best = None
             for _ in range(3):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                cyc, per_cu = moe.fetch_probe(buf, mode, shared, kb)
+                _, per_cu = moe.fetch_probe(buf, mode, shared, kb, cycles=cycles)
                 e1.record()
                 torch.cuda.synchronize()
                 r = per_cu / (e0.elapsed_time(e1) * 1e-3) / 1e9
@@ -215,12 +218,15 @@ def mfma_only(dev):
     import mixture_experts_layer_06_amd as moe
     out = {}
     ncu = torch.cuda.get_device_properties(dev).multi_processor_count
-    for name, fp8, iters, per_clk in (("bf16", False, 8192, 4096.0), ("fp8_e4m3", True, 4096, 8192.0)):
+    cycles = torch.zeros((ncu,), dtype=torch.int64, device=dev)
+    sink = torch.empty((ncu * 512,), dtype=torch.float32, device=dev)
+    for name, fp8, iters, per_clk in (("bf16", False, 16384, 4096.0), ("fp8_e4m3", True, 8192, 8192.0)):
+        moe.mfma_probe(fp8, 64, device=dev, cycles=cycles, sink=sink)  # warm
         best = None
         for _ in range(3):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            cyc, fl = moe.mfma_probe(fp8, iters, device=dev)
+            _, fl = moe.mfma_probe(fp8, iters, device=dev, cycles=cycles, sink=sink)
             e1.record()
             torch.cuda.synchronize()
             tf = fl * ncu / (e0.elapsed_time(e1) * 1e-3) / 1e12

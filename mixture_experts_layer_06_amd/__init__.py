@@ -427,24 +427,34 @@ def layer_fp8(x, w_router, w1, w1_scale, w2, w2_scale, K, bias=None, act=ACT_REL
     return y
 
 
-def fetch_probe(buf, mode, shared_window, kb_per_wave, stream=None):
+def fetch_probe(buf, mode, shared_window, kb_per_wave, stream=None, cycles=None):
     """moe_fetch_probe over the uint8 device tensor buf (mode 0: LDS DMA, 1:
     vector loads). Returns the per-compute-unit s_memtime ticks (int64
-    device tensor, one entry per CU) and the bytes each CU read; time the
+    device tensor, one entry per CU; pass `cycles` to reuse one, so that a
+    timed call launches nothing else) and the bytes each CU read; time the
     call with stream events for a rate."""
     ncu = torch.cuda.get_device_properties(buf.device).multi_processor_count
-    cycles = torch.zeros((ncu,), dtype=torch.int64, device=buf.device)
+    if cycles is None:
+        cycles = torch.zeros((ncu,), dtype=torch.int64, device=buf.device)
+    elif cycles.numel() != ncu or cycles.dtype != torch.int64 or cycles.device != buf.device:
+        raise ValueError("cycles must be an int64 tensor of one entry per compute unit on buf's device")
     _check(lib().moe_fetch_probe(_ptr(buf), buf.numel(), mode, 1 if shared_window else 0, kb_per_wave,
                                  _ptr(cycles), _stream(stream)), "moe_fetch_probe")
     return cycles, 8 * kb_per_wave * 1024
 
 
-def mfma_probe(fp8, iters, device="cuda", stream=None):
+def mfma_probe(fp8, iters, device="cuda", stream=None, cycles=None, sink=None):
     """moe_mfma_probe: per-CU s_memtime ticks (int64 device tensor) and the
-    flops each CU issued; time the call with stream events for a rate."""
+    flops each CU issued; pass `cycles` (int64, one per CU) and `sink`
+    (float32, 512 per CU) to reuse them, so that a timed call launches
+    nothing else; time the call with stream events for a rate."""
     ncu = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
-    cycles = torch.zeros((ncu,), dtype=torch.int64, device=device)
-    sink = torch.empty((ncu * 512,), dtype=torch.float32, device=device)
+    if cycles is None:
+        cycles = torch.zeros((ncu,), dtype=torch.int64, device=device)
+    if sink is None:
+        sink = torch.empty((ncu * 512,), dtype=torch.float32, device=device)
+    if cycles.numel() != ncu or cycles.dtype != torch.int64 or sink.numel() < ncu * 512 or sink.dtype != torch.float32:
+        raise ValueError("cycles: int64, one per compute unit; sink: float32, 512 per compute unit")
     _check(lib().moe_mfma_probe(FP8_E4M3 if fp8 else BF16, iters, _ptr(sink), _ptr(cycles), _stream(stream)),
            "moe_mfma_probe")
     return cycles, 8 * 8 * iters * (131072 if fp8 else 16384)

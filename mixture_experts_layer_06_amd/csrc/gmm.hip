@@ -955,7 +955,10 @@ __device__ __forceinline__ void pp_block(
 #pragma unroll
       for (int j = 0; j < 4; ++j) a16[4 * r + j] = f < C::kFI ? acc[f][g][j][r] : acct[g][j][r];
   };
-  auto store_out = [&](int f, int g, const float* acc16) {
+  // M: 0-3 = compile-time ReLU (bit 0) and gate (bit 1) cases, 4 = both
+  // decided at run time (the split-K path's one copy)
+  auto store_out = [&](int f, int g, const float* acc16, auto M) {
+    constexpr int kM = decltype(M)::value;
     const int ml = frag_row(f);
     const int nb = tile.n0 + wn * C::kWN + g * 64 + 16 * kq;
     if (ml >= tile.rows || nb >= N) return;  // N is a multiple of 16 here
@@ -964,8 +967,14 @@ __device__ __forceinline__ void pp_block(
     float v[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const float t = acc16[q] * sc;
-      v[q] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
+      float t = acc16[q] * sc;
+      if (kM == 4) {
+        t = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
+      } else {
+        if (kM & 1) t = t < 0.f ? 0.f : t;
+        if (kM & 2) t *= orow.gate;
+      }
+      v[q] = t;
     }
     bf16_t* o = out + orow.row * N + nb;
     reinterpret_cast<uint4*>(o)[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
@@ -975,16 +984,23 @@ __device__ __forceinline__ void pp_block(
   };
   if (wk.S == 1) {
     if (!wave_active) return;
+    auto store_all = [&](auto M) {
 #pragma unroll
-    for (int f = 0; f < C::kFI + 1; ++f) {
-      if (f == C::kFI && !extra) continue;  // compile-time f keeps the accumulators in registers
+      for (int f = 0; f < C::kFI + 1; ++f) {
+        if (f == C::kFI && !extra) continue;  // compile-time f keeps the accumulators in registers
 #pragma unroll
-      for (int g = 0; g < C::kFG; ++g) {
-        float a16[16];
-        frag_acc(f, g, a16);
-        store_out(f, g, a16);
+        for (int g = 0; g < C::kFG; ++g) {
+          float a16[16];
+          frag_acc(f, g, a16);
+          store_out(f, g, a16, M);
+        }
       }
-    }
+    };
+    const int m = (relu ? 1 : 0) | (gx.dst != nullptr && gx.gate != nullptr ? 2 : 0);
+    if (m == 0) store_all(std::integral_constant<int, 0>{});
+    else if (m == 1) store_all(std::integral_constant<int, 1>{});
+    else if (m == 2) store_all(std::integral_constant<int, 2>{});
+    else store_all(std::integral_constant<int, 3>{});
     return;
   }
   // Split tile: every part stores its fp32 partial tile [BM + kFold][BN];
@@ -1050,7 +1066,7 @@ __device__ __forceinline__ void pp_block(
 #pragma unroll
         for (int c = 0; c < 16; ++c) a16[c] = q == 0 ? p16[c] : a16[c] + p16[c];
       }
-      store_out(f, g, a16);
+      store_out(f, g, a16, std::integral_constant<int, 4>{});
     }
   }
 }
@@ -1725,7 +1741,10 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
   wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
   __syncthreads();  // every wave is done with the ring
 
-  if (wave_active) {
+  // accumulators -> scaled, activated, gated bf16 in the LDS copy of the
+  // output tile; ReLU and the gate are compile-time cases (one multiply per
+  // value when neither applies: this loop's arithmetic is the epilogue's cost)
+  auto stage = [&](auto relu_c, auto gate_c) {
     const float sc = ld_scale(a_scale) * ld_scale(w_scale);
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
@@ -1745,11 +1764,23 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float t = acc[i][j][4 * q + r] * rsc;
-            v[r] = ((relu && t < 0.f) ? 0.f : t) * orow.gate;
+            float t = acc[i][j][4 * q + r] * rsc;
+            if (decltype(relu_c)::value) t = t < 0.f ? 0.f : t;
+            if (decltype(gate_c)::value) t *= orow.gate;
+            v[r] = t;
           }
           *reinterpret_cast<uint2*>(lrow + c * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
+    }
+  };
+  if (wave_active) {
+    const bool gated = gx.dst != nullptr && gx.gate != nullptr;
+    if (relu) {
+      if (gated) stage(std::true_type{}, std::true_type{});
+      else stage(std::true_type{}, std::false_type{});
+    } else {
+      if (gated) stage(std::false_type{}, std::true_type{});
+      else stage(std::false_type{}, std::false_type{});
     }
   }
   __syncthreads();
