@@ -179,7 +179,7 @@ def cu_read_rate(dev, mfma=None):
     LDS DMA as the GEMM kernels fetch, and plain vector loads. A 256 x 256
     ping-pong GEMM tile reads 32 KB per 4.19 MFLOP (bf16); at the MFMA-only
     rate of one CU (mfma) that is the read rate it needs, and the DMA rate
-    from L2 over it bounds the tile's share of that MFMA rate."""
+    from L2 over it is the share of that MFMA rate the reads alone allow."""
     import torch
     import mixture_experts_layer_06_amd as moe
     out = {"unit": "GB/s per CU (mean over the launch)"}
