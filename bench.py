@@ -62,13 +62,18 @@ def parse():
     return ap.parse_args()
 
 
-GMM_SRC = os.path.join(ROOT, "mixture_experts_layer_06_amd", "csrc", "gmm.hip")
+GMM_SRC = [os.path.join(ROOT, "mixture_experts_layer_06_amd", "csrc", f) for f in ("gmm.hip", "common.h")]
 
 
-def source_digest(path=GMM_SRC) -> str:
+def source_digest(paths=GMM_SRC) -> str:
+    """Digest of the grouped GEMM's sources (its kernel file and the helpers
+    it includes): counter summaries taken on other sources are not used."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
