@@ -141,6 +141,17 @@ class Flush:
         torch.sum(self.buf, dim=0, out=self.sink)
 
 
+def pp_kernel_names(H, F):
+    """The bf16 ping-pong kernels GEMM 1 (K = H) and GEMM 2 (K = F) run on:
+    the persistent form for tiles of at most 64 K slices of 32 values."""
+    names = []
+    for k in (H, F):
+        n = "gmm_ppd_kernel" if (k + 31) // 32 <= 64 else "gmm_pp_kernel"
+        if n not in names:
+            names.append(n)
+    return " / ".join(names)
+
+
 def median_min(values):
     import numpy as np
     v = np.asarray(values, np.float64)
@@ -477,7 +488,7 @@ def bench_layer(args, dev):
         "config": {"workload": workload, "T": T, "H": H, "E": E, "K": K, "F": F,
                    "tokens_per_step": T, "parallelism": "single GPU"},
         "roofline": dict(roof, kernel="moe_gmm (" + ("gmm_f32_kernel" if dt == "f32" else "gmm_stream_kernel"
-                                                    if hbm_bound else "gmm_pp_kernel") + ")",
+                                                    if hbm_bound else pp_kernel_names(H, F)) + ")",
                          gmm_source=source_digest(),
                          launches_per_step=2, flops_per_launch=fl_launch,
                          bytes_per_launch=by_launch, avg_launch_ms=gmm_ms),
