@@ -166,6 +166,10 @@ moe_status moe_permute(const int32_t* topk_idx, const void* x, moe_dtype dt, int
  *            a partial last round on the GPU, those tiles are split along
  *            the reduction and their fp32 partial sums meet here; the parts
  *            are added in a fixed order, so results do not depend on timing.
+ *            It also holds the counters from which the bf16 kernel's
+ *            persistent form (K <= 2048) hands out tiles. Its contents need
+ *            no initialisation (the call clears what it uses, on the stream);
+ *            calls that may run at the same time must not share it.
  * Supported types (a_dt, w_dt -> out_dt): F32,F32->F32; BF16,BF16->BF16;
  * FP8,FP8->BF16 (FP8 requires MOE_QUANT_PER_TENSOR or, for a, MOE_QUANT_PER_TOKEN
  * and MOE_QUANT_PER_TENSOR for w).
