@@ -19,6 +19,9 @@
 // row i being expert 4i+j. The waves' partial scores are summed in a fixed
 // order in LDS. Loading the weights per chunk from global memory instead
 // made the address unit the bottleneck (8 weight loads per token load).
+// With at most 16 experts and H not split, route_small_kernel instead gives
+// each wave only the weight rows of its own chunks and one MFMA per chunk
+// (experts as the 16 rows), with no block barrier before the multiply.
 //
 // With few token tiles (decode) H is split over S blocks per tile so that
 // W_r streams through many CUs: each block writes its fp32 partial scores
@@ -157,20 +160,12 @@ __device__ __forceinline__ int row_min(int v) {
   return min(v, dpp_mov<0x140, 0xf>(v));
 }
 
-__device__ __forceinline__ void topk_softmax_rows(const float* lg, int stride, int nrow, int E, int K, bool hb,
-                                                  const float (&bv)[4], int32_t* idx_out, float* gate_out) {
+// v[i], alive[i]: this lane's scores (bias added, NaN as -inf) of experts
+// j + 16i and whether they exist; live: row r names a token.
+__device__ __forceinline__ void topk_softmax_rows_core(float (&v)[4], bool (&alive)[4], bool live, int K,
+                                                       int32_t* idx_out, float* gate_out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane >> 4, j = lane & 15;
-  const bool live = r < nrow;
-  const float* row = lg + (live ? r : 0) * stride;
-  float v[4];
-  bool alive[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = j + 16 * i;
-    alive[i] = e < E;
-    v[i] = alive[i] ? nan_to_ninf(hb ? row[e] + bv[i] : row[e]) : -INFINITY;
-  }
   float sv[8];
   int se[8];
 #pragma unroll
@@ -214,6 +209,23 @@ __device__ __forceinline__ void topk_softmax_rows(const float* lg, int stride, i
     idx_out[r * K + j] = my_e;
     gate_out[r * K + j] = mine * inv;
   }
+}
+
+__device__ __forceinline__ void topk_softmax_rows(const float* lg, int stride, int nrow, int E, int K, bool hb,
+                                                  const float (&bv)[4], int32_t* idx_out, float* gate_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane >> 4, j = lane & 15;
+  const bool live = r < nrow;
+  const float* row = lg + (live ? r : 0) * stride;
+  float v[4];
+  bool alive[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = j + 16 * i;
+    alive[i] = e < E;
+    v[i] = alive[i] ? nan_to_ninf(hb ? row[e] + bv[i] : row[e]) : -INFINITY;
+  }
+  topk_softmax_rows_core(v, alive, live, K, idx_out, gate_out);
 }
 
 // Fixed-order sum of the nw wave slices (stride `slice` floats) of element p.
@@ -429,6 +441,116 @@ __global__ __launch_bounds__(G * TF <= 2 ? 1024 : 512) void route_bf16_kernel(
   }
 }
 
+// Few experts (E <= 16, E % 4 == 0, H % 8 == 0, aligned rows), one block
+// per 16 tokens and H not split. One MFMA per 32-wide chunk of H: the 16
+// expert rows of W_r^T (rows past E zero) times the 16 token columns, so no
+// expert row is padded to 64. Wave w owns chunks [w*cpw, (w+1)*cpw) and
+// copies only the weight rows of those chunks (contiguous in W_r) into its
+// own LDS slab, so no block barrier precedes the multiply: the weight loads
+// and the token loads of a pass of up to kSmallPass chunks are all issued
+// at once, then the slab is written and read back in the row operand's
+// layout (lane (i, kq): expert i, h = 32c + 8kq .. +7) by the same wave. The
+// waves' partial scores (one 16 x 16 fragment each, written over the start
+// of the wave's own slab) are summed in wave order by the selecting lanes
+// themselves: 16-lane row r of wave w takes token 4w + r, lane j expert j.
+constexpr int kSmallPass = 8;  // chunks per pass
+
+template <int E_>
+constexpr int small_slab_bytes() { return kSmallPass * kChunk * E_ * 2; }
+
+template <int E_>
+__global__ __launch_bounds__(1024) void route_small_kernel(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias, int T, int H, int K,
+                                                          int32_t* __restrict__ idx, float* __restrict__ gate) {
+  static_assert(E_ % 4 == 0 && E_ <= 16, "few experts");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int kSlab = small_slab_bytes<E_>();
+  constexpr int kPieces = kSmallPass * kChunk * E_ * 2 / 16;  // 16-byte pieces of a full pass
+  constexpr int kPw = kPieces / kWave;                         // per lane
+  static_assert(kPieces % kWave == 0 && kSlab >= kTok * 16 * 4, "slab holds a pass and a partial fragment");
+  const int nw = blockDim.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t0 = blockIdx.x * kTok;
+  const int ntok = min(kTok, T - t0);
+  const int ci = lane & 15, kq = lane >> 4;
+  const int nch = cdiv(H, kChunk);
+  const int cpw = cdiv(nch, nw);
+  const int c_begin = w * cpw, c_end = min(nch, c_begin + cpw);
+  unsigned char* slab = smem + (size_t)w * kSlab;
+
+  const bool hb = bias != nullptr;
+  float bv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = ci + 16 * i;
+    bv[i] = (hb && e < E_) ? bias[e] : 0.f;
+  }
+
+  const __amdgpu_buffer_rsrc_t xs = make_rsrc(x + (int64_t)t0 * H, (uint32_t)ntok * (uint32_t)H * 2u);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(wr, (uint32_t)H * (uint32_t)E_ * 2u);
+  f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int cp = c_begin; cp < c_end; cp += kSmallPass) {
+    const int nc = min(kSmallPass, c_end - cp);
+    // weight rows [32cp, 32(cp + nc)): pieces past the pass or past W_r read 0
+    const int npiece = nc * kChunk * E_ * 2 / 16;
+    const uint32_t wbase = (uint32_t)cp * kChunk * E_ * 2u;
+    uint4 wv[kPw];
+#pragma unroll
+    for (int q = 0; q < kPw; ++q) {
+      const int pc = lane + kWave * q;
+      wv[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                  ws, (wbase + (uint32_t)pc * 16u) | (pc < npiece ? 0u : kOOB), 0, 0));
+    }
+    // token ci, h = 32c + 8kq .. +7 (rows past the block's tokens read 0)
+    uint4 xr[kSmallPass];
+#pragma unroll
+    for (int u = 0; u < kSmallPass; ++u) {
+      const int h = (cp + u) * kChunk + 8 * kq;
+      const bool in = u < nc && h < H;
+      xr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                  xs, ((uint32_t)ci * (uint32_t)H * 2u + (uint32_t)h * 2u) | (in ? 0u : kOOB), 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the pass is issued before the first wait
+    // the whole slab is rewritten (zeros past the pass), so chunks past nc
+    // multiply zeros by zeros and need no branch
+#pragma unroll
+    for (int q = 0; q < kPw; ++q)
+      *reinterpret_cast<uint4*>(slab + (size_t)(lane + kWave * q) * 16) = wv[q];
+    // the slab is this wave's alone: its LDS accesses complete in issue order
+    const uint16_t* wl = reinterpret_cast<const uint16_t*>(slab);
+    const int ce = ci < E_ ? ci : 0;
+#pragma unroll
+    for (int u = 0; u < kSmallPass; ++u) {
+      uint32_t a[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = u * kChunk + 8 * kq + 2 * r;
+        const uint32_t pr = (uint32_t)wl[row * E_ + ce] | ((uint32_t)wl[(row + 1) * E_ + ce] << 16);
+        a[r] = ci < E_ ? pr : 0u;
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(a[0], a[1], a[2], a[3])),
+                                                   __builtin_bit_cast(bf16x8_t, xr[u]), acc, 0, 0, 0);
+    }
+  }
+  // acc[r]: token ci, expert 4kq + r; the fragment goes over the slab's start
+  *reinterpret_cast<f32x4_t*>(slab + (size_t)(ci * 16 + 4 * kq) * 4) = acc;
+  __syncthreads();
+  // fixed-order sum over the waves by the selecting lanes: 16-lane row r of
+  // wave w takes token tt + r, lane j expert j
+  const int rr = lane >> 4;
+  for (int tt = 4 * w; tt < ntok; tt += 4 * nw) {
+    float sc = 0.f;
+    for (int q = 0; q < nw; ++q)
+      sc += reinterpret_cast<const float*>(smem + (size_t)q * kSlab)[(tt + rr) * 16 + ci];
+    float v[4] = {ci < E_ ? nan_to_ninf(hb ? sc + bv[0] : sc) : -INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    bool alive[4] = {ci < E_, false, false, false};
+    topk_softmax_rows_core(v, alive, rr < min(4, ntok - tt), K, idx + (int64_t)(t0 + tt) * K,
+                           gate + (int64_t)(t0 + tt) * K);
+  }
+}
+
 // Sum of the S partial score rows of a token (split order), bias, selection:
 // one wave per token, lane l owning experts l + 64i. The loads of 16 splits
 // are in flight before they are added, in split order.
@@ -568,6 +690,27 @@ void launch_bf16_tf(const RoutePlan& p, const void* x, const void* wr, const flo
   }
 }
 
+// Waves: up to one pass of chunks each, at most 16. LDS: one slab per wave.
+inline int small_waves(int H) {
+  const int nw = cdiv(cdiv(H, kChunk), kSmallPass);
+  return nw < 1 ? 1 : (nw > 16 ? 16 : nw);
+}
+
+template <int E_>
+void launch_small(const void* x, const void* wr, const float* bias, int T, int H, int K, int32_t* idx,
+                  float* gate, hipStream_t s) {
+  const int nw = small_waves(H);
+  const size_t lds = (size_t)nw * small_slab_bytes<E_>();
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_small_kernel<E_>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_done = true;
+  }
+  hipLaunchKernelGGL((route_small_kernel<E_>), dim3(cdiv(T, kTok)), dim3(nw * kWave), lds, s, (const bf16_t*)x,
+                     (const bf16_t*)wr, bias, T, H, K, idx, gate);
+}
+
 template <bool AL>
 void launch_bf16_e(const RoutePlan& p, const void* x, const void* wr, const float* bias, int T, int H,
                    int E, int K, int32_t* idx, float* gate, float* part, hipStream_t s) {
@@ -591,7 +734,12 @@ moe_status launch_route(const void* x, const void* wr, moe_dtype dt, const float
     const RoutePlan p = route_plan(T, H, E);
     const bool al = (H % 8 == 0) && (E % 4 == 0) && aligned16(x) && ((uintptr_t)wr & 7u) == 0;
     float* part = reinterpret_cast<float*>(ws);
-    if (al) launch_bf16_e<true>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
+    if (al && p.S == 1 && E <= 16) {
+      if (E == 4) launch_small<4>(x, wr, bias, T, H, K, idx, gate, s);
+      else if (E == 8) launch_small<8>(x, wr, bias, T, H, K, idx, gate, s);
+      else if (E == 12) launch_small<12>(x, wr, bias, T, H, K, idx, gate, s);
+      else launch_small<16>(x, wr, bias, T, H, K, idx, gate, s);
+    } else if (al) launch_bf16_e<true>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
     else launch_bf16_e<false>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
   } else {
     hipLaunchKernelGGL(route_f32_kernel, dim3(cdiv(T, kTok)), dim3(kWaves * kWave), (size_t)kTok * E * 4, s,

@@ -51,6 +51,12 @@ ROUTE_CASES = [
     ("t8200_e40", 8200, 128, 40, 4, "bf16", False, False),
     ("t16400_e128_bias", 16400, 256, 128, 8, "bf16", False, True),
     ("t8200_e72_ragged", 8200, 66, 72, 3, "bf16", False, False),
+    # at most 16 experts, H not split (one MFMA per chunk, per-wave weight rows):
+    # ragged tokens and H, exact ties, K = E, several passes per wave, E = 4/8/12/16
+    ("t4100_e8_bias", 4100, 264, 8, 2, "bf16", False, True),
+    ("t4096_e16_k4_int", 4096, 1024, 16, 4, "bf16", True, False),
+    ("t4096_e4_keq", 4096, 96, 4, 4, "bf16", False, False),
+    ("t4111_e12_passes_bias", 4111, 8200, 12, 3, "bf16", False, True),
 ]
 
 
@@ -83,11 +89,12 @@ def test_route_parity(case):
     np.testing.assert_allclose(gate.sum(1), 1.0, atol=1e-6)
 
 
-@pytest.mark.parametrize("T,H,E,K", [(48, 512, 8, 2), (64, 4096, 128, 8), (40, 256, 256, 8)])
+@pytest.mark.parametrize("T,H,E,K", [(48, 512, 8, 2), (64, 4096, 128, 8), (40, 256, 256, 8), (4100, 512, 8, 2)])
 def test_route_nan_scores_keep_valid_indices(T, H, E, K):
     """Tokens whose scores are NaN (a NaN in the token row): every slot still
     names a distinct expert in [0, E) (NaN counts as -inf); the other tokens
-    are unaffected. Covers the one-block and the split-H (finish kernel) paths."""
+    are unaffected. Covers the one-block, the split-H (finish kernel) and the
+    few-experts paths."""
     d = configs.layer_inputs("tiny", T=T, H=H, E=E, K=K, F=8, dtype="bf16", wid=47)
     x = d["x"].copy()
     nan_rows = [0, 5, T - 1]
@@ -140,6 +147,7 @@ def test_permute_chunked_path_skewed_with_empty_experts():
     (513, 33, 3, True),      # 1539 pairs: 7 waves, empty experts
     (1025, 4, 4, False),     # 4100 pairs: the smallest chunked case (two launches), long equal runs
     (4096, 8, 2, False),     # 8192 pairs: the prefill pair count, 8 chunks
+    (2731, 8, 3, True),      # 8193 pairs: ragged last chunk of one pair, empty experts
     (1250, 256, 4, False),   # 5000 pairs: chunked, ragged last chunk, E = 256
     (2048, 128, 8, False),   # decode T=256-like pair count x 8
     (12800, 256, 4, False),  # 51200 pairs x 256 experts: more counts than one LDS stage (three launches)
