@@ -45,7 +45,8 @@ bool any_dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt =
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct LayerWs {
-  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, gmm_ws, xp, hm, total;
+  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, gmm_ws, cnt, xp, hm, total;
+  int ncnt;  // ints at cnt: each GEMM's counters, cleared by the permute launch
 };
 
 LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
@@ -63,6 +64,9 @@ LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
   {
     const size_t g1 = gmm_ws_bytes(dt, E, (int)A, H, F), g2 = gmm_ws_bytes(dt, E, (int)A, F, H);
     L.gmm_ws = o; o += round256(g1 > g2 ? g1 : g2);  // shared by the two GEMMs (same stream)
+    // each GEMM's own counters, so both are cleared by the one permute launch
+    L.ncnt = (g1 || g2) ? 2 * gmm_counter_ints() : 0;
+    L.cnt = o; o += round256((size_t)L.ncnt * 4);
   }
   L.xp = o; o += round256((size_t)A * H * es);  // permuted rows; reused for GEMM 2 output
   // hidden activations; before GEMM 1 writes them the router's split-H partials live here
@@ -151,21 +155,27 @@ moe_status layer_run(const void* x, const void* w_router, const float* bias, con
   MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s));
   void* gws = base + L.gmm_ws;  // sized for whichever GEMM needs more (possibly none)
   void* gws1 = gmm_ws_bytes(dt, E, A, H, F) ? gws : nullptr;
+  // the GEMMs' counters, cleared by the permute launch (no clearing launch per GEMM)
+  int* cnt1 = L.ncnt ? (int*)(base + L.cnt) : nullptr;
+  int* cnt2 = L.ncnt ? cnt1 + L.ncnt / 2 : nullptr;
   if ((int64_t)T * H * dtype_size(dt) < (1ll << 31)) {
     // dispatch inside GEMM 1: its row r is token perm_src[r] / K
     MOE_TRY(launch_permute(idx, nullptr, dt, T, H, E, K, counts, offsets, psrc, pdst, nullptr,
-                           base + L.perm_ws, s));
+                           base + L.perm_ws, s, cnt1, L.ncnt));
     MOE_TRY(launch_gmm(x, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s,
-                       RowMap{psrc, K, T}));
+                       RowMap{psrc, K, T}, cnt1));
   } else {
-    MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s));
-    MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s));
+    MOE_TRY(launch_permute(idx, x, dt, T, H, E, K, counts, offsets, psrc, pdst, xp, base + L.perm_ws, s,
+                           cnt1, L.ncnt));
+    MOE_TRY(launch_gmm(xp, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s, RowMap{},
+                       cnt1));
   }
   void* gws2 = gmm_ws_bytes(dt, E, A, F, H) ? gws : nullptr;
   // GEMM 2 into the grouped rows, then the weighted combine (gates applied
   // once, in fp32, in the combine; storing gated rows from GEMM 2's epilogue
   // and summing K rows moves the same bytes and measured 1-5% slower)
-  MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, gws2, s));
+  MOE_TRY(launch_gmm(hm, dt, nullptr, w2, nullptr, offsets, E, A, F, H, MOE_ACT_NONE, xp, dt, gws2, s, RowMap{},
+                     cnt2));
   MOE_TRY(launch_combine(xp, dt, pdst, gate, T, K, H, y, s));
   return MOE_OK;
 }

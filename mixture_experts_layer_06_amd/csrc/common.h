@@ -90,9 +90,11 @@ size_t route_ws_bytes(int T, int H, int E, moe_dtype dt);
 moe_status launch_route(const void* x, const void* wr, moe_dtype dt, const float* bias, int T, int H,
                         int E, int K, int32_t* idx, float* gate, void* ws, hipStream_t s);
 size_t permute_ws_bytes(int T, int E, int K);
+// zero, nzero: ints that the index path's first kernel also sets to 0 (the
+// grouped GEMMs' counters when a later launch on the stream needs them clear).
 moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T, int H, int E, int K,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
-                          void* x_perm, void* ws, hipStream_t s);
+                          void* x_perm, void* ws, hipStream_t s, int* zero = nullptr, int nzero = 0);
 // Row maps of a grouped GEMM. Input: grouped row r reads row src[r] / div of
 // an input with `rows` rows (src == nullptr: row r itself); row_scale, when
 // set (E4M3 inputs), is a per-row activation scale indexed like the rows of
@@ -108,6 +110,7 @@ struct RowMap {
   const float* row_scale = nullptr;
 };
 size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N);
+int gmm_counter_ints();  // counters of one bf16 ping-pong GEMM launch (split parts and queues)
 int probe_device_cus();  // compute units of the current device (0 when the query fails)
 moe_status launch_fetch_probe(const void* buf, size_t bytes, int mode, int shared_window, int kb_per_wave,
                               unsigned long long* cycles, int ncu, hipStream_t s);
@@ -115,7 +118,10 @@ moe_status launch_mfma_probe(int fp8, int iters, float* sink, unsigned long long
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
                       moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s,
-                      RowMap gx = RowMap{});
+                      RowMap gx = RowMap{}, int* cnt_zeroed = nullptr);
+// cnt_zeroed: gmm_counter_ints() counters that an earlier launch on the
+// stream has set to 0; the bf16 ping-pong GEMM then uses them in place of the
+// counters in ws and launches no kernel to clear them.
 // One grouped GEMM's operands (the arguments of launch_gmm).
 struct GmmCall {
   const void* a;

@@ -2269,7 +2269,7 @@ inline int hin_b_of(int Hin) { return Hin * 2; }  // bf16 bytes per activation r
 template <class C>
 moe_status launch_pp(const void* a, const float* as, const void* w, const float* ws,
                      const int32_t* offsets, int e, int A, int Hin, int N, int relu, void* out,
-                     void* split, hipStream_t s, RowMap gx) {
+                     void* split, hipStream_t s, RowMap gx, int* cnt_zeroed) {
   static_assert(C::kBM == 256 && C::kBN == 256, "split scratch is sized for 256 x 256 tiles");
   static bool attr_done = false;
   if (!attr_done) {
@@ -2280,6 +2280,8 @@ moe_status launch_pp(const void* a, const float* as, const void* w, const float*
   const int ncu = device_cus();
   float* sws = reinterpret_cast<float*>(split);
   int* cnt = sws ? reinterpret_cast<int*>(sws + split_ws_floats(ncu)) : nullptr;
+  const bool zeroed = cnt && cnt_zeroed;  // counters cleared by an earlier launch
+  if (zeroed) cnt = cnt_zeroed;
   const int64_t mt_max = cdiv64(A, C::kBM) + (e < A ? e : A);
   const int64_t blocks = mt_max * cdiv64(N, C::kBN) + (sws ? 3 * (int64_t)ncu / 4 : 0);
   const int64_t grid = cdiv64(blocks, 8) * 8;
@@ -2296,14 +2298,14 @@ moe_status launch_pp(const void* a, const float* as, const void* w, const float*
                                 hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds + kTabLds);
       pattr_done = true;
     }
-    hipLaunchKernelGGL(split_reset_kernel, dim3(1), dim3(256), 0, s, cnt, ncu + 8);
+    if (!zeroed) hipLaunchKernelGGL(split_reset_kernel, dim3(1), dim3(256), 0, s, cnt, ncu + 8);
     const int64_t pgrid = grid < ncu ? grid : ncu;
     hipLaunchKernelGGL(gmm_ppd_kernel<C>, dim3((unsigned)pgrid), dim3(C::kNT), C::kLds + kTabLds, s,
                        (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N, relu,
                        (bf16_t*)out, sws, cnt, ncu, gx, cnt + ncu);
     return launch_status();
   }
-  if (cnt) hipLaunchKernelGGL(split_reset_kernel, dim3(1), dim3(256), 0, s, cnt, ncu);
+  if (cnt && !zeroed) hipLaunchKernelGGL(split_reset_kernel, dim3(1), dim3(256), 0, s, cnt, ncu);
   hipLaunchKernelGGL(gmm_pp_kernel<C>, dim3((unsigned)grid), dim3(C::kNT), C::kLds, s,
                      (const unsigned char*)a, (const unsigned char*)w, as, ws, offsets, e, A, Hin, N,
                      relu, (bf16_t*)out, sws, cnt, ncu, gx);
@@ -2406,12 +2408,15 @@ GmmPath gmm_path(moe_dtype in_dt, int e, int A, int Hin, int N) {
 size_t gmm_ws_bytes(moe_dtype in_dt, int e, int A, int Hin, int N) {
   if (A == 0 || gmm_path(in_dt, e, A, Hin, N) != GmmPath::PP) return 0;
   const int ncu = device_cus();
-  return split_ws_floats(ncu) * sizeof(float) + (size_t)(ncu + 8) * sizeof(int);  // + the persistent kernel's queues
+  return split_ws_floats(ncu) * sizeof(float) + (size_t)gmm_counter_ints() * sizeof(int);
 }
+
+int gmm_counter_ints() { return device_cus() + 8; }  // split counters, then the persistent kernel's queues
 
 moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, const void* w,
                       const float* w_scale, const int32_t* offsets, int e, int A, int Hin, int N,
-                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s, RowMap gx) {
+                      moe_act act, void* out, moe_dtype out_dt, void* ws, hipStream_t s, RowMap gx,
+                      int* cnt_zeroed) {
   if (A == 0) return MOE_OK;
   const int relu = act == MOE_ACT_RELU;
   if (in_dt == MOE_F32) {
@@ -2437,7 +2442,7 @@ moe_status launch_gmm(const void* a, moe_dtype in_dt, const float* a_scale, cons
                   ((int64_t)Hin * N * elem < (1ll << 31));
   constexpr int WM = kTiledWavesM, WN = kTiledWavesN;
   if (elem == 2 && al && N % 16 == 0)
-    return launch_pp<PpBf16>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s, gx);
+    return launch_pp<PpBf16>(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, ws, s, gx, cnt_zeroed);
   if (elem == 1 && al && N % 16 == 0)
     return launch_pp8w(a, a_scale, w, w_scale, offsets, e, A, Hin, N, relu, out, s, gx);
   if (elem == 2) {

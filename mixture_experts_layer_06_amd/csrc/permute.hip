@@ -114,7 +114,9 @@ __device__ __forceinline__ void rank_regs(const int ev[PL], int begin, int end, 
 // One block: whole index path for A <= kBlockA (see the file header).
 __global__ __launch_bounds__(kBlockWaves * kWave) void permute_block_kernel(
     const int32_t* __restrict__ idx, int A, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ perm_dst) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ perm_dst,
+    int* __restrict__ zero, int nzero) {
+  for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   constexpr int PL = kBlockA / kBlockWaves / kWave;  // pairs per lane (segments of <= kBlockA / nw)
   __shared__ int hist[kBlockWaves][256];  // count, then first row, per (wave, expert)
   __shared__ int tot[256];
@@ -170,8 +172,11 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void permute_block_kernel(
 // Chunk c: per-expert counts of its kChunk pairs (LDS atomics: counts only,
 // so the order in which they land does not matter).
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx, int A,
-                                                            int E, int32_t* __restrict__ chunk_counts) {
+                                                            int E, int32_t* __restrict__ chunk_counts,
+                                                            int* __restrict__ zero, int nzero) {
   constexpr int PT = kChunk / 256;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   __shared__ int hist[256];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   const int begin = blockIdx.x * kChunk;
@@ -392,19 +397,20 @@ size_t permute_ws_bytes(int T, int E, int K) {
 
 moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T, int H, int E, int K,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
-                          void* x_perm, void* ws, hipStream_t s) {
+                          void* x_perm, void* ws, hipStream_t s, int* zero, int nzero) {
+  if (!zero) nzero = 0;
   const int A = T * K;
   if (A <= kBlockA) {
     // about 256 pairs per wave, at most kBlockWaves waves
     int nw = cdiv(A, 256);
     nw = nw < 1 ? 1 : (nw > kBlockWaves ? kBlockWaves : nw);
     hipLaunchKernelGGL(permute_block_kernel, dim3(1), dim3(nw * kWave), 0, s, idx, A, E, counts,
-                       offsets, perm_src, perm_dst);
+                       offsets, perm_src, perm_dst, zero, nzero);
   } else {
     const int nch = cdiv(A, kChunk);
     int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);
     int32_t* chunk_base = chunk_counts + (int64_t)nch * E;
-    hipLaunchKernelGGL(permute_count_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts);
+    hipLaunchKernelGGL(permute_count_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts, zero, nzero);
     if ((int64_t)nch * E <= kScanInts) {
       // every chunk block scans the (staged) counts itself: two launches
       hipLaunchKernelGGL(permute_rank_scan_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts, nch,
