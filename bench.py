@@ -870,7 +870,7 @@ def cpu_baseline_tokens(run, T, target_s, what):
             break
         n = min(T, max(n + 1, int(n * min(8.0, (target_s / 2) / max(dt, 1e-3)))))
     return dict(cpu_info(nth), value=n / dt, unit="tokens/s", kind="oracle",
-                sample=f"{what} on the first {n} of {T} tokens, {dt:.1f} s")
+                sample=f"{what} on the first {n} of {T} tokens, {dt:.1f} s (growing runs {spent:.1f} s in all)")
 
 
 def cpu_baseline_layer(host, target_s):
