@@ -7,7 +7,7 @@
 // that page's constraints, adapted to one GPU that holds every expert.
 #include <mutex>
 
-#include "common.h"
+#include "dispatch.h"
 
 using namespace moe;
 
@@ -45,7 +45,7 @@ bool any_dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt =
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct LayerWs {
-  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, gmm_ws, cnt, xp, hm, total;
+  size_t idx, gate, counts, offsets, psrc, pdst, perm_ws, bcnt, gmm_ws, cnt, xp, hm, total;
   int ncnt;  // ints at cnt: each GEMM's counters, cleared by the permute launch
 };
 
@@ -61,6 +61,8 @@ LayerWs layer_ws_layout(int T, int H, int E, int K, int F, moe_dtype dt) {
   L.psrc = o; o += round256(A * 4);
   L.pdst = o; o += round256(A * 4);
   L.perm_ws = o; o += round256(permute_ws_bytes(T, E, K));
+  // the router's per-block expert counts (16-token blocks; few experts only)
+  L.bcnt = o; o += round256(E <= 16 ? (size_t)((T + 15) / 16) * E * 4 : 0);
   {
     const size_t g1 = gmm_ws_bytes(dt, E, (int)A, H, F), g2 = gmm_ws_bytes(dt, E, (int)A, F, H);
     L.gmm_ws = o; o += round256(g1 > g2 ? g1 : g2);  // shared by the two GEMMs (same stream)
@@ -152,16 +154,25 @@ moe_status layer_run(const void* x, const void* w_router, const float* bias, con
   void* xp = base + L.xp;
   void* hm = base + L.hm;
   const int A = T * K;
-  MOE_TRY(launch_route(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s));
+  // the router also writes its per-block expert counts where it can; the
+  // dispatch then ranks from them in one launch
+  int32_t* bcnt = E <= 16 ? (int32_t*)(base + L.bcnt) : nullptr;
+  int btok = 0;
+  MOE_TRY(launch_route_counted(x, w_router, dt, bias, T, H, E, K, idx, gate, hm, s, bcnt, &btok));
   void* gws = base + L.gmm_ws;  // sized for whichever GEMM needs more (possibly none)
   void* gws1 = gmm_ws_bytes(dt, E, A, H, F) ? gws : nullptr;
   // the GEMMs' counters, cleared by the permute launch (no clearing launch per GEMM)
   int* cnt1 = L.ncnt ? (int*)(base + L.cnt) : nullptr;
   int* cnt2 = L.ncnt ? cnt1 + L.ncnt / 2 : nullptr;
   if ((int64_t)T * H * dtype_size(dt) < (1ll << 31)) {
-    // dispatch inside GEMM 1: its row r is token perm_src[r] / K
-    MOE_TRY(launch_permute(idx, nullptr, dt, T, H, E, K, counts, offsets, psrc, pdst, nullptr,
-                           base + L.perm_ws, s, cnt1, L.ncnt));
+    // dispatch inside GEMM 1: its row r is token perm_src[r] / K. Above one
+    // block's worth of pairs the index path takes two launches unless the
+    // router's counts replace its counting launch.
+    if (btok > 0 && A > kPermuteBlockPairs && permute_counted_fits(T, E, K, btok))
+      MOE_TRY(launch_permute_counted(idx, T, E, K, bcnt, btok, counts, offsets, psrc, pdst, s, cnt1, L.ncnt));
+    else
+      MOE_TRY(launch_permute(idx, nullptr, dt, T, H, E, K, counts, offsets, psrc, pdst, nullptr,
+                             base + L.perm_ws, s, cnt1, L.ncnt));
     MOE_TRY(launch_gmm(x, dt, nullptr, w1, nullptr, offsets, E, A, H, F, act, hm, dt, gws1, s,
                        RowMap{psrc, K, T}, cnt1));
   } else {

@@ -21,13 +21,13 @@
 //   launch sits between the two instead.
 // Data path: one block per token reads its row once (16-byte vectors when
 // the row pitch allows) and writes it to its K destination rows.
-#include "common.h"
+#include "dispatch.h"
 
 namespace moe {
 namespace {
 
 constexpr int kChunk = 1024;   // pairs per chunk
-constexpr int kBlockA = 4096;   // one-block path up to this many pairs
+constexpr int kBlockA = kPermuteBlockPairs;  // one-block path up to this many pairs
 constexpr int kBlockWaves = 16;
 constexpr int kScanInts = 12288;  // (chunk, expert) counts a block stages in LDS at once
 
@@ -290,51 +290,67 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
   rank_regs<PL>(ev, begin, end, hist[w], perm_src, perm_dst);
 }
 
-// Chunk c when all (chunk, expert) counts fit in LDS: the scan of
-// permute_scan_kernel done by every block for itself. The block stages the
-// counts, thread e sums expert e over all chunks (its total) and over the
-// chunks before c (its prefix), an exclusive scan over experts gives the
-// expert offsets, and block 0 writes counts and offsets; then the four waves
-// count and rank the chunk's quarters as permute_rank_kernel does.
+// Chunk c when all count rows fit in LDS: the scan of permute_scan_kernel
+// done by every block for itself. Row r of chunk_counts holds the per-expert
+// counts of pairs [r * chunk / R, (r + 1) * chunk / R) (R = rows per chunk:
+// 1 after permute_count_kernel; more when the router wrote them per block of
+// tokens). The block stages the rows, thread e sums expert e over all rows
+// (its total) and over the rows before chunk c (its prefix), an exclusive
+// scan over experts gives the expert offsets, and block 0 writes counts and
+// offsets (and clears zero[0:nzero]); then the four waves count and rank the
+// chunk's quarters as permute_rank_kernel does (chunk <= kChunk pairs, a
+// multiple of 4).
 __global__ __launch_bounds__(256) void permute_rank_scan_kernel(const int32_t* __restrict__ idx, int A, int E,
                                                                 const int32_t* __restrict__ chunk_counts,
-                                                                int nchunks, int32_t* __restrict__ counts,
+                                                                int nrows, int R, int chunk,
+                                                                int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ perm_src,
-                                                                int32_t* __restrict__ perm_dst) {
+                                                                int32_t* __restrict__ perm_dst,
+                                                                int* __restrict__ zero, int nzero) {
   constexpr int kQuarter = kChunk / 4;
   constexpr int PL = kQuarter / kWave;
   __shared__ int cc[kScanInts];
   __shared__ int hist[4][256];
+  __shared__ int part[2][256];
   __shared__ int wsum[4];
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid & (kWave - 1);
   const int c = blockIdx.x;
-  const int begin = min(A, c * kChunk + w * kQuarter);
-  const int end = min(A, begin + kQuarter);
+  const int quarter = chunk / 4;
+  const int begin = min(A, c * chunk + w * quarter);
+  const int end = min(A, begin + quarter);
   int ev[PL];
   load_range<PL>(idx, begin, end, E, ev);  // in flight while the counts are staged
-  load_scan_tile(chunk_counts, nchunks * E, cc);
+  if (c == 0)
+    for (int i = tid; i < nzero; i += blockDim.x) zero[i] = 0;
+  load_scan_tile(chunk_counts, nrows * E, cc);
+  const int rows_before = c * R;
   __syncthreads();
-  int tot = 0, pre = 0;
-  if (tid < E) {
-    int c0 = 0;
-    for (; c0 + 8 <= nchunks; c0 += 8) {
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = cc[(c0 + u) * E + tid];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        tot += v[u];
-        pre += c0 + u < c ? v[u] : 0;
+  // expert e's total and prefix over the rows: thread (e, g) sums rows
+  // g, g + G, ... (G = 256 / E groups), then thread e adds the G sums
+  // (integers: the order does not change them)
+  const int G = 256 / E;
+  {
+    int t = 0, p = 0;
+    if (tid < G * E) {
+      const int e = tid % E;
+      for (int r = tid / E; r < nrows; r += G) {
+        const int v = cc[r * E + e];
+        t += v;
+        p += r < rows_before ? v : 0;
       }
     }
-    for (; c0 < nchunks; ++c0) {
-      const int v = cc[c0 * E + tid];
-      tot += v;
-      pre += c0 < c ? v : 0;
-    }
+    part[0][tid] = t;
+    part[1][tid] = p;
   }
+  __syncthreads();
+  int tot = 0, pre = 0;
+  if (tid < E)
+    for (int g = 0; g < G; ++g) {
+      tot += part[0][g * E + tid];
+      pre += part[1][g * E + tid];
+    }
   const int incl = wave_incl_scan(tot);
   if (lane == kWave - 1) wsum[w] = incl;
   count_regs<PL>(ev, begin, end, hist[w]);
@@ -413,8 +429,8 @@ moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T
     hipLaunchKernelGGL(permute_count_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts, zero, nzero);
     if ((int64_t)nch * E <= kScanInts) {
       // every chunk block scans the (staged) counts itself: two launches
-      hipLaunchKernelGGL(permute_rank_scan_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts, nch,
-                         counts, offsets, perm_src, perm_dst);
+      hipLaunchKernelGGL(permute_rank_scan_kernel, dim3(nch), dim3(256), 0, s, idx, A, E, chunk_counts, nch, 1,
+                         kChunk, counts, offsets, perm_src, perm_dst, nullptr, 0);
     } else {
       hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, A,
                          chunk_base, counts, offsets);
@@ -438,6 +454,29 @@ moe_status launch_permute(const int32_t* idx, const void* x, moe_dtype dt, int T
     else
       hipLaunchKernelGGL(permute_rows_kernel<1>, dim3(grid), dim3(256), 0, s, xs, rb, T, K, perm_dst, xd);
   }
+  return launch_status();
+}
+
+// Rows of tok_per_row tokens (tok_per_row * K pairs); R whole rows per chunk
+// of at most kChunk pairs.
+bool permute_counted_fits(int T, int E, int K, int tok_per_row) {
+  if (T <= 0 || tok_per_row <= 0 || tok_per_row % 4 != 0 || E > 256) return false;
+  const int64_t rp = (int64_t)tok_per_row * K;
+  return rp <= kChunk && (int64_t)cdiv(T, tok_per_row) * E <= kScanInts;
+}
+
+moe_status launch_permute_counted(const int32_t* idx, int T, int E, int K, const int32_t* row_counts,
+                                  int tok_per_row, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                                  int32_t* perm_dst, hipStream_t s, int* zero, int nzero) {
+  if (!permute_counted_fits(T, E, K, tok_per_row)) return MOE_ERR_BAD_SHAPE;
+  const int A = T * K;
+  const int rp = tok_per_row * K;
+  const int R = kChunk / rp;
+  const int chunk = R * rp;  // a multiple of 4, as tok_per_row is
+  const int nrows = cdiv(T, tok_per_row);
+  if (!zero) nzero = 0;
+  hipLaunchKernelGGL(permute_rank_scan_kernel, dim3(cdiv(A, chunk)), dim3(256), 0, s, idx, A, E, row_counts,
+                     nrows, R, chunk, counts, offsets, perm_src, perm_dst, zero, nzero);
   return launch_status();
 }
 

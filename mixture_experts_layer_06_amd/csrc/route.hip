@@ -34,7 +34,7 @@
 // holding it, the lowest index, so larger score wins and equal scores go to
 // the lower expert index. With at most 64 experts a wave selects four
 // tokens at once, one per 16-lane row.
-#include "common.h"
+#include "dispatch.h"
 
 
 namespace moe {
@@ -161,9 +161,10 @@ __device__ __forceinline__ int row_min(int v) {
 }
 
 // v[i], alive[i]: this lane's scores (bias added, NaN as -inf) of experts
-// j + 16i and whether they exist; live: row r names a token.
+// j + 16i and whether they exist; live: row r names a token. hist (LDS, or
+// nullptr): each selected expert's count is incremented.
 __device__ __forceinline__ void topk_softmax_rows_core(float (&v)[4], bool (&alive)[4], bool live, int K,
-                                                       int32_t* idx_out, float* gate_out) {
+                                                       int32_t* idx_out, float* gate_out, int* hist = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane >> 4, j = lane & 15;
   float sv[8];
@@ -208,6 +209,7 @@ __device__ __forceinline__ void topk_softmax_rows_core(float (&v)[4], bool (&ali
   if (live && j < K) {
     idx_out[r * K + j] = my_e;
     gate_out[r * K + j] = mine * inv;
+    if (hist) atomicAdd(&hist[my_e], 1);
   }
 }
 
@@ -453,6 +455,9 @@ __global__ __launch_bounds__(G * TF <= 2 ? 1024 : 512) void route_bf16_kernel(
 // waves' partial scores (one 16 x 16 fragment each, written over the start
 // of the wave's own slab) are summed in wave order by the selecting lanes
 // themselves: 16-lane row r of wave w takes token 4w + r, lane j expert j.
+// With blk_counts set the block also writes how many of its selections went
+// to each expert (row blockIdx.x of E counts), the per-chunk counts of the
+// dispatch.
 constexpr int kSmallPass = 8;  // chunks per pass
 
 template <int E_>
@@ -462,9 +467,12 @@ template <int E_>
 __global__ __launch_bounds__(1024) void route_small_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wr,
                                                           const float* __restrict__ bias, int T, int H, int K,
-                                                          int32_t* __restrict__ idx, float* __restrict__ gate) {
+                                                          int32_t* __restrict__ idx, float* __restrict__ gate,
+                                                          int32_t* __restrict__ blk_counts) {
   static_assert(E_ % 4 == 0 && E_ <= 16, "few experts");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int hist[16];  // the block's selections per expert (blk_counts != nullptr)
+  if (threadIdx.x < 16) hist[threadIdx.x] = 0;
   constexpr int kSlab = small_slab_bytes<E_>();
   constexpr int kPieces = kSmallPass * kChunk * E_ * 2 / 16;  // 16-byte pieces of a full pass
   constexpr int kPw = kPieces / kWave;                         // per lane
@@ -547,7 +555,11 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const bf16_t* __restr
     float v[4] = {ci < E_ ? nan_to_ninf(hb ? sc + bv[0] : sc) : -INFINITY, -INFINITY, -INFINITY, -INFINITY};
     bool alive[4] = {ci < E_, false, false, false};
     topk_softmax_rows_core(v, alive, rr < min(4, ntok - tt), K, idx + (int64_t)(t0 + tt) * K,
-                           gate + (int64_t)(t0 + tt) * K);
+                           gate + (int64_t)(t0 + tt) * K, blk_counts ? hist : nullptr);
+  }
+  if (blk_counts) {
+    __syncthreads();
+    if (threadIdx.x < E_) blk_counts[(int64_t)blockIdx.x * E_ + threadIdx.x] = hist[threadIdx.x];
   }
 }
 
@@ -698,17 +710,18 @@ inline int small_waves(int H) {
 
 template <int E_>
 void launch_small(const void* x, const void* wr, const float* bias, int T, int H, int K, int32_t* idx,
-                  float* gate, hipStream_t s) {
+                  float* gate, int32_t* blk_counts, hipStream_t s) {
   const int nw = small_waves(H);
   const size_t lds = (size_t)nw * small_slab_bytes<E_>();
   static bool attr_done = false;
   if (!attr_done) {
+    // 16 slabs at most; the kernel also has a small static array
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_small_kernel<E_>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 16 * small_slab_bytes<E_>());
     attr_done = true;
   }
   hipLaunchKernelGGL((route_small_kernel<E_>), dim3(cdiv(T, kTok)), dim3(nw * kWave), lds, s, (const bf16_t*)x,
-                     (const bf16_t*)wr, bias, T, H, K, idx, gate);
+                     (const bf16_t*)wr, bias, T, H, K, idx, gate, blk_counts);
 }
 
 template <bool AL>
@@ -729,16 +742,25 @@ size_t route_ws_bytes(int T, int H, int E, moe_dtype dt) {
 
 moe_status launch_route(const void* x, const void* wr, moe_dtype dt, const float* bias, int T, int H,
                         int E, int K, int32_t* idx, float* gate, void* ws, hipStream_t s) {
+  return launch_route_counted(x, wr, dt, bias, T, H, E, K, idx, gate, ws, s, nullptr, nullptr);
+}
+
+moe_status launch_route_counted(const void* x, const void* wr, moe_dtype dt, const float* bias, int T, int H,
+                                int E, int K, int32_t* idx, float* gate, void* ws, hipStream_t s,
+                                int32_t* blk_counts, int* blk_tokens) {
+  if (blk_tokens) *blk_tokens = 0;
   if (T == 0) return MOE_OK;
   if (dt == MOE_BF16) {
     const RoutePlan p = route_plan(T, H, E);
     const bool al = (H % 8 == 0) && (E % 4 == 0) && aligned16(x) && ((uintptr_t)wr & 7u) == 0;
     float* part = reinterpret_cast<float*>(ws);
     if (al && p.S == 1 && E <= 16) {
-      if (E == 4) launch_small<4>(x, wr, bias, T, H, K, idx, gate, s);
-      else if (E == 8) launch_small<8>(x, wr, bias, T, H, K, idx, gate, s);
-      else if (E == 12) launch_small<12>(x, wr, bias, T, H, K, idx, gate, s);
-      else launch_small<16>(x, wr, bias, T, H, K, idx, gate, s);
+      if (!blk_tokens) blk_counts = nullptr;
+      if (E == 4) launch_small<4>(x, wr, bias, T, H, K, idx, gate, blk_counts, s);
+      else if (E == 8) launch_small<8>(x, wr, bias, T, H, K, idx, gate, blk_counts, s);
+      else if (E == 12) launch_small<12>(x, wr, bias, T, H, K, idx, gate, blk_counts, s);
+      else launch_small<16>(x, wr, bias, T, H, K, idx, gate, blk_counts, s);
+      if (blk_counts) *blk_tokens = kTok;
     } else if (al) launch_bf16_e<true>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
     else launch_bf16_e<false>(p, x, wr, bias, T, H, E, K, idx, gate, part, s);
   } else {

@@ -39,6 +39,13 @@ LAYER_CASES = [
     ("skewed_small", dict(name="skewed", T=256)),
     ("decode_t16", dict(name="decode", T=16, H=1024, F=512, wid=61)),
     ("prefill_small", dict(name="prefill", T=128, H=512, F=1024, wid=62)),
+    # more than 4096 pairs and at most 16 experts: the router's per-block
+    # counts feed a one-launch dispatch (ragged last block, chunks of 21 or
+    # 64 blocks, K = E)
+    ("counted_e8_k3", dict(name="tiny", T=4100, H=256, E=8, K=3, F=256, dtype="bf16", wid=63)),
+    ("counted_e16_k1_bias", dict(name="tiny", T=5000, H=128, E=16, K=1, F=128, dtype="bf16", bias=True,
+                                 wid=64)),
+    ("counted_e4_k4", dict(name="tiny", T=4097, H=64, E=4, K=4, F=128, dtype="bf16", wid=65)),
 ]
 
 
