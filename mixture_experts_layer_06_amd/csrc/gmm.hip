@@ -709,7 +709,10 @@ struct PpCfg {
   static constexpr int kLdsW = 32 * BN * 2;                 // weights per slot
   static constexpr int kStage = kLdsX + kLdsW;
   static constexpr int kDummy = STAGES * kStage;            // 1 KB that soaks up unused DMA
-  static constexpr int kLds = kDummy + 1024;
+  static constexpr int kRing = kDummy + 1024;
+  static constexpr int kOutRow = BN * 2 + 16;                // bytes per row of the staged output tile
+  static constexpr int kOut = (BM + kFold) * kOutRow;
+  static constexpr int kLds = kRing > kOut ? kRing : kOut;  // 148.5 KB for 256 x 256
   static constexpr int kADma = kLdsA / 1024 / (kNT / 64);  // 1 KB DMA ops per wave per slot
   static constexpr int kWDma = kLdsW / 1024 / (kNT / 64);
   static constexpr int kPerStage = kADma + kWDma;          // vmcnt units per slot per lane
@@ -983,24 +986,66 @@ __device__ __forceinline__ bool pp_block(
                                                 pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
   };
   if (wk.S == 1) {
-    if (!wave_active) return true;
-    auto store_all = [&](auto M) {
+    // The output tile goes through LDS (rows of kOutRow bytes over the
+    // ring, which every wave has finished with): each lane writes its 16
+    // scaled, activated, gated bf16 columns per fragment, then 32 lanes per
+    // tile row store whole 512-byte rows, so every global store covers full
+    // cache lines instead of 64-byte pieces of 16 rows.
+    __syncthreads();
+    auto stage_all = [&](auto M) {
+      constexpr int kM = decltype(M)::value;
 #pragma unroll
       for (int f = 0; f < C::kFI + 1; ++f) {
         if (f == C::kFI && !extra) continue;  // compile-time f keeps the accumulators in registers
+        const int ml = frag_row(f);
+        if (ml >= tile.rows) continue;
+        const OutRow orow = out_row(gx, tile.row0 + ml, A);
+        if (orow.row < 0) continue;
+        unsigned char* lrow = smem + ml * C::kOutRow;
 #pragma unroll
         for (int g = 0; g < C::kFG; ++g) {
           float a16[16];
           frag_acc(f, g, a16);
-          store_out(f, g, a16, M);
+          float v[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            float t = a16[q] * sc;
+            if (kM & 1) t = t < 0.f ? 0.f : t;
+            if (kM & 2) t *= orow.gate;
+            v[q] = t;
+          }
+          uint4* o = reinterpret_cast<uint4*>(lrow + (wn * C::kWN + g * 64 + 16 * kq) * 2);
+          o[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7]));
+          o[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+                            pack_bf16x2(v[14], v[15]));
         }
       }
     };
-    const int m = (relu ? 1 : 0) | (gx.dst != nullptr && gx.gate != nullptr ? 2 : 0);
-    if (m == 0) store_all(std::integral_constant<int, 0>{});
-    else if (m == 1) store_all(std::integral_constant<int, 1>{});
-    else if (m == 2) store_all(std::integral_constant<int, 2>{});
-    else store_all(std::integral_constant<int, 3>{});
+    if (wave_active) {
+      const int m = (relu ? 1 : 0) | (gx.dst != nullptr && gx.gate != nullptr ? 2 : 0);
+      if (m == 0) stage_all(std::integral_constant<int, 0>{});
+      else if (m == 1) stage_all(std::integral_constant<int, 1>{});
+      else if (m == 2) stage_all(std::integral_constant<int, 2>{});
+      else stage_all(std::integral_constant<int, 3>{});
+    }
+    __syncthreads();
+    // 16 bytes (8 columns) per lane; rows past the tile's rows, rows without
+    // a destination and columns past N are skipped (N is a multiple of 16)
+    constexpr int kLanesRow = C::kBN * 2 / 16;
+    constexpr int kPasses = (C::kBM + C::kFold) * kLanesRow / C::kNT;
+    static_assert((C::kBM + C::kFold) * kLanesRow % C::kNT == 0, "whole passes");
+    const int nrows = tile.rows < C::kBM + C::kFold ? tile.rows : C::kBM + C::kFold;
+#pragma unroll 1
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int idx = ps * C::kNT + tid;
+      const int ml = idx / kLanesRow, c = (idx % kLanesRow) * 8;
+      if (ml >= nrows || tile.n0 + c >= N) continue;
+      const OutRow orow = out_row(gx, tile.row0 + ml, A);
+      if (orow.row < 0) continue;
+      *reinterpret_cast<uint4*>(out + orow.row * N + tile.n0 + c) =
+          *reinterpret_cast<const uint4*>(smem + ml * C::kOutRow + c * 2);
+    }
     return true;
   }
   // Split tile: every part stores its fp32 partial tile [BM + kFold][BN];
