@@ -17,7 +17,7 @@
 //    and memory phases between barriers (ping-pong). Weights are read 8 rows
 //    x 4 columns per lane and transposed with v_perm_b32, so MFMA j's row i
 //    is output column 4i + j and each lane ends with 16 consecutive output
-//    columns (32-byte stores).
+//    columns; the output tile is staged in LDS and stored as whole rows.
 //    An expert's last row piece of at most 32 rows rides on the tile before
 //    it, and a small last round of tiles is split 4 ways along K.
 //  * gmm_pp8_kernel (E4M3, aligned): the same scheme on 16x16x128 f8f6f4
@@ -708,8 +708,7 @@ struct PpCfg {
   static constexpr int kLdsX = (BM + kFold) * kDmaKB;       // ... with the folded tail rows
   static constexpr int kLdsW = 32 * BN * 2;                 // weights per slot
   static constexpr int kStage = kLdsX + kLdsW;
-  static constexpr int kDummy = STAGES * kStage;            // 1 KB that soaks up unused DMA
-  static constexpr int kRing = kDummy + 1024;
+  static constexpr int kRing = STAGES * kStage;
   static constexpr int kOutRow = BN * 2 + 16;                // bytes per row of the staged output tile
   static constexpr int kOut = (BM + kFold) * kOutRow;
   static constexpr int kLds = kRing > kOut ? kRing : kOut;  // 148.5 KB for 256 x 256
@@ -788,12 +787,10 @@ __device__ __forceinline__ bool pp_block(
   uint32_t a_kc[C::kADma + 1];
 #pragma unroll
   for (int q = 0; q < C::kADma; ++q) x_src((wave * C::kADma + q) * 1024 + lane * 16, a_voff[q], a_kc[q]);
-  // tail rows: waves 0 and 1 fetch rows BM..BM+15 and BM+16..BM+31; the
-  // other waves issue an out-of-range op into the dummy KB, so every wave
-  // counts the same number of ops per slice
+  // tail rows: waves 0 and 1 fetch rows BM..BM+15 and BM+16..BM+31 (one
+  // more op per slice than the other waves, whose wait counts exclude it)
   const bool tail_dma = wave < C::kFold / 16;
   x_src(C::kLdsA + wave * 1024 + lane * 16, a_voff[C::kADma], a_kc[C::kADma]);
-  if (!tail_dma) a_voff[C::kADma] = kOOB;
   uint32_t w_voff[C::kWDma];
 #pragma unroll
   for (int q = 0; q < C::kWDma; ++q) {
@@ -805,16 +802,17 @@ __device__ __forceinline__ bool pp_block(
   }
   // Past-the-end slices are issued too (out-of-range loads write zeros), so
   // every wait count is fixed.
-  auto issue = [&](int step, auto ex) {
+  // ex: the tile carries tail rows; td: this wave fetches some of them
+  auto issue = [&](int step, auto ex, auto td) {
     const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
     const int kb0 = step * kDmaKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
       dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < kext_b ? 0u : kOOB),
             base + (wave * C::kADma + q) * 1024);
-    if (decltype(ex)::value)
+    if (decltype(ex)::value && decltype(td)::value)
       dma16(asrd, (a_voff[C::kADma] + kb0) | (kb0 + (int)a_kc[C::kADma] < kext_b ? 0u : kOOB),
-            tail_dma ? base + C::kLdsA + wave * 1024 : lds0 + C::kDummy);
+            base + C::kLdsA + wave * 1024);
     const uint32_t kstep = step < nsteps ? (uint32_t)(step * 32) * (uint32_t)n_b : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
@@ -887,39 +885,39 @@ __device__ __forceinline__ bool pp_block(
   // The schedule; `ex` (compile time) adds the tail fragment and its DMA op.
   // Four straight-line loops (half x active), each with the same barriers and
   // DMA as its partner, so no loop carries a branch.
-  auto run = [&](auto ex) {
-    constexpr int kInFlight = (S - 2) * (C::kPerStage + (decltype(ex)::value ? 1 : 0));
+  auto run = [&](auto ex, auto td) {
+    constexpr int kInFlight = (S - 2) * (C::kPerStage + (decltype(ex)::value && decltype(td)::value ? 1 : 0));
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t) issue(t, ex);
+    for (int t = 0; t < S - 1; ++t) issue(t, ex, td);
     wait_vmcnt<kInFlight>();
     bar();  // barrier 0: slice 0 has landed
     if (wm == 0) {
       if (wave_active) {
         read_frags(0, ex);
-        issue(S - 1, ex);
+        issue(S - 1, ex, td);
         bar();
         for (int s = 0; s < nsteps; ++s) {
           multiply(ex);
           wait_vmcnt<kInFlight>();
           bar();
           read_frags(s + 1, ex);
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           bar();
         }
       } else {
-        issue(S - 1, ex);
+        issue(S - 1, ex, td);
         bar();
         for (int s = 0; s < nsteps; ++s) {
           wait_vmcnt<kInFlight>();
           bar();
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           bar();
         }
       }
       bar();  // matches the second half's last barrier
     } else {
       bar();
-      issue(S - 1, ex);
+      issue(S - 1, ex, td);
       if (wave_active) {
         read_frags(0, ex);
         wait_vmcnt<kInFlight>();
@@ -928,7 +926,7 @@ __device__ __forceinline__ bool pp_block(
           multiply(ex);
           bar();
           read_frags(s + 1, ex);
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           wait_vmcnt<kInFlight>();
           bar();
         }
@@ -937,15 +935,16 @@ __device__ __forceinline__ bool pp_block(
         bar();
         for (int s = 0; s < nsteps; ++s) {
           bar();
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           wait_vmcnt<kInFlight>();
           bar();
         }
       }
     }
   };
-  if (extra) run(std::true_type{});
-  else run(std::false_type{});
+  if (!extra) run(std::false_type{}, std::false_type{});
+  else if (tail_dma) run(std::true_type{}, std::true_type{});
+  else run(std::true_type{}, std::false_type{});
   wait_vmcnt<0>();  // no DMA may still be landing when the block's LDS is released
 
   const float sc = ld_scale(a_scale) * ld_scale(w_scale);
@@ -1587,8 +1586,7 @@ struct Pp8wCfg {
   static constexpr int kLdsX = (kBM + kFold) * kKB;  // ... with the folded tail rows
   static constexpr int kLdsW = kKB * kBN;        // 16 KB
   static constexpr int kStage = kLdsX + kLdsW;
-  static constexpr int kDummy = kStages * kStage;  // 1 KB that soaks up unused tail DMA
-  static constexpr int kRing = kDummy + 1024;      // 137 KB
+  static constexpr int kRing = kStages * kStage;   // 136 KB
   static constexpr int kOutRow = kBN * 2 + 16;     // bytes per row of the staged output tile
   static constexpr int kOut = (kBM + kFold) * kOutRow;
   static constexpr int kLds = kRing > kOut ? kRing : kOut;  // 148.5 KB
@@ -1640,12 +1638,10 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
   uint32_t a_voff[C::kADma + 1], a_kc[C::kADma + 1];
 #pragma unroll
   for (int q = 0; q < C::kADma; ++q) x_src((wave * C::kADma + q) * 1024 + lane * 16, a_voff[q], a_kc[q]);
-  // tail rows: waves 0 and 1 fetch rows BM..BM+15 and BM+16..BM+31; the
-  // other waves issue an out-of-range op into the dummy KB, so every wave
-  // counts the same number of ops per slice
+  // tail rows: waves 0 and 1 fetch rows BM..BM+15 and BM+16..BM+31 (one
+  // more op per slice than the other waves, whose wait counts exclude it)
   const bool tail_dma = wave < C::kFold * C::kKB / 1024;
   x_src(C::kLdsA + wave * 1024 + lane * 16, a_voff[C::kADma], a_kc[C::kADma]);
-  if (!tail_dma) a_voff[C::kADma] = kOOB;
   uint32_t w_voff[C::kWDma];
 #pragma unroll
   for (int q = 0; q < C::kWDma; ++q) {
@@ -1656,15 +1652,16 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
   }
   // Past-the-end slices are issued too (out-of-range loads write zeros); K
   // rows past Hin lie past the weight descriptor's end.
-  auto issue = [&](int step, auto ex) {
+  // ex: the tile carries tail rows; td: this wave fetches some of them
+  auto issue = [&](int step, auto ex, auto td) {
     const uint32_t base = lds0 + (step % C::kStages) * C::kStage;
     const int kb0 = step * C::kKB;
 #pragma unroll
     for (int q = 0; q < C::kADma; ++q)
       dma16(asrd, (a_voff[q] + kb0) | (kb0 + (int)a_kc[q] < rowb ? 0u : kOOB), base + (wave * C::kADma + q) * 1024);
-    if (decltype(ex)::value)
+    if (decltype(ex)::value && decltype(td)::value)
       dma16(asrd, (a_voff[C::kADma] + kb0) | (kb0 + (int)a_kc[C::kADma] < rowb ? 0u : kOOB),
-            tail_dma ? base + C::kLdsA + wave * 1024 : lds0 + C::kDummy);
+            base + C::kLdsA + wave * 1024);
     const uint32_t kstep = step < nsteps ? (uint32_t)kb0 * (uint32_t)N : kOOB;
 #pragma unroll
     for (int q = 0; q < C::kWDma; ++q)
@@ -1740,41 +1737,41 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
     }
   };
 
-  // The schedule: gmm_pp_kernel's; `ex` (compile time) adds the tail block
-  // and its DMA op.
-  auto run = [&](auto ex) {
-    constexpr int kInFlight = (S - 2) * (C::kPerStage + (decltype(ex)::value ? 1 : 0));
+  // The schedule: gmm_pp_kernel's; `ex` (compile time) adds the tail block,
+  // and `td` its DMA op in waves 0 and 1.
+  auto run = [&](auto ex, auto td) {
+    constexpr int kInFlight = (S - 2) * (C::kPerStage + (decltype(ex)::value && decltype(td)::value ? 1 : 0));
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t) issue(t, ex);
+    for (int t = 0; t < S - 1; ++t) issue(t, ex, td);
     wait_vmcnt<kInFlight>();
     bar();  // barrier 0: slice 0 has landed
     if (wm == 0) {
       if (wave_active) {
         read_frags(0, ex);
-        issue(S - 1, ex);
+        issue(S - 1, ex, td);
         bar();
         for (int s = 0; s < nsteps; ++s) {
           multiply(ex);
           wait_vmcnt<kInFlight>();
           bar();
           read_frags(s + 1, ex);
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           bar();
         }
       } else {
-        issue(S - 1, ex);
+        issue(S - 1, ex, td);
         bar();
         for (int s = 0; s < nsteps; ++s) {
           wait_vmcnt<kInFlight>();
           bar();
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           bar();
         }
       }
       bar();  // matches the second half's last barrier
     } else {
       bar();
-      issue(S - 1, ex);
+      issue(S - 1, ex, td);
       if (wave_active) {
         read_frags(0, ex);
         wait_vmcnt<kInFlight>();
@@ -1783,7 +1780,7 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
           multiply(ex);
           bar();
           read_frags(s + 1, ex);
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           wait_vmcnt<kInFlight>();
           bar();
         }
@@ -1792,15 +1789,16 @@ __device__ __forceinline__ void pp8w_block(unsigned char* smem, int p, const uns
         bar();
         for (int s = 0; s < nsteps; ++s) {
           bar();
-          issue(s + S, ex);
+          issue(s + S, ex, td);
           wait_vmcnt<kInFlight>();
           bar();
         }
       }
     }
   };
-  if (extra) run(std::true_type{});
-  else run(std::false_type{});
+  if (!extra) run(std::false_type{}, std::false_type{});
+  else if (tail_dma) run(std::true_type{}, std::true_type{});
+  else run(std::true_type{}, std::false_type{});
   // output map and per-row scales of this lane's rows, fetched while the
   // past-the-end DMA drains
   int dpre[5] = {0, 0, 0, 0, 0};
