@@ -9,7 +9,7 @@
 //            order and gated (by the GEMM's scattering epilogue).
 // Both are pure bandwidth kernels: blocks over (output token, column
 // stripe), 16-byte vector accesses when the row pitch allows, every input
-// row read once. Few tokens (decode) get several column stripes per token,
+// row read once (the weighted sum's loads and stores nontemporal). Few tokens (decode) get several column stripes per token,
 // so that each thread issues the loads of all K rows of one vector at once.
 #include "common.h"
 
@@ -33,6 +33,43 @@ __global__ __launch_bounds__(256) void combine_weighted_kernel(const void* __res
       // no permutation: rows t*K+k in place; no gate: weight 1
       src[k] = k < K ? (perm_dst != nullptr ? perm_dst[(int64_t)t * K + k] : t * K + k) : 0;
       g[k] = k < K ? (gate != nullptr ? gate[(int64_t)t * K + k] : 1.f) : 0.f;
+    }
+    if (VE * sizeof(E) == 16) {
+      // 16-byte vectors: the loads of all K rows are in flight before the
+      // first is used; rows are read once and outputs written once, so both
+      // are nontemporal
+      typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+      for (int j = blockIdx.y * blockDim.x + threadIdx.x; j < nv; j += gridDim.y * blockDim.x) {
+        u4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k < K)
+            v[k] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(yp + (int64_t)src[k] * N + (int64_t)j * VE));
+        float acc[VE];
+#pragma unroll
+        for (int q = 0; q < VE; ++q) acc[q] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k < K) {
+            E e[VE];
+            *reinterpret_cast<u4*>(e) = v[k];
+#pragma unroll
+            for (int q = 0; q < VE; ++q) {
+              const float f = BF16 ? bf16_to_f32((bf16_t)e[q]) : (float)e[q];
+              acc[q] = fmaf(g[k], f, acc[q]);
+            }
+          }
+        }
+        E o[VE];
+#pragma unroll
+        for (int q = 0; q < VE; ++q) {
+          if (BF16) o[q] = (E)f32_to_bf16(acc[q]);
+          else o[q] = (E)acc[q];
+        }
+        __builtin_nontemporal_store(*reinterpret_cast<u4*>(o),
+                                    reinterpret_cast<u4*>(out + (int64_t)t * N + (int64_t)j * VE));
+      }
+      continue;
     }
     for (int j = blockIdx.y * blockDim.x + threadIdx.x; j < nv; j += gridDim.y * blockDim.x) {
       float acc[VE];
