@@ -782,9 +782,14 @@ def test_gmm_mxfp4_grid_values_bit_exact_and_equal_to_fp8_mx():
 
 # ---------------------------------------------------------------- combine
 
-@pytest.mark.parametrize("dt,N", [("bf16", 264), ("bf16", 30), ("f32", 30), ("f32", 128)])
-def test_combine_weighted_parity(dt, N):
-    T, E, K = 200, 16, 6
+@pytest.mark.parametrize("dt,N,T,K", [("bf16", 264, 200, 6), ("bf16", 30, 200, 6), ("f32", 30, 200, 6),
+                                      ("f32", 128, 200, 6), ("bf16", 264, 200, 1), ("bf16", 264, 200, 8),
+                                      ("bf16", 4096, 2100, 2), ("f32", 1032, 2100, 3)])
+def test_combine_weighted_parity(dt, N, T, K):
+    """Every row path of the weighted sum: 16-byte vectors with all K row
+    loads issued first (several vectors per thread once T >= 2048 leaves one
+    column stripe per token), and the element-wise path for odd widths."""
+    E = 16
     idx = synth.random_routing(500, T, E, K)
     _, _, psrc, pdst = oracle.permute(idx, E)
     yp = synth.normal(501, (T * K, N), dtype=dt)
