@@ -235,6 +235,9 @@ GMM_CASES = [
     # last row pieces of 1..32 rows ride on the tile before (257, 513, 800 = 768+32,
     # 1055 = 1024+31, 288); 289 = 256+33 gets a tile of its own
     ("bf16_fold_tails", [257, 513, 800, 1055, 288, 289], 256, 320, "bf16"),
+    # K = 2112 (66 slices): one block per tile instead of the persistent form;
+    # folded tails and a 64-column last column tile through the staged epilogue
+    ("bf16_pp_long_k_fold", [257, 800, 289], 2112, 320, "bf16"),
     ("bf16_stream", [5, 0, 17, 30, 1, 0, 9, 12, 3, 31, 0, 2, 8, 16, 4, 7], 512, 320, "bf16"),
     ("bf16_stream_unaligned", [3, 0, 14, 6, 1, 9], 90, 100, "bf16"),
     ("bf16_stream_overflow_rows", [2, 80, 1, 0, 3, 1, 2, 3], 256, 192, "bf16"),
@@ -361,6 +364,7 @@ GATHER_CASES = [
     # (name, counts, Hin, N, dtype, K): one per kernel family, plus fold and split
     ("bf16_pp_fold", [257, 513, 800, 1055, 0, 289], 256, 320, "bf16", 2),
     ("bf16_pp_split", [1812, 1812], 544, 5120, "bf16", 4),
+    ("bf16_pp_long_k_fold", [257, 800, 0, 289], 2112, 320, "bf16", 2),
     ("bf16_tiled_unaligned", [270, 3, 0, 400], 300, 130, "bf16", 2),
     ("bf16_stream", [5, 0, 17, 30, 1, 0, 9, 12, 3, 31, 0, 2, 8, 16, 4, 7], 512, 320, "bf16", 8),
     ("bf16_stream_unaligned", [3, 0, 14, 6, 1, 9], 90, 100, "bf16", 3),
