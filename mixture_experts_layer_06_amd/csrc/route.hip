@@ -449,7 +449,7 @@ __global__ __launch_bounds__(G * TF <= 2 ? 1024 : 512) void route_bf16_kernel(
 // expert row is padded to 64. Wave w owns chunks [w*cpw, (w+1)*cpw) and
 // copies only the weight rows of those chunks (contiguous in W_r) into its
 // own LDS slab, so no block barrier precedes the multiply: the weight loads
-// and the token loads of a pass of up to kSmallPass chunks are all issued
+// and the token loads of a pass of up to small_pass<E_>() chunks are all issued
 // at once, then the slab is written and read back in the row operand's
 // layout (lane (i, kq): expert i, h = 32c + 8kq .. +7) by the same wave. The
 // waves' partial scores (one 16 x 16 fragment each, written over the start
@@ -458,10 +458,19 @@ __global__ __launch_bounds__(G * TF <= 2 ? 1024 : 512) void route_bf16_kernel(
 // With blk_counts set the block also writes how many of its selections went
 // to each expert (row blockIdx.x of E counts), the per-chunk counts of the
 // dispatch.
-constexpr int kSmallPass = 8;  // chunks per pass
+// Chunks per pass: 16 (a wave's 16 token loads and its weight loads of a
+// pass all in flight; 8 waves of 16 chunks measured 0.9 us faster than 16
+// waves of 8 on the prefill shape), 8 with 16 experts, whose weight loads
+// would not fit the register budget of 16 waves.
+template <int E_>
+constexpr int small_pass() { return E_ <= 12 ? 16 : 8; }
 
 template <int E_>
-constexpr int small_slab_bytes() { return kSmallPass * kChunk * E_ * 2; }
+constexpr int small_slab_bytes() { return small_pass<E_>() * kChunk * E_ * 2; }
+
+// Waves per block: at most 16, and their slabs within 156 KB of LDS.
+template <int E_>
+constexpr int small_max_waves() { return (156 * 1024) / small_slab_bytes<E_>() < 16 ? (156 * 1024) / small_slab_bytes<E_>() : 16; }
 
 template <int E_>
 __global__ __launch_bounds__(1024) void route_small_kernel(const bf16_t* __restrict__ x,
@@ -474,6 +483,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const bf16_t* __restr
   __shared__ int hist[16];  // the block's selections per expert (blk_counts != nullptr)
   if (threadIdx.x < 16) hist[threadIdx.x] = 0;
   constexpr int kSlab = small_slab_bytes<E_>();
+  constexpr int kSmallPass = small_pass<E_>();
   constexpr int kPieces = kSmallPass * kChunk * E_ * 2 / 16;  // 16-byte pieces of a full pass
   constexpr int kPw = kPieces / kWave;                         // per lane
   static_assert(kPieces % kWave == 0 && kSlab >= kTok * 16 * 4, "slab holds a pass and a partial fragment");
@@ -702,22 +712,25 @@ void launch_bf16_tf(const RoutePlan& p, const void* x, const void* wr, const flo
   }
 }
 
-// Waves: up to one pass of chunks each, at most 16. LDS: one slab per wave.
+// Waves: up to one pass of chunks each, at most small_max_waves. LDS: one
+// slab per wave.
+template <int E_>
 inline int small_waves(int H) {
-  const int nw = cdiv(cdiv(H, kChunk), kSmallPass);
-  return nw < 1 ? 1 : (nw > 16 ? 16 : nw);
+  const int nw = cdiv(cdiv(H, kChunk), small_pass<E_>());
+  return nw < 1 ? 1 : (nw > small_max_waves<E_>() ? small_max_waves<E_>() : nw);
 }
 
 template <int E_>
 void launch_small(const void* x, const void* wr, const float* bias, int T, int H, int K, int32_t* idx,
                   float* gate, int32_t* blk_counts, hipStream_t s) {
-  const int nw = small_waves(H);
+  const int nw = small_waves<E_>(H);
   const size_t lds = (size_t)nw * small_slab_bytes<E_>();
   static bool attr_done = false;
   if (!attr_done) {
-    // 16 slabs at most; the kernel also has a small static array
+    // small_max_waves slabs at most; the kernel also has a small static array
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_small_kernel<E_>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 16 * small_slab_bytes<E_>());
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              small_max_waves<E_>() * small_slab_bytes<E_>());
     attr_done = true;
   }
   hipLaunchKernelGGL((route_small_kernel<E_>), dim3(cdiv(T, kTok)), dim3(nw * kWave), lds, s, (const bf16_t*)x,

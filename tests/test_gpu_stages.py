@@ -40,6 +40,10 @@ ROUTE_CASES = [
     ("k_eq_e", 33, 96, 4, 4, "f32", False, False),
     # one case per router kernel instance: 64-expert groups 1/2/4, aligned or not
     ("prefill_like", 48, 4096, 8, 2, "bf16", False, False),
+    # the few-expert kernel with 5 waves whose passes stop short of 16 chunks
+    # (4 experts), and with 16 waves of 8-chunk passes (16 experts)
+    ("small_e4_h2112", 4096, 2112, 4, 2, "bf16", False, False),
+    ("small_e16_h4096", 4096, 4096, 16, 4, "bf16", False, False),
     ("e128_int_ties", 40, 256, 128, 8, "bf16", True, False),
     ("e100_ragged_bias", 50, 90, 100, 4, "bf16", False, True),
     ("e200_ragged", 20, 70, 200, 3, "bf16", False, False),
